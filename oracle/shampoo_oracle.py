@@ -1,0 +1,272 @@
+"""fp64 CPU oracle for the Shampoo optimizer step -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The GPU library never calls it, and the
+two share no code: this file restates the method from the pages with NumPy in
+fp64, block by block, with no blocking, fusion or reordering beyond what the
+definition states.
+
+Sources.  The method is described in "Scalable Second Order Optimization for
+Deep Learning" (Anil, Gupta, Koren, Regan, Singer); the only technical account
+on the pages is the Shampoo-at-scale podcast transcript:
+  * cue 6-8   -- one small statistics matrix per dimension of a 2-D weight,
+                 "L" for rows and "R" for columns, standing in for full-matrix
+                 Adagrad through a Kronecker product;
+  * cue 10    -- three extra pieces of work per step: accumulate gradient outer
+                 products into L and R; the inverse fourth roots of L and R;
+                 the preconditioned gradient multiply;
+  * cue 12    -- the root is the expensive step, done by coupled Newton or an
+                 SVD, in double precision because L and R are ill-conditioned;
+  * cue 14-16 -- roots recomputed only every so often and the last ones reused
+                 meanwhile; over-large layers split into blocks that are each
+                 preconditioned on their own (Lemma 2).
+Everything else (EMA weighting of the statistics, the damping rule
+eps = eps_rel * lambda_max, grafting to diagonal Adagrad, heavy-ball momentum,
+the Adagrad fallback for very large dimensions and for sparse embedding rows)
+is not on the pages; it is this library's stated configuration and every such
+choice is named where it is used.
+
+Root.  For a symmetric PSD factor the inverse p-th root is unique (the principal
+SPD root); the oracle obtains it from the symmetric eigendecomposition
+(numpy.linalg.eigh, LAPACK), which for SPD matrices is the SVD the transcript
+names in cue 12.  The GPU reaches the same matrix by coupled Newton iteration.
+
+Pins.  tests/test_oracle_pins.py checks every function here against exact
+rational brute force, 50-digit mpmath eigenvalues, SciPy's Schur-Pade
+fractional power, closed forms for diagonal and rank-1 gradients, and
+invariants.  The constants beta1, graft_eps and the cadence of the larger
+workloads are configuration, not outputs; no page fixes their values (their
+parity is unpinned, though both sides read them from one config).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# ----------------------------------------------------------------- config
+@dataclass
+class OracleConfig:
+    block_size: int
+    max_precond_dim: int = 0      # 0: no limit
+    root_p: int = 4
+    beta1: float = 0.9
+    beta2: float = 0.999
+    lr: float = 1e-3
+    eps_rel: float = 1e-6
+    graft_eps: float = 1e-10
+    cadence: int = 1
+
+
+# ------------------------------------------------------- blocking (Lemma 2)
+def split_dim(d: int, b: int) -> List[Tuple[int, int]]:
+    """Chunks (start, length) of one dimension: full chunks of b from the top
+    or left, the last one ragged.  Lemma 2 (podcast cue 16) blocks a layer and
+    preconditions each block separately; the pages give no partition rule, so
+    the plainest one is used: top-left aligned b x b tiles."""
+    if d <= 0:
+        return []
+    return [(s, min(b, d - s)) for s in range(0, d, b)]
+
+
+def blocks(m: int, n: int, b: int) -> List[Tuple[int, int, int, int]]:
+    """(r0, mb, c0, nb) for every block of an m x n tensor, row-major order."""
+    return [(r0, mb, c0, nb) for r0, mb in split_dim(m, b) for c0, nb in split_dim(n, b)]
+
+
+def uses_shampoo(m: int, n: int, cfg: OracleConfig) -> bool:
+    """Tensors with a dimension above max_precond_dim take diagonal Adagrad
+    instead (a configuration of this library, not of the pages)."""
+    return cfg.max_precond_dim <= 0 or max(m, n) <= cfg.max_precond_dim
+
+
+# -------------------------------------------------------------- statistics
+def ema_weights(beta2: float) -> Tuple[float, float]:
+    """(decay, weight of the new outer product).  The transcript says the
+    statistics accumulate outer products (cue 10); this library keeps an
+    exponential moving average with decay beta2, weighting the new term by
+    1 - beta2, and a plain sum when beta2 == 1."""
+    return beta2, (1.0 - beta2) if beta2 < 1.0 else 1.0
+
+
+def update_statistics(L: np.ndarray, R: np.ndarray, G: np.ndarray, beta2: float):
+    """L <- beta2 L + w G G^T,  R <- beta2 R + w G^T G  (cue 10), in fp64."""
+    d, w = ema_weights(beta2)
+    g = np.asarray(G, dtype=np.float64)
+    return d * L + w * (g @ g.T), d * R + w * (g.T @ g)
+
+
+# ------------------------------------------------------------ inverse root
+@dataclass
+class RootResult:
+    P: Optional[np.ndarray]     # None when the input is not finite
+    lam_max: float
+    lam_min: float
+    eps: float
+    kappa: float                # (lam_max + eps) / (lam_min + eps), eigenvalues clamped at 0
+    ok: bool
+
+
+def inverse_root(S: np.ndarray, eps_rel: float, p: int, eps: Optional[float] = None) -> RootResult:
+    """(S + eps I)^(-1/p) by symmetric eigendecomposition (cue 10: inverse
+    fourth root; cue 12: SVD route, double precision).
+
+    eps = eps_rel * lambda_max(S) unless an explicit eps is given (the GPU's own
+    eps, for stage-isolated comparison).  Eigenvalues below zero (rounding of a
+    PSD matrix) are clamped to zero before eps is added.  A factor whose
+    largest eigenvalue is not positive (no statistics yet) gets P = I.  A
+    non-finite factor returns ok=False and no P, so the caller keeps the
+    previous root (cue 14-16: training carries on with the last preconditioner).
+    The input is symmetrised as (S + S^T)/2 first."""
+    S = np.asarray(S, dtype=np.float64)
+    n = S.shape[0]
+    if not np.all(np.isfinite(S)):
+        return RootResult(None, np.nan, np.nan, np.nan, np.nan, False)
+    S = 0.5 * (S + S.T)
+    lam, V = np.linalg.eigh(S)
+    lmax = float(lam[-1]) if n else 0.0
+    if n == 0 or lmax <= 0.0:
+        return RootResult(np.eye(n), lmax, lmax, 0.0, 1.0, True)
+    e = eps_rel * lmax if eps is None else float(eps)
+    lam = np.maximum(lam, 0.0)
+    P = (V * (lam + e) ** (-1.0 / p)) @ V.T
+    return RootResult(P, lmax, float(lam[0]), e, (lmax + e) / (lam[0] + e), True)
+
+
+# --------------------------------------------------------- precondition
+def precondition(PL: np.ndarray, G: np.ndarray, PR: np.ndarray) -> np.ndarray:
+    """D = L^(-1/4) G R^(-1/4): the preconditioned gradient multiply (cue 10,
+    cue 14)."""
+    return PL @ np.asarray(G, dtype=np.float64) @ PR
+
+
+# ---------------------------------------------------------------- graft
+def adagrad_accumulate(a: np.ndarray, G: np.ndarray) -> np.ndarray:
+    """Diagonal Adagrad accumulator a <- a + G*G (a plain running sum)."""
+    g = np.asarray(G, dtype=np.float64)
+    return a + g * g
+
+
+def adagrad_direction(a: np.ndarray, G: np.ndarray, delta: float) -> np.ndarray:
+    """A = G / (sqrt(a) + delta), with a already including this step."""
+    return np.asarray(G, dtype=np.float64) / (np.sqrt(a) + delta)
+
+
+def graft(A_b: np.ndarray, D_b: np.ndarray) -> np.ndarray:
+    """Per-block grafting: keep D's direction, take Adagrad's magnitude,
+    U = D * ||A||_F / ||D||_F; U = 0 when ||D||_F = 0.  Not on the pages; a
+    configuration of this library (magnitude from diagonal Adagrad, direction
+    from Shampoo, per Lemma-2 block)."""
+    nd = float(np.sqrt(np.sum(D_b * D_b)))
+    if nd == 0.0:
+        return np.zeros_like(D_b)
+    return D_b * (float(np.sqrt(np.sum(A_b * A_b))) / nd)
+
+
+def momentum_update(mom: np.ndarray, W: np.ndarray, U: np.ndarray, beta1: float, lr: float):
+    """Heavy-ball momentum and the weight update: mom <- beta1 mom + U,
+    W <- W - lr mom.  Returns (mom, W)."""
+    mom = beta1 * mom + U
+    return mom, W - lr * mom
+
+
+def sparse_rows_update(a: np.ndarray, W: np.ndarray, rows: np.ndarray, g: np.ndarray,
+                       lr: float, delta: float):
+    """Sparse-row Adagrad for embedding tables: for each touched row r,
+    a_r += g_r^2 and W_r -= lr g_r / (sqrt(a_r) + delta); untouched rows and
+    momentum are left alone.  Rows must be distinct.  Returns (a, W)."""
+    a = a.copy()
+    W = W.copy()
+    gr = np.asarray(g, dtype=np.float64)
+    for k, r in enumerate(np.asarray(rows)):
+        a[r] = a[r] + gr[k] * gr[k]
+        W[r] = W[r] - lr * gr[k] / (np.sqrt(a[r]) + delta)
+    return a, W
+
+
+# ----------------------------------------------------------- whole step
+class _BlockState:
+    def __init__(self, mb: int, nb: int):
+        self.L = np.zeros((mb, mb))
+        self.R = np.zeros((nb, nb))
+        self.PL = np.eye(mb)
+        self.PR = np.eye(nb)
+        self.root_L: Optional[RootResult] = None
+        self.root_R: Optional[RootResult] = None
+
+
+class ShampooOracle:
+    """The whole optimizer step over a list of tensors, fp64.
+
+    shapes: list of (rows, cols, kind) with kind "dense" or "sparse".
+    weights: initial fp32 weights (converted to fp64).
+
+    step(grads, t) with grads[i] an (m, n) array for dense tensors or a
+    (rows, row_grads) pair for sparse tensors, t counted from 0:
+      1. statistics of every Shampoo block (cue 10);
+      2. if t % cadence == 0, inverse p-th roots of every factor (cue 10, 12,
+         14), keeping the previous root for a non-finite factor;
+      3. D = PL G PR per block (cue 10);
+      4. a += G*G per tensor, A = G/(sqrt(a)+delta), per-block graft U;
+         tensors over max_precond_dim use U = A;
+      5. heavy-ball momentum and weight update;
+      6. sparse tables: sparse-row Adagrad.
+    """
+
+    def __init__(self, cfg: OracleConfig, shapes: Sequence[Tuple[int, int, str]],
+                 weights: Sequence[np.ndarray]):
+        self.cfg = cfg
+        self.shapes = [(int(m), int(n), k) for m, n, k in shapes]
+        self.W = [np.asarray(w, dtype=np.float64).copy() for w in weights]
+        self.a = [np.zeros((m, n)) for m, n, _ in self.shapes]
+        self.mom = [np.zeros((m, n)) for m, n, _ in self.shapes]
+        self.blocks: Dict[int, List[Tuple[Tuple[int, int, int, int], _BlockState]]] = {}
+        for i, (m, n, kind) in enumerate(self.shapes):
+            if kind == "dense" and uses_shampoo(m, n, cfg):
+                self.blocks[i] = [(bk, _BlockState(bk[1], bk[3]))
+                                  for bk in blocks(m, n, cfg.block_size)]
+        self.last_D: Dict[int, np.ndarray] = {}
+
+    def step(self, grads, t: int) -> List[np.ndarray]:
+        cfg = self.cfg
+        recompute = (t % cfg.cadence) == 0
+        deltas = []
+        for i, (m, n, kind) in enumerate(self.shapes):
+            W_old = self.W[i]
+            if kind == "sparse":
+                rows, g = grads[i]
+                self.a[i], self.W[i] = sparse_rows_update(self.a[i], self.W[i], rows, g,
+                                                          cfg.lr, cfg.graft_eps)
+                deltas.append(self.W[i] - W_old)
+                continue
+            G = np.asarray(grads[i], dtype=np.float64)
+            self.a[i] = adagrad_accumulate(self.a[i], G)
+            A = adagrad_direction(self.a[i], G, cfg.graft_eps)
+            if i in self.blocks:
+                U = np.zeros((m, n))
+                D_full = np.zeros((m, n))
+                for (r0, mb, c0, nb), st in self.blocks[i]:
+                    Gb = G[r0:r0 + mb, c0:c0 + nb]
+                    st.L, st.R = update_statistics(st.L, st.R, Gb, cfg.beta2)
+                    if recompute:
+                        st.root_L = inverse_root(st.L, cfg.eps_rel, cfg.root_p)
+                        st.root_R = inverse_root(st.R, cfg.eps_rel, cfg.root_p)
+                        if st.root_L.ok:
+                            st.PL = st.root_L.P
+                        if st.root_R.ok:
+                            st.PR = st.root_R.P
+                    Db = precondition(st.PL, Gb, st.PR)
+                    D_full[r0:r0 + mb, c0:c0 + nb] = Db
+                    U[r0:r0 + mb, c0:c0 + nb] = graft(A[r0:r0 + mb, c0:c0 + nb], Db)
+                self.last_D[i] = D_full
+            else:
+                U = A
+            self.mom[i], self.W[i] = momentum_update(self.mom[i], self.W[i], U,
+                                                     cfg.beta1, cfg.lr)
+            deltas.append(self.W[i] - W_old)
+        return deltas
+
+    def block_states(self, i: int):
+        return self.blocks.get(i, [])
