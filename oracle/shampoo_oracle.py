@@ -109,17 +109,22 @@ class RootResult:
     ok: bool
 
 
-def inverse_root(S: np.ndarray, eps_rel: float, p: int, eps: Optional[float] = None) -> RootResult:
+def inverse_root(S: np.ndarray, eps_rel: float, p: int, eps: Optional[float] = None,
+                 clamp: bool = True) -> RootResult:
     """(S + eps I)^(-1/p) by symmetric eigendecomposition (cue 10: inverse
     fourth root; cue 12: SVD route, double precision).
 
     eps = eps_rel * lambda_max(S) unless an explicit eps is given (the GPU's own
-    eps, for stage-isolated comparison).  Eigenvalues below zero (rounding of a
-    PSD matrix) are clamped to zero before eps is added.  A factor whose
-    largest eigenvalue is not positive (no statistics yet) gets P = I.  A
-    non-finite factor returns ok=False and no P, so the caller keeps the
-    previous root (cue 14-16: training carries on with the last preconditioner).
-    The input is symmetrised as (S + S^T)/2 first."""
+    eps, for stage-isolated comparison).  With clamp=True (the optimizer's own
+    statistics), eigenvalues below zero -- rounding of a PSD matrix -- are
+    clamped to zero before eps is added.  With clamp=False the result is the
+    exact principal root of the damped matrix as given (used to check a GPU
+    root against the very matrix the GPU received); it requires
+    S + eps I to be positive definite, else ok=False.  A factor whose largest
+    eigenvalue is not positive (no statistics yet) gets P = I.  A non-finite
+    factor returns ok=False and no P, so the caller keeps the previous root
+    (cue 14-16: training carries on with the last preconditioner).  The input
+    is symmetrised as (S + S^T)/2 first."""
     S = np.asarray(S, dtype=np.float64)
     n = S.shape[0]
     if not np.all(np.isfinite(S)):
@@ -130,7 +135,10 @@ def inverse_root(S: np.ndarray, eps_rel: float, p: int, eps: Optional[float] = N
     if n == 0 or lmax <= 0.0:
         return RootResult(np.eye(n), lmax, lmax, 0.0, 1.0, True)
     e = eps_rel * lmax if eps is None else float(eps)
-    lam = np.maximum(lam, 0.0)
+    if clamp:
+        lam = np.maximum(lam, 0.0)
+    elif lam[0] + e <= 0.0:
+        return RootResult(None, lmax, float(lam[0]), e, np.inf, False)
     P = (V * (lam + e) ** (-1.0 / p)) @ V.T
     return RootResult(P, lmax, float(lam[0]), e, (lmax + e) / (lam[0] + e), True)
 

@@ -177,6 +177,15 @@ def test_root_scalar_and_degenerate_cases():
     e = 2e-6
     ref = H @ np.diag((np.maximum(lam, 0) + e) ** -0.25) @ H
     assert np.abs(r.P - ref).max() <= 1e-9 * np.abs(ref).max()
+    # unclamped: the exact root of the damped matrix as given
+    lam2 = np.array([-5e-7, 0.5, 1.0, 2.0])
+    S2 = H @ np.diag(lam2) @ H
+    ru = O.inverse_root(S2, 1e-6, 4, clamp=False)
+    ref2 = H @ np.diag((lam2 + e) ** -0.25) @ H
+    assert np.abs(ru.P - ref2).max() <= 1e-9 * np.abs(ref2).max()
+    rc = O.inverse_root(S2, 1e-6, 4)
+    assert np.abs(rc.P - ref2).max() > 1e-2 * np.abs(ref2).max()     # the two readings differ
+    assert not O.inverse_root(H @ np.diag([-3e-6, 0.5, 1.0, 2.0]) @ H, 1e-6, 4, clamp=False).ok
 
 
 # ------------------------------------------------------- whole-step closed forms
