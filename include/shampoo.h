@@ -1,0 +1,224 @@
+/*
+ * shampoo.h -- C-ABI of libshampoo_mi355x.so: the Shampoo optimizer step on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Scalable Second Order Optimization for Deep Learning" (Anil, Gupta,
+ * Koren, Regan, Singer).  The pages describe it in the Shampoo-at-scale
+ * podcast transcript: a 2-D weight keeps one statistics matrix per dimension,
+ * L (rows) and R (columns) (cues 6-7); each step adds three pieces of work --
+ * accumulate gradient outer products into L and R, take the inverse fourth
+ * roots of L and R, and multiply the gradient by them (cue 10); the roots are
+ * expensive, computed by coupled Newton iteration, in double precision when
+ * the statistics are ill-conditioned (cue 12), and only every so often, the
+ * last ones being reused in between (cue 14); over-large layers are split into
+ * blocks that are preconditioned separately (Lemma 2, cue 16).  The paper runs
+ * the roots on host CPUs; this library runs the whole step on the GPU.
+ *
+ * Not on the pages, and fixed by this library's configuration instead:
+ * exponential moving average of the statistics (beta2), damping
+ * eps = eps_rel * lambda_max of each factor, per-block grafting of the update
+ * magnitude to diagonal Adagrad, heavy-ball momentum (beta1), diagonal Adagrad
+ * for tensors with a dimension above max_precond_dim and sparse-row Adagrad
+ * for embedding tables.
+ *
+ * Conventions for every call below:
+ *   - All device pointers are HIP device memory on the current device; all
+ *     tensors are fp32, row-major, contiguous.
+ *   - `stream` is a hipStream_t passed as void* (NULL: the null stream).  Calls
+ *     enqueue work and return without waiting, except shampoo_bind_state and
+ *     shampoo_get_diagnostics, which wait for their own work.  Calls on one
+ *     handle must be ordered (issue them on one stream).  A handle is not
+ *     thread-safe.
+ *   - Return value: SHAMPOO_OK (0) or a negative shampoo_status.  Argument and
+ *     state errors are detected on the host before anything is enqueued.
+ *     Numerical conditions (non-finite statistics, a root that failed) never
+ *     fail a call: they are recorded per factor and read back with
+ *     shampoo_get_diagnostics.  No C++ exception crosses this interface.
+ */
+#ifndef SHAMPOO_MI355X_H
+#define SHAMPOO_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct shampoo_s shampoo_t; /* opaque; owns host memory only (the plan) */
+
+typedef enum {
+    SHAMPOO_OK = 0,
+    SHAMPOO_E_ARG = -1,         /* null pointer, bad size or shape, bad config value  */
+    SHAMPOO_E_STATE = -2,       /* no state bound, or state too small                 */
+    SHAMPOO_E_HIP = -3,         /* a HIP call or kernel launch failed                 */
+    SHAMPOO_E_NOMEM = -4,       /* host allocation failed                             */
+    SHAMPOO_E_UNSUPPORTED = -5  /* valid but not supported (e.g. root_p not 1,2,4,8)  */
+} shampoo_status;
+
+typedef enum {
+    SHAMPOO_ROOT_F32 = 0,  /* every factor's coupled-Newton root in fp32                  */
+    SHAMPOO_ROOT_F64 = 1,  /* every factor in fp64                                         */
+    SHAMPOO_ROOT_AUTO = 2  /* fp32 first; factors whose estimated condition number of
+                              S + eps I exceeds fp64_cond_threshold are redone in fp64 */
+} shampoo_root_mode;
+
+typedef enum {
+    SHAMPOO_DENSE = 0,       /* 2-D weight: Shampoo blocks, or diagonal Adagrad when a
+                                dimension exceeds max_precond_dim                    */
+    SHAMPOO_SPARSE_ROWS = 1  /* embedding table updated by sparse-row Adagrad        */
+} shampoo_tensor_kind;
+
+typedef struct {
+    int64_t rows, cols;  /* shape of the weight (and of its gradient) */
+    int32_t kind;        /* shampoo_tensor_kind */
+    int32_t reserved;    /* must be 0 */
+} shampoo_tensor_desc;
+
+typedef struct {
+    int32_t block_size;       /* b: Lemma-2 block edge; blocks are top-left aligned b x b
+                                 tiles, the last row/column of blocks ragged (>= 1)      */
+    int32_t max_precond_dim;  /* dense tensors with a dimension above this use diagonal
+                                 Adagrad; 0 = no limit                                   */
+    int32_t root_p;           /* p of the inverse p-th root; the pages use 4 (cue 10)    */
+    int32_t newton_iters;     /* coupled-Newton iterations per root (e.g. 20)           */
+    int32_t root_mode;        /* shampoo_root_mode                                       */
+    int32_t lanczos_steps;    /* Krylov steps for the eigenvalue estimates; 0 = 32       */
+    int32_t reserved;         /* must be 0 */
+    double beta1;             /* momentum: mom <- beta1 mom + U                          */
+    double beta2;             /* statistics: S <- beta2 S + (1-beta2) outer(G) (beta2<1),
+                                 S <- S + outer(G) when beta2 == 1; 1 - beta2 is formed in
+                                 double, so beta2 is double here                         */
+    double lr;                /* W <- W - lr mom                                          */
+    double eps_rel;           /* eps = eps_rel * lambda_max(S) per factor                */
+    double graft_eps;         /* delta in A = G / (sqrt(a) + delta)                      */
+    double fp64_cond_threshold; /* AUTO mode: kappa(S + eps I) above this -> fp64 root  */
+} shampoo_config;
+
+/* Row-sparse gradient of one SHAMPOO_SPARSE_ROWS table: n_rows distinct row
+ * ids (int32, device) and an n_rows x cols fp32 block of row gradients
+ * (device).  Rows must be distinct within one call; order is free. */
+typedef struct {
+    const int32_t* rows;
+    const float* row_grads;
+    int64_t n_rows;
+} shampoo_sparse_rows;
+
+/* One factor's numbers from the last shampoo_compute_inverse_roots. */
+typedef struct {
+    double lambda_max;   /* Krylov estimate of the largest eigenvalue of S           */
+    double eps;          /* eps_rel * lambda_max: the damping added to S              */
+    double kappa_est;    /* estimate of kappa(S + eps I) from the fp32 root (0: none) */
+    double residual;     /* max |M_N - I| of the coupled iteration that was committed */
+    int32_t block;       /* block index (see shampoo_block_info)                      */
+    int32_t side;        /* 0: L (rows), 1: R (columns)                               */
+    int32_t dim;         /* factor dimension                                          */
+    int32_t status;      /* bit mask of SHAMPOO_FACTOR_* below                         */
+} shampoo_factor_diag;
+
+enum {
+    SHAMPOO_FACTOR_NONFINITE_INPUT = 1,  /* S not finite: previous root kept            */
+    SHAMPOO_FACTOR_NONFINITE_ROOT = 2,   /* iteration went non-finite: previous kept    */
+    SHAMPOO_FACTOR_RESIDUAL_HIGH = 4,    /* committed, but max|M_N - I| > 1e-2          */
+    SHAMPOO_FACTOR_FP64 = 8,             /* root computed in fp64                        */
+    SHAMPOO_FACTOR_ZERO = 16             /* lambda_max <= 0 (no statistics): root = I   */
+};
+
+/* Where one block's state lives in the bound state buffer (byte offsets). */
+typedef struct {
+    int32_t tensor;       /* index into the tensor list                               */
+    int32_t row0, col0;   /* top-left element of the block in the tensor               */
+    int32_t rows, cols;   /* m_b, n_b (ragged at the edges)                            */
+    int32_t ld_l, ld_r;   /* leading dimension (padded) of the L- and R-side matrices  */
+    int32_t factor_l, factor_r; /* factor indices (diagnostics order)                 */
+    int64_t off_l, off_r;       /* fp64 statistics L (rows x rows), R (cols x cols)   */
+    int64_t off_pl, off_pr;     /* fp32 roots P_L, P_R                                */
+    int64_t off_pl64, off_pr64; /* fp64 roots, or -1 when root_mode is F32             */
+} shampoo_block_layout;
+
+/*
+ * shampoo_create -- build the plan for a list of tensors.
+ * cfg: hyper-parameters (copied).  tensors: n_tensors descriptors (copied).
+ * out: receives the handle.  Host only: no HIP call, no device memory.
+ * Dense tensors whose dimensions are both <= max_precond_dim (or any, when it
+ * is 0) are split into Lemma-2 blocks (cue 16); each block gets an L and an R
+ * factor.  Errors: SHAMPOO_E_ARG (null pointer, n_tensors < 1, a dimension
+ * < 1, block_size < 1, newton_iters < 1, beta2 outside (0,1], eps_rel < 0,
+ * unknown kind or root_mode), SHAMPOO_E_UNSUPPORTED (root_p not in
+ * {1,2,4,8}), SHAMPOO_E_NOMEM.
+ */
+int shampoo_create(const shampoo_config* cfg, int32_t n_tensors,
+                   const shampoo_tensor_desc* tensors, shampoo_t** out);
+
+/* Bytes of device state the handle needs (statistics, roots, Adagrad and
+ * momentum accumulators, scratch).  The caller allocates it (e.g. a PyTorch
+ * uint8 tensor), 256-byte aligned, and keeps it alive and in place for the
+ * handle's life.  Host only. */
+int shampoo_state_bytes(const shampoo_t* h, size_t* bytes);
+
+/* Attach the caller's device state buffer and initialise it on `stream`:
+ * statistics, accumulators and momentum zero, roots the identity, and the
+ * plan's descriptor tables uploaded.  Waits for that work to finish.
+ * Errors: SHAMPOO_E_ARG (null, not 256-byte aligned), SHAMPOO_E_STATE (bytes
+ * below shampoo_state_bytes), SHAMPOO_E_HIP. */
+int shampoo_bind_state(shampoo_t* h, void* dev_state, size_t bytes, void* stream);
+
+/* Statistics (cue 10): for every block, L <- beta2 L + w G_b G_b^T and
+ * R <- beta2 R + w G_b^T G_b, w = 1 - beta2 (1 when beta2 == 1): fp32
+ * gradients, fp64 products and accumulation on MFMA, fp64 storage.  grads: n_tensors device pointers, read only; entries of tensors that
+ * are not Shampoo-blocked are ignored (may be NULL).  Errors: SHAMPOO_E_ARG,
+ * SHAMPOO_E_STATE, SHAMPOO_E_HIP. */
+int shampoo_update_stats(shampoo_t* h, const float* const* grads, void* stream);
+
+/* Inverse roots (cue 10, 12, 14): for every factor S, lambda_max by Lanczos,
+ * eps = eps_rel * lambda_max, then P = (S + eps I)^(-1/p) by coupled Newton
+ * iteration (newton_iters steps; fp32, fp64 or routed per root_mode).  A
+ * factor with non-finite S or a non-finite result keeps its previous root; a
+ * factor with lambda_max <= 0 gets P = I.  The caller decides the cadence
+ * (call it when step % k == 0); in between, the last roots are used.
+ * Errors: SHAMPOO_E_STATE, SHAMPOO_E_HIP. */
+int shampoo_compute_inverse_roots(shampoo_t* h, void* stream);
+
+/* Preconditioned multiply and update (cue 10): for every block
+ * D_b = P_L G_b P_R; a <- a + G*G; A = G / (sqrt(a) + graft_eps);
+ * U_b = D_b ||A_b||_F / ||D_b||_F (0 when ||D_b|| = 0);
+ * mom <- beta1 mom + U; W <- W - lr mom.  Tensors above max_precond_dim take
+ * U = A.  Sparse tables: for each listed row r, a_r += g_r^2 and
+ * W_r -= lr g_r / (sqrt(a_r) + graft_eps); other rows untouched; no momentum.
+ * params: n_tensors device pointers, updated in place.  grads: as in
+ * shampoo_update_stats (dense tensors must be non-NULL).  sparse: NULL when
+ * there are no sparse tables, else n_tensors entries (entries of dense tensors
+ * ignored; n_rows == 0 allowed).  Errors: SHAMPOO_E_ARG, SHAMPOO_E_STATE,
+ * SHAMPOO_E_HIP. */
+int shampoo_precondition_and_apply(shampoo_t* h, float* const* params,
+                                   const float* const* grads,
+                                   const shampoo_sparse_rows* sparse, void* stream);
+
+/* Number of factors (2 per block) and blocks in the plan.  Host only. */
+int shampoo_num_factors(const shampoo_t* h, int32_t* n_factors, int32_t* n_blocks);
+
+/* Copy up to `cap` factor records from the last root pass into host memory
+ * (`out`), in factor order.  Waits for `stream`.  Errors: SHAMPOO_E_ARG,
+ * SHAMPOO_E_STATE, SHAMPOO_E_HIP. */
+int shampoo_get_diagnostics(shampoo_t* h, shampoo_factor_diag* out, int32_t cap, void* stream);
+
+/* Layout of block `block` (0 <= block < n_blocks).  Host only. */
+int shampoo_block_info(const shampoo_t* h, int32_t block, shampoo_block_layout* out);
+
+/* Byte offsets in the state buffer of tensor `tensor`'s Adagrad accumulator
+ * and momentum (both fp32, the tensor's shape; mom_off = -1 for sparse
+ * tables), and its block range [first_block, first_block + n_blocks).
+ * Host only. */
+int shampoo_tensor_info(const shampoo_t* h, int32_t tensor, int64_t* adagrad_off,
+                        int64_t* mom_off, int32_t* first_block, int32_t* n_blocks);
+
+/* Free the handle (host memory only; the caller frees the state buffer). */
+void shampoo_destroy(shampoo_t* h);
+
+/* Static text for a status code. */
+const char* shampoo_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SHAMPOO_MI355X_H */

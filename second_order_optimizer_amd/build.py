@@ -1,0 +1,42 @@
+"""Builds libshampoo_mi355x.so in-tree with hipcc for gfx950.
+
+    python -m second_order_optimizer_amd.build
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libshampoo_mi355x.so")
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.cpp", "kernels.hip")]
+HEADERS = [os.path.join(HERE, "csrc", f) for f in ("common.hpp", "kernels.hpp")] + [
+    os.path.join(ROOT, "include", "shampoo.h")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # packed fp32 VALU ops are turned off for every HIP translation unit
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-result",
+]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops" not in l and l.strip())
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{out}")
+    if verbose and out:
+        print(out, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,912 @@
+// C-ABI of libshampoo_mi355x.so: host planner, state layout and launch
+// sequence of the Shampoo step ("Scalable Second Order Optimization for Deep
+// Learning"; Shampoo-at-scale podcast transcript, cues 6-16).
+//
+// The planner splits every dense tensor into Lemma-2 blocks (cue 16), gives
+// each block an L and an R factor, lays out one device state buffer owned by
+// the caller, and precomputes every descriptor table the kernels read
+// (batched-GEMM tasks and tile maps, Lanczos jobs, Newton jobs, elementwise
+// row runs).  The per-call work is: refresh the gradient/weight pointer table
+// when it changed, then enqueue the kernels on the caller's stream.
+#include "../../include/shampoo.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace shampoo;
+
+namespace {
+
+constexpr int kTile = 128;            // batched-GEMM tile edge
+constexpr int kFactorPad = 32;        // factor matrices padded to a multiple of this
+constexpr int64_t kElemChunk = 16384; // elements per workgroup in elementwise kernels
+constexpr int kRingSlots = 16;        // pinned staging slots for per-call tables
+constexpr size_t kNewtonScratchBudget = size_t(4) << 30;  // bytes per precision
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+struct TensorPlan {
+    int64_t rows = 0, cols = 0;
+    int kind = 0;
+    int mode = 0;  // 0 Shampoo, 1 dense Adagrad, 2 sparse rows
+    int64_t off_a = -1, off_mom = -1, off_d = -1;  // bytes
+    int first_block = 0, n_blocks = 0, nbc = 0;
+};
+
+struct BlockPlan {
+    int tensor, r0, c0, mb, nb;
+    int fl, fr;
+    int64_t off_t;       // bytes: scratch T = G_b P_R (mb x nb)
+    int d_slot, d_tiles; // ||D||^2 partial slots
+    int a_slot, a_chunks;
+};
+
+struct FactorPlan {
+    int block, side, dim, ld;
+    int64_t off_s, off_p, off_p64;  // bytes (off_p64 = -1 when absent)
+};
+
+struct LaunchRef {
+    int64_t tasks_off = 0, tiles_off = 0;  // bytes
+    int ntiles = 0;
+};
+
+struct NewtonChunk {
+    int ld = 0;
+    int njobs = 0;
+    int64_t jobs_off = 0;                    // FactorJob table (bytes)
+    std::vector<LaunchRef> stages[2];        // per parity
+};
+
+// Host-side table builder: tables are appended to one blob that is copied
+// into the arena's table region at bind time.
+struct Blob {
+    std::vector<unsigned char> bytes;
+    template <typename T>
+    int64_t add(const std::vector<T>& v) {
+        const int64_t off = align_up((int64_t)bytes.size(), 256);
+        bytes.resize(off + v.size() * sizeof(T));
+        if (!v.empty()) std::memcpy(bytes.data() + off, v.data(), v.size() * sizeof(T));
+        return off;
+    }
+};
+
+}  // namespace
+
+struct shampoo_s {
+    shampoo_config cfg{};
+    int n = 0;
+    std::vector<TensorPlan> tensors;
+    std::vector<BlockPlan> blocks;
+    std::vector<FactorPlan> factors;
+    int n_sparse = 0;
+
+    // arena layout (bytes)
+    size_t total = 0;
+    int64_t off_bases = 0, off_sparse = 0, off_tables = 0, off_diag = 0, off_prec = 0;
+    int64_t off_scr32 = 0, off_scr64 = 0, off_partA = 0, off_partD = 0, off_scale = 0;
+    int n_partA = 0, n_partD = 0;
+    Blob blob;  // static tables (offsets relative to off_tables)
+
+    LaunchRef gram, apply1, apply2;
+    int64_t lanczos_s_off = 0, lanczos_p_off = 0, ident_jobs_off = 0;
+    int64_t blockchunks_off = 0, blocknorms_off = 0, rowchunks_off = 0;
+    int n_blockchunks = 0, n_rowchunks = 0;
+    std::vector<NewtonChunk> chunks32, chunks64;
+    std::vector<FactorDiag> diag_init;
+
+    // binding
+    unsigned char* arena = nullptr;
+    bool bound = false;
+    std::vector<uint64_t> bases_host;   // last uploaded pointer table
+    bool bases_valid = false;
+    unsigned char* ring = nullptr;      // pinned staging
+    size_t slot_bytes = 0;
+    hipEvent_t ring_ev[kRingSlots] = {};
+    bool ring_used[kRingSlots] = {};
+    int ring_next = 0;
+
+    ~shampoo_s() {
+        for (int i = 0; i < kRingSlots; ++i)
+            if (ring_ev[i]) (void)hipEventDestroy(ring_ev[i]);
+        if (ring) (void)hipHostFree(ring);
+    }
+};
+
+namespace {
+
+bool use_fp32(const shampoo_config& c) { return c.root_mode != SHAMPOO_ROOT_F64; }
+bool use_fp64(const shampoo_config& c) { return c.root_mode != SHAMPOO_ROOT_F32; }
+
+int newton_stage_count(int p) {  // GEMM launches per iteration
+    if (p == 1) return 1;
+    int s = 1;                     // X T and T^2
+    for (int q = 2; q < p; q *= 2) ++s;  // further squarings
+    return s + 1;                  // M <- T^p M
+}
+
+// Builds the per-parity GEMM launches of one Newton chunk.
+void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& fids, int ld,
+                        bool fp64, int64_t scratch_off_bytes) {
+    const int p = h->cfg.root_p;
+    const int64_t esz = fp64 ? 8 : 4;
+    const int64_t mat = (int64_t)ld * ld;
+    const int64_t sbase = scratch_off_bytes / esz;  // scratch start in elements (arena base 0)
+    const int tiles1 = ceil_div(ld, kTile);
+    const int tpt = tiles1 * tiles1;
+    ch.ld = ld;
+    ch.njobs = (int)fids.size();
+    std::vector<FactorJob> jobs;
+    for (size_t s = 0; s < fids.size(); ++s) {
+        const FactorPlan& f = h->factors[fids[s]];
+        FactorJob j{};
+        j.s_off = f.off_s / 8;
+        j.p_off = f.off_p / 4;
+        j.p64_off = f.off_p64 >= 0 ? f.off_p64 / 8 : -1;
+        j.x_off = (int64_t)s * 6 * mat;      // relative to the scratch pointer
+        j.m_off = j.x_off + 2 * mat;
+        j.n = f.dim;
+        j.ld = ld;
+        j.factor = fids[s];
+        jobs.push_back(j);
+    }
+    ch.jobs_off = h->blob.add(jobs);
+
+    auto mk = [&](int64_t a, int64_t b, int64_t c, int trans, int fid) {
+        GemmTask t{};
+        t.a_off = sbase + a; t.b_off = sbase + b; t.c_off = sbase + c;
+        t.a_base = t.b_base = t.c_base = 0;
+        t.M = t.N = t.K = ld;
+        t.lda = t.ldb = t.ldc = ld;
+        t.trans = trans;
+        t.tiles_n = tiles1;
+        t.factor = fid;
+        t.norm_slot = -1;
+        return t;
+    };
+    for (int q = 0; q < 2; ++q) {
+        std::vector<std::vector<GemmTask>> st(newton_stage_count(p));
+        for (size_t s = 0; s < fids.size(); ++s) {
+            const int64_t b = (int64_t)s * 6 * mat;
+            const int64_t Xq = b + q * mat, Xn = b + (1 - q) * mat;
+            const int64_t Mq = b + (2 + q) * mat, Mn = b + (3 - q) * mat;
+            const int64_t T2 = b + 4 * mat, T4 = b + 5 * mat;
+            const int fid = fids[s];
+            // stage 0: X <- X T(M) and T(M)^2 (p = 1: M <- T(M) M)
+            st[0].push_back(mk(Xq, Mq, Xn, 8, fid));
+            if (p == 1) {
+                st[0].push_back(mk(Mq, Mq, Mn, 4, fid));
+                continue;
+            }
+            st[0].push_back(mk(Mq, Mq, T2, 4 | 8, fid));
+            int k = 1;
+            int64_t cur = T2;
+            for (int e = 2; e < p; e *= 2) {
+                const int64_t nxt = (cur == T2) ? T4 : T2;
+                st[k++].push_back(mk(cur, cur, nxt, 0, fid));
+                cur = nxt;
+            }
+            st[k].push_back(mk(cur, Mq, Mn, 0, fid));
+        }
+        for (auto& tasks : st) {
+            std::vector<TileRef> tiles;
+            for (size_t i = 0; i < tasks.size(); ++i)
+                for (int t = 0; t < tpt; ++t) tiles.push_back({(int32_t)i, t});
+            LaunchRef L;
+            L.tasks_off = h->blob.add(tasks);
+            L.tiles_off = h->blob.add(tiles);
+            L.ntiles = (int)tiles.size();
+            ch.stages[q].push_back(L);
+        }
+    }
+}
+
+LaunchRef add_launch(Blob& blob, const std::vector<GemmTask>& tasks) {
+    std::vector<TileRef> tiles;
+    for (size_t i = 0; i < tasks.size(); ++i) {
+        const int nt = ceil_div(tasks[i].M, kTile) * tasks[i].tiles_n;
+        for (int t = 0; t < nt; ++t) tiles.push_back({(int32_t)i, t});
+    }
+    LaunchRef L;
+    L.tasks_off = blob.add(tasks);
+    L.tiles_off = blob.add(tiles);
+    L.ntiles = (int)tiles.size();
+    return L;
+}
+
+int build_plan(shampoo_s* h) {
+    const shampoo_config& c = h->cfg;
+    const int b = c.block_size;
+    int64_t off = 0;
+    auto take = [&](int64_t bytes) {
+        const int64_t o = align_up(off, 256);
+        off = o + std::max<int64_t>(bytes, 0);
+        return o;
+    };
+
+    // tensors and blocks
+    for (int t = 0; t < h->n; ++t) {
+        TensorPlan& tp = h->tensors[t];
+        if (tp.kind == SHAMPOO_SPARSE_ROWS) {
+            tp.mode = 2;
+            h->n_sparse++;
+            continue;
+        }
+        const bool shampoo = c.max_precond_dim <= 0 ||
+                             (tp.rows <= c.max_precond_dim && tp.cols <= c.max_precond_dim);
+        tp.mode = shampoo ? 0 : 1;
+        if (!shampoo) continue;
+        tp.first_block = (int)h->blocks.size();
+        tp.nbc = ceil_div(tp.cols, b);
+        for (int64_t r0 = 0; r0 < tp.rows; r0 += b)
+            for (int64_t c0 = 0; c0 < tp.cols; c0 += b) {
+                BlockPlan bp{};
+                bp.tensor = t;
+                bp.r0 = (int)r0;
+                bp.c0 = (int)c0;
+                bp.mb = (int)std::min<int64_t>(b, tp.rows - r0);
+                bp.nb = (int)std::min<int64_t>(b, tp.cols - c0);
+                bp.fl = 2 * (int)h->blocks.size();
+                bp.fr = bp.fl + 1;
+                h->blocks.push_back(bp);
+            }
+        tp.n_blocks = (int)h->blocks.size() - tp.first_block;
+    }
+    for (size_t i = 0; i < h->blocks.size(); ++i) {
+        const BlockPlan& bp = h->blocks[i];
+        for (int side = 0; side < 2; ++side) {
+            FactorPlan f{};
+            f.block = (int)i;
+            f.side = side;
+            f.dim = side == 0 ? bp.mb : bp.nb;
+            f.ld = (int)align_up(f.dim, kFactorPad);
+            f.off_p64 = -1;
+            h->factors.push_back(f);
+        }
+    }
+    const int nf = (int)h->factors.size();
+    const int nb = (int)h->blocks.size();
+
+    // arena: per-call tables, diagnostics, factor matrices
+    h->off_bases = take((1 + 2 * (int64_t)h->n) * 8);
+    h->off_sparse = take((int64_t)std::max(h->n_sparse, 1) * sizeof(SparseJob));
+    h->off_diag = take((int64_t)std::max(nf, 1) * sizeof(FactorDiag));
+    h->off_prec = take((int64_t)std::max(nf, 1) * 4);
+    for (auto& f : h->factors) f.off_s = take((int64_t)f.ld * f.ld * 8);  // fp64 statistics
+    for (auto& f : h->factors) f.off_p = take((int64_t)f.ld * f.ld * 4);
+    if (use_fp64(c))
+        for (auto& f : h->factors) f.off_p64 = take((int64_t)f.ld * f.ld * 8);
+
+    // tensors: accumulators, momentum, preconditioned gradient
+    for (auto& tp : h->tensors) {
+        const int64_t numel = tp.rows * tp.cols;
+        tp.off_a = take(numel * 4);
+        if (tp.mode != 2) tp.off_mom = take(numel * 4);
+        if (tp.mode == 0) tp.off_d = take(numel * 4);
+    }
+    for (auto& bp : h->blocks) bp.off_t = take((int64_t)bp.mb * bp.nb * 4);
+
+    // norm partial slots
+    int na = 0, nd = 0;
+    for (auto& bp : h->blocks) {
+        const int rows_per = (int)std::max<int64_t>(1, kElemChunk / bp.nb);
+        bp.a_slot = na;
+        bp.a_chunks = ceil_div(bp.mb, rows_per);
+        na += bp.a_chunks;
+        bp.d_slot = nd;
+        bp.d_tiles = ceil_div(bp.mb, kTile) * ceil_div(bp.nb, kTile);
+        nd += bp.d_tiles;
+    }
+    h->n_partA = na;
+    h->n_partD = nd;
+    h->off_partA = take((int64_t)std::max(na, 1) * 8);
+    h->off_partD = take((int64_t)std::max(nd, 1) * 8);
+    h->off_scale = take((int64_t)std::max(nb, 1) * 4);
+
+    // Newton root classes (by padded dimension) and scratch chunks
+    std::vector<int> lds;
+    for (auto& f : h->factors) lds.push_back(f.ld);
+    std::sort(lds.begin(), lds.end());
+    lds.erase(std::unique(lds.begin(), lds.end()), lds.end());
+    int64_t scr32 = 0, scr64 = 0;
+    struct Pending { int ld; std::vector<int> fids; bool fp64; };
+    std::vector<Pending> pend;
+    for (int ld : lds) {
+        std::vector<int> fids;
+        for (int i = 0; i < nf; ++i)
+            if (h->factors[i].ld == ld) fids.push_back(i);
+        for (int prec = 0; prec < 2; ++prec) {
+            const bool fp64 = prec == 1;
+            if ((fp64 && !use_fp64(c)) || (!fp64 && !use_fp32(c))) continue;
+            const int64_t per = 6 * (int64_t)ld * ld * (fp64 ? 8 : 4);
+            const int cap = (int)std::max<int64_t>(1, (int64_t)kNewtonScratchBudget / per);
+            for (size_t s = 0; s < fids.size(); s += cap) {
+                Pending pd;
+                pd.ld = ld;
+                pd.fp64 = fp64;
+                pd.fids.assign(fids.begin() + s, fids.begin() + std::min(fids.size(), s + cap));
+                int64_t& scr = fp64 ? scr64 : scr32;
+                scr = std::max(scr, per * (int64_t)pd.fids.size());
+                pend.push_back(std::move(pd));
+            }
+        }
+    }
+    h->off_scr32 = take(scr32);
+    h->off_scr64 = take(scr64);
+    h->off_tables = align_up(off, 256);
+
+    // ---- static tables
+    Blob& blob = h->blob;
+    // statistics: L = beta2 L + w G G^T, R = beta2 R + w G^T G (cue 10)
+    {
+        std::vector<GemmTask> tasks;
+        for (auto& bp : h->blocks) {
+            const TensorPlan& tp = h->tensors[bp.tensor];
+            const FactorPlan& fl = h->factors[bp.fl];
+            const FactorPlan& fr = h->factors[bp.fr];
+            GemmTask t{};
+            t.a_base = t.b_base = 1 + bp.tensor;
+            t.a_off = t.b_off = (int64_t)bp.r0 * tp.cols + bp.c0;
+            t.lda = t.ldb = (int)tp.cols;
+            t.c_base = 0;
+            t.factor = -1;
+            t.norm_slot = -1;
+            // L: op(A) = G_b (mb x nb), op(B) = G_b^T
+            t.c_off = fl.off_s / 8;
+            t.ldc = fl.ld;
+            t.M = t.N = bp.mb;
+            t.K = bp.nb;
+            t.trans = 2;
+            t.tiles_n = ceil_div(t.N, kTile);
+            tasks.push_back(t);
+            // R: op(A) = G_b^T (nb x mb), op(B) = G_b
+            t.c_off = fr.off_s / 8;
+            t.ldc = fr.ld;
+            t.M = t.N = bp.nb;
+            t.K = bp.mb;
+            t.trans = 1;
+            t.tiles_n = ceil_div(t.N, kTile);
+            tasks.push_back(t);
+        }
+        h->gram = add_launch(blob, tasks);
+    }
+    // apply: T = G_b P_R, then D = P_L T with ||D||^2 partials (cue 10)
+    {
+        std::vector<GemmTask> t1, t2;
+        for (auto& bp : h->blocks) {
+            const TensorPlan& tp = h->tensors[bp.tensor];
+            const FactorPlan& fl = h->factors[bp.fl];
+            const FactorPlan& fr = h->factors[bp.fr];
+            GemmTask t{};
+            t.a_base = 1 + bp.tensor;
+            t.a_off = (int64_t)bp.r0 * tp.cols + bp.c0;
+            t.lda = (int)tp.cols;
+            t.b_base = 0;
+            t.b_off = fr.off_p / 4;
+            t.ldb = fr.ld;
+            t.c_base = 0;
+            t.c_off = bp.off_t / 4;
+            t.ldc = bp.nb;
+            t.M = bp.mb; t.N = bp.nb; t.K = bp.nb;
+            t.trans = 0;
+            t.tiles_n = ceil_div(t.N, kTile);
+            t.factor = -1;
+            t.norm_slot = -1;
+            t1.push_back(t);
+            GemmTask u{};
+            u.a_base = 0; u.a_off = fl.off_p / 4; u.lda = fl.ld;
+            u.b_base = 0; u.b_off = bp.off_t / 4; u.ldb = bp.nb;
+            u.c_base = 0; u.c_off = tp.off_d / 4 + (int64_t)bp.r0 * tp.cols + bp.c0;
+            u.ldc = (int)tp.cols;
+            u.M = bp.mb; u.N = bp.nb; u.K = bp.mb;
+            u.trans = 0;
+            u.tiles_n = ceil_div(u.N, kTile);
+            u.factor = -1;
+            u.norm_slot = bp.d_slot;
+            t2.push_back(u);
+        }
+        h->apply1 = add_launch(blob, t1);
+        h->apply2 = add_launch(blob, t2);
+    }
+    // Lanczos jobs on statistics and on roots; identity jobs
+    {
+        std::vector<LanczosJob> js, jp;
+        std::vector<FactorJob> ident;
+        for (int i = 0; i < nf; ++i) {
+            const FactorPlan& f = h->factors[i];
+            js.push_back({f.off_s / 8, f.dim, f.ld, i, 0});
+            jp.push_back({f.off_p / 4, f.dim, f.ld, i, 0});
+            FactorJob j{};
+            j.p_off = f.off_p / 4;
+            j.p64_off = f.off_p64 >= 0 ? f.off_p64 / 8 : -1;
+            j.n = f.dim;
+            j.ld = f.ld;
+            j.factor = i;
+            ident.push_back(j);
+            FactorDiag d{};
+            d.block = f.block;
+            d.side = f.side;
+            d.dim = f.dim;
+            h->diag_init.push_back(d);
+        }
+        h->lanczos_s_off = blob.add(js);
+        h->lanczos_p_off = blob.add(jp);
+        h->ident_jobs_off = blob.add(ident);
+    }
+    for (auto& pd : pend) {
+        NewtonChunk ch;
+        build_newton_chunk(h, ch, pd.fids, pd.ld, pd.fp64, pd.fp64 ? h->off_scr64 : h->off_scr32);
+        (pd.fp64 ? h->chunks64 : h->chunks32).push_back(std::move(ch));
+    }
+    // elementwise tables
+    {
+        std::vector<BlockChunk> bcs;
+        std::vector<BlockNorms> bns;
+        for (size_t i = 0; i < h->blocks.size(); ++i) {
+            const BlockPlan& bp = h->blocks[i];
+            const TensorPlan& tp = h->tensors[bp.tensor];
+            const int rows_per = (int)std::max<int64_t>(1, kElemChunk / bp.nb);
+            for (int k = 0; k < bp.a_chunks; ++k) {
+                BlockChunk q{};
+                q.tensor = bp.tensor;
+                q.block = (int)i;
+                q.row0 = bp.r0 + k * rows_per;
+                q.nrows = std::min(rows_per, bp.mb - k * rows_per);
+                q.col0 = bp.c0;
+                q.ncols = bp.nb;
+                q.cols = (int)tp.cols;
+                q.slot = bp.a_slot + k;
+                q.a_off = tp.off_a / 4;
+                bcs.push_back(q);
+            }
+            bns.push_back({bp.a_slot, bp.a_chunks, bp.d_slot, bp.d_tiles});
+        }
+        h->n_blockchunks = (int)bcs.size();
+        h->blockchunks_off = blob.add(bcs);
+        h->blocknorms_off = blob.add(bns);
+        std::vector<RowChunk> rcs;
+        for (int t = 0; t < h->n; ++t) {
+            const TensorPlan& tp = h->tensors[t];
+            if (tp.mode == 2) continue;
+            const int rows_per = (int)std::max<int64_t>(1, kElemChunk / tp.cols);
+            for (int64_t r0 = 0; r0 < tp.rows; r0 += rows_per) {
+                RowChunk q{};
+                q.tensor = t;
+                q.mode = tp.mode;
+                q.row0 = (int)r0;
+                q.nrows = (int)std::min<int64_t>(rows_per, tp.rows - r0);
+                q.cols = (int)tp.cols;
+                q.block_size = b;
+                q.first_block = tp.first_block;
+                q.nbc = tp.nbc;
+                q.a_off = tp.off_a / 4;
+                q.m_off = tp.off_mom / 4;
+                q.d_off = tp.mode == 0 ? tp.off_d / 4 : 0;
+                rcs.push_back(q);
+            }
+        }
+        h->n_rowchunks = (int)rcs.size();
+        h->rowchunks_off = blob.add(rcs);
+    }
+    h->total = (size_t)align_up(h->off_tables + (int64_t)blob.bytes.size(), 256);
+    return SHAMPOO_OK;
+}
+
+int hip_err(hipError_t e) { return e == hipSuccess ? SHAMPOO_OK : SHAMPOO_E_HIP; }
+
+template <typename T>
+T* at(shampoo_s* h, int64_t off_bytes) {
+    return reinterpret_cast<T*>(h->arena + off_bytes);
+}
+template <typename T>
+T* tab(shampoo_s* h, int64_t blob_off) {
+    return reinterpret_cast<T*>(h->arena + h->off_tables + blob_off);
+}
+
+// Copies `bytes` of host data to the arena at `dst_off` through a pinned
+// staging slot (so the call stays asynchronous).
+int stage_upload(shampoo_s* h, const void* src, size_t bytes, int64_t dst_off, hipStream_t s) {
+    if (bytes == 0) return SHAMPOO_OK;
+    if (bytes > h->slot_bytes) return SHAMPOO_E_ARG;
+    const int k = h->ring_next;
+    h->ring_next = (k + 1) % kRingSlots;
+    if (h->ring_used[k]) {
+        hipError_t e = hipEventSynchronize(h->ring_ev[k]);
+        if (e != hipSuccess) return SHAMPOO_E_HIP;
+    }
+    unsigned char* slot = h->ring + (size_t)k * h->slot_bytes;
+    std::memcpy(slot, src, bytes);
+    hipError_t e = hipMemcpyAsync(h->arena + dst_off, slot, bytes, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return SHAMPOO_E_HIP;
+    e = hipEventRecord(h->ring_ev[k], s);
+    if (e != hipSuccess) return SHAMPOO_E_HIP;
+    h->ring_used[k] = true;
+    return SHAMPOO_OK;
+}
+
+int refresh_bases(shampoo_s* h, const float* const* grads, float* const* params, hipStream_t s) {
+    std::vector<uint64_t> nb = h->bases_host;
+    if (nb.empty()) nb.assign(1 + 2 * (size_t)h->n, 0);
+    nb[0] = reinterpret_cast<uint64_t>(h->arena);
+    for (int t = 0; t < h->n; ++t) {
+        if (grads) nb[1 + t] = reinterpret_cast<uint64_t>(grads[t]);
+        if (params) nb[1 + h->n + t] = reinterpret_cast<uint64_t>(params[t]);
+    }
+    if (h->bases_valid && nb == h->bases_host) return SHAMPOO_OK;
+    const int rc = stage_upload(h, nb.data(), nb.size() * 8, h->off_bases, s);
+    if (rc != SHAMPOO_OK) return rc;
+    h->bases_host = nb;
+    h->bases_valid = true;
+    return SHAMPOO_OK;
+}
+
+}  // namespace
+
+// =================================================================== C-ABI
+extern "C" {
+
+int shampoo_create(const shampoo_config* cfg, int32_t n_tensors, const shampoo_tensor_desc* tensors,
+                   shampoo_t** out) {
+    if (!cfg || !tensors || !out || n_tensors < 1) return SHAMPOO_E_ARG;
+    *out = nullptr;
+    const shampoo_config& c = *cfg;
+    if (c.block_size < 1 || c.newton_iters < 1 || c.max_precond_dim < 0 || c.lanczos_steps < 0)
+        return SHAMPOO_E_ARG;
+    if (!(c.beta2 > 0.0 && c.beta2 <= 1.0) || !(c.eps_rel >= 0.0) || !(c.graft_eps >= 0.0) ||
+        !std::isfinite(c.beta1) || !std::isfinite(c.lr) || c.reserved != 0)
+        return SHAMPOO_E_ARG;
+    if (c.root_mode < SHAMPOO_ROOT_F32 || c.root_mode > SHAMPOO_ROOT_AUTO) return SHAMPOO_E_ARG;
+    if (c.root_p != 1 && c.root_p != 2 && c.root_p != 4 && c.root_p != 8)
+        return SHAMPOO_E_UNSUPPORTED;
+    for (int t = 0; t < n_tensors; ++t) {
+        const shampoo_tensor_desc& d = tensors[t];
+        if (d.rows < 1 || d.cols < 1 || d.reserved != 0) return SHAMPOO_E_ARG;
+        if (d.kind != SHAMPOO_DENSE && d.kind != SHAMPOO_SPARSE_ROWS) return SHAMPOO_E_ARG;
+        if (d.rows > (int64_t)1 << 31 || d.cols > (int64_t)1 << 20) return SHAMPOO_E_UNSUPPORTED;
+    }
+    shampoo_s* h = new (std::nothrow) shampoo_s();
+    if (!h) return SHAMPOO_E_NOMEM;
+    try {
+        h->cfg = c;
+        if (h->cfg.lanczos_steps == 0) h->cfg.lanczos_steps = 32;
+        h->n = n_tensors;
+        h->tensors.resize(n_tensors);
+        for (int t = 0; t < n_tensors; ++t) {
+            h->tensors[t].rows = tensors[t].rows;
+            h->tensors[t].cols = tensors[t].cols;
+            h->tensors[t].kind = tensors[t].kind;
+        }
+        const int rc = build_plan(h);
+        if (rc != SHAMPOO_OK) {
+            delete h;
+            return rc;
+        }
+        // factor dimensions above the Lanczos limit are not supported
+        for (auto& f : h->factors)
+            if (f.dim > 1024) {
+                delete h;
+                return SHAMPOO_E_UNSUPPORTED;
+            }
+    } catch (const std::bad_alloc&) {
+        delete h;
+        return SHAMPOO_E_NOMEM;
+    }
+    *out = h;
+    return SHAMPOO_OK;
+}
+
+int shampoo_state_bytes(const shampoo_t* h, size_t* bytes) {
+    if (!h || !bytes) return SHAMPOO_E_ARG;
+    *bytes = h->total;
+    return SHAMPOO_OK;
+}
+
+int shampoo_num_factors(const shampoo_t* h, int32_t* n_factors, int32_t* n_blocks) {
+    if (!h) return SHAMPOO_E_ARG;
+    if (n_factors) *n_factors = (int32_t)h->factors.size();
+    if (n_blocks) *n_blocks = (int32_t)h->blocks.size();
+    return SHAMPOO_OK;
+}
+
+int shampoo_block_info(const shampoo_t* h, int32_t block, shampoo_block_layout* out) {
+    if (!h || !out || block < 0 || block >= (int32_t)h->blocks.size()) return SHAMPOO_E_ARG;
+    const BlockPlan& bp = h->blocks[block];
+    const FactorPlan& fl = h->factors[bp.fl];
+    const FactorPlan& fr = h->factors[bp.fr];
+    out->tensor = bp.tensor;
+    out->row0 = bp.r0;
+    out->col0 = bp.c0;
+    out->rows = bp.mb;
+    out->cols = bp.nb;
+    out->ld_l = fl.ld;
+    out->ld_r = fr.ld;
+    out->factor_l = bp.fl;
+    out->factor_r = bp.fr;
+    out->off_l = fl.off_s;
+    out->off_r = fr.off_s;
+    out->off_pl = fl.off_p;
+    out->off_pr = fr.off_p;
+    out->off_pl64 = fl.off_p64;
+    out->off_pr64 = fr.off_p64;
+    return SHAMPOO_OK;
+}
+
+int shampoo_tensor_info(const shampoo_t* h, int32_t tensor, int64_t* adagrad_off, int64_t* mom_off,
+                        int32_t* first_block, int32_t* n_blocks) {
+    if (!h || tensor < 0 || tensor >= h->n) return SHAMPOO_E_ARG;
+    const TensorPlan& tp = h->tensors[tensor];
+    if (adagrad_off) *adagrad_off = tp.off_a;
+    if (mom_off) *mom_off = tp.off_mom;
+    if (first_block) *first_block = tp.first_block;
+    if (n_blocks) *n_blocks = tp.n_blocks;
+    return SHAMPOO_OK;
+}
+
+int shampoo_bind_state(shampoo_t* h, void* dev_state, size_t bytes, void* stream) {
+    if (!h || !dev_state) return SHAMPOO_E_ARG;
+    if ((reinterpret_cast<uintptr_t>(dev_state) & 255) != 0) return SHAMPOO_E_ARG;
+    if (bytes < h->total) return SHAMPOO_E_STATE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    h->arena = static_cast<unsigned char*>(dev_state);
+    h->bound = false;
+    h->bases_valid = false;
+    h->bases_host.clear();
+    if (!h->ring) {
+        h->slot_bytes = (size_t)align_up(std::max<int64_t>((1 + 2 * (int64_t)h->n) * 8,
+                                                           (int64_t)std::max(h->n_sparse, 1) *
+                                                               sizeof(SparseJob)),
+                                         256);
+        if (hipHostMalloc(reinterpret_cast<void**>(&h->ring), h->slot_bytes * kRingSlots,
+                          hipHostMallocDefault) != hipSuccess) {
+            h->ring = nullptr;
+            return SHAMPOO_E_HIP;
+        }
+        for (int i = 0; i < kRingSlots; ++i)
+            if (hipEventCreateWithFlags(&h->ring_ev[i], hipEventDisableTiming) != hipSuccess)
+                return SHAMPOO_E_HIP;
+    }
+    for (int i = 0; i < kRingSlots; ++i) h->ring_used[i] = false;
+    int rc = hip_err(hipMemsetAsync(h->arena, 0, h->off_tables, s));
+    if (rc) return rc;
+    rc = hip_err(hipMemcpyAsync(h->arena + h->off_tables, h->blob.bytes.data(), h->blob.bytes.size(),
+                                hipMemcpyHostToDevice, s));
+    if (rc) return rc;
+    if (!h->diag_init.empty()) {
+        rc = hip_err(hipMemcpyAsync(h->arena + h->off_diag, h->diag_init.data(),
+                                    h->diag_init.size() * sizeof(FactorDiag), hipMemcpyHostToDevice,
+                                    s));
+        if (rc) return rc;
+    }
+    rc = hip_err(launch_set_identity(tab<FactorJob>(h, h->ident_jobs_off), (int)h->factors.size(),
+                                     at<float>(h, 0), s));
+    if (rc) return rc;
+    rc = refresh_bases(h, nullptr, nullptr, s);  // base 0 (the state buffer) for every kernel
+    if (rc) return rc;
+    rc = hip_err(hipStreamSynchronize(s));
+    if (rc) return rc;
+    h->bound = true;
+    return SHAMPOO_OK;
+}
+
+int shampoo_update_stats(shampoo_t* h, const float* const* grads, void* stream) {
+    if (!h || !grads) return SHAMPOO_E_ARG;
+    if (!h->bound) return SHAMPOO_E_STATE;
+    for (auto& bp : h->blocks)
+        if (!grads[bp.tensor]) return SHAMPOO_E_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int rc = refresh_bases(h, grads, nullptr, s);
+    if (rc) return rc;
+    const double b2 = h->cfg.beta2;
+    GemmArgs a{};
+    a.epi = EPI_AXPBY;
+    a.alpha = b2 < 1.0 ? 1.0 - b2 : 1.0;
+    a.beta = b2;
+    // fp32 gradients, fp64 products and statistics (exact products; the
+    // statistics keep the near-null spectrum that fp32 storage would round
+    // into the eps damping)
+    return hip_err(launch_gemm_f64_from_f32(tab<GemmTask>(h, h->gram.tasks_off),
+                                            tab<TileRef>(h, h->gram.tiles_off), h->gram.ntiles,
+                                            at<uint64_t>(h, h->off_bases), a, s));
+}
+
+namespace {
+int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const int32_t* gate,
+               int gate_val, hipStream_t s) {
+    const int p = h->cfg.root_p;
+    NewtonArgs na{};
+    na.p = p;
+    na.is_fp64 = fp64 ? 1 : 0;
+    na.gate = gate;
+    na.gate_val = gate_val;
+    void* scratch = h->arena + (fp64 ? h->off_scr64 : h->off_scr32);
+    FactorDiag* diag = at<FactorDiag>(h, h->off_diag);
+    GemmArgs g{};
+    g.epi = EPI_STORE;
+    g.alpha = 1.0;
+    g.beta = 0.0;
+    g.xc1 = (double)(p + 1) / p;
+    g.xc2 = -1.0 / p;
+    g.gate = gate;
+    g.gate_val = gate_val;
+    const uint64_t* bases = at<uint64_t>(h, h->off_bases);
+    for (auto& ch : chunks) {
+        const FactorJob* jobs = tab<FactorJob>(h, ch.jobs_off);
+        int rc = hip_err(launch_newton_init(fp64, jobs, ch.njobs, at<double>(h, 0), scratch, diag, na, s));
+        if (rc) return rc;
+        for (int it = 0; it < h->cfg.newton_iters; ++it) {
+            for (const LaunchRef& L : ch.stages[it & 1]) {
+                const GemmTask* tk = tab<GemmTask>(h, L.tasks_off);
+                const TileRef* tl = tab<TileRef>(h, L.tiles_off);
+                rc = hip_err(fp64 ? launch_gemm_f64(tk, tl, L.ntiles, bases, g, s)
+                                  : launch_gemm_f32(tk, tl, L.ntiles, bases, g, s));
+                if (rc) return rc;
+            }
+        }
+        // the final X, M sit in buffer (iters % 2) of each slot
+        rc = hip_err(launch_newton_commit(fp64, jobs, ch.njobs, at<float>(h, 0),
+                                          static_cast<unsigned char*>(scratch) +
+                                              (size_t)(h->cfg.newton_iters & 1) * ch.ld * ch.ld *
+                                                  (fp64 ? 8 : 4),
+                                          diag, na, s));
+        if (rc) return rc;
+    }
+    return SHAMPOO_OK;
+}
+}  // namespace
+
+int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
+    if (!h) return SHAMPOO_E_ARG;
+    if (!h->bound) return SHAMPOO_E_STATE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int nf = (int)h->factors.size();
+    if (nf == 0) return SHAMPOO_OK;
+    const shampoo_config& c = h->cfg;
+    FactorDiag* diag = at<FactorDiag>(h, h->off_diag);
+    int32_t* prec = at<int32_t>(h, h->off_prec);
+    LanczosArgs la{};
+    la.steps = c.lanczos_steps;
+    la.mode = 0;
+    la.p = c.root_p;
+    la.eps_rel = c.eps_rel;
+    la.threshold = c.fp64_cond_threshold;
+    la.diag = diag;
+    la.prec = prec;
+    la.route_all_fp64 = c.root_mode == SHAMPOO_ROOT_F64 ? 1 : 0;
+    int rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_s_off), nf, h->arena, true, la, s));
+    if (rc) return rc;
+    if (use_fp32(c)) {
+        rc = run_newton(h, h->chunks32, false, nullptr, 0, s);
+        if (rc) return rc;
+        LanczosArgs lp = la;
+        lp.mode = 1;
+        lp.auto_route = c.root_mode == SHAMPOO_ROOT_AUTO ? 1 : 0;
+        rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_p_off), nf, h->arena, false, lp, s));
+        if (rc) return rc;
+    }
+    if (use_fp64(c)) {
+        const bool gated = c.root_mode == SHAMPOO_ROOT_AUTO;
+        rc = run_newton(h, h->chunks64, true, gated ? prec : nullptr, 1, s);
+        if (rc) return rc;
+        if (!use_fp32(c)) {
+            LanczosArgs lp = la;
+            lp.mode = 1;
+            lp.auto_route = 0;
+            rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_p_off), nf, h->arena, false, lp, s));
+            if (rc) return rc;
+        }
+    }
+    return SHAMPOO_OK;
+}
+
+int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const float* const* grads,
+                                   const shampoo_sparse_rows* sparse, void* stream) {
+    if (!h || !params || !grads) return SHAMPOO_E_ARG;
+    if (!h->bound) return SHAMPOO_E_STATE;
+    for (int t = 0; t < h->n; ++t) {
+        if (!params[t]) return SHAMPOO_E_ARG;
+        if (h->tensors[t].mode != 2 && !grads[t]) return SHAMPOO_E_ARG;
+    }
+    if (h->n_sparse > 0 && !sparse) return SHAMPOO_E_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int rc = refresh_bases(h, grads, params, s);
+    if (rc) return rc;
+    const uint64_t* bases = at<uint64_t>(h, h->off_bases);
+    float* arena = at<float>(h, 0);
+    double* partA = at<double>(h, h->off_partA);
+    double* partD = at<double>(h, h->off_partD);
+    float* scale = at<float>(h, h->off_scale);
+    const shampoo_config& c = h->cfg;
+
+    rc = hip_err(launch_adagrad_norm(tab<BlockChunk>(h, h->blockchunks_off), h->n_blockchunks, bases,
+                                     arena, (float)c.graft_eps, partA, s));
+    if (rc) return rc;
+    GemmArgs g{};
+    g.epi = EPI_STORE;
+    g.alpha = 1.0;
+    g.norms = partD;
+    rc = hip_err(launch_gemm_f32(tab<GemmTask>(h, h->apply1.tasks_off),
+                                 tab<TileRef>(h, h->apply1.tiles_off), h->apply1.ntiles, bases, g, s));
+    if (rc) return rc;
+    rc = hip_err(launch_gemm_f32(tab<GemmTask>(h, h->apply2.tasks_off),
+                                 tab<TileRef>(h, h->apply2.tiles_off), h->apply2.ntiles, bases, g, s));
+    if (rc) return rc;
+    rc = hip_err(launch_block_scale(tab<BlockNorms>(h, h->blocknorms_off), (int)h->blocks.size(), partA,
+                                    partD, scale, s));
+    if (rc) return rc;
+    UpdateArgs ua{(float)c.beta1, (float)c.lr, (float)c.graft_eps};
+    rc = hip_err(launch_update(tab<RowChunk>(h, h->rowchunks_off), h->n_rowchunks, bases, h->n, arena,
+                               scale, ua, s));
+    if (rc) return rc;
+    if (h->n_sparse > 0) {
+        std::vector<SparseJob> jobs;
+        int64_t items = 0;
+        for (int t = 0; t < h->n; ++t) {
+            const TensorPlan& tp = h->tensors[t];
+            if (tp.mode != 2) continue;
+            const shampoo_sparse_rows& sr = sparse[t];
+            if (sr.n_rows < 0 || sr.n_rows > tp.rows) return SHAMPOO_E_ARG;
+            if (sr.n_rows == 0) continue;
+            if (!sr.rows || !sr.row_grads) return SHAMPOO_E_ARG;
+            SparseJob j{};
+            j.rows_ptr = reinterpret_cast<int64_t>(sr.rows);
+            j.grads_ptr = reinterpret_cast<int64_t>(sr.row_grads);
+            j.w_ptr = reinterpret_cast<int64_t>(params[t]);
+            j.a_off = tp.off_a / 4;
+            j.n_rows = sr.n_rows;
+            j.table_rows = tp.rows;
+            j.cols = (int)tp.cols;
+            j.vec = (tp.cols % 4 == 0) && ((reinterpret_cast<uintptr_t>(sr.row_grads) & 15) == 0) &&
+                    ((reinterpret_cast<uintptr_t>(params[t]) & 15) == 0);
+            j.first_item = items;
+            items += sr.n_rows * (j.vec ? tp.cols / 4 : tp.cols);
+            jobs.push_back(j);
+        }
+        if (!jobs.empty()) {
+            rc = stage_upload(h, jobs.data(), jobs.size() * sizeof(SparseJob), h->off_sparse, s);
+            if (rc) return rc;
+            rc = hip_err(launch_sparse_rows(at<SparseJob>(h, h->off_sparse), (int)jobs.size(), items,
+                                            arena, (float)c.lr, (float)c.graft_eps, s));
+            if (rc) return rc;
+        }
+    }
+    return SHAMPOO_OK;
+}
+
+int shampoo_get_diagnostics(shampoo_t* h, shampoo_factor_diag* out, int32_t cap, void* stream) {
+    if (!h || (!out && cap > 0) || cap < 0) return SHAMPOO_E_ARG;
+    if (!h->bound) return SHAMPOO_E_STATE;
+    static_assert(sizeof(shampoo_factor_diag) == sizeof(FactorDiag), "diag layout");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int n = std::min<int>(cap, (int)h->factors.size());
+    if (n > 0) {
+        int rc = hip_err(hipMemcpyAsync(out, h->arena + h->off_diag, (size_t)n * sizeof(FactorDiag),
+                                        hipMemcpyDeviceToHost, s));
+        if (rc) return rc;
+    }
+    return hip_err(hipStreamSynchronize(s));
+}
+
+void shampoo_destroy(shampoo_t* h) { delete h; }
+
+const char* shampoo_strerror(int status) {
+    switch (status) {
+        case SHAMPOO_OK: return "ok";
+        case SHAMPOO_E_ARG: return "invalid argument";
+        case SHAMPOO_E_STATE: return "state not bound or too small";
+        case SHAMPOO_E_HIP: return "HIP runtime or launch error";
+        case SHAMPOO_E_NOMEM: return "host allocation failed";
+        case SHAMPOO_E_UNSUPPORTED: return "unsupported configuration";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Descriptor structs shared by the host planner and the gfx950 kernels.
+//
+// All tables live in the caller's device state buffer ("arena").  A pointer
+// the kernels dereference is (base table entry) + (element offset): base 0 is
+// the arena itself, bases 1..n are the gradients of the n tensors of this
+// call, bases n+1..2n their weights.  The gradient/weight pointers change per
+// call and are refreshed by a small host-to-device copy; everything else is
+// built once by the planner.
+#pragma once
+#include <cstdint>
+
+namespace shampoo {
+
+constexpr int kMaxNewtonP = 8;
+
+// One C = op(A) * op(B) problem of the batched GEMM kernel (row-major
+// operands; op(X) = X or X^T).  The kernel covers it with 128x128 tiles.
+struct GemmTask {
+    int64_t a_off, b_off, c_off;  // element offsets from their bases
+    int32_t a_base, b_base, c_base;
+    int32_t M, N, K;              // op(A) is M x K, op(B) is K x N
+    int32_t lda, ldb, ldc;
+    int32_t trans;                // bit 0: op(A) = A^T, bit 1: op(B) = B^T
+    int32_t tiles_n;              // ceil(N / 128)
+    int32_t factor;               // gating factor id (-1: always run)
+    int32_t norm_slot;            // first slot of per-tile ||C||^2 partials, -1: none
+    int32_t pad_;
+};
+
+// A tile of the batched GEMM launch: which task and which 128x128 tile.
+struct TileRef {
+    int32_t task;
+    int32_t tile;
+};
+
+// One symmetric matrix for the Lanczos kernel.
+struct LanczosJob {
+    int64_t off;      // element offset of the matrix in the arena (fp64 statistics or fp32 root)
+    int32_t n;        // real dimension
+    int32_t ld;       // leading dimension
+    int32_t factor;   // factor id (diagnostics record)
+    int32_t pad_;
+};
+
+// Per-factor job of the Newton init / commit kernels.
+struct FactorJob {
+    int64_t s_off;    // fp64 statistics (arena elements of 8 bytes)
+    int64_t p_off;    // fp32 root
+    int64_t p64_off;  // fp64 root (arena element offset in doubles), -1 none
+    int64_t x_off;    // scratch X (elements of the scratch type)
+    int64_t m_off;    // scratch M
+    int32_t n;        // real dimension
+    int32_t ld;       // padded dimension (leading dim of every matrix)
+    int32_t factor;
+    int32_t pad_;
+};
+
+// A run of rows of one dense tensor for the elementwise kernels.
+struct RowChunk {
+    int32_t tensor;       // tensor index (its gradient/weight base = 1 + tensor, 1 + n + tensor)
+    int32_t mode;         // 0: Shampoo (graft), 1: dense Adagrad
+    int32_t row0, nrows;
+    int32_t cols;
+    int32_t block_size;
+    int32_t first_block;  // Shampoo: first block of the tensor
+    int32_t nbc;          // Shampoo: blocks per block-row
+    int64_t a_off;        // Adagrad accumulator (arena element offset)
+    int64_t m_off;        // momentum
+    int64_t d_off;        // preconditioned gradient D (Shampoo only)
+};
+
+// A run of rows inside one Shampoo block for the Adagrad/||A||^2 kernel.
+struct BlockChunk {
+    int32_t tensor, block;
+    int32_t row0, nrows;  // rows within the tensor
+    int32_t col0, ncols;  // columns of the block
+    int32_t cols;         // tensor row length
+    int32_t slot;         // partial ||A||^2 slot
+    int64_t a_off;        // accumulator of the tensor
+};
+
+// Per-block reduction ranges for the graft scale.
+struct BlockNorms {
+    int32_t a_first, a_count;  // partial ||A_b||^2 slots
+    int32_t d_first, d_count;  // partial ||D_b||^2 slots
+};
+
+// One sparse table of one call.
+struct SparseJob {
+    int64_t rows_ptr;     // const int32_t*
+    int64_t grads_ptr;    // const float*
+    int64_t w_ptr;        // float*
+    int64_t a_off;        // accumulator (arena elements)
+    int64_t n_rows;
+    int64_t first_item;   // prefix over jobs of n_rows * (cols / 4 or cols)
+    int64_t table_rows;   // rows of the table (row ids outside [0, table_rows) are skipped)
+    int32_t cols;
+    int32_t vec;          // 1: float4 path
+};
+
+// Device-side copy of the public diagnostics record (same layout).
+struct FactorDiag {
+    double lambda_max, eps, kappa_est, residual;
+    int32_t block, side, dim, status;
+};
+
+}  // namespace shampoo

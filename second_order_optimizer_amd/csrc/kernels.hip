@@ -1,0 +1,849 @@
+// gfx950 kernels of the Shampoo step.
+//
+// Method: "Scalable Second Order Optimization for Deep Learning" (Anil et al.);
+// Shampoo-at-scale podcast transcript, cues 6-16: per-dimension statistics
+// L, R; their inverse fourth roots by coupled Newton iteration (fp64 where the
+// statistics are ill-conditioned); the two-sided preconditioned multiply;
+// Lemma-2 blocking.  Grafting, momentum and the Adagrad fallbacks are this
+// library's configuration (not on the pages).
+//
+// Kernels:
+//   k_gemm<T>        batched C = alpha op(A) op(B) (+ beta C), 128x128 tiles on
+//                    MFMA (fp32: v_mfma_f32_32x32x2f32, fp64:
+//                    v_mfma_f64_16x16x4f64), operands staged through LDS;
+//                    optional on-the-fly Newton operand T = c1 I + c2 M and
+//                    per-tile ||C||^2 partials.  Used for the statistics, the
+//                    two-sided apply and the batched coupled-Newton chain.
+//   k_lanczos        Krylov extreme-eigenvalue estimate per symmetric matrix.
+//   k_newton_init<T> / k_newton_commit<T>  start and finish of the batched
+//                    coupled-Newton iteration.
+//   k_adagrad_norm   a <- a + G*G on Shampoo blocks and ||A_b||^2 partials.
+//   k_block_scale    graft factor ||A_b|| / ||D_b|| per block.
+//   k_update         momentum and weight update (and dense Adagrad fallback).
+//   k_sparse_rows    sparse-row Adagrad for embedding tables.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace shampoo {
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ double wave_sum(double v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ double wave_max(double v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Fixed-order block reduction over 256 threads (deterministic).
+__device__ __forceinline__ double block_sum_256(double v, double* red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+}
+__device__ __forceinline__ double block_max_256(double v, double* red) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    return fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+}
+
+template <typename T>
+__device__ __forceinline__ T* base_ptr(const uint64_t* bases, int b, int64_t off) {
+    return reinterpret_cast<T*>(bases[b]) + off;
+}
+
+// ============================================================ batched GEMM
+template <typename T> struct GemmTraits;
+template <> struct GemmTraits<float> {
+    static constexpr int BK = 32;   // k per LDS stage
+    static constexpr int VEC = 4;   // elements per 16-byte global load
+    static constexpr int PADE = 4;  // LDS row padding (elements)
+};
+template <> struct GemmTraits<double> {
+    static constexpr int BK = 16;
+    static constexpr int VEC = 2;
+    static constexpr int PADE = 2;
+};
+
+constexpr int BM = 128, BN = 128;
+
+template <typename T> struct Vec16;
+template <> struct Vec16<float> { using type = float4; };
+template <> struct Vec16<double> { using type = double2; };
+
+// Loads one BK-deep stage of op(X) (rows [r0, r0+128) x k [k0, k0+BK)) into
+// registers, converting the stored type TI to the compute type T.  `kcontig`:
+// X is stored with k contiguous (X[r*ld + k]); otherwise r contiguous
+// (X[k*ld + r]).  Out-of-range elements are zero.  The optional transform
+// (Newton operand) maps the value v at op-index (r, k) to c2 v + c1 [r == k].
+template <typename T, typename TI>
+struct StageLoader {
+    static constexpr int BK = GemmTraits<T>::BK;
+    static constexpr int VEC = GemmTraits<T>::VEC;
+    typedef TI vec_t __attribute__((ext_vector_type(VEC)));
+    T v[4][VEC];
+
+    __device__ __forceinline__ void load(const TI* __restrict__ X, int ld, bool kcontig,
+                                         int r0, int k0, int R, int K, bool aligned,
+                                         bool xf, T c1, T c2) {
+        const int t = threadIdx.x;
+        if (kcontig) {
+            // 8 threads x VEC cover BK along k; 32 rows per pass, 4 passes.
+            const int kq = t & 7, rr = t >> 3;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int r = r0 + rr + 32 * p;
+                const int k = k0 + kq * VEC;
+                if (aligned && r < R && k + VEC <= K) {
+                    const vec_t q = *reinterpret_cast<const vec_t*>(X + (int64_t)r * ld + k);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) v[p][e] = T(q[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        v[p][e] = (r < R && k + e < K) ? T(X[(int64_t)r * ld + k + e]) : T(0);
+                }
+                if (xf) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        v[p][e] = c2 * v[p][e] + ((r == k + e && r < R && k + e < K) ? c1 : T(0));
+                }
+            }
+        } else {
+            // RQ threads x VEC cover 128 rows; KR k-rows per pass, 4 passes.
+            constexpr int RQ = BM / VEC;
+            constexpr int KR = 256 / RQ;
+            const int rq = t % RQ, kr = t / RQ;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int k = k0 + kr + KR * p;
+                const int r = r0 + rq * VEC;
+                if (aligned && k < K && r + VEC <= R) {
+                    const vec_t q = *reinterpret_cast<const vec_t*>(X + (int64_t)k * ld + r);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) v[p][e] = T(q[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        v[p][e] = (k < K && r + e < R) ? T(X[(int64_t)k * ld + r + e]) : T(0);
+                }
+                if (xf) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        v[p][e] = c2 * v[p][e] + ((r + e == k && k < K && r + e < R) ? c1 : T(0));
+                }
+            }
+        }
+    }
+
+    // LDS layout: S[k][r] with row pitch 128 + PADE (r contiguous).
+    __device__ __forceinline__ void store(T* S, bool kcontig) const {
+        constexpr int P = BM + GemmTraits<T>::PADE;
+        const int t = threadIdx.x;
+        if (kcontig) {
+            const int kq = t & 7, rr = t >> 3;
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) S[(kq * VEC + e) * P + rr + 32 * p] = v[p][e];
+        } else {
+            constexpr int RQ = BM / VEC;
+            constexpr int KR = 256 / RQ;
+            const int rq = t % RQ, kr = t / RQ;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                typename Vec16<T>::type q;
+                T* qs = reinterpret_cast<T*>(&q);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) qs[e] = v[p][e];
+                *reinterpret_cast<typename Vec16<T>::type*>(&S[(kr + KR * p) * P + rq * VEC]) = q;
+            }
+        }
+    }
+};
+
+// MFMA micro-kernels: each wave owns a 64x64 sub-tile of the 128x128 tile.
+template <typename T> struct WaveTile;
+
+template <> struct WaveTile<float> {
+    // 2x2 tiles of 32x32 (v_mfma_f32_32x32x2f32: A lane l = A[l%32][l/32],
+    // B lane l = B[l/32][l%32], C lane l reg v = C[8(v/4) + 4(l/32) + v%4][l%32]).
+    typedef float acc_t __attribute__((ext_vector_type(16)));
+    acc_t acc[2][2];
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    }
+    __device__ __forceinline__ void compute(const float* As, const float* Bs, int wm, int wn) {
+        constexpr int P = BM + GemmTraits<float>::PADE;
+        const int lane = threadIdx.x & 63;
+        const int h = lane >> 5, c = lane & 31;
+#pragma unroll
+        for (int kk = 0; kk < GemmTraits<float>::BK; kk += 2) {
+            float a[2], b[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) a[i] = As[(kk + h) * P + wm * 64 + i * 32 + c];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) b[j] = Bs[(kk + h) * P + wn * 64 + j * 32 + c];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    template <typename F>
+    __device__ __forceinline__ void for_each(int wm, int wn, F&& f) const {
+        const int lane = threadIdx.x & 63;
+        const int h = lane >> 5, c = lane & 31;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    f(wm * 64 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3), wn * 64 + j * 32 + c,
+                      acc[i][j][v]);
+    }
+};
+
+template <> struct WaveTile<double> {
+    // 4x4 tiles of 16x16 (v_mfma_f64_16x16x4f64: A lane l = A[l%16][l/16],
+    // B lane l = B[l/16][l%16], C lane l reg v = C[l/16 + 4v][l%16] -- note
+    // the row order differs from the fp32 16x16x4 form).
+    typedef double acc_t __attribute__((ext_vector_type(4)));
+    acc_t acc[4][4];
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0;
+    }
+    __device__ __forceinline__ void compute(const double* As, const double* Bs, int wm, int wn) {
+        constexpr int P = BM + GemmTraits<double>::PADE;
+        const int lane = threadIdx.x & 63;
+        const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+        for (int kk = 0; kk < GemmTraits<double>::BK; kk += 4) {
+            double a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[(kk + g) * P + wm * 64 + i * 16 + c];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[(kk + g) * P + wn * 64 + j * 16 + c];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    template <typename F>
+    __device__ __forceinline__ void for_each(int wm, int wn, F&& f) const {
+        const int lane = threadIdx.x & 63;
+        const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    f(wm * 64 + i * 16 + g + 4 * v, wn * 64 + j * 16 + c, acc[i][j][v]);
+    }
+};
+
+// C (type T) = alpha op(A) op(B) (+ beta C); A, B stored as TA, TB and
+// converted to T on the way into LDS (fp32 gradients into an fp64 product are
+// exact: fp32 x fp32 fits the fp64 mantissa).
+template <typename T, typename TA, typename TB>
+__global__ __launch_bounds__(256) void k_gemm(const GemmTask* __restrict__ tasks,
+                                             const TileRef* __restrict__ tiles,
+                                             const uint64_t* __restrict__ bases, GemmArgs args) {
+    constexpr int BK = GemmTraits<T>::BK;
+    constexpr int P = BM + GemmTraits<T>::PADE;
+    __shared__ __align__(16) T As[BK * P];
+    __shared__ __align__(16) T Bs[BK * P];
+    __shared__ double red[4];
+
+    const TileRef tr = tiles[blockIdx.x];
+    const GemmTask tk = tasks[tr.task];
+    if (args.gate && tk.factor >= 0 && args.gate[tk.factor] != args.gate_val) return;
+
+    const int ti = tr.tile / tk.tiles_n, tj = tr.tile % tk.tiles_n;
+    const int i0 = ti * BM, j0 = tj * BN;
+    const TA* A = base_ptr<TA>(bases, tk.a_base, tk.a_off);
+    const TB* B = base_ptr<TB>(bases, tk.b_base, tk.b_off);
+    T* C = base_ptr<T>(bases, tk.c_base, tk.c_off);
+    const bool ta = tk.trans & 1, tb = (tk.trans >> 1) & 1;
+    const bool xa = (tk.trans >> 2) & 1, xb = (tk.trans >> 3) & 1;
+    // op(A) = A: A[i][k] has k contiguous.  op(A) = A^T: A[k][i], i contiguous.
+    const bool a_kc = !ta;
+    // op(B)[k][j]: B^T stored B[j][k] -> k contiguous; B stored B[k][j] -> j contiguous.
+    const bool b_kc = tb;
+    constexpr int VEC = GemmTraits<T>::VEC;
+    const bool a_al = ((reinterpret_cast<uintptr_t>(A) % (VEC * sizeof(TA))) == 0) && (tk.lda % VEC == 0);
+    const bool b_al = ((reinterpret_cast<uintptr_t>(B) % (VEC * sizeof(TB))) == 0) && (tk.ldb % VEC == 0);
+    const T c1 = T(args.xc1), c2 = T(args.xc2);
+
+    const int w = threadIdx.x >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    WaveTile<T> wt;
+    wt.zero();
+
+    StageLoader<T, TA> la;
+    StageLoader<T, TB> lb;
+    la.load(A, tk.lda, a_kc, i0, 0, tk.M, tk.K, a_al, xa, c1, c2);
+    lb.load(B, tk.ldb, b_kc, j0, 0, tk.N, tk.K, b_al, xb, c1, c2);
+    for (int k0 = 0; k0 < tk.K; k0 += BK) {
+        __syncthreads();
+        la.store(As, a_kc);
+        lb.store(Bs, b_kc);
+        __syncthreads();
+        if (k0 + BK < tk.K) {
+            la.load(A, tk.lda, a_kc, i0, k0 + BK, tk.M, tk.K, a_al, xa, c1, c2);
+            lb.load(B, tk.ldb, b_kc, j0, k0 + BK, tk.N, tk.K, b_al, xb, c1, c2);
+        }
+        wt.compute(As, Bs, wm, wn);
+    }
+
+    const T alpha = T(args.alpha), beta = T(args.beta);
+    const bool axpby = args.epi == EPI_AXPBY;
+    double nrm = 0.0;
+    wt.for_each(wm, wn, [&](int r, int c, T v) {
+        const int i = i0 + r, j = j0 + c;
+        if (i < tk.M && j < tk.N) {
+            T* p = C + (int64_t)i * tk.ldc + j;
+            T o = alpha * v;
+            if (axpby) o += beta * (*p);
+            *p = o;
+            nrm += double(o) * double(o);
+        }
+    });
+    if (tk.norm_slot >= 0 && args.norms) {
+        const double s = block_sum_256(nrm, red);
+        if (threadIdx.x == 0) args.norms[tk.norm_slot + tr.tile] = s;
+    }
+}
+
+// ================================================================ Lanczos
+// Extreme Ritz values of a symmetric matrix from `steps` Lanczos steps (no
+// reorthogonalisation: lost orthogonality only duplicates converged extreme
+// values, it never moves the largest Ritz value above lambda_max).  Vectors
+// in fp64 in LDS; the matrix is read in fp32 column-wise (coalesced; the
+// matrix is symmetric so S v = S^T v).  The tridiagonal's extremes come from
+// Sturm-count bisection.
+constexpr int kLanczosMaxN = 1024;
+constexpr int kLanczosMaxSteps = 64;
+
+__device__ int sturm_count(const double* al, const double* be, int m, double x) {
+    int cnt = 0;
+    double d = 1.0;
+    for (int k = 0; k < m; ++k) {
+        const double b2 = k ? be[k - 1] * be[k - 1] : 0.0;
+        d = (al[k] - x) - (k ? b2 / d : 0.0);
+        if (d == 0.0) d = -1e-300;
+        if (d < 0) ++cnt;
+    }
+    return cnt;
+}
+
+template <typename TM>
+__global__ __launch_bounds__(256) void k_lanczos(const LanczosJob* __restrict__ jobs,
+                                                const TM* __restrict__ arena, LanczosArgs args) {
+    __shared__ double v0[kLanczosMaxN], v1[kLanczosMaxN], wv[kLanczosMaxN];
+    __shared__ double al[kLanczosMaxSteps], be[kLanczosMaxSteps];
+    __shared__ double red[4];
+    __shared__ int m_used;
+    const LanczosJob jb = jobs[blockIdx.x];
+    const int n = jb.n, ld = jb.ld;
+    const TM* S = arena + jb.off;
+    const int t = threadIdx.x;
+    const int steps = min(args.steps, min(n, kLanczosMaxSteps));
+
+    // deterministic start vector from an integer hash, normalised
+    double s2 = 0.0;
+    for (int i = t; i < n; i += 256) {
+        uint32_t hsh = (uint32_t)i * 2654435761u + 0x9E3779B9u;
+        hsh ^= hsh >> 15; hsh *= 2246822519u; hsh ^= hsh >> 13;
+        const double x = 0.5 + (double)(hsh & 0xFFFFFF) / 16777216.0;  // in [0.5, 1.5)
+        v1[i] = x;
+        v0[i] = 0.0;
+        s2 += x * x;
+    }
+    const double nv = sqrt(block_sum_256(s2, red));
+    for (int i = t; i < n; i += 256) v1[i] /= nv;
+    if (t == 0) m_used = steps;
+    __syncthreads();
+
+    double beta_prev = 0.0;
+    for (int k = 0; k < steps; ++k) {
+        // w = S v
+        for (int j = t; j < n; j += 256) {
+            double acc = 0.0;
+            for (int i = 0; i < n; ++i) acc += (double)S[(int64_t)i * ld + j] * v1[i];
+            wv[j] = acc;
+        }
+        __syncthreads();
+        double d = 0.0;
+        for (int i = t; i < n; i += 256) d += wv[i] * v1[i];
+        const double alpha = block_sum_256(d, red);
+        double q = 0.0;
+        for (int i = t; i < n; i += 256) {
+            const double x = wv[i] - alpha * v1[i] - beta_prev * v0[i];
+            wv[i] = x;
+            q += x * x;
+        }
+        const double beta = sqrt(block_sum_256(q, red));
+        if (t == 0) { al[k] = alpha; be[k] = beta; }
+        const bool stop = !(beta > 1e-13 * fabs(alpha)) || !isfinite(alpha) || !isfinite(beta);
+        if (stop) {
+            if (t == 0) m_used = k + 1;
+            __syncthreads();
+            break;
+        }
+        for (int i = t; i < n; i += 256) {
+            v0[i] = v1[i];
+            v1[i] = wv[i] / beta;
+        }
+        beta_prev = beta;
+        __syncthreads();
+    }
+    __syncthreads();
+    if (t != 0) return;
+    const int m = m_used;
+    bool finite = true;
+    double lo = 0.0, hi = 0.0;
+    for (int k = 0; k < m; ++k) {
+        const double r = (k ? fabs(be[k - 1]) : 0.0) + (k + 1 < m ? fabs(be[k]) : 0.0);
+        if (!isfinite(al[k]) || !isfinite(r)) finite = false;
+        lo = k ? fmin(lo, al[k] - r) : al[k] - r;
+        hi = k ? fmax(hi, al[k] + r) : al[k] + r;
+    }
+    double lmax = NAN;
+    if (finite) {
+        double a = lo, b = hi;
+        for (int it = 0; it < 200 && b - a > 1e-15 * fmax(fabs(a), fabs(b)); ++it) {
+            const double mid = 0.5 * (a + b);
+            if (sturm_count(al, be, m, mid) >= m) b = mid; else a = mid;
+        }
+        lmax = b;
+    }
+    FactorDiag& dg = args.diag[jb.factor];
+    if (args.mode == 0) {
+        // statistics: lambda_max -> eps; status bits for the Newton pass
+        int st = 0;
+        if (!finite) st |= SHAMPOO_FACTOR_NONFINITE_INPUT_;
+        else if (!(lmax > 0.0)) st |= SHAMPOO_FACTOR_ZERO_;
+        dg.lambda_max = lmax;
+        dg.eps = (st == 0) ? args.eps_rel * lmax : 0.0;
+        dg.status = st;
+        dg.kappa_est = 0.0;
+        dg.residual = 0.0;
+        if (args.prec) args.prec[jb.factor] = args.route_all_fp64 ? 1 : 0;
+    } else {
+        // root: lambda_max(P) = (lambda_min(S) + eps)^(-1/p) -> kappa estimate.
+        // A factor whose fp32 iteration went non-finite or did not converge is
+        // routed to fp64 as well.
+        const int bad_in = dg.status & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_ZERO_);
+        double kap = 0.0;
+        if (!bad_in && finite && lmax > 0.0) kap = (dg.lambda_max + dg.eps) * pow(lmax, (double)args.p);
+        dg.kappa_est = kap;
+        if (args.prec && args.auto_route) {
+            const bool weak = (dg.status & (SHAMPOO_FACTOR_NONFINITE_ROOT_ | SHAMPOO_FACTOR_RESIDUAL_HIGH_)) != 0;
+            args.prec[jb.factor] = (!bad_in && (kap > args.threshold || weak)) ? 1 : 0;
+        }
+    }
+}
+
+// ======================================================= coupled Newton
+// Coupled Newton iteration for the inverse p-th root (Guo & Higham, SIAM J.
+// Matrix Anal. Appl. 28(3), 2006).  With A = sym(S) + eps I and
+// z = (p+1) / (2 lambda_max(A)):  X_0 = z^(1/p) I, M_0 = z A; then
+// T = ((p+1) I - M)/p, X <- X T, M <- T^p M.  M_k = X_k^p A throughout, so
+// M -> I and X -> A^(-1/p).  Padded rows/columns carry M = I, X = I and stay
+// decoupled (block diagonal).
+template <typename T>
+__global__ __launch_bounds__(256) void k_newton_init(const FactorJob* __restrict__ jobs,
+                                                    const double* __restrict__ stats,
+                                                    T* __restrict__ scratch,
+                                                    const FactorDiag* __restrict__ diag,
+                                                    NewtonArgs args) {
+    const FactorJob jb = jobs[blockIdx.x];
+    if (args.gate && args.gate[jb.factor] != args.gate_val) return;
+    const FactorDiag dg = diag[jb.factor];
+    const int n = jb.n, ld = jb.ld;
+    const double* S = stats + jb.s_off;
+    T* X = scratch + jb.x_off;
+    T* M = scratch + jb.m_off;
+    const bool ok = dg.status == 0;
+    const double lam = dg.lambda_max + dg.eps;
+    const T z = ok ? T((args.p + 1) / (2.0 * lam)) : T(1);
+    const T zr = ok ? T(pow((args.p + 1) / (2.0 * lam), 1.0 / args.p)) : T(1);
+    const T e = T(dg.eps);
+    const int64_t nn = (int64_t)ld * ld;
+    for (int64_t idx = threadIdx.x; idx < nn; idx += 256) {
+        const int i = (int)(idx / ld), j = (int)(idx % ld);
+        T m, x;
+        if (i < n && j < n && ok) {
+            const T s = T(0.5 * (S[(int64_t)i * ld + j] + S[(int64_t)j * ld + i]));
+            m = z * (s + (i == j ? e : T(0)));
+            x = (i == j) ? zr : T(0);
+        } else {
+            m = (i == j) ? T(1) : T(0);
+            x = (i == j) ? T(1) : T(0);
+        }
+        M[idx] = m;
+        X[idx] = x;
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_newton_commit(const FactorJob* __restrict__ jobs,
+                                                      float* __restrict__ arena,
+                                                      const T* __restrict__ scratch,
+                                                      FactorDiag* __restrict__ diag,
+                                                      NewtonArgs args) {
+    __shared__ double red[4];
+    const FactorJob jb = jobs[blockIdx.x];
+    if (args.gate && args.gate[jb.factor] != args.gate_val) return;
+    const int n = jb.n, ld = jb.ld;
+    const T* X = scratch + jb.x_off;
+    const T* M = scratch + jb.m_off;
+    float* P = arena + jb.p_off;
+    double* P64 = jb.p64_off >= 0 ? reinterpret_cast<double*>(arena) + jb.p64_off : nullptr;
+    const int st0 = diag[jb.factor].status & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_ZERO_);
+    const int64_t nn = (int64_t)ld * ld;
+    double res = 0.0, bad = 0.0;
+    if (st0 == 0) {
+        for (int64_t idx = threadIdx.x; idx < nn; idx += 256) {
+            const int i = (int)(idx / ld), j = (int)(idx % ld);
+            if (i < n && j < n) {
+                const double x = double(X[idx]);
+                const double r = fabs(double(M[idx]) - (i == j ? 1.0 : 0.0));
+                if (!isfinite(x) || !isfinite(r)) bad = 1.0;
+                res = fmax(res, r);
+            }
+        }
+    }
+    res = block_max_256(res, red);
+    bad = block_max_256(bad, red);
+    int st = st0;
+    if (st0 == 0 && bad > 0.0) st |= SHAMPOO_FACTOR_NONFINITE_ROOT_;
+    const bool keep = (st & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_NONFINITE_ROOT_)) != 0;
+    if (!keep) {
+        const bool ident = (st & SHAMPOO_FACTOR_ZERO_) != 0;
+        for (int64_t idx = threadIdx.x; idx < nn; idx += 256) {
+            const int i = (int)(idx / ld), j = (int)(idx % ld);
+            double x;
+            if (ident || i >= n || j >= n) x = (i == j) ? 1.0 : 0.0;
+            else x = double(X[idx]);
+            P[idx] = float(x);
+            if (P64) P64[idx] = x;
+        }
+    }
+    if (threadIdx.x == 0) {
+        FactorDiag& dg = diag[jb.factor];
+        if (!keep && !(st & SHAMPOO_FACTOR_ZERO_) && res > 1e-2) st |= SHAMPOO_FACTOR_RESIDUAL_HIGH_;
+        if (args.is_fp64) st |= SHAMPOO_FACTOR_FP64_;
+        else st &= ~SHAMPOO_FACTOR_FP64_;
+        dg.status = st;
+        dg.residual = (st0 == 0) ? res : 0.0;
+    }
+}
+
+// Identity roots for every factor (state initialisation).
+__global__ __launch_bounds__(256) void k_set_identity(const FactorJob* __restrict__ jobs,
+                                                     float* __restrict__ arena) {
+    const FactorJob jb = jobs[blockIdx.x];
+    const int ld = jb.ld;
+    float* P = arena + jb.p_off;
+    double* P64 = jb.p64_off >= 0 ? reinterpret_cast<double*>(arena) + jb.p64_off : nullptr;
+    const int64_t nn = (int64_t)ld * ld;
+    for (int64_t idx = threadIdx.x; idx < nn; idx += 256) {
+        const bool d = (idx / ld) == (idx % ld);
+        P[idx] = d ? 1.f : 0.f;
+        if (P64) P64[idx] = d ? 1.0 : 0.0;
+    }
+}
+
+// ================================================== elementwise: Adagrad
+// a <- a + G*G over one run of rows of a Shampoo block and the partial
+// ||A||^2 of A = G / (sqrt(a) + delta) for that run (fixed order).
+__global__ __launch_bounds__(256) void k_adagrad_norm(const BlockChunk* __restrict__ chunks,
+                                                     const uint64_t* __restrict__ bases,
+                                                     float* __restrict__ arena, float delta,
+                                                     double* __restrict__ partA) {
+    __shared__ double red[4];
+    const BlockChunk ch = chunks[blockIdx.x];
+    const float* G = reinterpret_cast<const float*>(bases[1 + ch.tensor]);
+    float* a = arena + ch.a_off;
+    const int64_t total = (int64_t)ch.nrows * ch.ncols;
+    double acc = 0.0;
+    const bool vec = (ch.ncols % 4 == 0) && (ch.cols % 4 == 0) && (ch.col0 % 4 == 0) &&
+                     ((reinterpret_cast<uintptr_t>(G) & 15) == 0);
+    if (vec) {
+        const int c4 = ch.ncols / 4;
+        const int64_t t4 = total / 4;
+        for (int64_t e = threadIdx.x; e < t4; e += 256) {
+            const int r = ch.row0 + (int)(e / c4);
+            const int c = ch.col0 + 4 * (int)(e % c4);
+            const int64_t idx = (int64_t)r * ch.cols + c;
+            const float4 g = *reinterpret_cast<const float4*>(G + idx);
+            float4 av = *reinterpret_cast<const float4*>(a + idx);
+            av.x += g.x * g.x; av.y += g.y * g.y; av.z += g.z * g.z; av.w += g.w * g.w;
+            *reinterpret_cast<float4*>(a + idx) = av;
+            const float A0 = g.x / (sqrtf(av.x) + delta), A1 = g.y / (sqrtf(av.y) + delta);
+            const float A2 = g.z / (sqrtf(av.z) + delta), A3 = g.w / (sqrtf(av.w) + delta);
+            acc += (double)(A0 * A0 + A1 * A1) + (double)(A2 * A2 + A3 * A3);
+        }
+    } else {
+        for (int64_t e = threadIdx.x; e < total; e += 256) {
+            const int r = ch.row0 + (int)(e / ch.ncols);
+            const int c = ch.col0 + (int)(e % ch.ncols);
+            const int64_t idx = (int64_t)r * ch.cols + c;
+            const float g = G[idx];
+            const float av = a[idx] + g * g;
+            a[idx] = av;
+            const float A = g / (sqrtf(av) + delta);
+            acc += (double)(A * A);
+        }
+    }
+    const double s = block_sum_256(acc, red);
+    if (threadIdx.x == 0) partA[ch.slot] = s;
+}
+
+__global__ void k_block_scale(const BlockNorms* __restrict__ bn, int nblocks,
+                              const double* __restrict__ partA, const double* __restrict__ partD,
+                              float* __restrict__ scale) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nblocks) return;
+    const BlockNorms q = bn[b];
+    double na = 0.0, nd = 0.0;
+    for (int k = 0; k < q.a_count; ++k) na += partA[q.a_first + k];
+    for (int k = 0; k < q.d_count; ++k) nd += partD[q.d_first + k];
+    scale[b] = nd > 0.0 ? (float)sqrt(na / nd) : 0.f;
+}
+
+// ================================================== elementwise: update
+// Shampoo rows:  U = scale_b D;  dense-Adagrad rows: a += g^2, U = g/(sqrt(a)+delta).
+// Then mom <- beta1 mom + U and W <- W - lr mom.
+__global__ __launch_bounds__(256) void k_update(const RowChunk* __restrict__ chunks,
+                                               const uint64_t* __restrict__ bases, int n_tensors,
+                                               float* __restrict__ arena,
+                                               const float* __restrict__ scale, UpdateArgs args) {
+    const RowChunk ch = chunks[blockIdx.x];
+    const float* G = reinterpret_cast<const float*>(bases[1 + ch.tensor]);
+    float* W = reinterpret_cast<float*>(bases[1 + n_tensors + ch.tensor]);
+    float* a = arena + ch.a_off;
+    float* mom = arena + ch.m_off;
+    const float* D = arena + ch.d_off;
+    const int64_t base = (int64_t)ch.row0 * ch.cols;
+    const int64_t total = (int64_t)ch.nrows * ch.cols;
+    const float b1 = args.beta1, lr = args.lr, dl = args.delta;
+    const bool vec = (ch.cols % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(G) & 15) == 0);
+    if (vec) {
+        const int64_t t4 = total / 4;
+        const int c4 = ch.cols / 4;
+        for (int64_t e = threadIdx.x; e < t4; e += 256) {
+            const int64_t idx = base + 4 * e;
+            float4 u;
+            if (ch.mode == 0) {
+                const int r = ch.row0 + (int)(e / c4);
+                const int c = 4 * (int)(e % c4);
+                const int blk = ch.first_block + (r / ch.block_size) * ch.nbc + c / ch.block_size;
+                const float s = scale[blk];
+                const float4 d = *reinterpret_cast<const float4*>(D + idx);
+                u = make_float4(s * d.x, s * d.y, s * d.z, s * d.w);
+            } else {
+                const float4 g = *reinterpret_cast<const float4*>(G + idx);
+                float4 av = *reinterpret_cast<const float4*>(a + idx);
+                av.x += g.x * g.x; av.y += g.y * g.y; av.z += g.z * g.z; av.w += g.w * g.w;
+                *reinterpret_cast<float4*>(a + idx) = av;
+                u = make_float4(g.x / (sqrtf(av.x) + dl), g.y / (sqrtf(av.y) + dl),
+                                g.z / (sqrtf(av.z) + dl), g.w / (sqrtf(av.w) + dl));
+            }
+            float4 m = *reinterpret_cast<const float4*>(mom + idx);
+            float4 w = *reinterpret_cast<const float4*>(W + idx);
+            m.x = b1 * m.x + u.x; m.y = b1 * m.y + u.y; m.z = b1 * m.z + u.z; m.w = b1 * m.w + u.w;
+            w.x -= lr * m.x; w.y -= lr * m.y; w.z -= lr * m.z; w.w -= lr * m.w;
+            *reinterpret_cast<float4*>(mom + idx) = m;
+            *reinterpret_cast<float4*>(W + idx) = w;
+        }
+    } else {
+        for (int64_t e = threadIdx.x; e < total; e += 256) {
+            const int64_t idx = base + e;
+            float u;
+            if (ch.mode == 0) {
+                const int r = ch.row0 + (int)(e / ch.cols);
+                const int c = (int)(e % ch.cols);
+                const int blk = ch.first_block + (r / ch.block_size) * ch.nbc + c / ch.block_size;
+                u = scale[blk] * D[idx];
+            } else {
+                const float g = G[idx];
+                const float av = a[idx] + g * g;
+                a[idx] = av;
+                u = g / (sqrtf(av) + dl);
+            }
+            const float m = b1 * mom[idx] + u;
+            mom[idx] = m;
+            W[idx] -= lr * m;
+        }
+    }
+}
+
+// ================================================ sparse-row Adagrad
+__global__ __launch_bounds__(256) void k_sparse_rows(const SparseJob* __restrict__ jobs, int njobs,
+                                                    int64_t total, float* __restrict__ arena,
+                                                    float lr, float delta) {
+    const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (item >= total) return;
+    int j = 0;
+    while (j + 1 < njobs && jobs[j + 1].first_item <= item) ++j;
+    const SparseJob jb = jobs[j];
+    const int64_t li = item - jb.first_item;
+    const int32_t* rows = reinterpret_cast<const int32_t*>(jb.rows_ptr);
+    const float* g = reinterpret_cast<const float*>(jb.grads_ptr);
+    float* W = reinterpret_cast<float*>(jb.w_ptr);
+    float* a = arena + jb.a_off;
+    if (jb.vec) {
+        const int c4 = jb.cols / 4;
+        const int64_t k = li / c4;
+        const int c = 4 * (int)(li % c4);
+        const int64_t r = rows[k];
+        if (r < 0 || r >= jb.table_rows) return;
+        const float4 gv = *reinterpret_cast<const float4*>(g + k * jb.cols + c);
+        float4 av = *reinterpret_cast<float4*>(a + r * jb.cols + c);
+        float4 wv = *reinterpret_cast<float4*>(W + r * jb.cols + c);
+        av.x += gv.x * gv.x; av.y += gv.y * gv.y; av.z += gv.z * gv.z; av.w += gv.w * gv.w;
+        wv.x -= lr * gv.x / (sqrtf(av.x) + delta);
+        wv.y -= lr * gv.y / (sqrtf(av.y) + delta);
+        wv.z -= lr * gv.z / (sqrtf(av.z) + delta);
+        wv.w -= lr * gv.w / (sqrtf(av.w) + delta);
+        *reinterpret_cast<float4*>(a + r * jb.cols + c) = av;
+        *reinterpret_cast<float4*>(W + r * jb.cols + c) = wv;
+    } else {
+        const int64_t k = li / jb.cols;
+        const int c = (int)(li % jb.cols);
+        const int64_t r = rows[k];
+        if (r < 0 || r >= jb.table_rows) return;
+        const float gv = g[k * jb.cols + c];
+        const float av = a[r * jb.cols + c] + gv * gv;
+        a[r * jb.cols + c] = av;
+        W[r * jb.cols + c] -= lr * gv / (sqrtf(av) + delta);
+    }
+}
+
+// ================================================================ launches
+hipError_t launch_gemm_f32(const GemmTask* tasks, const TileRef* tiles, int ntiles,
+                           const uint64_t* bases, const GemmArgs& a, hipStream_t s) {
+    if (ntiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL((k_gemm<float, float, float>), dim3(ntiles), dim3(256), 0, s, tasks, tiles,
+                       bases, a);
+    return hipGetLastError();
+}
+hipError_t launch_gemm_f64(const GemmTask* tasks, const TileRef* tiles, int ntiles,
+                           const uint64_t* bases, const GemmArgs& a, hipStream_t s) {
+    if (ntiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL((k_gemm<double, double, double>), dim3(ntiles), dim3(256), 0, s, tasks,
+                       tiles, bases, a);
+    return hipGetLastError();
+}
+hipError_t launch_gemm_f64_from_f32(const GemmTask* tasks, const TileRef* tiles, int ntiles,
+                                    const uint64_t* bases, const GemmArgs& a, hipStream_t s) {
+    if (ntiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL((k_gemm<double, float, float>), dim3(ntiles), dim3(256), 0, s, tasks,
+                       tiles, bases, a);
+    return hipGetLastError();
+}
+hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, bool fp64_matrix,
+                          const LanczosArgs& a, hipStream_t s) {
+    if (njobs <= 0) return hipSuccess;
+    if (fp64_matrix)
+        hipLaunchKernelGGL(k_lanczos<double>, dim3(njobs), dim3(256), 0, s, jobs,
+                           static_cast<const double*>(arena), a);
+    else
+        hipLaunchKernelGGL(k_lanczos<float>, dim3(njobs), dim3(256), 0, s, jobs,
+                           static_cast<const float*>(arena), a);
+    return hipGetLastError();
+}
+hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, const double* stats,
+                              void* scratch, const FactorDiag* diag, const NewtonArgs& a,
+                              hipStream_t s) {
+    if (njobs <= 0) return hipSuccess;
+    if (fp64)
+        hipLaunchKernelGGL(k_newton_init<double>, dim3(njobs), dim3(256), 0, s, jobs, stats,
+                           static_cast<double*>(scratch), diag, a);
+    else
+        hipLaunchKernelGGL(k_newton_init<float>, dim3(njobs), dim3(256), 0, s, jobs, stats,
+                           static_cast<float*>(scratch), diag, a);
+    return hipGetLastError();
+}
+hipError_t launch_newton_commit(bool fp64, const FactorJob* jobs, int njobs, float* arena,
+                                const void* scratch, FactorDiag* diag, const NewtonArgs& a,
+                                hipStream_t s) {
+    if (njobs <= 0) return hipSuccess;
+    if (fp64)
+        hipLaunchKernelGGL(k_newton_commit<double>, dim3(njobs), dim3(256), 0, s, jobs, arena,
+                           static_cast<const double*>(scratch), diag, a);
+    else
+        hipLaunchKernelGGL(k_newton_commit<float>, dim3(njobs), dim3(256), 0, s, jobs, arena,
+                           static_cast<const float*>(scratch), diag, a);
+    return hipGetLastError();
+}
+hipError_t launch_set_identity(const FactorJob* jobs, int njobs, float* arena, hipStream_t s) {
+    if (njobs <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_set_identity, dim3(njobs), dim3(256), 0, s, jobs, arena);
+    return hipGetLastError();
+}
+hipError_t launch_adagrad_norm(const BlockChunk* chunks, int nchunks, const uint64_t* bases,
+                               float* arena, float delta, double* partA, hipStream_t s) {
+    if (nchunks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_adagrad_norm, dim3(nchunks), dim3(256), 0, s, chunks, bases, arena, delta,
+                       partA);
+    return hipGetLastError();
+}
+hipError_t launch_block_scale(const BlockNorms* bn, int nblocks, const double* partA,
+                              const double* partD, float* scale, hipStream_t s) {
+    if (nblocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_block_scale, dim3((nblocks + 255) / 256), dim3(256), 0, s, bn, nblocks,
+                       partA, partD, scale);
+    return hipGetLastError();
+}
+hipError_t launch_update(const RowChunk* chunks, int nchunks, const uint64_t* bases, int n_tensors,
+                         float* arena, const float* scale, const UpdateArgs& a, hipStream_t s) {
+    if (nchunks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_update, dim3(nchunks), dim3(256), 0, s, chunks, bases, n_tensors, arena,
+                       scale, a);
+    return hipGetLastError();
+}
+hipError_t launch_sparse_rows(const SparseJob* jobs, int njobs, int64_t total, float* arena,
+                              float lr, float delta, hipStream_t s) {
+    if (njobs <= 0 || total <= 0) return hipSuccess;
+    const int64_t nb = (total + 255) / 256;
+    hipLaunchKernelGGL(k_sparse_rows, dim3((unsigned)nb), dim3(256), 0, s, jobs, njobs, total,
+                       arena, lr, delta);
+    return hipGetLastError();
+}
+
+}  // namespace shampoo

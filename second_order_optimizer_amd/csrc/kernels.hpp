@@ -1,0 +1,77 @@
+// Launch interface of the gfx950 kernels (host side).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "common.hpp"
+
+namespace shampoo {
+
+enum : int {
+    SHAMPOO_FACTOR_NONFINITE_INPUT_ = 1,
+    SHAMPOO_FACTOR_NONFINITE_ROOT_ = 2,
+    SHAMPOO_FACTOR_RESIDUAL_HIGH_ = 4,
+    SHAMPOO_FACTOR_FP64_ = 8,
+    SHAMPOO_FACTOR_ZERO_ = 16,
+};
+
+enum : int { EPI_STORE = 0, EPI_AXPBY = 1 };
+
+struct GemmArgs {
+    int epi;              // EPI_STORE or EPI_AXPBY
+    double alpha, beta;   // C = alpha acc (+ beta C)
+    double xc1, xc2;      // Newton operand transform c1 I + c2 X (trans bits 2/3)
+    const int32_t* gate;  // per-factor precision flags, or null
+    int32_t gate_val;     // run only tasks whose factor has this flag
+    double* norms;        // per-tile ||C||^2 partials (tasks with norm_slot >= 0)
+};
+
+struct LanczosArgs {
+    int steps;
+    int mode;             // 0: statistics (lambda_max, eps), 1: roots (kappa estimate)
+    int p;
+    int auto_route;       // mode 1: set prec flags from the kappa estimate
+    int route_all_fp64;   // mode 0: initial prec flag value
+    double eps_rel;
+    double threshold;
+    FactorDiag* diag;
+    int32_t* prec;
+};
+
+struct NewtonArgs {
+    int p;
+    int is_fp64;
+    const int32_t* gate;
+    int32_t gate_val;
+};
+
+struct UpdateArgs {
+    float beta1, lr, delta;
+};
+
+hipError_t launch_gemm_f32(const GemmTask* tasks, const TileRef* tiles, int ntiles,
+                           const uint64_t* bases, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_f64(const GemmTask* tasks, const TileRef* tiles, int ntiles,
+                           const uint64_t* bases, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_f64_from_f32(const GemmTask* tasks, const TileRef* tiles, int ntiles,
+                                    const uint64_t* bases, const GemmArgs& a, hipStream_t s);
+hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, bool fp64_matrix,
+                          const LanczosArgs& a, hipStream_t s);
+hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, const double* stats,
+                              void* scratch, const FactorDiag* diag, const NewtonArgs& a,
+                              hipStream_t s);
+hipError_t launch_newton_commit(bool fp64, const FactorJob* jobs, int njobs, float* arena,
+                                const void* scratch, FactorDiag* diag, const NewtonArgs& a,
+                                hipStream_t s);
+hipError_t launch_set_identity(const FactorJob* jobs, int njobs, float* arena, hipStream_t s);
+hipError_t launch_adagrad_norm(const BlockChunk* chunks, int nchunks, const uint64_t* bases,
+                               float* arena, float delta, double* partA, hipStream_t s);
+hipError_t launch_block_scale(const BlockNorms* bn, int nblocks, const double* partA,
+                              const double* partD, float* scale, hipStream_t s);
+hipError_t launch_update(const RowChunk* chunks, int nchunks, const uint64_t* bases, int n_tensors,
+                         float* arena, const float* scale, const UpdateArgs& a, hipStream_t s);
+hipError_t launch_sparse_rows(const SparseJob* jobs, int njobs, int64_t total, float* arena,
+                              float lr, float delta, hipStream_t s);
+
+}  // namespace shampoo

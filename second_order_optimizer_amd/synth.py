@@ -48,7 +48,7 @@ class Workload:
     tensors: List[TensorSpec]
     block_size: int
     max_precond_dim: int = 0        # 0: no limit; larger dims use diagonal Adagrad
-    root_mode: str = "f32"          # "f32", "f64" or "auto"
+    root_mode: str = "auto"         # "f32", "f64" or "auto" (fp64 when kappa > threshold)
     fp64_cond_threshold: float = 1e5
     cadence: int = 1                # inverse roots recomputed when step % cadence == 0
     newton_iters: int = 20
@@ -142,8 +142,7 @@ def workload(wid: int) -> Workload:
                         notes="6+6 layers, d_model 512, ffn 2048, 32000x512 embedding "
                               "on diagonal Adagrad")
     if wid == 2:
-        return Workload(2, "bert-large-b512", _bert_large(), 512, root_mode="auto",
-                        cadence=20, steps=80,
+        return Workload(2, "bert-large-b512", _bert_large(), 512, cadence=20, steps=80,
                         notes="24 layers, hidden 1024, ffn 4096; fp64 roots for "
                               "condition number > 1e5")
     if wid == 3:
