@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Throughput of the Shampoo optimizer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
+
+One step is the whole hot path over one batch of synthetic gradients already
+resident in HBM: statistics of every block, the inverse roots when
+step % cadence == 0, the two-sided preconditioning, grafting, momentum and
+the weight update (plus dense/sparse Adagrad where the workload has them).
+The timed steps are t = W .. W+K-1, so K/cadence root passes fall inside the
+timed region (the one at t = 0 is warm-up).
+
+Prints one JSON line: steps/s per 100M parameters (the headline), the
+inverse-root blocks/s and %MFMA of each MFMA stage, a per-kernel breakdown
+from HIP events recorded around every launch inside the timed region, the
+roofline of the dominant kernel, and the fp64 CPU oracle timed on a bounded
+sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+from second_order_optimizer_amd import synth  # noqa: E402
+
+METRIC = "Shampoo optimizer steps/sec per 100M params; inv-root blocks/sec; %MFMA peak"
+UNIT = "optimizer steps/s x (params / 1e8)"
+
+# MI355X published peaks (dense)
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6}
+
+KERNEL_SOURCES = [os.path.join(HERE, "second_order_optimizer_amd", "csrc", f)
+                  for f in ("kernels.hip", "api.cpp", "common.hpp", "kernels.hpp")]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ work model
+def work_model(wl, opt, n_fp64_factors_per_pass):
+    """Algorithmic flops / bytes per launch of each kernel family.
+
+    Statistics and apply count every product of the formulas as a dense GEMM
+    (2 M N K); the root counts 4 n^3 GEMMs x 2 flops x iterations per factor
+    (p = 4: X T, T^2, T^4, T^4 M).  Elementwise kernels count the bytes the
+    formulas must move once (fp32)."""
+    nb = opt.n_blocks
+    blocks = [opt.block(i) for i in range(nb)]
+    gram = sum(2.0 * (b.rows ** 2 * b.cols + b.cols ** 2 * b.rows) for b in blocks)
+    apply_t = sum(2.0 * b.rows * b.cols ** 2 for b in blocks)
+    apply_d = sum(2.0 * b.rows ** 2 * b.cols for b in blocks)
+    p = wl.root_p
+    gemms_per_iter = 2 + int(round(math.log2(p))) if p > 1 else 2
+    dims = [b.rows for b in blocks] + [b.cols for b in blocks]
+    root_flops_all = sum(gemms_per_iter * 2.0 * n ** 3 * wl.newton_iters for n in dims)
+    shampoo_params = sum(b.rows * b.cols for b in blocks)
+    dense_fallback = sum(t.numel for t in wl.tensors if t.kind == "dense") - shampoo_params
+    return {
+        "gram": gram, "apply_t": apply_t, "apply_d": apply_d,
+        "root_flops_all": root_flops_all,
+        "root_flops_per_factor_mean": root_flops_all / max(len(dims), 1),
+        "shampoo_params": shampoo_params, "dense_fallback": dense_fallback,
+    }
+
+
+# -------------------------------------------------------------------- CPU leg
+def cpu_baseline(wl, sample_ids, steps_plain=3):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload."""
+    from oracle import shampoo_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    cfg = O.OracleConfig(block_size=wl.block_size, max_precond_dim=wl.max_precond_dim,
+                         root_p=wl.root_p, beta1=wl.beta1, beta2=wl.beta2, lr=wl.lr,
+                         eps_rel=wl.eps_rel, graft_eps=wl.graft_eps, cadence=wl.cadence)
+    specs = [wl.tensors[i] for i in sample_ids]
+    orc = O.ShampooOracle(cfg, [(s.rows, s.cols, s.kind) for s in specs],
+                          [synth.initial_weight(wl, i) for i in sample_ids])
+    gs = synth.GradientStream(wl, sample_ids)
+    times = []
+    for t in range(1 + steps_plain):
+        g = gs.step(t)
+        grads = [g[i] if specs[k].kind == "dense" else g[i] for k, i in enumerate(sample_ids)]
+        t0 = time.perf_counter()
+        orc.step(grads, t)          # t = 0 recomputes every root
+        times.append(time.perf_counter() - t0)
+    t_plain = float(np.median(times[1:]))
+    t_root = max(times[0] - t_plain, 0.0)
+    t_amort = t_plain + t_root / wl.cadence
+    params = sum(s.numel for s in specs)
+    return {
+        "value": (1.0 / t_amort) * params / 1e8,
+        "unit": UNIT,
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{len(sample_ids)} of {len(wl.tensors)} tensors "
+                   f"({params / 1e6:.2f}M of {wl.n_params / 1e6:.2f}M params: "
+                   f"{', '.join(s.name for s in specs[:6])}{'...' if len(specs) > 6 else ''}); "
+                   f"1 step with every root recomputed ({times[0]:.2f} s) + {steps_plain} plain "
+                   f"steps (median {t_plain:.2f} s); amortised over cadence {wl.cadence}; "
+                   f"scaled by parameter count"),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def default_cpu_sample(wl):
+    if wl.wid == 1:   # one encoder and one decoder layer of the Transformer
+        return [i for i, t in enumerate(wl.tensors) if t.name.startswith(("enc0.", "dec0."))]
+    if wl.wid == 2:
+        return [i for i, t in enumerate(wl.tensors) if t.name.startswith("layer0.")][:2]
+    if wl.wid == 3:
+        return list(range(0, 14))
+    if wl.wid == 4:
+        return [0, 1, 2, 3]
+    return list(range(len(wl.tensors)))
+
+
+# ------------------------------------------------------------------- GPU leg
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=1,
+                    help="0: 256x512 b128, 1: Transformer-base b128 (default), 2: BERT-large "
+                         "b512, 3: ResNet-50 b256, 4: CTR MLP b1024 + sparse tables")
+    ap.add_argument("--root-mode", default=None, choices=["f32", "f64", "auto"])
+    ap.add_argument("--pool", type=int, default=4, help="distinct gradient sets kept in HBM")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="time without the per-launch events (no per-kernel breakdown)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the multi-GPU sharding is a design in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from second_order_optimizer_amd import shampoo as S
+
+    wl = synth.workload(args.workload)
+    if args.root_mode:
+        wl.root_mode = args.root_mode
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = S.make_config(wl.block_size, max_precond_dim=wl.max_precond_dim, root_p=wl.root_p,
+                        newton_iters=wl.newton_iters, root_mode=wl.root_mode, beta1=wl.beta1,
+                        beta2=wl.beta2, lr=wl.lr, eps_rel=wl.eps_rel, graft_eps=wl.graft_eps,
+                        fp64_cond_threshold=wl.fp64_cond_threshold)
+    shapes = [(t.rows, t.cols, 0 if t.kind == "dense" else 1) for t in wl.tensors]
+    t0 = time.time()
+    opt = S.Shampoo(shapes, cfg, device=dev)
+    params = [torch.from_numpy(synth.initial_weight(wl, i)).to(dev) for i in range(len(shapes))]
+    gs = synth.GradientStream(wl)
+    pool = []
+    for k in range(args.pool):
+        g = gs.step(k)
+        dense, sparse = [], {}
+        for i, spec in enumerate(wl.tensors):
+            if spec.kind == "dense":
+                dense.append(torch.from_numpy(g[i]).to(dev))
+            else:
+                rows, rg = g[i]
+                dense.append(None)
+                sparse[i] = (torch.from_numpy(rows).to(dev), torch.from_numpy(rg).to(dev))
+        pool.append((dense, sparse))
+    torch.cuda.synchronize()
+    print(f"# setup {time.time() - t0:.1f} s: {wl.name}, {wl.n_params / 1e6:.2f}M params, "
+          f"{opt.n_blocks} blocks, state {opt.state_bytes / 2**30:.2f} GiB", file=sys.stderr,
+          flush=True)
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    def step(t):
+        dense, sparse = pool[t % len(pool)]
+        opt.step(params, dense, t, wl.cadence, sparse if sparse else None)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    print(f"# warm-up {args.warmup} steps done", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if not args.no_profile:
+        opt.profile(True)
+        opt.profile_read()        # reset
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for t in range(args.warmup, args.warmup + args.steps):
+        step(t)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = ev0.elapsed_time(ev1)
+    prof = opt.profile_read() if not args.no_profile else {}
+    opt.profile(False)
+    ms_step = ms_total / args.steps
+    n_root_passes = sum(1 for t in range(args.warmup, args.warmup + args.steps)
+                        if t % wl.cadence == 0)
+    diag = opt.diagnostics()
+    n64 = sum(1 for d in diag if d.status & S.FACTOR_FP64)
+    wm = work_model(wl, opt, n64)
+
+    steps_per_s = 1000.0 / ms_step
+    value = steps_per_s * wl.n_params / 1e8
+
+    # per-kernel breakdown
+    def fam(name):
+        return prof.get(name, (0, 0.0))
+
+    stages = {}
+    fp64_share = n64 / max(len(diag), 1)
+    root_dims = [d.dim for d in diag]
+    flops_f32_root = sum((2 + int(round(math.log2(wl.root_p)))) * 2.0 * n ** 3 * wl.newton_iters
+                         for n in root_dims) if wl.root_mode != "f64" else 0.0
+    flops_f64_root = sum((2 + int(round(math.log2(wl.root_p)))) * 2.0 * d.dim ** 3 *
+                         wl.newton_iters for d in diag if d.status & S.FACTOR_FP64)
+    alg = {
+        # name: (work per launch, unit, bound, peak)
+        "stats_gram_f64": (wm["gram"], "TFLOP/s", "mfma", PEAK_TFLOPS["f64"]),
+        "apply_gemm_t": (wm["apply_t"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]),
+        "apply_gemm_d": (wm["apply_d"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]),
+        "adagrad_norm": (wm["shampoo_params"] * 12.0, "GB/s", "hbm", PEAK_HBM_GBS),
+        "update": (wm["shampoo_params"] * 20.0 + wm["dense_fallback"] * 28.0, "GB/s", "hbm",
+                   PEAK_HBM_GBS),
+    }
+    for name, (launches, tot) in prof.items():
+        if launches == 0:
+            continue
+        rec = {"launches": int(launches), "avg_ms": tot / launches,
+               "ms_per_step": tot / args.steps}
+        work = None
+        if name in alg:
+            work, unit, bound, peak = alg[name]
+        elif name == "newton_gemm_f32" and flops_f32_root > 0:
+            work = flops_f32_root * n_root_passes / launches
+            unit, bound, peak = "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]
+        elif name == "newton_gemm_f64" and flops_f64_root > 0:
+            work = flops_f64_root * n_root_passes / launches
+            unit, bound, peak = "TFLOP/s", "mfma", PEAK_TFLOPS["f64"]
+        if work is not None:
+            sec = rec["avg_ms"] / 1e3
+            ach = work / sec / (1e12 if unit == "TFLOP/s" else 1e9)
+            rec.update({"bound": bound, "achieved": ach, "peak": peak, "unit": unit,
+                        "frac": ach / peak})
+        stages[name] = rec
+
+    # the dominant kernel family by time in the timed region
+    roofline = None
+    dom = max(stages.items(), key=lambda kv: kv[1]["ms_per_step"]) if stages else None
+    if dom and "achieved" in dom[1]:
+        traffic = None
+        tf = os.path.join(HERE, "profiles", "traffic.json")
+        if os.path.exists(tf):
+            with open(tf) as f:
+                tj = json.load(f)
+            ent = tj.get(dom[0])
+            if ent and ent.get("kernel_hash") == kernel_hash() and \
+                    ent.get("workload") == wl.name:
+                traffic = ent.get("bytes_per_launch")
+        roofline = {"kernel": dom[0], "bound": dom[1]["bound"], "achieved": dom[1]["achieved"],
+                    "peak": dom[1]["peak"], "unit": dom[1]["unit"], "frac": dom[1]["frac"],
+                    "traffic": traffic}
+
+    root_ms = sum(prof.get(n, (0, 0.0))[1] for n in
+                  ("lanczos_stats", "lanczos_roots", "newton_init", "newton_gemm_f32",
+                   "newton_gemm_f64", "newton_commit"))
+    inv_root_blocks_per_s = (opt.n_blocks * n_root_passes / (root_ms / 1e3)) if root_ms > 0 else None
+    mfma_pct = {k: round(100 * v["frac"], 2) for k, v in stages.items() if v.get("bound") == "mfma"}
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 gradients/weights; f64 statistics; f32+f64 (routed) roots",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "params": wl.n_params, "blocks": opt.n_blocks,
+                   "block_size": wl.block_size, "root_cadence": wl.cadence,
+                   "newton_iters": wl.newton_iters, "root_mode": wl.root_mode,
+                   "max_precond_dim": wl.max_precond_dim, "parallelism": "single-gpu"},
+        "steps_per_s": steps_per_s,
+        "inv_root_blocks_per_s": inv_root_blocks_per_s,
+        "root_passes_timed": n_root_passes,
+        "fp64_factor_share_last_pass": fp64_share,
+        "mfma_pct": mfma_pct,
+        "stages": stages,
+        "roofline": roofline,
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (fp64 oracle) ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, default_cpu_sample(wl))
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

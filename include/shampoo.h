@@ -212,6 +212,22 @@ int shampoo_block_info(const shampoo_t* h, int32_t block, shampoo_block_layout* 
 int shampoo_tensor_info(const shampoo_t* h, int32_t tensor, int64_t* adagrad_off,
                         int64_t* mom_off, int32_t* first_block, int32_t* n_blocks);
 
+/* Per-kernel GPU time, for measurement tools.  While enabled, every kernel
+ * launch of the calls above is bracketed by two HIP events recorded on the
+ * call's stream (a few microseconds of host time per launch, no device
+ * synchronisation).  shampoo_profile_read waits for the recorded events, adds
+ * their elapsed times per kernel family into `out` (up to `cap` records, in a
+ * fixed order; *n_out receives the number written) and resets the counters.
+ * Errors: SHAMPOO_E_ARG, SHAMPOO_E_HIP. */
+typedef struct {
+    char name[32];       /* kernel family, e.g. "newton_gemm_f32"                     */
+    int64_t launches;    /* launches since the last read                              */
+    double total_ms;     /* summed event-to-event GPU time of those launches          */
+} shampoo_kernel_time;
+
+int shampoo_profile_enable(shampoo_t* h, int32_t on);
+int shampoo_profile_read(shampoo_t* h, shampoo_kernel_time* out, int32_t cap, int32_t* n_out);
+
 /* Free the handle (host memory only; the caller frees the state buffer). */
 void shampoo_destroy(shampoo_t* h);
 

@@ -80,6 +80,20 @@ struct Blob {
     }
 };
 
+enum ProfCat : int {
+    PC_STATS = 0, PC_LANCZOS_S, PC_LANCZOS_P, PC_NEWTON_INIT, PC_NEWTON_GEMM32, PC_NEWTON_GEMM64,
+    PC_NEWTON_COMMIT, PC_ADAGRAD, PC_APPLY_T, PC_APPLY_D, PC_SCALE, PC_UPDATE, PC_SPARSE, PC_COUNT
+};
+const char* const kProfNames[PC_COUNT] = {
+    "stats_gram_f64", "lanczos_stats", "lanczos_roots", "newton_init", "newton_gemm_f32",
+    "newton_gemm_f64", "newton_commit", "adagrad_norm", "apply_gemm_t", "apply_gemm_d",
+    "block_scale", "update", "sparse_rows"};
+
+struct ProfRec {
+    int cat;
+    hipEvent_t a, b;
+};
+
 }  // namespace
 
 struct shampoo_s {
@@ -115,7 +129,19 @@ struct shampoo_s {
     bool ring_used[kRingSlots] = {};
     int ring_next = 0;
 
+    // optional per-kernel timing
+    bool prof_on = false;
+    std::vector<ProfRec> prof_pending;
+    std::vector<hipEvent_t> prof_pool;
+    int64_t prof_launches[PC_COUNT] = {};
+    double prof_ms[PC_COUNT] = {};
+
     ~shampoo_s() {
+        for (auto& r : prof_pending) {
+            (void)hipEventDestroy(r.a);
+            (void)hipEventDestroy(r.b);
+        }
+        for (auto e : prof_pool) (void)hipEventDestroy(e);
         for (int i = 0; i < kRingSlots; ++i)
             if (ring_ev[i]) (void)hipEventDestroy(ring_ev[i]);
         if (ring) (void)hipHostFree(ring);
@@ -503,6 +529,36 @@ int build_plan(shampoo_s* h) {
 
 int hip_err(hipError_t e) { return e == hipSuccess ? SHAMPOO_OK : SHAMPOO_E_HIP; }
 
+hipEvent_t prof_event(shampoo_s* h) {
+    if (!h->prof_pool.empty()) {
+        hipEvent_t e = h->prof_pool.back();
+        h->prof_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Brackets one kernel launch with two events when timing is enabled.
+struct ProfScope {
+    shampoo_s* h;
+    int cat;
+    hipStream_t s;
+    hipEvent_t a = nullptr;
+    ProfScope(shampoo_s* h_, int cat_, hipStream_t s_) : h(h_), cat(cat_), s(s_) {
+        if (!h->prof_on) return;
+        a = prof_event(h);
+        if (a && hipEventRecord(a, s) != hipSuccess) a = nullptr;
+    }
+    ~ProfScope() {
+        if (!a) return;
+        hipEvent_t b = prof_event(h);
+        if (b && hipEventRecord(b, s) == hipSuccess) h->prof_pending.push_back({cat, a, b});
+        else h->prof_pool.push_back(a);
+    }
+};
+
 template <typename T>
 T* at(shampoo_s* h, int64_t off_bytes) {
     return reinterpret_cast<T*>(h->arena + off_bytes);
@@ -713,6 +769,7 @@ int shampoo_update_stats(shampoo_t* h, const float* const* grads, void* stream) 
     // fp32 gradients, fp64 products and statistics (exact products; the
     // statistics keep the near-null spectrum that fp32 storage would round
     // into the eps damping)
+    ProfScope ps(h, PC_STATS, s);
     return hip_err(launch_gemm_f64_from_f32(tab<GemmTask>(h, h->gram.tasks_off),
                                             tab<TileRef>(h, h->gram.tiles_off), h->gram.ntiles,
                                             at<uint64_t>(h, h->off_bases), a, s));
@@ -740,18 +797,24 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
     const uint64_t* bases = at<uint64_t>(h, h->off_bases);
     for (auto& ch : chunks) {
         const FactorJob* jobs = tab<FactorJob>(h, ch.jobs_off);
-        int rc = hip_err(launch_newton_init(fp64, jobs, ch.njobs, at<double>(h, 0), scratch, diag, na, s));
+        int rc;
+        {
+            ProfScope ps(h, PC_NEWTON_INIT, s);
+            rc = hip_err(launch_newton_init(fp64, jobs, ch.njobs, at<double>(h, 0), scratch, diag, na, s));
+        }
         if (rc) return rc;
         for (int it = 0; it < h->cfg.newton_iters; ++it) {
             for (const LaunchRef& L : ch.stages[it & 1]) {
                 const GemmTask* tk = tab<GemmTask>(h, L.tasks_off);
                 const TileRef* tl = tab<TileRef>(h, L.tiles_off);
+                ProfScope ps(h, fp64 ? PC_NEWTON_GEMM64 : PC_NEWTON_GEMM32, s);
                 rc = hip_err(fp64 ? launch_gemm_f64(tk, tl, L.ntiles, bases, g, s)
                                   : launch_gemm_f32(tk, tl, L.ntiles, bases, g, s));
                 if (rc) return rc;
             }
         }
         // the final X, M sit in buffer (iters % 2) of each slot
+        ProfScope ps(h, PC_NEWTON_COMMIT, s);
         rc = hip_err(launch_newton_commit(fp64, jobs, ch.njobs, at<float>(h, 0),
                                           static_cast<unsigned char*>(scratch) +
                                               (size_t)(h->cfg.newton_iters & 1) * ch.ld * ch.ld *
@@ -781,7 +844,11 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
     la.diag = diag;
     la.prec = prec;
     la.route_all_fp64 = c.root_mode == SHAMPOO_ROOT_F64 ? 1 : 0;
-    int rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_s_off), nf, h->arena, true, la, s));
+    int rc;
+    {
+        ProfScope ps(h, PC_LANCZOS_S, s);
+        rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_s_off), nf, h->arena, true, la, s));
+    }
     if (rc) return rc;
     if (use_fp32(c)) {
         rc = run_newton(h, h->chunks32, false, nullptr, 0, s);
@@ -789,7 +856,10 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
         LanczosArgs lp = la;
         lp.mode = 1;
         lp.auto_route = c.root_mode == SHAMPOO_ROOT_AUTO ? 1 : 0;
-        rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_p_off), nf, h->arena, false, lp, s));
+        {
+            ProfScope ps(h, PC_LANCZOS_P, s);
+            rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_p_off), nf, h->arena, false, lp, s));
+        }
         if (rc) return rc;
     }
     if (use_fp64(c)) {
@@ -800,6 +870,7 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
             LanczosArgs lp = la;
             lp.mode = 1;
             lp.auto_route = 0;
+            ProfScope ps(h, PC_LANCZOS_P, s);
             rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_p_off), nf, h->arena, false, lp, s));
             if (rc) return rc;
         }
@@ -826,25 +897,40 @@ int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const flo
     float* scale = at<float>(h, h->off_scale);
     const shampoo_config& c = h->cfg;
 
-    rc = hip_err(launch_adagrad_norm(tab<BlockChunk>(h, h->blockchunks_off), h->n_blockchunks, bases,
+    {
+        ProfScope ps(h, PC_ADAGRAD, s);
+        rc = hip_err(launch_adagrad_norm(tab<BlockChunk>(h, h->blockchunks_off), h->n_blockchunks, bases,
                                      arena, (float)c.graft_eps, partA, s));
+    }
     if (rc) return rc;
     GemmArgs g{};
     g.epi = EPI_STORE;
     g.alpha = 1.0;
     g.norms = partD;
-    rc = hip_err(launch_gemm_f32(tab<GemmTask>(h, h->apply1.tasks_off),
-                                 tab<TileRef>(h, h->apply1.tiles_off), h->apply1.ntiles, bases, g, s));
+    {
+        ProfScope ps(h, PC_APPLY_T, s);
+        rc = hip_err(launch_gemm_f32(tab<GemmTask>(h, h->apply1.tasks_off),
+                                     tab<TileRef>(h, h->apply1.tiles_off), h->apply1.ntiles, bases, g, s));
+    }
     if (rc) return rc;
-    rc = hip_err(launch_gemm_f32(tab<GemmTask>(h, h->apply2.tasks_off),
-                                 tab<TileRef>(h, h->apply2.tiles_off), h->apply2.ntiles, bases, g, s));
+    {
+        ProfScope ps(h, PC_APPLY_D, s);
+        rc = hip_err(launch_gemm_f32(tab<GemmTask>(h, h->apply2.tasks_off),
+                                     tab<TileRef>(h, h->apply2.tiles_off), h->apply2.ntiles, bases, g, s));
+    }
     if (rc) return rc;
-    rc = hip_err(launch_block_scale(tab<BlockNorms>(h, h->blocknorms_off), (int)h->blocks.size(), partA,
-                                    partD, scale, s));
+    {
+        ProfScope ps(h, PC_SCALE, s);
+        rc = hip_err(launch_block_scale(tab<BlockNorms>(h, h->blocknorms_off), (int)h->blocks.size(),
+                                        partA, partD, scale, s));
+    }
     if (rc) return rc;
     UpdateArgs ua{(float)c.beta1, (float)c.lr, (float)c.graft_eps};
-    rc = hip_err(launch_update(tab<RowChunk>(h, h->rowchunks_off), h->n_rowchunks, bases, h->n, arena,
-                               scale, ua, s));
+    {
+        ProfScope ps(h, PC_UPDATE, s);
+        rc = hip_err(launch_update(tab<RowChunk>(h, h->rowchunks_off), h->n_rowchunks, bases, h->n,
+                                   arena, scale, ua, s));
+    }
     if (rc) return rc;
     if (h->n_sparse > 0) {
         std::vector<SparseJob> jobs;
@@ -873,6 +959,7 @@ int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const flo
         if (!jobs.empty()) {
             rc = stage_upload(h, jobs.data(), jobs.size() * sizeof(SparseJob), h->off_sparse, s);
             if (rc) return rc;
+            ProfScope ps(h, PC_SPARSE, s);
             rc = hip_err(launch_sparse_rows(at<SparseJob>(h, h->off_sparse), (int)jobs.size(), items,
                                             arena, (float)c.lr, (float)c.graft_eps, s));
             if (rc) return rc;
@@ -893,6 +980,40 @@ int shampoo_get_diagnostics(shampoo_t* h, shampoo_factor_diag* out, int32_t cap,
         if (rc) return rc;
     }
     return hip_err(hipStreamSynchronize(s));
+}
+
+int shampoo_profile_enable(shampoo_t* h, int32_t on) {
+    if (!h) return SHAMPOO_E_ARG;
+    h->prof_on = on != 0;
+    return SHAMPOO_OK;
+}
+
+int shampoo_profile_read(shampoo_t* h, shampoo_kernel_time* out, int32_t cap, int32_t* n_out) {
+    if (!h || cap < 0 || (!out && cap > 0)) return SHAMPOO_E_ARG;
+    int rc = SHAMPOO_OK;
+    for (auto& r : h->prof_pending) {
+        float ms = 0.f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+            rc = SHAMPOO_E_HIP;
+        h->prof_launches[r.cat] += 1;
+        h->prof_ms[r.cat] += ms;
+        h->prof_pool.push_back(r.a);
+        h->prof_pool.push_back(r.b);
+    }
+    h->prof_pending.clear();
+    const int n = std::min<int>(cap, PC_COUNT);
+    for (int i = 0; i < n; ++i) {
+        std::memset(out[i].name, 0, sizeof(out[i].name));
+        std::strncpy(out[i].name, kProfNames[i], sizeof(out[i].name) - 1);
+        out[i].launches = h->prof_launches[i];
+        out[i].total_ms = h->prof_ms[i];
+    }
+    if (n_out) *n_out = n;
+    for (int i = 0; i < PC_COUNT; ++i) {
+        h->prof_launches[i] = 0;
+        h->prof_ms[i] = 0.0;
+    }
+    return rc;
 }
 
 void shampoo_destroy(shampoo_t* h) { delete h; }

@@ -60,6 +60,11 @@ class BlockLayout(ctypes.Structure):
                 ("off_pl64", ctypes.c_int64), ("off_pr64", ctypes.c_int64)]
 
 
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double)]
+
+
 # name -> (restype, argtypes); every symbol declared in include/shampoo.h
 _P = ctypes.c_void_p
 SIGNATURES = {
@@ -79,6 +84,9 @@ SIGNATURES = {
                                            ctypes.POINTER(ctypes.c_int64),
                                            ctypes.POINTER(ctypes.c_int32),
                                            ctypes.POINTER(ctypes.c_int32)]),
+    "shampoo_profile_enable": (ctypes.c_int, [_P, ctypes.c_int32]),
+    "shampoo_profile_read": (ctypes.c_int, [_P, ctypes.POINTER(KernelTime), ctypes.c_int32,
+                                            ctypes.POINTER(ctypes.c_int32)]),
     "shampoo_destroy": (None, [_P]),
     "shampoo_strerror": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -230,6 +238,16 @@ class Shampoo(Plan):
         if step % cadence == 0:
             self.compute_inverse_roots()
         self.precondition_and_apply(params, grads, sparse)
+
+    def profile(self, on: bool = True):
+        _check(lib().shampoo_profile_enable(self.h, 1 if on else 0), "shampoo_profile_enable")
+
+    def profile_read(self):
+        """{kernel family: (launches, total_ms)} since the last read."""
+        out = (KernelTime * 64)()
+        n = ctypes.c_int32()
+        _check(lib().shampoo_profile_read(self.h, out, 64, ctypes.byref(n)), "shampoo_profile_read")
+        return {out[i].name.decode(): (out[i].launches, out[i].total_ms) for i in range(n.value)}
 
     def diagnostics(self) -> List[FactorDiag]:
         out = (FactorDiag * max(self.n_factors, 1))()

@@ -1,0 +1,132 @@
+"""Host-side tests (no GPU): the C-ABI library loads and exports every symbol
+include/shampoo.h declares, the struct layouts agree, and the planner's block
+partition and state layout are right for every workload."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import shampoo_oracle as O
+from second_order_optimizer_amd import shampoo as S
+from second_order_optimizer_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "shampoo.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(shampoo_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = S.lib()
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(S.SIGNATURES), set(names) ^ set(S.SIGNATURES)
+
+
+def test_struct_sizes_match_header():
+    # sizes the C compiler gives (natural alignment, x86-64 / amdgcn agree)
+    assert ctypes.sizeof(S.TensorDesc) == 24
+    assert ctypes.sizeof(S.Config) == 80
+    assert ctypes.sizeof(S.SparseRows) == 24
+    assert ctypes.sizeof(S.FactorDiag) == 48
+    assert ctypes.sizeof(S.BlockLayout) == 88
+    assert ctypes.sizeof(S.KernelTime) == 48
+
+
+def test_strerror_and_argument_errors():
+    L = S.lib()
+    assert L.shampoo_strerror(0) == b"ok"
+    assert L.shampoo_strerror(-1) == b"invalid argument"
+    cfg = S.make_config(128)
+    h = S._P()
+    descs = (S.TensorDesc * 1)(S.TensorDesc(4, 4, 0, 0))
+    assert L.shampoo_create(None, 1, descs, ctypes.byref(h)) == -1
+    assert L.shampoo_create(ctypes.byref(cfg), 0, descs, ctypes.byref(h)) == -1
+    bad = (S.TensorDesc * 1)(S.TensorDesc(0, 4, 0, 0))
+    assert L.shampoo_create(ctypes.byref(cfg), 1, bad, ctypes.byref(h)) == -1
+    badk = (S.TensorDesc * 1)(S.TensorDesc(4, 4, 7, 0))
+    assert L.shampoo_create(ctypes.byref(cfg), 1, badk, ctypes.byref(h)) == -1
+    for field, val, rc in (("root_p", 3, -5), ("root_p", 16, -5), ("beta2", 0.0, -1),
+                           ("beta2", 1.5, -1), ("block_size", 0, -1), ("newton_iters", 0, -1),
+                           ("root_mode", 5, -1), ("eps_rel", -1.0, -1)):
+        c = S.make_config(128)
+        setattr(c, field, val)
+        assert L.shampoo_create(ctypes.byref(c), 1, descs, ctypes.byref(h)) == rc, field
+    # a dimension above the supported factor size is rejected up front
+    big = (S.TensorDesc * 1)(S.TensorDesc(2048, 64, 0, 0))
+    assert L.shampoo_create(ctypes.byref(S.make_config(2048)), 1, big, ctypes.byref(h)) == -5
+    # calls on an unbound handle
+    p = S.Plan([(8, 8, 0)], cfg)
+    arr = (S._P * 1)()
+    assert L.shampoo_update_stats(p.h, arr, None) == -2
+    assert L.shampoo_compute_inverse_roots(p.h, None) == -2
+    assert L.shampoo_update_stats(p.h, None, None) == -1
+    p.close()
+
+
+EXPECTED_BLOCKS = {0: 8, 1: 2688, 2: 1152, 3: 422, 4: 3}
+
+
+@pytest.mark.parametrize("wid", range(5))
+def test_planner_matches_oracle_partition(wid):
+    wl = synth.workload(wid)
+    cfg = S.make_config(wl.block_size, max_precond_dim=wl.max_precond_dim, root_mode=wl.root_mode)
+    p = S.Plan([(t.rows, t.cols, 0 if t.kind == "dense" else 1) for t in wl.tensors], cfg)
+    assert p.n_blocks == EXPECTED_BLOCKS[wid]
+    assert p.n_factors == 2 * p.n_blocks
+    ocfg = O.OracleConfig(block_size=wl.block_size, max_precond_dim=wl.max_precond_dim)
+    b = 0
+    for ti, t in enumerate(wl.tensors):
+        a_off, m_off, fb, nb = p.tensor(ti)
+        assert a_off >= 0 and a_off % 256 == 0
+        if t.kind == "sparse":
+            assert m_off == -1 and nb == 0
+            continue
+        assert m_off % 256 == 0
+        if not O.uses_shampoo(t.rows, t.cols, ocfg):
+            assert nb == 0
+            continue
+        assert fb == b
+        ob = O.blocks(t.rows, t.cols, wl.block_size)
+        assert nb == len(ob)
+        for (r0, mb, c0, ncol) in ob:
+            bl = p.block(b)
+            assert (bl.tensor, bl.row0, bl.rows, bl.col0, bl.cols) == (ti, r0, mb, c0, ncol)
+            assert bl.ld_l >= mb and bl.ld_r >= ncol and bl.ld_l % 32 == 0
+            assert (bl.factor_l, bl.factor_r) == (2 * b, 2 * b + 1)
+            b += 1
+    assert b == p.n_blocks
+    p.close()
+
+
+def test_state_regions_do_not_overlap():
+    """Every byte range the layout hands out is disjoint and inside the state."""
+    T = synth.TensorSpec
+    wl = synth.Workload(90, "mix", [T("a", 300, 200), T("b", 64, 147), T("e", 5000, 64),
+                                   T("s", 1000, 32, kind="sparse")], 128, max_precond_dim=4096)
+    cfg = S.make_config(128, root_mode="auto")
+    p = S.Plan([(t.rows, t.cols, 0 if t.kind == "dense" else 1) for t in wl.tensors], cfg)
+    spans = []
+    for i in range(p.n_blocks):
+        bl = p.block(i)
+        spans += [(bl.off_l, bl.ld_l ** 2 * 8), (bl.off_r, bl.ld_r ** 2 * 8),
+                  (bl.off_pl, bl.ld_l ** 2 * 4), (bl.off_pr, bl.ld_r ** 2 * 4),
+                  (bl.off_pl64, bl.ld_l ** 2 * 8), (bl.off_pr64, bl.ld_r ** 2 * 8)]
+    for ti, t in enumerate(wl.tensors):
+        a_off, m_off, _, _ = p.tensor(ti)
+        spans.append((a_off, t.numel * 4))
+        if m_off >= 0:
+            spans.append((m_off, t.numel * 4))
+    spans.sort()
+    for (o1, n1), (o2, _) in zip(spans, spans[1:]):
+        assert o1 + n1 <= o2
+    assert spans[-1][0] + spans[-1][1] <= p.state_bytes
+    p.close()
