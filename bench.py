@@ -239,11 +239,16 @@ def main():
 
     stages = {}
     fp64_share = n64 / max(len(diag), 1)
-    root_dims = [d.dim for d in diag]
-    flops_f32_root = sum((2 + int(round(math.log2(wl.root_p)))) * 2.0 * n ** 3 * wl.newton_iters
-                         for n in root_dims) if wl.root_mode != "f64" else 0.0
-    flops_f64_root = sum((2 + int(round(math.log2(wl.root_p)))) * 2.0 * d.dim ** 3 *
-                         wl.newton_iters for d in diag if d.status & S.FACTOR_FP64)
+    gpi = 2 + int(round(math.log2(wl.root_p)))      # GEMMs per coupled-Newton iteration
+    lds = []
+    for b in range(opt.n_blocks):
+        bl = opt.block(b)
+        lds += [bl.ld_l, bl.ld_r]
+    fl = [gpi * 2.0 * d.dim ** 3 * wl.newton_iters for d in diag]
+    f32 = wl.root_mode != "f64"
+    flops_fused_root = sum(x for x, ld in zip(fl, lds) if f32 and ld <= 128)
+    flops_f32_root = sum(x for x, ld in zip(fl, lds) if f32 and ld > 128)
+    flops_f64_root = sum(x for x, d in zip(fl, diag) if d.status & S.FACTOR_FP64)
     alg = {
         # name: (work per launch, unit, bound, peak)
         "stats_gram_f64": (wm["gram"], "TFLOP/s", "mfma", PEAK_TFLOPS["f64"]),
@@ -261,6 +266,9 @@ def main():
         work = None
         if name in alg:
             work, unit, bound, peak = alg[name]
+        elif name == "newton_fused_f32" and flops_fused_root > 0:
+            work = flops_fused_root * n_root_passes / launches
+            unit, bound, peak = "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]
         elif name == "newton_gemm_f32" and flops_f32_root > 0:
             work = flops_f32_root * n_root_passes / launches
             unit, bound, peak = "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]
@@ -293,7 +301,7 @@ def main():
 
     root_ms = sum(prof.get(n, (0, 0.0))[1] for n in
                   ("lanczos_stats", "lanczos_roots", "newton_init", "newton_gemm_f32",
-                   "newton_gemm_f64", "newton_commit"))
+                   "newton_gemm_f64", "newton_commit", "newton_fused_f32"))
     inv_root_blocks_per_s = (opt.n_blocks * n_root_passes / (root_ms / 1e3)) if root_ms > 0 else None
     mfma_pct = {k: round(100 * v["frac"], 2) for k, v in stages.items() if v.get("bound") == "mfma"}
 

@@ -63,6 +63,7 @@ struct LaunchRef {
 struct NewtonChunk {
     int ld = 0;
     int njobs = 0;
+    bool fused = false;                      // fp32, ld <= 128: one kernel, no scratch
     int64_t jobs_off = 0;                    // FactorJob table (bytes)
     std::vector<LaunchRef> stages[2];        // per parity
 };
@@ -82,12 +83,13 @@ struct Blob {
 
 enum ProfCat : int {
     PC_STATS = 0, PC_LANCZOS_S, PC_LANCZOS_P, PC_NEWTON_INIT, PC_NEWTON_GEMM32, PC_NEWTON_GEMM64,
-    PC_NEWTON_COMMIT, PC_ADAGRAD, PC_APPLY_T, PC_APPLY_D, PC_SCALE, PC_UPDATE, PC_SPARSE, PC_COUNT
+    PC_NEWTON_COMMIT, PC_ADAGRAD, PC_APPLY_T, PC_APPLY_D, PC_SCALE, PC_UPDATE, PC_SPARSE,
+    PC_NEWTON_FUSED, PC_COUNT
 };
 const char* const kProfNames[PC_COUNT] = {
     "stats_gram_f64", "lanczos_stats", "lanczos_roots", "newton_init", "newton_gemm_f32",
     "newton_gemm_f64", "newton_commit", "adagrad_norm", "apply_gemm_t", "apply_gemm_d",
-    "block_scale", "update", "sparse_rows"};
+    "block_scale", "update", "sparse_rows", "newton_fused_f32"};
 
 struct ProfRec {
     int cat;
@@ -111,7 +113,9 @@ struct shampoo_s {
     int n_partA = 0, n_partD = 0;
     Blob blob;  // static tables (offsets relative to off_tables)
 
-    LaunchRef gram, apply1, apply2;
+    LaunchRef gram, apply1, apply2;   // gram: blocks with a side > 128
+    int64_t gram128_off = 0;
+    int n_gram128 = 0;                // blocks of at most 128 x 128
     int64_t lanczos_s_off = 0, lanczos_p_off = 0, ident_jobs_off = 0;
     int64_t blockchunks_off = 0, blocknorms_off = 0, rowchunks_off = 0;
     int n_blockchunks = 0, n_rowchunks = 0;
@@ -162,7 +166,7 @@ int newton_stage_count(int p) {  // GEMM launches per iteration
 
 // Builds the per-parity GEMM launches of one Newton chunk.
 void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& fids, int ld,
-                        bool fp64, int64_t scratch_off_bytes) {
+                        bool fp64, bool fused, int64_t scratch_off_bytes) {
     const int p = h->cfg.root_p;
     const int64_t esz = fp64 ? 8 : 4;
     const int64_t mat = (int64_t)ld * ld;
@@ -186,6 +190,8 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
         jobs.push_back(j);
     }
     ch.jobs_off = h->blob.add(jobs);
+    ch.fused = fused;
+    if (fused) return;
 
     auto mk = [&](int64_t a, int64_t b, int64_t c, int trans, int fid) {
         GemmTask t{};
@@ -344,7 +350,7 @@ int build_plan(shampoo_s* h) {
     std::sort(lds.begin(), lds.end());
     lds.erase(std::unique(lds.begin(), lds.end()), lds.end());
     int64_t scr32 = 0, scr64 = 0;
-    struct Pending { int ld; std::vector<int> fids; bool fp64; };
+    struct Pending { int ld; std::vector<int> fids; bool fp64; bool fused; };
     std::vector<Pending> pend;
     for (int ld : lds) {
         std::vector<int> fids;
@@ -353,12 +359,17 @@ int build_plan(shampoo_s* h) {
         for (int prec = 0; prec < 2; ++prec) {
             const bool fp64 = prec == 1;
             if ((fp64 && !use_fp64(c)) || (!fp64 && !use_fp32(c))) continue;
+            if (!fp64 && ld <= 128) {   // fused LDS-resident kernel, no scratch
+                pend.push_back(Pending{ld, fids, false, true});
+                continue;
+            }
             const int64_t per = 6 * (int64_t)ld * ld * (fp64 ? 8 : 4);
             const int cap = (int)std::max<int64_t>(1, (int64_t)kNewtonScratchBudget / per);
             for (size_t s = 0; s < fids.size(); s += cap) {
                 Pending pd;
                 pd.ld = ld;
                 pd.fp64 = fp64;
+                pd.fused = false;
                 pd.fids.assign(fids.begin() + s, fids.begin() + std::min(fids.size(), s + cap));
                 int64_t& scr = fp64 ? scr64 : scr32;
                 scr = std::max(scr, per * (int64_t)pd.fids.size());
@@ -372,13 +383,30 @@ int build_plan(shampoo_s* h) {
 
     // ---- static tables
     Blob& blob = h->blob;
-    // statistics: L = beta2 L + w G G^T, R = beta2 R + w G^T G (cue 10)
+    // statistics: L = beta2 L + w G G^T, R = beta2 R + w G^T G (cue 10).
+    // Blocks of at most 128 x 128 go to the fused kernel, larger ones to the
+    // batched GEMM (two tasks per block).
     {
         std::vector<GemmTask> tasks;
+        std::vector<GramJob> small;
         for (auto& bp : h->blocks) {
             const TensorPlan& tp = h->tensors[bp.tensor];
             const FactorPlan& fl = h->factors[bp.fl];
             const FactorPlan& fr = h->factors[bp.fr];
+            if (bp.mb <= 128 && bp.nb <= 128) {
+                GramJob j{};
+                j.g_base = 1 + bp.tensor;
+                j.g_off = (int64_t)bp.r0 * tp.cols + bp.c0;
+                j.ldg = (int)tp.cols;
+                j.mb = bp.mb;
+                j.nb = bp.nb;
+                j.l_off = fl.off_s / 8;
+                j.r_off = fr.off_s / 8;
+                j.ld_l = fl.ld;
+                j.ld_r = fr.ld;
+                small.push_back(j);
+                continue;
+            }
             GemmTask t{};
             t.a_base = t.b_base = 1 + bp.tensor;
             t.a_off = t.b_off = (int64_t)bp.r0 * tp.cols + bp.c0;
@@ -404,6 +432,8 @@ int build_plan(shampoo_s* h) {
             tasks.push_back(t);
         }
         h->gram = add_launch(blob, tasks);
+        h->n_gram128 = (int)small.size();
+        h->gram128_off = blob.add(small);
     }
     // apply: T = G_b P_R, then D = P_L T with ||D||^2 partials (cue 10)
     {
@@ -470,7 +500,8 @@ int build_plan(shampoo_s* h) {
     }
     for (auto& pd : pend) {
         NewtonChunk ch;
-        build_newton_chunk(h, ch, pd.fids, pd.ld, pd.fp64, pd.fp64 ? h->off_scr64 : h->off_scr32);
+        build_newton_chunk(h, ch, pd.fids, pd.ld, pd.fp64, pd.fused,
+                           pd.fp64 ? h->off_scr64 : h->off_scr32);
         (pd.fp64 ? h->chunks64 : h->chunks32).push_back(std::move(ch));
     }
     // elementwise tables
@@ -770,6 +801,10 @@ int shampoo_update_stats(shampoo_t* h, const float* const* grads, void* stream) 
     // statistics keep the near-null spectrum that fp32 storage would round
     // into the eps damping)
     ProfScope ps(h, PC_STATS, s);
+    int rc2 = hip_err(launch_gram128(tab<GramJob>(h, h->gram128_off), h->n_gram128,
+                                     at<uint64_t>(h, h->off_bases), at<double>(h, 0), a.alpha,
+                                     a.beta, s));
+    if (rc2) return rc2;
     return hip_err(launch_gemm_f64_from_f32(tab<GemmTask>(h, h->gram.tasks_off),
                                             tab<TileRef>(h, h->gram.tiles_off), h->gram.ntiles,
                                             at<uint64_t>(h, h->off_bases), a, s));
@@ -798,6 +833,13 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
     for (auto& ch : chunks) {
         const FactorJob* jobs = tab<FactorJob>(h, ch.jobs_off);
         int rc;
+        if (ch.fused) {
+            ProfScope ps(h, PC_NEWTON_FUSED, s);
+            rc = hip_err(launch_newton128(jobs, ch.njobs, at<double>(h, 0), at<float>(h, 0), diag,
+                                          p, h->cfg.newton_iters, s));
+            if (rc) return rc;
+            continue;
+        }
         {
             ProfScope ps(h, PC_NEWTON_INIT, s);
             rc = hip_err(launch_newton_init(fp64, jobs, ch.njobs, at<double>(h, 0), scratch, diag, na, s));
@@ -855,6 +897,7 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
         if (rc) return rc;
         LanczosArgs lp = la;
         lp.mode = 1;
+        lp.steps = std::min(c.lanczos_steps, 16);  // kappa estimate: a factor-2 decision
         lp.auto_route = c.root_mode == SHAMPOO_ROOT_AUTO ? 1 : 0;
         {
             ProfScope ps(h, PC_LANCZOS_P, s);
@@ -869,6 +912,7 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
         if (!use_fp32(c)) {
             LanczosArgs lp = la;
             lp.mode = 1;
+            lp.steps = std::min(c.lanczos_steps, 16);
             lp.auto_route = 0;
             ProfScope ps(h, PC_LANCZOS_P, s);
             rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_p_off), nf, h->arena, false, lp, s));

@@ -27,6 +27,16 @@ struct GemmTask {
     int32_t pad_;
 };
 
+// One Shampoo block of at most 128 x 128 for the fused statistics kernel.
+struct GramJob {
+    int64_t g_off;        // element offset of G_b in its base (the tensor's gradient)
+    int64_t l_off, r_off; // fp64 statistics (arena elements of 8 bytes)
+    int32_t g_base;       // base index of the gradient
+    int32_t ldg;          // tensor row length
+    int32_t mb, nb;       // block shape
+    int32_t ld_l, ld_r;   // leading dims of L and R
+};
+
 // A tile of the batched GEMM launch: which task and which 128x128 tile.
 struct TileRef {
     int32_t task;

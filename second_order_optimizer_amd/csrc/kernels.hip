@@ -345,6 +345,138 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmTask* __restrict__ tasks
     }
 }
 
+// ====================================================== statistics <= 128
+// L <- beta L + alpha G G^T and R <- beta R + alpha G^T G for one block of at
+// most 128 x 128 per workgroup: G is read from HBM once into LDS (fp32,
+// zero-padded to 128 x 128) and both products run on fp64 MFMA
+// (v_mfma_f64_16x16x4f64) from that copy; fp32 x fp32 products are exact in
+// fp64.  Each wave owns a 64 x 64 quadrant of the output.
+constexpr int kGP = 132;  // LDS row pitch (floats): 16-byte aligned rows
+
+__global__ __launch_bounds__(256, 2) void k_gram128(const GramJob* __restrict__ jobs,
+                                                   const uint64_t* __restrict__ bases,
+                                                   double* __restrict__ stats, double alpha,
+                                                   double beta) {
+    __shared__ __align__(16) float Gs[128 * kGP];
+    const GramJob jb = jobs[blockIdx.x];
+    const float* G = reinterpret_cast<const float*>(bases[jb.g_base]) + jb.g_off;
+    const int t = threadIdx.x;
+    const int mb = jb.mb, nb = jb.nb, ld = jb.ldg;
+
+    // ---- stage G (rows x cols) into LDS, zero padded
+    const bool vec = (nb % 4 == 0) && (ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(G) & 15) == 0);
+    {
+        const int c4 = t & 31, r0 = t >> 5;   // 32 float4 per row, 8 rows per pass
+        float4 buf[16];
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+            const int r = r0 + 8 * p, c = 4 * c4;
+            if (r < mb && c < nb) {
+                if (vec) {
+                    buf[p] = *reinterpret_cast<const float4*>(G + (int64_t)r * ld + c);
+                } else {
+                    buf[p].x = G[(int64_t)r * ld + c];
+                    buf[p].y = (c + 1 < nb) ? G[(int64_t)r * ld + c + 1] : 0.f;
+                    buf[p].z = (c + 2 < nb) ? G[(int64_t)r * ld + c + 2] : 0.f;
+                    buf[p].w = (c + 3 < nb) ? G[(int64_t)r * ld + c + 3] : 0.f;
+                }
+            } else {
+                buf[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < 16; ++p)
+            *reinterpret_cast<float4*>(&Gs[(r0 + 8 * p) * kGP + 4 * c4]) = buf[p];
+    }
+    __syncthreads();
+
+    const int lane = t & 63, w = t >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int c = lane & 15, g = lane >> 4;
+    typedef double d4 __attribute__((ext_vector_type(4)));
+    typedef float f4 __attribute__((ext_vector_type(4)));
+
+    // ---- L = G G^T: A[i][k] = G[i][k], B[k][j] = G[j][k].  Lane group g
+    // supplies k = k0 + 4g + s in MFMA step s, so each lane reads four
+    // consecutive k of one row at once.
+    if (true) {
+        d4 acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = d4{0.0, 0.0, 0.0, 0.0};
+        const int K = (nb + 15) & ~15;
+        for (int k0 = 0; k0 < K; k0 += 16) {
+            f4 a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a[i] = *reinterpret_cast<const f4*>(&Gs[(wm * 64 + i * 16 + c) * kGP + k0 + 4 * g]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                b[j] = *reinterpret_cast<const f4*>(&Gs[(wn * 64 + j * 16 + c) * kGP + k0 + 4 * g]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[i][s], (double)b[j][s],
+                                                                        acc[i][j], 0, 0, 0);
+        }
+        double* L = stats + jb.l_off;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = wm * 64 + i * 16 + g + 4 * v, q = wn * 64 + j * 16 + c;
+                    if (r < mb && q < mb) {
+                        double* p = L + (int64_t)r * jb.ld_l + q;
+                        *p = alpha * acc[i][j][v] + beta * (*p);
+                    }
+                }
+    }
+    // ---- R = G^T G: A[i][k] = G[k][i], B[k][j] = G[k][j] (column reads)
+    {
+        d4 acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = d4{0.0, 0.0, 0.0, 0.0};
+        const int K = (mb + 15) & ~15;
+        for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float* row = &Gs[(k0 + 4 * g + s) * kGP];
+                double a[4], b[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] = (double)row[wm * 64 + i * 16 + c];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[j] = (double)row[wn * 64 + j * 16 + c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+            }
+        }
+        double* R = stats + jb.r_off;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = wm * 64 + i * 16 + g + 4 * v, q = wn * 64 + j * 16 + c;
+                    if (r < nb && q < nb) {
+                        double* p = R + (int64_t)r * jb.ld_r + q;
+                        *p = alpha * acc[i][j][v] + beta * (*p);
+                    }
+                }
+    }
+}
+
 // ================================================================ Lanczos
 // Extreme Ritz values of a symmetric matrix from `steps` Lanczos steps (no
 // reorthogonalisation: lost orthogonality only duplicates converged extreme
@@ -367,18 +499,29 @@ __device__ int sturm_count(const double* al, const double* be, int m, double x) 
     return cnt;
 }
 
+constexpr int kLanczosLdsN = 128;   // matrices up to this size are staged in LDS
+
 template <typename TM>
 __global__ __launch_bounds__(256) void k_lanczos(const LanczosJob* __restrict__ jobs,
                                                 const TM* __restrict__ arena, LanczosArgs args) {
     __shared__ double v0[kLanczosMaxN], v1[kLanczosMaxN], wv[kLanczosMaxN];
     __shared__ double al[kLanczosMaxSteps], be[kLanczosMaxSteps];
     __shared__ double red[4];
+    __shared__ float Ss[kLanczosLdsN * (kLanczosLdsN + 1)];
     __shared__ int m_used;
     const LanczosJob jb = jobs[blockIdx.x];
     const int n = jb.n, ld = jb.ld;
     const TM* S = arena + jb.off;
     const int t = threadIdx.x;
     const int steps = min(args.steps, min(n, kLanczosMaxSteps));
+    const bool in_lds = n <= kLanczosLdsN;
+    constexpr int SP = kLanczosLdsN + 1;  // LDS pitch: row r, column j at bank r + j
+    if (in_lds) {
+        for (int e = t; e < n * n; e += 256) {
+            const int i = e / n, j = e % n;
+            Ss[i * SP + j] = (float)S[(int64_t)i * ld + j];
+        }
+    }
 
     // deterministic start vector from an integer hash, normalised
     double s2 = 0.0;
@@ -398,10 +541,22 @@ __global__ __launch_bounds__(256) void k_lanczos(const LanczosJob* __restrict__ 
     double beta_prev = 0.0;
     for (int k = 0; k < steps; ++k) {
         // w = S v
-        for (int j = t; j < n; j += 256) {
+        if (in_lds) {
+            // thread (r, half) sums row r over one half of the columns
+            const int r = t & 127, hf = t >> 7;
+            const int j0 = hf * ((n + 1) / 2), j1 = min(n, j0 + (n + 1) / 2);
             double acc = 0.0;
-            for (int i = 0; i < n; ++i) acc += (double)S[(int64_t)i * ld + j] * v1[i];
-            wv[j] = acc;
+            if (r < n)
+                for (int j = j0; j < j1; ++j) acc += (double)Ss[r * SP + j] * v1[j];
+            if (hf == 1 && r < n) wv[r] = acc;
+            __syncthreads();
+            if (hf == 0 && r < n) wv[r] += acc;
+        } else {
+            for (int j = t; j < n; j += 256) {
+                double acc = 0.0;
+                for (int i = 0; i < n; ++i) acc += (double)S[(int64_t)i * ld + j] * v1[i];
+                wv[j] = acc;
+            }
         }
         __syncthreads();
         double d = 0.0;
@@ -568,6 +723,212 @@ __global__ __launch_bounds__(256) void k_newton_commit(const FactorJob* __restri
         else st &= ~SHAMPOO_FACTOR_FP64_;
         dg.status = st;
         dg.residual = (st0 == 0) ? res : 0.0;
+    }
+}
+
+// ------------------------------------------- fused fp32 Newton, n <= 128
+// The whole coupled iteration of one factor (padded to 128) in one
+// workgroup: the iterates stay in two LDS slots (128 x 129 fp32, 132 KB) and
+// in registers, so HBM is touched only to read S and write P.  Wave w owns
+// rows [32w, 32w+32) of every product, as 4 tiles of 32 x 32
+// (v_mfma_f32_32x32x2f32; C lane l reg v = C[8(v/4) + 4(l/32) + v%4][l%32]).
+// Per iteration (p = 4): X' = X T, T2 = T T, T4 = T2 T2, M' = T4 M with
+// T = c1 I + c2 M; the arithmetic (initial rounding, operand transform, k
+// order) is that of the batched path, so both give the same bits.
+constexpr int kNP = 129;  // LDS pitch (floats): row r, column j at bank r + j
+
+struct Strip {
+    float v[4][16];
+};
+
+__device__ __forceinline__ int strip_row(int w, int h, int v) {
+    return 32 * w + 8 * (v >> 2) + 4 * h + (v & 3);
+}
+
+// acc[q] += A[32w.., :] * B[:, 32q..]  (A, B in LDS, pitch kNP)
+template <int NA>
+__device__ __forceinline__ void strip_gemm(const float* const (&As)[NA], const float* Bs,
+                                           Strip (&acc)[NA], int w, int h, int c) {
+    typedef float f16v __attribute__((ext_vector_type(16)));
+    f16v r[NA][4];
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) r[a][q][v] = 0.f;
+#pragma unroll 4
+    for (int k0 = 0; k0 < 128; k0 += 2) {
+        float b[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) b[q] = Bs[(k0 + h) * kNP + 32 * q + c];
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+            const float av = As[a][(32 * w + c) * kNP + k0 + h];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                r[a][q] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b[q], r[a][q], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[a].v[q][v] = r[a][q][v];
+}
+
+__device__ __forceinline__ void strip_store(float* S, const Strip& x, int w, int h, int c) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) S[strip_row(w, h, v) * kNP + 32 * q + c] = x.v[q][v];
+}
+
+// T = c1 I + c2 M on a strip
+__device__ __forceinline__ void strip_newton_T(Strip& T, const Strip& M, float c1, float c2, int w,
+                                               int h, int c) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            T.v[q][v] = c2 * M.v[q][v] + ((strip_row(w, h, v) == 32 * q + c) ? c1 : 0.f);
+}
+
+__global__ __launch_bounds__(256, 1) void k_newton128(const FactorJob* __restrict__ jobs,
+                                                     const double* __restrict__ stats,
+                                                     float* __restrict__ arena,
+                                                     FactorDiag* __restrict__ diag, int p, int iters) {
+    __shared__ __align__(16) float S0[128 * kNP];
+    __shared__ __align__(16) float S1[128 * kNP];
+    __shared__ double red[4];
+    const FactorJob jb = jobs[blockIdx.x];
+    const FactorDiag dg = diag[jb.factor];
+    const int n = jb.n, ld = jb.ld;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int h = lane >> 5, c = lane & 31;
+    const int st0 = dg.status & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_ZERO_);
+    const bool ok = st0 == 0;
+    const double lam = dg.lambda_max + dg.eps;
+    const float z = ok ? float((p + 1) / (2.0 * lam)) : 1.f;
+    const float zr = ok ? float(pow((p + 1) / (2.0 * lam), 1.0 / p)) : 1.f;
+    const float e = float(dg.eps);
+    const float c1 = float((double)(p + 1) / p), c2 = float(-1.0 / p);
+
+    // ---- S (fp64) -> LDS as one fp64 matrix spanning both slots, then
+    // M0 = z (sym(S) + eps I) in registers; padding rows/columns are identity
+    double* Sd = reinterpret_cast<double*>(S0);   // 128 x 129 doubles = both slots
+    const double* Sg = stats + jb.s_off;
+    if (ok) {
+        for (int e2 = t; e2 < 128 * 128; e2 += 256) {
+            const int i = e2 >> 7, j = e2 & 127;
+            Sd[i * kNP + j] = (i < n && j < n) ? Sg[(int64_t)i * ld + j] : 0.0;
+        }
+    }
+    __syncthreads();
+    Strip M, X;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int i = strip_row(w, h, v), j = 32 * q + c;
+            float m, x;
+            if (i < n && j < n && ok) {
+                const float sv = float(0.5 * (Sd[i * kNP + j] + Sd[j * kNP + i]));
+                m = z * (sv + (i == j ? e : 0.f));
+                x = (i == j) ? zr : 0.f;
+            } else {
+                m = (i == j) ? 1.f : 0.f;
+                x = (i == j) ? 1.f : 0.f;
+            }
+            M.v[q][v] = m;
+            X.v[q][v] = x;
+        }
+    __syncthreads();   // Sd (aliasing S0/S1) is dead from here on
+    Strip T;
+    strip_newton_T(T, M, c1, c2, w, h, c);
+    strip_store(S0, T, w, h, c);
+    strip_store(S1, X, w, h, c);
+    __syncthreads();
+
+    for (int it = 0; it < iters; ++it) {
+        // X' = X T and T2 = T T (B operand T shared)
+        Strip acc2[2];
+        {
+            const float* As[2] = {S1, S0};
+            strip_gemm<2>(As, S0, acc2, w, h, c);
+        }
+        X = acc2[0];
+        Strip Tp = acc2[1];          // T^2
+        // further squarings: T^4, T^8 (p = 4, 8); p = 1 uses T itself
+        if (p == 1) Tp = T;
+        for (int e2 = 2; e2 < p; e2 *= 2) {
+            __syncthreads();         // everyone is done reading S1 (X) and S0 (T)
+            strip_store(S1, Tp, w, h, c);
+            __syncthreads();
+            Strip sq[1];
+            const float* As[1] = {S1};
+            strip_gemm<1>(As, S1, sq, w, h, c);
+            Tp = sq[0];
+        }
+        // M' = T^p M
+        __syncthreads();
+        strip_store(S0, Tp, w, h, c);
+        strip_store(S1, M, w, h, c);
+        __syncthreads();
+        {
+            Strip mm[1];
+            const float* As[1] = {S0};
+            strip_gemm<1>(As, S1, mm, w, h, c);
+            M = mm[0];
+        }
+        strip_newton_T(T, M, c1, c2, w, h, c);
+        __syncthreads();
+        strip_store(S0, T, w, h, c);
+        strip_store(S1, X, w, h, c);
+        __syncthreads();
+    }
+
+    // ---- commit: residual max |M - I|, finiteness, write P (or keep / identity)
+    double res = 0.0, bad = 0.0;
+    if (ok) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int i = strip_row(w, h, v), j = 32 * q + c;
+                if (i < n && j < n) {
+                    const double xv = X.v[q][v];
+                    const double r = fabs(double(M.v[q][v]) - (i == j ? 1.0 : 0.0));
+                    if (!isfinite(xv) || !isfinite(r)) bad = 1.0;
+                    res = fmax(res, r);
+                }
+            }
+    }
+    res = block_max_256(res, red);
+    bad = block_max_256(bad, red);
+    int st = st0;
+    if (ok && bad > 0.0) st |= SHAMPOO_FACTOR_NONFINITE_ROOT_;
+    const bool keep = (st & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_NONFINITE_ROOT_)) != 0;
+    if (!keep) {
+        const bool ident = (st & SHAMPOO_FACTOR_ZERO_) != 0;
+        float* P = arena + jb.p_off;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int i = strip_row(w, h, v), j = 32 * q + c;
+                if (i < ld && j < ld) {
+                    const float xv = (ident || i >= n || j >= n) ? ((i == j) ? 1.f : 0.f) : X.v[q][v];
+                    P[(int64_t)i * ld + j] = xv;
+                }
+            }
+    }
+    if (t == 0) {
+        if (!keep && !(st & SHAMPOO_FACTOR_ZERO_) && res > 1e-2) st |= SHAMPOO_FACTOR_RESIDUAL_HIGH_;
+        st &= ~SHAMPOO_FACTOR_FP64_;
+        diag[jb.factor].status = st;
+        diag[jb.factor].residual = ok ? res : 0.0;
     }
 }
 
@@ -776,9 +1137,17 @@ hipError_t launch_gemm_f64_from_f32(const GemmTask* tasks, const TileRef* tiles,
                        tiles, bases, a);
     return hipGetLastError();
 }
+hipError_t launch_gram128(const GramJob* jobs, int njobs, const uint64_t* bases, double* stats,
+                          double alpha, double beta, hipStream_t s) {
+    if (njobs <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_gram128, dim3(njobs), dim3(256), 0, s, jobs, bases, stats, alpha, beta);
+    return hipGetLastError();
+}
 hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, bool fp64_matrix,
                           const LanczosArgs& a, hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
+    // the kernel works on a fixed-size LDS layout; guard its limits here
+    if (a.steps < 1) return hipErrorInvalidValue;
     if (fp64_matrix)
         hipLaunchKernelGGL(k_lanczos<double>, dim3(njobs), dim3(256), 0, s, jobs,
                            static_cast<const double*>(arena), a);
@@ -809,6 +1178,13 @@ hipError_t launch_newton_commit(bool fp64, const FactorJob* jobs, int njobs, flo
     else
         hipLaunchKernelGGL(k_newton_commit<float>, dim3(njobs), dim3(256), 0, s, jobs, arena,
                            static_cast<const float*>(scratch), diag, a);
+    return hipGetLastError();
+}
+hipError_t launch_newton128(const FactorJob* jobs, int njobs, const double* stats, float* arena,
+                            FactorDiag* diag, int p, int iters, hipStream_t s) {
+    if (njobs <= 0) return hipSuccess;
+    if (p != 1 && p != 2 && p != 4 && p != 8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_newton128, dim3(njobs), dim3(256), 0, s, jobs, stats, arena, diag, p, iters);
     return hipGetLastError();
 }
 hipError_t launch_set_identity(const FactorJob* jobs, int njobs, float* arena, hipStream_t s) {

@@ -56,6 +56,8 @@ hipError_t launch_gemm_f64(const GemmTask* tasks, const TileRef* tiles, int ntil
                            const uint64_t* bases, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f64_from_f32(const GemmTask* tasks, const TileRef* tiles, int ntiles,
                                     const uint64_t* bases, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gram128(const GramJob* jobs, int njobs, const uint64_t* bases, double* stats,
+                          double alpha, double beta, hipStream_t s);
 hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, bool fp64_matrix,
                           const LanczosArgs& a, hipStream_t s);
 hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, const double* stats,
@@ -64,6 +66,8 @@ hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, const
 hipError_t launch_newton_commit(bool fp64, const FactorJob* jobs, int njobs, float* arena,
                                 const void* scratch, FactorDiag* diag, const NewtonArgs& a,
                                 hipStream_t s);
+hipError_t launch_newton128(const FactorJob* jobs, int njobs, const double* stats, float* arena,
+                            FactorDiag* diag, int p, int iters, hipStream_t s);
 hipError_t launch_set_identity(const FactorJob* jobs, int njobs, float* arena, hipStream_t s);
 hipError_t launch_adagrad_norm(const BlockChunk* chunks, int nchunks, const uint64_t* bases,
                                float* arena, float delta, double* partA, hipStream_t s);
