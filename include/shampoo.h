@@ -131,7 +131,9 @@ typedef struct {
     int32_t rows, cols;   /* m_b, n_b (ragged at the edges)                            */
     int32_t ld_l, ld_r;   /* leading dimension (padded) of the L- and R-side matrices  */
     int32_t factor_l, factor_r; /* factor indices (diagnostics order)                 */
-    int64_t off_l, off_r;       /* fp64 statistics L (rows x rows), R (cols x cols)   */
+    int64_t off_l, off_r;       /* fp64 statistics L (rows x rows), R (cols x cols),
+                                   row-major with leading dims ld_l, ld_r; symmetric,
+                                   only the upper triangle (column >= row) is kept    */
     int64_t off_pl, off_pr;     /* fp32 roots P_L, P_R                                */
     int64_t off_pl64, off_pr64; /* fp64 roots, or -1 when root_mode is F32             */
 } shampoo_block_layout;

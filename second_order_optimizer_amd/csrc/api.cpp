@@ -116,7 +116,9 @@ struct shampoo_s {
     LaunchRef gram, apply1, apply2;   // gram: blocks with a side > 128
     int64_t gram128_off = 0;
     int n_gram128 = 0;                // blocks of at most 128 x 128
-    int64_t lanczos_s_off = 0, lanczos_p_off = 0, ident_jobs_off = 0;
+    int64_t lanczos_s_off = 0, lanczos_p_off = 0, ident_jobs_off = 0;   // every factor
+    int64_t lanczos_s_big_off = 0, lanczos_p_big_off = 0;               // factors with ld > 128
+    int n_lanczos_big = 0;
     int64_t blockchunks_off = 0, blocknorms_off = 0, rowchunks_off = 0;
     int n_blockchunks = 0, n_rowchunks = 0;
     std::vector<NewtonChunk> chunks32, chunks64;
@@ -496,6 +498,15 @@ int build_plan(shampoo_s* h) {
         }
         h->lanczos_s_off = blob.add(js);
         h->lanczos_p_off = blob.add(jp);
+        std::vector<LanczosJob> jsb, jpb;
+        for (int i = 0; i < nf; ++i)
+            if (h->factors[i].ld > 128) {
+                jsb.push_back(js[i]);
+                jpb.push_back(jp[i]);
+            }
+        h->n_lanczos_big = (int)jsb.size();
+        h->lanczos_s_big_off = blob.add(jsb);
+        h->lanczos_p_big_off = blob.add(jpb);
         h->ident_jobs_off = blob.add(ident);
     }
     for (auto& pd : pend) {
@@ -812,7 +823,7 @@ int shampoo_update_stats(shampoo_t* h, const float* const* grads, void* stream) 
 
 namespace {
 int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const int32_t* gate,
-               int gate_val, hipStream_t s) {
+               int gate_val, int32_t* prec, hipStream_t s) {
     const int p = h->cfg.root_p;
     NewtonArgs na{};
     na.p = p;
@@ -834,9 +845,19 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
         const FactorJob* jobs = tab<FactorJob>(h, ch.jobs_off);
         int rc;
         if (ch.fused) {
+            // lambda_max, eps, the root and the kappa estimate of every factor
+            // up to 128 in one kernel
+            FusedArgs fa{};
+            fa.p = p;
+            fa.iters = h->cfg.newton_iters;
+            fa.steps_s = h->cfg.lanczos_steps;
+            fa.steps_p = std::min(h->cfg.lanczos_steps, 16);
+            fa.auto_route = h->cfg.root_mode == SHAMPOO_ROOT_AUTO ? 1 : 0;
+            fa.eps_rel = h->cfg.eps_rel;
+            fa.threshold = h->cfg.fp64_cond_threshold;
             ProfScope ps(h, PC_NEWTON_FUSED, s);
             rc = hip_err(launch_newton128(jobs, ch.njobs, at<double>(h, 0), at<float>(h, 0), diag,
-                                          p, h->cfg.newton_iters, s));
+                                          prec, fa, s));
             if (rc) return rc;
             continue;
         }
@@ -886,40 +907,43 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
     la.diag = diag;
     la.prec = prec;
     la.route_all_fp64 = c.root_mode == SHAMPOO_ROOT_F64 ? 1 : 0;
-    int rc;
+    LanczosArgs lp = la;
+    lp.mode = 1;
+    lp.steps = std::min(c.lanczos_steps, 16);  // kappa estimate: a factor-2 decision
+    int rc = SHAMPOO_OK;
+    if (use_fp32(c)) {
+        // factors up to 128: everything inside the fused kernel; larger ones:
+        // Lanczos on S, batched fp32 Newton, Lanczos on the root
+        {
+            ProfScope ps(h, PC_LANCZOS_S, s);
+            rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_s_big_off), h->n_lanczos_big,
+                                        h->arena, true, la, s));
+        }
+        if (rc) return rc;
+        rc = run_newton(h, h->chunks32, false, nullptr, 0, prec, s);
+        if (rc) return rc;
+        lp.auto_route = c.root_mode == SHAMPOO_ROOT_AUTO ? 1 : 0;
+        {
+            ProfScope ps(h, PC_LANCZOS_P, s);
+            rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_p_big_off), h->n_lanczos_big,
+                                        h->arena, false, lp, s));
+        }
+        if (rc) return rc;
+        if (c.root_mode == SHAMPOO_ROOT_AUTO)
+            rc = run_newton(h, h->chunks64, true, prec, 1, prec, s);
+        return rc;
+    }
+    // all fp64
     {
         ProfScope ps(h, PC_LANCZOS_S, s);
         rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_s_off), nf, h->arena, true, la, s));
     }
     if (rc) return rc;
-    if (use_fp32(c)) {
-        rc = run_newton(h, h->chunks32, false, nullptr, 0, s);
-        if (rc) return rc;
-        LanczosArgs lp = la;
-        lp.mode = 1;
-        lp.steps = std::min(c.lanczos_steps, 16);  // kappa estimate: a factor-2 decision
-        lp.auto_route = c.root_mode == SHAMPOO_ROOT_AUTO ? 1 : 0;
-        {
-            ProfScope ps(h, PC_LANCZOS_P, s);
-            rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_p_off), nf, h->arena, false, lp, s));
-        }
-        if (rc) return rc;
-    }
-    if (use_fp64(c)) {
-        const bool gated = c.root_mode == SHAMPOO_ROOT_AUTO;
-        rc = run_newton(h, h->chunks64, true, gated ? prec : nullptr, 1, s);
-        if (rc) return rc;
-        if (!use_fp32(c)) {
-            LanczosArgs lp = la;
-            lp.mode = 1;
-            lp.steps = std::min(c.lanczos_steps, 16);
-            lp.auto_route = 0;
-            ProfScope ps(h, PC_LANCZOS_P, s);
-            rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_p_off), nf, h->arena, false, lp, s));
-            if (rc) return rc;
-        }
-    }
-    return SHAMPOO_OK;
+    rc = run_newton(h, h->chunks64, true, nullptr, 1, prec, s);
+    if (rc) return rc;
+    lp.auto_route = 0;
+    ProfScope ps(h, PC_LANCZOS_P, s);
+    return hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_p_off), nf, h->arena, false, lp, s));
 }
 
 int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const float* const* grads,

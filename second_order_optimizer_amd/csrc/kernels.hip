@@ -350,8 +350,80 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmTask* __restrict__ tasks
 // most 128 x 128 per workgroup: G is read from HBM once into LDS (fp32,
 // zero-padded to 128 x 128) and both products run on fp64 MFMA
 // (v_mfma_f64_16x16x4f64) from that copy; fp32 x fp32 products are exact in
-// fp64.  Each wave owns a 64 x 64 quadrant of the output.
+// fp64.  L and R are symmetric, so only their upper triangles are formed and
+// stored: wave 0 takes the two diagonal 64 x 64 quadrants of L (10 of 16
+// 16x16 tiles each), wave 1 the off-diagonal quadrant of L, waves 2 and 3 the
+// same for R.  The lower triangle of the stored matrix is not maintained.
 constexpr int kGP = 132;  // LDS row pitch (floats): 16-byte aligned rows
+
+typedef double gd4 __attribute__((ext_vector_type(4)));
+typedef float gf4 __attribute__((ext_vector_type(4)));
+
+// One 64 x 64 quadrant (qi, qj) of L = G G^T (RSIDE = false) or R = G^T G.
+// DIAG: qi == qj, only tiles i <= j are formed.  Lane group g supplies
+// k = k0 + 4g + s in MFMA step s.
+template <bool DIAG, bool RSIDE>
+__device__ __forceinline__ void gram_quadrant(const float* Gs, int qi, int qj, int K, double* S,
+                                              int ldS, int nvalid, double alpha, double beta,
+                                              int c, int g) {
+    if (qi * 64 >= nvalid || qj * 64 >= nvalid) return;
+    gd4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = gd4{0.0, 0.0, 0.0, 0.0};
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        if (!RSIDE) {
+            gf4 a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a[i] = *reinterpret_cast<const gf4*>(&Gs[(qi * 64 + i * 16 + c) * kGP + k0 + 4 * g]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                b[j] = DIAG ? a[j]
+                            : *reinterpret_cast<const gf4*>(&Gs[(qj * 64 + j * 16 + c) * kGP + k0 + 4 * g]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (!DIAG || i <= j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+                                (double)a[i][s], (double)b[j][s], acc[i][j], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float* row = &Gs[(k0 + 4 * g + s) * kGP];
+                double a[4], b[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] = (double)row[qi * 64 + i * 16 + c];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[j] = DIAG ? a[j] : (double)row[qj * 64 + j * 16 + c];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (!DIAG || i <= j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (DIAG && i > j) continue;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = qi * 64 + i * 16 + g + 4 * v, q = qj * 64 + j * 16 + c;
+                if (r < nvalid && q < nvalid) {
+                    double* p = S + (int64_t)r * ldS + q;
+                    *p = alpha * acc[i][j][v] + beta * (*p);
+                }
+            }
+        }
+}
 
 __global__ __launch_bounds__(256, 2) void k_gram128(const GramJob* __restrict__ jobs,
                                                    const uint64_t* __restrict__ bases,
@@ -391,89 +463,20 @@ __global__ __launch_bounds__(256, 2) void k_gram128(const GramJob* __restrict__ 
     __syncthreads();
 
     const int lane = t & 63, w = t >> 6;
-    const int wm = w >> 1, wn = w & 1;
     const int c = lane & 15, g = lane >> 4;
-    typedef double d4 __attribute__((ext_vector_type(4)));
-    typedef float f4 __attribute__((ext_vector_type(4)));
-
-    // ---- L = G G^T: A[i][k] = G[i][k], B[k][j] = G[j][k].  Lane group g
-    // supplies k = k0 + 4g + s in MFMA step s, so each lane reads four
-    // consecutive k of one row at once.
-    if (true) {
-        d4 acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = d4{0.0, 0.0, 0.0, 0.0};
-        const int K = (nb + 15) & ~15;
-        for (int k0 = 0; k0 < K; k0 += 16) {
-            f4 a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = *reinterpret_cast<const f4*>(&Gs[(wm * 64 + i * 16 + c) * kGP + k0 + 4 * g]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                b[j] = *reinterpret_cast<const f4*>(&Gs[(wn * 64 + j * 16 + c) * kGP + k0 + 4 * g]);
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[i][s], (double)b[j][s],
-                                                                        acc[i][j], 0, 0, 0);
-        }
-        double* L = stats + jb.l_off;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int r = wm * 64 + i * 16 + g + 4 * v, q = wn * 64 + j * 16 + c;
-                    if (r < mb && q < mb) {
-                        double* p = L + (int64_t)r * jb.ld_l + q;
-                        *p = alpha * acc[i][j][v] + beta * (*p);
-                    }
-                }
-    }
-    // ---- R = G^T G: A[i][k] = G[k][i], B[k][j] = G[k][j] (column reads)
-    {
-        d4 acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = d4{0.0, 0.0, 0.0, 0.0};
-        const int K = (mb + 15) & ~15;
-        for (int k0 = 0; k0 < K; k0 += 16) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const float* row = &Gs[(k0 + 4 * g + s) * kGP];
-                double a[4], b[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) a[i] = (double)row[wm * 64 + i * 16 + c];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) b[j] = (double)row[wn * 64 + j * 16 + c];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
-            }
-        }
-        double* R = stats + jb.r_off;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int r = wm * 64 + i * 16 + g + 4 * v, q = wn * 64 + j * 16 + c;
-                    if (r < nb && q < nb) {
-                        double* p = R + (int64_t)r * jb.ld_r + q;
-                        *p = alpha * acc[i][j][v] + beta * (*p);
-                    }
-                }
+    const int KL = (nb + 15) & ~15, KR = (mb + 15) & ~15;
+    double* L = stats + jb.l_off;
+    double* R = stats + jb.r_off;
+    if (w == 0) {
+        gram_quadrant<true, false>(Gs, 0, 0, KL, L, jb.ld_l, mb, alpha, beta, c, g);
+        gram_quadrant<true, false>(Gs, 1, 1, KL, L, jb.ld_l, mb, alpha, beta, c, g);
+    } else if (w == 1) {
+        gram_quadrant<false, false>(Gs, 0, 1, KL, L, jb.ld_l, mb, alpha, beta, c, g);
+    } else if (w == 2) {
+        gram_quadrant<true, true>(Gs, 0, 0, KR, R, jb.ld_r, nb, alpha, beta, c, g);
+        gram_quadrant<true, true>(Gs, 1, 1, KR, R, jb.ld_r, nb, alpha, beta, c, g);
+    } else {
+        gram_quadrant<false, true>(Gs, 0, 1, KR, R, jb.ld_r, nb, alpha, beta, c, g);
     }
 }
 
@@ -499,6 +502,117 @@ __device__ int sturm_count(const double* al, const double* be, int m, double x) 
     return cnt;
 }
 
+// Largest eigenvalue of the m x m tridiagonal (al, be) by Sturm-count
+// multisection on one wave: every lane counts at its own point of the
+// bracket, so each round shrinks it 65-fold.  NaN for non-finite input.
+__device__ double tridiag_max_wave(const double* al, const double* be, int m) {
+    const int lane = threadIdx.x & 63;
+    double lo = 0.0, hi = 0.0;
+    bool finite = true;
+    for (int k = 0; k < m; ++k) {
+        const double r = (k ? fabs(be[k - 1]) : 0.0) + (k + 1 < m ? fabs(be[k]) : 0.0);
+        if (!isfinite(al[k]) || !isfinite(r)) finite = false;
+        lo = k ? fmin(lo, al[k] - r) : al[k] - r;
+        hi = k ? fmax(hi, al[k] + r) : al[k] + r;
+    }
+    if (!finite) return NAN;
+    for (int round = 0; round < 12; ++round) {
+        if (!(hi - lo > 1e-15 * fmax(fabs(lo), fabs(hi)))) break;
+        const double x = lo + (hi - lo) * (double)(lane + 1) / 65.0;
+        const bool above = sturm_count(al, be, m, x) >= m;   // x exceeds every eigenvalue
+        const uint64_t mask = __ballot(above);
+        if (mask == 0) {
+            lo = lo + (hi - lo) * 64.0 / 65.0;
+        } else {
+            const int f = __ffsll((unsigned long long)mask) - 1;
+            const double nlo = lo + (hi - lo) * (double)f / 65.0;
+            const double nhi = lo + (hi - lo) * (double)(f + 1) / 65.0;
+            lo = nlo;
+            hi = nhi;
+        }
+    }
+    return hi;
+}
+
+// Scratch of the in-LDS Lanczos (matrices of at most 128).
+struct LanczosLds {
+    double v0[128], v1[128], wv[128];
+    double al[kLanczosMaxSteps], be[kLanczosMaxSteps];
+    double res;
+    int m_used, stop;
+};
+
+// Largest Ritz value of an n x n symmetric matrix held in LDS
+// (A[i * pitch + j], n <= 128) after up to `steps` Lanczos steps; all 256
+// threads take part in the matrix-vector product, wave 0 does the vector work.
+template <typename TM>
+__device__ double lanczos_lds(const TM* A, int pitch, int n, int steps, LanczosLds& L) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    steps = min(steps, min(n, kLanczosMaxSteps));
+    if (w == 0) {
+        double s2 = 0.0;
+        for (int i = lane; i < n; i += 64) {
+            uint32_t hsh = (uint32_t)i * 2654435761u + 0x9E3779B9u;
+            hsh ^= hsh >> 15; hsh *= 2246822519u; hsh ^= hsh >> 13;
+            const double x = 0.5 + (double)(hsh & 0xFFFFFF) / 16777216.0;
+            L.v1[i] = x;
+            L.v0[i] = 0.0;
+            s2 += x * x;
+        }
+        const double inv = 1.0 / sqrt(wave_sum(s2));
+        for (int i = lane; i < n; i += 64) L.v1[i] *= inv;
+        if (lane == 0) { L.m_used = steps; L.stop = 0; }
+    }
+    __syncthreads();
+    double beta_prev = 0.0;
+    for (int k = 0; k < steps; ++k) {
+        const int r = t >> 1, hf = t & 1;
+        double acc = 0.0;
+        if (r < n) {
+            const int j1 = min(n, hf * 64 + 64);
+            for (int j = hf * 64; j < j1; ++j) acc += (double)A[r * pitch + j] * L.v1[j];
+        }
+        acc += __shfl_xor(acc, 1, 64);
+        if (hf == 0 && r < n) L.wv[r] = acc;
+        __syncthreads();
+        if (w == 0) {
+            double d = 0.0;
+            for (int i = lane; i < n; i += 64) d += L.wv[i] * L.v1[i];
+            const double alpha = wave_sum(d);
+            double q = 0.0;
+            for (int i = lane; i < n; i += 64) {
+                const double x = L.wv[i] - alpha * L.v1[i] - beta_prev * L.v0[i];
+                L.wv[i] = x;
+                q += x * x;
+            }
+            const double beta = sqrt(wave_sum(q));
+            const bool stop = !(beta > 1e-13 * fabs(alpha)) || !isfinite(alpha) || !isfinite(beta);
+            if (lane == 0) {
+                L.al[k] = alpha;
+                L.be[k] = beta;
+                L.stop = stop ? 1 : 0;
+                if (stop) L.m_used = k + 1;
+            }
+            if (!stop)
+                for (int i = lane; i < n; i += 64) {
+                    L.v0[i] = L.v1[i];
+                    L.v1[i] = L.wv[i] / beta;
+                }
+            beta_prev = beta;
+        }
+        __syncthreads();
+        if (L.stop) break;
+    }
+    if (w == 0) {
+        const double lm = tridiag_max_wave(L.al, L.be, L.m_used);
+        if (lane == 0) L.res = lm;
+    }
+    __syncthreads();
+    const double lm = L.res;
+    __syncthreads();
+    return lm;
+}
+
 constexpr int kLanczosLdsN = 128;   // matrices up to this size are staged in LDS
 
 template <typename TM>
@@ -517,9 +631,14 @@ __global__ __launch_bounds__(256) void k_lanczos(const LanczosJob* __restrict__ 
     const bool in_lds = n <= kLanczosLdsN;
     constexpr int SP = kLanczosLdsN + 1;  // LDS pitch: row r, column j at bank r + j
     if (in_lds) {
+        // symmetric matrix: only its upper triangle is read (mirrored in LDS)
         for (int e = t; e < n * n; e += 256) {
             const int i = e / n, j = e % n;
-            Ss[i * SP + j] = (float)S[(int64_t)i * ld + j];
+            if (j >= i) {
+                const float x = (float)S[(int64_t)i * ld + j];
+                Ss[i * SP + j] = x;
+                Ss[j * SP + i] = x;
+            }
         }
     }
 
@@ -660,7 +779,7 @@ __global__ __launch_bounds__(256) void k_newton_init(const FactorJob* __restrict
         const int i = (int)(idx / ld), j = (int)(idx % ld);
         T m, x;
         if (i < n && j < n && ok) {
-            const T s = T(0.5 * (S[(int64_t)i * ld + j] + S[(int64_t)j * ld + i]));
+            const T s = T(S[(int64_t)min(i, j) * ld + max(i, j)]);  // upper triangle
             m = z * (s + (i == j ? e : T(0)));
             x = (i == j) ? zr : T(0);
         } else {
@@ -798,34 +917,45 @@ __device__ __forceinline__ void strip_newton_T(Strip& T, const Strip& M, float c
 __global__ __launch_bounds__(256, 1) void k_newton128(const FactorJob* __restrict__ jobs,
                                                      const double* __restrict__ stats,
                                                      float* __restrict__ arena,
-                                                     FactorDiag* __restrict__ diag, int p, int iters) {
-    __shared__ __align__(16) float S0[128 * kNP];
-    __shared__ __align__(16) float S1[128 * kNP];
+                                                     FactorDiag* __restrict__ diag,
+                                                     int32_t* __restrict__ prec, FusedArgs args) {
+    // one buffer, two fp32 slots; at the start it holds S as one fp64 matrix
+    __shared__ __align__(16) float Sbuf[2 * 128 * kNP];
     __shared__ double red[4];
+    __shared__ LanczosLds lz;
+    float* const S0 = Sbuf;
+    float* const S1 = Sbuf + 128 * kNP;
     const FactorJob jb = jobs[blockIdx.x];
-    const FactorDiag dg = diag[jb.factor];
     const int n = jb.n, ld = jb.ld;
+    const int p = args.p, iters = args.iters;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int h = lane >> 5, c = lane & 31;
-    const int st0 = dg.status & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_ZERO_);
+
+    // ---- S (fp64, upper triangle) -> LDS as one symmetric fp64 matrix
+    // spanning both slots
+    double* Sd = reinterpret_cast<double*>(Sbuf);  // 128 x 129 doubles = both slots
+    const double* Sg = stats + jb.s_off;
+    for (int i = w; i < n; i += 4)
+        for (int j = i + lane; j < n; j += 64) {
+            const double x = Sg[(int64_t)i * ld + j];
+            Sd[i * kNP + j] = x;
+            Sd[j * kNP + i] = x;
+        }
+    __syncthreads();
+
+    // ---- lambda_max (Lanczos) -> eps, status
+    const double lmax = lanczos_lds<double>(Sd, kNP, n, args.steps_s, lz);
+    int st0 = 0;
+    if (!isfinite(lmax)) st0 = SHAMPOO_FACTOR_NONFINITE_INPUT_;
+    else if (!(lmax > 0.0)) st0 = SHAMPOO_FACTOR_ZERO_;
     const bool ok = st0 == 0;
-    const double lam = dg.lambda_max + dg.eps;
+    const double eps = ok ? args.eps_rel * lmax : 0.0;
+    const double lam = lmax + eps;
     const float z = ok ? float((p + 1) / (2.0 * lam)) : 1.f;
     const float zr = ok ? float(pow((p + 1) / (2.0 * lam), 1.0 / p)) : 1.f;
-    const float e = float(dg.eps);
+    const float e = float(eps);
     const float c1 = float((double)(p + 1) / p), c2 = float(-1.0 / p);
 
-    // ---- S (fp64) -> LDS as one fp64 matrix spanning both slots, then
-    // M0 = z (sym(S) + eps I) in registers; padding rows/columns are identity
-    double* Sd = reinterpret_cast<double*>(S0);   // 128 x 129 doubles = both slots
-    const double* Sg = stats + jb.s_off;
-    if (ok) {
-        for (int e2 = t; e2 < 128 * 128; e2 += 256) {
-            const int i = e2 >> 7, j = e2 & 127;
-            Sd[i * kNP + j] = (i < n && j < n) ? Sg[(int64_t)i * ld + j] : 0.0;
-        }
-    }
-    __syncthreads();
     Strip M, X;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -834,7 +964,7 @@ __global__ __launch_bounds__(256, 1) void k_newton128(const FactorJob* __restric
             const int i = strip_row(w, h, v), j = 32 * q + c;
             float m, x;
             if (i < n && j < n && ok) {
-                const float sv = float(0.5 * (Sd[i * kNP + j] + Sd[j * kNP + i]));
+                const float sv = float(Sd[min(i, j) * kNP + max(i, j)]);  // upper triangle
                 m = z * (sv + (i == j ? e : 0.f));
                 x = (i == j) ? zr : 0.f;
             } else {
@@ -924,11 +1054,26 @@ __global__ __launch_bounds__(256, 1) void k_newton128(const FactorJob* __restric
                 }
             }
     }
+    if (!keep && !(st & SHAMPOO_FACTOR_ZERO_) && res > 1e-2) st |= SHAMPOO_FACTOR_RESIDUAL_HIGH_;
+
+    // ---- kappa estimate from the root: lambda_max(X) = (lambda_min + eps)^(-1/p).
+    // X sits in slot S1 after the last iteration.
+    double kap = 0.0;
+    if (ok) {
+        const double lx = lanczos_lds<float>(S1, kNP, n, args.steps_p, lz);
+        if (isfinite(lx) && lx > 0.0) kap = lam * pow(lx, (double)p);
+    }
     if (t == 0) {
-        if (!keep && !(st & SHAMPOO_FACTOR_ZERO_) && res > 1e-2) st |= SHAMPOO_FACTOR_RESIDUAL_HIGH_;
-        st &= ~SHAMPOO_FACTOR_FP64_;
-        diag[jb.factor].status = st;
-        diag[jb.factor].residual = ok ? res : 0.0;
+        FactorDiag& dg = diag[jb.factor];
+        dg.lambda_max = lmax;
+        dg.eps = eps;
+        dg.kappa_est = kap;
+        dg.status = st;
+        dg.residual = ok ? res : 0.0;
+        if (prec) {
+            const bool weak = (st & (SHAMPOO_FACTOR_NONFINITE_ROOT_ | SHAMPOO_FACTOR_RESIDUAL_HIGH_)) != 0;
+            prec[jb.factor] = (args.auto_route && ok && (kap > args.threshold || weak)) ? 1 : 0;
+        }
     }
 }
 
@@ -1181,10 +1326,10 @@ hipError_t launch_newton_commit(bool fp64, const FactorJob* jobs, int njobs, flo
     return hipGetLastError();
 }
 hipError_t launch_newton128(const FactorJob* jobs, int njobs, const double* stats, float* arena,
-                            FactorDiag* diag, int p, int iters, hipStream_t s) {
+                            FactorDiag* diag, int32_t* prec, const FusedArgs& a, hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
-    if (p != 1 && p != 2 && p != 4 && p != 8) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_newton128, dim3(njobs), dim3(256), 0, s, jobs, stats, arena, diag, p, iters);
+    if (a.p != 1 && a.p != 2 && a.p != 4 && a.p != 8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_newton128, dim3(njobs), dim3(256), 0, s, jobs, stats, arena, diag, prec, a);
     return hipGetLastError();
 }
 hipError_t launch_set_identity(const FactorJob* jobs, int njobs, float* arena, hipStream_t s) {

@@ -46,6 +46,13 @@ struct NewtonArgs {
     int32_t gate_val;
 };
 
+struct FusedArgs {          // fused fp32 root of factors up to 128
+    int p, iters;
+    int steps_s, steps_p;   // Lanczos steps on S (lambda_max) and on the root (kappa)
+    int auto_route;         // set prec flags from the kappa estimate
+    double eps_rel, threshold;
+};
+
 struct UpdateArgs {
     float beta1, lr, delta;
 };
@@ -67,7 +74,7 @@ hipError_t launch_newton_commit(bool fp64, const FactorJob* jobs, int njobs, flo
                                 const void* scratch, FactorDiag* diag, const NewtonArgs& a,
                                 hipStream_t s);
 hipError_t launch_newton128(const FactorJob* jobs, int njobs, const double* stats, float* arena,
-                            FactorDiag* diag, int p, int iters, hipStream_t s);
+                            FactorDiag* diag, int32_t* prec, const FusedArgs& a, hipStream_t s);
 hipError_t launch_set_identity(const FactorJob* jobs, int njobs, float* arena, hipStream_t s);
 hipError_t launch_adagrad_norm(const BlockChunk* chunks, int nchunks, const uint64_t* bases,
                                float* arena, float delta, double* partA, hipStream_t s);

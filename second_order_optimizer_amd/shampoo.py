@@ -264,11 +264,17 @@ class Shampoo(Plan):
             n *= s
         return self.state[off: off + n * es].view(dtype).view(*shape)
 
-    def stats(self, b: int):
+    def stats(self, b: int, raw: bool = False):
+        """L, R of block b.  The library maintains only the upper triangle of
+        each (symmetric) factor; unless raw=True the full matrix is rebuilt
+        from it (a copy)."""
         bl = self.block(b)
         L = self._view(bl.off_l, (bl.ld_l, bl.ld_l), self.torch.float64)[: bl.rows, : bl.rows]
         R = self._view(bl.off_r, (bl.ld_r, bl.ld_r), self.torch.float64)[: bl.cols, : bl.cols]
-        return L, R
+        if raw:
+            return L, R
+        sym = lambda x: self.torch.triu(x) + self.torch.triu(x, 1).T
+        return sym(L), sym(R)
 
     def roots(self, b: int, fp64: bool = False):
         bl = self.block(b)
