@@ -70,9 +70,15 @@ def work_model(wl, opt, n_fp64_factors_per_pass):
     dims = [b.rows for b in blocks] + [b.cols for b in blocks]
     root_flops_all = sum(gemms_per_iter * 2.0 * n ** 3 * wl.newton_iters for n in dims)
     shampoo_params = sum(b.rows * b.cols for b in blocks)
+    small = [b for b in blocks if b.rows <= 128 and b.cols <= 128]
+    big = [b for b in blocks if not (b.rows <= 128 and b.cols <= 128)]
     dense_fallback = sum(t.numel for t in wl.tensors if t.kind == "dense") - shampoo_params
     return {
         "gram": gram, "apply_t": apply_t, "apply_d": apply_d,
+        "apply_small": sum(2.0 * (b.rows * b.cols ** 2 + b.rows ** 2 * b.cols) for b in small),
+        "apply_t_big": sum(2.0 * b.rows * b.cols ** 2 for b in big),
+        "apply_d_big": sum(2.0 * b.rows ** 2 * b.cols for b in big),
+        "shampoo_params_big": sum(b.rows * b.cols for b in big),
         "root_flops_all": root_flops_all,
         "root_flops_per_factor_mean": root_flops_all / max(len(dims), 1),
         "shampoo_params": shampoo_params, "dense_fallback": dense_fallback,
@@ -252,9 +258,10 @@ def main():
     alg = {
         # name: (work per launch, unit, bound, peak)
         "stats_gram_f64": (wm["gram"], "TFLOP/s", "mfma", PEAK_TFLOPS["f64"]),
-        "apply_gemm_t": (wm["apply_t"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]),
-        "apply_gemm_d": (wm["apply_d"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]),
-        "adagrad_norm": (wm["shampoo_params"] * 12.0, "GB/s", "hbm", PEAK_HBM_GBS),
+        "apply_gemm_t": (wm["apply_t_big"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]),
+        "apply_gemm_d": (wm["apply_d_big"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]),
+        "adagrad_norm": (wm["shampoo_params_big"] * 12.0, "GB/s", "hbm", PEAK_HBM_GBS),
+        "apply_fused": (wm["apply_small"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]),
         "update": (wm["shampoo_params"] * 20.0 + wm["dense_fallback"] * 28.0, "GB/s", "hbm",
                    PEAK_HBM_GBS),
     }

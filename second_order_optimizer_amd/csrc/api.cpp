@@ -45,6 +45,7 @@ struct TensorPlan {
 struct BlockPlan {
     int tensor, r0, c0, mb, nb;
     int fl, fr;
+    bool small;          // at most 128 x 128: fused statistics and apply kernels
     int64_t off_t;       // bytes: scratch T = G_b P_R (mb x nb)
     int d_slot, d_tiles; // ||D||^2 partial slots
     int a_slot, a_chunks;
@@ -84,12 +85,12 @@ struct Blob {
 enum ProfCat : int {
     PC_STATS = 0, PC_LANCZOS_S, PC_LANCZOS_P, PC_NEWTON_INIT, PC_NEWTON_GEMM32, PC_NEWTON_GEMM64,
     PC_NEWTON_COMMIT, PC_ADAGRAD, PC_APPLY_T, PC_APPLY_D, PC_SCALE, PC_UPDATE, PC_SPARSE,
-    PC_NEWTON_FUSED, PC_COUNT
+    PC_NEWTON_FUSED, PC_APPLY_FUSED, PC_COUNT
 };
 const char* const kProfNames[PC_COUNT] = {
     "stats_gram_f64", "lanczos_stats", "lanczos_roots", "newton_init", "newton_gemm_f32",
     "newton_gemm_f64", "newton_commit", "adagrad_norm", "apply_gemm_t", "apply_gemm_d",
-    "block_scale", "update", "sparse_rows", "newton_fused_f32"};
+    "block_scale", "update", "sparse_rows", "newton_fused_f32", "apply_fused"};
 
 struct ProfRec {
     int cat;
@@ -113,7 +114,9 @@ struct shampoo_s {
     int n_partA = 0, n_partD = 0;
     Blob blob;  // static tables (offsets relative to off_tables)
 
-    LaunchRef gram, apply1, apply2;   // gram: blocks with a side > 128
+    LaunchRef gram, apply1, apply2;   // blocks with a side > 128
+    int64_t apply128_off = 0;
+    int n_apply128 = 0;               // blocks of at most 128 x 128
     int64_t gram128_off = 0;
     int n_gram128 = 0;                // blocks of at most 128 x 128
     int64_t lanczos_s_off = 0, lanczos_p_off = 0, ident_jobs_off = 0;   // every factor
@@ -291,6 +294,7 @@ int build_plan(shampoo_s* h) {
                 bp.nb = (int)std::min<int64_t>(b, tp.cols - c0);
                 bp.fl = 2 * (int)h->blocks.size();
                 bp.fr = bp.fl + 1;
+                bp.small = bp.mb <= 128 && bp.nb <= 128;
                 h->blocks.push_back(bp);
             }
         tp.n_blocks = (int)h->blocks.size() - tp.first_block;
@@ -327,17 +331,17 @@ int build_plan(shampoo_s* h) {
         if (tp.mode != 2) tp.off_mom = take(numel * 4);
         if (tp.mode == 0) tp.off_d = take(numel * 4);
     }
-    for (auto& bp : h->blocks) bp.off_t = take((int64_t)bp.mb * bp.nb * 4);
+    for (auto& bp : h->blocks) bp.off_t = bp.small ? -1 : take((int64_t)bp.mb * bp.nb * 4);
 
     // norm partial slots
     int na = 0, nd = 0;
     for (auto& bp : h->blocks) {
         const int rows_per = (int)std::max<int64_t>(1, kElemChunk / bp.nb);
         bp.a_slot = na;
-        bp.a_chunks = ceil_div(bp.mb, rows_per);
+        bp.a_chunks = bp.small ? 1 : ceil_div(bp.mb, rows_per);
         na += bp.a_chunks;
         bp.d_slot = nd;
-        bp.d_tiles = ceil_div(bp.mb, kTile) * ceil_div(bp.nb, kTile);
+        bp.d_tiles = bp.small ? 1 : ceil_div(bp.mb, kTile) * ceil_div(bp.nb, kTile);
         nd += bp.d_tiles;
     }
     h->n_partA = na;
@@ -440,10 +444,30 @@ int build_plan(shampoo_s* h) {
     // apply: T = G_b P_R, then D = P_L T with ||D||^2 partials (cue 10)
     {
         std::vector<GemmTask> t1, t2;
+        std::vector<ApplyJob> small;
         for (auto& bp : h->blocks) {
             const TensorPlan& tp = h->tensors[bp.tensor];
             const FactorPlan& fl = h->factors[bp.fl];
             const FactorPlan& fr = h->factors[bp.fr];
+            if (bp.small) {
+                ApplyJob j{};
+                const int64_t o = (int64_t)bp.r0 * tp.cols + bp.c0;
+                j.g_base = 1 + bp.tensor;
+                j.g_off = o;
+                j.a_off = tp.off_a / 4 + o;
+                j.d_off = tp.off_d / 4 + o;
+                j.pl_off = fl.off_p / 4;
+                j.pr_off = fr.off_p / 4;
+                j.ldg = (int)tp.cols;
+                j.mb = bp.mb;
+                j.nb = bp.nb;
+                j.ld_l = fl.ld;
+                j.ld_r = fr.ld;
+                j.slot_a = bp.a_slot;
+                j.slot_d = bp.d_slot;
+                small.push_back(j);
+                continue;
+            }
             GemmTask t{};
             t.a_base = 1 + bp.tensor;
             t.a_off = (int64_t)bp.r0 * tp.cols + bp.c0;
@@ -474,6 +498,8 @@ int build_plan(shampoo_s* h) {
         }
         h->apply1 = add_launch(blob, t1);
         h->apply2 = add_launch(blob, t2);
+        h->n_apply128 = (int)small.size();
+        h->apply128_off = blob.add(small);
     }
     // Lanczos jobs on statistics and on roots; identity jobs
     {
@@ -523,7 +549,7 @@ int build_plan(shampoo_s* h) {
             const BlockPlan& bp = h->blocks[i];
             const TensorPlan& tp = h->tensors[bp.tensor];
             const int rows_per = (int)std::max<int64_t>(1, kElemChunk / bp.nb);
-            for (int k = 0; k < bp.a_chunks; ++k) {
+            for (int k = 0; !bp.small && k < bp.a_chunks; ++k) {
                 BlockChunk q{};
                 q.tensor = bp.tensor;
                 q.block = (int)i;
@@ -588,8 +614,9 @@ struct ProfScope {
     int cat;
     hipStream_t s;
     hipEvent_t a = nullptr;
-    ProfScope(shampoo_s* h_, int cat_, hipStream_t s_) : h(h_), cat(cat_), s(s_) {
-        if (!h->prof_on) return;
+    ProfScope(shampoo_s* h_, int cat_, hipStream_t s_, bool active = true)
+        : h(h_), cat(cat_), s(s_) {
+        if (!h->prof_on || !active) return;
         a = prof_event(h);
         if (a && hipEventRecord(a, s) != hipSuccess) a = nullptr;
     }
@@ -915,7 +942,7 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
         // factors up to 128: everything inside the fused kernel; larger ones:
         // Lanczos on S, batched fp32 Newton, Lanczos on the root
         {
-            ProfScope ps(h, PC_LANCZOS_S, s);
+            ProfScope ps(h, PC_LANCZOS_S, s, h->n_lanczos_big > 0);
             rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_s_big_off), h->n_lanczos_big,
                                         h->arena, true, la, s));
         }
@@ -924,7 +951,7 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
         if (rc) return rc;
         lp.auto_route = c.root_mode == SHAMPOO_ROOT_AUTO ? 1 : 0;
         {
-            ProfScope ps(h, PC_LANCZOS_P, s);
+            ProfScope ps(h, PC_LANCZOS_P, s, h->n_lanczos_big > 0);
             rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_p_big_off), h->n_lanczos_big,
                                         h->arena, false, lp, s));
         }
@@ -966,9 +993,15 @@ int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const flo
     const shampoo_config& c = h->cfg;
 
     {
-        ProfScope ps(h, PC_ADAGRAD, s);
+        ProfScope ps(h, PC_ADAGRAD, s, h->n_blockchunks > 0);
         rc = hip_err(launch_adagrad_norm(tab<BlockChunk>(h, h->blockchunks_off), h->n_blockchunks, bases,
                                      arena, (float)c.graft_eps, partA, s));
+    }
+    if (rc) return rc;
+    {
+        ProfScope ps(h, PC_APPLY_FUSED, s, h->n_apply128 > 0);
+        rc = hip_err(launch_apply128(tab<ApplyJob>(h, h->apply128_off), h->n_apply128, bases, arena,
+                                     (float)c.graft_eps, partA, partD, s));
     }
     if (rc) return rc;
     GemmArgs g{};
@@ -976,13 +1009,13 @@ int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const flo
     g.alpha = 1.0;
     g.norms = partD;
     {
-        ProfScope ps(h, PC_APPLY_T, s);
+        ProfScope ps(h, PC_APPLY_T, s, h->apply1.ntiles > 0);
         rc = hip_err(launch_gemm_f32(tab<GemmTask>(h, h->apply1.tasks_off),
                                      tab<TileRef>(h, h->apply1.tiles_off), h->apply1.ntiles, bases, g, s));
     }
     if (rc) return rc;
     {
-        ProfScope ps(h, PC_APPLY_D, s);
+        ProfScope ps(h, PC_APPLY_D, s, h->apply2.ntiles > 0);
         rc = hip_err(launch_gemm_f32(tab<GemmTask>(h, h->apply2.tasks_off),
                                      tab<TileRef>(h, h->apply2.tiles_off), h->apply2.ntiles, bases, g, s));
     }

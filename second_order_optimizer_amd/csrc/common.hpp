@@ -37,6 +37,18 @@ struct GramJob {
     int32_t ld_l, ld_r;   // leading dims of L and R
 };
 
+// One Shampoo block of at most 128 x 128 for the fused apply kernel.
+struct ApplyJob {
+    int64_t g_off;          // G_b in its base (the tensor's gradient)
+    int64_t a_off, d_off;   // Adagrad accumulator and D blocks (arena floats)
+    int64_t pl_off, pr_off; // fp32 roots (arena floats)
+    int32_t g_base;         // gradient base index
+    int32_t ldg;            // tensor row length (leading dim of G, a and D)
+    int32_t mb, nb;
+    int32_t ld_l, ld_r;
+    int32_t slot_a, slot_d; // ||A_b||^2 and ||D_b||^2 slots
+};
+
 // A tile of the batched GEMM launch: which task and which 128x128 tile.
 struct TileRef {
     int32_t task;

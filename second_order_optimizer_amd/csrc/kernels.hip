@@ -830,7 +830,7 @@ __global__ __launch_bounds__(256) void k_newton_commit(const FactorJob* __restri
             const int i = (int)(idx / ld), j = (int)(idx % ld);
             double x;
             if (ident || i >= n || j >= n) x = (i == j) ? 1.0 : 0.0;
-            else x = double(X[idx]);
+            else x = 0.5 * (double(X[idx]) + double(X[(int64_t)j * ld + i]));  // symmetric part
             P[idx] = float(x);
             if (P64) P64[idx] = x;
         }
@@ -1041,6 +1041,8 @@ __global__ __launch_bounds__(256, 1) void k_newton128(const FactorJob* __restric
     if (ok && bad > 0.0) st |= SHAMPOO_FACTOR_NONFINITE_ROOT_;
     const bool keep = (st & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_NONFINITE_ROOT_)) != 0;
     if (!keep) {
+        // the committed root is the symmetric part (X + X^T)/2 (the exact root
+        // is symmetric); X^T comes from slot S1, which holds X
         const bool ident = (st & SHAMPOO_FACTOR_ZERO_) != 0;
         float* P = arena + jb.p_off;
 #pragma unroll
@@ -1049,7 +1051,9 @@ __global__ __launch_bounds__(256, 1) void k_newton128(const FactorJob* __restric
             for (int v = 0; v < 16; ++v) {
                 const int i = strip_row(w, h, v), j = 32 * q + c;
                 if (i < ld && j < ld) {
-                    const float xv = (ident || i >= n || j >= n) ? ((i == j) ? 1.f : 0.f) : X.v[q][v];
+                    const float xv = (ident || i >= n || j >= n)
+                                         ? ((i == j) ? 1.f : 0.f)
+                                         : 0.5f * (X.v[q][v] + S1[j * kNP + i]);
                     P[(int64_t)i * ld + j] = xv;
                 }
             }
@@ -1074,6 +1078,170 @@ __global__ __launch_bounds__(256, 1) void k_newton128(const FactorJob* __restric
             const bool weak = (st & (SHAMPOO_FACTOR_NONFINITE_ROOT_ | SHAMPOO_FACTOR_RESIDUAL_HIGH_)) != 0;
             prec[jb.factor] = (args.auto_route && ok && (kap > args.threshold || weak)) ? 1 : 0;
         }
+    }
+}
+
+// --------------------------------------------------- fused apply, <= 128
+// One block per workgroup, one LDS slot (66 KB: two workgroups per CU):
+//  1. a <- a + G*G and ||A||^2 of A = G / (sqrt(a) + delta) while G is staged
+//     into LDS;
+//  2. T = G P_R in column strips (wave w: T[:, 32w..32w+32)), P_R streamed
+//     from L2 with an 8-step prefetch; T replaces G in LDS;
+//  3. D = P_L T in row strips (wave w: D[32w..32w+32, :)), the A operand read
+//     down the columns of P_L -- the committed roots are symmetric, so this
+//     is P_L itself -- again streamed with prefetch;
+//  4. ||D||^2 and D written in the tensor's layout.
+__global__ __launch_bounds__(256, 2) void k_apply128(const ApplyJob* __restrict__ jobs,
+                                                    const uint64_t* __restrict__ bases,
+                                                    float* __restrict__ arena, float delta,
+                                                    double* __restrict__ partA,
+                                                    double* __restrict__ partD) {
+    __shared__ __align__(16) float Sl[128 * kNP];
+    __shared__ double red[4];
+    const ApplyJob jb = jobs[blockIdx.x];
+    const float* G = reinterpret_cast<const float*>(bases[jb.g_base]) + jb.g_off;
+    float* a = arena + jb.a_off;
+    const int mb = jb.mb, nb = jb.nb, ld = jb.ldg;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int h = lane >> 5, c = lane & 31;
+    typedef float f16v __attribute__((ext_vector_type(16)));
+
+    // ---- 1. G -> LDS with the Adagrad accumulate on the way
+    double asum = 0.0;
+    {
+        const bool vec = (nb % 4 == 0) && (ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(G) & 15) == 0) &&
+                         ((reinterpret_cast<uintptr_t>(a) & 15) == 0);
+        const int c4 = t & 31, r0 = t >> 5;
+#pragma unroll 4
+        for (int p = 0; p < 16; ++p) {
+            const int r = r0 + 8 * p, cc = 4 * c4;
+            float gv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (r < mb && cc < nb) {
+                const int64_t o = (int64_t)r * ld + cc;
+                if (vec) {
+                    const float4 g4 = *reinterpret_cast<const float4*>(G + o);
+                    float4 a4 = *reinterpret_cast<const float4*>(a + o);
+                    gv[0] = g4.x; gv[1] = g4.y; gv[2] = g4.z; gv[3] = g4.w;
+                    a4.x += g4.x * g4.x; a4.y += g4.y * g4.y; a4.z += g4.z * g4.z; a4.w += g4.w * g4.w;
+                    *reinterpret_cast<float4*>(a + o) = a4;
+                    const float A0 = g4.x / (sqrtf(a4.x) + delta), A1 = g4.y / (sqrtf(a4.y) + delta);
+                    const float A2 = g4.z / (sqrtf(a4.z) + delta), A3 = g4.w / (sqrtf(a4.w) + delta);
+                    asum += (double)(A0 * A0 + A1 * A1) + (double)(A2 * A2 + A3 * A3);
+                } else {
+                    for (int e = 0; e < 4 && cc + e < nb; ++e) {
+                        const float g1 = G[o + e];
+                        const float av = a[o + e] + g1 * g1;
+                        a[o + e] = av;
+                        const float A = g1 / (sqrtf(av) + delta);
+                        asum += (double)(A * A);
+                        gv[e] = g1;
+                    }
+                }
+            }
+            float* d = &Sl[r * kNP + cc];
+            d[0] = gv[0]; d[1] = gv[1]; d[2] = gv[2]; d[3] = gv[3];
+        }
+    }
+    __syncthreads();
+
+    // ---- 2. T[:, 32w..] = G P_R[:, 32w..]; k runs over the first nb (rounded
+    // up to 16; beyond nb, P_R reads as zero)
+    const int KT = (nb + 15) & ~15;
+    const float* PR = arena + jb.pr_off;
+    const int colT = 32 * w + c;           // this lane's column of P_R / T
+    f16v tacc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tacc[r][v] = 0.f;
+    {
+        auto ld_pr = [&](int k) -> float {
+            return (k < nb && colT < nb) ? PR[(int64_t)k * jb.ld_r + colT] : 0.f;
+        };
+        float nxt[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) nxt[u] = ld_pr(2 * u + h);
+        for (int k0 = 0; k0 < KT; k0 += 16) {
+            float cur[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
+            if (k0 + 16 < KT) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) nxt[u] = ld_pr(k0 + 16 + 2 * u + h);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int k = k0 + 2 * u + h;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    tacc[r] = __builtin_amdgcn_mfma_f32_32x32x2f32(Sl[(32 * r + c) * kNP + k], cur[u],
+                                                                   tacc[r], 0, 0, 0);
+            }
+        }
+    }
+    __syncthreads();                       // every wave is done reading G
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            Sl[(32 * r + 8 * (v >> 2) + 4 * h + (v & 3)) * kNP + 32 * w + c] = tacc[r][v];
+    __syncthreads();
+
+    // ---- 3. D[32w.., :] = P_L[32w.., :] T; A operand P_L[32w + c][k] =
+    // P_L[k][32w + c] (symmetric), k over the first mb
+    const int KD = (mb + 15) & ~15;
+    const float* PL = arena + jb.pl_off;
+    const int rowD = 32 * w + c;
+    f16v dacc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dacc[q][v] = 0.f;
+    {
+        auto ld_pl = [&](int k) -> float {
+            return (k < mb && rowD < mb) ? PL[(int64_t)k * jb.ld_l + rowD] : 0.f;
+        };
+        float nxt[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) nxt[u] = ld_pl(2 * u + h);
+        for (int k0 = 0; k0 < KD; k0 += 16) {
+            float cur[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
+            if (k0 + 16 < KD) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) nxt[u] = ld_pl(k0 + 16 + 2 * u + h);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int k = k0 + 2 * u + h;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    dacc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur[u], Sl[k * kNP + 32 * q + c],
+                                                                   dacc[q], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- 4. ||D||^2 and D
+    double dsum = 0.0;
+    float* Dg = arena + jb.d_off;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int i = 32 * w + 8 * (v >> 2) + 4 * h + (v & 3), j = 32 * q + c;
+            if (i < mb && j < nb) {
+                const float x = dacc[q][v];
+                dsum += (double)x * (double)x;
+                Dg[(int64_t)i * ld + j] = x;
+            }
+        }
+    asum = block_sum_256(asum, red);
+    dsum = block_sum_256(dsum, red);
+    if (t == 0) {
+        partA[jb.slot_a] = asum;
+        partD[jb.slot_d] = dsum;
     }
 }
 
@@ -1330,6 +1498,13 @@ hipError_t launch_newton128(const FactorJob* jobs, int njobs, const double* stat
     if (njobs <= 0) return hipSuccess;
     if (a.p != 1 && a.p != 2 && a.p != 4 && a.p != 8) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_newton128, dim3(njobs), dim3(256), 0, s, jobs, stats, arena, diag, prec, a);
+    return hipGetLastError();
+}
+hipError_t launch_apply128(const ApplyJob* jobs, int njobs, const uint64_t* bases, float* arena,
+                           float delta, double* partA, double* partD, hipStream_t s) {
+    if (njobs <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_apply128, dim3(njobs), dim3(256), 0, s, jobs, bases, arena, delta, partA,
+                       partD);
     return hipGetLastError();
 }
 hipError_t launch_set_identity(const FactorJob* jobs, int njobs, float* arena, hipStream_t s) {

@@ -227,3 +227,18 @@ def test_zero_gradient_block_gives_identity_root_and_no_update():
     assert torch.equal(PL.cpu(), torch.eye(32)) and torch.equal(PR.cpu(), torch.eye(32))
     dW = run.params[0].cpu().numpy() - run.W0[0]
     assert np.all(dW[:32, :32] == 0.0)
+
+
+def test_committed_roots_are_symmetric():
+    """Roots are stored as the symmetric part of the iterate (the apply kernel
+    reads P_L down its columns, which is exact only for a symmetric P_L)."""
+    T = synth.TensorSpec
+    wl = _custom([T("a", 300, 200), T("b", 96, 64)], 128, steps=1)
+    for mode in ("auto", "f64"):
+        run = GpuRun(wl, root_mode=mode)
+        _, dev, sp = run.grads_at(0)
+        run.step(0, dev, sp)
+        torch.cuda.synchronize()
+        for b in range(run.opt.n_blocks):
+            for P in list(run.opt.roots(b)) + [x for x in run.opt.roots(b, fp64=True) if x is not None]:
+                assert torch.equal(P, P.T), (mode, b)
