@@ -702,7 +702,8 @@ int shampoo_create(const shampoo_config* cfg, int32_t n_tensors, const shampoo_t
     if (!h) return SHAMPOO_E_NOMEM;
     try {
         h->cfg = c;
-        if (h->cfg.lanczos_steps == 0) h->cfg.lanczos_steps = 32;
+        // lanczos_steps == 0: 20 steps for factors up to 128, 32 above (lambda_max
+        // to ~1e-9 relative on the workloads' statistics); 8 for the kappa estimate
         h->n = n_tensors;
         h->tensors.resize(n_tensors);
         for (int t = 0; t < n_tensors; ++t) {
@@ -877,8 +878,8 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
             FusedArgs fa{};
             fa.p = p;
             fa.iters = h->cfg.newton_iters;
-            fa.steps_s = h->cfg.lanczos_steps;
-            fa.steps_p = std::min(h->cfg.lanczos_steps, 16);
+            fa.steps_s = h->cfg.lanczos_steps > 0 ? h->cfg.lanczos_steps : 20;
+            fa.steps_p = h->cfg.lanczos_steps > 0 ? std::min(h->cfg.lanczos_steps, 8) : 8;
             fa.auto_route = h->cfg.root_mode == SHAMPOO_ROOT_AUTO ? 1 : 0;
             fa.eps_rel = h->cfg.eps_rel;
             fa.threshold = h->cfg.fp64_cond_threshold;
@@ -926,7 +927,7 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
     FactorDiag* diag = at<FactorDiag>(h, h->off_diag);
     int32_t* prec = at<int32_t>(h, h->off_prec);
     LanczosArgs la{};
-    la.steps = c.lanczos_steps;
+    la.steps = c.lanczos_steps > 0 ? c.lanczos_steps : 32;
     la.mode = 0;
     la.p = c.root_p;
     la.eps_rel = c.eps_rel;
@@ -936,7 +937,7 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
     la.route_all_fp64 = c.root_mode == SHAMPOO_ROOT_F64 ? 1 : 0;
     LanczosArgs lp = la;
     lp.mode = 1;
-    lp.steps = std::min(c.lanczos_steps, 16);  // kappa estimate: a factor-2 decision
+    lp.steps = std::min(la.steps, 8);  // kappa estimate: a factor-2 decision
     int rc = SHAMPOO_OK;
     if (use_fp32(c)) {
         // factors up to 128: everything inside the fused kernel; larger ones:

@@ -565,15 +565,41 @@ __device__ double lanczos_lds(const TM* A, int pitch, int n, int steps, LanczosL
     }
     __syncthreads();
     double beta_prev = 0.0;
+    // matrix-vector product: thread t takes rows 4(t>>3)..+3 and columns
+    // 16(t&7)..+15 (v in registers, independent loads), then a 3-level
+    // shuffle sum over the 8 column blocks of a row group
+    const int rg = t >> 3, cb = t & 7;
     for (int k = 0; k < steps; ++k) {
-        const int r = t >> 1, hf = t & 1;
-        double acc = 0.0;
-        if (r < n) {
-            const int j1 = min(n, hf * 64 + 64);
-            for (int j = hf * 64; j < j1; ++j) acc += (double)A[r * pitch + j] * L.v1[j];
+        double vr[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int j = 16 * cb + q;
+            vr[q] = (j < n) ? L.v1[j] : 0.0;
         }
-        acc += __shfl_xor(acc, 1, 64);
-        if (hf == 0 && r < n) L.wv[r] = acc;
+        double acc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * rg + i;
+            double s = 0.0;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int j = 16 * cb + q;
+                const double aij = (r < n && j < n) ? (double)A[r * pitch + j] : 0.0;
+                s += aij * vr[q];
+            }
+            acc[i] = s;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[i] += __shfl_xor(acc[i], 1, 64);
+            acc[i] += __shfl_xor(acc[i], 2, 64);
+            acc[i] += __shfl_xor(acc[i], 4, 64);
+        }
+        if (cb == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * rg + i < n) L.wv[4 * rg + i] = acc[i];
+        }
         __syncthreads();
         if (w == 0) {
             double d = 0.0;
@@ -914,12 +940,13 @@ __device__ __forceinline__ void strip_newton_T(Strip& T, const Strip& M, float c
             T.v[q][v] = c2 * M.v[q][v] + ((strip_row(w, h, v) == 32 * q + c) ? c1 : 0.f);
 }
 
+template <int PP>
 __global__ __launch_bounds__(256, 1) void k_newton128(const FactorJob* __restrict__ jobs,
                                                      const double* __restrict__ stats,
                                                      float* __restrict__ arena,
                                                      FactorDiag* __restrict__ diag,
                                                      int32_t* __restrict__ prec, FusedArgs args) {
-    // one buffer, two fp32 slots; at the start it holds S as one fp64 matrix
+    // two fp32 slots for the iterates; S0 holds S at the start
     __shared__ __align__(16) float Sbuf[2 * 128 * kNP];
     __shared__ double red[4];
     __shared__ LanczosLds lz;
@@ -927,24 +954,27 @@ __global__ __launch_bounds__(256, 1) void k_newton128(const FactorJob* __restric
     float* const S1 = Sbuf + 128 * kNP;
     const FactorJob jb = jobs[blockIdx.x];
     const int n = jb.n, ld = jb.ld;
-    const int p = args.p, iters = args.iters;
+    constexpr int p = PP;
+    const int iters = args.iters;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int h = lane >> 5, c = lane & 31;
 
-    // ---- S (fp64, upper triangle) -> LDS as one symmetric fp64 matrix
-    // spanning both slots
-    double* Sd = reinterpret_cast<double*>(Sbuf);  // 128 x 129 doubles = both slots
+    // ---- S (fp64, upper triangle) -> slot S0 as the symmetric fp32 matrix the
+    // fp32 iteration starts from
     const double* Sg = stats + jb.s_off;
-    for (int i = w; i < n; i += 4)
-        for (int j = i + lane; j < n; j += 64) {
-            const double x = Sg[(int64_t)i * ld + j];
-            Sd[i * kNP + j] = x;
-            Sd[j * kNP + i] = x;
+#pragma unroll 8
+    for (int e2 = t; e2 < 128 * 128; e2 += 256) {
+        const int i = e2 >> 7, j = e2 & 127;
+        if (i < n && j < n && j >= i) {
+            const float x = (float)Sg[(int64_t)i * ld + j];
+            S0[i * kNP + j] = x;
+            S0[j * kNP + i] = x;
         }
+    }
     __syncthreads();
 
     // ---- lambda_max (Lanczos) -> eps, status
-    const double lmax = lanczos_lds<double>(Sd, kNP, n, args.steps_s, lz);
+    const double lmax = lanczos_lds<float>(S0, kNP, n, args.steps_s, lz);
     int st0 = 0;
     if (!isfinite(lmax)) st0 = SHAMPOO_FACTOR_NONFINITE_INPUT_;
     else if (!(lmax > 0.0)) st0 = SHAMPOO_FACTOR_ZERO_;
@@ -964,7 +994,7 @@ __global__ __launch_bounds__(256, 1) void k_newton128(const FactorJob* __restric
             const int i = strip_row(w, h, v), j = 32 * q + c;
             float m, x;
             if (i < n && j < n && ok) {
-                const float sv = float(Sd[min(i, j) * kNP + max(i, j)]);  // upper triangle
+                const float sv = S0[i * kNP + j];
                 m = z * (sv + (i == j ? e : 0.f));
                 x = (i == j) ? zr : 0.f;
             } else {
@@ -974,7 +1004,7 @@ __global__ __launch_bounds__(256, 1) void k_newton128(const FactorJob* __restric
             M.v[q][v] = m;
             X.v[q][v] = x;
         }
-    __syncthreads();   // Sd (aliasing S0/S1) is dead from here on
+    __syncthreads();   // the staged S is dead from here on
     Strip T;
     strip_newton_T(T, M, c1, c2, w, h, c);
     strip_store(S0, T, w, h, c);
@@ -991,8 +1021,9 @@ __global__ __launch_bounds__(256, 1) void k_newton128(const FactorJob* __restric
         X = acc2[0];
         Strip Tp = acc2[1];          // T^2
         // further squarings: T^4, T^8 (p = 4, 8); p = 1 uses T itself
-        if (p == 1) Tp = T;
-        for (int e2 = 2; e2 < p; e2 *= 2) {
+        if constexpr (PP == 1) Tp = T;
+#pragma unroll
+        for (int e2 = 2; e2 < PP; e2 *= 2) {
             __syncthreads();         // everyone is done reading S1 (X) and S0 (T)
             strip_store(S1, Tp, w, h, c);
             __syncthreads();
@@ -1496,8 +1527,13 @@ hipError_t launch_newton_commit(bool fp64, const FactorJob* jobs, int njobs, flo
 hipError_t launch_newton128(const FactorJob* jobs, int njobs, const double* stats, float* arena,
                             FactorDiag* diag, int32_t* prec, const FusedArgs& a, hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
-    if (a.p != 1 && a.p != 2 && a.p != 4 && a.p != 8) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_newton128, dim3(njobs), dim3(256), 0, s, jobs, stats, arena, diag, prec, a);
+    switch (a.p) {
+        case 1: hipLaunchKernelGGL(k_newton128<1>, dim3(njobs), dim3(256), 0, s, jobs, stats, arena, diag, prec, a); break;
+        case 2: hipLaunchKernelGGL(k_newton128<2>, dim3(njobs), dim3(256), 0, s, jobs, stats, arena, diag, prec, a); break;
+        case 4: hipLaunchKernelGGL(k_newton128<4>, dim3(njobs), dim3(256), 0, s, jobs, stats, arena, diag, prec, a); break;
+        case 8: hipLaunchKernelGGL(k_newton128<8>, dim3(njobs), dim3(256), 0, s, jobs, stats, arena, diag, prec, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 hipError_t launch_apply128(const ApplyJob* jobs, int njobs, const uint64_t* bases, float* arena,
