@@ -490,7 +490,7 @@ __global__ __launch_bounds__(256, 2) void k_gram128(const GramJob* __restrict__ 
 constexpr int kLanczosMaxN = 1024;
 constexpr int kLanczosMaxSteps = 64;
 
-__device__ int sturm_count(const double* al, const double* be, int m, double x) {
+__device__ __forceinline__ int sturm_count(const double* al, const double* be, int m, double x) {
     int cnt = 0;
     double d = 1.0;
     for (int k = 0; k < m; ++k) {
@@ -505,7 +505,7 @@ __device__ int sturm_count(const double* al, const double* be, int m, double x) 
 // Largest eigenvalue of the m x m tridiagonal (al, be) by Sturm-count
 // multisection on one wave: every lane counts at its own point of the
 // bracket, so each round shrinks it 65-fold.  NaN for non-finite input.
-__device__ double tridiag_max_wave(const double* al, const double* be, int m) {
+__device__ __forceinline__ double tridiag_max_wave(const double* al, const double* be, int m) {
     const int lane = threadIdx.x & 63;
     double lo = 0.0, hi = 0.0;
     bool finite = true;
@@ -546,7 +546,7 @@ struct LanczosLds {
 // (A[i * pitch + j], n <= 128) after up to `steps` Lanczos steps; all 256
 // threads take part in the matrix-vector product, wave 0 does the vector work.
 template <typename TM>
-__device__ double lanczos_lds(const TM* A, int pitch, int n, int steps, LanczosLds& L) {
+__device__ __forceinline__ double lanczos_lds(const TM* A, int pitch, int n, int steps, LanczosLds& L) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     steps = min(steps, min(n, kLanczosMaxSteps));
     if (w == 0) {
