@@ -84,7 +84,7 @@ typedef struct {
     int32_t newton_iters;     /* coupled-Newton iterations per root (e.g. 20)           */
     int32_t root_mode;        /* shampoo_root_mode                                       */
     int32_t lanczos_steps;    /* Krylov steps for lambda_max; 0 = 20 for factors up to
-                                 128 and 32 above; the kappa estimate uses min(8, this)  */
+                                 128 and 24 above; the kappa estimate uses min(8, this)  */
     int32_t reserved;         /* must be 0 */
     double beta1;             /* momentum: mom <- beta1 mom + U                          */
     double beta2;             /* statistics: S <- beta2 S + (1-beta2) outer(G) (beta2<1),

@@ -251,7 +251,10 @@ LaunchRef add_launch(Blob& blob, const std::vector<GemmTask>& tasks) {
     std::vector<TileRef> tiles;
     for (size_t i = 0; i < tasks.size(); ++i) {
         const int nt = ceil_div(tasks[i].M, kTile) * tasks[i].tiles_n;
-        for (int t = 0; t < nt; ++t) tiles.push_back({(int32_t)i, t});
+        const bool upper = (tasks[i].trans >> 4) & 1;
+        for (int t = 0; t < nt; ++t)
+            if (!upper || t / tasks[i].tiles_n <= t % tasks[i].tiles_n)
+                tiles.push_back({(int32_t)i, t});
     }
     LaunchRef L;
     L.tasks_off = blob.add(tasks);
@@ -425,7 +428,7 @@ int build_plan(shampoo_s* h) {
             t.ldc = fl.ld;
             t.M = t.N = bp.mb;
             t.K = bp.nb;
-            t.trans = 2;
+            t.trans = 2 | 16 | 32;   // symmetric: upper tiles, mirrored
             t.tiles_n = ceil_div(t.N, kTile);
             tasks.push_back(t);
             // R: op(A) = G_b^T (nb x mb), op(B) = G_b
@@ -433,7 +436,7 @@ int build_plan(shampoo_s* h) {
             t.ldc = fr.ld;
             t.M = t.N = bp.nb;
             t.K = bp.mb;
-            t.trans = 1;
+            t.trans = 1 | 16 | 32;
             t.tiles_n = ceil_div(t.N, kTile);
             tasks.push_back(t);
         }
@@ -702,7 +705,7 @@ int shampoo_create(const shampoo_config* cfg, int32_t n_tensors, const shampoo_t
     if (!h) return SHAMPOO_E_NOMEM;
     try {
         h->cfg = c;
-        // lanczos_steps == 0: 20 steps for factors up to 128, 32 above (lambda_max
+        // lanczos_steps == 0: 20 steps for factors up to 128, 24 above (lambda_max
         // to ~1e-9 relative on the workloads' statistics); 8 for the kappa estimate
         h->n = n_tensors;
         h->tensors.resize(n_tensors);
@@ -927,7 +930,7 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
     FactorDiag* diag = at<FactorDiag>(h, h->off_diag);
     int32_t* prec = at<int32_t>(h, h->off_prec);
     LanczosArgs la{};
-    la.steps = c.lanczos_steps > 0 ? c.lanczos_steps : 32;
+    la.steps = c.lanczos_steps > 0 ? c.lanczos_steps : 24;
     la.mode = 0;
     la.p = c.root_p;
     la.eps_rel = c.eps_rel;

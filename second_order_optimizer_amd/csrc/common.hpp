@@ -20,7 +20,9 @@ struct GemmTask {
     int32_t a_base, b_base, c_base;
     int32_t M, N, K;              // op(A) is M x K, op(B) is K x N
     int32_t lda, ldb, ldc;
-    int32_t trans;                // bit 0: op(A) = A^T, bit 1: op(B) = B^T
+    int32_t trans;                // bit 0: op(A) = A^T, bit 1: op(B) = B^T, bits 2/3:
+                                  // Newton operand on A/B, bit 4: upper tiles only
+                                  // (symmetric C), bit 5: mirror off-diagonal tiles
     int32_t tiles_n;              // ceil(N / 128)
     int32_t factor;               // gating factor id (-1: always run)
     int32_t norm_slot;            // first slot of per-tile ||C||^2 partials, -1: none

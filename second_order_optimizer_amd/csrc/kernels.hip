@@ -275,8 +275,8 @@ template <> struct WaveTile<double> {
 // C (type T) = alpha op(A) op(B) (+ beta C); A, B stored as TA, TB and
 // converted to T on the way into LDS (fp32 gradients into an fp64 product are
 // exact: fp32 x fp32 fits the fp64 mantissa).
-template <typename T, typename TA, typename TB>
-__global__ __launch_bounds__(256) void k_gemm(const GemmTask* __restrict__ tasks,
+template <typename T, typename TA, typename TB, int MINW>
+__global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__ tasks,
                                              const TileRef* __restrict__ tiles,
                                              const uint64_t* __restrict__ bases, GemmArgs args) {
     constexpr int BK = GemmTraits<T>::BK;
@@ -328,6 +328,9 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmTask* __restrict__ tasks
 
     const T alpha = T(args.alpha), beta = T(args.beta);
     const bool axpby = args.epi == EPI_AXPBY;
+    // symmetric result computed on upper tiles only: an off-diagonal tile
+    // also writes its transpose
+    const bool mirror = ((tk.trans >> 5) & 1) && ti != tj;
     double nrm = 0.0;
     wt.for_each(wm, wn, [&](int r, int c, T v) {
         const int i = i0 + r, j = j0 + c;
@@ -336,6 +339,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmTask* __restrict__ tasks
             T o = alpha * v;
             if (axpby) o += beta * (*p);
             *p = o;
+            if (mirror) C[(int64_t)j * tk.ldc + i] = o;
             nrm += double(o) * double(o);
         }
     });
@@ -697,11 +701,28 @@ __global__ __launch_bounds__(256) void k_lanczos(const LanczosJob* __restrict__ 
             __syncthreads();
             if (hf == 0 && r < n) wv[r] += acc;
         } else {
-            for (int j = t; j < n; j += 256) {
-                double acc = 0.0;
-                for (int i = 0; i < n; ++i) acc += (double)S[(int64_t)i * ld + j] * v1[i];
-                wv[j] = acc;
+            // wave w sums rows i = w (mod 4), lane l columns l + 64m: coalesced
+            // row segments, many loads in flight; the four partial vectors are
+            // added in a fixed order (S is symmetric, so column sums are S v)
+            double* part = reinterpret_cast<double*>(Ss);   // 4 x n doubles
+            const int wv_ = t >> 6, l = t & 63;
+            double acc[16];
+#pragma unroll
+            for (int m = 0; m < 16; ++m) acc[m] = 0.0;
+#pragma unroll 2
+            for (int i = wv_; i < n; i += 4) {
+                const double vi = v1[i];
+                const TM* row = S + (int64_t)i * ld;
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                    if (l + 64 * m < n) acc[m] += (double)row[l + 64 * m] * vi;
             }
+#pragma unroll
+            for (int m = 0; m < 16; ++m)
+                if (l + 64 * m < n) part[wv_ * n + l + 64 * m] = acc[m];
+            __syncthreads();
+            for (int j = t; j < n; j += 256)
+                wv[j] = (part[j] + part[n + j]) + (part[2 * n + j] + part[3 * n + j]);
         }
         __syncthreads();
         double d = 0.0;
@@ -1463,21 +1484,21 @@ __global__ __launch_bounds__(256) void k_sparse_rows(const SparseJob* __restrict
 hipError_t launch_gemm_f32(const GemmTask* tasks, const TileRef* tiles, int ntiles,
                            const uint64_t* bases, const GemmArgs& a, hipStream_t s) {
     if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL((k_gemm<float, float, float>), dim3(ntiles), dim3(256), 0, s, tasks, tiles,
+    hipLaunchKernelGGL((k_gemm<float, float, float, 1>), dim3(ntiles), dim3(256), 0, s, tasks, tiles,
                        bases, a);
     return hipGetLastError();
 }
 hipError_t launch_gemm_f64(const GemmTask* tasks, const TileRef* tiles, int ntiles,
                            const uint64_t* bases, const GemmArgs& a, hipStream_t s) {
     if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL((k_gemm<double, double, double>), dim3(ntiles), dim3(256), 0, s, tasks,
+    hipLaunchKernelGGL((k_gemm<double, double, double, 2>), dim3(ntiles), dim3(256), 0, s, tasks,
                        tiles, bases, a);
     return hipGetLastError();
 }
 hipError_t launch_gemm_f64_from_f32(const GemmTask* tasks, const TileRef* tiles, int ntiles,
                                     const uint64_t* bases, const GemmArgs& a, hipStream_t s) {
     if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL((k_gemm<double, float, float>), dim3(ntiles), dim3(256), 0, s, tasks,
+    hipLaunchKernelGGL((k_gemm<double, float, float, 2>), dim3(ntiles), dim3(256), 0, s, tasks,
                        tiles, bases, a);
     return hipGetLastError();
 }
