@@ -119,9 +119,10 @@ struct shampoo_s {
     int n_apply128 = 0;               // blocks of at most 128 x 128
     int64_t gram128_off = 0;
     int n_gram128 = 0;                // blocks of at most 128 x 128
-    int64_t lanczos_s_off = 0, lanczos_p_off = 0, ident_jobs_off = 0;   // every factor
-    int64_t lanczos_s_big_off = 0, lanczos_p_big_off = 0;               // factors with ld > 128
-    int n_lanczos_big = 0;
+    int64_t ident_jobs_off = 0;
+    int64_t lanczos_s_small_off = 0, lanczos_p_small_off = 0;   // factors with ld <= 128
+    int64_t lanczos_s_big_off = 0, lanczos_p_big_off = 0;       // factors with ld > 128
+    int n_lanczos_small = 0, n_lanczos_big = 0;
     int64_t blockchunks_off = 0, blocknorms_off = 0, rowchunks_off = 0;
     int n_blockchunks = 0, n_rowchunks = 0;
     std::vector<NewtonChunk> chunks32, chunks64;
@@ -169,6 +170,22 @@ int newton_stage_count(int p) {  // GEMM launches per iteration
     return s + 1;                  // M <- T^p M
 }
 
+LaunchRef add_launch(Blob& blob, const std::vector<GemmTask>& tasks) {
+    std::vector<TileRef> tiles;
+    for (size_t i = 0; i < tasks.size(); ++i) {
+        const int nt = ceil_div(tasks[i].M, kTile) * tasks[i].tiles_n;
+        const bool upper = (tasks[i].trans >> 4) & 1;
+        for (int t = 0; t < nt; ++t)
+            if (!upper || t / tasks[i].tiles_n <= t % tasks[i].tiles_n)
+                tiles.push_back({(int32_t)i, t});
+    }
+    LaunchRef L;
+    L.tasks_off = blob.add(tasks);
+    L.tiles_off = blob.add(tiles);
+    L.ntiles = (int)tiles.size();
+    return L;
+}
+
 // Builds the per-parity GEMM launches of one Newton chunk.
 void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& fids, int ld,
                         bool fp64, bool fused, int64_t scratch_off_bytes) {
@@ -177,7 +194,6 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
     const int64_t mat = (int64_t)ld * ld;
     const int64_t sbase = scratch_off_bytes / esz;  // scratch start in elements (arena base 0)
     const int tiles1 = ceil_div(ld, kTile);
-    const int tpt = tiles1 * tiles1;
     ch.ld = ld;
     ch.njobs = (int)fids.size();
     std::vector<FactorJob> jobs;
@@ -224,43 +240,21 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
                 st[0].push_back(mk(Mq, Mq, Mn, 4, fid));
                 continue;
             }
-            st[0].push_back(mk(Mq, Mq, T2, 4 | 8, fid));
+            // T, T^2, T^4 and M are symmetric (M is kept so by mirroring), so
+            // the squarings and the M update form upper tiles only (16) and
+            // mirror them (32); X = X T is formed in full
+            st[0].push_back(mk(Mq, Mq, T2, 4 | 8 | 16 | 32, fid));
             int k = 1;
             int64_t cur = T2;
             for (int e = 2; e < p; e *= 2) {
                 const int64_t nxt = (cur == T2) ? T4 : T2;
-                st[k++].push_back(mk(cur, cur, nxt, 0, fid));
+                st[k++].push_back(mk(cur, cur, nxt, 16 | 32, fid));
                 cur = nxt;
             }
-            st[k].push_back(mk(cur, Mq, Mn, 0, fid));
+            st[k].push_back(mk(cur, Mq, Mn, 16 | 32, fid));
         }
-        for (auto& tasks : st) {
-            std::vector<TileRef> tiles;
-            for (size_t i = 0; i < tasks.size(); ++i)
-                for (int t = 0; t < tpt; ++t) tiles.push_back({(int32_t)i, t});
-            LaunchRef L;
-            L.tasks_off = h->blob.add(tasks);
-            L.tiles_off = h->blob.add(tiles);
-            L.ntiles = (int)tiles.size();
-            ch.stages[q].push_back(L);
-        }
+        for (auto& tasks : st) ch.stages[q].push_back(add_launch(h->blob, tasks));
     }
-}
-
-LaunchRef add_launch(Blob& blob, const std::vector<GemmTask>& tasks) {
-    std::vector<TileRef> tiles;
-    for (size_t i = 0; i < tasks.size(); ++i) {
-        const int nt = ceil_div(tasks[i].M, kTile) * tasks[i].tiles_n;
-        const bool upper = (tasks[i].trans >> 4) & 1;
-        for (int t = 0; t < nt; ++t)
-            if (!upper || t / tasks[i].tiles_n <= t % tasks[i].tiles_n)
-                tiles.push_back({(int32_t)i, t});
-    }
-    LaunchRef L;
-    L.tasks_off = blob.add(tasks);
-    L.tiles_off = blob.add(tiles);
-    L.ntiles = (int)tiles.size();
-    return L;
 }
 
 int build_plan(shampoo_s* h) {
@@ -525,15 +519,16 @@ int build_plan(shampoo_s* h) {
             d.dim = f.dim;
             h->diag_init.push_back(d);
         }
-        h->lanczos_s_off = blob.add(js);
-        h->lanczos_p_off = blob.add(jp);
-        std::vector<LanczosJob> jsb, jpb;
-        for (int i = 0; i < nf; ++i)
-            if (h->factors[i].ld > 128) {
-                jsb.push_back(js[i]);
-                jpb.push_back(jp[i]);
-            }
+        std::vector<LanczosJob> jss, jps, jsb, jpb;
+        for (int i = 0; i < nf; ++i) {
+            const bool big = h->factors[i].ld > 128;
+            (big ? jsb : jss).push_back(js[i]);
+            (big ? jpb : jps).push_back(jp[i]);
+        }
+        h->n_lanczos_small = (int)jss.size();
         h->n_lanczos_big = (int)jsb.size();
+        h->lanczos_s_small_off = blob.add(jss);
+        h->lanczos_p_small_off = blob.add(jps);
         h->lanczos_s_big_off = blob.add(jsb);
         h->lanczos_p_big_off = blob.add(jpb);
         h->ident_jobs_off = blob.add(ident);
@@ -942,39 +937,49 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
     lp.mode = 1;
     lp.steps = std::min(la.steps, 8);  // kappa estimate: a factor-2 decision
     int rc = SHAMPOO_OK;
+    auto lanczos = [&](int64_t small_off, int64_t big_off, bool on_stats, bool with_small,
+                       const LanczosArgs& a) -> int {
+        const void* base = h->arena;
+        ProfScope ps(h, on_stats ? PC_LANCZOS_S : PC_LANCZOS_P, s,
+                     h->n_lanczos_big > 0 || (with_small && h->n_lanczos_small > 0));
+        int r = SHAMPOO_OK;
+        if (with_small)
+            r = hip_err(launch_lanczos(tab<LanczosJob>(h, small_off), h->n_lanczos_small, base,
+                                       on_stats, false, a, s));
+        if (r) return r;
+        return hip_err(launch_lanczos(tab<LanczosJob>(h, big_off), h->n_lanczos_big, base, on_stats,
+                                      true, a, s));
+    };
     if (use_fp32(c)) {
         // factors up to 128: everything inside the fused kernel; larger ones:
         // Lanczos on S, batched fp32 Newton, Lanczos on the root
-        {
-            ProfScope ps(h, PC_LANCZOS_S, s, h->n_lanczos_big > 0);
-            rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_s_big_off), h->n_lanczos_big,
-                                        h->arena, true, la, s));
-        }
+        rc = lanczos(h->lanczos_s_small_off, h->lanczos_s_big_off, true, false, la);
         if (rc) return rc;
         rc = run_newton(h, h->chunks32, false, nullptr, 0, prec, s);
         if (rc) return rc;
         lp.auto_route = c.root_mode == SHAMPOO_ROOT_AUTO ? 1 : 0;
-        {
-            ProfScope ps(h, PC_LANCZOS_P, s, h->n_lanczos_big > 0);
-            rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_p_big_off), h->n_lanczos_big,
-                                        h->arena, false, lp, s));
-        }
+        rc = lanczos(h->lanczos_p_small_off, h->lanczos_p_big_off, false, false, lp);
         if (rc) return rc;
         if (c.root_mode == SHAMPOO_ROOT_AUTO)
             rc = run_newton(h, h->chunks64, true, prec, 1, prec, s);
         return rc;
     }
     // all fp64
+    LanczosArgs la_small = la;
+    la_small.steps = c.lanczos_steps > 0 ? c.lanczos_steps : 20;
     {
         ProfScope ps(h, PC_LANCZOS_S, s);
-        rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_s_off), nf, h->arena, true, la, s));
+        rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_s_small_off), h->n_lanczos_small,
+                                    h->arena, true, false, la_small, s));
+        if (!rc)
+            rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_s_big_off), h->n_lanczos_big,
+                                        h->arena, true, true, la, s));
     }
     if (rc) return rc;
     rc = run_newton(h, h->chunks64, true, nullptr, 1, prec, s);
     if (rc) return rc;
     lp.auto_route = 0;
-    ProfScope ps(h, PC_LANCZOS_P, s);
-    return hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_p_off), nf, h->arena, false, lp, s));
+    return lanczos(h->lanczos_p_small_off, h->lanczos_p_big_off, false, true, lp);
 }
 
 int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const float* const* grads,

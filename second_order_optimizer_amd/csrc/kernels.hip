@@ -643,132 +643,10 @@ __device__ __forceinline__ double lanczos_lds(const TM* A, int pitch, int n, int
     return lm;
 }
 
-constexpr int kLanczosLdsN = 128;   // matrices up to this size are staged in LDS
-
-template <typename TM>
-__global__ __launch_bounds__(256) void k_lanczos(const LanczosJob* __restrict__ jobs,
-                                                const TM* __restrict__ arena, LanczosArgs args) {
-    __shared__ double v0[kLanczosMaxN], v1[kLanczosMaxN], wv[kLanczosMaxN];
-    __shared__ double al[kLanczosMaxSteps], be[kLanczosMaxSteps];
-    __shared__ double red[4];
-    __shared__ float Ss[kLanczosLdsN * (kLanczosLdsN + 1)];
-    __shared__ int m_used;
-    const LanczosJob jb = jobs[blockIdx.x];
-    const int n = jb.n, ld = jb.ld;
-    const TM* S = arena + jb.off;
-    const int t = threadIdx.x;
-    const int steps = min(args.steps, min(n, kLanczosMaxSteps));
-    const bool in_lds = n <= kLanczosLdsN;
-    constexpr int SP = kLanczosLdsN + 1;  // LDS pitch: row r, column j at bank r + j
-    if (in_lds) {
-        // symmetric matrix: only its upper triangle is read (mirrored in LDS)
-        for (int e = t; e < n * n; e += 256) {
-            const int i = e / n, j = e % n;
-            if (j >= i) {
-                const float x = (float)S[(int64_t)i * ld + j];
-                Ss[i * SP + j] = x;
-                Ss[j * SP + i] = x;
-            }
-        }
-    }
-
-    // deterministic start vector from an integer hash, normalised
-    double s2 = 0.0;
-    for (int i = t; i < n; i += 256) {
-        uint32_t hsh = (uint32_t)i * 2654435761u + 0x9E3779B9u;
-        hsh ^= hsh >> 15; hsh *= 2246822519u; hsh ^= hsh >> 13;
-        const double x = 0.5 + (double)(hsh & 0xFFFFFF) / 16777216.0;  // in [0.5, 1.5)
-        v1[i] = x;
-        v0[i] = 0.0;
-        s2 += x * x;
-    }
-    const double nv = sqrt(block_sum_256(s2, red));
-    for (int i = t; i < n; i += 256) v1[i] /= nv;
-    if (t == 0) m_used = steps;
-    __syncthreads();
-
-    double beta_prev = 0.0;
-    for (int k = 0; k < steps; ++k) {
-        // w = S v
-        if (in_lds) {
-            // thread (r, half) sums row r over one half of the columns
-            const int r = t & 127, hf = t >> 7;
-            const int j0 = hf * ((n + 1) / 2), j1 = min(n, j0 + (n + 1) / 2);
-            double acc = 0.0;
-            if (r < n)
-                for (int j = j0; j < j1; ++j) acc += (double)Ss[r * SP + j] * v1[j];
-            if (hf == 1 && r < n) wv[r] = acc;
-            __syncthreads();
-            if (hf == 0 && r < n) wv[r] += acc;
-        } else {
-            // wave w sums rows i = w (mod 4), lane l columns l + 64m: coalesced
-            // row segments, many loads in flight; the four partial vectors are
-            // added in a fixed order (S is symmetric, so column sums are S v)
-            double* part = reinterpret_cast<double*>(Ss);   // 4 x n doubles
-            const int wv_ = t >> 6, l = t & 63;
-            double acc[16];
-#pragma unroll
-            for (int m = 0; m < 16; ++m) acc[m] = 0.0;
-#pragma unroll 2
-            for (int i = wv_; i < n; i += 4) {
-                const double vi = v1[i];
-                const TM* row = S + (int64_t)i * ld;
-#pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    if (l + 64 * m < n) acc[m] += (double)row[l + 64 * m] * vi;
-            }
-#pragma unroll
-            for (int m = 0; m < 16; ++m)
-                if (l + 64 * m < n) part[wv_ * n + l + 64 * m] = acc[m];
-            __syncthreads();
-            for (int j = t; j < n; j += 256)
-                wv[j] = (part[j] + part[n + j]) + (part[2 * n + j] + part[3 * n + j]);
-        }
-        __syncthreads();
-        double d = 0.0;
-        for (int i = t; i < n; i += 256) d += wv[i] * v1[i];
-        const double alpha = block_sum_256(d, red);
-        double q = 0.0;
-        for (int i = t; i < n; i += 256) {
-            const double x = wv[i] - alpha * v1[i] - beta_prev * v0[i];
-            wv[i] = x;
-            q += x * x;
-        }
-        const double beta = sqrt(block_sum_256(q, red));
-        if (t == 0) { al[k] = alpha; be[k] = beta; }
-        const bool stop = !(beta > 1e-13 * fabs(alpha)) || !isfinite(alpha) || !isfinite(beta);
-        if (stop) {
-            if (t == 0) m_used = k + 1;
-            __syncthreads();
-            break;
-        }
-        for (int i = t; i < n; i += 256) {
-            v0[i] = v1[i];
-            v1[i] = wv[i] / beta;
-        }
-        beta_prev = beta;
-        __syncthreads();
-    }
-    __syncthreads();
-    if (t != 0) return;
-    const int m = m_used;
-    bool finite = true;
-    double lo = 0.0, hi = 0.0;
-    for (int k = 0; k < m; ++k) {
-        const double r = (k ? fabs(be[k - 1]) : 0.0) + (k + 1 < m ? fabs(be[k]) : 0.0);
-        if (!isfinite(al[k]) || !isfinite(r)) finite = false;
-        lo = k ? fmin(lo, al[k] - r) : al[k] - r;
-        hi = k ? fmax(hi, al[k] + r) : al[k] + r;
-    }
-    double lmax = NAN;
-    if (finite) {
-        double a = lo, b = hi;
-        for (int it = 0; it < 200 && b - a > 1e-15 * fmax(fabs(a), fabs(b)); ++it) {
-            const double mid = 0.5 * (a + b);
-            if (sturm_count(al, be, m, mid) >= m) b = mid; else a = mid;
-        }
-        lmax = b;
-    }
+// Writes one factor's Lanczos result: mode 0 (statistics): lambda_max, eps,
+// status; mode 1 (root): kappa estimate and, in AUTO mode, the routing flag.
+__device__ __forceinline__ void lanczos_finish(const LanczosArgs& args, const LanczosJob& jb,
+                                               bool finite, double lmax) {
     FactorDiag& dg = args.diag[jb.factor];
     if (args.mode == 0) {
         // statistics: lambda_max -> eps; status bits for the Newton pass
@@ -796,10 +674,137 @@ __global__ __launch_bounds__(256) void k_lanczos(const LanczosJob* __restrict__ 
     }
 }
 
+constexpr int kLanczosLdsN = 128;   // matrices up to this size are staged in LDS
+
+// Largest eigenvalue estimate of one symmetric factor (n <= 128) per
+// workgroup: the matrix (upper triangle, mirrored) is staged into LDS in fp32
+// and lanczos_lds runs on it.
+template <typename TM>
+__global__ __launch_bounds__(256) void k_lanczos(const LanczosJob* __restrict__ jobs,
+                                                const TM* __restrict__ arena, LanczosArgs args) {
+    __shared__ __align__(16) float Ss[kLanczosLdsN * (kLanczosLdsN + 1)];
+    __shared__ LanczosLds lz;
+    const LanczosJob jb = jobs[blockIdx.x];
+    const int n = jb.n, ld = jb.ld;
+    const TM* S = arena + jb.off;
+    constexpr int SP = kLanczosLdsN + 1;
+#pragma unroll 8
+    for (int e = threadIdx.x; e < 128 * 128; e += 256) {
+        const int i = e >> 7, j = e & 127;
+        if (i < n && j < n && j >= i) {
+            const float x = (float)S[(int64_t)i * ld + j];
+            Ss[i * SP + j] = x;
+            Ss[j * SP + i] = x;
+        }
+    }
+    __syncthreads();
+    const double lmax = lanczos_lds<float>(Ss, SP, n, args.steps, lz);
+    if (threadIdx.x == 0) lanczos_finish(args, jb, isfinite(lmax), lmax);
+}
+
+// Same for one factor of 129..1024 per workgroup of 512 threads, matrix read
+// from memory: wave w sums rows i = w (mod 8), lane l columns l + 64m
+// (coalesced row segments, up to 16 loads in flight per row), and the eight
+// partial vectors are added in a fixed order (S is symmetric, so these column
+// sums are S v).  Vectors in fp64 in LDS.
+struct LanczosBig {
+    double v0[kLanczosMaxN], v1[kLanczosMaxN], wv[kLanczosMaxN];
+    double part[8 * kLanczosMaxN];
+    double al[kLanczosMaxSteps], be[kLanczosMaxSteps];
+    double red[8];
+    double res;
+    int m_used, stop;
+};
+
+__device__ __forceinline__ double block_sum_512(double v, double* red) {
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
+}
+
+template <typename TM>
+__global__ __launch_bounds__(512) void k_lanczos_big(const LanczosJob* __restrict__ jobs,
+                                                    const TM* __restrict__ arena, LanczosArgs args) {
+    __shared__ LanczosBig L;
+    const LanczosJob jb = jobs[blockIdx.x];
+    const int n = jb.n, ld = jb.ld;
+    const TM* S = arena + jb.off;
+    const int t = threadIdx.x, w = t >> 6, l = t & 63;
+    const int steps = min(args.steps, min(n, kLanczosMaxSteps));
+
+    double s2 = 0.0;
+    for (int i = t; i < n; i += 512) {
+        uint32_t hsh = (uint32_t)i * 2654435761u + 0x9E3779B9u;
+        hsh ^= hsh >> 15; hsh *= 2246822519u; hsh ^= hsh >> 13;
+        const double x = 0.5 + (double)(hsh & 0xFFFFFF) / 16777216.0;
+        L.v1[i] = x;
+        L.v0[i] = 0.0;
+        s2 += x * x;
+    }
+    const double inv = 1.0 / sqrt(block_sum_512(s2, L.red));
+    for (int i = t; i < n; i += 512) L.v1[i] *= inv;
+    if (t == 0) L.m_used = steps;
+    __syncthreads();
+
+    double beta_prev = 0.0;
+    for (int k = 0; k < steps; ++k) {
+        double acc[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) acc[m] = 0.0;
+#pragma unroll 2
+        for (int i = w; i < n; i += 8) {
+            const double vi = L.v1[i];
+            const TM* row = S + (int64_t)i * ld;
+#pragma unroll
+            for (int m = 0; m < 16; ++m)
+                if (l + 64 * m < n) acc[m] += (double)row[l + 64 * m] * vi;
+        }
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+            if (l + 64 * m < n) L.part[w * n + l + 64 * m] = acc[m];
+        __syncthreads();
+        double d = 0.0;
+        for (int j = t; j < n; j += 512) {
+            const double x = ((L.part[j] + L.part[n + j]) + (L.part[2 * n + j] + L.part[3 * n + j])) +
+                             ((L.part[4 * n + j] + L.part[5 * n + j]) + (L.part[6 * n + j] + L.part[7 * n + j]));
+            L.wv[j] = x;
+            d += x * L.v1[j];
+        }
+        const double alpha = block_sum_512(d, L.red);
+        double q = 0.0;
+        for (int j = t; j < n; j += 512) {
+            const double x = L.wv[j] - alpha * L.v1[j] - beta_prev * L.v0[j];
+            L.wv[j] = x;
+            q += x * x;
+        }
+        const double beta = sqrt(block_sum_512(q, L.red));
+        if (t == 0) { L.al[k] = alpha; L.be[k] = beta; }
+        const bool stop = !(beta > 1e-13 * fabs(alpha)) || !isfinite(alpha) || !isfinite(beta);
+        if (stop) {
+            if (t == 0) L.m_used = k + 1;
+            __syncthreads();
+            break;
+        }
+        for (int j = t; j < n; j += 512) {
+            L.v0[j] = L.v1[j];
+            L.v1[j] = L.wv[j] / beta;
+        }
+        beta_prev = beta;
+        __syncthreads();
+    }
+    __syncthreads();
+    if (w == 0) {
+        const double lm = tridiag_max_wave(L.al, L.be, L.m_used);
+        if (l == 0) lanczos_finish(args, jb, isfinite(lm), lm);
+    }
+}
+
 // ======================================================= coupled Newton
 // Coupled Newton iteration for the inverse p-th root (Guo & Higham, SIAM J.
-// Matrix Anal. Appl. 28(3), 2006).  With A = sym(S) + eps I and
-// z = (p+1) / (2 lambda_max(A)):  X_0 = z^(1/p) I, M_0 = z A; then
+// Matrix Anal. Appl. 28(3), 2006).  With A = S + eps I (S read from its upper
+// triangle) and z = (p+1) / (2 lambda_max(A)):  X_0 = z^(1/p) I, M_0 = z A; then
 // T = ((p+1) I - M)/p, X <- X T, M <- T^p M.  M_k = X_k^p A throughout, so
 // M -> I and X -> A^(-1/p).  Padded rows/columns carry M = I, X = I and stay
 // decoupled (block diagonal).
@@ -1509,16 +1514,24 @@ hipError_t launch_gram128(const GramJob* jobs, int njobs, const uint64_t* bases,
     return hipGetLastError();
 }
 hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, bool fp64_matrix,
-                          const LanczosArgs& a, hipStream_t s) {
+                          bool big, const LanczosArgs& a, hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
-    // the kernel works on a fixed-size LDS layout; guard its limits here
     if (a.steps < 1) return hipErrorInvalidValue;
-    if (fp64_matrix)
-        hipLaunchKernelGGL(k_lanczos<double>, dim3(njobs), dim3(256), 0, s, jobs,
-                           static_cast<const double*>(arena), a);
-    else
-        hipLaunchKernelGGL(k_lanczos<float>, dim3(njobs), dim3(256), 0, s, jobs,
-                           static_cast<const float*>(arena), a);
+    if (big) {
+        if (fp64_matrix)
+            hipLaunchKernelGGL(k_lanczos_big<double>, dim3(njobs), dim3(512), 0, s, jobs,
+                               static_cast<const double*>(arena), a);
+        else
+            hipLaunchKernelGGL(k_lanczos_big<float>, dim3(njobs), dim3(512), 0, s, jobs,
+                               static_cast<const float*>(arena), a);
+    } else {
+        if (fp64_matrix)
+            hipLaunchKernelGGL(k_lanczos<double>, dim3(njobs), dim3(256), 0, s, jobs,
+                               static_cast<const double*>(arena), a);
+        else
+            hipLaunchKernelGGL(k_lanczos<float>, dim3(njobs), dim3(256), 0, s, jobs,
+                               static_cast<const float*>(arena), a);
+    }
     return hipGetLastError();
 }
 hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, const double* stats,

@@ -66,7 +66,7 @@ hipError_t launch_gemm_f64_from_f32(const GemmTask* tasks, const TileRef* tiles,
 hipError_t launch_gram128(const GramJob* jobs, int njobs, const uint64_t* bases, double* stats,
                           double alpha, double beta, hipStream_t s);
 hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, bool fp64_matrix,
-                          const LanczosArgs& a, hipStream_t s);
+                          bool big, const LanczosArgs& a, hipStream_t s);
 hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, const double* stats,
                               void* scratch, const FactorDiag* diag, const NewtonArgs& a,
                               hipStream_t s);
