@@ -366,11 +366,11 @@ typedef float gf4 __attribute__((ext_vector_type(4)));
 // One 64 x 64 quadrant (qi, qj) of L = G G^T (RSIDE = false) or R = G^T G.
 // DIAG: qi == qj, only tiles i <= j are formed.  Lane group g supplies
 // k = k0 + 4g + s in MFMA step s.
-template <bool DIAG, bool RSIDE>
+template <bool DIAG, bool RSIDE, int JLO = 0, int JHI = 4>
 __device__ __forceinline__ void gram_quadrant(const float* Gs, int qi, int qj, int K, double* S,
                                               int ldS, int nvalid, double alpha, double beta,
                                               int c, int g) {
-    if (qi * 64 >= nvalid || qj * 64 >= nvalid) return;
+    if (qi * 64 >= nvalid || qj * 64 + JLO * 16 >= nvalid) return;
     gd4 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -383,7 +383,7 @@ __device__ __forceinline__ void gram_quadrant(const float* Gs, int qi, int qj, i
             for (int i = 0; i < 4; ++i)
                 a[i] = *reinterpret_cast<const gf4*>(&Gs[(qi * 64 + i * 16 + c) * kGP + k0 + 4 * g]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = JLO; j < JHI; ++j)
                 b[j] = DIAG ? a[j]
                             : *reinterpret_cast<const gf4*>(&Gs[(qj * 64 + j * 16 + c) * kGP + k0 + 4 * g]);
 #pragma unroll
@@ -391,7 +391,7 @@ __device__ __forceinline__ void gram_quadrant(const float* Gs, int qi, int qj, i
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                    for (int j = JLO; j < JHI; ++j)
                         if (!DIAG || i <= j)
                             acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(
                                 (double)a[i][s], (double)b[j][s], acc[i][j], 0, 0, 0);
@@ -403,11 +403,11 @@ __device__ __forceinline__ void gram_quadrant(const float* Gs, int qi, int qj, i
 #pragma unroll
                 for (int i = 0; i < 4; ++i) a[i] = (double)row[qi * 64 + i * 16 + c];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) b[j] = DIAG ? a[j] : (double)row[qj * 64 + j * 16 + c];
+                for (int j = JLO; j < JHI; ++j) b[j] = DIAG ? a[j] : (double)row[qj * 64 + j * 16 + c];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                    for (int j = JLO; j < JHI; ++j)
                         if (!DIAG || i <= j)
                             acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
             }
@@ -416,7 +416,7 @@ __device__ __forceinline__ void gram_quadrant(const float* Gs, int qi, int qj, i
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = JLO; j < JHI; ++j) {
             if (DIAG && i > j) continue;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -429,7 +429,7 @@ __device__ __forceinline__ void gram_quadrant(const float* Gs, int qi, int qj, i
         }
 }
 
-__global__ __launch_bounds__(256, 2) void k_gram128(const GramJob* __restrict__ jobs,
+__global__ __launch_bounds__(512, 2) void k_gram128(const GramJob* __restrict__ jobs,
                                                    const uint64_t* __restrict__ bases,
                                                    double* __restrict__ stats, double alpha,
                                                    double beta) {
@@ -442,11 +442,11 @@ __global__ __launch_bounds__(256, 2) void k_gram128(const GramJob* __restrict__ 
     // ---- stage G (rows x cols) into LDS, zero padded
     const bool vec = (nb % 4 == 0) && (ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(G) & 15) == 0);
     {
-        const int c4 = t & 31, r0 = t >> 5;   // 32 float4 per row, 8 rows per pass
-        float4 buf[16];
+        const int c4 = t & 31, r0 = t >> 5;   // 32 float4 per row, 16 rows per pass
+        float4 buf[8];
 #pragma unroll
-        for (int p = 0; p < 16; ++p) {
-            const int r = r0 + 8 * p, c = 4 * c4;
+        for (int p = 0; p < 8; ++p) {
+            const int r = r0 + 16 * p, c = 4 * c4;
             if (r < mb && c < nb) {
                 if (vec) {
                     buf[p] = *reinterpret_cast<const float4*>(G + (int64_t)r * ld + c);
@@ -461,26 +461,27 @@ __global__ __launch_bounds__(256, 2) void k_gram128(const GramJob* __restrict__ 
             }
         }
 #pragma unroll
-        for (int p = 0; p < 16; ++p)
-            *reinterpret_cast<float4*>(&Gs[(r0 + 8 * p) * kGP + 4 * c4]) = buf[p];
+        for (int p = 0; p < 8; ++p)
+            *reinterpret_cast<float4*>(&Gs[(r0 + 16 * p) * kGP + 4 * c4]) = buf[p];
     }
     __syncthreads();
 
+    // eight waves: L and R each as two diagonal quadrants (10 tiles each) and
+    // the off-diagonal quadrant split into two halves of 8 tiles
     const int lane = t & 63, w = t >> 6;
     const int c = lane & 15, g = lane >> 4;
     const int KL = (nb + 15) & ~15, KR = (mb + 15) & ~15;
     double* L = stats + jb.l_off;
     double* R = stats + jb.r_off;
-    if (w == 0) {
-        gram_quadrant<true, false>(Gs, 0, 0, KL, L, jb.ld_l, mb, alpha, beta, c, g);
-        gram_quadrant<true, false>(Gs, 1, 1, KL, L, jb.ld_l, mb, alpha, beta, c, g);
-    } else if (w == 1) {
-        gram_quadrant<false, false>(Gs, 0, 1, KL, L, jb.ld_l, mb, alpha, beta, c, g);
-    } else if (w == 2) {
-        gram_quadrant<true, true>(Gs, 0, 0, KR, R, jb.ld_r, nb, alpha, beta, c, g);
-        gram_quadrant<true, true>(Gs, 1, 1, KR, R, jb.ld_r, nb, alpha, beta, c, g);
-    } else {
-        gram_quadrant<false, true>(Gs, 0, 1, KR, R, jb.ld_r, nb, alpha, beta, c, g);
+    switch (w) {
+        case 0: gram_quadrant<true, false>(Gs, 0, 0, KL, L, jb.ld_l, mb, alpha, beta, c, g); break;
+        case 1: gram_quadrant<true, false>(Gs, 1, 1, KL, L, jb.ld_l, mb, alpha, beta, c, g); break;
+        case 2: gram_quadrant<false, false, 0, 2>(Gs, 0, 1, KL, L, jb.ld_l, mb, alpha, beta, c, g); break;
+        case 3: gram_quadrant<false, false, 2, 4>(Gs, 0, 1, KL, L, jb.ld_l, mb, alpha, beta, c, g); break;
+        case 4: gram_quadrant<true, true>(Gs, 0, 0, KR, R, jb.ld_r, nb, alpha, beta, c, g); break;
+        case 5: gram_quadrant<true, true>(Gs, 1, 1, KR, R, jb.ld_r, nb, alpha, beta, c, g); break;
+        case 6: gram_quadrant<false, true, 0, 2>(Gs, 0, 1, KR, R, jb.ld_r, nb, alpha, beta, c, g); break;
+        default: gram_quadrant<false, true, 2, 4>(Gs, 0, 1, KR, R, jb.ld_r, nb, alpha, beta, c, g); break;
     }
 }
 
@@ -1510,7 +1511,7 @@ hipError_t launch_gemm_f64_from_f32(const GemmTask* tasks, const TileRef* tiles,
 hipError_t launch_gram128(const GramJob* jobs, int njobs, const uint64_t* bases, double* stats,
                           double alpha, double beta, hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_gram128, dim3(njobs), dim3(256), 0, s, jobs, bases, stats, alpha, beta);
+    hipLaunchKernelGGL(k_gram128, dim3(njobs), dim3(512), 0, s, jobs, bases, stats, alpha, beta);
     return hipGetLastError();
 }
 hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, bool fp64_matrix,
