@@ -539,109 +539,110 @@ __device__ __forceinline__ double tridiag_max_wave(const double* al, const doubl
     return hi;
 }
 
-// Scratch of the in-LDS Lanczos (matrices of at most 128).
-struct LanczosLds {
-    double v0[128], v1[128], wv[128];
+// 128 x 128 fp32 matrices in LDS ("slots"): row pitch 129 floats, the column
+// index stored with its bits 2 and 5 exchanged.  With this layout the MFMA
+// operand reads of the fused kernels (lane (h, c) at row c, column k + 4h, or
+// at row k + 4h, column c), their strip stores and the row reads of the
+// Lanczos product each hit 64 distinct banks, and every address is a
+// per-lane base plus a compile-time offset.
+constexpr int kSP = 129;
+__host__ __device__ constexpr int pcol(int j) { return (j & ~0x24) | ((j & 4) << 3) | ((j >> 3) & 4); }
+__device__ __forceinline__ int sidx(int r, int j) { return r * kSP + pcol(j); }
+
+// Stages the symmetric n x n matrix whose upper triangle is at S (row pitch
+// ld, n <= 128) into a slot in fp32, zero outside n x n.
+template <typename TM>
+__device__ __forceinline__ void stage_sym(float* slot, const TM* S, int n, int ld) {
+#pragma unroll 4
+    for (int e = threadIdx.x; e < 128 * 128; e += 256) {
+        const int i = e >> 7, j = e & 127;
+        if (j >= i) {
+            const float x = (j < n) ? (float)S[(int64_t)i * ld + j] : 0.f;
+            slot[sidx(i, j)] = x;
+            slot[sidx(j, i)] = x;
+        }
+    }
+}
+
+// Scratch of the slot Lanczos.
+struct LanczosSlot {
+    double v1[128];
     double al[kLanczosMaxSteps], be[kLanczosMaxSteps];
+    double ra[4], rb[4];
     double res;
-    int m_used, stop;
 };
 
-// Largest Ritz value of an n x n symmetric matrix held in LDS
-// (A[i * pitch + j], n <= 128) after up to `steps` Lanczos steps; all 256
-// threads take part in the matrix-vector product, wave 0 does the vector work.
-template <typename TM>
-__device__ __forceinline__ double lanczos_lds(const TM* A, int pitch, int n, int steps, LanczosLds& L) {
+// Largest Ritz value of the symmetric n x n matrix held in a slot (entries
+// outside n x n zero, or an identity block that is decoupled from the rest)
+// after up to `steps` Lanczos steps.  Thread (wave w, lane l) owns row
+// r = 32w + l%32 and half of its columns; the two halves meet in one shuffle,
+// so v_r, the previous v_r and the new w_r stay in registers and only v is
+// shared through LDS.  Sums run in a fixed order: every thread sees the same
+// alpha and beta, so the early stop is uniform.
+__device__ __forceinline__ double lanczos_slot(const float* slot, int n, int steps, LanczosSlot& L) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int r = 32 * w + (lane & 31), hf = lane >> 5;
     steps = min(steps, min(n, kLanczosMaxSteps));
-    if (w == 0) {
-        double s2 = 0.0;
-        for (int i = lane; i < n; i += 64) {
-            uint32_t hsh = (uint32_t)i * 2654435761u + 0x9E3779B9u;
-            hsh ^= hsh >> 15; hsh *= 2246822519u; hsh ^= hsh >> 13;
-            const double x = 0.5 + (double)(hsh & 0xFFFFFF) / 16777216.0;
-            L.v1[i] = x;
-            L.v0[i] = 0.0;
-            s2 += x * x;
-        }
-        const double inv = 1.0 / sqrt(wave_sum(s2));
-        for (int i = lane; i < n; i += 64) L.v1[i] *= inv;
-        if (lane == 0) { L.m_used = steps; L.stop = 0; }
+    double v = 0.0;
+    if (r < n) {
+        uint32_t hsh = (uint32_t)r * 2654435761u + 0x9E3779B9u;
+        hsh ^= hsh >> 15; hsh *= 2246822519u; hsh ^= hsh >> 13;
+        v = 0.5 + (double)(hsh & 0xFFFFFF) / 16777216.0;
     }
+    {
+        const double s2 = wave_sum(hf == 0 ? v * v : 0.0);
+        if (lane == 0) L.ra[w] = s2;
+        __syncthreads();
+        v /= sqrt((L.ra[0] + L.ra[1]) + (L.ra[2] + L.ra[3]));
+    }
+    if (hf == 0) L.v1[r] = v;
     __syncthreads();
-    double beta_prev = 0.0;
-    // matrix-vector product: thread t takes rows 4(t>>3)..+3 and columns
-    // 16(t&7)..+15 (v in registers, independent loads), then a 3-level
-    // shuffle sum over the 8 column blocks of a row group
-    const int rg = t >> 3, cb = t & 7;
+    double v0 = 0.0, beta_prev = 0.0;
+    int m_used = steps;
+    // physical columns 32hf + 64u + q hold logical columns pcol(64u + q) + 4hf
+    const float* Ar = slot + r * kSP + 32 * hf;
+    const double* vb = L.v1 + 4 * hf;
     for (int k = 0; k < steps; ++k) {
-        double vr[16];
+        double s[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int j = 16 * cb + q;
-            vr[q] = (j < n) ? L.v1[j] : 0.0;
-        }
-        double acc[4];
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * rg + i;
-            double s = 0.0;
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int j = 16 * cb + q;
-                const double aij = (r < n && j < n) ? (double)A[r * pitch + j] : 0.0;
-                s += aij * vr[q];
+            for (int q = 0; q < 32; ++q) {
+                const int off = 64 * u + q;
+                s[q & 3] = fma((double)Ar[off], vb[pcol(off)], s[q & 3]);
             }
-            acc[i] = s;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[i] += __shfl_xor(acc[i], 1, 64);
-            acc[i] += __shfl_xor(acc[i], 2, 64);
-            acc[i] += __shfl_xor(acc[i], 4, 64);
-        }
-        if (cb == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (4 * rg + i < n) L.wv[4 * rg + i] = acc[i];
-        }
+        double wr = (s[0] + s[1]) + (s[2] + s[3]);
+        wr += __shfl_xor(wr, 32, 64);
+        const double d = wave_sum(hf == 0 ? wr * v : 0.0);
+        if (lane == 0) L.ra[w] = d;
         __syncthreads();
-        if (w == 0) {
-            double d = 0.0;
-            for (int i = lane; i < n; i += 64) d += L.wv[i] * L.v1[i];
-            const double alpha = wave_sum(d);
-            double q = 0.0;
-            for (int i = lane; i < n; i += 64) {
-                const double x = L.wv[i] - alpha * L.v1[i] - beta_prev * L.v0[i];
-                L.wv[i] = x;
-                q += x * x;
-            }
-            const double beta = sqrt(wave_sum(q));
-            const bool stop = !(beta > 1e-13 * fabs(alpha)) || !isfinite(alpha) || !isfinite(beta);
-            if (lane == 0) {
-                L.al[k] = alpha;
-                L.be[k] = beta;
-                L.stop = stop ? 1 : 0;
-                if (stop) L.m_used = k + 1;
-            }
-            if (!stop)
-                for (int i = lane; i < n; i += 64) {
-                    L.v0[i] = L.v1[i];
-                    L.v1[i] = L.wv[i] / beta;
-                }
-            beta_prev = beta;
-        }
+        const double alpha = (L.ra[0] + L.ra[1]) + (L.ra[2] + L.ra[3]);
+        const double x = wr - alpha * v - beta_prev * v0;
+        const double q2 = wave_sum(hf == 0 ? x * x : 0.0);
+        if (lane == 0) L.rb[w] = q2;
         __syncthreads();
-        if (L.stop) break;
+        const double beta = sqrt((L.rb[0] + L.rb[1]) + (L.rb[2] + L.rb[3]));
+        if (t == 0) {
+            L.al[k] = alpha;
+            L.be[k] = beta;
+        }
+        if (!(beta > 1e-13 * fabs(alpha)) || !isfinite(alpha) || !isfinite(beta)) {
+            m_used = k + 1;
+            break;
+        }
+        v0 = v;
+        v = x / beta;
+        if (hf == 0) L.v1[r] = v;
+        beta_prev = beta;
+        __syncthreads();
     }
+    __syncthreads();   // al, be complete
     if (w == 0) {
-        const double lm = tridiag_max_wave(L.al, L.be, L.m_used);
+        const double lm = tridiag_max_wave(L.al, L.be, m_used);
         if (lane == 0) L.res = lm;
     }
     __syncthreads();
-    const double lm = L.res;
-    __syncthreads();
-    return lm;
+    return L.res;
 }
 
 // Writes one factor's Lanczos result: mode 0 (statistics): lambda_max, eps,
@@ -675,31 +676,18 @@ __device__ __forceinline__ void lanczos_finish(const LanczosArgs& args, const La
     }
 }
 
-constexpr int kLanczosLdsN = 128;   // matrices up to this size are staged in LDS
-
 // Largest eigenvalue estimate of one symmetric factor (n <= 128) per
-// workgroup: the matrix (upper triangle, mirrored) is staged into LDS in fp32
-// and lanczos_lds runs on it.
+// workgroup: the matrix (upper triangle) is staged into a slot in fp32 and
+// lanczos_slot runs on it.
 template <typename TM>
-__global__ __launch_bounds__(256) void k_lanczos(const LanczosJob* __restrict__ jobs,
-                                                const TM* __restrict__ arena, LanczosArgs args) {
-    __shared__ __align__(16) float Ss[kLanczosLdsN * (kLanczosLdsN + 1)];
-    __shared__ LanczosLds lz;
+__global__ __launch_bounds__(256, 2) void k_lanczos(const LanczosJob* __restrict__ jobs,
+                                                   const TM* __restrict__ arena, LanczosArgs args) {
+    __shared__ __align__(16) float slot[128 * kSP];
+    __shared__ LanczosSlot lz;
     const LanczosJob jb = jobs[blockIdx.x];
-    const int n = jb.n, ld = jb.ld;
-    const TM* S = arena + jb.off;
-    constexpr int SP = kLanczosLdsN + 1;
-#pragma unroll 8
-    for (int e = threadIdx.x; e < 128 * 128; e += 256) {
-        const int i = e >> 7, j = e & 127;
-        if (i < n && j < n && j >= i) {
-            const float x = (float)S[(int64_t)i * ld + j];
-            Ss[i * SP + j] = x;
-            Ss[j * SP + i] = x;
-        }
-    }
+    stage_sym(slot, arena + jb.off, jb.n, jb.ld);
     __syncthreads();
-    const double lmax = lanczos_lds<float>(Ss, SP, n, args.steps, lz);
+    const double lmax = lanczos_slot(slot, jb.n, args.steps, lz);
     if (threadIdx.x == 0) lanczos_finish(args, jb, isfinite(lmax), lmax);
 }
 
@@ -899,109 +887,131 @@ __global__ __launch_bounds__(256) void k_newton_commit(const FactorJob* __restri
 }
 
 // ------------------------------------------- fused fp32 Newton, n <= 128
-// The whole coupled iteration of one factor (padded to 128) in one
-// workgroup: the iterates stay in two LDS slots (128 x 129 fp32, 132 KB) and
-// in registers, so HBM is touched only to read S and write P.  Wave w owns
-// rows [32w, 32w+32) of every product, as 4 tiles of 32 x 32
-// (v_mfma_f32_32x32x2f32; C lane l reg v = C[8(v/4) + 4(l/32) + v%4][l%32]).
-// Per iteration (p = 4): X' = X T, T2 = T T, T4 = T2 T2, M' = T4 M with
-// T = c1 I + c2 M; the arithmetic (initial rounding, operand transform, k
-// order) is that of the batched path, so both give the same bits.
-constexpr int kNP = 129;  // LDS pitch (floats): row r, column j at bank r + j
+// The whole coupled iteration of one factor (padded to 128) in one workgroup
+// of four waves, two workgroups per CU: the iterates live in registers as
+// column strips (wave w owns columns [32w, 32w+32) of X, M and the powers of
+// T, as four 32 x 32 MFMA accumulator tiles) and one LDS slot carries the
+// left operand of each product.  The right operand is the wave's own strip,
+// read straight from its registers: MFMA step (m', r) pairs the k-indices
+// 32m' + 8(r/4) + r%4 and that + 4, exactly the two rows the accumulator
+// layout keeps in register r of the two lane halves
+// (v_mfma_f32_32x32x2f32: C lane l reg v = C[8(v/4) + 4(l/32) + v%4][l%32]).
+// Per iteration (p = 4), with T = c1 I + c2 M: X' = c1 X + c2 X M (the same
+// as X T), T2 = T T and T4 = T2 T2 (both operands from the slot), M' = T4 M.
+// HBM is touched only to read S and to write P.
+constexpr int kNP = 129;  // LDS pitch (floats) of the fused apply
 
-struct Strip {
-    float v[4][16];
+struct CStrip {
+    float v[4][16];   // v[m][r] = Y[32m + 8(r/4) + 4h + r%4][32w + c]
 };
 
-__device__ __forceinline__ int strip_row(int w, int h, int v) {
-    return 32 * w + 8 * (v >> 2) + 4 * h + (v & 3);
-}
+__device__ __forceinline__ int crow(int m, int h, int r) { return 32 * m + 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// acc[q] += A[32w.., :] * B[:, 32q..]  (A, B in LDS, pitch kNP)
-template <int NA>
-__device__ __forceinline__ void strip_gemm(const float* const (&As)[NA], const float* Bs,
-                                           Strip (&acc)[NA], int w, int h, int c) {
-    typedef float f16v __attribute__((ext_vector_type(16)));
-    f16v r[NA][4];
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+// out = A B on the wave's column strip; A in the slot, bop(m', r) gives the
+// right operand B[crow(m', h, r)][32w + c].  The 64 k-steps are fully
+// unrolled (the right operand is indexed by register), with the four A
+// values of step s+1 loaded before the MFMAs of step s and a scheduling
+// barrier per step: the compiler may not hoist more loads, which keeps the
+// three live strips (192 registers) within the 256 of two waves per SIMD.
+// With B_FROM_SLOT the right operand is read from the slot as well.
+template <bool B_FROM_SLOT, typename BF>
+__device__ __forceinline__ void gemm_strip(const float* slot, BF&& bop, CStrip& out, int w, int h, int c) {
+    f16v acc[4];
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
+    // lane (h, c) reads A[32m + c][k0 + 4h] at physical column pcol(k0) + 32h,
+    // and B[k0 + 4h][32w + c]
+    const float* Ar = slot + c * kSP + 32 * h;
+    const float* Bc = slot + 4 * h * kSP + pcol(32 * w + c);
+    auto kof = [](int s) { return 32 * (s >> 4) + 8 * ((s & 15) >> 2) + (s & 3); };
+    float a[4], b;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) r[a][q][v] = 0.f;
-#pragma unroll 4
-    for (int k0 = 0; k0 < 128; k0 += 2) {
-        float b[4];
+    for (int m = 0; m < 4; ++m) a[m] = Ar[32 * m * kSP + pcol(kof(0))];
+    if constexpr (B_FROM_SLOT) b = Bc[kof(0) * kSP];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) b[q] = Bs[(k0 + h) * kNP + 32 * q + c];
+    for (int s = 0; s < 64; ++s) {
+        float an[4], bn = 0.f;
+        if (s + 1 < 64) {
 #pragma unroll
-        for (int a = 0; a < NA; ++a) {
-            const float av = As[a][(32 * w + c) * kNP + k0 + h];
+            for (int m = 0; m < 4; ++m) an[m] = Ar[32 * m * kSP + pcol(kof(s + 1))];
+            if constexpr (B_FROM_SLOT) bn = Bc[kof(s + 1) * kSP];
+        }
+        const float bv = B_FROM_SLOT ? b : bop(s >> 4, s & 15);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                r[a][q] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b[q], r[a][q], 0, 0, 0);
+        for (int m = 0; m < 4; ++m) acc[m] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[m], bv, acc[m], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < 64) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) a[m] = an[m];
+            b = bn;
         }
     }
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[a].v[q][v] = r[a][q][v];
+        for (int r = 0; r < 16; ++r) out.v[m][r] = acc[m][r];
 }
 
-__device__ __forceinline__ void strip_store(float* S, const Strip& x, int w, int h, int c) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) S[strip_row(w, h, v) * kNP + 32 * q + c] = x.v[q][v];
+template <typename BF>
+__device__ __forceinline__ void gemm_slot_reg(const float* slot, BF&& bop, CStrip& out, int w, int h, int c) {
+    gemm_strip<false>(slot, bop, out, w, h, c);
 }
 
-// T = c1 I + c2 M on a strip
-__device__ __forceinline__ void strip_newton_T(Strip& T, const Strip& M, float c1, float c2, int w,
+// out = A A with A in the slot (both operands read from LDS)
+__device__ __forceinline__ void gemm_slot_slot(const float* slot, CStrip& out, int w, int h, int c) {
+    gemm_strip<true>(slot, [](int, int) { return 0.f; }, out, w, h, c);
+}
+
+__device__ __forceinline__ void cstrip_store(float* slot, const CStrip& y, int w, int h, int c) {
+    float* d = slot + 4 * h * kSP + pcol(32 * w + c);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) d[(32 * m + 8 * (r >> 2) + (r & 3)) * kSP] = y.v[m][r];
+}
+
+// T = c1 I + c2 M into the slot from the wave's strip of M: c2 M everywhere,
+// then the lane that owns the diagonal element of column col adds c1 (its own
+// earlier write, so no barrier is needed in between).
+__device__ __forceinline__ void store_newton_t(float* slot, const CStrip& M, float c1, float c2, int w,
                                                int h, int c) {
+    float* d = slot + 4 * h * kSP + pcol(32 * w + c);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            T.v[q][v] = c2 * M.v[q][v] + ((strip_row(w, h, v) == 32 * q + c) ? c1 : 0.f);
+        for (int r = 0; r < 16; ++r) d[(32 * m + 8 * (r >> 2) + (r & 3)) * kSP] = c2 * M.v[m][r];
+    if (((c >> 2) & 1) == h) {
+        const int col = 32 * w + c;
+        slot[sidx(col, col)] += c1;
+    }
 }
 
 template <int PP>
-__global__ __launch_bounds__(256, 1) void k_newton128(const FactorJob* __restrict__ jobs,
+__global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restrict__ jobs,
                                                      const double* __restrict__ stats,
                                                      float* __restrict__ arena,
                                                      FactorDiag* __restrict__ diag,
                                                      int32_t* __restrict__ prec, FusedArgs args) {
-    // two fp32 slots for the iterates; S0 holds S at the start
-    __shared__ __align__(16) float Sbuf[2 * 128 * kNP];
+    __shared__ __align__(16) float slot[128 * kSP];
+    __shared__ LanczosSlot lz;
     __shared__ double red[4];
-    __shared__ LanczosLds lz;
-    float* const S0 = Sbuf;
-    float* const S1 = Sbuf + 128 * kNP;
     const FactorJob jb = jobs[blockIdx.x];
     const int n = jb.n, ld = jb.ld;
     constexpr int p = PP;
-    const int iters = args.iters;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int h = lane >> 5, c = lane & 31;
+    const int col = 32 * w + c;
 
-    // ---- S (fp64, upper triangle) -> slot S0 as the symmetric fp32 matrix the
-    // fp32 iteration starts from
-    const double* Sg = stats + jb.s_off;
-#pragma unroll 8
-    for (int e2 = t; e2 < 128 * 128; e2 += 256) {
-        const int i = e2 >> 7, j = e2 & 127;
-        if (i < n && j < n && j >= i) {
-            const float x = (float)Sg[(int64_t)i * ld + j];
-            S0[i * kNP + j] = x;
-            S0[j * kNP + i] = x;
-        }
-    }
+    // ---- S (fp64, upper triangle) -> slot, fp32, as the fp32 iteration sees it
+    stage_sym(slot, stats + jb.s_off, n, ld);
     __syncthreads();
 
     // ---- lambda_max (Lanczos) -> eps, status
-    const double lmax = lanczos_lds<float>(S0, kNP, n, args.steps_s, lz);
+    const double lmax = lanczos_slot(slot, n, args.steps_s, lz);
     int st0 = 0;
     if (!isfinite(lmax)) st0 = SHAMPOO_FACTOR_NONFINITE_INPUT_;
     else if (!(lmax > 0.0)) st0 = SHAMPOO_FACTOR_ZERO_;
@@ -1012,119 +1022,118 @@ __global__ __launch_bounds__(256, 1) void k_newton128(const FactorJob* __restric
     const float zr = ok ? float(pow((p + 1) / (2.0 * lam), 1.0 / p)) : 1.f;
     const float e = float(eps);
     const float c1 = float((double)(p + 1) / p), c2 = float(-1.0 / p);
+    const int iters = ok ? args.iters : 0;
 
-    Strip M, X;
+    // ---- M0 = z (S + eps I) in place in the slot (identity outside n x n),
+    // read into the strips; then X0 = z^(1/p) I (identity outside n x n).
+    // Element-wise passes run as rolled loops, so no per-element predicate
+    // lives across the iteration.
+    for (int e2 = t; e2 < 128 * 128; e2 += 256) {
+        const int i = e2 >> 7, j = e2 & 127;
+        float* q = slot + sidx(i, j);
+        *q = (ok && i < n && j < n) ? z * (*q + (i == j ? e : 0.f)) : (i == j ? 1.f : 0.f);
+    }
+    __syncthreads();
+    CStrip M;
+    {
+        const float* ms = slot + 4 * h * kSP + pcol(col);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int i = strip_row(w, h, v), j = 32 * q + c;
-            float m, x;
-            if (i < n && j < n && ok) {
-                const float sv = S0[i * kNP + j];
-                m = z * (sv + (i == j ? e : 0.f));
-                x = (i == j) ? zr : 0.f;
-            } else {
-                m = (i == j) ? 1.f : 0.f;
-                x = (i == j) ? 1.f : 0.f;
-            }
-            M.v[q][v] = m;
-            X.v[q][v] = x;
-        }
-    __syncthreads();   // the staged S is dead from here on
-    Strip T;
-    strip_newton_T(T, M, c1, c2, w, h, c);
-    strip_store(S0, T, w, h, c);
-    strip_store(S1, X, w, h, c);
+            for (int r = 0; r < 16; ++r) M.v[m][r] = ms[(32 * m + 8 * (r >> 2) + (r & 3)) * kSP];
+    }
+    __syncthreads();
+    for (int e2 = t; e2 < 128 * 128; e2 += 256) {
+        const int i = e2 >> 7, j = e2 & 127;
+        slot[sidx(i, j)] = (i == j) ? ((ok && i < n) ? zr : 1.f) : 0.f;
+    }
     __syncthreads();
 
+    // slot: X, registers: M.  X T = c1 X + c2 X M, so the first product takes
+    // M itself as its right operand.
     for (int it = 0; it < iters; ++it) {
-        // X' = X T and T2 = T T (B operand T shared)
-        Strip acc2[2];
+        auto bM = [&](int mb, int r) { return M.v[mb][r]; };
+        CStrip Xn;
+        gemm_slot_reg(slot, bM, Xn, w, h, c);                 // X M
         {
-            const float* As[2] = {S1, S0};
-            strip_gemm<2>(As, S0, acc2, w, h, c);
-        }
-        X = acc2[0];
-        Strip Tp = acc2[1];          // T^2
-        // further squarings: T^4, T^8 (p = 4, 8); p = 1 uses T itself
-        if constexpr (PP == 1) Tp = T;
+            const float* xs = slot + 4 * h * kSP + pcol(col);
 #pragma unroll
-        for (int e2 = 2; e2 < PP; e2 *= 2) {
-            __syncthreads();         // everyone is done reading S1 (X) and S0 (T)
-            strip_store(S1, Tp, w, h, c);
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    Xn.v[m][r] = fmaf(c2, Xn.v[m][r], c1 * xs[(32 * m + 8 * (r >> 2) + (r & 3)) * kSP]);
+        }
+        __syncthreads();
+        store_newton_t(slot, M, c1, c2, w, h, c);
+        __syncthreads();
+        if constexpr (PP == 1) {
+            gemm_slot_reg(slot, bM, M, w, h, c);              // M' = T M
+        } else {
+            CStrip Tp;
+            gemm_slot_slot(slot, Tp, w, h, c);             // T^2
+#pragma unroll
+            for (int e2 = 2; e2 < PP; e2 *= 2) {           // T^4, T^8
+                __syncthreads();
+                cstrip_store(slot, Tp, w, h, c);
+                __syncthreads();
+                gemm_slot_slot(slot, Tp, w, h, c);
+            }
             __syncthreads();
-            Strip sq[1];
-            const float* As[1] = {S1};
-            strip_gemm<1>(As, S1, sq, w, h, c);
-            Tp = sq[0];
+            cstrip_store(slot, Tp, w, h, c);
+            __syncthreads();
+            gemm_slot_reg(slot, bM, M, w, h, c);              // M' = T^p M
         }
-        // M' = T^p M
         __syncthreads();
-        strip_store(S0, Tp, w, h, c);
-        strip_store(S1, M, w, h, c);
-        __syncthreads();
-        {
-            Strip mm[1];
-            const float* As[1] = {S0};
-            strip_gemm<1>(As, S1, mm, w, h, c);
-            M = mm[0];
-        }
-        strip_newton_T(T, M, c1, c2, w, h, c);
-        __syncthreads();
-        strip_store(S0, T, w, h, c);
-        strip_store(S1, X, w, h, c);
+        cstrip_store(slot, Xn, w, h, c);
         __syncthreads();
     }
 
-    // ---- commit: residual max |M - I|, finiteness, write P (or keep / identity)
-    double res = 0.0, bad = 0.0;
-    if (ok) {
+    // ---- commit.  Outside n x n both iterates hold the identity, so the
+    // finiteness test and the residual run over the whole padded tile.
+    double bad = 0.0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int i = strip_row(w, h, v), j = 32 * q + c;
-                if (i < n && j < n) {
-                    const double xv = X.v[q][v];
-                    const double r = fabs(double(M.v[q][v]) - (i == j ? 1.0 : 0.0));
-                    if (!isfinite(xv) || !isfinite(r)) bad = 1.0;
-                    res = fmax(res, r);
-                }
-            }
-    }
-    res = block_max_256(res, red);
+        for (int r = 0; r < 16; ++r)
+            if (!isfinite(M.v[m][r])) bad = 1.0;
+    for (int e2 = t; e2 < 128 * 128; e2 += 256)
+        if (!isfinite(slot[e2 + (e2 >> 7)])) bad = 1.0;   // every stored element once
     bad = block_max_256(bad, red);
     int st = st0;
     if (ok && bad > 0.0) st |= SHAMPOO_FACTOR_NONFINITE_ROOT_;
     const bool keep = (st & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_NONFINITE_ROOT_)) != 0;
     if (!keep) {
         // the committed root is the symmetric part (X + X^T)/2 (the exact root
-        // is symmetric); X^T comes from slot S1, which holds X
+        // is symmetric); identity outside n x n and for a zero factor
         const bool ident = (st & SHAMPOO_FACTOR_ZERO_) != 0;
         float* P = arena + jb.p_off;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int i = strip_row(w, h, v), j = 32 * q + c;
-                if (i < ld && j < ld) {
-                    const float xv = (ident || i >= n || j >= n)
-                                         ? ((i == j) ? 1.f : 0.f)
-                                         : 0.5f * (X.v[q][v] + S1[j * kNP + i]);
-                    P[(int64_t)i * ld + j] = xv;
-                }
-            }
+        for (int e2 = t; e2 < ld * ld; e2 += 256) {
+            const int i = e2 / ld, j = e2 - i * ld;
+            const float xs = 0.5f * (slot[sidx(i, j)] + slot[sidx(j, i)]);
+            P[e2] = (ident || i >= n || j >= n) ? ((i == j) ? 1.f : 0.f) : xs;
+        }
     }
-    if (!keep && !(st & SHAMPOO_FACTOR_ZERO_) && res > 1e-2) st |= SHAMPOO_FACTOR_RESIDUAL_HIGH_;
 
     // ---- kappa estimate from the root: lambda_max(X) = (lambda_min + eps)^(-1/p).
-    // X sits in slot S1 after the last iteration.
+    // X is in the slot (identity block outside n x n, decoupled).
     double kap = 0.0;
     if (ok) {
-        const double lx = lanczos_lds<float>(S1, kNP, n, args.steps_p, lz);
+        const double lx = lanczos_slot(slot, n, args.steps_p, lz);
         if (isfinite(lx) && lx > 0.0) kap = lam * pow(lx, (double)p);
     }
+
+    // ---- residual max |M - I|: M into the slot, the owner of each diagonal
+    // element subtracts 1 from its own write
+    double res = 0.0;
+    if (ok) {
+        __syncthreads();   // the slot (X) is no longer read
+        cstrip_store(slot, M, w, h, c);
+        if (((c >> 2) & 1) == h) slot[sidx(col, col)] -= 1.f;
+        __syncthreads();
+        for (int e2 = t; e2 < 128 * 128; e2 += 256) res = fmax(res, (double)fabsf(slot[e2 + (e2 >> 7)]));
+        res = block_max_256(res, red);
+    }
+    if (!keep && !(st & SHAMPOO_FACTOR_ZERO_) && res > 1e-2) st |= SHAMPOO_FACTOR_RESIDUAL_HIGH_;
     if (t == 0) {
         FactorDiag& dg = diag[jb.factor];
         dg.lambda_max = lmax;
@@ -1162,7 +1171,6 @@ __global__ __launch_bounds__(256, 2) void k_apply128(const ApplyJob* __restrict_
     const int mb = jb.mb, nb = jb.nb, ld = jb.ldg;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int h = lane >> 5, c = lane & 31;
-    typedef float f16v __attribute__((ext_vector_type(16)));
 
     // ---- 1. G -> LDS with the Adagrad accumulate on the way
     double asum = 0.0;
