@@ -73,8 +73,18 @@ def work_model(wl, opt, n_fp64_factors_per_pass):
     small = [b for b in blocks if b.rows <= 128 and b.cols <= 128]
     big = [b for b in blocks if not (b.rows <= 128 and b.cols <= 128)]
     dense_fallback = sum(t.numel for t in wl.tensors if t.kind == "dense") - shampoo_params
+    # tensors whose blocks are all <= 128 get their momentum and weight update
+    # inside the fused apply kernel
+    has_big = {b.tensor for b in big}
+    fused = [b for b in small if b.tensor not in has_big]
+    unfused_params = shampoo_params - sum(b.rows * b.cols for b in fused)
+    # fused apply bytes: G, a (read+write), the two fp32 roots, and either
+    # D (write) or momentum and weight (read+write each)
+    apply_small_bytes = sum((28.0 if b.tensor not in has_big else 16.0) * b.rows * b.cols +
+                            4.0 * (b.ld_l ** 2 + b.ld_r ** 2) for b in small)
     return {
         "gram": gram, "apply_t": apply_t, "apply_d": apply_d,
+        "apply_small_bytes": apply_small_bytes, "unfused_params": unfused_params,
         "apply_small": sum(2.0 * (b.rows * b.cols ** 2 + b.rows ** 2 * b.cols) for b in small),
         "apply_t_big": sum(2.0 * b.rows * b.cols ** 2 for b in big),
         "apply_d_big": sum(2.0 * b.rows ** 2 * b.cols for b in big),
@@ -261,10 +271,14 @@ def main():
         "apply_gemm_t": (wm["apply_t_big"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]),
         "apply_gemm_d": (wm["apply_d_big"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]),
         "adagrad_norm": (wm["shampoo_params_big"] * 12.0, "GB/s", "hbm", PEAK_HBM_GBS),
-        "apply_fused": (wm["apply_small"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]),
-        "update": (wm["shampoo_params"] * 20.0 + wm["dense_fallback"] * 28.0, "GB/s", "hbm",
+        "update": (wm["unfused_params"] * 20.0 + wm["dense_fallback"] * 28.0, "GB/s", "hbm",
                    PEAK_HBM_GBS),
     }
+    # the fused apply is bounded by whichever of its MFMA and HBM floors is higher
+    if wm["apply_small"] / (PEAK_TFLOPS["f32"] * 1e12) >= wm["apply_small_bytes"] / (PEAK_HBM_GBS * 1e9):
+        alg["apply_fused"] = (wm["apply_small"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"])
+    else:
+        alg["apply_fused"] = (wm["apply_small_bytes"], "GB/s", "hbm", PEAK_HBM_GBS)
     for name, (launches, tot) in prof.items():
         if launches == 0:
             continue

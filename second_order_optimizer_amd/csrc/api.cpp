@@ -39,6 +39,7 @@ struct TensorPlan {
     int kind = 0;
     int mode = 0;  // 0 Shampoo, 1 dense Adagrad, 2 sparse rows
     int64_t off_a = -1, off_mom = -1, off_d = -1;  // bytes
+    bool fused = false;  // Shampoo tensor whose blocks are all <= 128: update inside the apply kernel
     int first_block = 0, n_blocks = 0, nbc = 0;
 };
 
@@ -295,6 +296,8 @@ int build_plan(shampoo_s* h) {
                 h->blocks.push_back(bp);
             }
         tp.n_blocks = (int)h->blocks.size() - tp.first_block;
+        tp.fused = true;
+        for (int k = tp.first_block; k < (int)h->blocks.size(); ++k) tp.fused = tp.fused && h->blocks[k].small;
     }
     for (size_t i = 0; i < h->blocks.size(); ++i) {
         const BlockPlan& bp = h->blocks[i];
@@ -326,7 +329,7 @@ int build_plan(shampoo_s* h) {
         const int64_t numel = tp.rows * tp.cols;
         tp.off_a = take(numel * 4);
         if (tp.mode != 2) tp.off_mom = take(numel * 4);
-        if (tp.mode == 0) tp.off_d = take(numel * 4);
+        if (tp.mode == 0 && !tp.fused) tp.off_d = take(numel * 4);
     }
     for (auto& bp : h->blocks) bp.off_t = bp.small ? -1 : take((int64_t)bp.mb * bp.nb * 4);
 
@@ -452,7 +455,10 @@ int build_plan(shampoo_s* h) {
                 j.g_base = 1 + bp.tensor;
                 j.g_off = o;
                 j.a_off = tp.off_a / 4 + o;
-                j.d_off = tp.off_d / 4 + o;
+                j.d_off = tp.fused ? -1 : tp.off_d / 4 + o;
+                j.m_off = tp.off_mom / 4 + o;
+                j.w_base = 1 + h->n + bp.tensor;
+                j.fuse = tp.fused ? 1 : 0;
                 j.pl_off = fl.off_p / 4;
                 j.pr_off = fr.off_p / 4;
                 j.ldg = (int)tp.cols;
@@ -568,7 +574,7 @@ int build_plan(shampoo_s* h) {
         std::vector<RowChunk> rcs;
         for (int t = 0; t < h->n; ++t) {
             const TensorPlan& tp = h->tensors[t];
-            if (tp.mode == 2) continue;
+            if (tp.mode == 2 || tp.fused) continue;
             const int rows_per = (int)std::max<int64_t>(1, kElemChunk / tp.cols);
             for (int64_t r0 = 0; r0 < tp.rows; r0 += rows_per) {
                 RowChunk q{};
@@ -1000,6 +1006,7 @@ int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const flo
     double* partD = at<double>(h, h->off_partD);
     float* scale = at<float>(h, h->off_scale);
     const shampoo_config& c = h->cfg;
+    const UpdateArgs ua{(float)c.beta1, (float)c.lr, (float)c.graft_eps};
 
     {
         ProfScope ps(h, PC_ADAGRAD, s, h->n_blockchunks > 0);
@@ -1010,7 +1017,7 @@ int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const flo
     {
         ProfScope ps(h, PC_APPLY_FUSED, s, h->n_apply128 > 0);
         rc = hip_err(launch_apply128(tab<ApplyJob>(h, h->apply128_off), h->n_apply128, bases, arena,
-                                     (float)c.graft_eps, partA, partD, s));
+                                     (float)c.graft_eps, partA, partD, ua, s));
     }
     if (rc) return rc;
     GemmArgs g{};
@@ -1035,9 +1042,8 @@ int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const flo
                                         partA, partD, scale, s));
     }
     if (rc) return rc;
-    UpdateArgs ua{(float)c.beta1, (float)c.lr, (float)c.graft_eps};
     {
-        ProfScope ps(h, PC_UPDATE, s);
+        ProfScope ps(h, PC_UPDATE, s, h->n_rowchunks > 0);
         rc = hip_err(launch_update(tab<RowChunk>(h, h->rowchunks_off), h->n_rowchunks, bases, h->n,
                                    arena, scale, ua, s));
     }

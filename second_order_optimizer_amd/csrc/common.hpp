@@ -49,6 +49,9 @@ struct ApplyJob {
     int32_t mb, nb;
     int32_t ld_l, ld_r;
     int32_t slot_a, slot_d; // ||A_b||^2 and ||D_b||^2 slots
+    int64_t m_off;          // momentum block (arena floats), used when fuse is set
+    int32_t w_base;         // weight base index, used when fuse is set
+    int32_t fuse;           // 1: graft, momentum and weight update in the same kernel
 };
 
 // A tile of the batched GEMM launch: which task and which 128x128 tile.

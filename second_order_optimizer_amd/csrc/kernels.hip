@@ -1157,12 +1157,13 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
 //  3. D = P_L T in row strips (wave w: D[32w..32w+32, :)), the A operand read
 //     down the columns of P_L -- the committed roots are symmetric, so this
 //     is P_L itself -- again streamed with prefetch;
-//  4. ||D||^2 and D written in the tensor's layout.
+//  4. ||D||^2, then D written in the tensor's layout, or (fuse) the graft,
+//     momentum and weight update applied in place.
 __global__ __launch_bounds__(256, 2) void k_apply128(const ApplyJob* __restrict__ jobs,
                                                     const uint64_t* __restrict__ bases,
                                                     float* __restrict__ arena, float delta,
                                                     double* __restrict__ partA,
-                                                    double* __restrict__ partD) {
+                                                    double* __restrict__ partD, UpdateArgs ua) {
     __shared__ __align__(16) float Sl[128 * kNP];
     __shared__ double red[4];
     const ApplyJob jb = jobs[blockIdx.x];
@@ -1289,25 +1290,89 @@ __global__ __launch_bounds__(256, 2) void k_apply128(const ApplyJob* __restrict_
         }
     }
 
-    // ---- 4. ||D||^2 and D
+    // ---- 4. ||D||^2; then either D to memory (the graft scale needs every
+    // block's norms first) or, for a block whose tensor is covered by such
+    // blocks only, the graft, momentum and weight update right here: the
+    // block's ||A||^2 and ||D||^2 are complete in this workgroup.
     double dsum = 0.0;
-    float* Dg = arena + jb.d_off;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int i = 32 * w + 8 * (v >> 2) + 4 * h + (v & 3), j = 32 * q + c;
-            if (i < mb && j < nb) {
-                const float x = dacc[q][v];
-                dsum += (double)x * (double)x;
-                Dg[(int64_t)i * ld + j] = x;
-            }
+            if (i < mb && j < nb) dsum += (double)dacc[q][v] * (double)dacc[q][v];
         }
     asum = block_sum_256(asum, red);
     dsum = block_sum_256(dsum, red);
     if (t == 0) {
         partA[jb.slot_a] = asum;
         partD[jb.slot_d] = dsum;
+    }
+    if (jb.fuse) {
+        const float sc = dsum > 0.0 ? (float)sqrt(asum / dsum) : 0.f;   // as in k_block_scale
+        float* W = reinterpret_cast<float*>(bases[jb.w_base]) + jb.g_off;
+        float* mo = arena + jb.m_off;
+        const float b1 = ua.beta1, lr = ua.lr;
+        // D through LDS (T is no longer read after the barrier), then the
+        // update in row-major order: 16-byte accesses, four rows of loads in
+        // flight before their stores
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                Sl[(32 * w + 8 * (v >> 2) + 4 * h + (v & 3)) * kNP + 32 * q + c] = dacc[q][v];
+        __syncthreads();
+        const bool vec = (nb % 4 == 0) && (ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0) &&
+                         ((reinterpret_cast<uintptr_t>(mo) & 15) == 0);
+        const int c4 = t & 31, r0 = t >> 5, cc = 4 * c4;
+        if (vec) {
+#pragma unroll
+            for (int p0 = 0; p0 < 16; p0 += 4) {
+                float4 m4[4], w4[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int r = r0 + 8 * (p0 + u);
+                    if (r < mb && cc < nb) {
+                        m4[u] = *reinterpret_cast<const float4*>(mo + (int64_t)r * ld + cc);
+                        w4[u] = *reinterpret_cast<const float4*>(W + (int64_t)r * ld + cc);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int r = r0 + 8 * (p0 + u);
+                    if (r < mb && cc < nb) {
+                        const float* d = &Sl[r * kNP + cc];
+                        float4 m = m4[u], wv = w4[u];
+                        m.x = b1 * m.x + sc * d[0]; m.y = b1 * m.y + sc * d[1];
+                        m.z = b1 * m.z + sc * d[2]; m.w = b1 * m.w + sc * d[3];
+                        wv.x -= lr * m.x; wv.y -= lr * m.y; wv.z -= lr * m.z; wv.w -= lr * m.w;
+                        *reinterpret_cast<float4*>(mo + (int64_t)r * ld + cc) = m;
+                        *reinterpret_cast<float4*>(W + (int64_t)r * ld + cc) = wv;
+                    }
+                }
+            }
+        } else {
+            for (int p = 0; p < 16; ++p) {
+                const int r = r0 + 8 * p;
+                if (r >= mb) continue;
+                for (int e = 0; e < 4 && cc + e < nb; ++e) {
+                    const int64_t o = (int64_t)r * ld + cc + e;
+                    const float m = b1 * mo[o] + sc * Sl[r * kNP + cc + e];
+                    mo[o] = m;
+                    W[o] -= lr * m;
+                }
+            }
+        }
+    } else {
+        float* Dg = arena + jb.d_off;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int i = 32 * w + 8 * (v >> 2) + 4 * h + (v & 3), j = 32 * q + c;
+                if (i < mb && j < nb) Dg[(int64_t)i * ld + j] = dacc[q][v];
+            }
     }
 }
 
@@ -1580,10 +1645,11 @@ hipError_t launch_newton128(const FactorJob* jobs, int njobs, const double* stat
     return hipGetLastError();
 }
 hipError_t launch_apply128(const ApplyJob* jobs, int njobs, const uint64_t* bases, float* arena,
-                           float delta, double* partA, double* partD, hipStream_t s) {
+                           float delta, double* partA, double* partD, const UpdateArgs& ua,
+                           hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_apply128, dim3(njobs), dim3(256), 0, s, jobs, bases, arena, delta, partA,
-                       partD);
+                       partD, ua);
     return hipGetLastError();
 }
 hipError_t launch_set_identity(const FactorJob* jobs, int njobs, float* arena, hipStream_t s) {

@@ -76,7 +76,8 @@ hipError_t launch_newton_commit(bool fp64, const FactorJob* jobs, int njobs, flo
 hipError_t launch_newton128(const FactorJob* jobs, int njobs, const double* stats, float* arena,
                             FactorDiag* diag, int32_t* prec, const FusedArgs& a, hipStream_t s);
 hipError_t launch_apply128(const ApplyJob* jobs, int njobs, const uint64_t* bases, float* arena,
-                           float delta, double* partA, double* partD, hipStream_t s);
+                           float delta, double* partA, double* partD, const UpdateArgs& ua,
+                           hipStream_t s);
 hipError_t launch_set_identity(const FactorJob* jobs, int njobs, float* arena, hipStream_t s);
 hipError_t launch_adagrad_norm(const BlockChunk* chunks, int nchunks, const uint64_t* bases,
                                float* arena, float delta, double* partA, hipStream_t s);
