@@ -1173,40 +1173,61 @@ __global__ __launch_bounds__(256, 2) void k_apply128(const ApplyJob* __restrict_
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int h = lane >> 5, c = lane & 31;
 
-    // ---- 1. G -> LDS with the Adagrad accumulate on the way
+    // ---- 1. G -> LDS with the Adagrad accumulate on the way (vector path:
+    // eight rows of loads in flight before their stores)
     double asum = 0.0;
     {
         const bool vec = (nb % 4 == 0) && (ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(G) & 15) == 0) &&
                          ((reinterpret_cast<uintptr_t>(a) & 15) == 0);
-        const int c4 = t & 31, r0 = t >> 5;
-#pragma unroll 4
-        for (int p = 0; p < 16; ++p) {
-            const int r = r0 + 8 * p, cc = 4 * c4;
-            float gv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (r < mb && cc < nb) {
-                const int64_t o = (int64_t)r * ld + cc;
-                if (vec) {
-                    const float4 g4 = *reinterpret_cast<const float4*>(G + o);
-                    float4 a4 = *reinterpret_cast<const float4*>(a + o);
-                    gv[0] = g4.x; gv[1] = g4.y; gv[2] = g4.z; gv[3] = g4.w;
-                    a4.x += g4.x * g4.x; a4.y += g4.y * g4.y; a4.z += g4.z * g4.z; a4.w += g4.w * g4.w;
-                    *reinterpret_cast<float4*>(a + o) = a4;
-                    const float A0 = g4.x / (sqrtf(a4.x) + delta), A1 = g4.y / (sqrtf(a4.y) + delta);
-                    const float A2 = g4.z / (sqrtf(a4.z) + delta), A3 = g4.w / (sqrtf(a4.w) + delta);
-                    asum += (double)(A0 * A0 + A1 * A1) + (double)(A2 * A2 + A3 * A3);
-                } else {
+        const int c4 = t & 31, r0 = t >> 5, cc = 4 * c4;
+        if (vec) {
+#pragma unroll
+            for (int p0 = 0; p0 < 16; p0 += 8) {
+                float4 g4[8], a4[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int r = r0 + 8 * (p0 + u);
+                    g4[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    a4[u] = g4[u];
+                    if (r < mb && cc < nb) {
+                        g4[u] = *reinterpret_cast<const float4*>(G + (int64_t)r * ld + cc);
+                        a4[u] = *reinterpret_cast<const float4*>(a + (int64_t)r * ld + cc);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int r = r0 + 8 * (p0 + u);
+                    const float4 gv = g4[u];
+                    if (r < mb && cc < nb) {
+                        float4 av = a4[u];
+                        av.x += gv.x * gv.x; av.y += gv.y * gv.y; av.z += gv.z * gv.z; av.w += gv.w * gv.w;
+                        *reinterpret_cast<float4*>(a + (int64_t)r * ld + cc) = av;
+                        const float A0 = gv.x / (sqrtf(av.x) + delta), A1 = gv.y / (sqrtf(av.y) + delta);
+                        const float A2 = gv.z / (sqrtf(av.z) + delta), A3 = gv.w / (sqrtf(av.w) + delta);
+                        asum += (double)(A0 * A0 + A1 * A1) + (double)(A2 * A2 + A3 * A3);
+                    }
+                    float* d = &Sl[r * kNP + cc];
+                    d[0] = gv.x; d[1] = gv.y; d[2] = gv.z; d[3] = gv.w;
+                }
+            }
+        } else {
+            for (int p = 0; p < 16; ++p) {
+                const int r = r0 + 8 * p;
+                float gv[4] = {0.f, 0.f, 0.f, 0.f};
+                if (r < mb) {
                     for (int e = 0; e < 4 && cc + e < nb; ++e) {
-                        const float g1 = G[o + e];
-                        const float av = a[o + e] + g1 * g1;
-                        a[o + e] = av;
+                        const int64_t o = (int64_t)r * ld + cc + e;
+                        const float g1 = G[o];
+                        const float av = a[o] + g1 * g1;
+                        a[o] = av;
                         const float A = g1 / (sqrtf(av) + delta);
                         asum += (double)(A * A);
                         gv[e] = g1;
                     }
                 }
+                float* d = &Sl[r * kNP + cc];
+                d[0] = gv[0]; d[1] = gv[1]; d[2] = gv[2]; d[3] = gv[3];
             }
-            float* d = &Sl[r * kNP + cc];
-            d[0] = gv[0]; d[1] = gv[1]; d[2] = gv[2]; d[3] = gv[3];
         }
     }
     __syncthreads();
