@@ -1149,70 +1149,70 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
 }
 
 // --------------------------------------------------- fused apply, <= 128
-// One block per workgroup, one LDS slot (66 KB: two workgroups per CU):
+// One block per workgroup of eight waves, one LDS tile (66 KB: two
+// workgroups, sixteen waves per CU):
 //  1. a <- a + G*G and ||A||^2 of A = G / (sqrt(a) + delta) while G is staged
-//     into LDS;
-//  2. T = G P_R in column strips (wave w: T[:, 32w..32w+32)), P_R streamed
-//     from L2 with an 8-step prefetch; T replaces G in LDS;
-//  3. D = P_L T in row strips (wave w: D[32w..32w+32, :)), the A operand read
-//     down the columns of P_L -- the committed roots are symmetric, so this
-//     is P_L itself -- again streamed with prefetch;
+//     into LDS (each thread: four rows of 16-byte loads in flight);
+//  2. T = G P_R: wave w takes column strip w%4 and row tiles 2(w/4), +1;
+//     P_R streamed from L2 with an 8-step prefetch; T replaces G in LDS;
+//  3. D = P_L T: wave w takes row strip w%4 and column tiles 2(w/4), +1; the
+//     A operand is read down the columns of P_L -- the committed roots are
+//     symmetric, so this is P_L itself -- again streamed with prefetch;
 //  4. ||D||^2, then D written in the tensor's layout, or (fuse) the graft,
-//     momentum and weight update applied in place.
-__global__ __launch_bounds__(256, 2) void k_apply128(const ApplyJob* __restrict__ jobs,
+//     momentum and weight update applied in place from D staged in LDS.
+__global__ __launch_bounds__(512, 4) void k_apply128(const ApplyJob* __restrict__ jobs,
                                                     const uint64_t* __restrict__ bases,
                                                     float* __restrict__ arena, float delta,
                                                     double* __restrict__ partA,
                                                     double* __restrict__ partD, UpdateArgs ua) {
     __shared__ __align__(16) float Sl[128 * kNP];
-    __shared__ double red[4];
+    __shared__ double red[8];
     const ApplyJob jb = jobs[blockIdx.x];
     const float* G = reinterpret_cast<const float*>(bases[jb.g_base]) + jb.g_off;
     float* a = arena + jb.a_off;
     const int mb = jb.mb, nb = jb.nb, ld = jb.ldg;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int h = lane >> 5, c = lane & 31;
+    const int c4 = t & 31, r0 = t >> 5, cc = 4 * c4;   // elementwise: 16 rows per pass
 
-    // ---- 1. G -> LDS with the Adagrad accumulate on the way (vector path:
-    // eight rows of loads in flight before their stores)
+    // ---- 1. G -> LDS with the Adagrad accumulate on the way
     double asum = 0.0;
     {
         const bool vec = (nb % 4 == 0) && (ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(G) & 15) == 0) &&
                          ((reinterpret_cast<uintptr_t>(a) & 15) == 0);
-        const int c4 = t & 31, r0 = t >> 5, cc = 4 * c4;
         if (vec) {
 #pragma unroll
-            for (int p0 = 0; p0 < 16; p0 += 8) {
-                float4 g4[8], a4[8];
+          for (int u0 = 0; u0 < 8; u0 += 4) {
+            float4 g4[4], a4[4];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int r = r0 + 8 * (p0 + u);
-                    g4[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-                    a4[u] = g4[u];
-                    if (r < mb && cc < nb) {
-                        g4[u] = *reinterpret_cast<const float4*>(G + (int64_t)r * ld + cc);
-                        a4[u] = *reinterpret_cast<const float4*>(a + (int64_t)r * ld + cc);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int r = r0 + 8 * (p0 + u);
-                    const float4 gv = g4[u];
-                    if (r < mb && cc < nb) {
-                        float4 av = a4[u];
-                        av.x += gv.x * gv.x; av.y += gv.y * gv.y; av.z += gv.z * gv.z; av.w += gv.w * gv.w;
-                        *reinterpret_cast<float4*>(a + (int64_t)r * ld + cc) = av;
-                        const float A0 = gv.x / (sqrtf(av.x) + delta), A1 = gv.y / (sqrtf(av.y) + delta);
-                        const float A2 = gv.z / (sqrtf(av.z) + delta), A3 = gv.w / (sqrtf(av.w) + delta);
-                        asum += (double)(A0 * A0 + A1 * A1) + (double)(A2 * A2 + A3 * A3);
-                    }
-                    float* d = &Sl[r * kNP + cc];
-                    d[0] = gv.x; d[1] = gv.y; d[2] = gv.z; d[3] = gv.w;
+            for (int u = 0; u < 4; ++u) {
+                const int r = r0 + 16 * (u0 + u);
+                g4[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                a4[u] = g4[u];
+                if (r < mb && cc < nb) {
+                    g4[u] = *reinterpret_cast<const float4*>(G + (int64_t)r * ld + cc);
+                    a4[u] = *reinterpret_cast<const float4*>(a + (int64_t)r * ld + cc);
                 }
             }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = r0 + 16 * (u0 + u);
+                const float4 gv = g4[u];
+                if (r < mb && cc < nb) {
+                    float4 av = a4[u];
+                    av.x += gv.x * gv.x; av.y += gv.y * gv.y; av.z += gv.z * gv.z; av.w += gv.w * gv.w;
+                    *reinterpret_cast<float4*>(a + (int64_t)r * ld + cc) = av;
+                    const float A0 = gv.x / (sqrtf(av.x) + delta), A1 = gv.y / (sqrtf(av.y) + delta);
+                    const float A2 = gv.z / (sqrtf(av.z) + delta), A3 = gv.w / (sqrtf(av.w) + delta);
+                    asum += (double)(A0 * A0 + A1 * A1) + (double)(A2 * A2 + A3 * A3);
+                }
+                float* d = &Sl[r * kNP + cc];
+                d[0] = gv.x; d[1] = gv.y; d[2] = gv.z; d[3] = gv.w;
+            }
+          }
         } else {
-            for (int p = 0; p < 16; ++p) {
-                const int r = r0 + 8 * p;
+            for (int u = 0; u < 8; ++u) {
+                const int r = r0 + 16 * u;
                 float gv[4] = {0.f, 0.f, 0.f, 0.f};
                 if (r < mb) {
                     for (int e = 0; e < 4 && cc + e < nb; ++e) {
@@ -1232,14 +1232,15 @@ __global__ __launch_bounds__(256, 2) void k_apply128(const ApplyJob* __restrict_
     }
     __syncthreads();
 
-    // ---- 2. T[:, 32w..] = G P_R[:, 32w..]; k runs over the first nb (rounded
-    // up to 16; beyond nb, P_R reads as zero)
+    const int st = w & 3, hv = w >> 2;     // strip and half of this wave
+    // ---- 2. T[32(2hv+r').., 32st..] = G[rows, :] P_R[:, 32st..]; k runs over
+    // the first nb (rounded up to 16; beyond nb, P_R reads as zero)
     const int KT = (nb + 15) & ~15;
     const float* PR = arena + jb.pr_off;
-    const int colT = 32 * w + c;           // this lane's column of P_R / T
-    f16v tacc[4];
+    const int colT = 32 * st + c;          // this lane's column of P_R / T
+    f16v tacc[2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
         for (int v = 0; v < 16; ++v) tacc[r][v] = 0.f;
     {
@@ -1261,28 +1262,28 @@ __global__ __launch_bounds__(256, 2) void k_apply128(const ApplyJob* __restrict_
             for (int u = 0; u < 8; ++u) {
                 const int k = k0 + 2 * u + h;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    tacc[r] = __builtin_amdgcn_mfma_f32_32x32x2f32(Sl[(32 * r + c) * kNP + k], cur[u],
-                                                                   tacc[r], 0, 0, 0);
+                for (int r = 0; r < 2; ++r)
+                    tacc[r] = __builtin_amdgcn_mfma_f32_32x32x2f32(Sl[(32 * (2 * hv + r) + c) * kNP + k],
+                                                                   cur[u], tacc[r], 0, 0, 0);
             }
         }
     }
     __syncthreads();                       // every wave is done reading G
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-            Sl[(32 * r + 8 * (v >> 2) + 4 * h + (v & 3)) * kNP + 32 * w + c] = tacc[r][v];
+            Sl[(32 * (2 * hv + r) + 8 * (v >> 2) + 4 * h + (v & 3)) * kNP + 32 * st + c] = tacc[r][v];
     __syncthreads();
 
-    // ---- 3. D[32w.., :] = P_L[32w.., :] T; A operand P_L[32w + c][k] =
-    // P_L[k][32w + c] (symmetric), k over the first mb
+    // ---- 3. D[32st.., 32(2hv+q')..] = P_L[32st.., :] T; A operand
+    // P_L[32st + c][k] = P_L[k][32st + c] (symmetric), k over the first mb
     const int KD = (mb + 15) & ~15;
     const float* PL = arena + jb.pl_off;
-    const int rowD = 32 * w + c;
-    f16v dacc[4];
+    const int rowD = 32 * st + c;
+    f16v dacc[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int v = 0; v < 16; ++v) dacc[q][v] = 0.f;
     {
@@ -1304,8 +1305,8 @@ __global__ __launch_bounds__(256, 2) void k_apply128(const ApplyJob* __restrict_
             for (int u = 0; u < 8; ++u) {
                 const int k = k0 + 2 * u + h;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    dacc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur[u], Sl[k * kNP + 32 * q + c],
+                for (int q = 0; q < 2; ++q)
+                    dacc[q] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur[u], Sl[k * kNP + 32 * (2 * hv + q) + c],
                                                                    dacc[q], 0, 0, 0);
             }
         }
@@ -1317,14 +1318,14 @@ __global__ __launch_bounds__(256, 2) void k_apply128(const ApplyJob* __restrict_
     // block's ||A||^2 and ||D||^2 are complete in this workgroup.
     double dsum = 0.0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int i = 32 * w + 8 * (v >> 2) + 4 * h + (v & 3), j = 32 * q + c;
+            const int i = 32 * st + 8 * (v >> 2) + 4 * h + (v & 3), j = 32 * (2 * hv + q) + c;
             if (i < mb && j < nb) dsum += (double)dacc[q][v] * (double)dacc[q][v];
         }
-    asum = block_sum_256(asum, red);
-    dsum = block_sum_256(dsum, red);
+    asum = block_sum_512(asum, red);
+    dsum = block_sum_512(dsum, red);
     if (t == 0) {
         partA[jb.slot_a] = asum;
         partD[jb.slot_d] = dsum;
@@ -1335,47 +1336,46 @@ __global__ __launch_bounds__(256, 2) void k_apply128(const ApplyJob* __restrict_
         float* mo = arena + jb.m_off;
         const float b1 = ua.beta1, lr = ua.lr;
         // D through LDS (T is no longer read after the barrier), then the
-        // update in row-major order: 16-byte accesses, four rows of loads in
-        // flight before their stores
+        // update in row-major order with 16-byte accesses, four rows of loads
+        // in flight before their stores
         __syncthreads();
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-                Sl[(32 * w + 8 * (v >> 2) + 4 * h + (v & 3)) * kNP + 32 * q + c] = dacc[q][v];
+                Sl[(32 * st + 8 * (v >> 2) + 4 * h + (v & 3)) * kNP + 32 * (2 * hv + q) + c] = dacc[q][v];
         __syncthreads();
         const bool vec = (nb % 4 == 0) && (ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0) &&
                          ((reinterpret_cast<uintptr_t>(mo) & 15) == 0);
-        const int c4 = t & 31, r0 = t >> 5, cc = 4 * c4;
         if (vec) {
 #pragma unroll
-            for (int p0 = 0; p0 < 16; p0 += 4) {
-                float4 m4[4], w4[4];
+          for (int u0 = 0; u0 < 8; u0 += 4) {
+            float4 m4[4], w4[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int r = r0 + 8 * (p0 + u);
-                    if (r < mb && cc < nb) {
-                        m4[u] = *reinterpret_cast<const float4*>(mo + (int64_t)r * ld + cc);
-                        w4[u] = *reinterpret_cast<const float4*>(W + (int64_t)r * ld + cc);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int r = r0 + 8 * (p0 + u);
-                    if (r < mb && cc < nb) {
-                        const float* d = &Sl[r * kNP + cc];
-                        float4 m = m4[u], wv = w4[u];
-                        m.x = b1 * m.x + sc * d[0]; m.y = b1 * m.y + sc * d[1];
-                        m.z = b1 * m.z + sc * d[2]; m.w = b1 * m.w + sc * d[3];
-                        wv.x -= lr * m.x; wv.y -= lr * m.y; wv.z -= lr * m.z; wv.w -= lr * m.w;
-                        *reinterpret_cast<float4*>(mo + (int64_t)r * ld + cc) = m;
-                        *reinterpret_cast<float4*>(W + (int64_t)r * ld + cc) = wv;
-                    }
+            for (int u = 0; u < 4; ++u) {
+                const int r = r0 + 16 * (u0 + u);
+                if (r < mb && cc < nb) {
+                    m4[u] = *reinterpret_cast<const float4*>(mo + (int64_t)r * ld + cc);
+                    w4[u] = *reinterpret_cast<const float4*>(W + (int64_t)r * ld + cc);
                 }
             }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = r0 + 16 * (u0 + u);
+                if (r < mb && cc < nb) {
+                    const float* d = &Sl[r * kNP + cc];
+                    float4 m = m4[u], wv = w4[u];
+                    m.x = b1 * m.x + sc * d[0]; m.y = b1 * m.y + sc * d[1];
+                    m.z = b1 * m.z + sc * d[2]; m.w = b1 * m.w + sc * d[3];
+                    wv.x -= lr * m.x; wv.y -= lr * m.y; wv.z -= lr * m.z; wv.w -= lr * m.w;
+                    *reinterpret_cast<float4*>(mo + (int64_t)r * ld + cc) = m;
+                    *reinterpret_cast<float4*>(W + (int64_t)r * ld + cc) = wv;
+                }
+            }
+          }
         } else {
-            for (int p = 0; p < 16; ++p) {
-                const int r = r0 + 8 * p;
+            for (int u = 0; u < 8; ++u) {
+                const int r = r0 + 16 * u;
                 if (r >= mb) continue;
                 for (int e = 0; e < 4 && cc + e < nb; ++e) {
                     const int64_t o = (int64_t)r * ld + cc + e;
@@ -1388,10 +1388,10 @@ __global__ __launch_bounds__(256, 2) void k_apply128(const ApplyJob* __restrict_
     } else {
         float* Dg = arena + jb.d_off;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int i = 32 * w + 8 * (v >> 2) + 4 * h + (v & 3), j = 32 * q + c;
+                const int i = 32 * st + 8 * (v >> 2) + 4 * h + (v & 3), j = 32 * (2 * hv + q) + c;
                 if (i < mb && j < nb) Dg[(int64_t)i * ld + j] = dacc[q][v];
             }
     }
@@ -1669,7 +1669,7 @@ hipError_t launch_apply128(const ApplyJob* jobs, int njobs, const uint64_t* base
                            float delta, double* partA, double* partD, const UpdateArgs& ua,
                            hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_apply128, dim3(njobs), dim3(256), 0, s, jobs, bases, arena, delta, partA,
+    hipLaunchKernelGGL(k_apply128, dim3(njobs), dim3(512), 0, s, jobs, bases, arena, delta, partA,
                        partD, ua);
     return hipGetLastError();
 }
