@@ -197,6 +197,18 @@ int shampoo_precondition_and_apply(shampoo_t* h, float* const* params,
                                    const float* const* grads,
                                    const shampoo_sparse_rows* sparse, void* stream);
 
+/* One optimizer step: shampoo_update_stats, then shampoo_compute_inverse_roots
+ * when compute_roots is non-zero (the caller's cadence, cue 14), then
+ * shampoo_precondition_and_apply, with the same arguments.  On a step without
+ * roots the statistics of a block (G, L, R) and its apply (G, a, P, mom, W)
+ * share only read-only inputs, so every block of at most 128 x 128 gets both
+ * from one kernel that reads G once.  Results: statistics and Adagrad
+ * accumulators bit for bit those of the three calls; momentum and weights to
+ * rounding (the two block norms of the graft are summed in another fixed
+ * order).  Errors: as the three calls. */
+int shampoo_step(shampoo_t* h, float* const* params, const float* const* grads,
+                 const shampoo_sparse_rows* sparse, int32_t compute_roots, void* stream);
+
 /* Number of factors (2 per block) and blocks in the plan.  Host only. */
 int shampoo_num_factors(const shampoo_t* h, int32_t* n_factors, int32_t* n_blocks);
 

@@ -86,12 +86,12 @@ struct Blob {
 enum ProfCat : int {
     PC_STATS = 0, PC_LANCZOS_S, PC_LANCZOS_P, PC_NEWTON_INIT, PC_NEWTON_GEMM32, PC_NEWTON_GEMM64,
     PC_NEWTON_COMMIT, PC_ADAGRAD, PC_APPLY_T, PC_APPLY_D, PC_SCALE, PC_UPDATE, PC_SPARSE,
-    PC_NEWTON_FUSED, PC_APPLY_FUSED, PC_COUNT
+    PC_NEWTON_FUSED, PC_APPLY_FUSED, PC_STEP_FUSED, PC_COUNT
 };
 const char* const kProfNames[PC_COUNT] = {
     "stats_gram_f64", "lanczos_stats", "lanczos_roots", "newton_init", "newton_gemm_f32",
     "newton_gemm_f64", "newton_commit", "adagrad_norm", "apply_gemm_t", "apply_gemm_d",
-    "block_scale", "update", "sparse_rows", "newton_fused_f32", "apply_fused"};
+    "block_scale", "update", "sparse_rows", "newton_fused_f32", "apply_fused", "step_fused"};
 
 struct ProfRec {
     int cat;
@@ -118,6 +118,7 @@ struct shampoo_s {
     LaunchRef gram, apply1, apply2;   // blocks with a side > 128
     int64_t apply128_off = 0;
     int n_apply128 = 0;               // blocks of at most 128 x 128
+    int64_t step128_off = 0;          // the same blocks for the fused step kernel
     int64_t gram128_off = 0;
     int n_gram128 = 0;                // blocks of at most 128 x 128
     int64_t ident_jobs_off = 0;
@@ -445,6 +446,7 @@ int build_plan(shampoo_s* h) {
     {
         std::vector<GemmTask> t1, t2;
         std::vector<ApplyJob> small;
+        std::vector<StepJob> steps;
         for (auto& bp : h->blocks) {
             const TensorPlan& tp = h->tensors[bp.tensor];
             const FactorPlan& fl = h->factors[bp.fl];
@@ -469,6 +471,11 @@ int build_plan(shampoo_s* h) {
                 j.slot_a = bp.a_slot;
                 j.slot_d = bp.d_slot;
                 small.push_back(j);
+                StepJob sj{};
+                sj.ap = j;
+                sj.l_off = fl.off_s / 8;
+                sj.r_off = fr.off_s / 8;
+                steps.push_back(sj);
                 continue;
             }
             GemmTask t{};
@@ -503,6 +510,7 @@ int build_plan(shampoo_s* h) {
         h->apply2 = add_launch(blob, t2);
         h->n_apply128 = (int)small.size();
         h->apply128_off = blob.add(small);
+        h->step128_off = blob.add(steps);
     }
     // Lanczos jobs on statistics and on roots; identity jobs
     {
@@ -827,30 +835,73 @@ int shampoo_bind_state(shampoo_t* h, void* dev_state, size_t bytes, void* stream
     return SHAMPOO_OK;
 }
 
-int shampoo_update_stats(shampoo_t* h, const float* const* grads, void* stream) {
-    if (!h || !grads) return SHAMPOO_E_ARG;
-    if (!h->bound) return SHAMPOO_E_STATE;
-    for (auto& bp : h->blocks)
-        if (!grads[bp.tensor]) return SHAMPOO_E_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    int rc = refresh_bases(h, grads, nullptr, s);
-    if (rc) return rc;
+}  // extern "C"
+
+namespace {
+// EMA weights of the statistics: S <- beta2 S + w G G^T, w = 1 - beta2
+// (formed in fp64), or a plain sum when beta2 == 1.
+GemmArgs stats_args(const shampoo_s* h) {
     const double b2 = h->cfg.beta2;
     GemmArgs a{};
     a.epi = EPI_AXPBY;
     a.alpha = b2 < 1.0 ? 1.0 - b2 : 1.0;
     a.beta = b2;
+    return a;
+}
+
+// Statistics kernels on stream s (pointer table already current).  With
+// skip_small the blocks of at most 128 x 128 are left to the fused step
+// kernel (enqueue_apply with fused_small).
+int enqueue_stats(shampoo_s* h, hipStream_t s, bool skip_small) {
+    const GemmArgs a = stats_args(h);
     // fp32 gradients, fp64 products and statistics (exact products; the
     // statistics keep the near-null spectrum that fp32 storage would round
     // into the eps damping)
-    ProfScope ps(h, PC_STATS, s);
-    int rc2 = hip_err(launch_gram128(tab<GramJob>(h, h->gram128_off), h->n_gram128,
-                                     at<uint64_t>(h, h->off_bases), at<double>(h, 0), a.alpha,
-                                     a.beta, s));
-    if (rc2) return rc2;
+    ProfScope ps(h, PC_STATS, s, h->gram.ntiles > 0 || (!skip_small && h->n_gram128 > 0));
+    if (!skip_small) {
+        const int rc2 = hip_err(launch_gram128(tab<GramJob>(h, h->gram128_off), h->n_gram128,
+                                               at<uint64_t>(h, h->off_bases), at<double>(h, 0),
+                                               a.alpha, a.beta, s));
+        if (rc2) return rc2;
+    }
     return hip_err(launch_gemm_f64_from_f32(tab<GemmTask>(h, h->gram.tasks_off),
                                             tab<TileRef>(h, h->gram.tiles_off), h->gram.ntiles,
                                             at<uint64_t>(h, h->off_bases), a, s));
+}
+
+int check_stats_args(const shampoo_s* h, const float* const* grads) {
+    if (!grads) return SHAMPOO_E_ARG;
+    for (auto& bp : h->blocks)
+        if (!grads[bp.tensor]) return SHAMPOO_E_ARG;
+    return SHAMPOO_OK;
+}
+
+int check_apply_args(const shampoo_s* h, float* const* params, const float* const* grads,
+                     const shampoo_sparse_rows* sparse) {
+    if (!params || !grads) return SHAMPOO_E_ARG;
+    for (int t = 0; t < h->n; ++t) {
+        if (!params[t]) return SHAMPOO_E_ARG;
+        if (h->tensors[t].mode != 2 && !grads[t]) return SHAMPOO_E_ARG;
+    }
+    if (h->n_sparse > 0 && !sparse) return SHAMPOO_E_ARG;
+    return SHAMPOO_OK;
+}
+
+int enqueue_apply(shampoo_s* h, float* const* params, const shampoo_sparse_rows* sparse,
+                  hipStream_t s, bool fused_small);
+}  // namespace
+
+extern "C" {
+
+int shampoo_update_stats(shampoo_t* h, const float* const* grads, void* stream) {
+    if (!h || !grads) return SHAMPOO_E_ARG;
+    if (!h->bound) return SHAMPOO_E_STATE;
+    int rc = check_stats_args(h, grads);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = refresh_bases(h, grads, nullptr, s);
+    if (rc) return rc;
+    return enqueue_stats(h, s, false);
 }
 
 namespace {
@@ -992,14 +1043,46 @@ int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const flo
                                    const shampoo_sparse_rows* sparse, void* stream) {
     if (!h || !params || !grads) return SHAMPOO_E_ARG;
     if (!h->bound) return SHAMPOO_E_STATE;
-    for (int t = 0; t < h->n; ++t) {
-        if (!params[t]) return SHAMPOO_E_ARG;
-        if (h->tensors[t].mode != 2 && !grads[t]) return SHAMPOO_E_ARG;
-    }
-    if (h->n_sparse > 0 && !sparse) return SHAMPOO_E_ARG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    int rc = refresh_bases(h, grads, params, s);
+    int rc = check_apply_args(h, params, grads, sparse);
     if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = refresh_bases(h, grads, params, s);
+    if (rc) return rc;
+    return enqueue_apply(h, params, sparse, s, false);
+}
+
+int shampoo_step(shampoo_t* h, float* const* params, const float* const* grads,
+                 const shampoo_sparse_rows* sparse, int32_t compute_roots, void* stream) {
+    if (!h || !params || !grads) return SHAMPOO_E_ARG;
+    if (!h->bound) return SHAMPOO_E_STATE;
+    int rc = check_stats_args(h, grads);
+    if (!rc) rc = check_apply_args(h, params, grads, sparse);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = refresh_bases(h, grads, params, s);
+    if (rc) return rc;
+    if (compute_roots) {
+        // the roots need this step's statistics, the apply needs the roots
+        rc = enqueue_stats(h, s, false);
+        if (!rc) rc = shampoo_compute_inverse_roots(h, stream);
+        if (!rc) rc = enqueue_apply(h, params, sparse, s, false);
+        return rc;
+    }
+    // no root pass: statistics and apply of each block <= 128 share one kernel
+    rc = enqueue_stats(h, s, true);
+    if (!rc) rc = enqueue_apply(h, params, sparse, s, true);
+    return rc;
+}
+
+}  // extern "C"
+
+namespace {
+// Apply kernels on stream s (pointer table already current).  fused_small:
+// the blocks of at most 128 x 128 go through the fused step kernel, which
+// also updates their statistics.
+int enqueue_apply(shampoo_s* h, float* const* params, const shampoo_sparse_rows* sparse,
+                  hipStream_t s, bool fused_small) {
+    int rc = SHAMPOO_OK;
     const uint64_t* bases = at<uint64_t>(h, h->off_bases);
     float* arena = at<float>(h, 0);
     double* partA = at<double>(h, h->off_partA);
@@ -1014,7 +1097,12 @@ int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const flo
                                      arena, (float)c.graft_eps, partA, s));
     }
     if (rc) return rc;
-    {
+    if (fused_small) {
+        const GemmArgs sa = stats_args(h);
+        ProfScope ps(h, PC_STEP_FUSED, s, h->n_apply128 > 0);
+        rc = hip_err(launch_step128(tab<StepJob>(h, h->step128_off), h->n_apply128, bases, arena,
+                                    sa.alpha, sa.beta, (float)c.graft_eps, partA, partD, ua, s));
+    } else {
         ProfScope ps(h, PC_APPLY_FUSED, s, h->n_apply128 > 0);
         rc = hip_err(launch_apply128(tab<ApplyJob>(h, h->apply128_off), h->n_apply128, bases, arena,
                                      (float)c.graft_eps, partA, partD, ua, s));
@@ -1083,6 +1171,9 @@ int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const flo
     }
     return SHAMPOO_OK;
 }
+}  // namespace
+
+extern "C" {
 
 int shampoo_get_diagnostics(shampoo_t* h, shampoo_factor_diag* out, int32_t cap, void* stream) {
     if (!h || (!out && cap > 0) || cap < 0) return SHAMPOO_E_ARG;

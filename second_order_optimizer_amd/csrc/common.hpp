@@ -54,6 +54,13 @@ struct ApplyJob {
     int32_t fuse;           // 1: graft, momentum and weight update in the same kernel
 };
 
+// One Shampoo block of at most 128 x 128 for the fused step kernel
+// (statistics and apply together, on steps without a root pass).
+struct StepJob {
+    ApplyJob ap;
+    int64_t l_off, r_off;   // fp64 statistics (arena elements of 8 bytes)
+};
+
 // A tile of the batched GEMM launch: which task and which 128x128 tile.
 struct TileRef {
     int32_t task;

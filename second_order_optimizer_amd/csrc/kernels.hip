@@ -413,23 +413,39 @@ __device__ __forceinline__ void gram_quadrant(const float* Gs, int qi, int qj, i
             }
         }
     }
+    // read-modify-write of the statistics, two tiles at a time: their eight
+    // loads in flight before the first store (the stores could alias later
+    // loads as far as the compiler knows, so it would not hoist them)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = JLO; j < JHI; ++j) {
-            if (DIAG && i > j) continue;
+        for (int j0 = JLO; j0 < JHI; j0 += 2) {
+            double old[2][4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = qi * 64 + i * 16 + g + 4 * v, q = qj * 64 + j * 16 + c;
-                if (r < nvalid && q < nvalid) {
-                    double* p = S + (int64_t)r * ldS + q;
-                    *p = alpha * acc[i][j][v] + beta * (*p);
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = j0 + jj;
+                if (j >= JHI || (DIAG && i > j)) continue;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = qi * 64 + i * 16 + g + 4 * v, q = qj * 64 + j * 16 + c;
+                    old[jj][v] = (r < nvalid && q < nvalid) ? S[(int64_t)r * ldS + q] : 0.0;
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = j0 + jj;
+                if (j >= JHI || (DIAG && i > j)) continue;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = qi * 64 + i * 16 + g + 4 * v, q = qj * 64 + j * 16 + c;
+                    if (r < nvalid && q < nvalid)
+                        S[(int64_t)r * ldS + q] = alpha * acc[i][j][v] + beta * old[jj][v];
                 }
             }
         }
 }
 
-__global__ __launch_bounds__(512, 2) void k_gram128(const GramJob* __restrict__ jobs,
+__global__ __launch_bounds__(512, 4) void k_gram128(const GramJob* __restrict__ jobs,
                                                    const uint64_t* __restrict__ bases,
                                                    double* __restrict__ stats, double alpha,
                                                    double beta) {
@@ -1397,6 +1413,295 @@ __global__ __launch_bounds__(512, 4) void k_apply128(const ApplyJob* __restrict_
     }
 }
 
+// ------------------------------------------------ fused step, blocks <= 128
+// Statistics and apply of one block in one workgroup of sixteen waves, for a
+// step without a root pass (the two then share only read-only inputs):
+//  0. G and P_L staged into LDS by all waves (G zero outside mb x nb, P_L
+//     zero outside mb x mb);
+//  1. waves 0-7: a <- a + G*G and ||A||^2 (G from LDS, accumulator rows
+//     loaded in phase 0), then L <- beta L + alpha G G^T and
+//     R <- beta R + alpha G^T G on fp64 MFMA (the quadrant split of the
+//     statistics kernel, one diagonal quadrant and one off-diagonal half per
+//     SIMD) with the read-modify-write of the upper triangles; at the same
+//     time waves 8-15: T = G P_R and D = P_L T on v_mfma_f32_16x16x4f32, wave
+//     8+y owning columns [16y, 16y+16) of T and D.  T's strip is the right operand of the second product straight from
+//     its accumulator registers: C lane l reg v = C[4(l/16) + v][l%16], so
+//     register (m', v) holds rows 16m' + v + {0, 4, 8, 12} across the four
+//     lane groups -- the four k-indices of one MFMA step;
+//  2. momentum and weight loads issued, ||A||^2 and ||D||^2 (fixed order), D
+//     into LDS;
+//  3. graft, momentum and weight update (or D out for a tensor that also has
+//     blocks > 128) by all waves, in row-major 16-byte accesses.
+// Each SIMD holds two waves of each half, so the fp64 products of one half
+// overlap the memory traffic of the other.
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ double block_sum_1024(double v, double* red) {
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        s0 += red[k];
+        s1 += red[8 + k];
+    }
+    return s0 + s1;
+}
+
+__global__ __launch_bounds__(1024) void k_step128(const StepJob* __restrict__ jobs,
+                                                 const uint64_t* __restrict__ bases,
+                                                 float* __restrict__ arena, double alpha, double beta,
+                                                 float delta, double* __restrict__ partA,
+                                                 double* __restrict__ partD, UpdateArgs ua) {
+    __shared__ __align__(16) float Gs[128 * kGP];
+    __shared__ __align__(16) float Ps[128 * kGP];
+    __shared__ double red[16];
+    const StepJob sj = jobs[blockIdx.x];
+    const ApplyJob& jb = sj.ap;
+    const float* G = reinterpret_cast<const float*>(bases[jb.g_base]) + jb.g_off;
+    float* a = arena + jb.a_off;
+    const int mb = jb.mb, nb = jb.nb, ld = jb.ldg;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const bool vec = (nb % 4 == 0) && (ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(G) & 15) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(a) & 15) == 0);
+
+    // ---- 0. G and P_L into LDS (32 float4 per row, 32 rows per pass); the
+    // statistics half (threads 0-511) also loads its eight rows of the Adagrad
+    // accumulator (16 rows per pass) for the Adagrad pass that opens phase 1
+    const int ac4 = t & 31, arr = (t >> 5) & 15, acc4 = 4 * ac4;
+    float4 a4[8];
+    if (w < 8 && vec) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int r = arr + 16 * u;
+            if (r < mb && acc4 < nb) a4[u] = *reinterpret_cast<const float4*>(a + (int64_t)r * ld + acc4);
+        }
+    }
+    {
+        const int c4 = t & 31, r0 = t >> 5, cc = 4 * c4;
+        const float* PL = arena + jb.pl_off;
+        float4 gv[4], pv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = r0 + 32 * u;
+            gv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            pv[u] = gv[u];
+            if (r < mb && cc < nb) {
+                if (vec) {
+                    gv[u] = *reinterpret_cast<const float4*>(G + (int64_t)r * ld + cc);
+                } else {
+                    const float* gr = G + (int64_t)r * ld + cc;
+                    gv[u].x = gr[0];
+                    if (cc + 1 < nb) gv[u].y = gr[1];
+                    if (cc + 2 < nb) gv[u].z = gr[2];
+                    if (cc + 3 < nb) gv[u].w = gr[3];
+                }
+            }
+            if (r < mb && cc < mb) {   // cc + 3 < ld_l: ld_l is a multiple of 32
+                pv[u] = *reinterpret_cast<const float4*>(PL + (int64_t)r * jb.ld_l + cc);
+                if (cc + 1 >= mb) pv[u].y = 0.f;
+                if (cc + 2 >= mb) pv[u].z = 0.f;
+                if (cc + 3 >= mb) pv[u].w = 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = r0 + 32 * u;
+            *reinterpret_cast<float4*>(&Gs[r * kGP + cc]) = gv[u];
+            *reinterpret_cast<float4*>(&Ps[r * kGP + cc]) = pv[u];
+        }
+    }
+    __syncthreads();
+
+    // ---- 1.
+    double asum = 0.0, dsum = 0.0;
+    f4v dacc[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) dacc[m] = f4v{0.f, 0.f, 0.f, 0.f};
+    const int i = lane & 15, g = lane >> 4;     // 16x16x4 lane coordinates
+    const int y = w - 8, col = 16 * y + i;      // apply half: this lane's column of T and D
+    if (w < 8) {
+        // a <- a + G*G and ||A||^2 (G from LDS; the accumulator rows are in
+        // flight since phase 0), while the apply half starts its products
+        if (vec) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int r = arr + 16 * u;
+                if (r < mb && acc4 < nb) {
+                    const float4 gq = *reinterpret_cast<const float4*>(&Gs[r * kGP + acc4]);
+                    float4 q = a4[u];
+                    q.x += gq.x * gq.x; q.y += gq.y * gq.y; q.z += gq.z * gq.z; q.w += gq.w * gq.w;
+                    *reinterpret_cast<float4*>(a + (int64_t)r * ld + acc4) = q;
+                    const float A0 = gq.x / (sqrtf(q.x) + delta), A1 = gq.y / (sqrtf(q.y) + delta);
+                    const float A2 = gq.z / (sqrtf(q.z) + delta), A3 = gq.w / (sqrtf(q.w) + delta);
+                    asum += (double)(A0 * A0 + A1 * A1) + (double)(A2 * A2 + A3 * A3);
+                }
+            }
+        } else {
+            for (int u = 0; u < 8; ++u) {
+                const int r = arr + 16 * u;
+                if (r >= mb) continue;
+                for (int e = 0; e < 4 && acc4 + e < nb; ++e) {
+                    const int64_t o = (int64_t)r * ld + acc4 + e;
+                    const float g1 = Gs[r * kGP + acc4 + e];
+                    const float av = a[o] + g1 * g1;
+                    a[o] = av;
+                    const float A = g1 / (sqrtf(av) + delta);
+                    asum += (double)(A * A);
+                }
+            }
+        }
+        // statistics: each diagonal quadrant of L and R on one wave (10 tiles),
+        // each off-diagonal quadrant split over two (8 tiles each).  Waves w
+        // and w + 4 share a SIMD, so each SIMD gets one diagonal quadrant and
+        // one off-diagonal half: 18 tiles of fp64 MFMA work per SIMD.
+        const int KL = (nb + 15) & ~15, KR = (mb + 15) & ~15;
+        double* stats = reinterpret_cast<double*>(arena);
+        double* L = stats + sj.l_off;
+        double* R = stats + sj.r_off;
+        switch (w) {
+            case 0: gram_quadrant<true, false>(Gs, 0, 0, KL, L, jb.ld_l, mb, alpha, beta, i, g); break;
+            case 1: gram_quadrant<true, false>(Gs, 1, 1, KL, L, jb.ld_l, mb, alpha, beta, i, g); break;
+            case 2: gram_quadrant<true, true>(Gs, 0, 0, KR, R, jb.ld_r, nb, alpha, beta, i, g); break;
+            case 3: gram_quadrant<true, true>(Gs, 1, 1, KR, R, jb.ld_r, nb, alpha, beta, i, g); break;
+            case 4: gram_quadrant<false, false, 0, 2>(Gs, 0, 1, KL, L, jb.ld_l, mb, alpha, beta, i, g); break;
+            case 5: gram_quadrant<false, false, 2, 4>(Gs, 0, 1, KL, L, jb.ld_l, mb, alpha, beta, i, g); break;
+            case 6: gram_quadrant<false, true, 0, 2>(Gs, 0, 1, KR, R, jb.ld_r, nb, alpha, beta, i, g); break;
+            default: gram_quadrant<false, true, 2, 4>(Gs, 0, 1, KR, R, jb.ld_r, nb, alpha, beta, i, g); break;
+        }
+    } else {
+        // T[:, 16y..] = G P_R[:, 16y..]: A operand G[16m + i][k + g] from LDS,
+        // B operand P_R[k + g][col] streamed with an 8-step prefetch
+        f4v tacc[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) tacc[m] = f4v{0.f, 0.f, 0.f, 0.f};
+        {
+            const float* PR = arena + jb.pr_off;
+            const int KT = (nb + 3) & ~3;
+            auto ld_pr = [&](int k) -> float {
+                return (k < nb && col < nb) ? PR[(int64_t)k * jb.ld_r + col] : 0.f;
+            };
+            float nxt[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) nxt[u] = ld_pr(4 * u + g);
+            for (int k0 = 0; k0 < KT; k0 += 32) {
+                float cur[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
+                if (k0 + 32 < KT) {
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) nxt[u] = ld_pr(k0 + 32 + 4 * u + g);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int k = k0 + 4 * u;
+                    if (k < KT) {
+#pragma unroll
+                        for (int m = 0; m < 8; ++m)
+                            tacc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(Gs[(16 * m + i) * kGP + k + g], cur[u],
+                                                                           tacc[m], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        // D[:, 16y..] = P_L T[:, 16y..]: step (m', v) takes k = 16m' + 4g + v in
+        // lane group g; A operand P_L[16m + i][k] = P_L[k][16m + i] (symmetric)
+#pragma unroll
+        for (int mq = 0; mq < 8; ++mq) {
+            if (16 * mq >= mb) break;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int k = 16 * mq + 4 * g + v;
+                const float b = tacc[mq][v];
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+                    dacc[m] = __builtin_amdgcn_mfma_f32_16x16x4f32(Ps[k * kGP + 16 * m + i], b, dacc[m], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * m + 4 * g + v;
+                if (r < mb && col < nb) dsum += (double)dacc[m][v] * (double)dacc[m][v];
+            }
+    }
+
+    // ---- 2. momentum and weight rows of phase 3 in flight (32 rows per pass,
+    // four rows per thread), norms, D into LDS (G is no longer read past
+    // these barriers)
+    const int c4 = t & 31, r0 = t >> 5, cc = 4 * c4;
+    float* W = reinterpret_cast<float*>(bases[jb.w_base]) + jb.g_off;
+    float* mo = arena + jb.m_off;
+    const bool vw = jb.fuse && vec && ((reinterpret_cast<uintptr_t>(W) & 15) == 0) &&
+                    ((reinterpret_cast<uintptr_t>(mo) & 15) == 0);
+    float4 m4[4], w4[4];
+    if (vw) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = r0 + 32 * u;
+            if (r < mb && cc < nb) {
+                m4[u] = *reinterpret_cast<const float4*>(mo + (int64_t)r * ld + cc);
+                w4[u] = *reinterpret_cast<const float4*>(W + (int64_t)r * ld + cc);
+            }
+        }
+    }
+    asum = block_sum_1024(asum, red);
+    dsum = block_sum_1024(dsum, red);
+    if (t == 0) {
+        partA[jb.slot_a] = asum;
+        partD[jb.slot_d] = dsum;
+    }
+    if (w >= 8) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) Gs[(16 * m + 4 * g + v) * kGP + col] = dacc[m][v];
+    }
+    __syncthreads();
+
+    // ---- 3. update (or D out)
+    if (jb.fuse) {
+        const float sc = dsum > 0.0 ? (float)sqrt(asum / dsum) : 0.f;   // as in k_block_scale
+        const float b1 = ua.beta1, lr = ua.lr;
+        if (vw) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = r0 + 32 * u;
+                if (r < mb && cc < nb) {
+                    const float4 d = *reinterpret_cast<const float4*>(&Gs[r * kGP + cc]);
+                    float4 m = m4[u], wv = w4[u];
+                    m.x = b1 * m.x + sc * d.x; m.y = b1 * m.y + sc * d.y;
+                    m.z = b1 * m.z + sc * d.z; m.w = b1 * m.w + sc * d.w;
+                    wv.x -= lr * m.x; wv.y -= lr * m.y; wv.z -= lr * m.z; wv.w -= lr * m.w;
+                    *reinterpret_cast<float4*>(mo + (int64_t)r * ld + cc) = m;
+                    *reinterpret_cast<float4*>(W + (int64_t)r * ld + cc) = wv;
+                }
+            }
+        } else {
+            for (int u = 0; u < 4; ++u) {
+                const int r = r0 + 32 * u;
+                if (r >= mb) continue;
+                for (int e = 0; e < 4 && cc + e < nb; ++e) {
+                    const int64_t o = (int64_t)r * ld + cc + e;
+                    const float m = b1 * mo[o] + sc * Gs[r * kGP + cc + e];
+                    mo[o] = m;
+                    W[o] -= lr * m;
+                }
+            }
+        }
+    } else {
+        float* Dg = arena + jb.d_off;
+        for (int u = 0; u < 4; ++u) {
+            const int r = r0 + 32 * u;
+            if (r >= mb) continue;
+            for (int e = 0; e < 4 && cc + e < nb; ++e) Dg[(int64_t)r * ld + cc + e] = Gs[r * kGP + cc + e];
+        }
+    }
+}
+
 // Identity roots for every factor (state initialisation).
 __global__ __launch_bounds__(256) void k_set_identity(const FactorJob* __restrict__ jobs,
                                                      float* __restrict__ arena) {
@@ -1663,6 +1968,14 @@ hipError_t launch_newton128(const FactorJob* jobs, int njobs, const double* stat
         case 8: hipLaunchKernelGGL(k_newton128<8>, dim3(njobs), dim3(256), 0, s, jobs, stats, arena, diag, prec, a); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+hipError_t launch_step128(const StepJob* jobs, int njobs, const uint64_t* bases, float* arena,
+                          double alpha, double beta, float delta, double* partA, double* partD,
+                          const UpdateArgs& ua, hipStream_t s) {
+    if (njobs <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_step128, dim3(njobs), dim3(1024), 0, s, jobs, bases, arena, alpha, beta,
+                       delta, partA, partD, ua);
     return hipGetLastError();
 }
 hipError_t launch_apply128(const ApplyJob* jobs, int njobs, const uint64_t* bases, float* arena,

@@ -65,6 +65,9 @@ hipError_t launch_gemm_f64_from_f32(const GemmTask* tasks, const TileRef* tiles,
                                     const uint64_t* bases, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gram128(const GramJob* jobs, int njobs, const uint64_t* bases, double* stats,
                           double alpha, double beta, hipStream_t s);
+hipError_t launch_step128(const StepJob* jobs, int njobs, const uint64_t* bases, float* arena,
+                          double alpha, double beta, float delta, double* partA, double* partD,
+                          const UpdateArgs& ua, hipStream_t s);
 hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, bool fp64_matrix,
                           bool big, const LanczosArgs& a, hipStream_t s);
 hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, const double* stats,

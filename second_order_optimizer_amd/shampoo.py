@@ -76,6 +76,8 @@ SIGNATURES = {
     "shampoo_compute_inverse_roots": (ctypes.c_int, [_P, _P]),
     "shampoo_precondition_and_apply": (ctypes.c_int, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P),
                                                       ctypes.POINTER(SparseRows), _P]),
+    "shampoo_step": (ctypes.c_int, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P),
+                                    ctypes.POINTER(SparseRows), ctypes.c_int32, _P]),
     "shampoo_num_factors": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int32),
                                            ctypes.POINTER(ctypes.c_int32)]),
     "shampoo_get_diagnostics": (ctypes.c_int, [_P, ctypes.POINTER(FactorDiag), ctypes.c_int32, _P]),
@@ -211,8 +213,7 @@ class Shampoo(Plan):
         _check(lib().shampoo_compute_inverse_roots(self.h, self._stream()),
                "shampoo_compute_inverse_roots")
 
-    def precondition_and_apply(self, params, grads, sparse=None):
-        """sparse: dict tensor index -> (int32 rows, fp32 row grads) device tensors."""
+    def _apply_args(self, params, grads, sparse):
         pa = self._ptrs(params, lambda k: True, "params")
         ga = self._ptrs(grads, lambda k: k == DENSE, "grads")
         sp = None
@@ -229,11 +230,23 @@ class Shampoo(Plan):
                     raise ValueError(f"sparse[{i}] must be (int32 rows, fp32 rows x {c})")
                 keep.append((rows, g))
                 sp[i] = SparseRows(rows.data_ptr(), g.data_ptr(), rows.numel())
+        return pa, ga, sp, keep
+
+    def precondition_and_apply(self, params, grads, sparse=None):
+        """sparse: dict tensor index -> (int32 rows, fp32 row grads) device tensors."""
+        pa, ga, sp, _keep = self._apply_args(params, grads, sparse)
         _check(lib().shampoo_precondition_and_apply(self.h, pa, ga, sp, self._stream()),
                "shampoo_precondition_and_apply")
 
     def step(self, params, grads, step: int, cadence: int, sparse=None):
-        """One optimizer step: statistics, roots when step % cadence == 0, apply."""
+        """One optimizer step (shampoo_step): statistics, roots when
+        step % cadence == 0, apply."""
+        pa, ga, sp, _keep = self._apply_args(params, grads, sparse)
+        _check(lib().shampoo_step(self.h, pa, ga, sp, 1 if step % cadence == 0 else 0,
+                                  self._stream()), "shampoo_step")
+
+    def step_separate(self, params, grads, step: int, cadence: int, sparse=None):
+        """The same step as three calls on one stream (no concurrency)."""
         self.update_stats(grads)
         if step % cadence == 0:
             self.compute_inverse_roots()

@@ -242,3 +242,40 @@ def test_committed_roots_are_symmetric():
         for b in range(run.opt.n_blocks):
             for P in list(run.opt.roots(b)) + [x for x in run.opt.roots(b, fp64=True) if x is not None]:
                 assert torch.equal(P, P.T), (mode, b)
+
+
+def test_step_entry_point_matches_separate_calls():
+    """shampoo_step (on steps without roots: statistics and apply of each
+    block <= 128 in the fused step kernel) against the three separate calls:
+    statistics and Adagrad accumulators bit for bit (same per-element
+    arithmetic), weights to rounding (the two block norms of the graft are
+    summed in another fixed order).  Small blocks whose tensor is updated in
+    the kernel, a tensor with a block > 128 (D goes through memory), a
+    diagonal-Adagrad fallback tensor and a sparse table; roots every 3 steps."""
+    T = synth.TensorSpec
+    wl = _custom([T("small", 100, 70), T("big", 300, 200), T("wide", 40, 400),
+                  T("emb", 500, 32, kind="sparse", grad="sparse_rows"), T("sq", 128, 128)], 256,
+                 max_precond_dim=256, cadence=3, steps=7)
+    runs = [GpuRun(wl), GpuRun(wl)]
+    worst = 0.0
+    for t in range(7):
+        W0 = [p.clone() for p in runs[1].params]
+        for k, run in enumerate(runs):
+            _, dev, sp = run.grads_at(t)
+            if k == 0:
+                run.opt.step(run.params, dev, t, wl.cadence, sp)
+            else:
+                run.opt.step_separate(run.params, dev, t, wl.cadence, sp)
+        torch.cuda.synchronize()
+        for b in range(runs[0].opt.n_blocks):
+            for x, y in zip(runs[0].opt.stats(b, raw=True), runs[1].opt.stats(b, raw=True)):
+                assert torch.equal(x, y), (t, b)
+        for i in range(len(wl.tensors)):
+            (a0, _), (a1, _) = runs[0].opt.accumulators(i), runs[1].opt.accumulators(i)
+            assert torch.equal(a0, a1), (t, i)
+            d0 = (runs[0].params[i] - W0[i]).double().cpu().numpy()
+            d1 = (runs[1].params[i] - W0[i]).double().cpu().numpy()
+            e = rel_fro(d0, d1)
+            worst = max(worst, e)
+            assert e <= 1e-5, (t, i, e)
+    say(f"shampoo_step vs separate calls: statistics bitwise, worst update diff {worst:.1e}")

@@ -68,6 +68,8 @@ def test_strerror_and_argument_errors():
     arr = (S._P * 1)()
     assert L.shampoo_update_stats(p.h, arr, None) == -2
     assert L.shampoo_compute_inverse_roots(p.h, None) == -2
+    assert L.shampoo_step(p.h, arr, arr, None, 0, None) == -2
+    assert L.shampoo_step(p.h, None, arr, None, 1, None) == -1
     assert L.shampoo_update_stats(p.h, None, None) == -1
     p.close()
 
