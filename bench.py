@@ -82,8 +82,14 @@ def work_model(wl, opt, n_fp64_factors_per_pass):
     # D (write) or momentum and weight (read+write each)
     apply_small_bytes = sum((28.0 if b.tensor not in has_big else 16.0) * b.rows * b.cols +
                             4.0 * (b.ld_l ** 2 + b.ld_r ** 2) for b in small)
+    # fused step kernel (steps without roots, blocks <= 128): statistics
+    # (fp64 MFMA, upper triangles read and written in fp64) plus the apply
+    step_small_bytes = apply_small_bytes + sum(
+        8.0 * (b.rows * (b.rows + 1) + b.cols * (b.cols + 1)) for b in small)
     return {
         "gram": gram, "apply_t": apply_t, "apply_d": apply_d,
+        "gram_small": sum(2.0 * (b.rows ** 2 * b.cols + b.cols ** 2 * b.rows) for b in small),
+        "step_small_bytes": step_small_bytes,
         "apply_small_bytes": apply_small_bytes, "unfused_params": unfused_params,
         "apply_small": sum(2.0 * (b.rows * b.cols ** 2 + b.rows ** 2 * b.cols) for b in small),
         "apply_t_big": sum(2.0 * b.rows * b.cols ** 2 for b in big),
@@ -279,11 +285,31 @@ def main():
         alg["apply_fused"] = (wm["apply_small"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"])
     else:
         alg["apply_fused"] = (wm["apply_small_bytes"], "GB/s", "hbm", PEAK_HBM_GBS)
+    # the fused step kernel: fp64 statistics and fp32 apply share the matrix
+    # pipe, so its MFMA floor is the sum of both times at their peaks; its
+    # roofline is the higher of that floor and the HBM floor
+    t_mfma_step = (wm["gram_small"] / (PEAK_TFLOPS["f64"] * 1e12) +
+                   wm["apply_small"] / (PEAK_TFLOPS["f32"] * 1e12))
+    t_hbm_step = wm["step_small_bytes"] / (PEAK_HBM_GBS * 1e9)
     for name, (launches, tot) in prof.items():
         if launches == 0:
             continue
         rec = {"launches": int(launches), "avg_ms": tot / launches,
                "ms_per_step": tot / args.steps}
+        if name == "step_fused":
+            sec = rec["avg_ms"] / 1e3
+            rec.update({"mfma_floor_frac": t_mfma_step / sec, "hbm_floor_frac": t_hbm_step / sec,
+                        "hbm_achieved_gbs": wm["step_small_bytes"] / sec / 1e9})
+            if t_mfma_step >= t_hbm_step:
+                # an fp64 flop counts as two fp32 flops (the fp64 peak is half)
+                eq = (2.0 * wm["gram_small"] + wm["apply_small"]) / sec / 1e12
+                rec.update({"bound": "mfma", "achieved": eq, "peak": PEAK_TFLOPS["f32"],
+                            "unit": "TFLOP/s (fp32-equivalent)", "frac": t_mfma_step / sec})
+            else:
+                rec.update({"bound": "hbm", "achieved": wm["step_small_bytes"] / sec / 1e9,
+                            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": t_hbm_step / sec})
+            stages[name] = rec
+            continue
         work = None
         if name in alg:
             work, unit, bound, peak = alg[name]
