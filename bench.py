@@ -169,6 +169,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--root-parts", type=int, default=0,
+                    help="staggered root pass: recompute 1/P of the roots every cadence/P "
+                         "steps (P must divide the cadence); 0 = one pass every cadence steps")
     ap.add_argument("--no-profile", action="store_true",
                     help="time without the per-launch events (no per-kernel breakdown)")
     args = ap.parse_args()
@@ -189,7 +192,7 @@ def main():
     cfg = S.make_config(wl.block_size, max_precond_dim=wl.max_precond_dim, root_p=wl.root_p,
                         newton_iters=wl.newton_iters, root_mode=wl.root_mode, beta1=wl.beta1,
                         beta2=wl.beta2, lr=wl.lr, eps_rel=wl.eps_rel, graft_eps=wl.graft_eps,
-                        fp64_cond_threshold=wl.fp64_cond_threshold)
+                        fp64_cond_threshold=wl.fp64_cond_threshold, root_parts=args.root_parts)
     shapes = [(t.rows, t.cols, 0 if t.kind == "dense" else 1) for t in wl.tensors]
     t0 = time.time()
     opt = S.Shampoo(shapes, cfg, device=dev)
@@ -237,15 +240,25 @@ def main():
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev0.record(stream)
+    marks = []                  # one event after every step: per-step GPU time
     for t in range(args.warmup, args.warmup + args.steps):
         step(t)
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        marks.append(e)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_total = ev0.elapsed_time(ev1)
+    per_step = [ev0.elapsed_time(marks[0])] + [a.elapsed_time(b) for a, b in zip(marks, marks[1:])]
+    per_step.sort()
+    step_ms = {"p50": per_step[len(per_step) // 2],
+               "p99": per_step[min(len(per_step) - 1, int(0.99 * len(per_step)))],
+               "max": per_step[-1]}
     prof = opt.profile_read() if not args.no_profile else {}
     opt.profile(False)
     ms_step = ms_total / args.steps
+    # root passes in the timed steps (a staggered pass counts 1/P per part)
     n_root_passes = sum(1 for t in range(args.warmup, args.warmup + args.steps)
                         if t % wl.cadence == 0)
     diag = opt.diagnostics()
@@ -368,6 +381,7 @@ def main():
         "config": {"workload": wl.name, "params": wl.n_params, "blocks": opt.n_blocks,
                    "block_size": wl.block_size, "root_cadence": wl.cadence,
                    "newton_iters": wl.newton_iters, "root_mode": wl.root_mode,
+                   "root_parts": args.root_parts,
                    "max_precond_dim": wl.max_precond_dim, "parallelism": "single-gpu"},
         "steps_per_s": steps_per_s,
         "inv_root_blocks_per_s": inv_root_blocks_per_s,
@@ -377,6 +391,7 @@ def main():
         "stages": stages,
         "roofline": roofline,
         "wall_s_timed": wall,
+        "step_ms": step_ms,
     }
     if not args.no_cpu_baseline:
         print("# cpu baseline (fp64 oracle) ...", file=sys.stderr, flush=True)

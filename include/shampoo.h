@@ -85,7 +85,11 @@ typedef struct {
     int32_t root_mode;        /* shampoo_root_mode                                       */
     int32_t lanczos_steps;    /* Krylov steps for lambda_max; 0 = 20 for factors up to
                                  128 and 24 above; the kappa estimate uses min(8, this)  */
-    int32_t reserved;         /* must be 0 */
+    int32_t root_parts;       /* staggered root pass (cue 14-16: roots are computed off
+                                 the critical path and swapped in): 0 or 1 = one pass
+                                 over every factor; P >= 2 also plans P parts, part q
+                                 holding the factors of the blocks b with b % P == q
+                                 (shampoo_compute_inverse_roots_part, shampoo_step)      */
     double beta1;             /* momentum: mom <- beta1 mom + U                          */
     double beta2;             /* statistics: S <- beta2 S + (1-beta2) outer(G) (beta2<1),
                                  S <- S + outer(G) when beta2 == 1; 1 - beta2 is formed in
@@ -182,6 +186,16 @@ int shampoo_update_stats(shampoo_t* h, const float* const* grads, void* stream);
  * Errors: SHAMPOO_E_STATE, SHAMPOO_E_HIP. */
 int shampoo_compute_inverse_roots(shampoo_t* h, void* stream);
 
+/* One part of a staggered root pass: the inverse roots, exactly as
+ * shampoo_compute_inverse_roots computes them, of the factors of the blocks b
+ * with b % root_parts == part (block numbering: tensors in order, blocks
+ * row-major within a tensor).  Calling part (t / (k/P)) % P whenever
+ * t % (k/P) == 0 (P = root_parts dividing the cadence k) refreshes every root
+ * once per k steps and spreads the cost of a pass evenly over the steps.
+ * Errors: SHAMPOO_E_ARG (root_parts < 2 or part out of range),
+ * SHAMPOO_E_STATE, SHAMPOO_E_HIP. */
+int shampoo_compute_inverse_roots_part(shampoo_t* h, int32_t part, void* stream);
+
 /* Preconditioned multiply and update (cue 10): for every block
  * D_b = P_L G_b P_R; a <- a + G*G; A = G / (sqrt(a) + graft_eps);
  * U_b = D_b ||A_b||_F / ||D_b||_F (0 when ||D_b|| = 0);
@@ -197,17 +211,25 @@ int shampoo_precondition_and_apply(shampoo_t* h, float* const* params,
                                    const float* const* grads,
                                    const shampoo_sparse_rows* sparse, void* stream);
 
-/* One optimizer step: shampoo_update_stats, then shampoo_compute_inverse_roots
- * when compute_roots is non-zero (the caller's cadence, cue 14), then
- * shampoo_precondition_and_apply, with the same arguments.  On a step without
- * roots the statistics of a block (G, L, R) and its apply (G, a, P, mom, W)
- * share only read-only inputs, so every block of at most 128 x 128 gets both
- * from one kernel that reads G once.  Results: statistics and Adagrad
- * accumulators bit for bit those of the three calls; momentum and weights to
- * rounding (the two block norms of the graft are summed in another fixed
- * order).  Errors: as the three calls. */
+/* Root selector of shampoo_step. */
+enum {
+    SHAMPOO_ROOTS_NONE = -1,  /* no roots this step                                      */
+    SHAMPOO_ROOTS_ALL = -2    /* every root (shampoo_compute_inverse_roots); a value
+                                 0 <= q < root_parts selects part q instead
+                                 (shampoo_compute_inverse_roots_part)                    */
+};
+
+/* One optimizer step: shampoo_update_stats, then the roots that `roots`
+ * selects, then shampoo_precondition_and_apply, with the same arguments.  On
+ * a step without roots the statistics of a block (G, L, R) and its apply (G,
+ * a, P, mom, W) share only read-only inputs, so every block of at most
+ * 128 x 128 gets both from one kernel that reads G once.  Results:
+ * statistics and Adagrad accumulators bit for bit those of the separate
+ * calls; momentum and weights to rounding (the two block norms of the graft
+ * are summed in another fixed order).  Errors: as the separate calls, and
+ * SHAMPOO_E_ARG for an invalid `roots`. */
 int shampoo_step(shampoo_t* h, float* const* params, const float* const* grads,
-                 const shampoo_sparse_rows* sparse, int32_t compute_roots, void* stream);
+                 const shampoo_sparse_rows* sparse, int32_t roots, void* stream);
 
 /* Number of factors (2 per block) and blocks in the plan.  Host only. */
 int shampoo_num_factors(const shampoo_t* h, int32_t* n_factors, int32_t* n_blocks);

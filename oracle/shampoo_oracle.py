@@ -58,6 +58,7 @@ class OracleConfig:
     eps_rel: float = 1e-6
     graft_eps: float = 1e-10
     cadence: int = 1
+    root_parts: int = 1           # > 1: staggered root recompute (see root_due)
 
 
 # ------------------------------------------------------- blocking (Lemma 2)
@@ -205,6 +206,26 @@ class _BlockState:
         self.root_R: Optional[RootResult] = None
 
 
+def root_due(block_index: int, t: int, cadence: int, parts: int) -> bool:
+    """Whether the roots of Shampoo block `block_index` (counted over all
+    tensors, in order) are recomputed at step t, after that step's statistics.
+
+    The roots are recomputed only every so often and the accelerator keeps
+    using the last ones in between (podcast cue 14); the pages move that work
+    off the critical path by computing it in the background (cues 14-16).
+    With parts == 1 every root is recomputed at t = 0, k, 2k, ... (k the
+    cadence).  With parts = P > 1 (P dividing k) the blocks are split by
+    index modulo P and one part is recomputed every k/P steps, part
+    (t / (k/P)) mod P: each root is still refreshed once every k steps, and
+    the cost of a root pass is spread evenly over the steps."""
+    if parts <= 1:
+        return t % cadence == 0
+    if cadence % parts != 0:
+        raise ValueError("root_parts must divide the cadence")
+    window = cadence // parts
+    return t % window == 0 and (t // window) % parts == block_index % parts
+
+
 class ShampooOracle:
     """The whole optimizer step over a list of tensors, fp64.
 
@@ -214,7 +235,8 @@ class ShampooOracle:
     step(grads, t) with grads[i] an (m, n) array for dense tensors or a
     (rows, row_grads) pair for sparse tensors, t counted from 0:
       1. statistics of every Shampoo block (cue 10);
-      2. if t % cadence == 0, inverse p-th roots of every factor (cue 10, 12,
+      2. inverse p-th roots of the factors of every block that root_due
+         selects (all of them at t % cadence == 0 by default; cue 10, 12,
          14), keeping the previous root for a non-finite factor;
       3. D = PL G PR per block (cue 10);
       4. a += G*G per tensor, A = G/(sqrt(a)+delta), per-block graft U;
@@ -239,8 +261,8 @@ class ShampooOracle:
 
     def step(self, grads, t: int) -> List[np.ndarray]:
         cfg = self.cfg
-        recompute = (t % cfg.cadence) == 0
         deltas = []
+        gblock = 0   # global block index over the tensors, in order
         for i, (m, n, kind) in enumerate(self.shapes):
             W_old = self.W[i]
             if kind == "sparse":
@@ -258,6 +280,8 @@ class ShampooOracle:
                 for (r0, mb, c0, nb), st in self.blocks[i]:
                     Gb = G[r0:r0 + mb, c0:c0 + nb]
                     st.L, st.R = update_statistics(st.L, st.R, Gb, cfg.beta2)
+                    recompute = root_due(gblock, t, cfg.cadence, cfg.root_parts)
+                    gblock += 1
                     if recompute:
                         st.root_L = inverse_root(st.L, cfg.eps_rel, cfg.root_p)
                         st.root_R = inverse_root(st.R, cfg.eps_rel, cfg.root_p)

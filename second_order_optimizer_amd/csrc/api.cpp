@@ -70,6 +70,14 @@ struct NewtonChunk {
     std::vector<LaunchRef> stages[2];        // per parity
 };
 
+// The launches of one root pass over a set of factors.
+struct RootTables {
+    int64_t lanczos_s_small_off = 0, lanczos_p_small_off = 0;   // factors with ld <= 128
+    int64_t lanczos_s_big_off = 0, lanczos_p_big_off = 0;       // factors with ld > 128
+    int n_lanczos_small = 0, n_lanczos_big = 0;
+    std::vector<NewtonChunk> chunks32, chunks64;
+};
+
 // Host-side table builder: tables are appended to one blob that is copied
 // into the arena's table region at bind time.
 struct Blob {
@@ -122,12 +130,11 @@ struct shampoo_s {
     int64_t gram128_off = 0;
     int n_gram128 = 0;                // blocks of at most 128 x 128
     int64_t ident_jobs_off = 0;
-    int64_t lanczos_s_small_off = 0, lanczos_p_small_off = 0;   // factors with ld <= 128
-    int64_t lanczos_s_big_off = 0, lanczos_p_big_off = 0;       // factors with ld > 128
-    int n_lanczos_small = 0, n_lanczos_big = 0;
+    // root-pass tables: [0] every factor; [1 + q] part q of a staggered pass
+    // (factors of the blocks b with b % root_parts == q)
+    std::vector<RootTables> roots;
     int64_t blockchunks_off = 0, blocknorms_off = 0, rowchunks_off = 0;
     int n_blockchunks = 0, n_rowchunks = 0;
-    std::vector<NewtonChunk> chunks32, chunks64;
     std::vector<FactorDiag> diag_init;
 
     // binding
@@ -357,23 +364,31 @@ int build_plan(shampoo_s* h) {
     std::sort(lds.begin(), lds.end());
     lds.erase(std::unique(lds.begin(), lds.end()), lds.end());
     int64_t scr32 = 0, scr64 = 0;
-    struct Pending { int ld; std::vector<int> fids; bool fp64; bool fused; };
+    struct Pending { int set; int ld; std::vector<int> fids; bool fp64; bool fused; };
     std::vector<Pending> pend;
+    const int nparts = c.root_parts > 1 ? c.root_parts : 0;
+    h->roots.assign(1 + nparts, RootTables{});
+    auto in_set = [&](int set, int i) {
+        return set == 0 || h->factors[i].block % nparts == set - 1;
+    };
+    for (int set = 0; set <= nparts; ++set)
     for (int ld : lds) {
         std::vector<int> fids;
         for (int i = 0; i < nf; ++i)
-            if (h->factors[i].ld == ld) fids.push_back(i);
+            if (h->factors[i].ld == ld && in_set(set, i)) fids.push_back(i);
+        if (fids.empty()) continue;
         for (int prec = 0; prec < 2; ++prec) {
             const bool fp64 = prec == 1;
             if ((fp64 && !use_fp64(c)) || (!fp64 && !use_fp32(c))) continue;
             if (!fp64 && ld <= 128) {   // fused LDS-resident kernel, no scratch
-                pend.push_back(Pending{ld, fids, false, true});
+                pend.push_back(Pending{set, ld, fids, false, true});
                 continue;
             }
             const int64_t per = 6 * (int64_t)ld * ld * (fp64 ? 8 : 4);
             const int cap = (int)std::max<int64_t>(1, (int64_t)kNewtonScratchBudget / per);
             for (size_t s = 0; s < fids.size(); s += cap) {
                 Pending pd;
+                pd.set = set;
                 pd.ld = ld;
                 pd.fp64 = fp64;
                 pd.fused = false;
@@ -533,25 +548,30 @@ int build_plan(shampoo_s* h) {
             d.dim = f.dim;
             h->diag_init.push_back(d);
         }
-        std::vector<LanczosJob> jss, jps, jsb, jpb;
-        for (int i = 0; i < nf; ++i) {
-            const bool big = h->factors[i].ld > 128;
-            (big ? jsb : jss).push_back(js[i]);
-            (big ? jpb : jps).push_back(jp[i]);
+        for (int set = 0; set <= nparts; ++set) {
+            std::vector<LanczosJob> jss, jps, jsb, jpb;
+            for (int i = 0; i < nf; ++i) {
+                if (!in_set(set, i)) continue;
+                const bool big = h->factors[i].ld > 128;
+                (big ? jsb : jss).push_back(js[i]);
+                (big ? jpb : jps).push_back(jp[i]);
+            }
+            RootTables& rt = h->roots[set];
+            rt.n_lanczos_small = (int)jss.size();
+            rt.n_lanczos_big = (int)jsb.size();
+            rt.lanczos_s_small_off = blob.add(jss);
+            rt.lanczos_p_small_off = blob.add(jps);
+            rt.lanczos_s_big_off = blob.add(jsb);
+            rt.lanczos_p_big_off = blob.add(jpb);
         }
-        h->n_lanczos_small = (int)jss.size();
-        h->n_lanczos_big = (int)jsb.size();
-        h->lanczos_s_small_off = blob.add(jss);
-        h->lanczos_p_small_off = blob.add(jps);
-        h->lanczos_s_big_off = blob.add(jsb);
-        h->lanczos_p_big_off = blob.add(jpb);
         h->ident_jobs_off = blob.add(ident);
     }
     for (auto& pd : pend) {
         NewtonChunk ch;
         build_newton_chunk(h, ch, pd.fids, pd.ld, pd.fp64, pd.fused,
                            pd.fp64 ? h->off_scr64 : h->off_scr32);
-        (pd.fp64 ? h->chunks64 : h->chunks32).push_back(std::move(ch));
+        RootTables& rt = h->roots[pd.set];
+        (pd.fp64 ? rt.chunks64 : rt.chunks32).push_back(std::move(ch));
     }
     // elementwise tables
     {
@@ -699,7 +719,7 @@ int shampoo_create(const shampoo_config* cfg, int32_t n_tensors, const shampoo_t
     if (c.block_size < 1 || c.newton_iters < 1 || c.max_precond_dim < 0 || c.lanczos_steps < 0)
         return SHAMPOO_E_ARG;
     if (!(c.beta2 > 0.0 && c.beta2 <= 1.0) || !(c.eps_rel >= 0.0) || !(c.graft_eps >= 0.0) ||
-        !std::isfinite(c.beta1) || !std::isfinite(c.lr) || c.reserved != 0)
+        !std::isfinite(c.beta1) || !std::isfinite(c.lr) || c.root_parts < 0)
         return SHAMPOO_E_ARG;
     if (c.root_mode < SHAMPOO_ROOT_F32 || c.root_mode > SHAMPOO_ROOT_AUTO) return SHAMPOO_E_ARG;
     if (c.root_p != 1 && c.root_p != 2 && c.root_p != 4 && c.root_p != 8)
@@ -972,10 +992,12 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
 }
 }  // namespace
 
-int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
-    if (!h) return SHAMPOO_E_ARG;
-    if (!h->bound) return SHAMPOO_E_STATE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+}  // extern "C"
+
+namespace {
+// One root pass over the factors of rt (every factor, or one part of a
+// staggered pass).
+int enqueue_roots(shampoo_s* h, RootTables& rt, hipStream_t s) {
     const int nf = (int)h->factors.size();
     if (nf == 0) return SHAMPOO_OK;
     const shampoo_config& c = h->cfg;
@@ -998,27 +1020,27 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
                        const LanczosArgs& a) -> int {
         const void* base = h->arena;
         ProfScope ps(h, on_stats ? PC_LANCZOS_S : PC_LANCZOS_P, s,
-                     h->n_lanczos_big > 0 || (with_small && h->n_lanczos_small > 0));
+                     rt.n_lanczos_big > 0 || (with_small && rt.n_lanczos_small > 0));
         int r = SHAMPOO_OK;
         if (with_small)
-            r = hip_err(launch_lanczos(tab<LanczosJob>(h, small_off), h->n_lanczos_small, base,
+            r = hip_err(launch_lanczos(tab<LanczosJob>(h, small_off), rt.n_lanczos_small, base,
                                        on_stats, false, a, s));
         if (r) return r;
-        return hip_err(launch_lanczos(tab<LanczosJob>(h, big_off), h->n_lanczos_big, base, on_stats,
+        return hip_err(launch_lanczos(tab<LanczosJob>(h, big_off), rt.n_lanczos_big, base, on_stats,
                                       true, a, s));
     };
     if (use_fp32(c)) {
         // factors up to 128: everything inside the fused kernel; larger ones:
         // Lanczos on S, batched fp32 Newton, Lanczos on the root
-        rc = lanczos(h->lanczos_s_small_off, h->lanczos_s_big_off, true, false, la);
+        rc = lanczos(rt.lanczos_s_small_off, rt.lanczos_s_big_off, true, false, la);
         if (rc) return rc;
-        rc = run_newton(h, h->chunks32, false, nullptr, 0, prec, s);
+        rc = run_newton(h, rt.chunks32, false, nullptr, 0, prec, s);
         if (rc) return rc;
         lp.auto_route = c.root_mode == SHAMPOO_ROOT_AUTO ? 1 : 0;
-        rc = lanczos(h->lanczos_p_small_off, h->lanczos_p_big_off, false, false, lp);
+        rc = lanczos(rt.lanczos_p_small_off, rt.lanczos_p_big_off, false, false, lp);
         if (rc) return rc;
         if (c.root_mode == SHAMPOO_ROOT_AUTO)
-            rc = run_newton(h, h->chunks64, true, prec, 1, prec, s);
+            rc = run_newton(h, rt.chunks64, true, prec, 1, prec, s);
         return rc;
     }
     // all fp64
@@ -1026,17 +1048,34 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
     la_small.steps = c.lanczos_steps > 0 ? c.lanczos_steps : 20;
     {
         ProfScope ps(h, PC_LANCZOS_S, s);
-        rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_s_small_off), h->n_lanczos_small,
+        rc = hip_err(launch_lanczos(tab<LanczosJob>(h, rt.lanczos_s_small_off), rt.n_lanczos_small,
                                     h->arena, true, false, la_small, s));
         if (!rc)
-            rc = hip_err(launch_lanczos(tab<LanczosJob>(h, h->lanczos_s_big_off), h->n_lanczos_big,
+            rc = hip_err(launch_lanczos(tab<LanczosJob>(h, rt.lanczos_s_big_off), rt.n_lanczos_big,
                                         h->arena, true, true, la, s));
     }
     if (rc) return rc;
-    rc = run_newton(h, h->chunks64, true, nullptr, 1, prec, s);
+    rc = run_newton(h, rt.chunks64, true, nullptr, 1, prec, s);
     if (rc) return rc;
     lp.auto_route = 0;
-    return lanczos(h->lanczos_p_small_off, h->lanczos_p_big_off, false, true, lp);
+    return lanczos(rt.lanczos_p_small_off, rt.lanczos_p_big_off, false, true, lp);
+}
+}  // namespace
+
+extern "C" {
+
+int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
+    if (!h) return SHAMPOO_E_ARG;
+    if (!h->bound) return SHAMPOO_E_STATE;
+    return enqueue_roots(h, h->roots[0], static_cast<hipStream_t>(stream));
+}
+
+int shampoo_compute_inverse_roots_part(shampoo_t* h, int32_t part, void* stream) {
+    if (!h) return SHAMPOO_E_ARG;
+    const int nparts = (int)h->roots.size() - 1;
+    if (nparts < 1 || part < 0 || part >= nparts) return SHAMPOO_E_ARG;
+    if (!h->bound) return SHAMPOO_E_STATE;
+    return enqueue_roots(h, h->roots[1 + part], static_cast<hipStream_t>(stream));
 }
 
 int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const float* const* grads,
@@ -1052,8 +1091,11 @@ int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const flo
 }
 
 int shampoo_step(shampoo_t* h, float* const* params, const float* const* grads,
-                 const shampoo_sparse_rows* sparse, int32_t compute_roots, void* stream) {
+                 const shampoo_sparse_rows* sparse, int32_t roots, void* stream) {
     if (!h || !params || !grads) return SHAMPOO_E_ARG;
+    const int nparts = (int)h->roots.size() - 1;
+    if (roots != SHAMPOO_ROOTS_NONE && roots != SHAMPOO_ROOTS_ALL && (roots < 0 || roots >= nparts))
+        return SHAMPOO_E_ARG;
     if (!h->bound) return SHAMPOO_E_STATE;
     int rc = check_stats_args(h, grads);
     if (!rc) rc = check_apply_args(h, params, grads, sparse);
@@ -1061,10 +1103,10 @@ int shampoo_step(shampoo_t* h, float* const* params, const float* const* grads,
     hipStream_t s = static_cast<hipStream_t>(stream);
     rc = refresh_bases(h, grads, params, s);
     if (rc) return rc;
-    if (compute_roots) {
+    if (roots != SHAMPOO_ROOTS_NONE) {
         // the roots need this step's statistics, the apply needs the roots
         rc = enqueue_stats(h, s, false);
-        if (!rc) rc = shampoo_compute_inverse_roots(h, stream);
+        if (!rc) rc = enqueue_roots(h, h->roots[roots == SHAMPOO_ROOTS_ALL ? 0 : 1 + roots], s);
         if (!rc) rc = enqueue_apply(h, params, sparse, s, false);
         return rc;
     }

@@ -33,7 +33,7 @@ class Config(ctypes.Structure):
     _fields_ = [("block_size", ctypes.c_int32), ("max_precond_dim", ctypes.c_int32),
                 ("root_p", ctypes.c_int32), ("newton_iters", ctypes.c_int32),
                 ("root_mode", ctypes.c_int32), ("lanczos_steps", ctypes.c_int32),
-                ("reserved", ctypes.c_int32),
+                ("root_parts", ctypes.c_int32),
                 ("beta1", ctypes.c_double), ("beta2", ctypes.c_double), ("lr", ctypes.c_double),
                 ("eps_rel", ctypes.c_double), ("graft_eps", ctypes.c_double),
                 ("fp64_cond_threshold", ctypes.c_double)]
@@ -74,6 +74,7 @@ SIGNATURES = {
     "shampoo_bind_state": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
     "shampoo_update_stats": (ctypes.c_int, [_P, ctypes.POINTER(_P), _P]),
     "shampoo_compute_inverse_roots": (ctypes.c_int, [_P, _P]),
+    "shampoo_compute_inverse_roots_part": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
     "shampoo_precondition_and_apply": (ctypes.c_int, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P),
                                                       ctypes.POINTER(SparseRows), _P]),
     "shampoo_step": (ctypes.c_int, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P),
@@ -125,9 +126,25 @@ def make_config(block_size: int, *, max_precond_dim: int = 0, root_p: int = 4,
                 newton_iters: int = 20, root_mode: str = "f32", lanczos_steps: int = 0,
                 beta1: float = 0.9, beta2: float = 0.999, lr: float = 1e-3,
                 eps_rel: float = 1e-6, graft_eps: float = 1e-10,
-                fp64_cond_threshold: float = 1e5) -> Config:
+                fp64_cond_threshold: float = 1e5, root_parts: int = 0) -> Config:
     return Config(block_size, max_precond_dim, root_p, newton_iters, ROOT_MODES[root_mode],
-                  lanczos_steps, 0, beta1, beta2, lr, eps_rel, graft_eps, fp64_cond_threshold)
+                  lanczos_steps, root_parts, beta1, beta2, lr, eps_rel, graft_eps,
+                  fp64_cond_threshold)
+
+
+ROOTS_NONE, ROOTS_ALL = -1, -2
+
+
+def root_selector(step: int, cadence: int, parts: int) -> int:
+    """Which roots a step recomputes: every root at step % cadence == 0, or,
+    with parts = P >= 2 (P dividing the cadence), part (step / (cadence/P)) % P
+    whenever step % (cadence/P) == 0."""
+    if parts <= 1:
+        return ROOTS_ALL if step % cadence == 0 else ROOTS_NONE
+    if cadence % parts:
+        raise ValueError("root_parts must divide the cadence")
+    window = cadence // parts
+    return (step // window) % parts if step % window == 0 else ROOTS_NONE
 
 
 class Plan:
@@ -213,6 +230,10 @@ class Shampoo(Plan):
         _check(lib().shampoo_compute_inverse_roots(self.h, self._stream()),
                "shampoo_compute_inverse_roots")
 
+    def compute_inverse_roots_part(self, part: int):
+        _check(lib().shampoo_compute_inverse_roots_part(self.h, part, self._stream()),
+               "shampoo_compute_inverse_roots_part")
+
     def _apply_args(self, params, grads, sparse):
         pa = self._ptrs(params, lambda k: True, "params")
         ga = self._ptrs(grads, lambda k: k == DENSE, "grads")
@@ -242,14 +263,17 @@ class Shampoo(Plan):
         """One optimizer step (shampoo_step): statistics, roots when
         step % cadence == 0, apply."""
         pa, ga, sp, _keep = self._apply_args(params, grads, sparse)
-        _check(lib().shampoo_step(self.h, pa, ga, sp, 1 if step % cadence == 0 else 0,
-                                  self._stream()), "shampoo_step")
+        sel = root_selector(step, cadence, self.cfg.root_parts)
+        _check(lib().shampoo_step(self.h, pa, ga, sp, sel, self._stream()), "shampoo_step")
 
     def step_separate(self, params, grads, step: int, cadence: int, sparse=None):
         """The same step as three calls on one stream (no concurrency)."""
         self.update_stats(grads)
-        if step % cadence == 0:
+        sel = root_selector(step, cadence, self.cfg.root_parts)
+        if sel == ROOTS_ALL:
             self.compute_inverse_roots()
+        elif sel >= 0:
+            self.compute_inverse_roots_part(sel)
         self.precondition_and_apply(params, grads, sparse)
 
     def profile(self, on: bool = True):

@@ -37,7 +37,10 @@ def check_blocks(run, orc, k, t, root_tol=ROOT32_TOL, check_roots=True, kappa_ga
     factors are held to 1e-8 (their fp64 root), the rest to `root_tol`.
     kappa_gate: only factors whose oracle kappa is below it are held to the
     fp32 bar (F32 mode on ill-conditioned statistics)."""
-    diag = run.opt.diagnostics() if check_roots else None
+    """check_roots: True/False, or a predicate on the global block index
+    (the blocks whose roots this step recomputed)."""
+    due = check_roots if callable(check_roots) else (lambda b: bool(check_roots))
+    diag = run.opt.diagnostics()
     worst = [0.0, 0.0, 0.0]
     _, _, fb, nb = run.opt.tensor(k)
     for j, (bk, st) in enumerate(orc.block_states(k)):
@@ -48,7 +51,7 @@ def check_blocks(run, orc, k, t, root_tol=ROOT32_TOL, check_roots=True, kappa_ga
         eL, eR = rel_fro(_np(L), st.L), rel_fro(_np(R), st.R)
         worst[0] = max(worst[0], eL, eR)
         assert eL <= STATS_TOL and eR <= STATS_TOL, (t, b, eL, eR)
-        if not check_roots:
+        if not due(b):
             continue
         P32 = run.opt.roots(b)
         P64 = run.opt.roots(b, fp64=True)
@@ -77,7 +80,7 @@ def check_blocks(run, orc, k, t, root_tol=ROOT32_TOL, check_roots=True, kappa_ga
                 worst[1] = max(worst[1], e, e64)
                 assert e <= root_tol and e64 <= root_tol, (t, b, f, e, e64, d.status, d.residual,
                                                            exact.kappa)
-            if run.cfg.root_mode == 2 and check_roots:
+            if run.cfg.root_mode == 2:
                 # routing: clearly ill-conditioned factors went fp64, clearly
                 # well-conditioned ones stayed fp32 (factor-2 band)
                 thr = run.cfg.fp64_cond_threshold
@@ -91,8 +94,10 @@ def check_blocks(run, orc, k, t, root_tol=ROOT32_TOL, check_roots=True, kappa_ga
 def run_parity(wl, ids=None, steps=None, root_tol=ROOT32_TOL, kappa_gate=None, **over):
     ids = list(range(len(wl.tensors))) if ids is None else ids
     run = GpuRun(wl, ids, **over)
-    orc = make_oracle(wl, ids, **{k: v for k, v in over.items() if k in ("cadence", "beta1")})
+    orc = make_oracle(wl, ids, **{k: v for k, v in over.items()
+                                  if k in ("cadence", "beta1", "root_parts")})
     cad = over.get("cadence", wl.cadence)
+    parts = over.get("root_parts", 0)
     steps = wl.steps if steps is None else steps
     worst = [0.0, 0.0, 0.0, 0.0]
     n64 = 0
@@ -109,7 +114,7 @@ def run_parity(wl, ids=None, steps=None, root_tol=ROOT32_TOL, kappa_gate=None, *
             assert e <= UPDATE_TOL, (t, k, e)
             if k in orc.blocks:
                 w = check_blocks(run, orc, k, t, root_tol=root_tol, kappa_gate=kappa_gate,
-                                 check_roots=(t % cad == 0))
+                                 check_roots=lambda b: O.root_due(b, t, cad, parts))
                 worst[:3] = [max(a, b) for a, b in zip(worst[:3], w)]
         if t % cad == 0:
             n64 += sum(1 for d in run.opt.diagnostics() if d.status & FP64)
@@ -134,6 +139,25 @@ def test_cfg0_all_fp32_well_conditioned_factors():
 def test_cfg0_roots_f64():
     """Same workload with every root in fp64: stage-isolated <= 1e-8."""
     run_parity(synth.workload(0), steps=3, root_mode="f64")
+
+
+def test_staggered_root_parts():
+    """Staggered root pass: 8 blocks of 128 (cfg0 shapes), roots every 4
+    steps in 2 and in 4 parts (one part every 2 steps / every step); every
+    part's roots stage-isolated on the step that recomputes them, statistics
+    and updates against the oracle on the same schedule."""
+    for parts in (2, 4):
+        wl = synth.workload(0)
+        wl.cadence = 4
+        run_parity(wl, steps=8, root_parts=parts)
+
+
+def test_staggered_root_parts_large_blocks():
+    """The same with blocks above 128 (batched Newton chain and the big-block
+    Lanczos) and ragged edges: 3 parts, roots every 3 steps."""
+    T = synth.TensorSpec
+    wl = _custom([T("a", 300, 200), T("b", 64, 147), T("c", 256, 256)], 256, cadence=3, steps=6)
+    run_parity(wl, root_parts=3)
 
 
 def _custom(tensors, b, **kw):
@@ -244,7 +268,8 @@ def test_committed_roots_are_symmetric():
                 assert torch.equal(P, P.T), (mode, b)
 
 
-def test_step_entry_point_matches_separate_calls():
+@pytest.mark.parametrize("parts", [0, 3])
+def test_step_entry_point_matches_separate_calls(parts):
     """shampoo_step (on steps without roots: statistics and apply of each
     block <= 128 in the fused step kernel) against the three separate calls:
     statistics and Adagrad accumulators bit for bit (same per-element
@@ -255,8 +280,8 @@ def test_step_entry_point_matches_separate_calls():
     T = synth.TensorSpec
     wl = _custom([T("small", 100, 70), T("big", 300, 200), T("wide", 40, 400),
                   T("emb", 500, 32, kind="sparse", grad="sparse_rows"), T("sq", 128, 128)], 256,
-                 max_precond_dim=256, cadence=3, steps=7)
-    runs = [GpuRun(wl), GpuRun(wl)]
+                 max_precond_dim=256, cadence=6 if parts else 3, steps=7)
+    runs = [GpuRun(wl, root_parts=parts), GpuRun(wl, root_parts=parts)]
     worst = 0.0
     for t in range(7):
         W0 = [p.clone() for p in runs[1].params]

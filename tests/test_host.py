@@ -68,8 +68,20 @@ def test_strerror_and_argument_errors():
     arr = (S._P * 1)()
     assert L.shampoo_update_stats(p.h, arr, None) == -2
     assert L.shampoo_compute_inverse_roots(p.h, None) == -2
-    assert L.shampoo_step(p.h, arr, arr, None, 0, None) == -2
-    assert L.shampoo_step(p.h, None, arr, None, 1, None) == -1
+    assert L.shampoo_step(p.h, arr, arr, None, S.ROOTS_NONE, None) == -2
+    assert L.shampoo_step(p.h, None, arr, None, S.ROOTS_ALL, None) == -1
+    # a part index needs a plan with root_parts >= 2
+    assert L.shampoo_step(p.h, arr, arr, None, 0, None) == -1
+    assert L.shampoo_compute_inverse_roots_part(p.h, 0, None) == -1
+    p.close()
+    p = S.Plan([(8, 8, 0), (8, 8, 0), (8, 8, 0)], S.make_config(4, root_parts=3))
+    assert L.shampoo_compute_inverse_roots_part(p.h, 3, None) == -1
+    assert L.shampoo_compute_inverse_roots_part(p.h, -1, None) == -1
+    assert L.shampoo_compute_inverse_roots_part(p.h, 2, None) == -2      # unbound
+    assert L.shampoo_step(p.h, arr, arr, None, 3, None) == -1
+    c = S.make_config(4)
+    c.root_parts = -1
+    assert L.shampoo_create(ctypes.byref(c), 1, descs, ctypes.byref(h)) == -1
     assert L.shampoo_update_stats(p.h, None, None) == -1
     p.close()
 

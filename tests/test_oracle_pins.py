@@ -376,3 +376,43 @@ def test_sparse_rows_by_hand():
     # a_0 = [9+16, 16+9] = [25, 25]; step = 0.5 * [4, 3] / 5
     assert np.allclose(dW[0], [-0.4, -0.3], rtol=1e-15, atol=0)
     assert np.all(dW[1:] == 0)
+
+
+def test_staggered_root_schedule_closed_form():
+    """Staggered roots (root_parts > 1): scalar blocks with a constant gradient
+    g have closed-form statistics L_t = R_t = g^2 (1 - beta2^(t+1)), so the
+    preconditioned gradient D_t = g (L_s (1 + eps_rel))^(-1/2) names the step
+    s whose statistics produced the current roots (identity roots, D = g,
+    before the first recompute).  The expected recompute steps are written
+    out by hand for cadence 4: with 2 parts, blocks 0, 2 at steps 0, 4 and
+    blocks 1, 3 at 2, 6; with 4 parts, block b at steps b and b + 4; with
+    1 part, every block at 0 and 4."""
+    beta2, eps_rel = 0.9, 1e-6
+    gs = [0.5, -1.5, 2.0, 0.25]
+    expected = {
+        1: {0: [0, 4], 1: [0, 4], 2: [0, 4], 3: [0, 4]},
+        2: {0: [0, 4], 1: [2, 6], 2: [0, 4], 3: [2, 6]},
+        4: {0: [0, 4], 1: [1, 5], 2: [2, 6], 3: [3, 7]},
+    }
+    for parts, sched in expected.items():
+        cfg = O.OracleConfig(block_size=1, beta2=beta2, eps_rel=eps_rel, cadence=4, root_parts=parts,
+                             beta1=0.0)
+        orc = O.ShampooOracle(cfg, [(1, 1, "dense")] * 4, [np.zeros((1, 1))] * 4)
+        for t in range(8):
+            orc.step([np.array([[g]]) for g in gs], t)
+            for b, g in enumerate(gs):
+                done = [s for s in sched[b] if s <= t]
+                if not done:
+                    want = g
+                else:
+                    s = done[-1]
+                    want = g / np.sqrt(g * g * (1 - beta2 ** (s + 1)) * (1 + eps_rel))
+                got = orc.last_D[b][0, 0]
+                assert abs(got - want) <= 1e-12 * abs(want), (parts, t, b, got, want)
+
+
+def test_staggered_roots_need_parts_dividing_cadence():
+    cfg = O.OracleConfig(block_size=1, cadence=4, root_parts=3)
+    orc = O.ShampooOracle(cfg, [(1, 1, "dense")], [np.zeros((1, 1))])
+    with pytest.raises(ValueError):
+        orc.step([np.ones((1, 1))], 0)
