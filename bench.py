@@ -172,6 +172,9 @@ def main():
     ap.add_argument("--root-parts", type=int, default=0,
                     help="staggered root pass: recompute 1/P of the roots every cadence/P "
                          "steps (P must divide the cadence); 0 = one pass every cadence steps")
+    ap.add_argument("--async-roots", action="store_true",
+                    help="with --root-parts: each part computed in the background on a stream "
+                         "of the library's own and swapped in when the next part starts")
     ap.add_argument("--no-profile", action="store_true",
                     help="time without the per-launch events (no per-kernel breakdown)")
     args = ap.parse_args()
@@ -195,7 +198,7 @@ def main():
                         fp64_cond_threshold=wl.fp64_cond_threshold, root_parts=args.root_parts)
     shapes = [(t.rows, t.cols, 0 if t.kind == "dense" else 1) for t in wl.tensors]
     t0 = time.time()
-    opt = S.Shampoo(shapes, cfg, device=dev)
+    opt = S.Shampoo(shapes, cfg, device=dev, async_roots=args.async_roots)
     params = [torch.from_numpy(synth.initial_weight(wl, i)).to(dev) for i in range(len(shapes))]
     gs = synth.GradientStream(wl)
     pool = []
@@ -246,6 +249,8 @@ def main():
         e = torch.cuda.Event(enable_timing=True)
         e.record(stream)
         marks.append(e)
+    if args.async_roots:
+        opt.roots_async_end()   # the part still in flight belongs to the timed work
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -381,7 +386,7 @@ def main():
         "config": {"workload": wl.name, "params": wl.n_params, "blocks": opt.n_blocks,
                    "block_size": wl.block_size, "root_cadence": wl.cadence,
                    "newton_iters": wl.newton_iters, "root_mode": wl.root_mode,
-                   "root_parts": args.root_parts,
+                   "root_parts": args.root_parts, "async_roots": bool(args.async_roots),
                    "max_precond_dim": wl.max_precond_dim, "parallelism": "single-gpu"},
         "steps_per_s": steps_per_s,
         "inv_root_blocks_per_s": inv_root_blocks_per_s,

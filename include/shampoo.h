@@ -196,6 +196,24 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream);
  * SHAMPOO_E_STATE, SHAMPOO_E_HIP. */
 int shampoo_compute_inverse_roots_part(shampoo_t* h, int32_t part, void* stream);
 
+/* The same part computed in the background (cues 14-16: the roots are
+ * produced off the critical path while training continues on the last ones,
+ * and swapped in when ready).  shampoo_roots_async_begin enqueues on `stream`
+ * a snapshot of the part's statistics and current roots, then runs the part's
+ * root pass on a stream of the library's own (default priority) that reads
+ * the snapshot and writes staged roots; the calls that follow on `stream`
+ * (statistics, apply) keep using the current roots.  shampoo_roots_async_end
+ * makes `stream` wait for that pass and swaps the staged roots in (a factor
+ * whose root failed keeps its previous one); it does nothing when no part is
+ * in flight.  The result does not depend on timing: roots computed from the
+ * statistics after the step that began the part take effect where end is
+ * called.  Only one part can be in flight; while one is, the synchronous root
+ * calls fail with SHAMPOO_E_STATE and the part's diagnostics are being
+ * written.  Errors: SHAMPOO_E_ARG (root_parts < 2 or part out of range),
+ * SHAMPOO_E_STATE, SHAMPOO_E_HIP. */
+int shampoo_roots_async_begin(shampoo_t* h, int32_t part, void* stream);
+int shampoo_roots_async_end(shampoo_t* h, void* stream);
+
 /* Preconditioned multiply and update (cue 10): for every block
  * D_b = P_L G_b P_R; a <- a + G*G; A = G / (sqrt(a) + graft_eps);
  * U_b = D_b ||A_b||_F / ||D_b||_F (0 when ||D_b|| = 0);

@@ -59,6 +59,7 @@ class OracleConfig:
     graft_eps: float = 1e-10
     cadence: int = 1
     root_parts: int = 1           # > 1: staggered root recompute (see root_due)
+    root_delay: int = 0           # steps between computing roots and using them
 
 
 # ------------------------------------------------------- blocking (Lemma 2)
@@ -204,6 +205,8 @@ class _BlockState:
         self.PR = np.eye(nb)
         self.root_L: Optional[RootResult] = None
         self.root_R: Optional[RootResult] = None
+        # roots computed but not yet in effect: (step they take effect, L, R)
+        self.pending = None
 
 
 def root_due(block_index: int, t: int, cadence: int, parts: int) -> bool:
@@ -237,7 +240,11 @@ class ShampooOracle:
       1. statistics of every Shampoo block (cue 10);
       2. inverse p-th roots of the factors of every block that root_due
          selects (all of them at t % cadence == 0 by default; cue 10, 12,
-         14), keeping the previous root for a non-finite factor;
+         14), keeping the previous root for a non-finite factor.  With
+         root_delay = d > 0 the roots computed at step t (from the statistics
+         after step t) take effect at step t + d, before that step's apply:
+         the roots are produced in the background while the accelerator keeps
+         using the last ones (cues 14-16);
       3. D = PL G PR per block (cue 10);
       4. a += G*G per tensor, A = G/(sqrt(a)+delta), per-block graft U;
          tensors over max_precond_dim use U = A;
@@ -263,6 +270,16 @@ class ShampooOracle:
         cfg = self.cfg
         deltas = []
         gblock = 0   # global block index over the tensors, in order
+        # roots computed root_delay steps ago take effect now
+        for blist in self.blocks.values():
+            for _, st in blist:
+                if st.pending is not None and st.pending[0] <= t:
+                    _, rl, rr = st.pending
+                    st.pending = None
+                    if rl.ok:
+                        st.PL = rl.P
+                    if rr.ok:
+                        st.PR = rr.P
         for i, (m, n, kind) in enumerate(self.shapes):
             W_old = self.W[i]
             if kind == "sparse":
@@ -285,10 +302,13 @@ class ShampooOracle:
                     if recompute:
                         st.root_L = inverse_root(st.L, cfg.eps_rel, cfg.root_p)
                         st.root_R = inverse_root(st.R, cfg.eps_rel, cfg.root_p)
-                        if st.root_L.ok:
-                            st.PL = st.root_L.P
-                        if st.root_R.ok:
-                            st.PR = st.root_R.P
+                        if cfg.root_delay > 0:
+                            st.pending = (t + cfg.root_delay, st.root_L, st.root_R)
+                        else:
+                            if st.root_L.ok:
+                                st.PL = st.root_L.P
+                            if st.root_R.ok:
+                                st.PR = st.root_R.P
                     Db = precondition(st.PL, Gb, st.PR)
                     D_full[r0:r0 + mb, c0:c0 + nb] = Db
                     U[r0:r0 + mb, c0:c0 + nb] = graft(A[r0:r0 + mb, c0:c0 + nb], Db)

@@ -133,6 +133,15 @@ struct shampoo_s {
     // root-pass tables: [0] every factor; [1 + q] part q of a staggered pass
     // (factors of the blocks b with b % root_parts == q)
     std::vector<RootTables> roots;
+    // the asynchronous pass: per part, root tables on the snapshot/staging
+    // areas and the copy jobs around them; a side stream and its events
+    std::vector<RootTables> async_roots;
+    std::vector<int64_t> async_begin_off, async_end_off;
+    std::vector<int> async_begin_n, async_end_n;
+    int64_t off_snap = 0, off_stage = 0;
+    hipStream_t side = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    int async_part = -1;             // part in flight, or -1
     int64_t blockchunks_off = 0, blocknorms_off = 0, rowchunks_off = 0;
     int n_blockchunks = 0, n_rowchunks = 0;
     std::vector<FactorDiag> diag_init;
@@ -164,6 +173,9 @@ struct shampoo_s {
         for (int i = 0; i < kRingSlots; ++i)
             if (ring_ev[i]) (void)hipEventDestroy(ring_ev[i]);
         if (ring) (void)hipHostFree(ring);
+        if (ev_fork) (void)hipEventDestroy(ev_fork);
+        if (ev_join) (void)hipEventDestroy(ev_join);
+        if (side) (void)hipStreamDestroy(side);
     }
 };
 
@@ -366,12 +378,17 @@ int build_plan(shampoo_s* h) {
     int64_t scr32 = 0, scr64 = 0;
     struct Pending { int set; int ld; std::vector<int> fids; bool fp64; bool fused; };
     std::vector<Pending> pend;
+    // sets: 0 every factor; 1..P the parts of a staggered pass; P+1..2P the
+    // same parts reading a snapshot of their statistics and writing staged
+    // roots (the asynchronous pass on the library's own stream)
     const int nparts = c.root_parts > 1 ? c.root_parts : 0;
     h->roots.assign(1 + nparts, RootTables{});
+    h->async_roots.assign(nparts, RootTables{});
+    auto part_of = [&](int set) { return set <= nparts ? set - 1 : set - 1 - nparts; };
     auto in_set = [&](int set, int i) {
-        return set == 0 || h->factors[i].block % nparts == set - 1;
+        return set == 0 || h->factors[i].block % nparts == part_of(set);
     };
-    for (int set = 0; set <= nparts; ++set)
+    for (int set = 0; set <= 2 * nparts; ++set)
     for (int ld : lds) {
         std::vector<int> fids;
         for (int i = 0; i < nf; ++i)
@@ -401,6 +418,32 @@ int build_plan(shampoo_s* h) {
     }
     h->off_scr32 = take(scr32);
     h->off_scr64 = take(scr64);
+    // snapshot (fp64 statistics) and staging (fp32 roots) areas of the
+    // asynchronous pass, sized for the largest part; per-factor places
+    std::vector<int64_t> snap_at(nf, -1), stage_at(nf, -1);
+    if (nparts > 0) {
+        int64_t snap_max = 0, stage_max = 0;
+        std::vector<int64_t> snap_rel(nf), stage_rel(nf);
+        for (int q = 0; q < nparts; ++q) {
+            int64_t a = 0, b = 0;
+            for (int i = 0; i < nf; ++i) {
+                if (h->factors[i].block % nparts != q) continue;
+                const int64_t ld = h->factors[i].ld;
+                snap_rel[i] = a;
+                stage_rel[i] = b;
+                a += ld * ld * 8;
+                b += ld * ld * 4;
+            }
+            snap_max = std::max(snap_max, a);
+            stage_max = std::max(stage_max, b);
+        }
+        h->off_snap = take(snap_max);
+        h->off_stage = take(stage_max);
+        for (int i = 0; i < nf; ++i) {
+            snap_at[i] = h->off_snap + snap_rel[i];
+            stage_at[i] = h->off_stage + stage_rel[i];
+        }
+    }
     h->off_tables = align_up(off, 256);
 
     // ---- static tables
@@ -548,15 +591,21 @@ int build_plan(shampoo_s* h) {
             d.dim = f.dim;
             h->diag_init.push_back(d);
         }
-        for (int set = 0; set <= nparts; ++set) {
+        for (int set = 0; set <= 2 * nparts; ++set) {
             std::vector<LanczosJob> jss, jps, jsb, jpb;
+            const bool async = set > nparts;
             for (int i = 0; i < nf; ++i) {
                 if (!in_set(set, i)) continue;
                 const bool big = h->factors[i].ld > 128;
-                (big ? jsb : jss).push_back(js[i]);
-                (big ? jpb : jps).push_back(jp[i]);
+                LanczosJob a = js[i], b = jp[i];
+                if (async) {
+                    a.off = snap_at[i] / 8;
+                    b.off = stage_at[i] / 4;
+                }
+                (big ? jsb : jss).push_back(a);
+                (big ? jpb : jps).push_back(b);
             }
-            RootTables& rt = h->roots[set];
+            RootTables& rt = async ? h->async_roots[set - 1 - nparts] : h->roots[set];
             rt.n_lanczos_small = (int)jss.size();
             rt.n_lanczos_big = (int)jsb.size();
             rt.lanczos_s_small_off = blob.add(jss);
@@ -568,10 +617,44 @@ int build_plan(shampoo_s* h) {
     }
     for (auto& pd : pend) {
         NewtonChunk ch;
+        const bool async = pd.set > nparts;
+        std::vector<std::pair<int64_t, int64_t>> saved;
+        if (async)   // the job tables of this chunk read the snapshot, write the staging area
+            for (int i : pd.fids) {
+                saved.push_back({h->factors[i].off_s, h->factors[i].off_p});
+                h->factors[i].off_s = snap_at[i];
+                h->factors[i].off_p = stage_at[i];
+            }
         build_newton_chunk(h, ch, pd.fids, pd.ld, pd.fp64, pd.fused,
                            pd.fp64 ? h->off_scr64 : h->off_scr32);
-        RootTables& rt = h->roots[pd.set];
+        if (async)
+            for (size_t k = 0; k < pd.fids.size(); ++k) {
+                h->factors[pd.fids[k]].off_s = saved[k].first;
+                h->factors[pd.fids[k]].off_p = saved[k].second;
+            }
+        RootTables& rt = async ? h->async_roots[pd.set - 1 - nparts] : h->roots[pd.set];
         (pd.fp64 ? rt.chunks64 : rt.chunks32).push_back(std::move(ch));
+    }
+    // copy jobs of the asynchronous pass: snapshot S and P of a part, and the
+    // swap of its staged roots
+    h->async_begin_off.assign(nparts, 0);
+    h->async_end_off.assign(nparts, 0);
+    h->async_begin_n.assign(nparts, 0);
+    h->async_end_n.assign(nparts, 0);
+    for (int q = 0; q < nparts; ++q) {
+        std::vector<CopyJob> b, e;
+        for (int i = 0; i < nf; ++i) {
+            const FactorPlan& f = h->factors[i];
+            if (f.block % nparts != q) continue;
+            const int64_t n2 = (int64_t)f.ld * f.ld;
+            b.push_back({f.off_s, snap_at[i], n2 * 8});
+            b.push_back({f.off_p, stage_at[i], n2 * 4});
+            e.push_back({stage_at[i], f.off_p, n2 * 4});
+        }
+        h->async_begin_n[q] = (int)b.size();
+        h->async_end_n[q] = (int)e.size();
+        h->async_begin_off[q] = blob.add(b);
+        h->async_end_off[q] = blob.add(e);
     }
     // elementwise tables
     {
@@ -833,6 +916,17 @@ int shampoo_bind_state(shampoo_t* h, void* dev_state, size_t bytes, void* stream
                 return SHAMPOO_E_HIP;
     }
     for (int i = 0; i < kRingSlots; ++i) h->ring_used[i] = false;
+    if (h->roots.size() > 1 && !h->side) {
+        // default priority, non-blocking with respect to the null stream
+        if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess) {
+            h->side = nullptr;
+            return SHAMPOO_E_HIP;
+        }
+        if (hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess)
+            return SHAMPOO_E_HIP;
+    }
+    h->async_part = -1;
     int rc = hip_err(hipMemsetAsync(h->arena, 0, h->off_tables, s));
     if (rc) return rc;
     rc = hip_err(hipMemcpyAsync(h->arena + h->off_tables, h->blob.bytes.data(), h->blob.bytes.size(),
@@ -1066,7 +1160,7 @@ extern "C" {
 
 int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
     if (!h) return SHAMPOO_E_ARG;
-    if (!h->bound) return SHAMPOO_E_STATE;
+    if (!h->bound || h->async_part >= 0) return SHAMPOO_E_STATE;
     return enqueue_roots(h, h->roots[0], static_cast<hipStream_t>(stream));
 }
 
@@ -1074,8 +1168,44 @@ int shampoo_compute_inverse_roots_part(shampoo_t* h, int32_t part, void* stream)
     if (!h) return SHAMPOO_E_ARG;
     const int nparts = (int)h->roots.size() - 1;
     if (nparts < 1 || part < 0 || part >= nparts) return SHAMPOO_E_ARG;
-    if (!h->bound) return SHAMPOO_E_STATE;
+    if (!h->bound || h->async_part >= 0) return SHAMPOO_E_STATE;
     return enqueue_roots(h, h->roots[1 + part], static_cast<hipStream_t>(stream));
+}
+
+int shampoo_roots_async_begin(shampoo_t* h, int32_t part, void* stream) {
+    if (!h) return SHAMPOO_E_ARG;
+    const int nparts = (int)h->roots.size() - 1;
+    if (nparts < 1 || part < 0 || part >= nparts) return SHAMPOO_E_ARG;
+    if (!h->bound || h->async_part >= 0) return SHAMPOO_E_STATE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // snapshot of the part's statistics and current roots, in stream order
+    int rc = hip_err(launch_copy_jobs(tab<CopyJob>(h, h->async_begin_off[part]), h->async_begin_n[part],
+                                      h->arena, s));
+    if (!rc) rc = hip_err(hipEventRecord(h->ev_fork, s));
+    if (!rc) rc = hip_err(hipStreamWaitEvent(h->side, h->ev_fork, 0));
+    if (rc) return rc;
+    // the root pass of the part on the library's stream: it reads the
+    // snapshot and writes the staged roots (and the part's diagnostics)
+    rc = enqueue_roots(h, h->async_roots[part], h->side);
+    const int rc_ev = hip_err(hipEventRecord(h->ev_join, h->side));
+    if (rc) return rc;
+    if (rc_ev) return rc_ev;
+    h->async_part = part;
+    return SHAMPOO_OK;
+}
+
+int shampoo_roots_async_end(shampoo_t* h, void* stream) {
+    if (!h) return SHAMPOO_E_ARG;
+    if (!h->bound) return SHAMPOO_E_STATE;
+    if (h->async_part < 0) return SHAMPOO_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int q = h->async_part;
+    int rc = hip_err(hipStreamWaitEvent(s, h->ev_join, 0));
+    if (!rc) rc = hip_err(launch_copy_jobs(tab<CopyJob>(h, h->async_end_off[q]), h->async_end_n[q],
+                                           h->arena, s));
+    if (rc) return rc;
+    h->async_part = -1;
+    return SHAMPOO_OK;
 }
 
 int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const float* const* grads,
@@ -1096,7 +1226,7 @@ int shampoo_step(shampoo_t* h, float* const* params, const float* const* grads,
     const int nparts = (int)h->roots.size() - 1;
     if (roots != SHAMPOO_ROOTS_NONE && roots != SHAMPOO_ROOTS_ALL && (roots < 0 || roots >= nparts))
         return SHAMPOO_E_ARG;
-    if (!h->bound) return SHAMPOO_E_STATE;
+    if (!h->bound || (roots != SHAMPOO_ROOTS_NONE && h->async_part >= 0)) return SHAMPOO_E_STATE;
     int rc = check_stats_args(h, grads);
     if (!rc) rc = check_apply_args(h, params, grads, sparse);
     if (rc) return rc;

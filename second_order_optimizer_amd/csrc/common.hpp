@@ -61,6 +61,11 @@ struct StepJob {
     int64_t l_off, r_off;   // fp64 statistics (arena elements of 8 bytes)
 };
 
+// One contiguous copy inside the state buffer (bytes, multiples of 16).
+struct CopyJob {
+    int64_t src, dst, bytes;
+};
+
 // A tile of the batched GEMM launch: which task and which 128x128 tile.
 struct TileRef {
     int32_t task;

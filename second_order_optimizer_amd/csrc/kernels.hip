@@ -1702,6 +1702,25 @@ __global__ __launch_bounds__(1024) void k_step128(const StepJob* __restrict__ jo
     }
 }
 
+// Copies inside the state buffer, one job per workgroup (snapshot of the
+// statistics and roots of a root-pass part, and the swap of its new roots).
+__global__ __launch_bounds__(256) void k_copy_jobs(const CopyJob* __restrict__ jobs,
+                                                  unsigned char* __restrict__ arena) {
+    const CopyJob jb = jobs[blockIdx.x];
+    const float4* src = reinterpret_cast<const float4*>(arena + jb.src);
+    float4* dst = reinterpret_cast<float4*>(arena + jb.dst);
+    const int64_t n = jb.bytes / 16;
+    for (int64_t e = threadIdx.x; e < n; e += 4 * 256) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (e + 256 * u < n) v[u] = src[e + 256 * u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (e + 256 * u < n) dst[e + 256 * u] = v[u];
+    }
+}
+
 // Identity roots for every factor (state initialisation).
 __global__ __launch_bounds__(256) void k_set_identity(const FactorJob* __restrict__ jobs,
                                                      float* __restrict__ arena) {
@@ -1984,6 +2003,11 @@ hipError_t launch_apply128(const ApplyJob* jobs, int njobs, const uint64_t* base
     if (njobs <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_apply128, dim3(njobs), dim3(512), 0, s, jobs, bases, arena, delta, partA,
                        partD, ua);
+    return hipGetLastError();
+}
+hipError_t launch_copy_jobs(const CopyJob* jobs, int njobs, unsigned char* arena, hipStream_t s) {
+    if (njobs <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_copy_jobs, dim3(njobs), dim3(256), 0, s, jobs, arena);
     return hipGetLastError();
 }
 hipError_t launch_set_identity(const FactorJob* jobs, int njobs, float* arena, hipStream_t s) {

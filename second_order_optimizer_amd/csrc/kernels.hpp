@@ -81,6 +81,7 @@ hipError_t launch_newton128(const FactorJob* jobs, int njobs, const double* stat
 hipError_t launch_apply128(const ApplyJob* jobs, int njobs, const uint64_t* bases, float* arena,
                            float delta, double* partA, double* partD, const UpdateArgs& ua,
                            hipStream_t s);
+hipError_t launch_copy_jobs(const CopyJob* jobs, int njobs, unsigned char* arena, hipStream_t s);
 hipError_t launch_set_identity(const FactorJob* jobs, int njobs, float* arena, hipStream_t s);
 hipError_t launch_adagrad_norm(const BlockChunk* chunks, int nchunks, const uint64_t* bases,
                                float* arena, float delta, double* partA, hipStream_t s);

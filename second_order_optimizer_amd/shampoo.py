@@ -75,6 +75,8 @@ SIGNATURES = {
     "shampoo_update_stats": (ctypes.c_int, [_P, ctypes.POINTER(_P), _P]),
     "shampoo_compute_inverse_roots": (ctypes.c_int, [_P, _P]),
     "shampoo_compute_inverse_roots_part": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
+    "shampoo_roots_async_begin": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
+    "shampoo_roots_async_end": (ctypes.c_int, [_P, _P]),
     "shampoo_precondition_and_apply": (ctypes.c_int, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P),
                                                       ctypes.POINTER(SparseRows), _P]),
     "shampoo_step": (ctypes.c_int, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P),
@@ -193,8 +195,15 @@ class Plan:
 class Shampoo(Plan):
     """Device-bound optimizer: the state buffer is a uint8 CUDA tensor."""
 
-    def __init__(self, shapes, cfg: Config, device="cuda"):
+    def __init__(self, shapes, cfg: Config, device="cuda", async_roots: bool = False):
+        """async_roots (needs cfg.root_parts >= 2): each due part of the root
+        pass runs in the background from the statistics of the step that
+        starts it, and its roots take effect when the next part starts
+        (cadence / root_parts steps later)."""
         import torch
+        if async_roots and cfg.root_parts < 2:
+            raise ValueError("async_roots needs root_parts >= 2")
+        self.async_roots = async_roots
         super().__init__(shapes, cfg)
         self.torch = torch
         dev = torch.device(device)
@@ -264,12 +273,35 @@ class Shampoo(Plan):
         step % cadence == 0, apply."""
         pa, ga, sp, _keep = self._apply_args(params, grads, sparse)
         sel = root_selector(step, cadence, self.cfg.root_parts)
+        if self.async_roots:
+            if sel >= 0:   # the part started cadence/P steps ago takes effect now
+                self.roots_async_end()
+            _check(lib().shampoo_step(self.h, pa, ga, sp, ROOTS_NONE, self._stream()),
+                   "shampoo_step")
+            if sel >= 0:
+                self.roots_async_begin(sel)
+            return
         _check(lib().shampoo_step(self.h, pa, ga, sp, sel, self._stream()), "shampoo_step")
+
+    def roots_async_begin(self, part: int):
+        _check(lib().shampoo_roots_async_begin(self.h, part, self._stream()),
+               "shampoo_roots_async_begin")
+
+    def roots_async_end(self):
+        _check(lib().shampoo_roots_async_end(self.h, self._stream()), "shampoo_roots_async_end")
 
     def step_separate(self, params, grads, step: int, cadence: int, sparse=None):
         """The same step as three calls on one stream (no concurrency)."""
-        self.update_stats(grads)
         sel = root_selector(step, cadence, self.cfg.root_parts)
+        if self.async_roots:
+            if sel >= 0:
+                self.roots_async_end()
+            self.update_stats(grads)
+            self.precondition_and_apply(params, grads, sparse)
+            if sel >= 0:
+                self.roots_async_begin(sel)
+            return
+        self.update_stats(grads)
         if sel == ROOTS_ALL:
             self.compute_inverse_roots()
         elif sel >= 0:

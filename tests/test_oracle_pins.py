@@ -416,3 +416,29 @@ def test_staggered_roots_need_parts_dividing_cadence():
     orc = O.ShampooOracle(cfg, [(1, 1, "dense")], [np.zeros((1, 1))])
     with pytest.raises(ValueError):
         orc.step([np.ones((1, 1))], 0)
+
+
+def test_delayed_roots_closed_form():
+    """Roots produced in the background (root_delay d): the roots computed at
+    step s from the statistics after step s take effect at step s + d, before
+    that step's apply.  Scalar blocks as above; cadence 4 in 4 parts with a
+    delay of 1 step (block b recomputed at b and b + 4, used from b + 1 and
+    b + 5), and one pass every 4 steps with a delay of 2 (computed at 0 and
+    4, used from 2 and 6)."""
+    beta2, eps_rel = 0.9, 1e-6
+    gs = [0.5, -1.5, 2.0, 0.25]
+    cases = {
+        (4, 1): {0: [(0, 1), (4, 5)], 1: [(1, 2), (5, 6)], 2: [(2, 3), (6, 7)], 3: [(3, 4), (7, 8)]},
+        (1, 2): {b: [(0, 2), (4, 6)] for b in range(4)},
+    }
+    for (parts, delay), sched in cases.items():
+        cfg = O.OracleConfig(block_size=1, beta2=beta2, eps_rel=eps_rel, cadence=4, root_parts=parts,
+                             root_delay=delay, beta1=0.0)
+        orc = O.ShampooOracle(cfg, [(1, 1, "dense")] * 4, [np.zeros((1, 1))] * 4)
+        for t in range(8):
+            orc.step([np.array([[g]]) for g in gs], t)
+            for b, g in enumerate(gs):
+                live = [s for s, used_from in sched[b] if used_from <= t]
+                want = g if not live else g / np.sqrt(g * g * (1 - beta2 ** (live[-1] + 1)) * (1 + eps_rel))
+                got = orc.last_D[b][0, 0]
+                assert abs(got - want) <= 1e-12 * abs(want), (parts, delay, t, b, got, want)
