@@ -90,6 +90,13 @@ typedef struct {
                                  over every factor; P >= 2 also plans P parts, part q
                                  holding the factors of the blocks b with b % P == q
                                  (shampoo_compute_inverse_roots_part, shampoo_step)      */
+    int32_t large_layer;      /* dense tensors too large for Shampoo blocks (a dimension
+                                 above max_precond_dim): 0 = diagonal Adagrad; 1 = when
+                                 the other dimension fits, one-sided preconditioning of
+                                 that side only (Lemma 1, cue 16: for a giant embedding
+                                 or softmax layer only one of L or R is used), with the
+                                 exponent -2/root_p so that the one factor carries the
+                                 whole -1/2 of full-matrix Adagrad; needs an even root_p */
     double beta1;             /* momentum: mom <- beta1 mom + U                          */
     double beta2;             /* statistics: S <- beta2 S + (1-beta2) outer(G) (beta2<1),
                                  S <- S + outer(G) when beta2 == 1; 1 - beta2 is formed in

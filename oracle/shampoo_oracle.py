@@ -60,6 +60,7 @@ class OracleConfig:
     cadence: int = 1
     root_parts: int = 1           # > 1: staggered root recompute (see root_due)
     root_delay: int = 0           # steps between computing roots and using them
+    large_layer: int = 0          # 1: one-sided preconditioning (see one_sided_side)
 
 
 # ------------------------------------------------------- blocking (Lemma 2)
@@ -85,6 +86,22 @@ def uses_shampoo(m: int, n: int, cfg: OracleConfig) -> bool:
 
 
 # -------------------------------------------------------------- statistics
+def one_sided_side(m: int, n: int, cfg: "OracleConfig") -> Optional[str]:
+    """Lemma 1 (podcast cue 16): for a layer too large to precondition on both
+    sides (a giant embedding or softmax), only one of L or R is used.  A
+    dense tensor that does not use Shampoo blocks gets one-sided
+    preconditioning when large_layer is set and one dimension fits under
+    max_precond_dim: "R" (statistics G^T G, D = G P) when the columns fit,
+    else "L" (G G^T, D = P G).  None: diagonal Adagrad."""
+    if not cfg.large_layer or cfg.max_precond_dim <= 0 or uses_shampoo(m, n, cfg):
+        return None
+    if n <= cfg.max_precond_dim:
+        return "R"
+    if m <= cfg.max_precond_dim:
+        return "L"
+    return None
+
+
 def ema_weights(beta2: float) -> Tuple[float, float]:
     """(decay, weight of the new outer product).  The transcript says the
     statistics accumulate outer products (cue 10); this library keeps an
@@ -209,6 +226,17 @@ class _BlockState:
         self.pending = None
 
 
+class _OneSidedState:
+    """Statistics and root of a one-sided (Lemma 1) tensor."""
+
+    def __init__(self, side: str, dim: int):
+        self.side = side
+        self.S = np.zeros((dim, dim))
+        self.P = np.eye(dim)
+        self.root: Optional[RootResult] = None
+        self.pending = None
+
+
 def root_due(block_index: int, t: int, cadence: int, parts: int) -> bool:
     """Whether the roots of Shampoo block `block_index` (counted over all
     tensors, in order) are recomputed at step t, after that step's statistics.
@@ -247,7 +275,9 @@ class ShampooOracle:
          using the last ones (cues 14-16);
       3. D = PL G PR per block (cue 10);
       4. a += G*G per tensor, A = G/(sqrt(a)+delta), per-block graft U;
-         tensors over max_precond_dim use U = A;
+         tensors over max_precond_dim use U = A, or with large_layer the
+         one-sided preconditioner (Lemma 1) of the side that fits, grafted
+         over the whole tensor;
       5. heavy-ball momentum and weight update;
       6. sparse tables: sparse-row Adagrad.
     """
@@ -264,6 +294,16 @@ class ShampooOracle:
             if kind == "dense" and uses_shampoo(m, n, cfg):
                 self.blocks[i] = [(bk, _BlockState(bk[1], bk[3]))
                                   for bk in blocks(m, n, cfg.block_size)]
+        # one-sided tensors, numbered for the root schedule after every block
+        n_blocks = sum(len(v) for v in self.blocks.values())
+        self.one_sided: Dict[int, Tuple[int, _OneSidedState]] = {}
+        for i, (m, n, kind) in enumerate(self.shapes):
+            side = one_sided_side(m, n, cfg) if kind == "dense" else None
+            if side is not None:
+                if cfg.root_p % 2:
+                    raise ValueError("one-sided preconditioning needs an even root_p")
+                self.one_sided[i] = (n_blocks + len(self.one_sided),
+                                     _OneSidedState(side, n if side == "R" else m))
         self.last_D: Dict[int, np.ndarray] = {}
 
     def step(self, grads, t: int) -> List[np.ndarray]:
@@ -280,6 +320,12 @@ class ShampooOracle:
                         st.PL = rl.P
                     if rr.ok:
                         st.PR = rr.P
+        for _, os_st in self.one_sided.values():
+            if os_st.pending is not None and os_st.pending[0] <= t:
+                _, rr = os_st.pending
+                os_st.pending = None
+                if rr.ok:
+                    os_st.P = rr.P
         for i, (m, n, kind) in enumerate(self.shapes):
             W_old = self.W[i]
             if kind == "sparse":
@@ -313,6 +359,22 @@ class ShampooOracle:
                     D_full[r0:r0 + mb, c0:c0 + nb] = Db
                     U[r0:r0 + mb, c0:c0 + nb] = graft(A[r0:r0 + mb, c0:c0 + nb], Db)
                 self.last_D[i] = D_full
+            elif i in self.one_sided:
+                # Lemma 1: S <- beta2 S + w G^T G (or G G^T), P = (S + eps I)^(-2/p)
+                # (the one factor carries the whole -1/2), D = G P (or P G),
+                # grafted over the whole tensor
+                idx, st = self.one_sided[i]
+                d, w = ema_weights(cfg.beta2)
+                st.S = d * st.S + w * ((G.T @ G) if st.side == "R" else (G @ G.T))
+                if root_due(idx, t, cfg.cadence, cfg.root_parts):
+                    st.root = inverse_root(st.S, cfg.eps_rel, cfg.root_p // 2)
+                    if cfg.root_delay > 0:
+                        st.pending = (t + cfg.root_delay, st.root)
+                    elif st.root.ok:
+                        st.P = st.root.P
+                D = (G @ st.P) if st.side == "R" else (st.P @ G)
+                self.last_D[i] = D
+                U = graft(A, D)
             else:
                 U = A
             self.mom[i], self.W[i] = momentum_update(self.mom[i], self.W[i], U,

@@ -33,7 +33,7 @@ class Config(ctypes.Structure):
     _fields_ = [("block_size", ctypes.c_int32), ("max_precond_dim", ctypes.c_int32),
                 ("root_p", ctypes.c_int32), ("newton_iters", ctypes.c_int32),
                 ("root_mode", ctypes.c_int32), ("lanczos_steps", ctypes.c_int32),
-                ("root_parts", ctypes.c_int32),
+                ("root_parts", ctypes.c_int32), ("large_layer", ctypes.c_int32),
                 ("beta1", ctypes.c_double), ("beta2", ctypes.c_double), ("lr", ctypes.c_double),
                 ("eps_rel", ctypes.c_double), ("graft_eps", ctypes.c_double),
                 ("fp64_cond_threshold", ctypes.c_double)]
@@ -128,9 +128,10 @@ def make_config(block_size: int, *, max_precond_dim: int = 0, root_p: int = 4,
                 newton_iters: int = 20, root_mode: str = "f32", lanczos_steps: int = 0,
                 beta1: float = 0.9, beta2: float = 0.999, lr: float = 1e-3,
                 eps_rel: float = 1e-6, graft_eps: float = 1e-10,
-                fp64_cond_threshold: float = 1e5, root_parts: int = 0) -> Config:
+                fp64_cond_threshold: float = 1e5, root_parts: int = 0,
+                large_layer: int = 0) -> Config:
     return Config(block_size, max_precond_dim, root_p, newton_iters, ROOT_MODES[root_mode],
-                  lanczos_steps, root_parts, beta1, beta2, lr, eps_rel, graft_eps,
+                  lanczos_steps, root_parts, large_layer, beta1, beta2, lr, eps_rel, graft_eps,
                   fp64_cond_threshold)
 
 

@@ -442,3 +442,72 @@ def test_delayed_roots_closed_form():
                 want = g if not live else g / np.sqrt(g * g * (1 - beta2 ** (live[-1] + 1)) * (1 + eps_rel))
                 got = orc.last_D[b][0, 0]
                 assert abs(got - want) <= 1e-12 * abs(want), (parts, delay, t, b, got, want)
+
+
+def _full_matrix_inv_sqrt(H):
+    lam, V = np.linalg.eigh(H)
+    return (V * lam ** -0.5) @ V.T
+
+
+@pytest.mark.parametrize("shape,side", [((7, 3), "R"), ((3, 7), "L")])
+def test_one_sided_matches_kronecker_full_matrix(shape, side):
+    """Lemma 1 (cue 16): a tensor preconditioned on one side only.  The
+    one-sided preconditioner is the full-matrix one restricted to the
+    Kronecker structure I_m (x) (R + eps I) (right) or (L + eps I) (x) I_n
+    (left), raised to -1/2: built here explicitly (21 x 21) and applied to
+    vec(G) (row-major), after two steps of statistics."""
+    m, n = shape
+    rng = np.random.default_rng(3)
+    cfg = O.OracleConfig(block_size=2, max_precond_dim=4, large_layer=1, beta2=0.9, cadence=1)
+    orc = O.ShampooOracle(cfg, [(m, n, "dense")], [np.zeros((m, n))])
+    assert O.one_sided_side(m, n, cfg) == side
+    Gs = [rng.standard_normal((m, n)) for _ in range(2)]
+    S = np.zeros((n, n)) if side == "R" else np.zeros((m, m))
+    for t, G in enumerate(Gs):
+        orc.step([G], t)
+        S = 0.9 * S + 0.1 * ((G.T @ G) if side == "R" else (G @ G.T))
+    eps = 1e-6 * np.linalg.eigvalsh(S)[-1]
+    Sd = S + eps * np.eye(S.shape[0])
+    H = np.kron(np.eye(m), Sd) if side == "R" else np.kron(Sd, np.eye(n))
+    D_ref = (_full_matrix_inv_sqrt(H) @ Gs[-1].reshape(-1)).reshape(m, n)
+    assert np.allclose(orc.last_D[0], D_ref, rtol=1e-9, atol=1e-12)
+
+
+def test_one_sided_rank_one_closed_form():
+    """G = u v^T, one step from zero statistics: R = w |u|^2 v v^T has the one
+    eigenvalue lam = w |u|^2 |v|^2 along v, so D = G P = G / sqrt(lam + eps),
+    eps = 1e-6 lam; the graft rescales it to ||A||."""
+    rng = np.random.default_rng(4)
+    u, v = rng.standard_normal(9), rng.standard_normal(3)
+    G = np.outer(u, v)
+    cfg = O.OracleConfig(block_size=2, max_precond_dim=4, large_layer=1, beta2=0.99, cadence=1,
+                         beta1=0.0, lr=1.0)
+    orc = O.ShampooOracle(cfg, [(9, 3, "dense")], [np.zeros((9, 3))])
+    dW = orc.step([G], 0)[0]
+    lam = 0.01 * (u @ u) * (v @ v)
+    D = G / np.sqrt(lam * (1 + 1e-6))
+    assert np.allclose(orc.last_D[0], D, rtol=1e-12)
+    A = G / (np.abs(G) + 1e-10)                  # a = G^2 after one step
+    U = D * np.linalg.norm(A) / np.linalg.norm(D)
+    assert np.allclose(dW, -U, rtol=1e-12)
+
+
+def test_one_sided_fallbacks_and_numbering():
+    """Without large_layer, or when neither side fits, the diagonal Adagrad
+    fallback stays; one-sided tensors are numbered for the root schedule
+    after every Shampoo block: with one 2 x 2 block and one one-sided tensor,
+    2 parts and cadence 2, the block's roots come at t = 0, 2 and the
+    one-sided root at t = 1, 3 (identity preconditioner at t = 0)."""
+    cfg0 = O.OracleConfig(block_size=2, max_precond_dim=4)
+    assert O.one_sided_side(9, 3, cfg0) is None
+    cfg1 = O.OracleConfig(block_size=2, max_precond_dim=4, large_layer=1)
+    assert O.one_sided_side(9, 8, cfg1) is None and O.one_sided_side(2, 2, cfg1) is None
+    cfg = O.OracleConfig(block_size=2, max_precond_dim=4, large_layer=1, cadence=2, root_parts=2,
+                         beta2=0.9)
+    orc = O.ShampooOracle(cfg, [(2, 2, "dense"), (9, 3, "dense")], [np.zeros((2, 2)), np.zeros((9, 3))])
+    assert orc.one_sided[1][0] == 1
+    G = np.arange(1.0, 28.0).reshape(9, 3) / 10.0
+    orc.step([np.eye(2), G], 0)
+    assert np.allclose(orc.last_D[1], G)          # no one-sided root yet
+    orc.step([np.eye(2), G], 1)
+    assert not np.allclose(orc.last_D[1], G)
