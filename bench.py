@@ -53,6 +53,28 @@ def kernel_hash() -> str:
 
 
 # ------------------------------------------------------------------ work model
+def factor_dims(opt, root_p):
+    """(dimension, root exponent) of every factor, in factor order: L and R
+    of each Lemma-2 block, then the one factor of each one-sided block
+    (exponent root_p / 2)."""
+    blocks = [opt.block(i) for i in range(opt.n_blocks)]
+    out = []
+    for b in blocks:
+        if not b.one_sided:
+            out += [(b.rows, root_p), (b.cols, root_p)]
+    for b in blocks:
+        if b.one_sided:
+            out.append((b.cols if b.factor_r >= 0 else b.rows, root_p // 2))
+    return out
+
+
+def newton_flops(n, p, iters):
+    """Coupled-Newton GEMM flops of one n x n root: X T, then T^p M by
+    repeated squaring (log2 p - 1 squarings after T^2) and the M update."""
+    gemms = 2 + int(round(math.log2(p))) if p > 1 else 2
+    return gemms * 2.0 * n ** 3 * iters
+
+
 def work_model(wl, opt, n_fp64_factors_per_pass):
     """Algorithmic flops / bytes per launch of each kernel family.
 
@@ -62,16 +84,20 @@ def work_model(wl, opt, n_fp64_factors_per_pass):
     formulas must move once (fp32)."""
     nb = opt.n_blocks
     blocks = [opt.block(i) for i in range(nb)]
+    onesided = [b for b in blocks if b.one_sided]
+    blocks = [b for b in blocks if not b.one_sided]
     gram = sum(2.0 * (b.rows ** 2 * b.cols + b.cols ** 2 * b.rows) for b in blocks)
     apply_t = sum(2.0 * b.rows * b.cols ** 2 for b in blocks)
     apply_d = sum(2.0 * b.rows ** 2 * b.cols for b in blocks)
-    p = wl.root_p
-    gemms_per_iter = 2 + int(round(math.log2(p))) if p > 1 else 2
-    dims = [b.rows for b in blocks] + [b.cols for b in blocks]
-    root_flops_all = sum(gemms_per_iter * 2.0 * n ** 3 * wl.newton_iters for n in dims)
-    shampoo_params = sum(b.rows * b.cols for b in blocks)
+    # one-sided blocks (Lemma 1): S = G^T G or G G^T and D = G P or P G are
+    # each 2 dim numel flops
+    onesided_flops = sum(2.0 * (b.cols if b.factor_r >= 0 else b.rows) * b.rows * b.cols
+                         for b in onesided)
+    dims = [(dim, p) for dim, p in factor_dims(opt, wl.root_p)]
+    root_flops_all = sum(newton_flops(n, p, wl.newton_iters) for n, p in dims)
+    shampoo_params = sum(b.rows * b.cols for b in blocks) + sum(b.rows * b.cols for b in onesided)
     small = [b for b in blocks if b.rows <= 128 and b.cols <= 128]
-    big = [b for b in blocks if not (b.rows <= 128 and b.cols <= 128)]
+    big = [b for b in blocks if not (b.rows <= 128 and b.cols <= 128)] + onesided
     dense_fallback = sum(t.numel for t in wl.tensors if t.kind == "dense") - shampoo_params
     # tensors whose blocks are all <= 128 get their momentum and weight update
     # inside the fused apply kernel
@@ -92,8 +118,10 @@ def work_model(wl, opt, n_fp64_factors_per_pass):
         "step_small_bytes": step_small_bytes,
         "apply_small_bytes": apply_small_bytes, "unfused_params": unfused_params,
         "apply_small": sum(2.0 * (b.rows * b.cols ** 2 + b.rows ** 2 * b.cols) for b in small),
-        "apply_t_big": sum(2.0 * b.rows * b.cols ** 2 for b in big),
-        "apply_d_big": sum(2.0 * b.rows ** 2 * b.cols for b in big),
+        "apply_t_big": sum(2.0 * b.rows * b.cols ** 2 for b in big if not b.one_sided),
+        "apply_d_big": sum(2.0 * b.rows ** 2 * b.cols for b in big if not b.one_sided) +
+        onesided_flops,
+        "stats_onesided": onesided_flops,
         "shampoo_params_big": sum(b.rows * b.cols for b in big),
         "root_flops_all": root_flops_all,
         "root_flops_per_factor_mean": root_flops_all / max(len(dims), 1),
@@ -175,6 +203,10 @@ def main():
     ap.add_argument("--async-roots", action="store_true",
                     help="with --root-parts: each part computed in the background on a stream "
                          "of the library's own and swapped in when the next part starts")
+    ap.add_argument("--large-layer", action="store_true",
+                    help="one-sided preconditioning (Lemma 1) of dense tensors with one "
+                         "dimension above max_precond_dim (the embedding of the Transformer "
+                         "workload) instead of diagonal Adagrad")
     ap.add_argument("--no-profile", action="store_true",
                     help="time without the per-launch events (no per-kernel breakdown)")
     args = ap.parse_args()
@@ -195,7 +227,8 @@ def main():
     cfg = S.make_config(wl.block_size, max_precond_dim=wl.max_precond_dim, root_p=wl.root_p,
                         newton_iters=wl.newton_iters, root_mode=wl.root_mode, beta1=wl.beta1,
                         beta2=wl.beta2, lr=wl.lr, eps_rel=wl.eps_rel, graft_eps=wl.graft_eps,
-                        fp64_cond_threshold=wl.fp64_cond_threshold, root_parts=args.root_parts)
+                        fp64_cond_threshold=wl.fp64_cond_threshold, root_parts=args.root_parts,
+                        large_layer=1 if args.large_layer else 0)
     shapes = [(t.rows, t.cols, 0 if t.kind == "dense" else 1) for t in wl.tensors]
     t0 = time.time()
     opt = S.Shampoo(shapes, cfg, device=dev, async_roots=args.async_roots)
@@ -279,19 +312,16 @@ def main():
 
     stages = {}
     fp64_share = n64 / max(len(diag), 1)
-    gpi = 2 + int(round(math.log2(wl.root_p)))      # GEMMs per coupled-Newton iteration
-    lds = []
-    for b in range(opt.n_blocks):
-        bl = opt.block(b)
-        lds += [bl.ld_l, bl.ld_r]
-    fl = [gpi * 2.0 * d.dim ** 3 * wl.newton_iters for d in diag]
+    fdims = factor_dims(opt, wl.root_p)
+    fl = [newton_flops(n, p, wl.newton_iters) for n, p in fdims]
     f32 = wl.root_mode != "f64"
-    flops_fused_root = sum(x for x, ld in zip(fl, lds) if f32 and ld <= 128)
-    flops_f32_root = sum(x for x, ld in zip(fl, lds) if f32 and ld > 128)
+    flops_fused_root = sum(x for x, (n, _) in zip(fl, fdims) if f32 and n <= 128)
+    flops_f32_root = sum(x for x, (n, _) in zip(fl, fdims) if f32 and n > 128)
     flops_f64_root = sum(x for x, d in zip(fl, diag) if d.status & S.FACTOR_FP64)
     alg = {
         # name: (work per launch, unit, bound, peak)
         "stats_gram_f64": (wm["gram"], "TFLOP/s", "mfma", PEAK_TFLOPS["f64"]),
+        "stats_onesided": (wm["stats_onesided"], "TFLOP/s", "mfma", PEAK_TFLOPS["f64"]),
         "apply_gemm_t": (wm["apply_t_big"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]),
         "apply_gemm_d": (wm["apply_d_big"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]),
         "adagrad_norm": (wm["shampoo_params_big"] * 12.0, "GB/s", "hbm", PEAK_HBM_GBS),
@@ -387,6 +417,7 @@ def main():
                    "block_size": wl.block_size, "root_cadence": wl.cadence,
                    "newton_iters": wl.newton_iters, "root_mode": wl.root_mode,
                    "root_parts": args.root_parts, "async_roots": bool(args.async_roots),
+                   "large_layer": bool(args.large_layer),
                    "max_precond_dim": wl.max_precond_dim, "parallelism": "single-gpu"},
         "steps_per_s": steps_per_s,
         "inv_root_blocks_per_s": inv_root_blocks_per_s,

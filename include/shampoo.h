@@ -136,13 +136,18 @@ enum {
     SHAMPOO_FACTOR_ZERO = 16             /* lambda_max <= 0 (no statistics): root = I   */
 };
 
-/* Where one block's state lives in the bound state buffer (byte offsets). */
+/* Where one block's state lives in the bound state buffer (byte offsets).
+ * A one-sided block (large_layer = 1) is a whole tensor with a single factor:
+ * the fields of the side that is not preconditioned are ld 0, factor -1 and
+ * offsets -1; its statistic S is kept in both triangles and its roots are
+ * (S + eps I)^(-2/root_p). */
 typedef struct {
     int32_t tensor;       /* index into the tensor list                               */
     int32_t row0, col0;   /* top-left element of the block in the tensor               */
     int32_t rows, cols;   /* m_b, n_b (ragged at the edges)                            */
     int32_t ld_l, ld_r;   /* leading dimension (padded) of the L- and R-side matrices  */
     int32_t factor_l, factor_r; /* factor indices (diagnostics order)                 */
+    int32_t one_sided;    /* 1: one-sided block of a large layer (Lemma 1)             */
     int64_t off_l, off_r;       /* fp64 statistics L (rows x rows), R (cols x cols),
                                    row-major with leading dims ld_l, ld_r; symmetric,
                                    only the upper triangle (column >= row) is kept    */
@@ -156,10 +161,15 @@ typedef struct {
  * out: receives the handle.  Host only: no HIP call, no device memory.
  * Dense tensors whose dimensions are both <= max_precond_dim (or any, when it
  * is 0) are split into Lemma-2 blocks (cue 16); each block gets an L and an R
- * factor.  Errors: SHAMPOO_E_ARG (null pointer, n_tensors < 1, a dimension
+ * factor.  With large_layer = 1, a dense tensor with one dimension above
+ * max_precond_dim and the other within it becomes one more block, numbered
+ * after every Lemma-2 block (tensors in order), with one factor for the side
+ * that fits.  Errors: SHAMPOO_E_ARG (null pointer, n_tensors < 1, a dimension
  * < 1, block_size < 1, newton_iters < 1, beta2 outside (0,1], eps_rel < 0,
- * unknown kind or root_mode), SHAMPOO_E_UNSUPPORTED (root_p not in
- * {1,2,4,8}), SHAMPOO_E_NOMEM.
+ * unknown kind or root_mode, large_layer not 0 or 1), SHAMPOO_E_UNSUPPORTED
+ * (root_p not in {1,2,4,8}; root_p odd with large_layer = 1; a factor
+ * dimension above 1024; rows above 2^31 - 1 or cols above 2^20),
+ * SHAMPOO_E_NOMEM.
  */
 int shampoo_create(const shampoo_config* cfg, int32_t n_tensors,
                    const shampoo_tensor_desc* tensors, shampoo_t** out);
@@ -179,13 +189,17 @@ int shampoo_bind_state(shampoo_t* h, void* dev_state, size_t bytes, void* stream
 
 /* Statistics (cue 10): for every block, L <- beta2 L + w G_b G_b^T and
  * R <- beta2 R + w G_b^T G_b, w = 1 - beta2 (1 when beta2 == 1): fp32
- * gradients, fp64 products and accumulation on MFMA, fp64 storage.  grads: n_tensors device pointers, read only; entries of tensors that
- * are not Shampoo-blocked are ignored (may be NULL).  Errors: SHAMPOO_E_ARG,
- * SHAMPOO_E_STATE, SHAMPOO_E_HIP. */
+ * gradients, fp64 products and accumulation on MFMA, fp64 storage.  A
+ * one-sided block updates only its one factor, S <- beta2 S + w G^T G (R) or
+ * w G G^T (L), the product split over the long dimension and the partial
+ * products summed in a fixed order.  grads: n_tensors device pointers, read
+ * only; entries of tensors without blocks are ignored (may be NULL).
+ * Errors: SHAMPOO_E_ARG, SHAMPOO_E_STATE, SHAMPOO_E_HIP. */
 int shampoo_update_stats(shampoo_t* h, const float* const* grads, void* stream);
 
 /* Inverse roots (cue 10, 12, 14): for every factor S, lambda_max by Lanczos,
- * eps = eps_rel * lambda_max, then P = (S + eps I)^(-1/p) by coupled Newton
+ * eps = eps_rel * lambda_max, then P = (S + eps I)^(-1/p) (p = root_p, or
+ * root_p / 2 for the factor of a one-sided block) by coupled Newton
  * iteration (newton_iters steps; fp32, fp64 or routed per root_mode).  A
  * factor with non-finite S or a non-finite result keeps its previous root; a
  * factor with lambda_max <= 0 gets P = I.  The caller decides the cadence
@@ -224,8 +238,9 @@ int shampoo_roots_async_end(shampoo_t* h, void* stream);
 /* Preconditioned multiply and update (cue 10): for every block
  * D_b = P_L G_b P_R; a <- a + G*G; A = G / (sqrt(a) + graft_eps);
  * U_b = D_b ||A_b||_F / ||D_b||_F (0 when ||D_b|| = 0);
- * mom <- beta1 mom + U; W <- W - lr mom.  Tensors above max_precond_dim take
- * U = A.  Sparse tables: for each listed row r, a_r += g_r^2 and
+ * mom <- beta1 mom + U; W <- W - lr mom.  A one-sided block takes D = G P (R)
+ * or P G (L) and grafts over the whole tensor; other tensors above
+ * max_precond_dim take U = A.  Sparse tables: for each listed row r, a_r += g_r^2 and
  * W_r -= lr g_r / (sqrt(a_r) + graft_eps); other rows untouched; no momentum.
  * params: n_tensors device pointers, updated in place.  grads: as in
  * shampoo_update_stats (dense tensors must be non-NULL).  sparse: NULL when
@@ -256,7 +271,8 @@ enum {
 int shampoo_step(shampoo_t* h, float* const* params, const float* const* grads,
                  const shampoo_sparse_rows* sparse, int32_t roots, void* stream);
 
-/* Number of factors (2 per block) and blocks in the plan.  Host only. */
+/* Number of factors (2 per Lemma-2 block, 1 per one-sided block) and blocks
+ * in the plan.  Host only. */
 int shampoo_num_factors(const shampoo_t* h, int32_t* n_factors, int32_t* n_blocks);
 
 /* Copy up to `cap` factor records from the last root pass into host memory

@@ -30,6 +30,8 @@ constexpr int kFactorPad = 32;        // factor matrices padded to a multiple of
 constexpr int64_t kElemChunk = 16384; // elements per workgroup in elementwise kernels
 constexpr int kRingSlots = 16;        // pinned staging slots for per-call tables
 constexpr size_t kNewtonScratchBudget = size_t(4) << 30;  // bytes per precision
+constexpr int kSplitKTiles = 1024;    // one-sided statistics: target tiles per launch
+constexpr int kSplitKMin = 256;       // and shortest chunk of the long dimension
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -40,12 +42,14 @@ struct TensorPlan {
     int mode = 0;  // 0 Shampoo, 1 dense Adagrad, 2 sparse rows
     int64_t off_a = -1, off_mom = -1, off_d = -1;  // bytes
     bool fused = false;  // Shampoo tensor whose blocks are all <= 128: update inside the apply kernel
+    int os_side = -1;    // one-sided (Lemma 1): 0 L (G G^T, D = P G), 1 R (G^T G, D = G P)
     int first_block = 0, n_blocks = 0, nbc = 0;
 };
 
 struct BlockPlan {
     int tensor, r0, c0, mb, nb;
-    int fl, fr;
+    int fl, fr;          // factor ids; a one-sided block has one factor (fl == fr)
+    bool one_sided;      // the whole tensor, preconditioned on one side (Lemma 1)
     bool small;          // at most 128 x 128: fused statistics and apply kernels
     int64_t off_t;       // bytes: scratch T = G_b P_R (mb x nb)
     int d_slot, d_tiles; // ||D||^2 partial slots
@@ -54,6 +58,7 @@ struct BlockPlan {
 
 struct FactorPlan {
     int block, side, dim, ld;
+    int p = 4;                      // root exponent: P = (S + eps I)^(-1/p)
     int64_t off_s, off_p, off_p64;  // bytes (off_p64 = -1 when absent)
 };
 
@@ -64,6 +69,7 @@ struct LaunchRef {
 
 struct NewtonChunk {
     int ld = 0;
+    int p = 4;                               // root exponent of its factors
     int njobs = 0;
     bool fused = false;                      // fp32, ld <= 128: one kernel, no scratch
     int64_t jobs_off = 0;                    // FactorJob table (bytes)
@@ -94,12 +100,13 @@ struct Blob {
 enum ProfCat : int {
     PC_STATS = 0, PC_LANCZOS_S, PC_LANCZOS_P, PC_NEWTON_INIT, PC_NEWTON_GEMM32, PC_NEWTON_GEMM64,
     PC_NEWTON_COMMIT, PC_ADAGRAD, PC_APPLY_T, PC_APPLY_D, PC_SCALE, PC_UPDATE, PC_SPARSE,
-    PC_NEWTON_FUSED, PC_APPLY_FUSED, PC_STEP_FUSED, PC_COUNT
+    PC_NEWTON_FUSED, PC_APPLY_FUSED, PC_STEP_FUSED, PC_STATS_SPLITK, PC_COUNT
 };
 const char* const kProfNames[PC_COUNT] = {
     "stats_gram_f64", "lanczos_stats", "lanczos_roots", "newton_init", "newton_gemm_f32",
     "newton_gemm_f64", "newton_commit", "adagrad_norm", "apply_gemm_t", "apply_gemm_d",
-    "block_scale", "update", "sparse_rows", "newton_fused_f32", "apply_fused", "step_fused"};
+    "block_scale", "update", "sparse_rows", "newton_fused_f32", "apply_fused", "step_fused",
+    "stats_onesided"};
 
 struct ProfRec {
     int cat;
@@ -124,6 +131,9 @@ struct shampoo_s {
     Blob blob;  // static tables (offsets relative to off_tables)
 
     LaunchRef gram, apply1, apply2;   // blocks with a side > 128
+    LaunchRef splitk;                 // one-sided statistics: partial products
+    int64_t symred_jobs_off = 0, symred_tiles_off = 0;
+    int n_symred_tiles = 0;           // and their fixed-order sum
     int64_t apply128_off = 0;
     int n_apply128 = 0;               // blocks of at most 128 x 128
     int64_t step128_off = 0;          // the same blocks for the fused step kernel
@@ -209,8 +219,8 @@ LaunchRef add_launch(Blob& blob, const std::vector<GemmTask>& tasks) {
 
 // Builds the per-parity GEMM launches of one Newton chunk.
 void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& fids, int ld,
-                        bool fp64, bool fused, int64_t scratch_off_bytes) {
-    const int p = h->cfg.root_p;
+                        bool fp64, bool fused, int64_t scratch_off_bytes, int p) {
+    ch.p = p;
     const int64_t esz = fp64 ? 8 : 4;
     const int64_t mat = (int64_t)ld * ld;
     const int64_t sbase = scratch_off_bytes / esz;  // scratch start in elements (arena base 0)
@@ -299,7 +309,15 @@ int build_plan(shampoo_s* h) {
         const bool shampoo = c.max_precond_dim <= 0 ||
                              (tp.rows <= c.max_precond_dim && tp.cols <= c.max_precond_dim);
         tp.mode = shampoo ? 0 : 1;
-        if (!shampoo) continue;
+        if (!shampoo) {
+            // Lemma 1: precondition the side that fits, the other not at all
+            if (c.large_layer == 1) {
+                if (tp.cols <= c.max_precond_dim) tp.os_side = 1;
+                else if (tp.rows <= c.max_precond_dim) tp.os_side = 0;
+            }
+            if (tp.os_side >= 0) tp.mode = 0;
+            continue;
+        }
         tp.first_block = (int)h->blocks.size();
         tp.nbc = ceil_div(tp.cols, b);
         for (int64_t r0 = 0; r0 < tp.rows; r0 += b)
@@ -319,14 +337,35 @@ int build_plan(shampoo_s* h) {
         tp.fused = true;
         for (int k = tp.first_block; k < (int)h->blocks.size(); ++k) tp.fused = tp.fused && h->blocks[k].small;
     }
+    // one-sided tensors: one block each, numbered after every Shampoo block
+    const int n_regular = (int)h->blocks.size();
+    for (int t = 0; t < h->n; ++t) {
+        TensorPlan& tp = h->tensors[t];
+        if (tp.os_side < 0) continue;
+        BlockPlan bp{};
+        bp.tensor = t;
+        bp.r0 = bp.c0 = 0;
+        bp.mb = (int)tp.rows;
+        bp.nb = (int)tp.cols;
+        bp.fl = bp.fr = 2 * n_regular + ((int)h->blocks.size() - n_regular);
+        bp.one_sided = true;
+        bp.small = false;
+        tp.first_block = (int)h->blocks.size();
+        tp.n_blocks = 1;
+        tp.nbc = 1;
+        h->blocks.push_back(bp);
+    }
     for (size_t i = 0; i < h->blocks.size(); ++i) {
         const BlockPlan& bp = h->blocks[i];
         for (int side = 0; side < 2; ++side) {
+            const int os = h->tensors[bp.tensor].os_side;
+            if (bp.one_sided && side != os) continue;
             FactorPlan f{};
             f.block = (int)i;
             f.side = side;
             f.dim = side == 0 ? bp.mb : bp.nb;
             f.ld = (int)align_up(f.dim, kFactorPad);
+            f.p = bp.one_sided ? c.root_p / 2 : c.root_p;
             f.off_p64 = -1;
             h->factors.push_back(f);
         }
@@ -351,7 +390,24 @@ int build_plan(shampoo_s* h) {
         if (tp.mode != 2) tp.off_mom = take(numel * 4);
         if (tp.mode == 0 && !tp.fused) tp.off_d = take(numel * 4);
     }
-    for (auto& bp : h->blocks) bp.off_t = bp.small ? -1 : take((int64_t)bp.mb * bp.nb * 4);
+    for (auto& bp : h->blocks)
+        bp.off_t = (bp.small || bp.one_sided) ? -1 : take((int64_t)bp.mb * bp.nb * 4);
+    // one-sided statistics: the product over the long dimension is split into
+    // chunks (enough 128 x 128 tiles to fill the GPU); one fp64 partial per chunk
+    std::vector<int> splitk_chunks(h->blocks.size(), 0), splitk_len(h->blocks.size(), 0);
+    std::vector<int64_t> splitk_at(h->blocks.size(), -1);
+    for (size_t i = 0; i < h->blocks.size(); ++i) {
+        const BlockPlan& bp = h->blocks[i];
+        if (!bp.one_sided) continue;
+        const FactorPlan& f = h->factors[bp.fl];
+        const int64_t K = f.side == 1 ? bp.mb : bp.nb;       // the long dimension
+        const int ut = ceil_div(f.dim, kTile) * (ceil_div(f.dim, kTile) + 1) / 2;
+        const int want = std::max(1, ceil_div(kSplitKTiles, ut));
+        const int64_t len = align_up(std::max<int64_t>(ceil_div(K, want), kSplitKMin), 32);
+        splitk_len[i] = (int)std::min<int64_t>(len, K);
+        splitk_chunks[i] = ceil_div(K, splitk_len[i]);
+        splitk_at[i] = take((int64_t)splitk_chunks[i] * f.ld * f.ld * 8);
+    }
 
     // norm partial slots
     int na = 0, nd = 0;
@@ -371,12 +427,12 @@ int build_plan(shampoo_s* h) {
     h->off_scale = take((int64_t)std::max(nb, 1) * 4);
 
     // Newton root classes (by padded dimension) and scratch chunks
-    std::vector<int> lds;
-    for (auto& f : h->factors) lds.push_back(f.ld);
+    std::vector<std::pair<int, int>> lds;   // (ld, p) classes
+    for (auto& f : h->factors) lds.push_back({f.ld, f.p});
     std::sort(lds.begin(), lds.end());
     lds.erase(std::unique(lds.begin(), lds.end()), lds.end());
     int64_t scr32 = 0, scr64 = 0;
-    struct Pending { int set; int ld; std::vector<int> fids; bool fp64; bool fused; };
+    struct Pending { int set; int ld; int p; std::vector<int> fids; bool fp64; bool fused; };
     std::vector<Pending> pend;
     // sets: 0 every factor; 1..P the parts of a staggered pass; P+1..2P the
     // same parts reading a snapshot of their statistics and writing staged
@@ -389,16 +445,16 @@ int build_plan(shampoo_s* h) {
         return set == 0 || h->factors[i].block % nparts == part_of(set);
     };
     for (int set = 0; set <= 2 * nparts; ++set)
-    for (int ld : lds) {
+    for (auto [ld, pe] : lds) {
         std::vector<int> fids;
         for (int i = 0; i < nf; ++i)
-            if (h->factors[i].ld == ld && in_set(set, i)) fids.push_back(i);
+            if (h->factors[i].ld == ld && h->factors[i].p == pe && in_set(set, i)) fids.push_back(i);
         if (fids.empty()) continue;
         for (int prec = 0; prec < 2; ++prec) {
             const bool fp64 = prec == 1;
             if ((fp64 && !use_fp64(c)) || (!fp64 && !use_fp32(c))) continue;
             if (!fp64 && ld <= 128) {   // fused LDS-resident kernel, no scratch
-                pend.push_back(Pending{set, ld, fids, false, true});
+                pend.push_back(Pending{set, ld, pe, fids, false, true});
                 continue;
             }
             const int64_t per = 6 * (int64_t)ld * ld * (fp64 ? 8 : 4);
@@ -407,6 +463,7 @@ int build_plan(shampoo_s* h) {
                 Pending pd;
                 pd.set = set;
                 pd.ld = ld;
+                pd.p = pe;
                 pd.fp64 = fp64;
                 pd.fused = false;
                 pd.fids.assign(fids.begin() + s, fids.begin() + std::min(fids.size(), s + cap));
@@ -454,10 +511,50 @@ int build_plan(shampoo_s* h) {
     {
         std::vector<GemmTask> tasks;
         std::vector<GramJob> small;
-        for (auto& bp : h->blocks) {
+        std::vector<GemmTask> sk;
+        std::vector<SymReduceJob> red;
+        std::vector<TileRef> red_tiles;
+        for (size_t bi = 0; bi < h->blocks.size(); ++bi) {
+            const BlockPlan& bp = h->blocks[bi];
             const TensorPlan& tp = h->tensors[bp.tensor];
             const FactorPlan& fl = h->factors[bp.fl];
             const FactorPlan& fr = h->factors[bp.fr];
+            if (bp.one_sided) {
+                // partial c: S_c = G_c^T G_c (R; G_c rows [c len, (c+1) len)) or
+                // G_c G_c^T (L; G_c those columns), upper 128 x 128 tiles
+                const FactorPlan& f = fl;
+                const int len = splitk_len[bi];
+                const int64_t K = f.side == 1 ? bp.mb : bp.nb;
+                for (int ck = 0; ck < splitk_chunks[bi]; ++ck) {
+                    GemmTask t{};
+                    const int64_t k0 = (int64_t)ck * len;
+                    t.a_base = t.b_base = 1 + bp.tensor;
+                    t.a_off = t.b_off = f.side == 1 ? k0 * tp.cols : k0;
+                    t.lda = t.ldb = (int)tp.cols;
+                    t.c_base = 0;
+                    t.c_off = splitk_at[bi] / 8 + (int64_t)ck * f.ld * f.ld;
+                    t.ldc = f.ld;
+                    t.M = t.N = f.dim;
+                    t.K = (int)std::min<int64_t>(len, K - k0);
+                    t.trans = (f.side == 1 ? 1 : 2) | 16;
+                    t.tiles_n = ceil_div(t.N, kTile);
+                    t.factor = -1;
+                    t.norm_slot = -1;
+                    sk.push_back(t);
+                }
+                SymReduceJob r{};
+                r.part_off = splitk_at[bi] / 8;
+                r.s_off = f.off_s / 8;
+                r.nparts = splitk_chunks[bi];
+                r.dim = f.dim;
+                r.ld = f.ld;
+                r.tiles = ceil_div(f.dim, 32);
+                for (int a = 0; a < r.tiles; ++a)
+                    for (int b2 = a; b2 < r.tiles; ++b2)
+                        red_tiles.push_back({(int32_t)red.size(), a * r.tiles + b2});
+                red.push_back(r);
+                continue;
+            }
             if (bp.mb <= 128 && bp.nb <= 128) {
                 GramJob j{};
                 j.g_base = 1 + bp.tensor;
@@ -499,6 +596,10 @@ int build_plan(shampoo_s* h) {
         h->gram = add_launch(blob, tasks);
         h->n_gram128 = (int)small.size();
         h->gram128_off = blob.add(small);
+        h->splitk = add_launch(blob, sk);
+        h->symred_jobs_off = blob.add(red);
+        h->symred_tiles_off = blob.add(red_tiles);
+        h->n_symred_tiles = (int)red_tiles.size();
     }
     // apply: T = G_b P_R, then D = P_L T with ||D||^2 partials (cue 10)
     {
@@ -509,6 +610,27 @@ int build_plan(shampoo_s* h) {
             const TensorPlan& tp = h->tensors[bp.tensor];
             const FactorPlan& fl = h->factors[bp.fl];
             const FactorPlan& fr = h->factors[bp.fr];
+            if (bp.one_sided) {
+                // D = G P (R) or P G (L), with ||D||^2 partials per tile
+                GemmTask u{};
+                if (fl.side == 1) {
+                    u.a_base = 1 + bp.tensor; u.a_off = 0; u.lda = (int)tp.cols;
+                    u.b_base = 0; u.b_off = fl.off_p / 4; u.ldb = fl.ld;
+                    u.K = bp.nb;
+                } else {
+                    u.a_base = 0; u.a_off = fl.off_p / 4; u.lda = fl.ld;
+                    u.b_base = 1 + bp.tensor; u.b_off = 0; u.ldb = (int)tp.cols;
+                    u.K = bp.mb;
+                }
+                u.c_base = 0; u.c_off = tp.off_d / 4; u.ldc = (int)tp.cols;
+                u.M = bp.mb; u.N = bp.nb;
+                u.trans = 0;
+                u.tiles_n = ceil_div(u.N, kTile);
+                u.factor = -1;
+                u.norm_slot = bp.d_slot;
+                t2.push_back(u);
+                continue;
+            }
             if (bp.small) {
                 ApplyJob j{};
                 const int64_t o = (int64_t)bp.r0 * tp.cols + bp.c0;
@@ -576,8 +698,8 @@ int build_plan(shampoo_s* h) {
         std::vector<FactorJob> ident;
         for (int i = 0; i < nf; ++i) {
             const FactorPlan& f = h->factors[i];
-            js.push_back({f.off_s / 8, f.dim, f.ld, i, 0});
-            jp.push_back({f.off_p / 4, f.dim, f.ld, i, 0});
+            js.push_back({f.off_s / 8, f.dim, f.ld, i, f.p});
+            jp.push_back({f.off_p / 4, f.dim, f.ld, i, f.p});
             FactorJob j{};
             j.p_off = f.off_p / 4;
             j.p64_off = f.off_p64 >= 0 ? f.off_p64 / 8 : -1;
@@ -626,7 +748,7 @@ int build_plan(shampoo_s* h) {
                 h->factors[i].off_p = stage_at[i];
             }
         build_newton_chunk(h, ch, pd.fids, pd.ld, pd.fp64, pd.fused,
-                           pd.fp64 ? h->off_scr64 : h->off_scr32);
+                           pd.fp64 ? h->off_scr64 : h->off_scr32, pd.p);
         if (async)
             for (size_t k = 0; k < pd.fids.size(); ++k) {
                 h->factors[pd.fids[k]].off_s = saved[k].first;
@@ -694,7 +816,7 @@ int build_plan(shampoo_s* h) {
                 q.row0 = (int)r0;
                 q.nrows = (int)std::min<int64_t>(rows_per, tp.rows - r0);
                 q.cols = (int)tp.cols;
-                q.block_size = b;
+                q.block_size = tp.os_side >= 0 ? (1 << 30) : b;  // one-sided: one block
                 q.first_block = tp.first_block;
                 q.nbc = tp.nbc;
                 q.a_off = tp.off_a / 4;
@@ -807,11 +929,13 @@ int shampoo_create(const shampoo_config* cfg, int32_t n_tensors, const shampoo_t
     if (c.root_mode < SHAMPOO_ROOT_F32 || c.root_mode > SHAMPOO_ROOT_AUTO) return SHAMPOO_E_ARG;
     if (c.root_p != 1 && c.root_p != 2 && c.root_p != 4 && c.root_p != 8)
         return SHAMPOO_E_UNSUPPORTED;
+    if (c.large_layer != 0 && c.large_layer != 1) return SHAMPOO_E_ARG;
+    if (c.large_layer == 1 && c.root_p % 2) return SHAMPOO_E_UNSUPPORTED;  // exponent -2/root_p
     for (int t = 0; t < n_tensors; ++t) {
         const shampoo_tensor_desc& d = tensors[t];
         if (d.rows < 1 || d.cols < 1 || d.reserved != 0) return SHAMPOO_E_ARG;
         if (d.kind != SHAMPOO_DENSE && d.kind != SHAMPOO_SPARSE_ROWS) return SHAMPOO_E_ARG;
-        if (d.rows > (int64_t)1 << 31 || d.cols > (int64_t)1 << 20) return SHAMPOO_E_UNSUPPORTED;
+        if (d.rows > INT32_MAX || d.cols > (int64_t)1 << 20) return SHAMPOO_E_UNSUPPORTED;
     }
     shampoo_s* h = new (std::nothrow) shampoo_s();
     if (!h) return SHAMPOO_E_NOMEM;
@@ -864,6 +988,7 @@ int shampoo_block_info(const shampoo_t* h, int32_t block, shampoo_block_layout* 
     const FactorPlan& fl = h->factors[bp.fl];
     const FactorPlan& fr = h->factors[bp.fr];
     out->tensor = bp.tensor;
+    out->one_sided = bp.one_sided ? 1 : 0;
     out->row0 = bp.r0;
     out->col0 = bp.c0;
     out->rows = bp.mb;
@@ -878,6 +1003,14 @@ int shampoo_block_info(const shampoo_t* h, int32_t block, shampoo_block_layout* 
     out->off_pr = fr.off_p;
     out->off_pl64 = fl.off_p64;
     out->off_pr64 = fr.off_p64;
+    if (bp.one_sided) {   // only the side that was kept
+        const bool r = fl.side == 1;
+        (r ? out->ld_l : out->ld_r) = 0;
+        (r ? out->factor_l : out->factor_r) = -1;
+        (r ? out->off_l : out->off_r) = -1;
+        (r ? out->off_pl : out->off_pr) = -1;
+        (r ? out->off_pl64 : out->off_pr64) = -1;
+    }
     return SHAMPOO_OK;
 }
 
@@ -971,16 +1104,35 @@ int enqueue_stats(shampoo_s* h, hipStream_t s, bool skip_small) {
     // fp32 gradients, fp64 products and statistics (exact products; the
     // statistics keep the near-null spectrum that fp32 storage would round
     // into the eps damping)
-    ProfScope ps(h, PC_STATS, s, h->gram.ntiles > 0 || (!skip_small && h->n_gram128 > 0));
-    if (!skip_small) {
-        const int rc2 = hip_err(launch_gram128(tab<GramJob>(h, h->gram128_off), h->n_gram128,
-                                               at<uint64_t>(h, h->off_bases), at<double>(h, 0),
-                                               a.alpha, a.beta, s));
-        if (rc2) return rc2;
+    {
+        ProfScope ps(h, PC_STATS, s, h->gram.ntiles > 0 || (!skip_small && h->n_gram128 > 0));
+        if (!skip_small) {
+            const int rc2 = hip_err(launch_gram128(tab<GramJob>(h, h->gram128_off), h->n_gram128,
+                                                   at<uint64_t>(h, h->off_bases), at<double>(h, 0),
+                                                   a.alpha, a.beta, s));
+            if (rc2) return rc2;
+        }
+        const int rc = hip_err(launch_gemm_f64_from_f32(tab<GemmTask>(h, h->gram.tasks_off),
+                                                        tab<TileRef>(h, h->gram.tiles_off),
+                                                        h->gram.ntiles, at<uint64_t>(h, h->off_bases),
+                                                        a, s));
+        if (rc) return rc;
     }
-    return hip_err(launch_gemm_f64_from_f32(tab<GemmTask>(h, h->gram.tasks_off),
-                                            tab<TileRef>(h, h->gram.tiles_off), h->gram.ntiles,
-                                            at<uint64_t>(h, h->off_bases), a, s));
+    if (h->n_symred_tiles == 0) return SHAMPOO_OK;
+    // one-sided statistics (Lemma 1): split-K partial products, then their
+    // fixed-order sum into S = beta2 S + w sum_c part_c
+    ProfScope ps(h, PC_STATS_SPLITK, s);
+    GemmArgs pa{};
+    pa.epi = EPI_STORE;
+    pa.alpha = 1.0;
+    pa.beta = 0.0;
+    int rc = hip_err(launch_gemm_f64_from_f32(tab<GemmTask>(h, h->splitk.tasks_off),
+                                              tab<TileRef>(h, h->splitk.tiles_off), h->splitk.ntiles,
+                                              at<uint64_t>(h, h->off_bases), pa, s));
+    if (rc) return rc;
+    return hip_err(launch_sym_reduce(tab<SymReduceJob>(h, h->symred_jobs_off),
+                                     tab<TileRef>(h, h->symred_tiles_off), h->n_symred_tiles,
+                                     at<double>(h, 0), a.alpha, a.beta, s));
 }
 
 int check_stats_args(const shampoo_s* h, const float* const* grads) {
@@ -1021,9 +1173,7 @@ int shampoo_update_stats(shampoo_t* h, const float* const* grads, void* stream) 
 namespace {
 int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const int32_t* gate,
                int gate_val, int32_t* prec, hipStream_t s) {
-    const int p = h->cfg.root_p;
     NewtonArgs na{};
-    na.p = p;
     na.is_fp64 = fp64 ? 1 : 0;
     na.gate = gate;
     na.gate_val = gate_val;
@@ -1033,12 +1183,14 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
     g.epi = EPI_STORE;
     g.alpha = 1.0;
     g.beta = 0.0;
-    g.xc1 = (double)(p + 1) / p;
-    g.xc2 = -1.0 / p;
     g.gate = gate;
     g.gate_val = gate_val;
     const uint64_t* bases = at<uint64_t>(h, h->off_bases);
     for (auto& ch : chunks) {
+        const int p = ch.p;
+        na.p = p;
+        g.xc1 = (double)(p + 1) / p;
+        g.xc2 = -1.0 / p;
         const FactorJob* jobs = tab<FactorJob>(h, ch.jobs_off);
         int rc;
         if (ch.fused) {
@@ -1100,7 +1252,6 @@ int enqueue_roots(shampoo_s* h, RootTables& rt, hipStream_t s) {
     LanczosArgs la{};
     la.steps = c.lanczos_steps > 0 ? c.lanczos_steps : 24;
     la.mode = 0;
-    la.p = c.root_p;
     la.eps_rel = c.eps_rel;
     la.threshold = c.fp64_cond_threshold;
     la.diag = diag;

@@ -66,6 +66,18 @@ struct CopyJob {
     int64_t src, dst, bytes;
 };
 
+// Sum of the split-K partial products of one large statistic (one-sided
+// preconditioning): S <- beta S + alpha sum_c part_c, over the upper
+// triangle, written to both triangles.  part_c holds the upper 128 x 128
+// tiles of chunk c's product (leading dim ld, ld * ld doubles apart).
+struct SymReduceJob {
+    int64_t part_off;   // first partial (arena elements of 8 bytes)
+    int64_t s_off;      // statistic (arena elements of 8 bytes)
+    int32_t nparts;     // number of partials
+    int32_t dim, ld;
+    int32_t tiles;      // 32 x 32 tiles per side: ceil(dim / 32)
+};
+
 // A tile of the batched GEMM launch: which task and which 128x128 tile.
 struct TileRef {
     int32_t task;
@@ -78,7 +90,7 @@ struct LanczosJob {
     int32_t n;        // real dimension
     int32_t ld;       // leading dimension
     int32_t factor;   // factor id (diagnostics record)
-    int32_t pad_;
+    int32_t p;        // root exponent of the factor (mode 1: kappa of S from that of P)
 };
 
 // Per-factor job of the Newton init / commit kernels.

@@ -17,6 +17,8 @@
 //   k_lanczos        Krylov extreme-eigenvalue estimate per symmetric matrix.
 //   k_newton_init<T> / k_newton_commit<T>  start and finish of the batched
 //                    coupled-Newton iteration.
+//   k_sym_reduce     fixed-order sum of split-K partial statistics (one-sided
+//                    preconditioning of a large layer) into S, both triangles.
 //   k_adagrad_norm   a <- a + G*G on Shampoo blocks and ||A_b||^2 partials.
 //   k_block_scale    graft factor ||A_b|| / ||D_b|| per block.
 //   k_update         momentum and weight update (and dense Adagrad fallback).
@@ -683,7 +685,7 @@ __device__ __forceinline__ void lanczos_finish(const LanczosArgs& args, const La
         // routed to fp64 as well.
         const int bad_in = dg.status & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_ZERO_);
         double kap = 0.0;
-        if (!bad_in && finite && lmax > 0.0) kap = (dg.lambda_max + dg.eps) * pow(lmax, (double)args.p);
+        if (!bad_in && finite && lmax > 0.0) kap = (dg.lambda_max + dg.eps) * pow(lmax, (double)jb.p);
         dg.kappa_est = kap;
         if (args.prec && args.auto_route) {
             const bool weak = (dg.status & (SHAMPOO_FACTOR_NONFINITE_ROOT_ | SHAMPOO_FACTOR_RESIDUAL_HIGH_)) != 0;
@@ -1721,6 +1723,73 @@ __global__ __launch_bounds__(256) void k_copy_jobs(const CopyJob* __restrict__ j
     }
 }
 
+// ====================================== one-sided statistics: split-K sum
+// S <- beta S + alpha sum_c part_c on one 32 x 32 tile pair (bi <= bj) of a
+// statistic whose product was split over the long dimension.  The partials
+// are added in chunk order (fixed, so the result does not depend on the
+// launch); the tile is written at (bi, bj) and its transpose at (bj, bi),
+// and on a diagonal tile the lower half is the transpose of the upper half,
+// so S stays exactly symmetric.  Partials and S beyond dim are not touched
+// (the batched GEMM writes only i, j < dim of the upper 128 x 128 tiles,
+// which contain every 32 x 32 pair bi <= bj).
+__global__ __launch_bounds__(256) void k_sym_reduce(const SymReduceJob* __restrict__ jobs,
+                                                   const TileRef* __restrict__ tiles,
+                                                   double* __restrict__ arena, double alpha,
+                                                   double beta) {
+    __shared__ double T[32][33];
+    const TileRef tr = tiles[blockIdx.x];
+    const SymReduceJob jb = jobs[tr.task];
+    const int bi = tr.tile / jb.tiles, bj = tr.tile % jb.tiles;
+    const int r = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 4;
+    const int i = bi * 32 + r, j0 = bj * 32 + c0;
+    const int64_t mat = (int64_t)jb.ld * jb.ld;
+    double* S = arena + jb.s_off;
+    const double* P = arena + jb.part_off + (int64_t)i * jb.ld + j0;
+    // ld is a multiple of 32, so the 4 columns are in the row (possibly padding)
+    double2 v0 = make_double2(0.0, 0.0), v1 = make_double2(0.0, 0.0);
+    if (i < jb.dim) {
+        int c = 0;
+        for (; c + 2 <= jb.nparts; c += 2) {
+            const double2 a0 = *reinterpret_cast<const double2*>(P + c * mat);
+            const double2 a1 = *reinterpret_cast<const double2*>(P + c * mat + 2);
+            const double2 b0 = *reinterpret_cast<const double2*>(P + (c + 1) * mat);
+            const double2 b1 = *reinterpret_cast<const double2*>(P + (c + 1) * mat + 2);
+            v0.x += a0.x; v0.y += a0.y; v1.x += a1.x; v1.y += a1.y;
+            v0.x += b0.x; v0.y += b0.y; v1.x += b1.x; v1.y += b1.y;
+        }
+        if (c < jb.nparts) {
+            const double2 a0 = *reinterpret_cast<const double2*>(P + c * mat);
+            const double2 a1 = *reinterpret_cast<const double2*>(P + c * mat + 2);
+            v0.x += a0.x; v0.y += a0.y; v1.x += a1.x; v1.y += a1.y;
+        }
+        const double* So = S + (int64_t)i * jb.ld + j0;
+        const double2 s0 = *reinterpret_cast<const double2*>(So);
+        const double2 s1 = *reinterpret_cast<const double2*>(So + 2);
+        v0.x = beta * s0.x + alpha * v0.x; v0.y = beta * s0.y + alpha * v0.y;
+        v1.x = beta * s1.x + alpha * v1.x; v1.y = beta * s1.y + alpha * v1.y;
+    }
+    T[r][c0] = v0.x; T[r][c0 + 1] = v0.y; T[r][c0 + 2] = v1.x; T[r][c0 + 3] = v1.y;
+    __syncthreads();
+    // every read of S above (this tile and, for bi < bj, none of the mirror
+    // tile) is done before the writes below
+    if (bi == bj) {
+        if (i < jb.dim)
+            for (int e = 0; e < 4; ++e) {
+                const int c = c0 + e;
+                if (j0 + e < jb.dim) S[(int64_t)i * jb.ld + j0 + e] = r <= c ? T[r][c] : T[c][r];
+            }
+        return;
+    }
+    if (i < jb.dim)
+        for (int e = 0; e < 4; ++e)
+            if (j0 + e < jb.dim) S[(int64_t)i * jb.ld + j0 + e] = T[r][c0 + e];
+    // transpose: row bj*32 + r, columns bi*32 + c0 .. + 3
+    const int it = bj * 32 + r, jt = bi * 32 + c0;
+    if (it < jb.dim)
+        for (int e = 0; e < 4; ++e)
+            if (jt + e < jb.dim) S[(int64_t)it * jb.ld + jt + e] = T[c0 + e][r];
+}
+
 // Identity roots for every factor (state initialisation).
 __global__ __launch_bounds__(256) void k_set_identity(const FactorJob* __restrict__ jobs,
                                                      float* __restrict__ arena) {
@@ -2008,6 +2077,12 @@ hipError_t launch_apply128(const ApplyJob* jobs, int njobs, const uint64_t* base
 hipError_t launch_copy_jobs(const CopyJob* jobs, int njobs, unsigned char* arena, hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_copy_jobs, dim3(njobs), dim3(256), 0, s, jobs, arena);
+    return hipGetLastError();
+}
+hipError_t launch_sym_reduce(const SymReduceJob* jobs, const TileRef* tiles, int ntiles,
+                             double* arena, double alpha, double beta, hipStream_t s) {
+    if (ntiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_sym_reduce, dim3(ntiles), dim3(256), 0, s, jobs, tiles, arena, alpha, beta);
     return hipGetLastError();
 }
 hipError_t launch_set_identity(const FactorJob* jobs, int njobs, float* arena, hipStream_t s) {

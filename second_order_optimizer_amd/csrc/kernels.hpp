@@ -30,7 +30,6 @@ struct GemmArgs {
 struct LanczosArgs {
     int steps;
     int mode;             // 0: statistics (lambda_max, eps), 1: roots (kappa estimate)
-    int p;
     int auto_route;       // mode 1: set prec flags from the kappa estimate
     int route_all_fp64;   // mode 0: initial prec flag value
     double eps_rel;
@@ -82,6 +81,8 @@ hipError_t launch_apply128(const ApplyJob* jobs, int njobs, const uint64_t* base
                            float delta, double* partA, double* partD, const UpdateArgs& ua,
                            hipStream_t s);
 hipError_t launch_copy_jobs(const CopyJob* jobs, int njobs, unsigned char* arena, hipStream_t s);
+hipError_t launch_sym_reduce(const SymReduceJob* jobs, const TileRef* tiles, int ntiles,
+                             double* arena, double alpha, double beta, hipStream_t s);
 hipError_t launch_set_identity(const FactorJob* jobs, int njobs, float* arena, hipStream_t s);
 hipError_t launch_adagrad_norm(const BlockChunk* chunks, int nchunks, const uint64_t* bases,
                                float* arena, float delta, double* partA, hipStream_t s);

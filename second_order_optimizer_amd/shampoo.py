@@ -55,7 +55,8 @@ class BlockLayout(ctypes.Structure):
     _fields_ = [("tensor", ctypes.c_int32), ("row0", ctypes.c_int32), ("col0", ctypes.c_int32),
                 ("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("ld_l", ctypes.c_int32),
                 ("ld_r", ctypes.c_int32), ("factor_l", ctypes.c_int32),
-                ("factor_r", ctypes.c_int32), ("off_l", ctypes.c_int64),
+                ("factor_r", ctypes.c_int32), ("one_sided", ctypes.c_int32),
+                ("off_l", ctypes.c_int64),
                 ("off_r", ctypes.c_int64), ("off_pl", ctypes.c_int64), ("off_pr", ctypes.c_int64),
                 ("off_pl64", ctypes.c_int64), ("off_pr64", ctypes.c_int64)]
 
@@ -334,29 +335,35 @@ class Shampoo(Plan):
             n *= s
         return self.state[off: off + n * es].view(dtype).view(*shape)
 
+    def _sq(self, off: int, ld: int, n: int, dtype):
+        # the n x n leading part of a padded square matrix, None when absent
+        if off < 0:
+            return None
+        return self._view(off, (ld, ld), dtype)[:n, :n]
+
     def stats(self, b: int, raw: bool = False):
-        """L, R of block b.  The library maintains only the upper triangle of
-        each (symmetric) factor; unless raw=True the full matrix is rebuilt
-        from it (a copy)."""
+        """L, R of block b (None for the side a one-sided block does not
+        keep).  The library maintains the upper triangle of each symmetric
+        factor (a one-sided factor also its lower one); unless raw=True the
+        full matrix is rebuilt from the upper triangle (a copy)."""
         bl = self.block(b)
-        L = self._view(bl.off_l, (bl.ld_l, bl.ld_l), self.torch.float64)[: bl.rows, : bl.rows]
-        R = self._view(bl.off_r, (bl.ld_r, bl.ld_r), self.torch.float64)[: bl.cols, : bl.cols]
+        f64 = self.torch.float64
+        L = self._sq(bl.off_l, bl.ld_l, bl.rows, f64)
+        R = self._sq(bl.off_r, bl.ld_r, bl.cols, f64)
         if raw:
             return L, R
-        sym = lambda x: self.torch.triu(x) + self.torch.triu(x, 1).T
+        sym = lambda x: None if x is None else self.torch.triu(x) + self.torch.triu(x, 1).T
         return sym(L), sym(R)
 
     def roots(self, b: int, fp64: bool = False):
         bl = self.block(b)
         if fp64:
-            if bl.off_pl64 < 0:
+            if bl.off_pl64 < 0 and bl.off_pr64 < 0:
                 return None, None
-            PL = self._view(bl.off_pl64, (bl.ld_l, bl.ld_l), self.torch.float64)
-            PR = self._view(bl.off_pr64, (bl.ld_r, bl.ld_r), self.torch.float64)
+            dt, ol, orr = self.torch.float64, bl.off_pl64, bl.off_pr64
         else:
-            PL = self._view(bl.off_pl, (bl.ld_l, bl.ld_l), self.torch.float32)
-            PR = self._view(bl.off_pr, (bl.ld_r, bl.ld_r), self.torch.float32)
-        return PL[: bl.rows, : bl.rows], PR[: bl.cols, : bl.cols]
+            dt, ol, orr = self.torch.float32, bl.off_pl, bl.off_pr
+        return self._sq(ol, bl.ld_l, bl.rows, dt), self._sq(orr, bl.ld_r, bl.cols, dt)
 
     def accumulators(self, t: int):
         a_off, m_off, _, _ = self.tensor(t)

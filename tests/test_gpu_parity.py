@@ -32,13 +32,50 @@ def _np(t):
     return t.detach().cpu().numpy().astype(np.float64)
 
 
+def check_root(run, S, P32, P64, d, p, where, root_tol=ROOT32_TOL, kappa_gate=None, worst=None):
+    """One factor's root, stage-isolated: the oracle's eigh root of the GPU's
+    own S with the GPU's eps (for the fp32 iteration also of S rounded to
+    fp32, the matrix it receives).  fp64-routed factors are held to 1e-8,
+    the rest to `root_tol`; kappa_gate: only factors whose oracle kappa is
+    below it are held to the fp32 bar (F32 mode on ill-conditioned
+    statistics)."""
+    worst = [0.0, 0.0, 0.0] if worst is None else worst
+    Sn = _np(S)
+    # the exact root of the damped matrix the kernel received
+    ref = O.inverse_root(Sn, 0.0, p, eps=d.eps, clamp=False)
+    assert ref.ok, where
+    exact = O.inverse_root(Sn, run.cfg.eps_rel, p)
+    assert abs(d.lambda_max - exact.lam_max) <= 1e-4 * exact.lam_max, where
+    if d.status & FP64:
+        e = rel_fro(_np(P64), ref.P)
+        worst[2] = max(worst[2], e)
+        assert e <= ROOT64_TOL, (where, e, d.status, d.residual)
+        assert rel_fro(_np(P32), ref.P) <= 1e-6
+    else:
+        # the fp32 iteration receives S rounded to fp32 (and fp32 eps)
+        S32 = Sn.astype(np.float32).astype(np.float64)
+        ref32 = O.inverse_root(S32, 0.0, p, eps=float(np.float32(d.eps)), clamp=False)
+        e = rel_fro(_np(P32), ref32.P)
+        e64 = rel_fro(_np(P32), ref.P)
+        if kappa_gate is None or exact.kappa <= kappa_gate:
+            worst[1] = max(worst[1], e, e64)
+            assert e <= root_tol and e64 <= root_tol, (where, e, e64, d.status, d.residual,
+                                                       exact.kappa)
+    if run.cfg.root_mode == 2:
+        # routing: clearly ill-conditioned factors went fp64, clearly
+        # well-conditioned ones stayed fp32 (factor-2 band)
+        thr = run.cfg.fp64_cond_threshold
+        if exact.kappa > 2 * thr:
+            assert d.status & FP64, (where, exact.kappa, d.kappa_est)
+        if exact.kappa < 0.5 * thr:
+            assert not d.status & FP64, (where, exact.kappa, d.kappa_est)
+    return worst
+
+
 def check_blocks(run, orc, k, t, root_tol=ROOT32_TOL, check_roots=True, kappa_gate=None):
-    """Statistics vs the oracle chain; roots stage-isolated.  fp64-routed
-    factors are held to 1e-8 (their fp64 root), the rest to `root_tol`.
-    kappa_gate: only factors whose oracle kappa is below it are held to the
-    fp32 bar (F32 mode on ill-conditioned statistics)."""
-    """check_roots: True/False, or a predicate on the global block index
-    (the blocks whose roots this step recomputed)."""
+    """Statistics of tensor k's blocks vs the oracle chain; roots
+    stage-isolated (check_root).  check_roots: True/False, or a predicate on
+    the global block index (the blocks whose roots this step recomputed)."""
     due = check_roots if callable(check_roots) else (lambda b: bool(check_roots))
     diag = run.opt.diagnostics() if check_roots is not False else None
     worst = [0.0, 0.0, 0.0]
@@ -56,38 +93,34 @@ def check_blocks(run, orc, k, t, root_tol=ROOT32_TOL, check_roots=True, kappa_ga
         P32 = run.opt.roots(b)
         P64 = run.opt.roots(b, fp64=True)
         for side, (S, f) in enumerate(((L, bl.factor_l), (R, bl.factor_r))):
-            d = diag[f]
-            Sn = _np(S)
-            # the exact root of the damped matrix the kernel received
-            ref = O.inverse_root(Sn, 0.0, run.cfg.root_p, eps=d.eps, clamp=False)
-            assert ref.ok, (t, b, f)
-            exact = O.inverse_root(Sn, run.cfg.eps_rel, run.cfg.root_p)
-            assert abs(d.lambda_max - exact.lam_max) <= 1e-4 * exact.lam_max, (t, b, f)
-            if d.status & FP64:
-                e = rel_fro(_np(P64[side]), ref.P)
-                worst[2] = max(worst[2], e)
-                assert e <= ROOT64_TOL, (t, b, f, e, d.status, d.residual)
-                assert rel_fro(_np(P32[side]), ref.P) <= 1e-6
-            else:
-                # the fp32 iteration receives S rounded to fp32 (and fp32 eps)
-                S32 = Sn.astype(np.float32).astype(np.float64)
-                ref32 = O.inverse_root(S32, 0.0, run.cfg.root_p, eps=float(np.float32(d.eps)),
-                                       clamp=False)
-                e = rel_fro(_np(P32[side]), ref32.P)
-                e64 = rel_fro(_np(P32[side]), ref.P)
-                if kappa_gate is not None and exact.kappa > kappa_gate:
-                    continue
-                worst[1] = max(worst[1], e, e64)
-                assert e <= root_tol and e64 <= root_tol, (t, b, f, e, e64, d.status, d.residual,
-                                                           exact.kappa)
-            if run.cfg.root_mode == 2:
-                # routing: clearly ill-conditioned factors went fp64, clearly
-                # well-conditioned ones stayed fp32 (factor-2 band)
-                thr = run.cfg.fp64_cond_threshold
-                if exact.kappa > 2 * thr:
-                    assert d.status & FP64, (t, b, f, exact.kappa, d.kappa_est)
-                if exact.kappa < 0.5 * thr:
-                    assert not d.status & FP64, (t, b, f, exact.kappa, d.kappa_est)
+            check_root(run, S, P32[side], P64[side], diag[f], run.cfg.root_p, (t, b, f),
+                       root_tol, kappa_gate, worst)
+    return worst
+
+
+def check_one_sided(run, orc, k, t, due, root_tol=ROOT32_TOL):
+    """A one-sided tensor (Lemma 1): its one statistic against the oracle's,
+    kept symmetric in both triangles, and, on a root step, its root of
+    exponent 2/root_p stage-isolated."""
+    idx, st = orc.one_sided[k]
+    _, _, fb, nb = run.opt.tensor(k)
+    assert (fb, nb) == (idx, 1)
+    bl = run.opt.block(fb)
+    side = 1 if st.side == "R" else 0
+    assert bl.one_sided == 1 and (bl.factor_r if side else bl.factor_l) >= 0
+    assert (bl.factor_l if side else bl.factor_r) == -1
+    S = run.opt.stats(fb)[side]
+    raw = run.opt.stats(fb, raw=True)[side]
+    assert torch.equal(raw, raw.T), (t, k)
+    e = rel_fro(_np(S), st.S)
+    assert e <= STATS_TOL, (t, k, e)
+    worst = [e, 0.0, 0.0]
+    if due(idx):
+        f = bl.factor_r if side else bl.factor_l
+        d = run.opt.diagnostics()[f]
+        assert (d.block, d.side, d.dim) == (idx, side, st.S.shape[0])
+        check_root(run, S, run.opt.roots(fb)[side], run.opt.roots(fb, fp64=True)[side], d,
+                   run.cfg.root_p // 2, (t, k, f), root_tol, None, worst)
     return worst
 
 
@@ -95,7 +128,7 @@ def run_parity(wl, ids=None, steps=None, root_tol=ROOT32_TOL, kappa_gate=None, *
     ids = list(range(len(wl.tensors))) if ids is None else ids
     run = GpuRun(wl, ids, **over)
     orc = make_oracle(wl, ids, **{k: v for k, v in over.items()
-                                  if k in ("cadence", "beta1", "root_parts")})
+                                  if k in ("cadence", "beta1", "root_parts", "large_layer")})
     cad = over.get("cadence", wl.cadence)
     parts = over.get("root_parts", 0)
     steps = wl.steps if steps is None else steps
@@ -112,9 +145,13 @@ def run_parity(wl, ids=None, steps=None, root_tol=ROOT32_TOL, kappa_gate=None, *
             e = rel_fro(dW, dws[k])
             worst[3] = max(worst[3], e)
             assert e <= UPDATE_TOL, (t, k, e)
+            due = lambda b: O.root_due(b, t, cad, parts)
             if k in orc.blocks:
                 w = check_blocks(run, orc, k, t, root_tol=root_tol, kappa_gate=kappa_gate,
-                                 check_roots=lambda b: O.root_due(b, t, cad, parts))
+                                 check_roots=due)
+                worst[:3] = [max(a, b) for a, b in zip(worst[:3], w)]
+            if k in orc.one_sided:
+                w = check_one_sided(run, orc, k, t, due, root_tol=root_tol)
                 worst[:3] = [max(a, b) for a, b in zip(worst[:3], w)]
         if t % cad == 0:
             n64 += sum(1 for d in run.opt.diagnostics() if d.status & FP64)
@@ -199,6 +236,54 @@ def test_async_root_parts(fused_step):
 
 def _custom(tensors, b, **kw):
     return synth.Workload(wid=50 + b, name=f"custom-b{b}", tensors=tensors, block_size=b, **kw)
+
+
+@pytest.mark.parametrize("root_p", [4, 2])
+def test_one_sided_large_layers(root_p):
+    """Lemma 1 (large_layer = 1): tensors with one dimension above
+    max_precond_dim = 320 are preconditioned on the side that fits, with
+    exponent -2/root_p, grafted over the whole tensor.  A tall tensor whose
+    columns fit (R side, 96: the fused root kernel), a wide one whose rows fit
+    (L side, 100), a tall one with a 300 side (batched Newton chain and the
+    big-factor Lanczos; ragged split-K chunks of its 2500 rows), beside
+    Lemma-2 blocks, a tensor too large on both sides (diagonal Adagrad) and a
+    sparse table.  Roots every 2 steps; statistics, roots (stage-isolated) and
+    updates against the oracle."""
+    T = synth.TensorSpec
+    wl = _custom([T("tall", 3000, 96), T("a", 250, 200), T("wide", 100, 5000),
+                  T("tall300", 2500, 300, grad="student_t"), T("huge", 600, 700),
+                  T("emb", 700, 64, kind="sparse", grad="sparse_rows")], 128,
+                 max_precond_dim=320, cadence=2, steps=4, root_p=root_p,
+                 newton_iters=20 if root_p == 4 else 28)
+    # (root_p = 2: the Lemma-2 factors take p = 2, which needs a few more
+    # iterations for the fp64 bar at kappa ~ 1e6, as in the small-block p = 2
+    # test; the one-sided factors take p = 1)
+    run, orc = run_parity(wl, large_layer=1)
+    assert sorted(orc.one_sided) == [0, 2, 3]
+
+
+def test_one_sided_root_parts_and_step_entry():
+    """One-sided blocks in a staggered root pass (numbered after the Lemma-2
+    blocks, as in the oracle's schedule) through shampoo_step."""
+    T = synth.TensorSpec
+    wl = _custom([T("tall", 3000, 96), T("a", 250, 200), T("wide", 100, 5000)], 128,
+                 max_precond_dim=256, cadence=4, steps=8)
+    ids = [0, 1, 2]
+    run = GpuRun(wl, ids, root_parts=2, large_layer=1)
+    orc = make_oracle(wl, ids, cadence=4, root_parts=2, large_layer=1)
+    for t in range(8):
+        host, dev, sp = run.grads_at(t)
+        before = [_np(p) for p in run.params]
+        run.opt.step(run.params, dev, t, 4, sp)
+        torch.cuda.synchronize()
+        dws = orc.step(host, t)
+        for k in range(3):
+            e = rel_fro(_np(run.params[k]) - before[k], dws[k])
+            assert e <= UPDATE_TOL, (t, k, e)
+        due = lambda b: O.root_due(b, t, 4, 2)
+        check_blocks(run, orc, 1, t, check_roots=due)
+        for k in (0, 2):
+            check_one_sided(run, orc, k, t, due)
 
 
 def test_ragged_multitile_and_stale_roots():

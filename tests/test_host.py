@@ -121,12 +121,14 @@ def test_planner_matches_oracle_partition(wid):
     p.close()
 
 
-def test_state_regions_do_not_overlap():
-    """Every byte range the layout hands out is disjoint and inside the state."""
+@pytest.mark.parametrize("large_layer", [0, 1])
+def test_state_regions_do_not_overlap(large_layer):
+    """Every byte range the layout hands out is disjoint and inside the state
+    (with large_layer, the 5000 x 64 tensor is a one-sided block)."""
     T = synth.TensorSpec
     wl = synth.Workload(90, "mix", [T("a", 300, 200), T("b", 64, 147), T("e", 5000, 64),
                                    T("s", 1000, 32, kind="sparse")], 128, max_precond_dim=4096)
-    cfg = S.make_config(128, root_mode="auto")
+    cfg = S.make_config(128, root_mode="auto", max_precond_dim=4096, large_layer=large_layer)
     p = S.Plan([(t.rows, t.cols, 0 if t.kind == "dense" else 1) for t in wl.tensors], cfg)
     spans = []
     for i in range(p.n_blocks):
@@ -134,6 +136,8 @@ def test_state_regions_do_not_overlap():
         spans += [(bl.off_l, bl.ld_l ** 2 * 8), (bl.off_r, bl.ld_r ** 2 * 8),
                   (bl.off_pl, bl.ld_l ** 2 * 4), (bl.off_pr, bl.ld_r ** 2 * 4),
                   (bl.off_pl64, bl.ld_l ** 2 * 8), (bl.off_pr64, bl.ld_r ** 2 * 8)]
+    assert sum(p.block(i).one_sided for i in range(p.n_blocks)) == large_layer
+    spans = [(o, n) for o, n in spans if o >= 0]
     for ti, t in enumerate(wl.tensors):
         a_off, m_off, _, _ = p.tensor(ti)
         spans.append((a_off, t.numel * 4))
@@ -144,3 +148,64 @@ def test_state_regions_do_not_overlap():
         assert o1 + n1 <= o2
     assert spans[-1][0] + spans[-1][1] <= p.state_bytes
     p.close()
+
+
+def test_one_sided_plan_numbering_and_layout():
+    """large_layer = 1 (Lemma 1): a dense tensor with one dimension above
+    max_precond_dim gets one block with one factor for the side that fits,
+    numbered after every Lemma-2 block, as the oracle numbers it for the root
+    schedule; a tensor with both dimensions too large stays diagonal Adagrad."""
+    T = synth.TensorSpec
+    tensors = [T("tall", 3000, 96), T("a", 250, 200), T("wide", 100, 5000), T("huge", 900, 900),
+               T("s", 1000, 32, kind="sparse"), T("b", 64, 147)]
+    shapes = [(t.rows, t.cols, 0 if t.kind == "dense" else 1) for t in tensors]
+    cfg = S.make_config(128, max_precond_dim=256, root_mode="auto", large_layer=1)
+    ocfg = O.OracleConfig(block_size=128, max_precond_dim=256, large_layer=1)
+    orc = O.ShampooOracle(ocfg, [(t.rows, t.cols, t.kind) for t in tensors],
+                          [np.zeros((t.rows, t.cols), np.float32) for t in tensors])
+    p = S.Plan(shapes, cfg)
+    n_reg = sum(len(v) for v in orc.blocks.values())
+    assert n_reg == 2 * 2 + 1 * 2   # a: 2x2 blocks, b: 1x2
+    assert p.n_blocks == n_reg + 2
+    assert p.n_factors == 2 * n_reg + 2
+    expect = {0: "R", 2: "L"}
+    for ti, side in expect.items():
+        idx, st = orc.one_sided[ti]
+        assert st.side == side
+        _, _, fb, nb = p.tensor(ti)
+        assert (fb, nb) == (idx, 1)
+        bl = p.block(fb)
+        t = tensors[ti]
+        assert bl.one_sided == 1
+        assert (bl.tensor, bl.row0, bl.col0, bl.rows, bl.cols) == (ti, 0, 0, t.rows, t.cols)
+        if side == "R":
+            assert bl.factor_l == -1 and bl.off_l == -1 and bl.off_pl == -1 and bl.ld_l == 0
+            assert bl.factor_r == 2 * n_reg + (idx - n_reg) and bl.ld_r == 96
+        else:
+            assert bl.factor_r == -1 and bl.off_r == -1 and bl.off_pr == -1 and bl.ld_r == 0
+            assert bl.factor_l == 2 * n_reg + (idx - n_reg) and bl.ld_l == 128
+    assert p.tensor(3)[3] == 0 and 3 not in orc.one_sided   # both sides too large
+    # regular blocks keep their numbering and factor ids
+    for b in range(n_reg):
+        bl = p.block(b)
+        assert bl.one_sided == 0 and (bl.factor_l, bl.factor_r) == (2 * b, 2 * b + 1)
+    p.close()
+    # large_layer off: the same tensors plan no one-sided block
+    p = S.Plan(shapes, S.make_config(128, max_precond_dim=256))
+    assert p.n_blocks == n_reg and p.tensor(0)[3] == 0
+    p.close()
+
+
+def test_one_sided_config_errors():
+    L = S.lib()
+    h = S._P()
+    descs = (S.TensorDesc * 1)(S.TensorDesc(3000, 64, 0, 0))
+    c = S.make_config(64, max_precond_dim=128, large_layer=2)
+    assert L.shampoo_create(ctypes.byref(c), 1, descs, ctypes.byref(h)) == -1
+    # the one factor takes the exponent -2/root_p: root_p must be even
+    c = S.make_config(64, max_precond_dim=128, large_layer=1, root_p=1)
+    assert L.shampoo_create(ctypes.byref(c), 1, descs, ctypes.byref(h)) == -5
+    # a one-sided factor above the supported dimension
+    big = (S.TensorDesc * 1)(S.TensorDesc(5000, 2048, 0, 0))
+    c = S.make_config(64, max_precond_dim=4096, large_layer=1)
+    assert L.shampoo_create(ctypes.byref(c), 1, big, ctypes.byref(h)) == -5
