@@ -1851,16 +1851,23 @@ __global__ __launch_bounds__(256) void k_adagrad_norm(const BlockChunk* __restri
     if (threadIdx.x == 0) partA[ch.slot] = s;
 }
 
-__global__ void k_block_scale(const BlockNorms* __restrict__ bn, int nblocks,
-                              const double* __restrict__ partA, const double* __restrict__ partD,
-                              float* __restrict__ scale) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= nblocks) return;
+// One wave per block: lane l sums partials l, l + 64, ... in order, then a
+// fixed butterfly across the wave (a fixed order whatever the launch; one
+// partial per side reduces to that partial exactly).
+__global__ __launch_bounds__(256) void k_block_scale(const BlockNorms* __restrict__ bn, int nblocks,
+                                                    const double* __restrict__ partA,
+                                                    const double* __restrict__ partD,
+                                                    float* __restrict__ scale) {
+    const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int l = threadIdx.x & 63;
+    if (b >= nblocks) return;   // uniform per wave
     const BlockNorms q = bn[b];
     double na = 0.0, nd = 0.0;
-    for (int k = 0; k < q.a_count; ++k) na += partA[q.a_first + k];
-    for (int k = 0; k < q.d_count; ++k) nd += partD[q.d_first + k];
-    scale[b] = nd > 0.0 ? (float)sqrt(na / nd) : 0.f;
+    for (int k = l; k < q.a_count; k += 64) na += partA[q.a_first + k];
+    for (int k = l; k < q.d_count; k += 64) nd += partD[q.d_first + k];
+    na = wave_sum(na);
+    nd = wave_sum(nd);
+    if (l == 0) scale[b] = nd > 0.0 ? (float)sqrt(na / nd) : 0.f;
 }
 
 // ================================================== elementwise: update
@@ -2100,7 +2107,7 @@ hipError_t launch_adagrad_norm(const BlockChunk* chunks, int nchunks, const uint
 hipError_t launch_block_scale(const BlockNorms* bn, int nblocks, const double* partA,
                               const double* partD, float* scale, hipStream_t s) {
     if (nblocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_block_scale, dim3((nblocks + 255) / 256), dim3(256), 0, s, bn, nblocks,
+    hipLaunchKernelGGL(k_block_scale, dim3((nblocks + 3) / 4), dim3(256), 0, s, bn, nblocks,
                        partA, partD, scale);
     return hipGetLastError();
 }
