@@ -86,14 +86,20 @@ def uses_shampoo(m: int, n: int, cfg: OracleConfig) -> bool:
 
 
 # -------------------------------------------------------------- statistics
-def one_sided_side(m: int, n: int, cfg: "OracleConfig") -> Optional[str]:
+def one_sided_side(m: int, n: int, cfg: "OracleConfig", kind: str = "dense") -> Optional[str]:
     """Lemma 1 (podcast cue 16): for a layer too large to precondition on both
     sides (a giant embedding or softmax), only one of L or R is used.  A
     dense tensor that does not use Shampoo blocks gets one-sided
     preconditioning when large_layer is set and one dimension fits under
     max_precond_dim: "R" (statistics G^T G, D = G P) when the columns fit,
-    else "L" (G G^T, D = P G).  None: diagonal Adagrad."""
-    if not cfg.large_layer or cfg.max_precond_dim <= 0 or uses_shampoo(m, n, cfg):
+    else "L" (G G^T, D = P G).  A sparse-row table (an embedding) gets "R"
+    when large_layer is set and its columns fit (any, when max_precond_dim
+    is 0).  None: diagonal (or sparse-row) Adagrad."""
+    if not cfg.large_layer:
+        return None
+    if kind == "sparse":
+        return "R" if cfg.max_precond_dim <= 0 or n <= cfg.max_precond_dim else None
+    if cfg.max_precond_dim <= 0 or uses_shampoo(m, n, cfg):
         return None
     if n <= cfg.max_precond_dim:
         return "R"
@@ -298,7 +304,7 @@ class ShampooOracle:
         n_blocks = sum(len(v) for v in self.blocks.values())
         self.one_sided: Dict[int, Tuple[int, _OneSidedState]] = {}
         for i, (m, n, kind) in enumerate(self.shapes):
-            side = one_sided_side(m, n, cfg) if kind == "dense" else None
+            side = one_sided_side(m, n, cfg, kind)
             if side is not None:
                 if cfg.root_p % 2:
                     raise ValueError("one-sided preconditioning needs an even root_p")
@@ -330,8 +336,11 @@ class ShampooOracle:
             W_old = self.W[i]
             if kind == "sparse":
                 rows, g = grads[i]
-                self.a[i], self.W[i] = sparse_rows_update(self.a[i], self.W[i], rows, g,
-                                                          cfg.lr, cfg.graft_eps)
+                if i in self.one_sided:
+                    self._sparse_one_sided(i, np.asarray(rows), np.asarray(g, dtype=np.float64), t)
+                else:
+                    self.a[i], self.W[i] = sparse_rows_update(self.a[i], self.W[i], rows, g,
+                                                              cfg.lr, cfg.graft_eps)
                 deltas.append(self.W[i] - W_old)
                 continue
             G = np.asarray(grads[i], dtype=np.float64)
@@ -363,15 +372,8 @@ class ShampooOracle:
                 # Lemma 1: S <- beta2 S + w G^T G (or G G^T), P = (S + eps I)^(-2/p)
                 # (the one factor carries the whole -1/2), D = G P (or P G),
                 # grafted over the whole tensor
-                idx, st = self.one_sided[i]
-                d, w = ema_weights(cfg.beta2)
-                st.S = d * st.S + w * ((G.T @ G) if st.side == "R" else (G @ G.T))
-                if root_due(idx, t, cfg.cadence, cfg.root_parts):
-                    st.root = inverse_root(st.S, cfg.eps_rel, cfg.root_p // 2)
-                    if cfg.root_delay > 0:
-                        st.pending = (t + cfg.root_delay, st.root)
-                    elif st.root.ok:
-                        st.P = st.root.P
+                _, st = self.one_sided[i]
+                self._one_sided_stats_and_root(i, (G.T @ G) if st.side == "R" else (G @ G.T), t)
                 D = (G @ st.P) if st.side == "R" else (st.P @ G)
                 self.last_D[i] = D
                 U = graft(A, D)
@@ -381,6 +383,41 @@ class ShampooOracle:
                                                      cfg.beta1, cfg.lr)
             deltas.append(self.W[i] - W_old)
         return deltas
+
+    def _one_sided_stats_and_root(self, i: int, outer: np.ndarray, t: int):
+        """S <- beta2 S + w outer; on a root step of this tensor's block,
+        P = (S + eps I)^(-2/p): the one factor carries the whole -1/2."""
+        cfg = self.cfg
+        idx, st = self.one_sided[i]
+        d, w = ema_weights(cfg.beta2)
+        st.S = d * st.S + w * outer
+        if root_due(idx, t, cfg.cadence, cfg.root_parts):
+            st.root = inverse_root(st.S, cfg.eps_rel, cfg.root_p // 2)
+            if cfg.root_delay > 0:
+                st.pending = (t + cfg.root_delay, st.root)
+            elif st.root.ok:
+                st.P = st.root.P
+
+    def _sparse_one_sided(self, i: int, rows: np.ndarray, g: np.ndarray, t: int):
+        """One-sided preconditioning of a sparse-row table: the R side, with
+        the row-sparse gradient G (g on the listed rows, 0 elsewhere):
+        S <- beta2 S + w G^T G = beta2 S + w g^T g; D = G P (nonzero on the
+        listed rows only); a += G*G and A = G / (sqrt(a) + delta) on those
+        rows; U = graft(A, D) over the table; W -= lr U.  No momentum, as
+        for the sparse-row Adagrad this replaces, so untouched rows keep
+        their weights.  Rows must be distinct."""
+        cfg = self.cfg
+        _, st = self.one_sided[i]
+        self._one_sided_stats_and_root(i, g.T @ g, t)
+        D = g @ st.P
+        a = self.a[i].copy()
+        a[rows] = a[rows] + g * g
+        A = g / (np.sqrt(a[rows]) + cfg.graft_eps)
+        U = graft(A, D)
+        W = self.W[i].copy()
+        W[rows] = W[rows] - cfg.lr * U
+        self.a[i], self.W[i] = a, W
+        self.last_D[i] = D
 
     def block_states(self, i: int):
         return self.blocks.get(i, [])

@@ -511,3 +511,47 @@ def test_one_sided_fallbacks_and_numbering():
     assert np.allclose(orc.last_D[1], G)          # no one-sided root yet
     orc.step([np.eye(2), G], 1)
     assert not np.allclose(orc.last_D[1], G)
+
+
+def test_sparse_one_sided_equals_dense_on_scattered_gradient():
+    """A sparse-row table with large_layer (R side) is the dense one-sided
+    path on the row-sparse gradient G (g scattered into zero rows) with no
+    momentum (beta1 = 0): same statistics, same weights, over steps with
+    different row sets, one of them empty; rows never listed keep their
+    weights bitwise."""
+    m, n = 12, 3
+    rng = np.random.default_rng(6)
+    kw = dict(block_size=2, max_precond_dim=4, large_layer=1, beta2=0.9, cadence=2, lr=0.1)
+    W0 = rng.standard_normal((m, n))
+    sp = O.ShampooOracle(O.OracleConfig(**kw), [(m, n, "sparse")], [W0])
+    dn = O.ShampooOracle(O.OracleConfig(beta1=0.0, **kw), [(m, n, "dense")], [W0])
+    assert sp.one_sided[0][1].side == "R" and dn.one_sided[0][1].side == "R"
+    row_sets = [np.array([1, 4, 7, 8]), np.array([4, 0, 11]), np.array([], dtype=np.int64),
+                np.array([2, 4, 9, 10, 1])]
+    for t, rows in enumerate(row_sets):
+        g = rng.standard_normal((len(rows), n))
+        G = np.zeros((m, n))
+        G[rows] = g
+        sp.step([(rows, g)], t)
+        dn.step([G], t)
+        assert np.allclose(sp.one_sided[0][1].S, dn.one_sided[0][1].S, rtol=1e-13, atol=1e-15)
+        assert np.allclose(sp.W[0], dn.W[0], rtol=1e-12, atol=1e-14), t
+    listed = set(np.concatenate(row_sets).tolist())
+    for r in range(m):
+        if r not in listed:
+            assert np.array_equal(sp.W[0][r], W0[r])
+    assert not np.allclose(sp.W[0][1], W0[1])
+
+
+def test_sparse_one_sided_side_rule():
+    """Sparse tables take the R side when large_layer is set and the columns
+    fit (any width when max_precond_dim is 0); otherwise sparse-row Adagrad."""
+    on = O.OracleConfig(block_size=2, max_precond_dim=4, large_layer=1)
+    assert O.one_sided_side(1000, 4, on, "sparse") == "R"
+    assert O.one_sided_side(1000, 5, on, "sparse") is None
+    assert O.one_sided_side(3, 3, on, "sparse") == "R"
+    unlimited = O.OracleConfig(block_size=2, max_precond_dim=0, large_layer=1)
+    assert O.one_sided_side(1000, 64, unlimited, "sparse") == "R"
+    assert O.one_sided_side(1000, 64, unlimited, "dense") is None   # uses Lemma-2 blocks
+    off = O.OracleConfig(block_size=2, max_precond_dim=4)
+    assert O.one_sided_side(1000, 4, off, "sparse") is None
