@@ -91,13 +91,19 @@ def work_model(wl, opt, n_fp64_factors_per_pass):
     apply_d = sum(2.0 * b.rows ** 2 * b.cols for b in blocks)
     # one-sided blocks (Lemma 1): S = G^T G or G G^T and D = G P or P G are
     # each 2 dim numel flops
-    onesided_flops = sum(2.0 * (b.cols if b.factor_r >= 0 else b.rows) * b.rows * b.cols
-                         for b in onesided)
+    def listed_rows(b):   # a sparse table's statistics and apply see the listed rows only
+        t = wl.tensors[b.tensor]
+        return round(wl.sparse_frac * t.rows) if t.kind == "sparse" else b.rows
+    def os_flops(bs):
+        return sum(2.0 * (b.cols if b.factor_r >= 0 else b.rows) * listed_rows(b) * b.cols
+                   for b in bs)
+    sparse_os = [b for b in onesided if wl.tensors[b.tensor].kind == "sparse"]
+    dense_os = [b for b in onesided if wl.tensors[b.tensor].kind == "dense"]
     dims = [(dim, p) for dim, p in factor_dims(opt, wl.root_p)]
     root_flops_all = sum(newton_flops(n, p, wl.newton_iters) for n, p in dims)
-    shampoo_params = sum(b.rows * b.cols for b in blocks) + sum(b.rows * b.cols for b in onesided)
+    shampoo_params = sum(b.rows * b.cols for b in blocks) + sum(b.rows * b.cols for b in dense_os)
     small = [b for b in blocks if b.rows <= 128 and b.cols <= 128]
-    big = [b for b in blocks if not (b.rows <= 128 and b.cols <= 128)] + onesided
+    big = [b for b in blocks if not (b.rows <= 128 and b.cols <= 128)] + dense_os
     dense_fallback = sum(t.numel for t in wl.tensors if t.kind == "dense") - shampoo_params
     # tensors whose blocks are all <= 128 get their momentum and weight update
     # inside the fused apply kernel
@@ -120,8 +126,10 @@ def work_model(wl, opt, n_fp64_factors_per_pass):
         "apply_small": sum(2.0 * (b.rows * b.cols ** 2 + b.rows ** 2 * b.cols) for b in small),
         "apply_t_big": sum(2.0 * b.rows * b.cols ** 2 for b in big if not b.one_sided),
         "apply_d_big": sum(2.0 * b.rows ** 2 * b.cols for b in big if not b.one_sided) +
-        onesided_flops,
-        "stats_onesided": onesided_flops,
+        os_flops(dense_os),
+        "stats_onesided": os_flops(dense_os),
+        "stats_onesided_rows": os_flops(sparse_os), "apply_onesided_rows": os_flops(sparse_os),
+        "onesided_rows_elems": sum(listed_rows(b) * b.cols for b in sparse_os),
         "shampoo_params_big": sum(b.rows * b.cols for b in big),
         "root_flops_all": root_flops_all,
         "root_flops_per_factor_mean": root_flops_all / max(len(dims), 1),
@@ -322,6 +330,11 @@ def main():
         # name: (work per launch, unit, bound, peak)
         "stats_gram_f64": (wm["gram"], "TFLOP/s", "mfma", PEAK_TFLOPS["f64"]),
         "stats_onesided": (wm["stats_onesided"], "TFLOP/s", "mfma", PEAK_TFLOPS["f64"]),
+        "stats_onesided_rows": (wm["stats_onesided_rows"], "TFLOP/s", "mfma", PEAK_TFLOPS["f64"]),
+        "apply_onesided_rows": (wm["apply_onesided_rows"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]),
+        # g read, a read and written (row ids aside); D read, W read and written
+        "onesided_rows_norm": (wm["onesided_rows_elems"] * 12.0, "GB/s", "hbm", PEAK_HBM_GBS),
+        "onesided_rows_update": (wm["onesided_rows_elems"] * 12.0, "GB/s", "hbm", PEAK_HBM_GBS),
         "apply_gemm_t": (wm["apply_t_big"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]),
         "apply_gemm_d": (wm["apply_d_big"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]),
         "adagrad_norm": (wm["shampoo_params_big"] * 12.0, "GB/s", "hbm", PEAK_HBM_GBS),

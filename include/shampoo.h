@@ -81,7 +81,11 @@ typedef struct {
     int32_t max_precond_dim;  /* dense tensors with a dimension above this use diagonal
                                  Adagrad; 0 = no limit                                   */
     int32_t root_p;           /* p of the inverse p-th root; the pages use 4 (cue 10)    */
-    int32_t newton_iters;     /* coupled-Newton iterations per root (e.g. 20)           */
+    int32_t newton_iters;     /* coupled-Newton iterations per root at p = 4 (e.g. 20);
+                                 a factor with exponent p < 4 runs
+                                 ceil(newton_iters log g_4 / log g_p), g_p = ((p+1)/p)^p
+                                 (p = 2: 23, p = 1: 26 for 20), the steps that close the
+                                 same eigenvalue gap                                     */
     int32_t root_mode;        /* shampoo_root_mode                                       */
     int32_t lanczos_steps;    /* Krylov steps for lambda_max; 0 = 20 for factors up to
                                  128 and 24 above; the kappa estimate uses min(8, this)  */
@@ -96,7 +100,10 @@ typedef struct {
                                  that side only (Lemma 1, cue 16: for a giant embedding
                                  or softmax layer only one of L or R is used), with the
                                  exponent -2/root_p so that the one factor carries the
-                                 whole -1/2 of full-matrix Adagrad; needs an even root_p */
+                                 whole -1/2 of full-matrix Adagrad; needs an even root_p.
+                                 With 1, sparse-row tables whose columns fit (any, when
+                                 max_precond_dim is 0) get the column side instead of
+                                 sparse-row Adagrad                                      */
     double beta1;             /* momentum: mom <- beta1 mom + U                          */
     double beta2;             /* statistics: S <- beta2 S + (1-beta2) outer(G) (beta2<1),
                                  S <- S + outer(G) when beta2 == 1; 1 - beta2 is formed in
@@ -162,9 +169,10 @@ typedef struct {
  * Dense tensors whose dimensions are both <= max_precond_dim (or any, when it
  * is 0) are split into Lemma-2 blocks (cue 16); each block gets an L and an R
  * factor.  With large_layer = 1, a dense tensor with one dimension above
- * max_precond_dim and the other within it becomes one more block, numbered
- * after every Lemma-2 block (tensors in order), with one factor for the side
- * that fits.  Errors: SHAMPOO_E_ARG (null pointer, n_tensors < 1, a dimension
+ * max_precond_dim and the other within it, and a sparse-row table whose
+ * columns fit, become one more block each, numbered after every Lemma-2
+ * block (tensors in order), with one factor for the side that fits (R for a
+ * table).  Errors: SHAMPOO_E_ARG (null pointer, n_tensors < 1, a dimension
  * < 1, block_size < 1, newton_iters < 1, beta2 outside (0,1], eps_rel < 0,
  * unknown kind or root_mode, large_layer not 0 or 1), SHAMPOO_E_UNSUPPORTED
  * (root_p not in {1,2,4,8}; root_p odd with large_layer = 1; a factor
@@ -192,10 +200,16 @@ int shampoo_bind_state(shampoo_t* h, void* dev_state, size_t bytes, void* stream
  * gradients, fp64 products and accumulation on MFMA, fp64 storage.  A
  * one-sided block updates only its one factor, S <- beta2 S + w G^T G (R) or
  * w G G^T (L), the product split over the long dimension and the partial
- * products summed in a fixed order.  grads: n_tensors device pointers, read
- * only; entries of tensors without blocks are ignored (may be NULL).
- * Errors: SHAMPOO_E_ARG, SHAMPOO_E_STATE, SHAMPOO_E_HIP. */
-int shampoo_update_stats(shampoo_t* h, const float* const* grads, void* stream);
+ * products summed in a fixed order.  A sparse-row table with one-sided
+ * preconditioning adds the products of this call's row gradients,
+ * S <- beta2 S + w g^T g (only decaying when it lists no rows).  grads:
+ * n_tensors device pointers, read only; entries of tensors without blocks
+ * are ignored (may be NULL).  sparse: as in shampoo_precondition_and_apply;
+ * read only for sparse-row tables with one-sided preconditioning, may be NULL
+ * when the plan has none.  Errors: SHAMPOO_E_ARG, SHAMPOO_E_STATE,
+ * SHAMPOO_E_HIP. */
+int shampoo_update_stats(shampoo_t* h, const float* const* grads,
+                         const shampoo_sparse_rows* sparse, void* stream);
 
 /* Inverse roots (cue 10, 12, 14): for every factor S, lambda_max by Lanczos,
  * eps = eps_rel * lambda_max, then P = (S + eps I)^(-1/p) (p = root_p, or
@@ -240,7 +254,12 @@ int shampoo_roots_async_end(shampoo_t* h, void* stream);
  * U_b = D_b ||A_b||_F / ||D_b||_F (0 when ||D_b|| = 0);
  * mom <- beta1 mom + U; W <- W - lr mom.  A one-sided block takes D = G P (R)
  * or P G (L) and grafts over the whole tensor; other tensors above
- * max_precond_dim take U = A.  Sparse tables: for each listed row r, a_r += g_r^2 and
+ * max_precond_dim take U = A.  A sparse-row table with one-sided
+ * preconditioning takes, on its listed rows, a_r += g_r^2,
+ * A = g / (sqrt(a) + graft_eps), D = g P_R, U = D ||A||_F / ||D||_F (norms over
+ * the listed rows) and W_r -= lr U_r: no momentum, and rows not listed are
+ * untouched; row ids outside the table are skipped by the accumulator and
+ * weight updates (their gradients still enter the statistics).  Sparse tables: for each listed row r, a_r += g_r^2 and
  * W_r -= lr g_r / (sqrt(a_r) + graft_eps); other rows untouched; no momentum.
  * params: n_tensors device pointers, updated in place.  grads: as in
  * shampoo_update_stats (dense tensors must be non-NULL).  sparse: NULL when

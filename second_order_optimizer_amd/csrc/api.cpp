@@ -32,6 +32,7 @@ constexpr int kRingSlots = 16;        // pinned staging slots for per-call table
 constexpr size_t kNewtonScratchBudget = size_t(4) << 30;  // bytes per precision
 constexpr int kSplitKTiles = 1024;    // one-sided statistics: target tiles per launch
 constexpr int kSplitKMin = 256;       // and shortest chunk of the long dimension
+constexpr int kSosMaxChunks = 64;     // sparse one-sided tables: split-K chunks per call, at most
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -42,7 +43,8 @@ struct TensorPlan {
     int mode = 0;  // 0 Shampoo, 1 dense Adagrad, 2 sparse rows
     int64_t off_a = -1, off_mom = -1, off_d = -1;  // bytes
     bool fused = false;  // Shampoo tensor whose blocks are all <= 128: update inside the apply kernel
-    int os_side = -1;    // one-sided (Lemma 1): 0 L (G G^T, D = P G), 1 R (G^T G, D = G P)
+    int os_side = -1;    // one-sided (Lemma 1): 0 L (G G^T, D = P G), 1 R (G^T G, D = G P);
+                         // a sparse-row table (mode 2) with os_side 1 gets its rows per call
     int first_block = 0, n_blocks = 0, nbc = 0;
 };
 
@@ -62,6 +64,13 @@ struct FactorPlan {
     int64_t off_s, off_p, off_p64;  // bytes (off_p64 = -1 when absent)
 };
 
+// A sparse-row table with one-sided preconditioning: what the per-call
+// tables of its statistics and apply need.
+struct SosPlan {
+    int tensor, block, factor;
+    int64_t part_off;    // split-K partials (bytes), kSosMaxChunks x ld^2 fp64
+};
+
 struct LaunchRef {
     int64_t tasks_off = 0, tiles_off = 0;  // bytes
     int ntiles = 0;
@@ -70,6 +79,7 @@ struct LaunchRef {
 struct NewtonChunk {
     int ld = 0;
     int p = 4;                               // root exponent of its factors
+    int iters = 20;                          // coupled-Newton iterations (newton_iters_for)
     int njobs = 0;
     bool fused = false;                      // fp32, ld <= 128: one kernel, no scratch
     int64_t jobs_off = 0;                    // FactorJob table (bytes)
@@ -100,13 +110,15 @@ struct Blob {
 enum ProfCat : int {
     PC_STATS = 0, PC_LANCZOS_S, PC_LANCZOS_P, PC_NEWTON_INIT, PC_NEWTON_GEMM32, PC_NEWTON_GEMM64,
     PC_NEWTON_COMMIT, PC_ADAGRAD, PC_APPLY_T, PC_APPLY_D, PC_SCALE, PC_UPDATE, PC_SPARSE,
-    PC_NEWTON_FUSED, PC_APPLY_FUSED, PC_STEP_FUSED, PC_STATS_SPLITK, PC_COUNT
+    PC_NEWTON_FUSED, PC_APPLY_FUSED, PC_STEP_FUSED, PC_STATS_SPLITK, PC_SOS_STATS, PC_SOS_NORM,
+    PC_SOS_APPLY, PC_SOS_UPDATE, PC_COUNT
 };
 const char* const kProfNames[PC_COUNT] = {
     "stats_gram_f64", "lanczos_stats", "lanczos_roots", "newton_init", "newton_gemm_f32",
     "newton_gemm_f64", "newton_commit", "adagrad_norm", "apply_gemm_t", "apply_gemm_d",
     "block_scale", "update", "sparse_rows", "newton_fused_f32", "apply_fused", "step_fused",
-    "stats_onesided"};
+    "stats_onesided", "stats_onesided_rows", "onesided_rows_norm", "apply_onesided_rows",
+    "onesided_rows_update"};
 
 struct ProfRec {
     int cat;
@@ -132,6 +144,8 @@ struct shampoo_s {
 
     LaunchRef gram, apply1, apply2;   // blocks with a side > 128
     LaunchRef splitk;                 // one-sided statistics: partial products
+    std::vector<SosPlan> sos;         // sparse-row tables with one-sided preconditioning
+    int64_t off_sos_stats = 0, off_sos_apply = 0;  // their per-call tables
     int64_t symred_jobs_off = 0, symred_tiles_off = 0;
     int n_symred_tiles = 0;           // and their fixed-order sum
     int64_t apply128_off = 0;
@@ -153,7 +167,7 @@ struct shampoo_s {
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     int async_part = -1;             // part in flight, or -1
     int64_t blockchunks_off = 0, blocknorms_off = 0, rowchunks_off = 0;
-    int n_blockchunks = 0, n_rowchunks = 0;
+    int n_blockchunks = 0, n_rowchunks = 0, n_blocknorms = 0;
     std::vector<FactorDiag> diag_init;
 
     // binding
@@ -217,10 +231,22 @@ LaunchRef add_launch(Blob& blob, const std::vector<GemmTask>& tasks) {
     return L;
 }
 
+// Coupled-Newton iterations for exponent p.  newton_iters is the count at
+// p = 4.  In the first phase of the iteration the smallest scaled eigenvalue
+// of M grows by g_p = ((p + 1) / p)^p per step (2.44 at p = 4, 2.25 at p = 2,
+// 2 at p = 1), so a smaller exponent takes newton_iters log g_4 / log g_p
+// steps to close the same gap (a one-sided factor takes p = root_p / 2).
+int newton_iters_for(const shampoo_config& c, int p) {
+    if (p >= 4) return c.newton_iters;
+    const double g4 = 4.0 * std::log(5.0 / 4.0), gp = p * std::log((p + 1.0) / p);
+    return (int)std::ceil(c.newton_iters * g4 / gp);
+}
+
 // Builds the per-parity GEMM launches of one Newton chunk.
 void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& fids, int ld,
                         bool fp64, bool fused, int64_t scratch_off_bytes, int p) {
     ch.p = p;
+    ch.iters = newton_iters_for(h->cfg, p);
     const int64_t esz = fp64 ? 8 : 4;
     const int64_t mat = (int64_t)ld * ld;
     const int64_t sbase = scratch_off_bytes / esz;  // scratch start in elements (arena base 0)
@@ -304,6 +330,9 @@ int build_plan(shampoo_s* h) {
         if (tp.kind == SHAMPOO_SPARSE_ROWS) {
             tp.mode = 2;
             h->n_sparse++;
+            // Lemma 1 for an embedding table: the column side, when it fits
+            if (c.large_layer == 1 && (c.max_precond_dim <= 0 || tp.cols <= c.max_precond_dim))
+                tp.os_side = 1;
             continue;
         }
         const bool shampoo = c.max_precond_dim <= 0 ||
@@ -388,7 +417,8 @@ int build_plan(shampoo_s* h) {
         const int64_t numel = tp.rows * tp.cols;
         tp.off_a = take(numel * 4);
         if (tp.mode != 2) tp.off_mom = take(numel * 4);
-        if (tp.mode == 0 && !tp.fused) tp.off_d = take(numel * 4);
+        if ((tp.mode == 0 && !tp.fused) || (tp.mode == 2 && tp.os_side >= 0))
+            tp.off_d = take(numel * 4);   // sparse one-sided: D of the listed rows
     }
     for (auto& bp : h->blocks)
         bp.off_t = (bp.small || bp.one_sided) ? -1 : take((int64_t)bp.mb * bp.nb * 4);
@@ -400,6 +430,11 @@ int build_plan(shampoo_s* h) {
         const BlockPlan& bp = h->blocks[i];
         if (!bp.one_sided) continue;
         const FactorPlan& f = h->factors[bp.fl];
+        if (h->tensors[bp.tensor].mode == 2) {   // rows per call: chunks fixed per call
+            splitk_at[i] = take((int64_t)kSosMaxChunks * f.ld * f.ld * 8);
+            h->sos.push_back({bp.tensor, (int)i, bp.fl, splitk_at[i]});
+            continue;
+        }
         const int64_t K = f.side == 1 ? bp.mb : bp.nb;       // the long dimension
         const int ut = ceil_div(f.dim, kTile) * (ceil_div(f.dim, kTile) + 1) / 2;
         const int want = std::max(1, ceil_div(kSplitKTiles, ut));
@@ -501,6 +536,23 @@ int build_plan(shampoo_s* h) {
             stage_at[i] = h->off_stage + stage_rel[i];
         }
     }
+    // per-call tables of the sparse one-sided tables (largest possible call)
+    if (!h->sos.empty()) {
+        int64_t st = 0, ap = 0;
+        const int64_t n = (int64_t)h->sos.size();
+        for (const SosPlan& sp : h->sos) {
+            const FactorPlan& f = h->factors[sp.factor];
+            const BlockPlan& bp = h->blocks[sp.block];
+            const int64_t t1 = ceil_div(f.dim, kTile), t32 = ceil_div(f.dim, 32);
+            st += kSosMaxChunks * (int64_t)(sizeof(GemmTask) + t1 * (t1 + 1) / 2 * sizeof(TileRef)) +
+                  t32 * (t32 + 1) / 2 * (int64_t)sizeof(TileRef);
+            ap += (int64_t)ceil_div(bp.mb, kTile) * ceil_div(bp.nb, kTile) * sizeof(TileRef);
+        }
+        st += n * (int64_t)sizeof(SymReduceJob) + 4 * 256;
+        ap += n * (int64_t)(sizeof(SosJob) + sizeof(GemmTask) + sizeof(BlockNorms)) + 4 * 256;
+        h->off_sos_stats = take(st);
+        h->off_sos_apply = take(ap);
+    }
     h->off_tables = align_up(off, 256);
 
     // ---- static tables
@@ -519,6 +571,7 @@ int build_plan(shampoo_s* h) {
             const TensorPlan& tp = h->tensors[bp.tensor];
             const FactorPlan& fl = h->factors[bp.fl];
             const FactorPlan& fr = h->factors[bp.fr];
+            if (bp.one_sided && tp.mode == 2) continue;   // sparse rows: per call
             if (bp.one_sided) {
                 // partial c: S_c = G_c^T G_c (R; G_c rows [c len, (c+1) len)) or
                 // G_c G_c^T (L; G_c those columns), upper 128 x 128 tiles
@@ -610,6 +663,7 @@ int build_plan(shampoo_s* h) {
             const TensorPlan& tp = h->tensors[bp.tensor];
             const FactorPlan& fl = h->factors[bp.fl];
             const FactorPlan& fr = h->factors[bp.fr];
+            if (bp.one_sided && tp.mode == 2) continue;   // sparse rows: per call
             if (bp.one_sided) {
                 // D = G P (R) or P G (L), with ||D||^2 partials per tile
                 GemmTask u{};
@@ -786,6 +840,7 @@ int build_plan(shampoo_s* h) {
             const BlockPlan& bp = h->blocks[i];
             const TensorPlan& tp = h->tensors[bp.tensor];
             const int rows_per = (int)std::max<int64_t>(1, kElemChunk / bp.nb);
+            if (tp.mode == 2) continue;   // sparse one-sided table: norms per call
             for (int k = 0; !bp.small && k < bp.a_chunks; ++k) {
                 BlockChunk q{};
                 q.tensor = bp.tensor;
@@ -799,9 +854,10 @@ int build_plan(shampoo_s* h) {
                 q.a_off = tp.off_a / 4;
                 bcs.push_back(q);
             }
-            bns.push_back({bp.a_slot, bp.a_chunks, bp.d_slot, bp.d_tiles});
+            bns.push_back({bp.a_slot, bp.a_chunks, bp.d_slot, bp.d_tiles, (int)i, 0});
         }
         h->n_blockchunks = (int)bcs.size();
+        h->n_blocknorms = (int)bns.size();
         h->blockchunks_off = blob.add(bcs);
         h->blocknorms_off = blob.add(bns);
         std::vector<RowChunk> rcs;
@@ -874,11 +930,17 @@ T* tab(shampoo_s* h, int64_t blob_off) {
     return reinterpret_cast<T*>(h->arena + h->off_tables + blob_off);
 }
 
-// Copies `bytes` of host data to the arena at `dst_off` through a pinned
-// staging slot (so the call stays asynchronous).
+// Copies `bytes` of host data to the arena at `dst_off` through pinned
+// staging slots (so the call stays asynchronous), one slot per piece.
 int stage_upload(shampoo_s* h, const void* src, size_t bytes, int64_t dst_off, hipStream_t s) {
+    while (bytes > h->slot_bytes) {
+        const int rc = stage_upload(h, src, h->slot_bytes, dst_off, s);
+        if (rc) return rc;
+        src = static_cast<const unsigned char*>(src) + h->slot_bytes;
+        dst_off += (int64_t)h->slot_bytes;
+        bytes -= h->slot_bytes;
+    }
     if (bytes == 0) return SHAMPOO_OK;
-    if (bytes > h->slot_bytes) return SHAMPOO_E_ARG;
     const int k = h->ring_next;
     h->ring_next = (k + 1) % kRingSlots;
     if (h->ring_used[k]) {
@@ -895,7 +957,10 @@ int stage_upload(shampoo_s* h, const void* src, size_t bytes, int64_t dst_off, h
     return SHAMPOO_OK;
 }
 
-int refresh_bases(shampoo_s* h, const float* const* grads, float* const* params, hipStream_t s) {
+// The per-call pointer table: the state buffer, each tensor's gradient (for
+// a sparse one-sided table, its row gradients) and weights.
+int refresh_bases(shampoo_s* h, const float* const* grads, float* const* params,
+                  const shampoo_sparse_rows* sparse, hipStream_t s) {
     std::vector<uint64_t> nb = h->bases_host;
     if (nb.empty()) nb.assign(1 + 2 * (size_t)h->n, 0);
     nb[0] = reinterpret_cast<uint64_t>(h->arena);
@@ -903,6 +968,9 @@ int refresh_bases(shampoo_s* h, const float* const* grads, float* const* params,
         if (grads) nb[1 + t] = reinterpret_cast<uint64_t>(grads[t]);
         if (params) nb[1 + h->n + t] = reinterpret_cast<uint64_t>(params[t]);
     }
+    if (sparse)
+        for (const SosPlan& sp : h->sos)
+            nb[1 + sp.tensor] = reinterpret_cast<uint64_t>(sparse[sp.tensor].row_grads);
     if (h->bases_valid && nb == h->bases_host) return SHAMPOO_OK;
     const int rc = stage_upload(h, nb.data(), nb.size() * 8, h->off_bases, s);
     if (rc != SHAMPOO_OK) return rc;
@@ -1035,10 +1103,11 @@ int shampoo_bind_state(shampoo_t* h, void* dev_state, size_t bytes, void* stream
     h->bases_valid = false;
     h->bases_host.clear();
     if (!h->ring) {
-        h->slot_bytes = (size_t)align_up(std::max<int64_t>((1 + 2 * (int64_t)h->n) * 8,
-                                                           (int64_t)std::max(h->n_sparse, 1) *
-                                                               sizeof(SparseJob)),
-                                         256);
+        h->slot_bytes = (size_t)align_up(
+            std::max<int64_t>({(1 + 2 * (int64_t)h->n) * 8,
+                               (int64_t)std::max(h->n_sparse, 1) * (int64_t)sizeof(SparseJob),
+                               h->sos.empty() ? 0 : (int64_t)64 << 10}),
+            256);
         if (hipHostMalloc(reinterpret_cast<void**>(&h->ring), h->slot_bytes * kRingSlots,
                           hipHostMallocDefault) != hipSuccess) {
             h->ring = nullptr;
@@ -1074,7 +1143,7 @@ int shampoo_bind_state(shampoo_t* h, void* dev_state, size_t bytes, void* stream
     rc = hip_err(launch_set_identity(tab<FactorJob>(h, h->ident_jobs_off), (int)h->factors.size(),
                                      at<float>(h, 0), s));
     if (rc) return rc;
-    rc = refresh_bases(h, nullptr, nullptr, s);  // base 0 (the state buffer) for every kernel
+    rc = refresh_bases(h, nullptr, nullptr, nullptr, s);  // base 0 (the state buffer) for every kernel
     if (rc) return rc;
     rc = hip_err(hipStreamSynchronize(s));
     if (rc) return rc;
@@ -1096,10 +1165,12 @@ GemmArgs stats_args(const shampoo_s* h) {
     return a;
 }
 
+int enqueue_sos_stats(shampoo_s* h, const shampoo_sparse_rows* sparse, hipStream_t s);
+
 // Statistics kernels on stream s (pointer table already current).  With
 // skip_small the blocks of at most 128 x 128 are left to the fused step
 // kernel (enqueue_apply with fused_small).
-int enqueue_stats(shampoo_s* h, hipStream_t s, bool skip_small) {
+int enqueue_stats(shampoo_s* h, hipStream_t s, bool skip_small, const shampoo_sparse_rows* sparse) {
     const GemmArgs a = stats_args(h);
     // fp32 gradients, fp64 products and statistics (exact products; the
     // statistics keep the near-null spectrum that fp32 storage would round
@@ -1116,6 +1187,10 @@ int enqueue_stats(shampoo_s* h, hipStream_t s, bool skip_small) {
                                                         tab<TileRef>(h, h->gram.tiles_off),
                                                         h->gram.ntiles, at<uint64_t>(h, h->off_bases),
                                                         a, s));
+        if (rc) return rc;
+    }
+    if (!h->sos.empty()) {
+        const int rc = enqueue_sos_stats(h, sparse, s);
         if (rc) return rc;
     }
     if (h->n_symred_tiles == 0) return SHAMPOO_OK;
@@ -1135,10 +1210,17 @@ int enqueue_stats(shampoo_s* h, hipStream_t s, bool skip_small) {
                                      at<double>(h, 0), a.alpha, a.beta, s));
 }
 
-int check_stats_args(const shampoo_s* h, const float* const* grads) {
+int check_stats_args(const shampoo_s* h, const float* const* grads,
+                     const shampoo_sparse_rows* sparse) {
     if (!grads) return SHAMPOO_E_ARG;
     for (auto& bp : h->blocks)
-        if (!grads[bp.tensor]) return SHAMPOO_E_ARG;
+        if (h->tensors[bp.tensor].mode != 2 && !grads[bp.tensor]) return SHAMPOO_E_ARG;
+    if (!h->sos.empty() && !sparse) return SHAMPOO_E_ARG;
+    for (const SosPlan& sp : h->sos) {
+        const shampoo_sparse_rows& sr = sparse[sp.tensor];
+        if (sr.n_rows < 0 || sr.n_rows > h->tensors[sp.tensor].rows) return SHAMPOO_E_ARG;
+        if (sr.n_rows > 0 && (!sr.rows || !sr.row_grads)) return SHAMPOO_E_ARG;
+    }
     return SHAMPOO_OK;
 }
 
@@ -1150,24 +1232,32 @@ int check_apply_args(const shampoo_s* h, float* const* params, const float* cons
         if (h->tensors[t].mode != 2 && !grads[t]) return SHAMPOO_E_ARG;
     }
     if (h->n_sparse > 0 && !sparse) return SHAMPOO_E_ARG;
+    for (const SosPlan& sp : h->sos) {
+        const shampoo_sparse_rows& sr = sparse[sp.tensor];
+        if (sr.n_rows < 0 || sr.n_rows > h->tensors[sp.tensor].rows) return SHAMPOO_E_ARG;
+        if (sr.n_rows > 0 && (!sr.rows || !sr.row_grads)) return SHAMPOO_E_ARG;
+    }
     return SHAMPOO_OK;
 }
 
 int enqueue_apply(shampoo_s* h, float* const* params, const shampoo_sparse_rows* sparse,
                   hipStream_t s, bool fused_small);
+int enqueue_sos_apply(shampoo_s* h, float* const* params, const shampoo_sparse_rows* sparse,
+                      hipStream_t s);
 }  // namespace
 
 extern "C" {
 
-int shampoo_update_stats(shampoo_t* h, const float* const* grads, void* stream) {
+int shampoo_update_stats(shampoo_t* h, const float* const* grads,
+                         const shampoo_sparse_rows* sparse, void* stream) {
     if (!h || !grads) return SHAMPOO_E_ARG;
     if (!h->bound) return SHAMPOO_E_STATE;
-    int rc = check_stats_args(h, grads);
+    int rc = check_stats_args(h, grads, sparse);
     if (rc) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    rc = refresh_bases(h, grads, nullptr, s);
+    rc = refresh_bases(h, grads, nullptr, sparse, s);
     if (rc) return rc;
-    return enqueue_stats(h, s, false);
+    return enqueue_stats(h, s, false, sparse);
 }
 
 namespace {
@@ -1198,7 +1288,7 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
             // up to 128 in one kernel
             FusedArgs fa{};
             fa.p = p;
-            fa.iters = h->cfg.newton_iters;
+            fa.iters = ch.iters;
             fa.steps_s = h->cfg.lanczos_steps > 0 ? h->cfg.lanczos_steps : 20;
             fa.steps_p = h->cfg.lanczos_steps > 0 ? std::min(h->cfg.lanczos_steps, 8) : 8;
             fa.auto_route = h->cfg.root_mode == SHAMPOO_ROOT_AUTO ? 1 : 0;
@@ -1215,7 +1305,7 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
             rc = hip_err(launch_newton_init(fp64, jobs, ch.njobs, at<double>(h, 0), scratch, diag, na, s));
         }
         if (rc) return rc;
-        for (int it = 0; it < h->cfg.newton_iters; ++it) {
+        for (int it = 0; it < ch.iters; ++it) {
             for (const LaunchRef& L : ch.stages[it & 1]) {
                 const GemmTask* tk = tab<GemmTask>(h, L.tasks_off);
                 const TileRef* tl = tab<TileRef>(h, L.tiles_off);
@@ -1229,7 +1319,7 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
         ProfScope ps(h, PC_NEWTON_COMMIT, s);
         rc = hip_err(launch_newton_commit(fp64, jobs, ch.njobs, at<float>(h, 0),
                                           static_cast<unsigned char*>(scratch) +
-                                              (size_t)(h->cfg.newton_iters & 1) * ch.ld * ch.ld *
+                                              (size_t)(ch.iters & 1) * ch.ld * ch.ld *
                                                   (fp64 ? 8 : 4),
                                           diag, na, s));
         if (rc) return rc;
@@ -1366,7 +1456,7 @@ int shampoo_precondition_and_apply(shampoo_t* h, float* const* params, const flo
     int rc = check_apply_args(h, params, grads, sparse);
     if (rc) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    rc = refresh_bases(h, grads, params, s);
+    rc = refresh_bases(h, grads, params, sparse, s);
     if (rc) return rc;
     return enqueue_apply(h, params, sparse, s, false);
 }
@@ -1378,21 +1468,21 @@ int shampoo_step(shampoo_t* h, float* const* params, const float* const* grads,
     if (roots != SHAMPOO_ROOTS_NONE && roots != SHAMPOO_ROOTS_ALL && (roots < 0 || roots >= nparts))
         return SHAMPOO_E_ARG;
     if (!h->bound || (roots != SHAMPOO_ROOTS_NONE && h->async_part >= 0)) return SHAMPOO_E_STATE;
-    int rc = check_stats_args(h, grads);
+    int rc = check_stats_args(h, grads, sparse);
     if (!rc) rc = check_apply_args(h, params, grads, sparse);
     if (rc) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    rc = refresh_bases(h, grads, params, s);
+    rc = refresh_bases(h, grads, params, sparse, s);
     if (rc) return rc;
     if (roots != SHAMPOO_ROOTS_NONE) {
         // the roots need this step's statistics, the apply needs the roots
-        rc = enqueue_stats(h, s, false);
+        rc = enqueue_stats(h, s, false, sparse);
         if (!rc) rc = enqueue_roots(h, h->roots[roots == SHAMPOO_ROOTS_ALL ? 0 : 1 + roots], s);
         if (!rc) rc = enqueue_apply(h, params, sparse, s, false);
         return rc;
     }
     // no root pass: statistics and apply of each block <= 128 share one kernel
-    rc = enqueue_stats(h, s, true);
+    rc = enqueue_stats(h, s, true, sparse);
     if (!rc) rc = enqueue_apply(h, params, sparse, s, true);
     return rc;
 }
@@ -1400,6 +1490,162 @@ int shampoo_step(shampoo_t* h, float* const* params, const float* const* grads,
 }  // extern "C"
 
 namespace {
+// Sparse-row tables with one-sided preconditioning (Lemma 1, R side): the
+// statistics of this call's listed rows, S <- beta2 S + w g^T g.  The rows
+// are cut into at most kSosMaxChunks chunks of at least kSplitKMin rows;
+// each chunk's product goes to its own fp64 partial and k_sym_reduce sums
+// them in chunk order (with no rows, S only decays).  Per-call tables go
+// through the staging ring into the state buffer.
+int enqueue_sos_stats(shampoo_s* h, const shampoo_sparse_rows* sparse, hipStream_t s) {
+    std::vector<GemmTask> tasks;
+    std::vector<SymReduceJob> red;
+    std::vector<TileRef> rtiles;
+    for (const SosPlan& sp : h->sos) {
+        const FactorPlan& f = h->factors[sp.factor];
+        const TensorPlan& tp = h->tensors[sp.tensor];
+        const int64_t n = sparse[sp.tensor].n_rows;
+        int chunks = 0;
+        if (n > 0) {
+            const int want = std::min<int>(kSosMaxChunks, ceil_div(n, kSplitKMin));
+            const int64_t len = align_up(ceil_div(n, want), 32);
+            chunks = ceil_div(n, len);
+            for (int ck = 0; ck < chunks; ++ck) {
+                GemmTask t{};
+                const int64_t k0 = (int64_t)ck * len;
+                t.a_base = t.b_base = 1 + sp.tensor;   // the row gradients (n x cols)
+                t.a_off = t.b_off = k0 * tp.cols;
+                t.lda = t.ldb = (int)tp.cols;
+                t.c_base = 0;
+                t.c_off = sp.part_off / 8 + (int64_t)ck * f.ld * f.ld;
+                t.ldc = f.ld;
+                t.M = t.N = f.dim;
+                t.K = (int)std::min<int64_t>(len, n - k0);
+                t.trans = 1 | 16;
+                t.tiles_n = ceil_div(t.N, kTile);
+                t.factor = -1;
+                t.norm_slot = -1;
+                tasks.push_back(t);
+            }
+        }
+        SymReduceJob r{};
+        r.part_off = sp.part_off / 8;
+        r.s_off = f.off_s / 8;
+        r.nparts = chunks;
+        r.dim = f.dim;
+        r.ld = f.ld;
+        r.tiles = ceil_div(f.dim, 32);
+        for (int a = 0; a < r.tiles; ++a)
+            for (int b = a; b < r.tiles; ++b) rtiles.push_back({(int32_t)red.size(), a * r.tiles + b});
+        red.push_back(r);
+    }
+    Blob b;
+    const LaunchRef L = add_launch(b, tasks);
+    const int64_t o_red = b.add(red), o_rtiles = b.add(rtiles);
+    int rc = stage_upload(h, b.bytes.data(), b.bytes.size(), h->off_sos_stats, s);
+    if (rc) return rc;
+    const GemmArgs a = stats_args(h);
+    GemmArgs pa{};
+    pa.epi = EPI_STORE;
+    pa.alpha = 1.0;
+    pa.beta = 0.0;
+    ProfScope ps(h, PC_SOS_STATS, s);
+    rc = hip_err(launch_gemm_f64_from_f32(at<GemmTask>(h, h->off_sos_stats + L.tasks_off),
+                                          at<TileRef>(h, h->off_sos_stats + L.tiles_off), L.ntiles,
+                                          at<uint64_t>(h, h->off_bases), pa, s));
+    if (rc) return rc;
+    return hip_err(launch_sym_reduce(at<SymReduceJob>(h, h->off_sos_stats + o_red),
+                                     at<TileRef>(h, h->off_sos_stats + o_rtiles), (int)rtiles.size(),
+                                     at<double>(h, 0), a.alpha, a.beta, s));
+}
+
+// The apply of the sparse one-sided tables for this call: a += g*g and
+// ||A||^2 over the listed rows, D = g P_R with ||D||^2 per tile, the graft
+// scale over the table, then W_r -= lr s D_r on the listed rows.
+int enqueue_sos_apply(shampoo_s* h, float* const* params, const shampoo_sparse_rows* sparse,
+                      hipStream_t s) {
+    const shampoo_config& c = h->cfg;
+    std::vector<SosJob> jobs;
+    std::vector<GemmTask> tasks;
+    std::vector<BlockNorms> bns;
+    int chunks = 0;
+    for (const SosPlan& sp : h->sos) {
+        const TensorPlan& tp = h->tensors[sp.tensor];
+        const FactorPlan& f = h->factors[sp.factor];
+        const BlockPlan& bp = h->blocks[sp.block];
+        const shampoo_sparse_rows& sr = sparse[sp.tensor];
+        const int64_t n = sr.n_rows;
+        const int rows_per = (int)std::max<int64_t>(1, kElemChunk / tp.cols);
+        const int nch = n > 0 ? ceil_div(n, rows_per) : 0;
+        SosJob j{};
+        j.rows_ptr = reinterpret_cast<int64_t>(sr.rows);
+        j.grads_ptr = reinterpret_cast<int64_t>(sr.row_grads);
+        j.w_ptr = reinterpret_cast<int64_t>(params[sp.tensor]);
+        j.a_off = tp.off_a / 4;
+        j.d_off = tp.off_d / 4;
+        j.n_rows = n;
+        j.table_rows = tp.rows;
+        j.cols = (int)tp.cols;
+        j.chunk_rows = rows_per;
+        j.first_chunk = chunks;
+        j.slot_a = bp.a_slot;
+        j.block = sp.block;
+        j.vec = (tp.cols % 4 == 0) && ((reinterpret_cast<uintptr_t>(sr.row_grads) & 15) == 0) &&
+                ((reinterpret_cast<uintptr_t>(params[sp.tensor]) & 15) == 0);
+        jobs.push_back(j);
+        chunks += nch;
+        int d_tiles = 0;
+        if (n > 0) {
+            GemmTask u{};
+            u.a_base = 1 + sp.tensor; u.a_off = 0; u.lda = (int)tp.cols;   // g (n x cols)
+            u.b_base = 0; u.b_off = f.off_p / 4; u.ldb = f.ld;
+            u.c_base = 0; u.c_off = tp.off_d / 4; u.ldc = (int)tp.cols;
+            u.M = (int)n; u.N = (int)tp.cols; u.K = (int)tp.cols;
+            u.trans = 0;
+            u.tiles_n = ceil_div(u.N, kTile);
+            u.factor = -1;
+            u.norm_slot = bp.d_slot;
+            tasks.push_back(u);
+            d_tiles = ceil_div(n, kTile) * u.tiles_n;
+        }
+        bns.push_back({bp.a_slot, nch, bp.d_slot, d_tiles, sp.block, 0});
+    }
+    Blob b;
+    const int64_t o_jobs = b.add(jobs);
+    const LaunchRef L = add_launch(b, tasks);
+    const int64_t o_bn = b.add(bns);
+    int rc = stage_upload(h, b.bytes.data(), b.bytes.size(), h->off_sos_apply, s);
+    if (rc) return rc;
+    const SosJob* dj = at<SosJob>(h, h->off_sos_apply + o_jobs);
+    float* arena = at<float>(h, 0);
+    double* partA = at<double>(h, h->off_partA);
+    double* partD = at<double>(h, h->off_partD);
+    float* scale = at<float>(h, h->off_scale);
+    {
+        ProfScope ps(h, PC_SOS_NORM, s, chunks > 0);
+        rc = hip_err(launch_sos_norm(dj, (int)jobs.size(), chunks, arena, (float)c.graft_eps, partA, s));
+    }
+    if (rc) return rc;
+    GemmArgs g{};
+    g.epi = EPI_STORE;
+    g.alpha = 1.0;
+    g.norms = partD;
+    {
+        ProfScope ps(h, PC_SOS_APPLY, s, L.ntiles > 0);
+        rc = hip_err(launch_gemm_f32(at<GemmTask>(h, h->off_sos_apply + L.tasks_off),
+                                     at<TileRef>(h, h->off_sos_apply + L.tiles_off), L.ntiles,
+                                     at<uint64_t>(h, h->off_bases), g, s));
+    }
+    if (rc) return rc;
+    {
+        ProfScope ps(h, PC_SCALE, s);
+        rc = hip_err(launch_block_scale(at<BlockNorms>(h, h->off_sos_apply + o_bn), (int)bns.size(),
+                                        partA, partD, scale, s));
+    }
+    if (rc) return rc;
+    ProfScope ps(h, PC_SOS_UPDATE, s, chunks > 0);
+    return hip_err(launch_sos_update(dj, (int)jobs.size(), chunks, arena, scale, (float)c.lr, s));
+}
+
 // Apply kernels on stream s (pointer table already current).  fused_small:
 // the blocks of at most 128 x 128 go through the fused step kernel, which
 // also updates their statistics.
@@ -1449,7 +1695,7 @@ int enqueue_apply(shampoo_s* h, float* const* params, const shampoo_sparse_rows*
     if (rc) return rc;
     {
         ProfScope ps(h, PC_SCALE, s);
-        rc = hip_err(launch_block_scale(tab<BlockNorms>(h, h->blocknorms_off), (int)h->blocks.size(),
+        rc = hip_err(launch_block_scale(tab<BlockNorms>(h, h->blocknorms_off), h->n_blocknorms,
                                         partA, partD, scale, s));
     }
     if (rc) return rc;
@@ -1459,12 +1705,16 @@ int enqueue_apply(shampoo_s* h, float* const* params, const shampoo_sparse_rows*
                                    arena, scale, ua, s));
     }
     if (rc) return rc;
+    if (!h->sos.empty()) {
+        rc = enqueue_sos_apply(h, params, sparse, s);
+        if (rc) return rc;
+    }
     if (h->n_sparse > 0) {
         std::vector<SparseJob> jobs;
         int64_t items = 0;
         for (int t = 0; t < h->n; ++t) {
             const TensorPlan& tp = h->tensors[t];
-            if (tp.mode != 2) continue;
+            if (tp.mode != 2 || tp.os_side >= 0) continue;
             const shampoo_sparse_rows& sr = sparse[t];
             if (sr.n_rows < 0 || sr.n_rows > tp.rows) return SHAMPOO_E_ARG;
             if (sr.n_rows == 0) continue;

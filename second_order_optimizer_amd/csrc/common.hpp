@@ -134,6 +134,8 @@ struct BlockChunk {
 struct BlockNorms {
     int32_t a_first, a_count;  // partial ||A_b||^2 slots
     int32_t d_first, d_count;  // partial ||D_b||^2 slots
+    int32_t block;             // graft scale index (the block)
+    int32_t pad_;
 };
 
 // One sparse table of one call.
@@ -146,6 +148,25 @@ struct SparseJob {
     int64_t first_item;   // prefix over jobs of n_rows * (cols / 4 or cols)
     int64_t table_rows;   // rows of the table (row ids outside [0, table_rows) are skipped)
     int32_t cols;
+    int32_t vec;          // 1: float4 path
+};
+
+// One sparse-row table with one-sided preconditioning, for one call: its
+// listed rows are processed in chunks of chunk_rows rows, one workgroup each
+// (chunks of all tables numbered consecutively from first_chunk).
+struct SosJob {
+    int64_t rows_ptr;     // const int32_t*: listed row ids (distinct)
+    int64_t grads_ptr;    // const float*: n_rows x cols row gradients g
+    int64_t w_ptr;        // float*: the table's weights
+    int64_t a_off;        // Adagrad accumulator of the table (arena floats)
+    int64_t d_off;        // D = g P, n_rows x cols (arena floats)
+    int64_t n_rows;
+    int64_t table_rows;   // row ids outside [0, table_rows) are skipped
+    int32_t cols;
+    int32_t chunk_rows;
+    int32_t first_chunk;
+    int32_t slot_a;       // first ||A||^2 partial slot (one per chunk)
+    int32_t block;        // graft scale index (the table's block)
     int32_t vec;          // 1: float4 path
 };
 

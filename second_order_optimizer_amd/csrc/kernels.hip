@@ -19,6 +19,9 @@
 //                    coupled-Newton iteration.
 //   k_sym_reduce     fixed-order sum of split-K partial statistics (one-sided
 //                    preconditioning of a large layer) into S, both triangles.
+//   k_sos_norm / k_sos_update  sparse-row tables with one-sided
+//                    preconditioning: accumulator and ||A||^2 over the listed
+//                    rows; W_r -= lr s D_r on those rows.
 //   k_adagrad_norm   a <- a + G*G on Shampoo blocks and ||A_b||^2 partials.
 //   k_block_scale    graft factor ||A_b|| / ||D_b|| per block.
 //   k_update         momentum and weight update (and dense Adagrad fallback).
@@ -1867,7 +1870,7 @@ __global__ __launch_bounds__(256) void k_block_scale(const BlockNorms* __restric
     for (int k = l; k < q.d_count; k += 64) nd += partD[q.d_first + k];
     na = wave_sum(na);
     nd = wave_sum(nd);
-    if (l == 0) scale[b] = nd > 0.0 ? (float)sqrt(na / nd) : 0.f;
+    if (l == 0) scale[q.block] = nd > 0.0 ? (float)sqrt(na / nd) : 0.f;
 }
 
 // ================================================== elementwise: update
@@ -1934,6 +1937,105 @@ __global__ __launch_bounds__(256) void k_update(const RowChunk* __restrict__ chu
             const float m = b1 * mom[idx] + u;
             mom[idx] = m;
             W[idx] -= lr * m;
+        }
+    }
+}
+
+// ============================= sparse-row tables, one-sided preconditioning
+// The job of workgroup `chunk`: the last job whose first chunk is <= chunk
+// (a handful of tables per call: a linear scan over the small table).
+__device__ __forceinline__ int sos_job_of(const SosJob* __restrict__ jobs, int njobs, int chunk) {
+    int j = 0;
+    while (j + 1 < njobs && jobs[j + 1].first_chunk <= chunk) ++j;
+    return j;
+}
+
+// On one chunk of a table's listed rows: a_r <- a_r + g*g and the partial
+// ||A||^2 of A = g / (sqrt(a_r) + delta) (fixed order per chunk).
+__global__ __launch_bounds__(256) void k_sos_norm(const SosJob* __restrict__ jobs, int njobs,
+                                                 float* __restrict__ arena, float delta,
+                                                 double* __restrict__ partA) {
+    __shared__ double red[4];
+    const SosJob jb = jobs[sos_job_of(jobs, njobs, blockIdx.x)];
+    const int c = blockIdx.x - jb.first_chunk;
+    const int64_t i0 = (int64_t)c * jb.chunk_rows;
+    const int64_t i1 = i0 + jb.chunk_rows < jb.n_rows ? i0 + jb.chunk_rows : jb.n_rows;
+    const int32_t* rows = reinterpret_cast<const int32_t*>(jb.rows_ptr);
+    const float* G = reinterpret_cast<const float*>(jb.grads_ptr);
+    float* a = arena + jb.a_off;
+    const int cols = jb.cols;
+    double acc = 0.0;
+    if (jb.vec) {
+        const int c4 = cols / 4;
+        const int64_t total = (i1 - i0) * c4;
+        for (int64_t e = threadIdx.x; e < total; e += 256) {
+            const int64_t i = i0 + e / c4;
+            const int q = (int)(e % c4);
+            const int64_t r = rows[i];
+            if (r < 0 || r >= jb.table_rows) continue;
+            const float4 g = reinterpret_cast<const float4*>(G + i * cols)[q];
+            float4* ap = reinterpret_cast<float4*>(a + r * cols) + q;
+            float4 av = *ap;
+            av.x += g.x * g.x; av.y += g.y * g.y; av.z += g.z * g.z; av.w += g.w * g.w;
+            *ap = av;
+            const float A0 = g.x / (sqrtf(av.x) + delta), A1 = g.y / (sqrtf(av.y) + delta);
+            const float A2 = g.z / (sqrtf(av.z) + delta), A3 = g.w / (sqrtf(av.w) + delta);
+            acc += (double)(A0 * A0 + A1 * A1) + (double)(A2 * A2 + A3 * A3);
+        }
+    } else {
+        const int64_t total = (i1 - i0) * cols;
+        for (int64_t e = threadIdx.x; e < total; e += 256) {
+            const int64_t i = i0 + e / cols;
+            const int q = (int)(e % cols);
+            const int64_t r = rows[i];
+            if (r < 0 || r >= jb.table_rows) continue;
+            const float g = G[i * cols + q];
+            const float av = a[r * cols + q] + g * g;
+            a[r * cols + q] = av;
+            const float A = g / (sqrtf(av) + delta);
+            acc += (double)(A * A);
+        }
+    }
+    const double s = block_sum_256(acc, red);
+    if (threadIdx.x == 0) partA[jb.slot_a + c] = s;
+}
+
+// W_r <- W_r - lr s D_i for the listed rows (s the table's graft scale; no
+// momentum, so rows that are not listed are not touched).
+__global__ __launch_bounds__(256) void k_sos_update(const SosJob* __restrict__ jobs, int njobs,
+                                                   const float* __restrict__ arena,
+                                                   const float* __restrict__ scale, float lr) {
+    const SosJob jb = jobs[sos_job_of(jobs, njobs, blockIdx.x)];
+    const int c = blockIdx.x - jb.first_chunk;
+    const int64_t i0 = (int64_t)c * jb.chunk_rows;
+    const int64_t i1 = i0 + jb.chunk_rows < jb.n_rows ? i0 + jb.chunk_rows : jb.n_rows;
+    const int32_t* rows = reinterpret_cast<const int32_t*>(jb.rows_ptr);
+    const float* D = arena + jb.d_off;
+    float* W = reinterpret_cast<float*>(jb.w_ptr);
+    const float s = scale[jb.block];
+    const int cols = jb.cols;
+    if (jb.vec) {
+        const int c4 = cols / 4;
+        const int64_t total = (i1 - i0) * c4;
+        for (int64_t e = threadIdx.x; e < total; e += 256) {
+            const int64_t i = i0 + e / c4;
+            const int q = (int)(e % c4);
+            const int64_t r = rows[i];
+            if (r < 0 || r >= jb.table_rows) continue;
+            const float4 d = reinterpret_cast<const float4*>(D + i * cols)[q];
+            float4* wp = reinterpret_cast<float4*>(W + r * cols) + q;
+            float4 w = *wp;
+            w.x -= lr * (s * d.x); w.y -= lr * (s * d.y); w.z -= lr * (s * d.z); w.w -= lr * (s * d.w);
+            *wp = w;
+        }
+    } else {
+        const int64_t total = (i1 - i0) * cols;
+        for (int64_t e = threadIdx.x; e < total; e += 256) {
+            const int64_t i = i0 + e / cols;
+            const int q = (int)(e % cols);
+            const int64_t r = rows[i];
+            if (r < 0 || r >= jb.table_rows) continue;
+            W[r * cols + q] -= lr * (s * D[i * cols + q]);
         }
     }
 }
@@ -2090,6 +2192,18 @@ hipError_t launch_sym_reduce(const SymReduceJob* jobs, const TileRef* tiles, int
                              double* arena, double alpha, double beta, hipStream_t s) {
     if (ntiles <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_sym_reduce, dim3(ntiles), dim3(256), 0, s, jobs, tiles, arena, alpha, beta);
+    return hipGetLastError();
+}
+hipError_t launch_sos_norm(const SosJob* jobs, int njobs, int nchunks, float* arena, float delta,
+                           double* partA, hipStream_t s) {
+    if (nchunks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_sos_norm, dim3(nchunks), dim3(256), 0, s, jobs, njobs, arena, delta, partA);
+    return hipGetLastError();
+}
+hipError_t launch_sos_update(const SosJob* jobs, int njobs, int nchunks, float* arena,
+                             const float* scale, float lr, hipStream_t s) {
+    if (nchunks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_sos_update, dim3(nchunks), dim3(256), 0, s, jobs, njobs, arena, scale, lr);
     return hipGetLastError();
 }
 hipError_t launch_set_identity(const FactorJob* jobs, int njobs, float* arena, hipStream_t s) {

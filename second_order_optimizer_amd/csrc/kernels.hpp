@@ -81,6 +81,10 @@ hipError_t launch_apply128(const ApplyJob* jobs, int njobs, const uint64_t* base
                            float delta, double* partA, double* partD, const UpdateArgs& ua,
                            hipStream_t s);
 hipError_t launch_copy_jobs(const CopyJob* jobs, int njobs, unsigned char* arena, hipStream_t s);
+hipError_t launch_sos_norm(const SosJob* jobs, int njobs, int nchunks, float* arena, float delta,
+                           double* partA, hipStream_t s);
+hipError_t launch_sos_update(const SosJob* jobs, int njobs, int nchunks, float* arena,
+                             const float* scale, float lr, hipStream_t s);
 hipError_t launch_sym_reduce(const SymReduceJob* jobs, const TileRef* tiles, int ntiles,
                              double* arena, double alpha, double beta, hipStream_t s);
 hipError_t launch_set_identity(const FactorJob* jobs, int njobs, float* arena, hipStream_t s);

@@ -73,7 +73,7 @@ SIGNATURES = {
                                       ctypes.POINTER(TensorDesc), ctypes.POINTER(_P)]),
     "shampoo_state_bytes": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_size_t)]),
     "shampoo_bind_state": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
-    "shampoo_update_stats": (ctypes.c_int, [_P, ctypes.POINTER(_P), _P]),
+    "shampoo_update_stats": (ctypes.c_int, [_P, ctypes.POINTER(_P), ctypes.POINTER(SparseRows), _P]),
     "shampoo_compute_inverse_roots": (ctypes.c_int, [_P, _P]),
     "shampoo_compute_inverse_roots_part": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
     "shampoo_roots_async_begin": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
@@ -233,9 +233,12 @@ class Shampoo(Plan):
             arr[i] = t.data_ptr()
         return arr
 
-    def update_stats(self, grads):
+    def update_stats(self, grads, sparse=None):
+        """sparse: as in precondition_and_apply; read for sparse-row tables
+        with one-sided preconditioning (large_layer)."""
         arr = self._ptrs(grads, lambda k: False, "grads")
-        _check(lib().shampoo_update_stats(self.h, arr, self._stream()), "shampoo_update_stats")
+        sp, _keep = self._sparse_args(sparse)
+        _check(lib().shampoo_update_stats(self.h, arr, sp, self._stream()), "shampoo_update_stats")
 
     def compute_inverse_roots(self):
         _check(lib().shampoo_compute_inverse_roots(self.h, self._stream()),
@@ -248,6 +251,10 @@ class Shampoo(Plan):
     def _apply_args(self, params, grads, sparse):
         pa = self._ptrs(params, lambda k: True, "params")
         ga = self._ptrs(grads, lambda k: k == DENSE, "grads")
+        sp, keep = self._sparse_args(sparse)
+        return pa, ga, sp, keep
+
+    def _sparse_args(self, sparse):
         sp = None
         keep = []
         if any(k == SPARSE_ROWS for _, _, k in self.shapes):
@@ -262,7 +269,7 @@ class Shampoo(Plan):
                     raise ValueError(f"sparse[{i}] must be (int32 rows, fp32 rows x {c})")
                 keep.append((rows, g))
                 sp[i] = SparseRows(rows.data_ptr(), g.data_ptr(), rows.numel())
-        return pa, ga, sp, keep
+        return sp, keep
 
     def precondition_and_apply(self, params, grads, sparse=None):
         """sparse: dict tensor index -> (int32 rows, fp32 row grads) device tensors."""
@@ -298,12 +305,12 @@ class Shampoo(Plan):
         if self.async_roots:
             if sel >= 0:
                 self.roots_async_end()
-            self.update_stats(grads)
+            self.update_stats(grads, sparse)
             self.precondition_and_apply(params, grads, sparse)
             if sel >= 0:
                 self.roots_async_begin(sel)
             return
-        self.update_stats(grads)
+        self.update_stats(grads, sparse)
         if sel == ROOTS_ALL:
             self.compute_inverse_roots()
         elif sel >= 0:

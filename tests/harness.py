@@ -81,7 +81,7 @@ class GpuRun:
         if self.opt.async_roots:
             self.opt.step_separate(self.params, grads_dev, step, cad, sparse)
             return
-        self.opt.update_stats(grads_dev)
+        self.opt.update_stats(grads_dev, sparse)
         if roots is not None:
             sel = S.ROOTS_ALL if roots else S.ROOTS_NONE
         else:

@@ -66,7 +66,7 @@ def test_strerror_and_argument_errors():
     # calls on an unbound handle
     p = S.Plan([(8, 8, 0)], cfg)
     arr = (S._P * 1)()
-    assert L.shampoo_update_stats(p.h, arr, None) == -2
+    assert L.shampoo_update_stats(p.h, arr, None, None) == -2
     assert L.shampoo_compute_inverse_roots(p.h, None) == -2
     assert L.shampoo_step(p.h, arr, arr, None, S.ROOTS_NONE, None) == -2
     assert L.shampoo_step(p.h, None, arr, None, S.ROOTS_ALL, None) == -1
@@ -82,7 +82,7 @@ def test_strerror_and_argument_errors():
     c = S.make_config(4)
     c.root_parts = -1
     assert L.shampoo_create(ctypes.byref(c), 1, descs, ctypes.byref(h)) == -1
-    assert L.shampoo_update_stats(p.h, None, None) == -1
+    assert L.shampoo_update_stats(p.h, None, None, None) == -1
     p.close()
 
 
@@ -124,7 +124,8 @@ def test_planner_matches_oracle_partition(wid):
 @pytest.mark.parametrize("large_layer", [0, 1])
 def test_state_regions_do_not_overlap(large_layer):
     """Every byte range the layout hands out is disjoint and inside the state
-    (with large_layer, the 5000 x 64 tensor is a one-sided block)."""
+    (with large_layer, the 5000 x 64 tensor and the sparse table are
+    one-sided blocks)."""
     T = synth.TensorSpec
     wl = synth.Workload(90, "mix", [T("a", 300, 200), T("b", 64, 147), T("e", 5000, 64),
                                    T("s", 1000, 32, kind="sparse")], 128, max_precond_dim=4096)
@@ -136,7 +137,8 @@ def test_state_regions_do_not_overlap(large_layer):
         spans += [(bl.off_l, bl.ld_l ** 2 * 8), (bl.off_r, bl.ld_r ** 2 * 8),
                   (bl.off_pl, bl.ld_l ** 2 * 4), (bl.off_pr, bl.ld_r ** 2 * 4),
                   (bl.off_pl64, bl.ld_l ** 2 * 8), (bl.off_pr64, bl.ld_r ** 2 * 8)]
-    assert sum(p.block(i).one_sided for i in range(p.n_blocks)) == large_layer
+    # large_layer: the 5000 x 64 tensor and the sparse table
+    assert sum(p.block(i).one_sided for i in range(p.n_blocks)) == 2 * large_layer
     spans = [(o, n) for o, n in spans if o >= 0]
     for ti, t in enumerate(wl.tensors):
         a_off, m_off, _, _ = p.tensor(ti)
@@ -166,9 +168,9 @@ def test_one_sided_plan_numbering_and_layout():
     p = S.Plan(shapes, cfg)
     n_reg = sum(len(v) for v in orc.blocks.values())
     assert n_reg == 2 * 2 + 1 * 2   # a: 2x2 blocks, b: 1x2
-    assert p.n_blocks == n_reg + 2
-    assert p.n_factors == 2 * n_reg + 2
-    expect = {0: "R", 2: "L"}
+    assert p.n_blocks == n_reg + 3
+    assert p.n_factors == 2 * n_reg + 3
+    expect = {0: "R", 2: "L", 4: "R"}   # 4: the sparse table
     for ti, side in expect.items():
         idx, st = orc.one_sided[ti]
         assert st.side == side
@@ -180,7 +182,8 @@ def test_one_sided_plan_numbering_and_layout():
         assert (bl.tensor, bl.row0, bl.col0, bl.rows, bl.cols) == (ti, 0, 0, t.rows, t.cols)
         if side == "R":
             assert bl.factor_l == -1 and bl.off_l == -1 and bl.off_pl == -1 and bl.ld_l == 0
-            assert bl.factor_r == 2 * n_reg + (idx - n_reg) and bl.ld_r == 96
+            assert bl.factor_r == 2 * n_reg + (idx - n_reg)
+            assert bl.ld_r == (96 if ti == 0 else 32)
         else:
             assert bl.factor_r == -1 and bl.off_r == -1 and bl.off_pr == -1 and bl.ld_r == 0
             assert bl.factor_l == 2 * n_reg + (idx - n_reg) and bl.ld_l == 128
