@@ -30,9 +30,10 @@ constexpr int kFactorPad = 32;        // factor matrices padded to a multiple of
 constexpr int64_t kElemChunk = 16384; // elements per workgroup in elementwise kernels
 constexpr int kRingSlots = 16;        // pinned staging slots for per-call tables
 constexpr size_t kNewtonScratchBudget = size_t(4) << 30;  // bytes per precision
-constexpr int kSplitKTiles = 1024;    // one-sided statistics: target tiles per launch
-constexpr int kSplitKMin = 256;       // and shortest chunk of the long dimension
-constexpr int kSosMaxChunks = 64;     // sparse one-sided tables: split-K chunks per call, at most
+constexpr int kSplitKTiles = 512;     // one-sided statistics: target tiles per launch
+constexpr int kSplitKMin = 512;       // and shortest chunk of the long dimension
+constexpr int kSosMaxChunks = 64;     // sparse one-sided tables: split-K chunks per call, at most,
+constexpr int kSosMinRows = 256;      // of at least this many listed rows (measured best)
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -1492,7 +1493,7 @@ int shampoo_step(shampoo_t* h, float* const* params, const float* const* grads,
 namespace {
 // Sparse-row tables with one-sided preconditioning (Lemma 1, R side): the
 // statistics of this call's listed rows, S <- beta2 S + w g^T g.  The rows
-// are cut into at most kSosMaxChunks chunks of at least kSplitKMin rows;
+// are cut into at most kSosMaxChunks chunks of at least kSosMinRows rows;
 // each chunk's product goes to its own fp64 partial and k_sym_reduce sums
 // them in chunk order (with no rows, S only decays).  Per-call tables go
 // through the staging ring into the state buffer.
@@ -1506,7 +1507,7 @@ int enqueue_sos_stats(shampoo_s* h, const shampoo_sparse_rows* sparse, hipStream
         const int64_t n = sparse[sp.tensor].n_rows;
         int chunks = 0;
         if (n > 0) {
-            const int want = std::min<int>(kSosMaxChunks, ceil_div(n, kSplitKMin));
+            const int want = std::min<int>(kSosMaxChunks, ceil_div(n, kSosMinRows));
             const int64_t len = align_up(ceil_div(n, want), 32);
             chunks = ceil_div(n, len);
             for (int ck = 0; ck < chunks; ++ck) {

@@ -216,18 +216,14 @@ template <> struct WaveTile<float> {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     }
-    template <typename F>
-    __device__ __forceinline__ void for_each(int wm, int wn, F&& f) const {
+    // accumulator value idx = (2 i + j) 16 + v and its place (r, c) in the tile
+    static constexpr int NV = 64;
+    __device__ __forceinline__ float get(int idx, int wm, int wn, int& r, int& c) const {
         const int lane = threadIdx.x & 63;
-        const int h = lane >> 5, c = lane & 31;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    f(wm * 64 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3), wn * 64 + j * 32 + c,
-                      acc[i][j][v]);
+        const int i = idx >> 5, j = (idx >> 4) & 1, v = idx & 15;
+        r = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        c = wn * 64 + j * 32 + (lane & 31);
+        return acc[i][j][v];
     }
 };
 
@@ -263,24 +259,21 @@ template <> struct WaveTile<double> {
                     acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     }
-    template <typename F>
-    __device__ __forceinline__ void for_each(int wm, int wn, F&& f) const {
+    // accumulator value idx = (4 i + j) 4 + v and its place (r, c) in the tile
+    static constexpr int NV = 64;
+    __device__ __forceinline__ double get(int idx, int wm, int wn, int& r, int& c) const {
         const int lane = threadIdx.x & 63;
-        const int g = lane >> 4, c = lane & 15;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    f(wm * 64 + i * 16 + g + 4 * v, wn * 64 + j * 16 + c, acc[i][j][v]);
+        const int i = idx >> 4, j = (idx >> 2) & 3, v = idx & 3;
+        r = wm * 64 + i * 16 + (lane >> 4) + 4 * v;
+        c = wn * 64 + j * 16 + (lane & 15);
+        return acc[i][j][v];
     }
 };
 
 // C (type T) = alpha op(A) op(B) (+ beta C); A, B stored as TA, TB and
 // converted to T on the way into LDS (fp32 gradients into an fp64 product are
 // exact: fp32 x fp32 fits the fp64 mantissa).
-template <typename T, typename TA, typename TB, int MINW>
+template <typename T, typename TA, typename TB, int MINW, bool AXPBY>
 __global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__ tasks,
                                              const TileRef* __restrict__ tiles,
                                              const uint64_t* __restrict__ bases, GemmArgs args) {
@@ -332,22 +325,43 @@ __global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__
     }
 
     const T alpha = T(args.alpha), beta = T(args.beta);
-    const bool axpby = args.epi == EPI_AXPBY;
+    constexpr bool axpby = AXPBY;   // the launcher picks it from args.epi
     // symmetric result computed on upper tiles only: an off-diagonal tile
     // also writes its transpose
     const bool mirror = ((tk.trans >> 5) & 1) && ti != tj;
+    // in groups of 16 values: the old C values of a group are all loaded
+    // before its stores (a store may alias a later load as far as the
+    // compiler knows, so one element at a time would serialize the round
+    // trips); mirrored values land in the transposed tile, which no
+    // workgroup reads
     double nrm = 0.0;
-    wt.for_each(wm, wn, [&](int r, int c, T v) {
-        const int i = i0 + r, j = j0 + c;
-        if (i < tk.M && j < tk.N) {
-            T* p = C + (int64_t)i * tk.ldc + j;
-            T o = alpha * v;
-            if (axpby) o += beta * (*p);
-            *p = o;
-            if (mirror) C[(int64_t)j * tk.ldc + i] = o;
-            nrm += double(o) * double(o);
+    constexpr int NV = WaveTile<T>::NV, GRP = 16;
+#pragma unroll
+    for (int g0 = 0; g0 < NV; g0 += GRP) {
+        T old[GRP];
+        if constexpr (axpby) {
+#pragma unroll
+            for (int e = 0; e < GRP; ++e) {
+                int r, c;
+                (void)wt.get(g0 + e, wm, wn, r, c);
+                const int i = i0 + r, j = j0 + c;
+                old[e] = (i < tk.M && j < tk.N) ? C[(int64_t)i * tk.ldc + j] : T(0);
+            }
         }
-    });
+#pragma unroll
+        for (int e = 0; e < GRP; ++e) {
+            int r, c;
+            const T v = wt.get(g0 + e, wm, wn, r, c);
+            const int i = i0 + r, j = j0 + c;
+            if (i < tk.M && j < tk.N) {
+                T o = alpha * v;
+                if constexpr (axpby) o += beta * old[e];
+                C[(int64_t)i * tk.ldc + j] = o;
+                if (mirror) C[(int64_t)j * tk.ldc + i] = o;
+                nrm += double(o) * double(o);
+            }
+        }
+    }
     if (tk.norm_slot >= 0 && args.norms) {
         const double s = block_sum_256(nrm, red);
         if (threadIdx.x == 0) args.norms[tk.norm_slot + tr.tile] = s;
@@ -2086,22 +2100,34 @@ __global__ __launch_bounds__(256) void k_sparse_rows(const SparseJob* __restrict
 hipError_t launch_gemm_f32(const GemmTask* tasks, const TileRef* tiles, int ntiles,
                            const uint64_t* bases, const GemmArgs& a, hipStream_t s) {
     if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL((k_gemm<float, float, float, 1>), dim3(ntiles), dim3(256), 0, s, tasks, tiles,
-                       bases, a);
+    if (a.epi == EPI_AXPBY)
+        hipLaunchKernelGGL((k_gemm<float, float, float, 1, true>), dim3(ntiles), dim3(256), 0, s,
+                           tasks, tiles, bases, a);
+    else
+        hipLaunchKernelGGL((k_gemm<float, float, float, 1, false>), dim3(ntiles), dim3(256), 0, s,
+                           tasks, tiles, bases, a);
     return hipGetLastError();
 }
 hipError_t launch_gemm_f64(const GemmTask* tasks, const TileRef* tiles, int ntiles,
                            const uint64_t* bases, const GemmArgs& a, hipStream_t s) {
     if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL((k_gemm<double, double, double, 2>), dim3(ntiles), dim3(256), 0, s, tasks,
-                       tiles, bases, a);
+    if (a.epi == EPI_AXPBY)
+        hipLaunchKernelGGL((k_gemm<double, double, double, 2, true>), dim3(ntiles), dim3(256), 0, s,
+                           tasks, tiles, bases, a);
+    else
+        hipLaunchKernelGGL((k_gemm<double, double, double, 2, false>), dim3(ntiles), dim3(256), 0, s,
+                           tasks, tiles, bases, a);
     return hipGetLastError();
 }
 hipError_t launch_gemm_f64_from_f32(const GemmTask* tasks, const TileRef* tiles, int ntiles,
                                     const uint64_t* bases, const GemmArgs& a, hipStream_t s) {
     if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL((k_gemm<double, float, float, 2>), dim3(ntiles), dim3(256), 0, s, tasks,
-                       tiles, bases, a);
+    if (a.epi == EPI_AXPBY)
+        hipLaunchKernelGGL((k_gemm<double, float, float, 2, true>), dim3(ntiles), dim3(256), 0, s,
+                           tasks, tiles, bases, a);
+    else
+        hipLaunchKernelGGL((k_gemm<double, float, float, 2, false>), dim3(ntiles), dim3(256), 0, s,
+                           tasks, tiles, bases, a);
     return hipGetLastError();
 }
 hipError_t launch_gram128(const GramJob* jobs, int njobs, const uint64_t* bases, double* stats,
