@@ -27,6 +27,7 @@ namespace {
 
 constexpr int kTile = 128;            // batched-GEMM tile edge
 constexpr int kFactorPad = 32;        // factor matrices padded to a multiple of this
+constexpr int kXcds = 8;              // MI355X: 8 XCDs, workgroup b dispatched to XCD b % 8
 constexpr int64_t kElemChunk = 16384; // elements per workgroup in elementwise kernels
 constexpr int kRingSlots = 16;        // pinned staging slots for per-call tables
 constexpr size_t kNewtonScratchBudget = size_t(4) << 30;  // bytes per precision
@@ -216,15 +217,53 @@ int newton_stage_count(int p) {  // GEMM launches per iteration
     return s + 1;                  // M <- T^p M
 }
 
-LaunchRef add_launch(Blob& blob, const std::vector<GemmTask>& tasks) {
-    std::vector<TileRef> tiles;
+// The tile table of one batched-GEMM launch, in dispatch order.  Workgroup b
+// runs on XCD b % 8, and each XCD has its own L2; the tiles of one task
+// share its A and B panels.  So whole tasks go to XCDs (in order, each to the
+// least-loaded one by tiles x K, which balances uneven tasks and spreads the
+// tasks of a gated launch), the per-XCD counts are evened out by moving tail
+// tiles, and the lists are interleaved: entry 8k + x is XCD x's k-th tile.
+std::vector<TileRef> xcd_tile_order(const std::vector<GemmTask>& tasks) {
+    std::vector<std::vector<TileRef>> lists(kXcds);
+    std::vector<double> load(kXcds, 0.0);
+    size_t n = 0;
     for (size_t i = 0; i < tasks.size(); ++i) {
         const int nt = ceil_div(tasks[i].M, kTile) * tasks[i].tiles_n;
         const bool upper = (tasks[i].trans >> 4) & 1;
+        const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+        const size_t before = lists[x].size();
         for (int t = 0; t < nt; ++t)
             if (!upper || t / tasks[i].tiles_n <= t % tasks[i].tiles_n)
-                tiles.push_back({(int32_t)i, t});
+                lists[x].push_back({(int32_t)i, t});
+        n += lists[x].size() - before;
+        load[x] += (double)(lists[x].size() - before) * std::max(tasks[i].K, 1);
     }
+    const size_t q = n / kXcds, r = n % kXcds;
+    std::vector<TileRef> pool;
+    for (int x = 0; x < kXcds; ++x) {
+        const size_t want = q + ((size_t)x < r ? 1 : 0);
+        while (lists[x].size() > want) {
+            pool.push_back(lists[x].back());
+            lists[x].pop_back();
+        }
+    }
+    for (int x = 0; x < kXcds; ++x) {
+        const size_t want = q + ((size_t)x < r ? 1 : 0);
+        while (lists[x].size() < want) {
+            lists[x].push_back(pool.back());
+            pool.pop_back();
+        }
+    }
+    std::vector<TileRef> tiles;
+    tiles.reserve(n);
+    for (size_t k = 0; k <= q; ++k)
+        for (int x = 0; x < kXcds; ++x)
+            if (k < lists[x].size()) tiles.push_back(lists[x][k]);
+    return tiles;
+}
+
+LaunchRef add_launch(Blob& blob, const std::vector<GemmTask>& tasks) {
+    const std::vector<TileRef> tiles = xcd_tile_order(tasks);
     LaunchRef L;
     L.tasks_off = blob.add(tasks);
     L.tiles_off = blob.add(tiles);
