@@ -67,9 +67,18 @@ __device__ __forceinline__ double block_max_256(double v, double* red) {
     return fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
 }
 
+// A pointer from the per-call pointer table, cast through the global address
+// space so that the compiler emits global (not flat) memory instructions:
+// flat loads also count against the LDS wait counter, so an LDS wait would
+// stall on them.
+template <typename T>
+__device__ __forceinline__ T* global_ptr(uint64_t addr) {
+    typedef __attribute__((address_space(1))) T gT;
+    return (T*)reinterpret_cast<gT*>(addr);
+}
 template <typename T>
 __device__ __forceinline__ T* base_ptr(const uint64_t* bases, int b, int64_t off) {
-    return reinterpret_cast<T*>(bases[b]) + off;
+    return global_ptr<T>(bases[b]) + off;
 }
 
 // ============================================================ batched GEMM
@@ -94,8 +103,10 @@ template <> struct Vec16<double> { using type = double2; };
 // Loads one BK-deep stage of op(X) (rows [r0, r0+128) x k [k0, k0+BK)) into
 // registers, converting the stored type TI to the compute type T.  `kcontig`:
 // X is stored with k contiguous (X[r*ld + k]); otherwise r contiguous
-// (X[k*ld + r]).  Out-of-range elements are zero.  The optional transform
-// (Newton operand) maps the value v at op-index (r, k) to c2 v + c1 [r == k].
+// (X[k*ld + r]).  Out-of-range elements are zero; a stage wholly in range
+// takes a path without checks.  The optional transform (Newton operand) maps
+// the value v at op-index (r, k) to c2 v + c1 [r == k], the diagonal term
+// only on stages that meet the diagonal.
 template <typename T, typename TI>
 struct StageLoader {
     static constexpr int BK = GemmTraits<T>::BK;
@@ -107,26 +118,51 @@ struct StageLoader {
                                          int r0, int k0, int R, int K, bool aligned,
                                          bool xf, T c1, T c2) {
         const int t = threadIdx.x;
+        // uniform over the workgroup: the whole stage is in range (no checks),
+        // and whether it meets the diagonal r == k
+        const bool full = aligned && r0 + BM <= R && k0 + BK <= K;
+        const bool dg = xf && k0 < r0 + BM && r0 < k0 + BK;
         if (kcontig) {
             // 8 threads x VEC cover BK along k; 32 rows per pass, 4 passes.
             const int kq = t & 7, rr = t >> 3;
+            if (full) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int r = r0 + rr + 32 * p;
-                const int k = k0 + kq * VEC;
-                if (aligned && r < R && k + VEC <= K) {
-                    const vec_t q = *reinterpret_cast<const vec_t*>(X + (int64_t)r * ld + k);
+                for (int p = 0; p < 4; ++p) {
+                    const vec_t q = *reinterpret_cast<const vec_t*>(
+                        X + (int64_t)(r0 + rr + 32 * p) * ld + k0 + kq * VEC);
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) v[p][e] = T(q[e]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        v[p][e] = (r < R && k + e < K) ? T(X[(int64_t)r * ld + k + e]) : T(0);
                 }
-                if (xf) {
+            } else {
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        v[p][e] = c2 * v[p][e] + ((r == k + e && r < R && k + e < K) ? c1 : T(0));
+                for (int p = 0; p < 4; ++p) {
+                    const int r = r0 + rr + 32 * p;
+                    const int k = k0 + kq * VEC;
+                    if (aligned && r < R && k + VEC <= K) {
+                        const vec_t q = *reinterpret_cast<const vec_t*>(X + (int64_t)r * ld + k);
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) v[p][e] = T(q[e]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e)
+                            v[p][e] = (r < R && k + e < K) ? T(X[(int64_t)r * ld + k + e]) : T(0);
+                    }
+                }
+            }
+            if (xf) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) v[p][e] *= c2;
+                if (dg) {
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const int r = r0 + rr + 32 * p;
+                        const int k = k0 + kq * VEC;
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e)
+                            if (r == k + e && r < R && k + e < K) v[p][e] += c1;
+                    }
                 }
             }
         } else {
@@ -134,23 +170,44 @@ struct StageLoader {
             constexpr int RQ = BM / VEC;
             constexpr int KR = 256 / RQ;
             const int rq = t % RQ, kr = t / RQ;
+            if (full) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int k = k0 + kr + KR * p;
-                const int r = r0 + rq * VEC;
-                if (aligned && k < K && r + VEC <= R) {
-                    const vec_t q = *reinterpret_cast<const vec_t*>(X + (int64_t)k * ld + r);
+                for (int p = 0; p < 4; ++p) {
+                    const vec_t q = *reinterpret_cast<const vec_t*>(
+                        X + (int64_t)(k0 + kr + KR * p) * ld + r0 + rq * VEC);
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) v[p][e] = T(q[e]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        v[p][e] = (k < K && r + e < R) ? T(X[(int64_t)k * ld + r + e]) : T(0);
                 }
-                if (xf) {
+            } else {
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        v[p][e] = c2 * v[p][e] + ((r + e == k && k < K && r + e < R) ? c1 : T(0));
+                for (int p = 0; p < 4; ++p) {
+                    const int k = k0 + kr + KR * p;
+                    const int r = r0 + rq * VEC;
+                    if (aligned && k < K && r + VEC <= R) {
+                        const vec_t q = *reinterpret_cast<const vec_t*>(X + (int64_t)k * ld + r);
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) v[p][e] = T(q[e]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e)
+                            v[p][e] = (k < K && r + e < R) ? T(X[(int64_t)k * ld + r + e]) : T(0);
+                    }
+                }
+            }
+            if (xf) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) v[p][e] *= c2;
+                if (dg) {
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const int k = k0 + kr + KR * p;
+                        const int r = r0 + rq * VEC;
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e)
+                            if (r + e == k && k < K && r + e < R) v[p][e] += c1;
+                    }
                 }
             }
         }
@@ -470,7 +527,7 @@ __global__ __launch_bounds__(512, 4) void k_gram128(const GramJob* __restrict__ 
                                                    double beta) {
     __shared__ __align__(16) float Gs[128 * kGP];
     const GramJob jb = jobs[blockIdx.x];
-    const float* G = reinterpret_cast<const float*>(bases[jb.g_base]) + jb.g_off;
+    const float* G = base_ptr<const float>(bases, jb.g_base, jb.g_off);
     const int t = threadIdx.x;
     const int mb = jb.mb, nb = jb.nb, ld = jb.ldg;
 
@@ -1203,7 +1260,7 @@ __global__ __launch_bounds__(512, 4) void k_apply128(const ApplyJob* __restrict_
     __shared__ __align__(16) float Sl[128 * kNP];
     __shared__ double red[8];
     const ApplyJob jb = jobs[blockIdx.x];
-    const float* G = reinterpret_cast<const float*>(bases[jb.g_base]) + jb.g_off;
+    const float* G = base_ptr<const float>(bases, jb.g_base, jb.g_off);
     float* a = arena + jb.a_off;
     const int mb = jb.mb, nb = jb.nb, ld = jb.ldg;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -1367,7 +1424,7 @@ __global__ __launch_bounds__(512, 4) void k_apply128(const ApplyJob* __restrict_
     }
     if (jb.fuse) {
         const float sc = dsum > 0.0 ? (float)sqrt(asum / dsum) : 0.f;   // as in k_block_scale
-        float* W = reinterpret_cast<float*>(bases[jb.w_base]) + jb.g_off;
+        float* W = base_ptr<float>(bases, jb.w_base, jb.g_off);
         float* mo = arena + jb.m_off;
         const float b1 = ua.beta1, lr = ua.lr;
         // D through LDS (T is no longer read after the barrier), then the
@@ -1479,7 +1536,7 @@ __global__ __launch_bounds__(1024) void k_step128(const StepJob* __restrict__ jo
     __shared__ double red[16];
     const StepJob sj = jobs[blockIdx.x];
     const ApplyJob& jb = sj.ap;
-    const float* G = reinterpret_cast<const float*>(bases[jb.g_base]) + jb.g_off;
+    const float* G = base_ptr<const float>(bases, jb.g_base, jb.g_off);
     float* a = arena + jb.a_off;
     const int mb = jb.mb, nb = jb.nb, ld = jb.ldg;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -1652,7 +1709,7 @@ __global__ __launch_bounds__(1024) void k_step128(const StepJob* __restrict__ jo
     // four rows per thread), norms, D into LDS (G is no longer read past
     // these barriers)
     const int c4 = t & 31, r0 = t >> 5, cc = 4 * c4;
-    float* W = reinterpret_cast<float*>(bases[jb.w_base]) + jb.g_off;
+    float* W = base_ptr<float>(bases, jb.w_base, jb.g_off);
     float* mo = arena + jb.m_off;
     const bool vw = jb.fuse && vec && ((reinterpret_cast<uintptr_t>(W) & 15) == 0) &&
                     ((reinterpret_cast<uintptr_t>(mo) & 15) == 0);
@@ -1831,7 +1888,7 @@ __global__ __launch_bounds__(256) void k_adagrad_norm(const BlockChunk* __restri
                                                      double* __restrict__ partA) {
     __shared__ double red[4];
     const BlockChunk ch = chunks[blockIdx.x];
-    const float* G = reinterpret_cast<const float*>(bases[1 + ch.tensor]);
+    const float* G = base_ptr<const float>(bases, 1 + ch.tensor, 0);
     float* a = arena + ch.a_off;
     const int64_t total = (int64_t)ch.nrows * ch.ncols;
     double acc = 0.0;
@@ -1895,8 +1952,8 @@ __global__ __launch_bounds__(256) void k_update(const RowChunk* __restrict__ chu
                                                float* __restrict__ arena,
                                                const float* __restrict__ scale, UpdateArgs args) {
     const RowChunk ch = chunks[blockIdx.x];
-    const float* G = reinterpret_cast<const float*>(bases[1 + ch.tensor]);
-    float* W = reinterpret_cast<float*>(bases[1 + n_tensors + ch.tensor]);
+    const float* G = base_ptr<const float>(bases, 1 + ch.tensor, 0);
+    float* W = base_ptr<float>(bases, 1 + n_tensors + ch.tensor, 0);
     float* a = arena + ch.a_off;
     float* mom = arena + ch.m_off;
     const float* D = arena + ch.d_off;
@@ -1974,8 +2031,8 @@ __global__ __launch_bounds__(256) void k_sos_norm(const SosJob* __restrict__ job
     const int c = blockIdx.x - jb.first_chunk;
     const int64_t i0 = (int64_t)c * jb.chunk_rows;
     const int64_t i1 = i0 + jb.chunk_rows < jb.n_rows ? i0 + jb.chunk_rows : jb.n_rows;
-    const int32_t* rows = reinterpret_cast<const int32_t*>(jb.rows_ptr);
-    const float* G = reinterpret_cast<const float*>(jb.grads_ptr);
+    const int32_t* rows = global_ptr<const int32_t>(jb.rows_ptr);
+    const float* G = global_ptr<const float>(jb.grads_ptr);
     float* a = arena + jb.a_off;
     const int cols = jb.cols;
     double acc = 0.0;
@@ -2023,9 +2080,9 @@ __global__ __launch_bounds__(256) void k_sos_update(const SosJob* __restrict__ j
     const int c = blockIdx.x - jb.first_chunk;
     const int64_t i0 = (int64_t)c * jb.chunk_rows;
     const int64_t i1 = i0 + jb.chunk_rows < jb.n_rows ? i0 + jb.chunk_rows : jb.n_rows;
-    const int32_t* rows = reinterpret_cast<const int32_t*>(jb.rows_ptr);
+    const int32_t* rows = global_ptr<const int32_t>(jb.rows_ptr);
     const float* D = arena + jb.d_off;
-    float* W = reinterpret_cast<float*>(jb.w_ptr);
+    float* W = global_ptr<float>(jb.w_ptr);
     const float s = scale[jb.block];
     const int cols = jb.cols;
     if (jb.vec) {
@@ -2064,9 +2121,9 @@ __global__ __launch_bounds__(256) void k_sparse_rows(const SparseJob* __restrict
     while (j + 1 < njobs && jobs[j + 1].first_item <= item) ++j;
     const SparseJob jb = jobs[j];
     const int64_t li = item - jb.first_item;
-    const int32_t* rows = reinterpret_cast<const int32_t*>(jb.rows_ptr);
-    const float* g = reinterpret_cast<const float*>(jb.grads_ptr);
-    float* W = reinterpret_cast<float*>(jb.w_ptr);
+    const int32_t* rows = global_ptr<const int32_t>(jb.rows_ptr);
+    const float* g = global_ptr<const float>(jb.grads_ptr);
+    float* W = global_ptr<float>(jb.w_ptr);
     float* a = arena + jb.a_off;
     if (jb.vec) {
         const int c4 = jb.cols / 4;
