@@ -783,16 +783,15 @@ __global__ __launch_bounds__(256, 2) void k_lanczos(const LanczosJob* __restrict
     if (threadIdx.x == 0) lanczos_finish(args, jb, isfinite(lmax), lmax);
 }
 
-// Same for one factor of 129..1024 per workgroup of 512 threads, matrix read
-// from memory: wave w sums rows i = w (mod 8), lane l columns l + 64m
-// (coalesced row segments, up to 16 loads in flight per row), and the eight
-// partial vectors are added in a fixed order (S is symmetric, so these column
-// sums are S v).  Vectors in fp64 in LDS.
+// Same for one factor of 129..1024 per workgroup of 1024 threads, matrix read
+// from memory: w = S v as row dot products, wave w taking rows i = w (mod 16)
+// four at a time (64 loads in flight per lane), lane l columns l + 64m
+// (coalesced row segments) against v held in registers, each row's sum a
+// fixed butterfly over the wave.  Vectors in fp64 in LDS.
 struct LanczosBig {
     double v0[kLanczosMaxN], v1[kLanczosMaxN], wv[kLanczosMaxN];
-    double part[8 * kLanczosMaxN];
     double al[kLanczosMaxSteps], be[kLanczosMaxSteps];
-    double red[8];
+    double red[16];
     double res;
     int m_used, stop;
 };
@@ -805,8 +804,22 @@ __device__ __forceinline__ double block_sum_512(double v, double* red) {
     return ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
 }
 
+__device__ __forceinline__ double block_sum_1024(double v, double* red) {
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        s0 += red[k];
+        s1 += red[8 + k];
+    }
+    return s0 + s1;
+}
+
 template <typename TM>
-__global__ __launch_bounds__(512) void k_lanczos_big(const LanczosJob* __restrict__ jobs,
+__global__ __launch_bounds__(1024) void k_lanczos_big(const LanczosJob* __restrict__ jobs,
                                                     const TM* __restrict__ arena, LanczosArgs args) {
     __shared__ LanczosBig L;
     const LanczosJob jb = jobs[blockIdx.x];
@@ -816,7 +829,7 @@ __global__ __launch_bounds__(512) void k_lanczos_big(const LanczosJob* __restric
     const int steps = min(args.steps, min(n, kLanczosMaxSteps));
 
     double s2 = 0.0;
-    for (int i = t; i < n; i += 512) {
+    for (int i = t; i < n; i += 1024) {
         uint32_t hsh = (uint32_t)i * 2654435761u + 0x9E3779B9u;
         hsh ^= hsh >> 15; hsh *= 2246822519u; hsh ^= hsh >> 13;
         const double x = 0.5 + (double)(hsh & 0xFFFFFF) / 16777216.0;
@@ -824,43 +837,48 @@ __global__ __launch_bounds__(512) void k_lanczos_big(const LanczosJob* __restric
         L.v0[i] = 0.0;
         s2 += x * x;
     }
-    const double inv = 1.0 / sqrt(block_sum_512(s2, L.red));
-    for (int i = t; i < n; i += 512) L.v1[i] *= inv;
+    const double inv = 1.0 / sqrt(block_sum_1024(s2, L.red));
+    for (int i = t; i < n; i += 1024) L.v1[i] *= inv;
     if (t == 0) L.m_used = steps;
     __syncthreads();
 
     double beta_prev = 0.0;
     for (int k = 0; k < steps; ++k) {
-        double acc[16];
+        // w = S v as row dot products (S symmetric): v in registers, each
+        // wave takes rows w, w + 8, ..., four rows' loads in flight at once
+        double vr[16];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) acc[m] = 0.0;
-#pragma unroll 2
-        for (int i = w; i < n; i += 8) {
-            const double vi = L.v1[i];
-            const TM* row = S + (int64_t)i * ld;
+        for (int m = 0; m < 16; ++m) vr[m] = (l + 64 * m < n) ? L.v1[l + 64 * m] : 0.0;
+        for (int i0 = w; i0 < n; i0 += 64) {
+            double acc[4];
 #pragma unroll
-            for (int m = 0; m < 16; ++m)
-                if (l + 64 * m < n) acc[m] += (double)row[l + 64 * m] * vi;
+            for (int r = 0; r < 4; ++r) {
+                acc[r] = 0.0;
+                const int i = i0 + 16 * r;
+                if (i < n) {
+                    const TM* row = S + (int64_t)i * ld;
+#pragma unroll
+                    for (int m = 0; m < 16; ++m)
+                        if (l + 64 * m < n) acc[r] += (double)row[l + 64 * m] * vr[m];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const double x = wave_sum(acc[r]);
+                if (l == 0 && i0 + 16 * r < n) L.wv[i0 + 16 * r] = x;
+            }
         }
-#pragma unroll
-        for (int m = 0; m < 16; ++m)
-            if (l + 64 * m < n) L.part[w * n + l + 64 * m] = acc[m];
         __syncthreads();
         double d = 0.0;
-        for (int j = t; j < n; j += 512) {
-            const double x = ((L.part[j] + L.part[n + j]) + (L.part[2 * n + j] + L.part[3 * n + j])) +
-                             ((L.part[4 * n + j] + L.part[5 * n + j]) + (L.part[6 * n + j] + L.part[7 * n + j]));
-            L.wv[j] = x;
-            d += x * L.v1[j];
-        }
-        const double alpha = block_sum_512(d, L.red);
+        for (int j = t; j < n; j += 1024) d += L.wv[j] * L.v1[j];
+        const double alpha = block_sum_1024(d, L.red);
         double q = 0.0;
-        for (int j = t; j < n; j += 512) {
+        for (int j = t; j < n; j += 1024) {
             const double x = L.wv[j] - alpha * L.v1[j] - beta_prev * L.v0[j];
             L.wv[j] = x;
             q += x * x;
         }
-        const double beta = sqrt(block_sum_512(q, L.red));
+        const double beta = sqrt(block_sum_1024(q, L.red));
         if (t == 0) { L.al[k] = alpha; L.be[k] = beta; }
         const bool stop = !(beta > 1e-13 * fabs(alpha)) || !isfinite(alpha) || !isfinite(beta);
         if (stop) {
@@ -868,7 +886,7 @@ __global__ __launch_bounds__(512) void k_lanczos_big(const LanczosJob* __restric
             __syncthreads();
             break;
         }
-        for (int j = t; j < n; j += 512) {
+        for (int j = t; j < n; j += 1024) {
             L.v0[j] = L.v1[j];
             L.v1[j] = L.wv[j] / beta;
         }
@@ -1512,19 +1530,6 @@ __global__ __launch_bounds__(512, 4) void k_apply128(const ApplyJob* __restrict_
 // overlap the memory traffic of the other.
 typedef float f4v __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ double block_sum_1024(double v, double* red) {
-    v = wave_sum(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    double s0 = 0.0, s1 = 0.0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        s0 += red[k];
-        s1 += red[8 + k];
-    }
-    return s0 + s1;
-}
 
 __global__ __launch_bounds__(1024) void k_step128(const StepJob* __restrict__ jobs,
                                                  const uint64_t* __restrict__ bases,
@@ -2199,10 +2204,10 @@ hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, 
     if (a.steps < 1) return hipErrorInvalidValue;
     if (big) {
         if (fp64_matrix)
-            hipLaunchKernelGGL(k_lanczos_big<double>, dim3(njobs), dim3(512), 0, s, jobs,
+            hipLaunchKernelGGL(k_lanczos_big<double>, dim3(njobs), dim3(1024), 0, s, jobs,
                                static_cast<const double*>(arena), a);
         else
-            hipLaunchKernelGGL(k_lanczos_big<float>, dim3(njobs), dim3(512), 0, s, jobs,
+            hipLaunchKernelGGL(k_lanczos_big<float>, dim3(njobs), dim3(1024), 0, s, jobs,
                                static_cast<const float*>(arena), a);
     } else {
         if (fp64_matrix)
