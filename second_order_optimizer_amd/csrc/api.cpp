@@ -331,15 +331,15 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
             const int64_t Mq = b + (2 + q) * mat, Mn = b + (3 - q) * mat;
             const int64_t T2 = b + 4 * mat, T4 = b + 5 * mat;
             const int fid = fids[s];
-            // stage 0: X <- X T(M) and T(M)^2 (p = 1: M <- T(M) M)
-            st[0].push_back(mk(Xq, Mq, Xn, 8, fid));
+            // stage 0: X <- X T(M) and T(M)^2 (p = 1: M <- T(M) M).  X, M and
+            // T(M) are polynomials in the same matrix A, so every product
+            // here is symmetric: upper tiles only (16), mirrored (32)
+            st[0].push_back(mk(Xq, Mq, Xn, 8 | 16 | 32, fid));
             if (p == 1) {
-                st[0].push_back(mk(Mq, Mq, Mn, 4, fid));
+                st[0].push_back(mk(Mq, Mq, Mn, 4 | 16 | 32, fid));
                 continue;
             }
-            // T, T^2, T^4 and M are symmetric (M is kept so by mirroring), so
-            // the squarings and the M update form upper tiles only (16) and
-            // mirror them (32); X = X T is formed in full
+            // the squarings and the M update likewise
             st[0].push_back(mk(Mq, Mq, T2, 4 | 8 | 16 | 32, fid));
             int k = 1;
             int64_t cur = T2;
