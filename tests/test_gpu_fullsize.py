@@ -177,3 +177,84 @@ def test_fullsize_sampled(wid):
         w = run.check(t, g, before, before_rows)
         agg = {k: max(agg.get(k, 0.0), v) for k, v in w.items()}
     say(f"{run.wl.name}: worst " + " ".join(f"{k} {v:.2e}" for k, v in agg.items()))
+
+
+@pytest.mark.parametrize("wid", [1, 4])
+def test_fullsize_one_sided(wid):
+    """The same at full size with large_layer = 1 (Lemma 1): the Transformer's
+    32000 x 512 embedding on a 512 R factor, and the CTR tables on 128 R
+    factors.  A one-sided tensor is independent of the others (one block,
+    its own graft), so an oracle of that tensor alone, fed the same
+    gradients, must give the GPU's statistic, root (stage-isolated, exponent
+    2/root_p) and update: the whole embedding, and the two smallest tables."""
+    from second_order_optimizer_amd import shampoo as S
+    wl = synth.workload(wid)
+    dev = torch.device("cuda", 0)
+    cfg = gpu_config(wl, large_layer=1)
+    shapes = [(t.rows, t.cols, 0 if t.kind == "dense" else 1) for t in wl.tensors]
+    opt = S.Shampoo(shapes, cfg, device=dev)
+    params = [torch.from_numpy(synth.initial_weight(wl, i)).to(dev) for i in range(len(shapes))]
+    gs = synth.GradientStream(wl)
+    if wid == 1:
+        picks = [i for i, t in enumerate(wl.tensors) if t.kind == "dense" and
+                 max(t.rows, t.cols) > wl.max_precond_dim]
+    else:
+        sp = [i for i, t in enumerate(wl.tensors) if t.kind == "sparse"]
+        picks = sorted(sp, key=lambda i: wl.tensors[i].rows)[:2]
+    assert picks
+    orcs = {}
+    for i in picks:
+        t = wl.tensors[i]
+        orcs[i] = O.ShampooOracle(oracle_config(wl, large_layer=1), [(t.rows, t.cols, t.kind)],
+                                  [synth.initial_weight(wl, i)])
+        assert 0 in orcs[i].one_sided
+    worst = dict(stats=0.0, r32=0.0, r64=0.0, upd=0.0)
+    for step in range(3):
+        g = gs.step(step)
+        dense, sparse = [], {}
+        for i, spec in enumerate(wl.tensors):
+            if spec.kind == "dense":
+                dense.append(torch.from_numpy(g[i]).to(dev))
+            else:
+                r, rg = g[i]
+                dense.append(None)
+                sparse[i] = (torch.from_numpy(r).to(dev), torch.from_numpy(rg).to(dev))
+        before = {i: params[i].cpu().numpy().astype(np.float64) for i in picks}
+        opt.step(params, dense, step, wl.cadence, sparse if sparse else None)
+        torch.cuda.synchronize()
+        roots_now = step % wl.cadence == 0
+        diag = opt.diagnostics() if roots_now else None
+        for i in picks:
+            dW_ref = orcs[i].step([g[i]], step)[0]
+            dW = params[i].cpu().numpy().astype(np.float64) - before[i]
+            e = rel_fro(dW, dW_ref)
+            worst["upd"] = max(worst["upd"], e)
+            assert e <= UPDATE_TOL, (wl.name, step, i, e)
+            if wl.tensors[i].kind == "sparse":
+                untouched = np.all(dW_ref == 0.0, axis=1)
+                assert np.array_equal(dW[untouched], np.zeros_like(dW[untouched]))
+            _, _, fb, nb = opt.tensor(i)
+            bl = opt.block(fb)
+            assert nb == 1 and bl.one_sided == 1 and bl.factor_r >= 0
+            Sm = opt.stats(fb)[1].cpu().numpy()
+            st = orcs[i].one_sided[0][1]
+            es = rel_fro(Sm, st.S)
+            worst["stats"] = max(worst["stats"], es)
+            assert es <= STATS_TOL, (wl.name, step, i, es)
+            if not roots_now:
+                continue
+            d = diag[bl.factor_r]
+            p = wl.root_p // 2
+            ref = O.inverse_root(Sm, 0.0, p, eps=d.eps, clamp=False)
+            if d.status & FP64:
+                e = rel_fro(opt.roots(fb, fp64=True)[1].cpu().numpy(), ref.P)
+                worst["r64"] = max(worst["r64"], e)
+                assert e <= ROOT64_TOL, (wl.name, step, i, e)
+            else:
+                S32 = Sm.astype(np.float32).astype(np.float64)
+                ref32 = O.inverse_root(S32, 0.0, p, eps=float(np.float32(d.eps)), clamp=False)
+                P32 = opt.roots(fb)[1].cpu().numpy().astype(np.float64)
+                e = max(rel_fro(P32, ref32.P), rel_fro(P32, ref.P))
+                worst["r32"] = max(worst["r32"], e)
+                assert e <= ROOT32_TOL, (wl.name, step, i, e)
+    say(f"{wl.name} one-sided {picks}: worst " + " ".join(f"{k} {v:.2e}" for k, v in worst.items()))
