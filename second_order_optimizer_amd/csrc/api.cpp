@@ -139,7 +139,7 @@ struct shampoo_s {
 
     // arena layout (bytes)
     size_t total = 0;
-    int64_t off_bases = 0, off_sparse = 0, off_tables = 0, off_diag = 0, off_prec = 0;
+    int64_t off_bases = 0, off_sparse = 0, off_tables = 0, off_diag = 0, off_prec = 0, off_chk = 0;
     int64_t off_scr32 = 0, off_scr64 = 0, off_partA = 0, off_partD = 0, off_scale = 0;
     int n_partA = 0, n_partD = 0;
     Blob blob;  // static tables (offsets relative to off_tables)
@@ -447,6 +447,7 @@ int build_plan(shampoo_s* h) {
     h->off_sparse = take((int64_t)std::max(h->n_sparse, 1) * sizeof(SparseJob));
     h->off_diag = take((int64_t)std::max(nf, 1) * sizeof(FactorDiag));
     h->off_prec = take((int64_t)std::max(nf, 1) * 4);
+    h->off_chk = take((int64_t)std::max(nf, 1) * 16);   // Newton finish: per-factor check slots
     for (auto& f : h->factors) f.off_s = take((int64_t)f.ld * f.ld * 8);  // fp64 statistics
     for (auto& f : h->factors) f.off_p = take((int64_t)f.ld * f.ld * 4);
     if (use_fp64(c))
@@ -1307,6 +1308,7 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
     na.is_fp64 = fp64 ? 1 : 0;
     na.gate = gate;
     na.gate_val = gate_val;
+    na.chk = at<unsigned long long>(h, h->off_chk);
     void* scratch = h->arena + (fp64 ? h->off_scr64 : h->off_scr32);
     FactorDiag* diag = at<FactorDiag>(h, h->off_diag);
     GemmArgs g{};
@@ -1342,7 +1344,8 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
         }
         {
             ProfScope ps(h, PC_NEWTON_INIT, s);
-            rc = hip_err(launch_newton_init(fp64, jobs, ch.njobs, at<double>(h, 0), scratch, diag, na, s));
+            rc = hip_err(launch_newton_init(fp64, jobs, ch.njobs, ch.ld, at<double>(h, 0), scratch, diag,
+                                            na, s));
         }
         if (rc) return rc;
         for (int it = 0; it < ch.iters; ++it) {
@@ -1357,7 +1360,7 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
         }
         // the final X, M sit in buffer (iters % 2) of each slot
         ProfScope ps(h, PC_NEWTON_COMMIT, s);
-        rc = hip_err(launch_newton_commit(fp64, jobs, ch.njobs, at<float>(h, 0),
+        rc = hip_err(launch_newton_commit(fp64, jobs, ch.njobs, ch.ld, at<float>(h, 0),
                                           static_cast<unsigned char*>(scratch) +
                                               (size_t)(ch.iters & 1) * ch.ld * ch.ld *
                                                   (fp64 ? 8 : 4),

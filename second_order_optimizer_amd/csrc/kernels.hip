@@ -907,92 +907,158 @@ __global__ __launch_bounds__(1024) void k_lanczos_big(const LanczosJob* __restri
 // T = ((p+1) I - M)/p, X <- X T, M <- T^p M.  M_k = X_k^p A throughout, so
 // M -> I and X -> A^(-1/p).  Padded rows/columns carry M = I, X = I and stay
 // decoupled (block diagonal).
+// The 32 x 32 tiles (ti, tj) of a factor (blockIdx.y) are shared out over
+// gridDim.x workgroups (tile = blockIdx.x + k gridDim.x); each thread takes 4
+// consecutive columns of one row of a tile.  The statistic is read from its
+// upper triangle: a tile below the diagonal reads its mirror tile
+// (coalesced) and transposes it in LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void k_newton_init(const FactorJob* __restrict__ jobs,
                                                     const double* __restrict__ stats,
                                                     T* __restrict__ scratch,
                                                     const FactorDiag* __restrict__ diag,
                                                     NewtonArgs args) {
-    const FactorJob jb = jobs[blockIdx.x];
+    __shared__ double ts[32][33];
+    const FactorJob jb = jobs[blockIdx.y];
     if (args.gate && args.gate[jb.factor] != args.gate_val) return;
+    const int n = jb.n, ld = jb.ld, nt = ld >> 5;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {   // the finish's check slots of this pass
+        args.chk[2 * jb.factor] = 0ull;
+        args.chk[2 * jb.factor + 1] = 0ull;
+    }
     const FactorDiag dg = diag[jb.factor];
-    const int n = jb.n, ld = jb.ld;
-    const double* S = stats + jb.s_off;
-    T* X = scratch + jb.x_off;
-    T* M = scratch + jb.m_off;
     const bool ok = dg.status == 0;
     const double lam = dg.lambda_max + dg.eps;
     const T z = ok ? T((args.p + 1) / (2.0 * lam)) : T(1);
     const T zr = ok ? T(pow((args.p + 1) / (2.0 * lam), 1.0 / args.p)) : T(1);
     const T e = T(dg.eps);
-    const int64_t nn = (int64_t)ld * ld;
-    for (int64_t idx = threadIdx.x; idx < nn; idx += 256) {
-        const int i = (int)(idx / ld), j = (int)(idx % ld);
-        T m, x;
-        if (i < n && j < n && ok) {
-            const T s = T(S[(int64_t)min(i, j) * ld + max(i, j)]);  // upper triangle
-            m = z * (s + (i == j ? e : T(0)));
-            x = (i == j) ? zr : T(0);
-        } else {
-            m = (i == j) ? T(1) : T(0);
-            x = (i == j) ? T(1) : T(0);
+    const double* S = stats + jb.s_off;
+    T* X = scratch + jb.x_off;
+    T* M = scratch + jb.m_off;
+    const int r = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 4;
+    for (int tile = blockIdx.x; tile < nt * nt; tile += gridDim.x) {
+        const int ti = tile / nt, tj = tile % nt;
+        const int br = ti <= tj ? ti : tj, bc = ti <= tj ? tj : ti;   // the upper tile
+        __syncthreads();   // the previous tile's reads of ts are done
+        if (ok) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ts[r][c0 + q] = S[(int64_t)(32 * br + r) * ld + 32 * bc + c0 + q];
         }
-        M[idx] = m;
-        X[idx] = x;
+        __syncthreads();
+        const int i = 32 * ti + r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = c0 + q, j = 32 * tj + c;
+            T m, x;
+            if (i < n && j < n && ok) {
+                const int a = ti < tj ? r : (ti > tj ? c : min(r, c));
+                const int b = ti < tj ? c : (ti > tj ? r : max(r, c));
+                m = z * (T(ts[a][b]) + (i == j ? e : T(0)));
+                x = (i == j) ? zr : T(0);
+            } else {
+                m = (i == j) ? T(1) : T(0);
+                x = (i == j) ? T(1) : T(0);
+            }
+            M[(int64_t)i * ld + j] = m;
+            X[(int64_t)i * ld + j] = x;
+        }
     }
 }
 
+// Finish, part 1 (same sharing of tiles): max |M - I| and whether X or M went
+// non-finite, over the real n x n part, into the factor's check slots
+// (atomic max of the bit patterns of non-negative doubles, which order like
+// the values, so the result does not depend on the order).
+template <typename T>
+__global__ __launch_bounds__(256) void k_newton_check(const FactorJob* __restrict__ jobs,
+                                                     const T* __restrict__ scratch,
+                                                     const FactorDiag* __restrict__ diag,
+                                                     NewtonArgs args) {
+    __shared__ double red[4];
+    const FactorJob jb = jobs[blockIdx.y];
+    if (args.gate && args.gate[jb.factor] != args.gate_val) return;
+    if (diag[jb.factor].status & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_ZERO_)) return;
+    const int n = jb.n, ld = jb.ld, nt = ld >> 5;
+    const T* X = scratch + jb.x_off;
+    const T* M = scratch + jb.m_off;
+    const int r = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 4;
+    double res = 0.0, bad = 0.0;
+    for (int tile = blockIdx.x; tile < nt * nt; tile += gridDim.x) {
+        const int ti = tile / nt, tj = tile % nt;
+        const int i = 32 * ti + r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int j = 32 * tj + c0 + q;
+            if (i < n && j < n) {
+                const double x = double(X[(int64_t)i * ld + j]);
+                const double d = fabs(double(M[(int64_t)i * ld + j]) - (i == j ? 1.0 : 0.0));
+                if (!isfinite(x) || !isfinite(d)) bad = 1.0;
+                else res = fmax(res, d);
+            }
+        }
+    }
+    res = block_max_256(res, red);
+    bad = block_max_256(bad, red);
+    if (threadIdx.x == 0) {
+        atomicMax(&args.chk[2 * jb.factor], (unsigned long long)__double_as_longlong(res));
+        if (bad > 0.0) atomicMax(&args.chk[2 * jb.factor + 1], 1ull);
+    }
+}
+
+// Finish, part 2 (same sharing of tiles): unless the factor's input or iterate went
+// non-finite (then its previous root stays), the root is the symmetric part
+// of X (the tile and its mirror, transposed in LDS), the identity for a
+// factor with no statistics, identity on the padding; tile 0 records the
+// status and the residual.
 template <typename T>
 __global__ __launch_bounds__(256) void k_newton_commit(const FactorJob* __restrict__ jobs,
                                                       float* __restrict__ arena,
                                                       const T* __restrict__ scratch,
                                                       FactorDiag* __restrict__ diag,
                                                       NewtonArgs args) {
-    __shared__ double red[4];
-    const FactorJob jb = jobs[blockIdx.x];
+    __shared__ double tm[32][33];
+    const FactorJob jb = jobs[blockIdx.y];
     if (args.gate && args.gate[jb.factor] != args.gate_val) return;
-    const int n = jb.n, ld = jb.ld;
-    const T* X = scratch + jb.x_off;
-    const T* M = scratch + jb.m_off;
-    float* P = arena + jb.p_off;
-    double* P64 = jb.p64_off >= 0 ? reinterpret_cast<double*>(arena) + jb.p64_off : nullptr;
+    const int n = jb.n, ld = jb.ld, nt = ld >> 5;
+    // status bits set before the iteration; this pass only adds others
     const int st0 = diag[jb.factor].status & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_ZERO_);
-    const int64_t nn = (int64_t)ld * ld;
-    double res = 0.0, bad = 0.0;
-    if (st0 == 0) {
-        for (int64_t idx = threadIdx.x; idx < nn; idx += 256) {
-            const int i = (int)(idx / ld), j = (int)(idx % ld);
-            if (i < n && j < n) {
-                const double x = double(X[idx]);
-                const double r = fabs(double(M[idx]) - (i == j ? 1.0 : 0.0));
-                if (!isfinite(x) || !isfinite(r)) bad = 1.0;
-                res = fmax(res, r);
-            }
-        }
-    }
-    res = block_max_256(res, red);
-    bad = block_max_256(bad, red);
     int st = st0;
-    if (st0 == 0 && bad > 0.0) st |= SHAMPOO_FACTOR_NONFINITE_ROOT_;
+    if (st0 == 0 && args.chk[2 * jb.factor + 1] != 0ull) st |= SHAMPOO_FACTOR_NONFINITE_ROOT_;
     const bool keep = (st & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_NONFINITE_ROOT_)) != 0;
-    if (!keep) {
-        const bool ident = (st & SHAMPOO_FACTOR_ZERO_) != 0;
-        for (int64_t idx = threadIdx.x; idx < nn; idx += 256) {
-            const int i = (int)(idx / ld), j = (int)(idx % ld);
-            double x;
-            if (ident || i >= n || j >= n) x = (i == j) ? 1.0 : 0.0;
-            else x = 0.5 * (double(X[idx]) + double(X[(int64_t)j * ld + i]));  // symmetric part
-            P[idx] = float(x);
-            if (P64) P64[idx] = x;
-        }
-    }
-    if (threadIdx.x == 0) {
+    const double res = st0 == 0 ? __longlong_as_double((long long)args.chk[2 * jb.factor]) : 0.0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
         FactorDiag& dg = diag[jb.factor];
         if (!keep && !(st & SHAMPOO_FACTOR_ZERO_) && res > 1e-2) st |= SHAMPOO_FACTOR_RESIDUAL_HIGH_;
         if (args.is_fp64) st |= SHAMPOO_FACTOR_FP64_;
         else st &= ~SHAMPOO_FACTOR_FP64_;
         dg.status = st;
-        dg.residual = (st0 == 0) ? res : 0.0;
+        dg.residual = res;
+    }
+    if (keep) return;
+    const bool ident = (st & SHAMPOO_FACTOR_ZERO_) != 0;
+    const T* X = scratch + jb.x_off;
+    float* P = arena + jb.p_off;
+    double* P64 = jb.p64_off >= 0 ? reinterpret_cast<double*>(arena) + jb.p64_off : nullptr;
+    const int r = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 4;
+    for (int tile = blockIdx.x; tile < nt * nt; tile += gridDim.x) {
+        const int ti = tile / nt, tj = tile % nt;
+        __syncthreads();   // the previous tile's reads of tm are done
+        if (!ident) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                tm[r][c0 + q] = double(X[(int64_t)(32 * tj + r) * ld + 32 * ti + c0 + q]);
+        }
+        __syncthreads();
+        const int i = 32 * ti + r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = c0 + q, j = 32 * tj + c;
+            double x;
+            if (ident || i >= n || j >= n) x = (i == j) ? 1.0 : 0.0;
+            else x = 0.5 * (double(X[(int64_t)i * ld + j]) + tm[c][r]);   // symmetric part
+            P[(int64_t)i * ld + j] = float(x);
+            if (P64) P64[(int64_t)i * ld + j] = x;
+        }
     }
 }
 
@@ -2219,28 +2285,39 @@ hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, 
     }
     return hipGetLastError();
 }
-hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, const double* stats,
-                              void* scratch, const FactorDiag* diag, const NewtonArgs& a,
-                              hipStream_t s) {
+hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, int ld,
+                              const double* stats, void* scratch, const FactorDiag* diag,
+                              const NewtonArgs& a, hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
+    // one workgroup per tile; factors up to 128 (chunks of the gated fp64
+    // chain, where most factors exit at once) one workgroup per factor
+    const dim3 grid(ld <= 128 ? 1 : (ld / 32) * (ld / 32), njobs);
     if (fp64)
-        hipLaunchKernelGGL(k_newton_init<double>, dim3(njobs), dim3(256), 0, s, jobs, stats,
+        hipLaunchKernelGGL(k_newton_init<double>, grid, dim3(256), 0, s, jobs, stats,
                            static_cast<double*>(scratch), diag, a);
     else
-        hipLaunchKernelGGL(k_newton_init<float>, dim3(njobs), dim3(256), 0, s, jobs, stats,
+        hipLaunchKernelGGL(k_newton_init<float>, grid, dim3(256), 0, s, jobs, stats,
                            static_cast<float*>(scratch), diag, a);
     return hipGetLastError();
 }
-hipError_t launch_newton_commit(bool fp64, const FactorJob* jobs, int njobs, float* arena,
+hipError_t launch_newton_commit(bool fp64, const FactorJob* jobs, int njobs, int ld, float* arena,
                                 const void* scratch, FactorDiag* diag, const NewtonArgs& a,
                                 hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
-    if (fp64)
-        hipLaunchKernelGGL(k_newton_commit<double>, dim3(njobs), dim3(256), 0, s, jobs, arena,
+    // one workgroup per tile; factors up to 128 (chunks of the gated fp64
+    // chain, where most factors exit at once) one workgroup per factor
+    const dim3 grid(ld <= 128 ? 1 : (ld / 32) * (ld / 32), njobs);
+    if (fp64) {
+        hipLaunchKernelGGL(k_newton_check<double>, grid, dim3(256), 0, s, jobs,
                            static_cast<const double*>(scratch), diag, a);
-    else
-        hipLaunchKernelGGL(k_newton_commit<float>, dim3(njobs), dim3(256), 0, s, jobs, arena,
+        hipLaunchKernelGGL(k_newton_commit<double>, grid, dim3(256), 0, s, jobs, arena,
+                           static_cast<const double*>(scratch), diag, a);
+    } else {
+        hipLaunchKernelGGL(k_newton_check<float>, grid, dim3(256), 0, s, jobs,
                            static_cast<const float*>(scratch), diag, a);
+        hipLaunchKernelGGL(k_newton_commit<float>, grid, dim3(256), 0, s, jobs, arena,
+                           static_cast<const float*>(scratch), diag, a);
+    }
     return hipGetLastError();
 }
 hipError_t launch_newton128(const FactorJob* jobs, int njobs, const double* stats, float* arena,

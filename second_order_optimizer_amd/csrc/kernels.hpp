@@ -43,6 +43,7 @@ struct NewtonArgs {
     int is_fp64;
     const int32_t* gate;
     int32_t gate_val;
+    unsigned long long* chk;   // per factor: [2f] max |M - I| (bits), [2f + 1] non-finite flag
 };
 
 struct FusedArgs {          // fused fp32 root of factors up to 128
@@ -69,10 +70,12 @@ hipError_t launch_step128(const StepJob* jobs, int njobs, const uint64_t* bases,
                           const UpdateArgs& ua, hipStream_t s);
 hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, bool fp64_matrix,
                           bool big, const LanczosArgs& a, hipStream_t s);
-hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, const double* stats,
-                              void* scratch, const FactorDiag* diag, const NewtonArgs& a,
-                              hipStream_t s);
-hipError_t launch_newton_commit(bool fp64, const FactorJob* jobs, int njobs, float* arena,
+// Newton start and finish, one workgroup per 32 x 32 tile of every factor of
+// a chunk (factors of leading dimension ld).
+hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, int ld,
+                              const double* stats, void* scratch, const FactorDiag* diag,
+                              const NewtonArgs& a, hipStream_t s);
+hipError_t launch_newton_commit(bool fp64, const FactorJob* jobs, int njobs, int ld, float* arena,
                                 const void* scratch, FactorDiag* diag, const NewtonArgs& a,
                                 hipStream_t s);
 hipError_t launch_newton128(const FactorJob* jobs, int njobs, const double* stats, float* arena,
