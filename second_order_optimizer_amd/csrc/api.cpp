@@ -140,6 +140,7 @@ struct shampoo_s {
     // arena layout (bytes)
     size_t total = 0;
     int64_t off_bases = 0, off_sparse = 0, off_tables = 0, off_diag = 0, off_prec = 0, off_chk = 0;
+    int64_t off_lzwork = 0;
     int64_t off_scr32 = 0, off_scr64 = 0, off_partA = 0, off_partD = 0, off_scale = 0;
     int n_partA = 0, n_partD = 0;
     Blob blob;  // static tables (offsets relative to off_tables)
@@ -448,6 +449,7 @@ int build_plan(shampoo_s* h) {
     h->off_diag = take((int64_t)std::max(nf, 1) * sizeof(FactorDiag));
     h->off_prec = take((int64_t)std::max(nf, 1) * 4);
     h->off_chk = take((int64_t)std::max(nf, 1) * 16);   // Newton finish: per-factor check slots
+    h->off_lzwork = take((int64_t)kLanczosSplitMax * kLzWork * 8);  // split Lanczos records
     for (auto& f : h->factors) f.off_s = take((int64_t)f.ld * f.ld * 8);  // fp64 statistics
     for (auto& f : h->factors) f.off_p = take((int64_t)f.ld * f.ld * 4);
     if (use_fp64(c))
@@ -1389,6 +1391,7 @@ int enqueue_roots(shampoo_s* h, RootTables& rt, hipStream_t s) {
     la.threshold = c.fp64_cond_threshold;
     la.diag = diag;
     la.prec = prec;
+    la.work = at<double>(h, h->off_lzwork);
     la.route_all_fp64 = c.root_mode == SHAMPOO_ROOT_F64 ? 1 : 0;
     LanczosArgs lp = la;
     lp.mode = 1;

@@ -900,6 +900,122 @@ __global__ __launch_bounds__(1024) void k_lanczos_big(const LanczosJob* __restri
     }
 }
 
+// The same Lanczos iteration for a few factors of 129..1024, split over
+// launches so that one factor's product S v runs on many workgroups: per
+// step, k_lz_matvec (one workgroup per 64 rows of a factor, each row summed
+// exactly as in k_lanczos_big) and k_lz_update (one workgroup per factor:
+// alpha, beta, the next vector); the vectors and the tridiagonal live in a
+// per-factor work record.  The arithmetic, and so the result, is that of
+// k_lanczos_big.
+constexpr int kLzV0 = 0, kLzV1 = kLanczosMaxN, kLzW = 2 * kLanczosMaxN, kLzAl = 3 * kLanczosMaxN,
+              kLzBe = kLzAl + kLanczosMaxSteps, kLzMisc = kLzBe + kLanczosMaxSteps;
+// misc: [0] beta of the previous step, [1] steps used, [2] stopped flag
+static_assert(kLzMisc + 3 <= kLzWork, "Lanczos work record");
+
+__global__ __launch_bounds__(1024) void k_lz_start(const LanczosJob* __restrict__ jobs,
+                                                  double* __restrict__ work, int steps_max) {
+    __shared__ double red[16];
+    const LanczosJob jb = jobs[blockIdx.x];
+    double* wk = work + (int64_t)blockIdx.x * kLzWork;
+    const int n = jb.n, t = threadIdx.x;
+    double s2 = 0.0;
+    for (int i = t; i < n; i += 1024) {
+        uint32_t hsh = (uint32_t)i * 2654435761u + 0x9E3779B9u;
+        hsh ^= hsh >> 15; hsh *= 2246822519u; hsh ^= hsh >> 13;
+        const double x = 0.5 + (double)(hsh & 0xFFFFFF) / 16777216.0;
+        wk[kLzV1 + i] = x;
+        wk[kLzV0 + i] = 0.0;
+        s2 += x * x;
+    }
+    const double inv = 1.0 / sqrt(block_sum_1024(s2, red));
+    for (int i = t; i < n; i += 1024) wk[kLzV1 + i] *= inv;
+    if (t == 0) {
+        wk[kLzMisc] = 0.0;
+        wk[kLzMisc + 1] = (double)min(steps_max, min(n, kLanczosMaxSteps));
+        wk[kLzMisc + 2] = 0.0;
+    }
+}
+
+template <typename TM>
+__global__ __launch_bounds__(256) void k_lz_matvec(const LanczosJob* __restrict__ jobs,
+                                                  const TM* __restrict__ arena,
+                                                  double* __restrict__ work, int k) {
+    const LanczosJob jb = jobs[blockIdx.y];
+    double* wk = work + (int64_t)blockIdx.y * kLzWork;
+    const int n = jb.n, ld = jb.ld;
+    if (wk[kLzMisc + 2] != 0.0 || k >= (int)wk[kLzMisc + 1]) return;   // uniform
+    const int r0 = 64 * blockIdx.x;
+    if (r0 >= n) return;
+    const TM* S = arena + jb.off;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    double vr[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) vr[m] = (l + 64 * m < n) ? wk[kLzV1 + l + 64 * m] : 0.0;
+    for (int i0 = r0 + w; i0 < r0 + 64 && i0 < n; i0 += 16) {
+        double acc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            acc[r] = 0.0;
+            const int i = i0 + 4 * r;
+            if (i < n && i < r0 + 64) {
+                const TM* row = S + (int64_t)i * ld;
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                    if (l + 64 * m < n) acc[r] += (double)row[l + 64 * m] * vr[m];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const double x = wave_sum(acc[r]);
+            const int i = i0 + 4 * r;
+            if (l == 0 && i < n && i < r0 + 64) wk[kLzW + i] = x;
+        }
+    }
+}
+
+__global__ __launch_bounds__(1024) void k_lz_update(const LanczosJob* __restrict__ jobs,
+                                                   double* __restrict__ work, int k) {
+    __shared__ double red[16];
+    const LanczosJob jb = jobs[blockIdx.x];
+    double* wk = work + (int64_t)blockIdx.x * kLzWork;
+    const int n = jb.n, t = threadIdx.x;
+    if (wk[kLzMisc + 2] != 0.0 || k >= (int)wk[kLzMisc + 1]) return;   // uniform
+    const double beta_prev = wk[kLzMisc];
+    double d = 0.0;
+    for (int j = t; j < n; j += 1024) d += wk[kLzW + j] * wk[kLzV1 + j];
+    const double alpha = block_sum_1024(d, red);
+    double q = 0.0;
+    for (int j = t; j < n; j += 1024) {
+        const double x = wk[kLzW + j] - alpha * wk[kLzV1 + j] - beta_prev * wk[kLzV0 + j];
+        wk[kLzW + j] = x;
+        q += x * x;
+    }
+    const double beta = sqrt(block_sum_1024(q, red));
+    const bool stop = !(beta > 1e-13 * fabs(alpha)) || !isfinite(alpha) || !isfinite(beta);
+    if (t == 0) {
+        wk[kLzAl + k] = alpha;
+        wk[kLzBe + k] = beta;
+        if (stop) {
+            wk[kLzMisc + 1] = (double)(k + 1);
+            wk[kLzMisc + 2] = 1.0;
+        }
+        wk[kLzMisc] = beta;
+    }
+    if (stop) return;
+    for (int j = t; j < n; j += 1024) {
+        wk[kLzV0 + j] = wk[kLzV1 + j];
+        wk[kLzV1 + j] = wk[kLzW + j] / beta;
+    }
+}
+
+__global__ __launch_bounds__(64) void k_lz_finish(const LanczosJob* __restrict__ jobs,
+                                                 const double* __restrict__ work, LanczosArgs args) {
+    const LanczosJob jb = jobs[blockIdx.x];
+    const double* wk = work + (int64_t)blockIdx.x * kLzWork;
+    const double lm = tridiag_max_wave(wk + kLzAl, wk + kLzBe, (int)wk[kLzMisc + 1]);
+    if (threadIdx.x == 0) lanczos_finish(args, jb, isfinite(lm), lm);
+}
+
 // ======================================================= coupled Newton
 // Coupled Newton iteration for the inverse p-th root (Guo & Higham, SIAM J.
 // Matrix Anal. Appl. 28(3), 2006).  With A = S + eps I (S read from its upper
@@ -2268,7 +2384,22 @@ hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, 
                           bool big, const LanczosArgs& a, hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
     if (a.steps < 1) return hipErrorInvalidValue;
-    if (big) {
+    if (big && njobs <= kLanczosSplitMax && a.work) {
+        // few factors: the product of each step on many workgroups
+        hipLaunchKernelGGL(k_lz_start, dim3(njobs), dim3(1024), 0, s, jobs, a.work, a.steps);
+        const dim3 mv(kLanczosMaxN / 64, njobs);
+        const int steps = std::min(a.steps, kLanczosMaxSteps);
+        for (int k = 0; k < steps; ++k) {
+            if (fp64_matrix)
+                hipLaunchKernelGGL(k_lz_matvec<double>, mv, dim3(256), 0, s, jobs,
+                                   static_cast<const double*>(arena), a.work, k);
+            else
+                hipLaunchKernelGGL(k_lz_matvec<float>, mv, dim3(256), 0, s, jobs,
+                                   static_cast<const float*>(arena), a.work, k);
+            hipLaunchKernelGGL(k_lz_update, dim3(njobs), dim3(1024), 0, s, jobs, a.work, k);
+        }
+        hipLaunchKernelGGL(k_lz_finish, dim3(njobs), dim3(64), 0, s, jobs, a.work, a);
+    } else if (big) {
         if (fp64_matrix)
             hipLaunchKernelGGL(k_lanczos_big<double>, dim3(njobs), dim3(1024), 0, s, jobs,
                                static_cast<const double*>(arena), a);

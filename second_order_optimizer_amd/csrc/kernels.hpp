@@ -27,6 +27,11 @@ struct GemmArgs {
     double* norms;        // per-tile ||C||^2 partials (tasks with norm_slot >= 0)
 };
 
+// Lanczos on at most this many factors > 128 splits each step's product over
+// many workgroups (a work record of kLzWork doubles per factor).
+constexpr int kLanczosSplitMax = 32;
+constexpr int kLzWork = 3 * 1024 + 2 * 64 + 4;
+
 struct LanczosArgs {
     int steps;
     int mode;             // 0: statistics (lambda_max, eps), 1: roots (kappa estimate)
@@ -36,6 +41,7 @@ struct LanczosArgs {
     double threshold;
     FactorDiag* diag;
     int32_t* prec;
+    double* work;         // factors > 128: split Lanczos work records (kLanczosSplitMax of them)
 };
 
 struct NewtonArgs {
