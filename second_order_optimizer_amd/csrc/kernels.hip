@@ -36,9 +36,28 @@
 namespace shampoo {
 
 // ---------------------------------------------------------------- helpers
+// One DPP step on a double (both halves moved the same way; rows outside
+// ROWM take 0).
+template <int CTRL, int ROWM>
+__device__ __forceinline__ double dpp_d(double v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROWM, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROWM, 0xf, false);
+    return __hiloint2double(hi, lo);
+}
+// Sum over the 64 lanes of a wave, returned to every lane; called with all
+// lanes active.  DPP moves (no LDS): pairs and quads, rows of 16 by two
+// rotations, then the row broadcasts 15 and 31 leave the total in lane 63,
+// which is read out.  A fixed order, so the result is deterministic.
 __device__ __forceinline__ double wave_sum(double v) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_d<0xB1, 0xf>(v);    // quad_perm [1,0,3,2]
+    v += dpp_d<0x4E, 0xf>(v);    // quad_perm [2,3,0,1]
+    v += dpp_d<0x124, 0xf>(v);   // row_ror:4
+    v += dpp_d<0x128, 0xf>(v);   // row_ror:8
+    v += dpp_d<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_d<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+    const int lo = __builtin_amdgcn_readlane(__double2loint(v), 63);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(v), 63);
+    return __hiloint2double(hi, lo);
 }
 __device__ __forceinline__ float wave_sum(float v) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
