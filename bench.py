@@ -409,7 +409,7 @@ def main():
 
     root_ms = sum(prof.get(n, (0, 0.0))[1] for n in
                   ("lanczos_stats", "lanczos_roots", "newton_init", "newton_gemm_f32",
-                   "newton_gemm_f64", "newton_commit", "newton_fused_f32"))
+                   "newton_gemm_f64", "newton_commit", "newton_fused_f32", "route_compact"))
     inv_root_blocks_per_s = (opt.n_blocks * n_root_passes / (root_ms / 1e3)) if root_ms > 0 else None
     mfma_pct = {k: round(100 * v["frac"], 2) for k, v in stages.items() if v.get("bound") == "mfma"}
 

@@ -178,6 +178,13 @@ typedef struct {
  * (root_p not in {1,2,4,8}; root_p odd with large_layer = 1; a factor
  * dimension above 1024; rows above 2^31 - 1 or cols above 2^20),
  * SHAMPOO_E_NOMEM.
+ * Scratch: the batched coupled-Newton iteration (fp32 factors above 128 and
+ * every fp64 root) runs in chunks of factors whose scratch (six ld x ld
+ * matrices per factor) stays within 4 GiB per precision; the environment
+ * variable SHAMPOO_NEWTON_SCRATCH_BYTES, read here, sets another limit (a
+ * chunk holds at least one factor).  In AUTO mode the fp64 chain runs on the
+ * factors routed to fp64 only, packed in factor order into the leading chunks
+ * of their class.
  */
 int shampoo_create(const shampoo_config* cfg, int32_t n_tensors,
                    const shampoo_tensor_desc* tensors, shampoo_t** out);

@@ -14,6 +14,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -30,7 +31,7 @@ constexpr int kFactorPad = 32;        // factor matrices padded to a multiple of
 constexpr int kXcds = 8;              // MI355X: 8 XCDs, workgroup b dispatched to XCD b % 8
 constexpr int64_t kElemChunk = 16384; // elements per workgroup in elementwise kernels
 constexpr int kRingSlots = 16;        // pinned staging slots for per-call tables
-constexpr size_t kNewtonScratchBudget = size_t(4) << 30;  // bytes per precision
+constexpr size_t kNewtonScratchBudget = size_t(4) << 30;  // bytes per precision (default)
 constexpr int kSplitKTiles = 512;     // one-sided statistics: target tiles per launch
 constexpr int kSplitKMin = 512;       // and shortest chunk of the long dimension
 constexpr int kSosMaxChunks = 64;     // sparse one-sided tables: split-K chunks per call, at most,
@@ -85,6 +86,8 @@ struct NewtonChunk {
     int njobs = 0;
     bool fused = false;                      // fp32, ld <= 128: one kernel, no scratch
     int64_t jobs_off = 0;                    // FactorJob table (bytes)
+    bool compact = false;                    // gated fp64 chain on packed slots: the jobs
+    int64_t slot_jobs_off = 0;               // are written on the device (arena bytes)
     std::vector<LaunchRef> stages[2];        // per parity
 };
 
@@ -94,6 +97,8 @@ struct RootTables {
     int64_t lanczos_s_big_off = 0, lanczos_p_big_off = 0;       // factors with ld > 128
     int n_lanczos_small = 0, n_lanczos_big = 0;
     std::vector<NewtonChunk> chunks32, chunks64;
+    std::vector<CompactClass> compact;       // classes of the packed fp64 chain
+    int64_t compact_off = 0;
 };
 
 // Host-side table builder: tables are appended to one blob that is copied
@@ -113,14 +118,14 @@ enum ProfCat : int {
     PC_STATS = 0, PC_LANCZOS_S, PC_LANCZOS_P, PC_NEWTON_INIT, PC_NEWTON_GEMM32, PC_NEWTON_GEMM64,
     PC_NEWTON_COMMIT, PC_ADAGRAD, PC_APPLY_T, PC_APPLY_D, PC_SCALE, PC_UPDATE, PC_SPARSE,
     PC_NEWTON_FUSED, PC_APPLY_FUSED, PC_STEP_FUSED, PC_STATS_SPLITK, PC_SOS_STATS, PC_SOS_NORM,
-    PC_SOS_APPLY, PC_SOS_UPDATE, PC_COUNT
+    PC_SOS_APPLY, PC_SOS_UPDATE, PC_ROUTE, PC_COUNT
 };
 const char* const kProfNames[PC_COUNT] = {
     "stats_gram_f64", "lanczos_stats", "lanczos_roots", "newton_init", "newton_gemm_f32",
     "newton_gemm_f64", "newton_commit", "adagrad_norm", "apply_gemm_t", "apply_gemm_d",
     "block_scale", "update", "sparse_rows", "newton_fused_f32", "apply_fused", "step_fused",
     "stats_onesided", "stats_onesided_rows", "onesided_rows_norm", "apply_onesided_rows",
-    "onesided_rows_update"};
+    "onesided_rows_update", "route_compact"};
 
 struct ProfRec {
     int cat;
@@ -141,6 +146,8 @@ struct shampoo_s {
     size_t total = 0;
     int64_t off_bases = 0, off_sparse = 0, off_tables = 0, off_diag = 0, off_prec = 0, off_chk = 0;
     int64_t off_lzwork = 0;
+    int64_t off_slot_jobs = 0, off_slot_live = 0;  // packed fp64 chain: slot jobs and flags
+    int64_t slot_tmpl_off = 0;                     // and the template job of every slot entry
     int64_t off_scr32 = 0, off_scr64 = 0, off_partA = 0, off_partD = 0, off_scale = 0;
     int n_partA = 0, n_partD = 0;
     Blob blob;  // static tables (offsets relative to off_tables)
@@ -284,8 +291,10 @@ int newton_iters_for(const shampoo_config& c, int p) {
 }
 
 // Builds the per-parity GEMM launches of one Newton chunk.
+// gids: the gating id of each factor's products (default: the factor id).
 void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& fids, int ld,
-                        bool fp64, bool fused, int64_t scratch_off_bytes, int p) {
+                        bool fp64, bool fused, int64_t scratch_off_bytes, int p,
+                        const std::vector<int>* gids = nullptr) {
     ch.p = p;
     ch.iters = newton_iters_for(h->cfg, p);
     const int64_t esz = fp64 ? 8 : 4;
@@ -331,7 +340,7 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
             const int64_t Xq = b + q * mat, Xn = b + (1 - q) * mat;
             const int64_t Mq = b + (2 + q) * mat, Mn = b + (3 - q) * mat;
             const int64_t T2 = b + 4 * mat, T4 = b + 5 * mat;
-            const int fid = fids[s];
+            const int fid = gids ? (*gids)[s] : fids[s];
             // stage 0: X <- X T(M) and T(M)^2 (p = 1: M <- T(M) M).  X, M and
             // T(M) are polynomials in the same matrix A, so every product
             // here is symmetric: upper tiles only (16), mirrored (32)
@@ -510,7 +519,16 @@ int build_plan(shampoo_s* h) {
     std::sort(lds.begin(), lds.end());
     lds.erase(std::unique(lds.begin(), lds.end()), lds.end());
     int64_t scr32 = 0, scr64 = 0;
-    struct Pending { int set; int ld; int p; std::vector<int> fids; bool fp64; bool fused; };
+    struct Pending {
+        int set; int ld; int p; std::vector<int> fids; bool fp64; bool fused;
+        bool compact = false; int cap = 0; int slot_first = 0;
+    };
+    int n_slots = 0;
+    int64_t scratch_budget = (int64_t)kNewtonScratchBudget;
+    if (const char* e = std::getenv("SHAMPOO_NEWTON_SCRATCH_BYTES")) {
+        const long long v = std::atoll(e);
+        if (v > 0) scratch_budget = v;
+    }
     std::vector<Pending> pend;
     // sets: 0 every factor; 1..P the parts of a staggered pass; P+1..2P the
     // same parts reading a snapshot of their statistics and writing staged
@@ -536,7 +554,19 @@ int build_plan(shampoo_s* h) {
                 continue;
             }
             const int64_t per = 6 * (int64_t)ld * ld * (fp64 ? 8 : 4);
-            const int cap = (int)std::max<int64_t>(1, (int64_t)kNewtonScratchBudget / per);
+            const int cap = (int)std::max<int64_t>(1, scratch_budget / per);
+            if (fp64 && c.root_mode == SHAMPOO_ROOT_AUTO) {
+                // the gated fp64 chain of AUTO runs on packed slots: the
+                // routed factors of the class fill its first chunks
+                Pending pd{set, ld, pe, fids, true, false};
+                pd.compact = true;
+                pd.cap = cap;
+                pd.slot_first = n_slots;
+                n_slots += (int)fids.size();
+                scr64 = std::max(scr64, per * (int64_t)std::min<size_t>(fids.size(), cap));
+                pend.push_back(std::move(pd));
+                continue;
+            }
             for (size_t s = 0; s < fids.size(); s += cap) {
                 Pending pd;
                 pd.set = set;
@@ -553,6 +583,8 @@ int build_plan(shampoo_s* h) {
     }
     h->off_scr32 = take(scr32);
     h->off_scr64 = take(scr64);
+    h->off_slot_jobs = take((int64_t)n_slots * sizeof(FactorJob));
+    h->off_slot_live = take((int64_t)n_slots * 4);
     // snapshot (fp64 statistics) and staging (fp32 roots) areas of the
     // asynchronous pass, sized for the largest part; per-factor places
     std::vector<int64_t> snap_at(nf, -1), stage_at(nf, -1);
@@ -834,8 +866,8 @@ int build_plan(shampoo_s* h) {
         }
         h->ident_jobs_off = blob.add(ident);
     }
+    std::vector<FactorJob> slot_tmpl(n_slots);
     for (auto& pd : pend) {
-        NewtonChunk ch;
         const bool async = pd.set > nparts;
         std::vector<std::pair<int64_t, int64_t>> saved;
         if (async)   // the job tables of this chunk read the snapshot, write the staging area
@@ -844,16 +876,49 @@ int build_plan(shampoo_s* h) {
                 h->factors[i].off_s = snap_at[i];
                 h->factors[i].off_p = stage_at[i];
             }
-        build_newton_chunk(h, ch, pd.fids, pd.ld, pd.fp64, pd.fused,
-                           pd.fp64 ? h->off_scr64 : h->off_scr32, pd.p);
+        RootTables& rt = async ? h->async_roots[pd.set - 1 - nparts] : h->roots[pd.set];
+        const int64_t scr = pd.fp64 ? h->off_scr64 : h->off_scr32;
+        if (pd.compact) {
+            // template jobs of the class (scratch places are set when packed)
+            const int n = (int)pd.fids.size();
+            for (int k = 0; k < n; ++k) {
+                const FactorPlan& f = h->factors[pd.fids[k]];
+                FactorJob j{};
+                j.s_off = f.off_s / 8;
+                j.p_off = f.off_p / 4;
+                j.p64_off = f.off_p64 >= 0 ? f.off_p64 / 8 : -1;
+                j.n = f.dim;
+                j.ld = pd.ld;
+                j.factor = pd.fids[k];
+                slot_tmpl[pd.slot_first + k] = j;
+            }
+            rt.compact.push_back(CompactClass{pd.slot_first, n, pd.cap, 0, (int64_t)pd.ld * pd.ld});
+            // chunk q holds slots [q cap, (q+1) cap); its products are gated
+            // by the slot flags
+            for (int q0 = 0; q0 < n; q0 += pd.cap) {
+                const int m = std::min(pd.cap, n - q0);
+                std::vector<int> fids(pd.fids.begin() + q0, pd.fids.begin() + q0 + m), gids(m);
+                for (int k = 0; k < m; ++k) gids[k] = pd.slot_first + q0 + k;
+                NewtonChunk ch;
+                build_newton_chunk(h, ch, fids, pd.ld, true, false, scr, pd.p, &gids);
+                ch.compact = true;
+                ch.slot_jobs_off = h->off_slot_jobs + (int64_t)(pd.slot_first + q0) * sizeof(FactorJob);
+                rt.chunks64.push_back(std::move(ch));
+            }
+        } else {
+            NewtonChunk ch;
+            build_newton_chunk(h, ch, pd.fids, pd.ld, pd.fp64, pd.fused, scr, pd.p);
+            (pd.fp64 ? rt.chunks64 : rt.chunks32).push_back(std::move(ch));
+        }
         if (async)
             for (size_t k = 0; k < pd.fids.size(); ++k) {
                 h->factors[pd.fids[k]].off_s = saved[k].first;
                 h->factors[pd.fids[k]].off_p = saved[k].second;
             }
-        RootTables& rt = async ? h->async_roots[pd.set - 1 - nparts] : h->roots[pd.set];
-        (pd.fp64 ? rt.chunks64 : rt.chunks32).push_back(std::move(ch));
     }
+    h->slot_tmpl_off = blob.add(slot_tmpl);
+    for (auto& rt : h->roots) rt.compact_off = blob.add(rt.compact);
+    for (auto& rt : h->async_roots) rt.compact_off = blob.add(rt.compact);
     // copy jobs of the asynchronous pass: snapshot S and P of a part, and the
     // swap of its staged roots
     h->async_begin_off.assign(nparts, 0);
@@ -1325,7 +1390,13 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
         na.p = p;
         g.xc1 = (double)(p + 1) / p;
         g.xc2 = -1.0 / p;
-        const FactorJob* jobs = tab<FactorJob>(h, ch.jobs_off);
+        // a packed chain reads the slot jobs written by k_route_compact and
+        // gates its products by the slot flags
+        const FactorJob* jobs = ch.compact ? at<FactorJob>(h, ch.slot_jobs_off)
+                                           : tab<FactorJob>(h, ch.jobs_off);
+        na.gate = ch.compact ? nullptr : gate;
+        g.gate = ch.compact ? at<int32_t>(h, h->off_slot_live) : gate;
+        g.gate_val = ch.compact ? 1 : gate_val;
         int rc;
         if (ch.fused) {
             // lambda_max, eps, the root and the kappa estimate of every factor
@@ -1420,8 +1491,18 @@ int enqueue_roots(shampoo_s* h, RootTables& rt, hipStream_t s) {
         lp.auto_route = c.root_mode == SHAMPOO_ROOT_AUTO ? 1 : 0;
         rc = lanczos(rt.lanczos_p_small_off, rt.lanczos_p_big_off, false, false, lp);
         if (rc) return rc;
-        if (c.root_mode == SHAMPOO_ROOT_AUTO)
+        if (c.root_mode == SHAMPOO_ROOT_AUTO) {
+            {
+                ProfScope ps(h, PC_ROUTE, s, !rt.compact.empty());
+                rc = hip_err(launch_route_compact(tab<CompactClass>(h, rt.compact_off),
+                                                  (int)rt.compact.size(),
+                                                  tab<FactorJob>(h, h->slot_tmpl_off), prec, 1,
+                                                  at<FactorJob>(h, h->off_slot_jobs),
+                                                  at<int32_t>(h, h->off_slot_live), s));
+            }
+            if (rc) return rc;
             rc = run_newton(h, rt.chunks64, true, prec, 1, prec, s);
+        }
         return rc;
     }
     // all fp64

@@ -106,6 +106,19 @@ struct FactorJob {
     int32_t pad_;
 };
 
+// One class (padded dimension, root exponent) of the gated fp64 Newton chain.
+// The factors whose precision flag routes them to fp64 are packed, in class
+// order, into the leading slots of the class, so that the chain's launches
+// run on the routed factors only; slot k's scratch sits at place k mod cap
+// of its chunk.
+struct CompactClass {
+    int32_t first;   // first entry of the class in the template, slot-job and slot-flag arrays
+    int32_t n;       // factors (and slots) in the class
+    int32_t cap;     // slots per scratch chunk
+    int32_t pad_;
+    int64_t mat;     // ld * ld (six scratch matrices per slot)
+};
+
 // A run of rows of one dense tensor for the elementwise kernels.
 struct RowChunk {
     int32_t tensor;       // tensor index (its gradient/weight base = 1 + tensor, 1 + n + tensor)

@@ -1036,6 +1036,55 @@ __global__ __launch_bounds__(64) void k_lz_finish(const LanczosJob* __restrict__
 }
 
 // ======================================================= coupled Newton
+// Packs, per class of the gated fp64 chain (one workgroup each), the factors
+// whose precision flag equals gate_val into the leading slots of the class in
+// class order (a ballot prefix sum per pass of 1024 factors).  Slot k gets
+// the factor's job with the scratch place k mod cap of its chunk and flag 1;
+// the slots past the count get factor -1 (the chain's start and finish skip
+// them) and flag 0 (its products skip them).
+__global__ __launch_bounds__(1024) void k_route_compact(const CompactClass* __restrict__ cls,
+                                                       const FactorJob* __restrict__ tmpl,
+                                                       const int32_t* __restrict__ prec, int gate_val,
+                                                       FactorJob* __restrict__ slots,
+                                                       int32_t* __restrict__ live) {
+    __shared__ int wtot[16];
+    const CompactClass c = cls[blockIdx.x];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    int carry = 0;
+    for (int base = 0; base < c.n; base += 1024) {
+        const int i = base + t;
+        FactorJob j{};
+        bool f = false;
+        if (i < c.n) {
+            j = tmpl[c.first + i];
+            f = prec[j.factor] == gate_val;
+        }
+        const unsigned long long m = __ballot(f);
+        if (lane == 0) wtot[w] = __popcll(m);
+        __syncthreads();
+        int before = carry, tot = 0;
+        for (int q = 0; q < 16; ++q) {
+            before += q < w ? wtot[q] : 0;
+            tot += wtot[q];
+        }
+        if (f) {
+            const int k = before + __popcll(m & ((1ull << lane) - 1ull));
+            j.x_off = (int64_t)(k % c.cap) * 6 * c.mat;
+            j.m_off = j.x_off + 2 * c.mat;
+            slots[c.first + k] = j;
+            live[c.first + k] = 1;
+        }
+        carry += tot;
+        __syncthreads();   // wtot is rewritten by the next pass
+    }
+    for (int k = carry + t; k < c.n; k += 1024) {
+        FactorJob j{};
+        j.factor = -1;
+        slots[c.first + k] = j;
+        live[c.first + k] = 0;
+    }
+}
+
 // Coupled Newton iteration for the inverse p-th root (Guo & Higham, SIAM J.
 // Matrix Anal. Appl. 28(3), 2006).  With A = S + eps I (S read from its upper
 // triangle) and z = (p+1) / (2 lambda_max(A)):  X_0 = z^(1/p) I, M_0 = z A; then
@@ -1055,7 +1104,7 @@ __global__ __launch_bounds__(256) void k_newton_init(const FactorJob* __restrict
                                                     NewtonArgs args) {
     __shared__ double ts[32][33];
     const FactorJob jb = jobs[blockIdx.y];
-    if (args.gate && args.gate[jb.factor] != args.gate_val) return;
+    if (jb.factor < 0 || (args.gate && args.gate[jb.factor] != args.gate_val)) return;
     const int n = jb.n, ld = jb.ld, nt = ld >> 5;
     if (blockIdx.x == 0 && threadIdx.x == 0) {   // the finish's check slots of this pass
         args.chk[2 * jb.factor] = 0ull;
@@ -1111,7 +1160,7 @@ __global__ __launch_bounds__(256) void k_newton_check(const FactorJob* __restric
                                                      NewtonArgs args) {
     __shared__ double red[4];
     const FactorJob jb = jobs[blockIdx.y];
-    if (args.gate && args.gate[jb.factor] != args.gate_val) return;
+    if (jb.factor < 0 || (args.gate && args.gate[jb.factor] != args.gate_val)) return;
     if (diag[jb.factor].status & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_ZERO_)) return;
     const int n = jb.n, ld = jb.ld, nt = ld >> 5;
     const T* X = scratch + jb.x_off;
@@ -1153,7 +1202,7 @@ __global__ __launch_bounds__(256) void k_newton_commit(const FactorJob* __restri
                                                       NewtonArgs args) {
     __shared__ double tm[32][33];
     const FactorJob jb = jobs[blockIdx.y];
-    if (args.gate && args.gate[jb.factor] != args.gate_val) return;
+    if (jb.factor < 0 || (args.gate && args.gate[jb.factor] != args.gate_val)) return;
     const int n = jb.n, ld = jb.ld, nt = ld >> 5;
     // status bits set before the iteration; this pass only adds others
     const int st0 = diag[jb.factor].status & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_ZERO_);
@@ -2433,6 +2482,14 @@ hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, 
             hipLaunchKernelGGL(k_lanczos<float>, dim3(njobs), dim3(256), 0, s, jobs,
                                static_cast<const float*>(arena), a);
     }
+    return hipGetLastError();
+}
+hipError_t launch_route_compact(const CompactClass* cls, int ncls, const FactorJob* tmpl,
+                                const int32_t* prec, int gate_val, FactorJob* slots, int32_t* live,
+                                hipStream_t s) {
+    if (ncls <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_route_compact, dim3(ncls), dim3(1024), 0, s, cls, tmpl, prec, gate_val, slots,
+                       live);
     return hipGetLastError();
 }
 hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, int ld,

@@ -76,6 +76,11 @@ hipError_t launch_step128(const StepJob* jobs, int njobs, const uint64_t* bases,
                           const UpdateArgs& ua, hipStream_t s);
 hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, bool fp64_matrix,
                           bool big, const LanczosArgs& a, hipStream_t s);
+// Packs the factors of each class routed to fp64 (flag gate_val) into the
+// class's leading slots: slot jobs and slot flags (one workgroup per class).
+hipError_t launch_route_compact(const CompactClass* cls, int ncls, const FactorJob* tmpl,
+                                const int32_t* prec, int gate_val, FactorJob* slots, int32_t* live,
+                                hipStream_t s);
 // Newton start and finish, one workgroup per 32 x 32 tile of every factor of
 // a chunk (factors of leading dimension ld).
 hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, int ld,

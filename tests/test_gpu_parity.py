@@ -186,6 +186,38 @@ def test_cfg0_roots_f64():
     run_parity(synth.workload(0), steps=3, root_mode="f64")
 
 
+def test_packed_fp64_chain_over_several_chunks(monkeypatch):
+    """AUTO runs the fp64 chain on the routed factors only, packed in factor
+    order into slots; a scratch budget of one factor of 128 spreads cfg0's
+    routed factors over several chunks.  The roots, diagnostics and updates
+    are bitwise those of the one-chunk run, and parity with the oracle holds."""
+    wl = synth.workload(0)
+    runs = []
+    for budget in (None, 6 * 128 * 128 * 8):
+        if budget is not None:
+            monkeypatch.setenv("SHAMPOO_NEWTON_SCRATCH_BYTES", str(budget))
+        say(f"packed fp64 chain, scratch budget {budget}")
+        run = GpuRun(wl)
+        for t in range(2):
+            _, dev, sp = run.grads_at(t)
+            run.step(t, dev, sp, cadence=1)
+            torch.cuda.synchronize()
+            if t == 0:
+                routed = sum(1 for d in run.opt.diagnostics() if d.status & FP64)
+                assert routed >= 2, routed   # more than one chunk of one slot
+        runs.append(run)
+    one, many = runs
+    for a, b in zip(one.params, many.params):
+        assert torch.equal(a, b)
+    for i in range(one.opt.n_blocks):
+        for x, y in zip(one.opt.roots(i, fp64=True) + one.opt.roots(i),
+                        many.opt.roots(i, fp64=True) + many.opt.roots(i)):
+            assert torch.equal(x, y), i
+    for d1, d2 in zip(one.opt.diagnostics(), many.opt.diagnostics()):
+        assert (d1.status, d1.residual, d1.kappa_est) == (d2.status, d2.residual, d2.kappa_est)
+    run_parity(wl, steps=2)
+
+
 def test_staggered_root_parts():
     """Staggered root pass: 8 blocks of 128 (cfg0 shapes), roots every 4
     steps in 2 and in 4 parts (one part every 2 steps / every step); every

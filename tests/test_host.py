@@ -212,3 +212,23 @@ def test_one_sided_config_errors():
     big = (S.TensorDesc * 1)(S.TensorDesc(5000, 2048, 0, 0))
     c = S.make_config(64, max_precond_dim=4096, large_layer=1)
     assert L.shampoo_create(ctypes.byref(c), 1, big, ctypes.byref(h)) == -5
+
+
+def test_newton_scratch_budget_from_environment(monkeypatch):
+    """The batched Newton scratch (six ld x ld matrices per factor of a chunk)
+    follows SHAMPOO_NEWTON_SCRATCH_BYTES, read at create: 8 factors of 256 in
+    AUTO mode take 8 slots per precision by default, and with a budget of
+    3 MiB two fp32 slots and one fp64 slot (more chunks, more launch tables)."""
+    shapes = [(512, 512, 0)]
+    cfg = S.make_config(256, root_mode="auto")
+    p = S.Plan(shapes, cfg)
+    full = p.state_bytes
+    p.close()
+    monkeypatch.setenv("SHAMPOO_NEWTON_SCRATCH_BYTES", str(3 << 20))
+    p = S.Plan(shapes, cfg)
+    small = p.state_bytes
+    p.close()
+    per32, per64 = 6 * 256 * 256 * 4, 6 * 256 * 256 * 8
+    saved = (8 - 2) * per32 + (8 - 1) * per64
+    # the launch tables of the extra chunks (a few KB) take some of it back
+    assert 0 <= saved - (full - small) < 64 << 10
