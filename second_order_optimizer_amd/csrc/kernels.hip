@@ -602,25 +602,26 @@ __global__ __launch_bounds__(512, 4) void k_gram128(const GramJob* __restrict__ 
 // values, it never moves the largest Ritz value above lambda_max).  Vectors
 // in fp64 in LDS; the matrix is read in fp32 column-wise (coalesced; the
 // matrix is symmetric so S v = S^T v).  The tridiagonal's extremes come from
-// Sturm-count bisection.
+// Sturm-count multisection.
 constexpr int kLanczosMaxN = 1024;
 constexpr int kLanczosMaxSteps = 64;
 
-__device__ __forceinline__ int sturm_count(const double* al, const double* be, int m, double x) {
-    int cnt = 0;
-    double d = 1.0;
-    for (int k = 0; k < m; ++k) {
-        const double b2 = k ? be[k - 1] * be[k - 1] : 0.0;
-        d = (al[k] - x) - (k ? b2 / d : 0.0);
-        if (d == 0.0) d = -1e-300;
-        if (d < 0) ++cnt;
-    }
-    return cnt;
+// One step of the Sturm recurrence d_k = (a_k - x) - b_{k-1}^2 / d_{k-1}, the
+// quotient taken as b^2 times the hardware reciprocal refined by one Newton
+// step (full double accuracy; the raw reciprocal is kept when d_{k-1} is
+// infinite, where the refinement would give NaN and the quotient is 0).
+__device__ __forceinline__ double sturm_step(double d, double a_minus_x, double b2) {
+    double r = __builtin_amdgcn_rcp(d);
+    const double rr = fma(r, fma(-d, r, 1.0), r);
+    r = rr == rr ? rr : r;
+    d = fma(-b2, r, a_minus_x);
+    return d == 0.0 ? -1e-300 : d;
 }
 
 // Largest eigenvalue of the m x m tridiagonal (al, be) by Sturm-count
-// multisection on one wave: every lane counts at its own point of the
-// bracket, so each round shrinks it 65-fold.  NaN for non-finite input.
+// multisection on one wave: every lane counts the eigenvalues below two
+// points of the bracket (two independent recurrences in flight), so each
+// round shrinks it 129-fold.  NaN for non-finite input.
 __device__ __forceinline__ double tridiag_max_wave(const double* al, const double* be, int m) {
     const int lane = threadIdx.x & 63;
     double lo = 0.0, hi = 0.0;
@@ -634,15 +635,28 @@ __device__ __forceinline__ double tridiag_max_wave(const double* al, const doubl
     if (!finite) return NAN;
     for (int round = 0; round < 12; ++round) {
         if (!(hi - lo > 1e-15 * fmax(fabs(lo), fabs(hi)))) break;
-        const double x = lo + (hi - lo) * (double)(lane + 1) / 65.0;
-        const bool above = sturm_count(al, be, m, x) >= m;   // x exceeds every eigenvalue
-        const uint64_t mask = __ballot(above);
-        if (mask == 0) {
-            lo = lo + (hi - lo) * 64.0 / 65.0;
+        const double h = (hi - lo) / 129.0;
+        const double x0 = lo + h * (double)(2 * lane + 1), x1 = lo + h * (double)(2 * lane + 2);
+        double d0 = al[0] - x0, d1 = al[0] - x1;
+        if (d0 == 0.0) d0 = -1e-300;
+        if (d1 == 0.0) d1 = -1e-300;
+        int c0 = d0 < 0.0, c1 = d1 < 0.0;
+        for (int k = 1; k < m; ++k) {
+            const double b2 = be[k - 1] * be[k - 1], a = al[k];
+            d0 = sturm_step(d0, a - x0, b2);
+            d1 = sturm_step(d1, a - x1, b2);
+            c0 += d0 < 0.0;
+            c1 += d1 < 0.0;
+        }
+        // the first point above every eigenvalue (point j = 2 lane + 1 + s)
+        const uint64_t m0 = __ballot(c0 >= m), m1 = __ballot(c1 >= m);
+        int j = 129;
+        if (m0) j = 2 * (__ffsll((unsigned long long)m0) - 1) + 1;
+        if (m1) j = min(j, 2 * (__ffsll((unsigned long long)m1) - 1) + 2);
+        if (j == 129) {
+            lo = lo + h * 128.0;
         } else {
-            const int f = __ffsll((unsigned long long)mask) - 1;
-            const double nlo = lo + (hi - lo) * (double)f / 65.0;
-            const double nhi = lo + (hi - lo) * (double)(f + 1) / 65.0;
+            const double nlo = lo + h * (double)(j - 1), nhi = lo + h * (double)j;
             lo = nlo;
             hi = nhi;
         }
@@ -661,16 +675,25 @@ __host__ __device__ constexpr int pcol(int j) { return (j & ~0x24) | ((j & 4) <<
 __device__ __forceinline__ int sidx(int r, int j) { return r * kSP + pcol(j); }
 
 // Stages the symmetric n x n matrix whose upper triangle is at S (row pitch
-// ld, n <= 128) into a slot in fp32, zero outside n x n.
+// ld, n <= 128) into a slot in fp32, zero outside n x n: sixteen loads in
+// flight per thread, then their stores (each upper element and its mirror).
 template <typename TM>
 __device__ __forceinline__ void stage_sym(float* slot, const TM* S, int n, int ld) {
-#pragma unroll 4
-    for (int e = threadIdx.x; e < 128 * 128; e += 256) {
-        const int i = e >> 7, j = e & 127;
-        if (j >= i) {
-            const float x = (j < n) ? (float)S[(int64_t)i * ld + j] : 0.f;
-            slot[sidx(i, j)] = x;
-            slot[sidx(j, i)] = x;
+    constexpr int kB = 16;
+    for (int e0 = 0; e0 < 128 * 128; e0 += 256 * kB) {
+        float x[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int e = e0 + 256 * u + threadIdx.x, i = e >> 7, j = e & 127;
+            x[u] = (j >= i && j < n) ? (float)S[(int64_t)i * ld + j] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int e = e0 + 256 * u + threadIdx.x, i = e >> 7, j = e & 127;
+            if (j >= i) {
+                slot[sidx(i, j)] = x[u];
+                slot[sidx(j, i)] = x[u];
+            }
         }
     }
 }
@@ -715,13 +738,20 @@ __device__ __forceinline__ double lanczos_slot(const float* slot, int n, int ste
     const double* vb = L.v1 + 4 * hf;
     for (int k = 0; k < steps; ++k) {
         double s[4] = {0.0, 0.0, 0.0, 0.0};
+        // each half-row's 32 matrix entries and 32 vector entries are read
+        // before any product, so the LDS reads stay in flight together
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 2; ++u) {
+            float ar[32];
+            double vr[32];
 #pragma unroll
             for (int q = 0; q < 32; ++q) {
-                const int off = 64 * u + q;
-                s[q & 3] = fma((double)Ar[off], vb[pcol(off)], s[q & 3]);
+                ar[q] = Ar[64 * u + q];
+                vr[q] = vb[pcol(64 * u + q)];
             }
+#pragma unroll
+            for (int q = 0; q < 32; ++q) s[q & 3] = fma((double)ar[q], vr[q], s[q & 3]);
+        }
         double wr = (s[0] + s[1]) + (s[2] + s[3]);
         wr += __shfl_xor(wr, 32, 64);
         const double d = wave_sum(hf == 0 ? wr * v : 0.0);
