@@ -700,7 +700,7 @@ __device__ __forceinline__ void stage_sym(float* slot, const TM* S, int n, int l
 
 // Scratch of the slot Lanczos.
 struct LanczosSlot {
-    double v1[128];
+    alignas(16) float vf[128];   // v rounded to fp32, the operand of the product
     double al[kLanczosMaxSteps], be[kLanczosMaxSteps];
     double ra[4], rb[4];
     double res;
@@ -711,8 +711,14 @@ struct LanczosSlot {
 // after up to `steps` Lanczos steps.  Thread (wave w, lane l) owns row
 // r = 32w + l%32 and half of its columns; the two halves meet in one shuffle,
 // so v_r, the previous v_r and the new w_r stay in registers and only v is
-// shared through LDS.  Sums run in a fixed order: every thread sees the same
-// alpha and beta, so the early stop is uniform.
+// shared through LDS.  The product S v is formed in fp32 (the slot holds S in
+// fp32; v rounded to fp32, read four entries at a time as an LDS broadcast;
+// eight fp32 partial sums of eight terms each), which perturbs the Ritz
+// values by about 1e-6 of lambda_max; the recurrence itself runs in fp64.
+// ROWREG: the thread's 64 matrix entries are read into registers once.
+// Sums run in a fixed order: every thread sees the same alpha and beta, so
+// the early stop is uniform.
+template <bool ROWREG>
 __device__ __forceinline__ double lanczos_slot(const float* slot, int n, int steps, LanczosSlot& L) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int r = 32 * w + (lane & 31), hf = lane >> 5;
@@ -729,30 +735,38 @@ __device__ __forceinline__ double lanczos_slot(const float* slot, int n, int ste
         __syncthreads();
         v /= sqrt((L.ra[0] + L.ra[1]) + (L.ra[2] + L.ra[3]));
     }
-    if (hf == 0) L.v1[r] = v;
+    if (hf == 0) L.vf[r] = (float)v;
+    // physical columns 32hf + 64u + q hold logical columns pcol(64u + q) + 4hf;
+    // pcol keeps bits 0-1, so four consecutive q are four consecutive columns
+    const float* Ar = slot + r * kSP + 32 * hf;
+    const float* vb = L.vf + 4 * hf;
+    float row[ROWREG ? 64 : 1];
+    if constexpr (ROWREG) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int q = 0; q < 32; ++q) row[32 * u + q] = Ar[64 * u + q];
+    }
     __syncthreads();
     double v0 = 0.0, beta_prev = 0.0;
     int m_used = steps;
-    // physical columns 32hf + 64u + q hold logical columns pcol(64u + q) + 4hf
-    const float* Ar = slot + r * kSP + 32 * hf;
-    const double* vb = L.v1 + 4 * hf;
     for (int k = 0; k < steps; ++k) {
-        double s[4] = {0.0, 0.0, 0.0, 0.0};
-        // each half-row's 32 matrix entries and 32 vector entries are read
-        // before any product, so the LDS reads stay in flight together
+        float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            float ar[32];
-            double vr[32];
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int q = 0; q < 32; ++q) {
-                ar[q] = Ar[64 * u + q];
-                vr[q] = vb[pcol(64 * u + q)];
+            for (int a = 0; a < 8; ++a) {
+                const float4 vv = *reinterpret_cast<const float4*>(vb + pcol(64 * u + 4 * a));
+                float x[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = ROWREG ? row[32 * u + 4 * a + e] : Ar[64 * u + 4 * a + e];
+                s[4 * u + 0] = fmaf(x[0], vv.x, s[4 * u + 0]);
+                s[4 * u + 1] = fmaf(x[1], vv.y, s[4 * u + 1]);
+                s[4 * u + 2] = fmaf(x[2], vv.z, s[4 * u + 2]);
+                s[4 * u + 3] = fmaf(x[3], vv.w, s[4 * u + 3]);
             }
-#pragma unroll
-            for (int q = 0; q < 32; ++q) s[q & 3] = fma((double)ar[q], vr[q], s[q & 3]);
-        }
-        double wr = (s[0] + s[1]) + (s[2] + s[3]);
+        double wr = (((double)s[0] + (double)s[1]) + ((double)s[2] + (double)s[3])) +
+                    (((double)s[4] + (double)s[5]) + ((double)s[6] + (double)s[7]));
         wr += __shfl_xor(wr, 32, 64);
         const double d = wave_sum(hf == 0 ? wr * v : 0.0);
         if (lane == 0) L.ra[w] = d;
@@ -773,7 +787,7 @@ __device__ __forceinline__ double lanczos_slot(const float* slot, int n, int ste
         }
         v0 = v;
         v = x / beta;
-        if (hf == 0) L.v1[r] = v;
+        if (hf == 0) L.vf[r] = (float)v;
         beta_prev = beta;
         __syncthreads();
     }
@@ -828,7 +842,7 @@ __global__ __launch_bounds__(256, 2) void k_lanczos(const LanczosJob* __restrict
     const LanczosJob jb = jobs[blockIdx.x];
     stage_sym(slot, arena + jb.off, jb.n, jb.ld);
     __syncthreads();
-    const double lmax = lanczos_slot(slot, jb.n, args.steps, lz);
+    const double lmax = lanczos_slot<true>(slot, jb.n, args.steps, lz);
     if (threadIdx.x == 0) lanczos_finish(args, jb, isfinite(lmax), lmax);
 }
 
@@ -1401,7 +1415,7 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
     __syncthreads();
 
     // ---- lambda_max (Lanczos) -> eps, status
-    const double lmax = lanczos_slot(slot, n, args.steps_s, lz);
+    const double lmax = lanczos_slot<true>(slot, n, args.steps_s, lz);
     int st0 = 0;
     if (!isfinite(lmax)) st0 = SHAMPOO_FACTOR_NONFINITE_INPUT_;
     else if (!(lmax > 0.0)) st0 = SHAMPOO_FACTOR_ZERO_;
@@ -1508,7 +1522,7 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
     // X is in the slot (identity block outside n x n, decoupled).
     double kap = 0.0;
     if (ok) {
-        const double lx = lanczos_slot(slot, n, args.steps_p, lz);
+        const double lx = lanczos_slot<false>(slot, n, args.steps_p, lz);
         if (isfinite(lx) && lx > 0.0) kap = lam * pow(lx, (double)p);
     }
 
