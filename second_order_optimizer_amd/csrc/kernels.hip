@@ -1403,6 +1403,7 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
     __shared__ __align__(16) float slot[128 * kSP];
     __shared__ LanczosSlot lz;
     __shared__ double red[4];
+    __shared__ double sh_lmax;   // re-read after the iteration: no set-up value lives across it
     const FactorJob jb = jobs[blockIdx.x];
     const int n = jb.n, ld = jb.ld;
     constexpr int p = PP;
@@ -1415,18 +1416,29 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
     __syncthreads();
 
     // ---- lambda_max (Lanczos) -> eps, status
-    const double lmax = lanczos_slot<true>(slot, n, args.steps_s, lz);
-    int st0 = 0;
-    if (!isfinite(lmax)) st0 = SHAMPOO_FACTOR_NONFINITE_INPUT_;
-    else if (!(lmax > 0.0)) st0 = SHAMPOO_FACTOR_ZERO_;
-    const bool ok = st0 == 0;
-    const double eps = ok ? args.eps_rel * lmax : 0.0;
-    const double lam = lmax + eps;
-    const float z = ok ? float((p + 1) / (2.0 * lam)) : 1.f;
-    const float zr = ok ? float(pow((p + 1) / (2.0 * lam), 1.0 / p)) : 1.f;
-    const float e = float(eps);
+    auto setup = [&](double lm, int& st, bool& good, double& ep, double& la) {
+        st = 0;
+        if (!isfinite(lm)) st = SHAMPOO_FACTOR_NONFINITE_INPUT_;
+        else if (!(lm > 0.0)) st = SHAMPOO_FACTOR_ZERO_;
+        good = st == 0;
+        ep = good ? args.eps_rel * lm : 0.0;
+        la = lm + ep;
+    };
+    float z, zr, e;
+    int iters;
+    bool okp;
+    {
+        const double lm = lanczos_slot<true>(slot, n, args.steps_s, lz);
+        if (t == 0) sh_lmax = lm;
+        int st;
+        double ep, la;
+        setup(lm, st, okp, ep, la);
+        z = okp ? float((p + 1) / (2.0 * la)) : 1.f;
+        zr = okp ? float(pow((p + 1) / (2.0 * la), 1.0 / p)) : 1.f;
+        e = float(ep);
+        iters = okp ? args.iters : 0;
+    }
     const float c1 = float((double)(p + 1) / p), c2 = float(-1.0 / p);
-    const int iters = ok ? args.iters : 0;
 
     // ---- M0 = z (S + eps I) in place in the slot (identity outside n x n),
     // read into the strips; then X0 = z^(1/p) I (identity outside n x n).
@@ -1435,7 +1447,7 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
     for (int e2 = t; e2 < 128 * 128; e2 += 256) {
         const int i = e2 >> 7, j = e2 & 127;
         float* q = slot + sidx(i, j);
-        *q = (ok && i < n && j < n) ? z * (*q + (i == j ? e : 0.f)) : (i == j ? 1.f : 0.f);
+        *q = (okp && i < n && j < n) ? z * (*q + (i == j ? e : 0.f)) : (i == j ? 1.f : 0.f);
     }
     __syncthreads();
     CStrip M;
@@ -1449,7 +1461,7 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
     __syncthreads();
     for (int e2 = t; e2 < 128 * 128; e2 += 256) {
         const int i = e2 >> 7, j = e2 & 127;
-        slot[sidx(i, j)] = (i == j) ? ((ok && i < n) ? zr : 1.f) : 0.f;
+        slot[sidx(i, j)] = (i == j) ? ((okp && i < n) ? zr : 1.f) : 0.f;
     }
     __syncthreads();
 
@@ -1494,6 +1506,11 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
 
     // ---- commit.  Outside n x n both iterates hold the identity, so the
     // finiteness test and the residual run over the whole padded tile.
+    const double lmax = sh_lmax;
+    int st0;
+    bool ok;
+    double eps, lam;
+    setup(lmax, st0, ok, eps, lam);
     double bad = 0.0;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -1522,7 +1539,7 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
     // X is in the slot (identity block outside n x n, decoupled).
     double kap = 0.0;
     if (ok) {
-        const double lx = lanczos_slot<false>(slot, n, args.steps_p, lz);
+        const double lx = lanczos_slot<true>(slot, n, args.steps_p, lz);
         if (isfinite(lx) && lx > 0.0) kap = lam * pow(lx, (double)p);
     }
 
