@@ -847,12 +847,15 @@ __global__ __launch_bounds__(256, 2) void k_lanczos(const LanczosJob* __restrict
 }
 
 // Same for one factor of 129..1024 per workgroup of 1024 threads, matrix read
-// from memory: w = S v as row dot products, wave w taking rows i = w (mod 16)
-// four at a time (64 loads in flight per lane), lane l columns l + 64m
-// (coalesced row segments) against v held in registers, each row's sum a
-// fixed butterfly over the wave.  Vectors in fp64 in LDS.
+// from memory, upper triangle only (half the bytes of the full matrix): wave w
+// takes rows i = w (mod 16) four at a time, lane l columns l + 64m >= i
+// (coalesced row segments) against v held in registers; each row's dot
+// product is a fixed-order sum over the wave, and the mirrored entries' terms
+// collect per lane and column, then over the sixteen waves in wave order.
+// Vectors in fp64 in LDS.
 struct LanczosBig {
     double v0[kLanczosMaxN], v1[kLanczosMaxN], wv[kLanczosMaxN];
+    double part[16 * kLanczosMaxN];   // per-wave column sums of the product
     double al[kLanczosMaxSteps], be[kLanczosMaxSteps];
     double red[16];
     double res;
@@ -907,11 +910,17 @@ __global__ __launch_bounds__(1024) void k_lanczos_big(const LanczosJob* __restri
 
     double beta_prev = 0.0;
     for (int k = 0; k < steps; ++k) {
-        // w = S v as row dot products (S symmetric): v in registers, each
-        // wave takes rows w, w + 8, ..., four rows' loads in flight at once
-        double vr[16];
+        // w = S v from the upper triangle of S only (the matrix is symmetric):
+        // row i's entries j >= i give its dot product with v (summed over the
+        // wave), and each entry j > i also adds S_ij v_i to the lane's
+        // partial of w_j.  v in registers; each wave takes rows w, w + 16,
+        // ..., four rows' loads in flight at once.
+        double vr[16], wc[16];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) vr[m] = (l + 64 * m < n) ? L.v1[l + 64 * m] : 0.0;
+        for (int m = 0; m < 16; ++m) {
+            vr[m] = (l + 64 * m < n) ? L.v1[l + 64 * m] : 0.0;
+            wc[m] = 0.0;
+        }
         for (int i0 = w; i0 < n; i0 += 64) {
             double acc[4];
 #pragma unroll
@@ -920,9 +929,16 @@ __global__ __launch_bounds__(1024) void k_lanczos_big(const LanczosJob* __restri
                 const int i = i0 + 16 * r;
                 if (i < n) {
                     const TM* row = S + (int64_t)i * ld;
+                    const double vi = L.v1[i];
 #pragma unroll
-                    for (int m = 0; m < 16; ++m)
-                        if (l + 64 * m < n) acc[r] += (double)row[l + 64 * m] * vr[m];
+                    for (int m = 0; m < 16; ++m) {
+                        const int j = l + 64 * m;
+                        if (j >= i && j < n) {
+                            const double sij = (double)row[j];
+                            acc[r] += sij * vr[m];
+                            if (j > i) wc[m] += sij * vi;
+                        }
+                    }
                 }
             }
 #pragma unroll
@@ -931,9 +947,20 @@ __global__ __launch_bounds__(1024) void k_lanczos_big(const LanczosJob* __restri
                 if (l == 0 && i0 + 16 * r < n) L.wv[i0 + 16 * r] = x;
             }
         }
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+            if (l + 64 * m < n) L.part[w * kLanczosMaxN + l + 64 * m] = wc[m];
         __syncthreads();
+        // w_j = (row part) + the sixteen waves' column parts, in wave order
         double d = 0.0;
-        for (int j = t; j < n; j += 1024) d += L.wv[j] * L.v1[j];
+        for (int j = t; j < n; j += 1024) {
+            double cs = 0.0;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) cs += L.part[q * kLanczosMaxN + j];
+            const double wj = L.wv[j] + cs;
+            L.wv[j] = wj;
+            d += wj * L.v1[j];
+        }
         const double alpha = block_sum_1024(d, L.red);
         double q = 0.0;
         for (int j = t; j < n; j += 1024) {
