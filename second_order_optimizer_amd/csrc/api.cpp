@@ -34,6 +34,7 @@ constexpr int kRingSlots = 16;        // pinned staging slots for per-call table
 constexpr size_t kNewtonScratchBudget = size_t(4) << 30;  // bytes per precision (default)
 constexpr int kSplitKTiles = 512;     // one-sided statistics: target tiles per launch
 constexpr int kSplitKMin = 512;       // and shortest chunk of the long dimension
+constexpr int kNewtonSplitTiles = 256;  // Newton stages with fewer tiles are split over k
 constexpr int kSosMaxChunks = 64;     // sparse one-sided tables: split-K chunks per call, at most,
 constexpr int kSosMinRows = 256;      // of at least this many listed rows (measured best)
 
@@ -79,6 +80,15 @@ struct LaunchRef {
     int ntiles = 0;
 };
 
+// One GEMM launch of a Newton iteration; a launch with few tiles is split
+// over k into `parts` partial products that a second launch sums.
+struct NewtonStage {
+    LaunchRef gemm;
+    int parts = 1;
+    int64_t sum_jobs_off = 0, sum_tiles_off = 0;   // SplitSumJob / TileRef tables (bytes)
+    int sum_ntiles = 0;
+};
+
 struct NewtonChunk {
     int ld = 0;
     int p = 4;                               // root exponent of its factors
@@ -88,7 +98,7 @@ struct NewtonChunk {
     int64_t jobs_off = 0;                    // FactorJob table (bytes)
     bool compact = false;                    // gated fp64 chain on packed slots: the jobs
     int64_t slot_jobs_off = 0;               // are written on the device (arena bytes)
-    std::vector<LaunchRef> stages[2];        // per parity
+    std::vector<NewtonStage> stages[2];      // per parity
 };
 
 // The launches of one root pass over a set of factors.
@@ -149,6 +159,7 @@ struct shampoo_s {
     int64_t off_slot_jobs = 0, off_slot_live = 0;  // packed fp64 chain: slot jobs and flags
     int64_t slot_tmpl_off = 0;                     // and the template job of every slot entry
     int64_t off_scr32 = 0, off_scr64 = 0, off_partA = 0, off_partD = 0, off_scale = 0;
+    int64_t off_split32 = 0, off_split64 = 0;   // partial products of split Newton stages
     int n_partA = 0, n_partD = 0;
     Blob blob;  // static tables (offsets relative to off_tables)
 
@@ -279,6 +290,29 @@ LaunchRef add_launch(Blob& blob, const std::vector<GemmTask>& tasks) {
     return L;
 }
 
+// Split-K parts for a Newton stage of `tiles` upper 128 x 128 tiles over
+// k = ld: 1 when the stage already fills the GPU, else the largest power of
+// two up to 8 that keeps the parts' tiles within 1024 and each part a
+// multiple of 32 and at least 64 deep.
+int newton_split(int tiles, int ld) {
+    if (tiles >= kNewtonSplitTiles) return 1;
+    int s = 1;
+    while (s < 8 && tiles * s * 2 <= 1024 && ld % (64 * s) == 0 && ld / (2 * s) >= 64) s *= 2;
+    return s;
+}
+
+// Partial-product scratch of the split stages of a chunk of nf factors
+// (stage 0 has two products per factor, the others one).
+int64_t newton_split_bytes(int nf, int ld, int64_t esz) {
+    const int t1 = ceil_div(ld, kTile), ut = t1 * (t1 + 1) / 2;
+    int64_t best = 0;
+    for (int tasks : {2 * nf, nf}) {
+        const int parts = newton_split(tasks * ut, ld);
+        if (parts > 1) best = std::max(best, (int64_t)tasks * parts * ld * ld * esz);
+    }
+    return best;
+}
+
 // Coupled-Newton iterations for exponent p.  newton_iters is the count at
 // p = 4.  In the first phase of the iteration the smallest scaled eigenvalue
 // of M grows by g_p = ((p + 1) / p)^p per step (2.44 at p = 4, 2.25 at p = 2,
@@ -292,9 +326,10 @@ int newton_iters_for(const shampoo_config& c, int p) {
 
 // Builds the per-parity GEMM launches of one Newton chunk.
 // gids: the gating id of each factor's products (default: the factor id).
+// split_off_bytes: the partial-product scratch of split stages.
 void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& fids, int ld,
                         bool fp64, bool fused, int64_t scratch_off_bytes, int p,
-                        const std::vector<int>* gids = nullptr) {
+                        int64_t split_off_bytes, const std::vector<int>* gids = nullptr) {
     ch.p = p;
     ch.iters = newton_iters_for(h->cfg, p);
     const int64_t esz = fp64 ? 8 : 4;
@@ -360,7 +395,44 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
             }
             st[k].push_back(mk(cur, Mq, Mn, 16 | 32, fid));
         }
-        for (auto& tasks : st) ch.stages[q].push_back(add_launch(h->blob, tasks));
+        // a stage with few tiles is split over k: part c of a product sums
+        // k in [c ld/parts, (c+1) ld/parts) into its own partial (upper
+        // tiles), and the sum writes both triangles of the destination
+        const int ut = tiles1 * (tiles1 + 1) / 2;
+        for (auto& tasks : st) {
+            NewtonStage ns;
+            const int parts = newton_split((int)tasks.size() * ut, ld);
+            if (parts == 1) {
+                ns.gemm = add_launch(h->blob, tasks);
+            } else {
+                const int64_t pbase = split_off_bytes / esz;
+                const int kp = ld / parts, t32 = ld / 32;
+                std::vector<GemmTask> sp;
+                std::vector<SplitSumJob> jobs;
+                std::vector<TileRef> tl;
+                for (size_t i = 0; i < tasks.size(); ++i) {
+                    const GemmTask& t = tasks[i];
+                    const int64_t po = pbase + (int64_t)i * parts * mat;
+                    for (int c = 0; c < parts; ++c) {
+                        GemmTask u = t;
+                        u.kb = c * kp;
+                        u.K = (c + 1) * kp;
+                        u.c_off = po + c * mat;
+                        u.trans &= ~32;
+                        sp.push_back(u);
+                    }
+                    jobs.push_back(SplitSumJob{po, t.c_off, parts, ld, t32, t.factor});
+                    for (int bi = 0; bi < t32; ++bi)
+                        for (int bj = bi; bj < t32; ++bj) tl.push_back(TileRef{(int32_t)i, bi * t32 + bj});
+                }
+                ns.gemm = add_launch(h->blob, sp);
+                ns.parts = parts;
+                ns.sum_jobs_off = h->blob.add(jobs);
+                ns.sum_tiles_off = h->blob.add(tl);
+                ns.sum_ntiles = (int)tl.size();
+            }
+            ch.stages[q].push_back(ns);
+        }
     }
 }
 
@@ -524,6 +596,7 @@ int build_plan(shampoo_s* h) {
         bool compact = false; int cap = 0; int slot_first = 0;
     };
     int n_slots = 0;
+    int64_t split32 = 0, split64 = 0;
     int64_t scratch_budget = (int64_t)kNewtonScratchBudget;
     if (const char* e = std::getenv("SHAMPOO_NEWTON_SCRATCH_BYTES")) {
         const long long v = std::atoll(e);
@@ -563,7 +636,11 @@ int build_plan(shampoo_s* h) {
                 pd.cap = cap;
                 pd.slot_first = n_slots;
                 n_slots += (int)fids.size();
-                scr64 = std::max(scr64, per * (int64_t)std::min<size_t>(fids.size(), cap));
+                const int n = (int)fids.size();
+                scr64 = std::max(scr64, per * (int64_t)std::min(n, cap));
+                // chunks of cap slots and a last, smaller one
+                split64 = std::max(split64, newton_split_bytes(std::min(n, cap), ld, 8));
+                if (n > cap && n % cap) split64 = std::max(split64, newton_split_bytes(n % cap, ld, 8));
                 pend.push_back(std::move(pd));
                 continue;
             }
@@ -577,12 +654,16 @@ int build_plan(shampoo_s* h) {
                 pd.fids.assign(fids.begin() + s, fids.begin() + std::min(fids.size(), s + cap));
                 int64_t& scr = fp64 ? scr64 : scr32;
                 scr = std::max(scr, per * (int64_t)pd.fids.size());
+                int64_t& spl = fp64 ? split64 : split32;
+                spl = std::max(spl, newton_split_bytes((int)pd.fids.size(), ld, fp64 ? 8 : 4));
                 pend.push_back(std::move(pd));
             }
         }
     }
     h->off_scr32 = take(scr32);
     h->off_scr64 = take(scr64);
+    h->off_split32 = take(split32);
+    h->off_split64 = take(split64);
     h->off_slot_jobs = take((int64_t)n_slots * sizeof(FactorJob));
     h->off_slot_live = take((int64_t)n_slots * 4);
     // snapshot (fp64 statistics) and staging (fp32 roots) areas of the
@@ -900,14 +981,15 @@ int build_plan(shampoo_s* h) {
                 std::vector<int> fids(pd.fids.begin() + q0, pd.fids.begin() + q0 + m), gids(m);
                 for (int k = 0; k < m; ++k) gids[k] = pd.slot_first + q0 + k;
                 NewtonChunk ch;
-                build_newton_chunk(h, ch, fids, pd.ld, true, false, scr, pd.p, &gids);
+                build_newton_chunk(h, ch, fids, pd.ld, true, false, scr, pd.p, h->off_split64, &gids);
                 ch.compact = true;
                 ch.slot_jobs_off = h->off_slot_jobs + (int64_t)(pd.slot_first + q0) * sizeof(FactorJob);
                 rt.chunks64.push_back(std::move(ch));
             }
         } else {
             NewtonChunk ch;
-            build_newton_chunk(h, ch, pd.fids, pd.ld, pd.fp64, pd.fused, scr, pd.p);
+            build_newton_chunk(h, ch, pd.fids, pd.ld, pd.fp64, pd.fused, scr, pd.p,
+                               pd.fp64 ? h->off_split64 : h->off_split32);
             (pd.fp64 ? rt.chunks64 : rt.chunks32).push_back(std::move(ch));
         }
         if (async)
@@ -1422,12 +1504,16 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
         }
         if (rc) return rc;
         for (int it = 0; it < ch.iters; ++it) {
-            for (const LaunchRef& L : ch.stages[it & 1]) {
-                const GemmTask* tk = tab<GemmTask>(h, L.tasks_off);
-                const TileRef* tl = tab<TileRef>(h, L.tiles_off);
+            for (const NewtonStage& S : ch.stages[it & 1]) {
+                const GemmTask* tk = tab<GemmTask>(h, S.gemm.tasks_off);
+                const TileRef* tl = tab<TileRef>(h, S.gemm.tiles_off);
                 ProfScope ps(h, fp64 ? PC_NEWTON_GEMM64 : PC_NEWTON_GEMM32, s);
-                rc = hip_err(fp64 ? launch_gemm_f64(tk, tl, L.ntiles, bases, g, s)
-                                  : launch_gemm_f32(tk, tl, L.ntiles, bases, g, s));
+                rc = hip_err(fp64 ? launch_gemm_f64(tk, tl, S.gemm.ntiles, bases, g, s)
+                                  : launch_gemm_f32(tk, tl, S.gemm.ntiles, bases, g, s));
+                if (!rc && S.parts > 1)
+                    rc = hip_err(launch_split_sum(fp64, tab<SplitSumJob>(h, S.sum_jobs_off),
+                                                  tab<TileRef>(h, S.sum_tiles_off), S.sum_ntiles,
+                                                  h->arena, g.gate, g.gate_val, s));
                 if (rc) return rc;
             }
         }

@@ -26,7 +26,7 @@ struct GemmTask {
     int32_t tiles_n;              // ceil(N / 128)
     int32_t factor;               // gating factor id (-1: always run)
     int32_t norm_slot;            // first slot of per-tile ||C||^2 partials, -1: none
-    int32_t pad_;
+    int32_t kb;                   // first k of the product (a split-K part sums k in [kb, K))
 };
 
 // One Shampoo block of at most 128 x 128 for the fused statistics kernel.
@@ -76,6 +76,18 @@ struct SymReduceJob {
     int32_t nparts;     // number of partials
     int32_t dim, ld;
     int32_t tiles;      // 32 x 32 tiles per side: ceil(dim / 32)
+};
+
+// One symmetric product of the batched Newton chain that was split over k:
+// C = sum of its nparts partial products (upper 128 x 128 tiles of each), in
+// part order, written to both triangles of C.
+struct SplitSumJob {
+    int64_t part_off;   // first partial (elements of the chain's type from the arena base)
+    int64_t c_off;      // destination C (same units)
+    int32_t nparts;     // partials, ld * ld elements apart
+    int32_t ld;         // padded dimension (a multiple of 32)
+    int32_t tiles;      // ld / 32
+    int32_t gate;       // gating id (-1: always run)
 };
 
 // A tile of the batched GEMM launch: which task and which 128x128 tile.

@@ -135,12 +135,12 @@ struct StageLoader {
 
     __device__ __forceinline__ void load(const TI* __restrict__ X, int ld, bool kcontig,
                                          int r0, int k0, int R, int K, bool aligned,
-                                         bool xf, T c1, T c2) {
+                                         bool xf, T c1, T c2, int dk) {
         const int t = threadIdx.x;
         // uniform over the workgroup: the whole stage is in range (no checks),
         // and whether it meets the diagonal r == k
         const bool full = aligned && r0 + BM <= R && k0 + BK <= K;
-        const bool dg = xf && k0 < r0 + BM && r0 < k0 + BK;
+        const bool dg = xf && k0 + dk < r0 + BM && r0 < k0 + dk + BK;
         if (kcontig) {
             // 8 threads x VEC cover BK along k; 32 rows per pass, 4 passes.
             const int kq = t & 7, rr = t >> 3;
@@ -180,7 +180,7 @@ struct StageLoader {
                         const int k = k0 + kq * VEC;
 #pragma unroll
                         for (int e = 0; e < VEC; ++e)
-                            if (r == k + e && r < R && k + e < K) v[p][e] += c1;
+                            if (r == k + e + dk && r < R && k + e < K) v[p][e] += c1;
                     }
                 }
             }
@@ -225,7 +225,7 @@ struct StageLoader {
                         const int r = r0 + rq * VEC;
 #pragma unroll
                         for (int e = 0; e < VEC; ++e)
-                            if (r + e == k && k < K && r + e < R) v[p][e] += c1;
+                            if (r + e == k + dk && k < K && r + e < R) v[p][e] += c1;
                     }
                 }
             }
@@ -386,16 +386,28 @@ __global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__
 
     StageLoader<T, TA> la;
     StageLoader<T, TB> lb;
-    la.load(A, tk.lda, a_kc, i0, 0, tk.M, tk.K, a_al, xa, c1, c2);
-    lb.load(B, tk.ldb, b_kc, j0, 0, tk.N, tk.K, b_al, xb, c1, c2);
-    for (int k0 = 0; k0 < tk.K; k0 += BK) {
+    // A split-K part sums k in [kb, K).  fp32: the operands are offset to
+    // k = kb and the loop runs from 0 (a Newton operand's diagonal is found
+    // with offset kb); fp64: the loop runs from kb.  The two forms compute the
+    // same; each keeps its kernel at the register count of the unsplit loop
+    // (measured: the other form costs fp32 an occupancy step, fp64 spills).
+    constexpr bool kofs = sizeof(T) == 4;
+    const int kb = tk.kb;
+    const int kfirst = kofs ? 0 : kb, Kp = kofs ? tk.K - kb : tk.K, dk = kofs ? kb : 0;
+    if (kofs) {
+        A += a_kc ? (int64_t)kb : (int64_t)kb * tk.lda;
+        B += b_kc ? (int64_t)kb : (int64_t)kb * tk.ldb;
+    }
+    la.load(A, tk.lda, a_kc, i0, kfirst, tk.M, Kp, a_al, xa, c1, c2, dk);
+    lb.load(B, tk.ldb, b_kc, j0, kfirst, tk.N, Kp, b_al, xb, c1, c2, dk);
+    for (int k0 = kfirst; k0 < Kp; k0 += BK) {
         __syncthreads();
         la.store(As, a_kc);
         lb.store(Bs, b_kc);
         __syncthreads();
         if (k0 + BK < tk.K) {
-            la.load(A, tk.lda, a_kc, i0, k0 + BK, tk.M, tk.K, a_al, xa, c1, c2);
-            lb.load(B, tk.ldb, b_kc, j0, k0 + BK, tk.N, tk.K, b_al, xb, c1, c2);
+            la.load(A, tk.lda, a_kc, i0, k0 + BK, tk.M, Kp, a_al, xa, c1, c2, dk);
+            lb.load(B, tk.ldb, b_kc, j0, k0 + BK, tk.N, Kp, b_al, xb, c1, c2, dk);
         }
         wt.compute(As, Bs, wm, wn);
     }
@@ -2207,6 +2219,54 @@ __global__ __launch_bounds__(256) void k_sym_reduce(const SymReduceJob* __restri
             if (jt + e < jb.dim) S[(int64_t)it * jb.ld + jt + e] = T[c0 + e][r];
 }
 
+// Split-K products of the batched Newton chain: C = sum of the parts, in part
+// order, on one 32 x 32 tile pair (bi <= bj) of the symmetric product; the
+// tile is written at (bi, bj) and its transpose at (bj, bi) (a diagonal tile's
+// lower half from its upper half), over the whole padded ld x ld.
+template <typename T>
+__global__ __launch_bounds__(256) void k_split_sum(const SplitSumJob* __restrict__ jobs,
+                                                  const TileRef* __restrict__ tiles,
+                                                  T* __restrict__ base, const int32_t* __restrict__ gate,
+                                                  int gate_val) {
+    __shared__ T tt[32][33];
+    const TileRef tr = tiles[blockIdx.x];
+    const SplitSumJob jb = jobs[tr.task];
+    if (gate && jb.gate >= 0 && gate[jb.gate] != gate_val) return;
+    const int bi = tr.tile / jb.tiles, bj = tr.tile % jb.tiles;
+    const int r = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 4;
+    const int64_t mat = (int64_t)jb.ld * jb.ld;
+    const T* P = base + jb.part_off + (int64_t)(bi * 32 + r) * jb.ld + bj * 32 + c0;
+    T v[4] = {T(0), T(0), T(0), T(0)};
+    for (int c = 0; c < jb.nparts; ++c) {   // 16-byte aligned: ld and c0 are multiples of 4
+        const T* q = P + c * mat;
+        if constexpr (sizeof(T) == 4) {
+            const float4 a = *reinterpret_cast<const float4*>(q);
+            v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+        } else {
+            const double2 a = *reinterpret_cast<const double2*>(q);
+            const double2 b = *reinterpret_cast<const double2*>(q + 2);
+            v[0] += a.x; v[1] += a.y; v[2] += b.x; v[3] += b.y;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tt[r][c0 + e] = v[e];
+    __syncthreads();
+    T* C = base + jb.c_off;
+    if (bi == bj) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = c0 + e;
+            C[(int64_t)(bi * 32 + r) * jb.ld + bj * 32 + c] = r <= c ? tt[r][c] : tt[c][r];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            C[(int64_t)(bi * 32 + r) * jb.ld + bj * 32 + c0 + e] = tt[r][c0 + e];
+            C[(int64_t)(bj * 32 + r) * jb.ld + bi * 32 + c0 + e] = tt[c0 + e][r];
+        }
+    }
+}
+
 // Identity roots for every factor (state initialisation).
 __global__ __launch_bounds__(256) void k_set_identity(const FactorJob* __restrict__ jobs,
                                                      float* __restrict__ arena) {
@@ -2570,6 +2630,17 @@ hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, 
             hipLaunchKernelGGL(k_lanczos<float>, dim3(njobs), dim3(256), 0, s, jobs,
                                static_cast<const float*>(arena), a);
     }
+    return hipGetLastError();
+}
+hipError_t launch_split_sum(bool fp64, const SplitSumJob* jobs, const TileRef* tiles, int ntiles,
+                            void* arena, const int32_t* gate, int gate_val, hipStream_t s) {
+    if (ntiles <= 0) return hipSuccess;
+    if (fp64)
+        hipLaunchKernelGGL(k_split_sum<double>, dim3(ntiles), dim3(256), 0, s, jobs, tiles,
+                           static_cast<double*>(arena), gate, gate_val);
+    else
+        hipLaunchKernelGGL(k_split_sum<float>, dim3(ntiles), dim3(256), 0, s, jobs, tiles,
+                           static_cast<float*>(arena), gate, gate_val);
     return hipGetLastError();
 }
 hipError_t launch_route_compact(const CompactClass* cls, int ncls, const FactorJob* tmpl,

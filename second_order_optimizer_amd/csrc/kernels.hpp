@@ -76,6 +76,10 @@ hipError_t launch_step128(const StepJob* jobs, int njobs, const uint64_t* bases,
                           const UpdateArgs& ua, hipStream_t s);
 hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, bool fp64_matrix,
                           bool big, const LanczosArgs& a, hipStream_t s);
+// Sums the split-K parts of symmetric Newton products (one workgroup per
+// 32 x 32 tile pair) into both triangles of their destinations.
+hipError_t launch_split_sum(bool fp64, const SplitSumJob* jobs, const TileRef* tiles, int ntiles,
+                            void* arena, const int32_t* gate, int gate_val, hipStream_t s);
 // Packs the factors of each class routed to fp64 (flag gate_val) into the
 // class's leading slots: slot jobs and slot flags (one workgroup per class).
 hipError_t launch_route_compact(const CompactClass* cls, int ncls, const FactorJob* tmpl,

@@ -214,11 +214,31 @@ def test_one_sided_config_errors():
     assert L.shampoo_create(ctypes.byref(c), 1, big, ctypes.byref(h)) == -5
 
 
+def _newton_split_bytes(nf, ld, esz):
+    """Partial-product scratch of the split-K stages of a Newton chunk of nf
+    factors: a stage of fewer than 256 upper 128-tiles is split over k into
+    the largest power of two (up to 8) of parts that keeps its tiles within
+    1024 and each part a multiple of 32 and at least 64 deep; stage 0 has two
+    products per factor, the others one."""
+    t1 = -(-ld // 128)
+    ut = t1 * (t1 + 1) // 2
+    best = 0
+    for tasks in (2 * nf, nf):
+        tiles, s = tasks * ut, 1
+        if tiles < 256:
+            while s < 8 and tiles * s * 2 <= 1024 and ld % (64 * s) == 0 and ld // (2 * s) >= 64:
+                s *= 2
+        if s > 1:
+            best = max(best, tasks * s * ld * ld * esz)
+    return best
+
+
 def test_newton_scratch_budget_from_environment(monkeypatch):
     """The batched Newton scratch (six ld x ld matrices per factor of a chunk)
     follows SHAMPOO_NEWTON_SCRATCH_BYTES, read at create: 8 factors of 256 in
     AUTO mode take 8 slots per precision by default, and with a budget of
-    3 MiB two fp32 slots and one fp64 slot (more chunks, more launch tables)."""
+    3 MiB two fp32 slots and one fp64 slot (more chunks, more launch tables);
+    the partial products of split-K stages shrink with the chunks."""
     shapes = [(512, 512, 0)]
     cfg = S.make_config(256, root_mode="auto")
     p = S.Plan(shapes, cfg)
@@ -230,5 +250,7 @@ def test_newton_scratch_budget_from_environment(monkeypatch):
     p.close()
     per32, per64 = 6 * 256 * 256 * 4, 6 * 256 * 256 * 8
     saved = (8 - 2) * per32 + (8 - 1) * per64
+    saved += _newton_split_bytes(8, 256, 4) - _newton_split_bytes(2, 256, 4)
+    saved += _newton_split_bytes(8, 256, 8) - _newton_split_bytes(1, 256, 8)
     # the launch tables of the extra chunks (a few KB) take some of it back
     assert 0 <= saved - (full - small) < 64 << 10
