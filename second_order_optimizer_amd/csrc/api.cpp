@@ -165,6 +165,9 @@ struct shampoo_s {
 
     LaunchRef gram, apply1, apply2;   // blocks with a side > 128
     LaunchRef splitk;                 // one-sided statistics: partial products
+    LaunchRef gsplit;                 // blocks > 128 when few: statistics split over k
+    int64_t gred_jobs_off = 0, gred_tiles_off = 0;
+    int n_gred_tiles = 0;             // and the fixed-order sum of their partials
     std::vector<SosPlan> sos;         // sparse-row tables with one-sided preconditioning
     int64_t off_sos_stats = 0, off_sos_apply = 0;  // their per-call tables
     int64_t symred_jobs_off = 0, symred_tiles_off = 0;
@@ -567,6 +570,31 @@ int build_plan(shampoo_s* h) {
         splitk_chunks[i] = ceil_div(K, splitk_len[i]);
         splitk_at[i] = take((int64_t)splitk_chunks[i] * f.ld * f.ld * 8);
     }
+    // statistics of the blocks above 128: when all their upper 128 x 128 tiles
+    // would leave most of the GPU idle (a few large blocks), each product is
+    // split over k as well, into parts of at least 256 (multiples of 32)
+    auto upper_tiles = [](int d) { const int t = ceil_div(d, kTile); return t * (t + 1) / 2; };
+    int gram_tiles = 0;
+    for (auto& bp : h->blocks)
+        if (!bp.one_sided && !bp.small) gram_tiles += upper_tiles(bp.mb) + upper_tiles(bp.nb);
+    const int gram_parts = (gram_tiles > 0 && gram_tiles < kNewtonSplitTiles)
+                               ? std::min(8, ceil_div(2 * kNewtonSplitTiles, gram_tiles)) : 1;
+    // per block: part length over the columns (L) and over the rows (R)
+    std::vector<int> glen_l(h->blocks.size(), 0), glen_r(h->blocks.size(), 0);
+    std::vector<int64_t> gsplit_at(h->blocks.size(), -1);
+    if (gram_parts > 1)
+        for (size_t i = 0; i < h->blocks.size(); ++i) {
+            const BlockPlan& bp = h->blocks[i];
+            if (bp.one_sided || bp.small) continue;
+            auto len_of = [&](int K) {
+                return (int)std::min<int64_t>(K, align_up(std::max(ceil_div(K, gram_parts), 256), 32));
+            };
+            glen_l[i] = len_of(bp.nb);
+            glen_r[i] = len_of(bp.mb);
+            const int64_t ldl = h->factors[bp.fl].ld, ldr = h->factors[bp.fr].ld;
+            gsplit_at[i] = take((ceil_div(bp.nb, glen_l[i]) * ldl * ldl +
+                                 ceil_div(bp.mb, glen_r[i]) * ldr * ldr) * 8);
+        }
 
     // norm partial slots
     int na = 0, nd = 0;
@@ -719,9 +747,9 @@ int build_plan(shampoo_s* h) {
     {
         std::vector<GemmTask> tasks;
         std::vector<GramJob> small;
-        std::vector<GemmTask> sk;
-        std::vector<SymReduceJob> red;
-        std::vector<TileRef> red_tiles;
+        std::vector<GemmTask> sk, gs;
+        std::vector<SymReduceJob> red, gred;
+        std::vector<TileRef> red_tiles, gred_tiles;
         for (size_t bi = 0; bi < h->blocks.size(); ++bi) {
             const BlockPlan& bp = h->blocks[bi];
             const TensorPlan& tp = h->tensors[bp.tensor];
@@ -778,6 +806,47 @@ int build_plan(shampoo_s* h) {
                 small.push_back(j);
                 continue;
             }
+            if (gsplit_at[bi] >= 0) {
+                // part c of L: G_c G_c^T over columns [c len, ...) of G_b; of R:
+                // G_c^T G_c over rows [c len, ...); upper tiles into partials
+                int64_t at = gsplit_at[bi] / 8;
+                for (int side = 0; side < 2; ++side) {
+                    const FactorPlan& f = side == 0 ? fl : fr;
+                    const int K = side == 0 ? bp.nb : bp.mb, len = side == 0 ? glen_l[bi] : glen_r[bi];
+                    const int parts = ceil_div(K, len);
+                    for (int ck = 0; ck < parts; ++ck) {
+                        GemmTask t{};
+                        const int64_t k0 = (int64_t)ck * len;
+                        t.a_base = t.b_base = 1 + bp.tensor;
+                        t.a_off = t.b_off = (int64_t)bp.r0 * tp.cols + bp.c0 +
+                                            (side == 0 ? k0 : k0 * tp.cols);
+                        t.lda = t.ldb = (int)tp.cols;
+                        t.c_base = 0;
+                        t.c_off = at + (int64_t)ck * f.ld * f.ld;
+                        t.ldc = f.ld;
+                        t.M = t.N = f.dim;
+                        t.K = (int)std::min<int64_t>(len, K - k0);
+                        t.trans = (side == 0 ? 2 : 1) | 16;
+                        t.tiles_n = ceil_div(t.N, kTile);
+                        t.factor = -1;
+                        t.norm_slot = -1;
+                        gs.push_back(t);
+                    }
+                    SymReduceJob r{};
+                    r.part_off = at;
+                    r.s_off = f.off_s / 8;
+                    r.nparts = parts;
+                    r.dim = f.dim;
+                    r.ld = f.ld;
+                    r.tiles = ceil_div(f.dim, 32);
+                    for (int a = 0; a < r.tiles; ++a)
+                        for (int b2 = a; b2 < r.tiles; ++b2)
+                            gred_tiles.push_back({(int32_t)gred.size(), a * r.tiles + b2});
+                    gred.push_back(r);
+                    at += (int64_t)parts * f.ld * f.ld;
+                }
+                continue;
+            }
             GemmTask t{};
             t.a_base = t.b_base = 1 + bp.tensor;
             t.a_off = t.b_off = (int64_t)bp.r0 * tp.cols + bp.c0;
@@ -809,6 +878,10 @@ int build_plan(shampoo_s* h) {
         h->symred_jobs_off = blob.add(red);
         h->symred_tiles_off = blob.add(red_tiles);
         h->n_symred_tiles = (int)red_tiles.size();
+        h->gsplit = add_launch(blob, gs);
+        h->gred_jobs_off = blob.add(gred);
+        h->gred_tiles_off = blob.add(gred_tiles);
+        h->n_gred_tiles = (int)gred_tiles.size();
     }
     // apply: T = G_b P_R, then D = P_L T with ||D||^2 partials (cue 10)
     {
@@ -1366,18 +1439,34 @@ int enqueue_stats(shampoo_s* h, hipStream_t s, bool skip_small, const shampoo_sp
     // statistics keep the near-null spectrum that fp32 storage would round
     // into the eps damping)
     {
-        ProfScope ps(h, PC_STATS, s, h->gram.ntiles > 0 || (!skip_small && h->n_gram128 > 0));
+        ProfScope ps(h, PC_STATS, s,
+                     h->gram.ntiles > 0 || h->gsplit.ntiles > 0 || (!skip_small && h->n_gram128 > 0));
         if (!skip_small) {
             const int rc2 = hip_err(launch_gram128(tab<GramJob>(h, h->gram128_off), h->n_gram128,
                                                    at<uint64_t>(h, h->off_bases), at<double>(h, 0),
                                                    a.alpha, a.beta, s));
             if (rc2) return rc2;
         }
-        const int rc = hip_err(launch_gemm_f64_from_f32(tab<GemmTask>(h, h->gram.tasks_off),
-                                                        tab<TileRef>(h, h->gram.tiles_off),
-                                                        h->gram.ntiles, at<uint64_t>(h, h->off_bases),
-                                                        a, s));
+        int rc = hip_err(launch_gemm_f64_from_f32(tab<GemmTask>(h, h->gram.tasks_off),
+                                                  tab<TileRef>(h, h->gram.tiles_off),
+                                                  h->gram.ntiles, at<uint64_t>(h, h->off_bases),
+                                                  a, s));
         if (rc) return rc;
+        if (h->gsplit.ntiles > 0) {
+            // a few large blocks: partial products over k, then their
+            // fixed-order sum into S = beta2 S + w sum_c part_c
+            GemmArgs pa{};
+            pa.epi = EPI_STORE;
+            pa.alpha = 1.0;
+            rc = hip_err(launch_gemm_f64_from_f32(tab<GemmTask>(h, h->gsplit.tasks_off),
+                                                  tab<TileRef>(h, h->gsplit.tiles_off), h->gsplit.ntiles,
+                                                  at<uint64_t>(h, h->off_bases), pa, s));
+            if (!rc)
+                rc = hip_err(launch_sym_reduce(tab<SymReduceJob>(h, h->gred_jobs_off),
+                                               tab<TileRef>(h, h->gred_tiles_off), h->n_gred_tiles,
+                                               at<double>(h, 0), a.alpha, a.beta, s));
+            if (rc) return rc;
+        }
     }
     if (!h->sos.empty()) {
         const int rc = enqueue_sos_stats(h, sparse, s);
