@@ -35,6 +35,7 @@ constexpr size_t kNewtonScratchBudget = size_t(4) << 30;  // bytes per precision
 constexpr int kSplitKTiles = 512;     // one-sided statistics: target tiles per launch
 constexpr int kSplitKMin = 512;       // and shortest chunk of the long dimension
 constexpr int kNewtonSplitTiles = 256;  // Newton stages with fewer tiles are split over k
+constexpr int kPersistGrid = 512;       // workgroups of a persistent (packed, <= 128) fp64 stage
 constexpr int kSosMaxChunks = 64;     // sparse one-sided tables: split-K chunks per call, at most,
 constexpr int kSosMinRows = 256;      // of at least this many listed rows (measured best)
 
@@ -84,6 +85,8 @@ struct LaunchRef {
 // over k into `parts` partial products that a second launch sums.
 struct NewtonStage {
     LaunchRef gemm;
+    bool sorted = false;   // tile table in slot order: the persistent GEMM form
+    int chain = 1;         // products per slot run in order by one workgroup
     int parts = 1;
     int64_t sum_jobs_off = 0, sum_tiles_off = 0;   // SplitSumJob / TileRef tables (bytes)
     int sum_ntiles = 0;
@@ -284,6 +287,23 @@ std::vector<TileRef> xcd_tile_order(const std::vector<GemmTask>& tasks) {
     return tiles;
 }
 
+// A launch whose tile table is in task order (tasks sorted by gating id), for
+// the persistent form of the GEMM kernel.
+LaunchRef add_launch_sorted(Blob& blob, const std::vector<GemmTask>& tasks) {
+    std::vector<TileRef> tiles;
+    for (size_t i = 0; i < tasks.size(); ++i) {
+        const int nt = ceil_div(tasks[i].M, kTile) * tasks[i].tiles_n;
+        const bool upper = (tasks[i].trans >> 4) & 1;
+        for (int t = 0; t < nt; ++t)
+            if (!upper || t / tasks[i].tiles_n <= t % tasks[i].tiles_n) tiles.push_back({(int32_t)i, t});
+    }
+    LaunchRef L;
+    L.tasks_off = blob.add(tasks);
+    L.tiles_off = blob.add(tiles);
+    L.ntiles = (int)tiles.size();
+    return L;
+}
+
 LaunchRef add_launch(Blob& blob, const std::vector<GemmTask>& tasks) {
     const std::vector<TileRef> tiles = xcd_tile_order(tasks);
     LaunchRef L;
@@ -402,6 +422,28 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
         // k in [c ld/parts, (c+1) ld/parts) into its own partial (upper
         // tiles), and the sum writes both triangles of the destination
         const int ut = tiles1 * (tiles1 + 1) / 2;
+        // a packed fp64 chain of factors up to 128 (one tile per product):
+        // one launch per iteration in the persistent form, each workgroup
+        // taking a slot's products in order (X T, T^2, ..., T^p M); with
+        // nothing routed that is one launch of a few hundred workgroups that
+        // stop at once, instead of one launch per stage and a workgroup per tile
+        if (gids != nullptr && ld <= kTile) {
+            const size_t n = fids.size();
+            std::vector<GemmTask> seq;
+            int per = 0;
+            for (size_t k = 0; k < st.size(); ++k) per += (int)(st[k].size() / n);
+            for (size_t sl = 0; sl < n; ++sl)
+                for (size_t k = 0; k < st.size(); ++k) {
+                    const size_t m = st[k].size() / n;   // products of this stage per slot
+                    for (size_t j = 0; j < m; ++j) seq.push_back(st[k][sl * m + j]);
+                }
+            NewtonStage ns;
+            ns.sorted = true;
+            ns.chain = per;
+            ns.gemm = add_launch_sorted(h->blob, seq);
+            ch.stages[q].push_back(ns);
+            continue;
+        }
         for (auto& tasks : st) {
             NewtonStage ns;
             const int parts = newton_split((int)tasks.size() * ut, ld);
@@ -666,9 +708,12 @@ int build_plan(shampoo_s* h) {
                 n_slots += (int)fids.size();
                 const int n = (int)fids.size();
                 scr64 = std::max(scr64, per * (int64_t)std::min(n, cap));
-                // chunks of cap slots and a last, smaller one
-                split64 = std::max(split64, newton_split_bytes(std::min(n, cap), ld, 8));
-                if (n > cap && n % cap) split64 = std::max(split64, newton_split_bytes(n % cap, ld, 8));
+                // chunks of cap slots and a last, smaller one (factors up to
+                // 128 run their products per slot, never split)
+                if (ld > kTile) {
+                    split64 = std::max(split64, newton_split_bytes(std::min(n, cap), ld, 8));
+                    if (n > cap && n % cap) split64 = std::max(split64, newton_split_bytes(n % cap, ld, 8));
+                }
                 pend.push_back(std::move(pd));
                 continue;
             }
@@ -1117,7 +1162,9 @@ int build_plan(shampoo_s* h) {
                 q.a_off = tp.off_a / 4;
                 bcs.push_back(q);
             }
-            bns.push_back({bp.a_slot, bp.a_chunks, bp.d_slot, bp.d_tiles, (int)i, 0});
+            // a tensor whose blocks are all <= 128 is updated inside the fused
+            // kernels, which form each block's graft scale themselves
+            if (!tp.fused) bns.push_back({bp.a_slot, bp.a_chunks, bp.d_slot, bp.d_tiles, (int)i, 0});
         }
         h->n_blockchunks = (int)bcs.size();
         h->n_blocknorms = (int)bns.size();
@@ -1597,6 +1644,8 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
                 const GemmTask* tk = tab<GemmTask>(h, S.gemm.tasks_off);
                 const TileRef* tl = tab<TileRef>(h, S.gemm.tiles_off);
                 ProfScope ps(h, fp64 ? PC_NEWTON_GEMM64 : PC_NEWTON_GEMM32, s);
+                g.persist = (fp64 && S.sorted) ? kPersistGrid : 0;
+                g.chain = S.chain;
                 rc = hip_err(fp64 ? launch_gemm_f64(tk, tl, S.gemm.ntiles, bases, g, s)
                                   : launch_gemm_f32(tk, tl, S.gemm.ntiles, bases, g, s));
                 if (!rc && S.parts > 1)
@@ -1996,7 +2045,7 @@ int enqueue_apply(shampoo_s* h, float* const* params, const shampoo_sparse_rows*
     }
     if (rc) return rc;
     {
-        ProfScope ps(h, PC_SCALE, s);
+        ProfScope ps(h, PC_SCALE, s, h->n_blocknorms > 0);
         rc = hip_err(launch_block_scale(tab<BlockNorms>(h, h->blocknorms_off), h->n_blocknorms,
                                         partA, partD, scale, s));
     }

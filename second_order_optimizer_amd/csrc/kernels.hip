@@ -349,19 +349,17 @@ template <> struct WaveTile<double> {
 // C (type T) = alpha op(A) op(B) (+ beta C); A, B stored as TA, TB and
 // converted to T on the way into LDS (fp32 gradients into an fp64 product are
 // exact: fp32 x fp32 fits the fp64 mantissa).
-template <typename T, typename TA, typename TB, int MINW, bool AXPBY>
-__global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__ tasks,
-                                             const TileRef* __restrict__ tiles,
-                                             const uint64_t* __restrict__ bases, GemmArgs args) {
+// One tile of a batched-GEMM launch (entry e of the tile table); false if
+// its task is gated off.
+template <typename T, typename TA, typename TB, bool AXPBY>
+__device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ tasks,
+                                          const TileRef* __restrict__ tiles,
+                                          const uint64_t* __restrict__ bases, const GemmArgs& args,
+                                          T* As, T* Bs, double* red) {
     constexpr int BK = GemmTraits<T>::BK;
-    constexpr int P = BM + GemmTraits<T>::PADE;
-    __shared__ __align__(16) T As[BK * P];
-    __shared__ __align__(16) T Bs[BK * P];
-    __shared__ double red[4];
-
-    const TileRef tr = tiles[blockIdx.x];
+    const TileRef tr = tiles[e];
     const GemmTask tk = tasks[tr.task];
-    if (args.gate && tk.factor >= 0 && args.gate[tk.factor] != args.gate_val) return;
+    if (args.gate && tk.factor >= 0 && args.gate[tk.factor] != args.gate_val) return false;
 
     const int ti = tr.tile / tk.tiles_n, tj = tr.tile % tk.tiles_n;
     const int i0 = ti * BM, j0 = tj * BN;
@@ -453,6 +451,40 @@ __global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__
     if (tk.norm_slot >= 0 && args.norms) {
         const double s = block_sum_256(nrm, red);
         if (threadIdx.x == 0) args.norms[tk.norm_slot + tr.tile] = s;
+    }
+    return true;
+}
+
+template <typename T, typename TA, typename TB, int MINW, bool AXPBY, bool PERSIST>
+__global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__ tasks,
+                                             const TileRef* __restrict__ tiles,
+                                             const uint64_t* __restrict__ bases, GemmArgs args) {
+    constexpr int BK = GemmTraits<T>::BK;
+    constexpr int P = BM + GemmTraits<T>::PADE;
+    __shared__ __align__(16) T As[BK * P];
+    __shared__ __align__(16) T Bs[BK * P];
+    __shared__ double red[4];
+    if constexpr (PERSIST) {
+        // the table is sorted by gating id and the live ids are a prefix, so
+        // the first gated tile a workgroup meets ends it; a group of `chain`
+        // products runs in order on one workgroup (the barrier between them
+        // also makes each product's stores visible to the next one's loads)
+        const int C = args.chain > 1 ? args.chain : 1;
+        bool first = true;
+        for (int e0 = blockIdx.x * C; e0 < args.ntiles; e0 += gridDim.x * C) {
+            bool live = true;
+            for (int j = 0; j < C && e0 + j < args.ntiles; ++j) {
+                if (!first) __syncthreads();   // the previous tile's LDS reads and stores are done
+                first = false;
+                if (!gemm_tile<T, TA, TB, AXPBY>(e0 + j, tasks, tiles, bases, args, As, Bs, red)) {
+                    live = false;
+                    break;
+                }
+            }
+            if (!live) break;
+        }
+    } else {
+        (void)gemm_tile<T, TA, TB, AXPBY>(blockIdx.x, tasks, tiles, bases, args, As, Bs, red);
     }
 }
 
@@ -2561,21 +2593,30 @@ hipError_t launch_gemm_f32(const GemmTask* tasks, const TileRef* tiles, int ntil
                            const uint64_t* bases, const GemmArgs& a, hipStream_t s) {
     if (ntiles <= 0) return hipSuccess;
     if (a.epi == EPI_AXPBY)
-        hipLaunchKernelGGL((k_gemm<float, float, float, 1, true>), dim3(ntiles), dim3(256), 0, s,
+        hipLaunchKernelGGL((k_gemm<float, float, float, 1, true, false>), dim3(ntiles), dim3(256), 0, s,
                            tasks, tiles, bases, a);
     else
-        hipLaunchKernelGGL((k_gemm<float, float, float, 1, false>), dim3(ntiles), dim3(256), 0, s,
+        hipLaunchKernelGGL((k_gemm<float, float, float, 1, false, false>), dim3(ntiles), dim3(256), 0, s,
                            tasks, tiles, bases, a);
     return hipGetLastError();
 }
 hipError_t launch_gemm_f64(const GemmTask* tasks, const TileRef* tiles, int ntiles,
                            const uint64_t* bases, const GemmArgs& a, hipStream_t s) {
     if (ntiles <= 0) return hipSuccess;
+    if (a.persist > 0 && a.epi != EPI_AXPBY) {
+        GemmArgs b = a;
+        b.ntiles = ntiles;
+        const int groups = (ntiles + (a.chain > 1 ? a.chain : 1) - 1) / (a.chain > 1 ? a.chain : 1);
+        hipLaunchKernelGGL((k_gemm<double, double, double, 2, false, true>),
+                           dim3(groups < a.persist ? groups : a.persist), dim3(256), 0, s, tasks, tiles,
+                           bases, b);
+        return hipGetLastError();
+    }
     if (a.epi == EPI_AXPBY)
-        hipLaunchKernelGGL((k_gemm<double, double, double, 2, true>), dim3(ntiles), dim3(256), 0, s,
+        hipLaunchKernelGGL((k_gemm<double, double, double, 2, true, false>), dim3(ntiles), dim3(256), 0, s,
                            tasks, tiles, bases, a);
     else
-        hipLaunchKernelGGL((k_gemm<double, double, double, 2, false>), dim3(ntiles), dim3(256), 0, s,
+        hipLaunchKernelGGL((k_gemm<double, double, double, 2, false, false>), dim3(ntiles), dim3(256), 0, s,
                            tasks, tiles, bases, a);
     return hipGetLastError();
 }
@@ -2583,10 +2624,10 @@ hipError_t launch_gemm_f64_from_f32(const GemmTask* tasks, const TileRef* tiles,
                                     const uint64_t* bases, const GemmArgs& a, hipStream_t s) {
     if (ntiles <= 0) return hipSuccess;
     if (a.epi == EPI_AXPBY)
-        hipLaunchKernelGGL((k_gemm<double, float, float, 2, true>), dim3(ntiles), dim3(256), 0, s,
+        hipLaunchKernelGGL((k_gemm<double, float, float, 2, true, false>), dim3(ntiles), dim3(256), 0, s,
                            tasks, tiles, bases, a);
     else
-        hipLaunchKernelGGL((k_gemm<double, float, float, 2, false>), dim3(ntiles), dim3(256), 0, s,
+        hipLaunchKernelGGL((k_gemm<double, float, float, 2, false, false>), dim3(ntiles), dim3(256), 0, s,
                            tasks, tiles, bases, a);
     return hipGetLastError();
 }

@@ -25,6 +25,14 @@ struct GemmArgs {
     const int32_t* gate;  // per-factor precision flags, or null
     int32_t gate_val;     // run only tasks whose factor has this flag
     double* norms;        // per-tile ||C||^2 partials (tasks with norm_slot >= 0)
+    // fp64 store launches only: > 0 runs that many workgroups over a tile
+    // table sorted by gating id (a workgroup stops at its first gated tile,
+    // as every later one is gated too); ntiles is the table's length.  With
+    // chain > 1 the table holds groups of `chain` one-tile products that one
+    // workgroup runs in order, each reading what the previous ones wrote.
+    int32_t persist;
+    int32_t ntiles;
+    int32_t chain;
 };
 
 // Lanczos on at most this many factors > 128 splits each step's product over
