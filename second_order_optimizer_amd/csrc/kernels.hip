@@ -1541,7 +1541,19 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
     for (int it = 0; it < iters; ++it) {
         auto bM = [&](int mb, int r) { return M.v[mb][r]; };
         CStrip Xn;
-        gemm_slot_reg(slot, bM, Xn, w, h, c);                 // X M
+        if (it == 0) {
+            // X_0 is diagonal (z^(1/p) inside n x n, 1 outside), so X_0 M only
+            // scales the rows of M (the product would add zeros to the same value)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * m + 8 * (r >> 2) + 4 * h + (r & 3);
+                    Xn.v[m][r] = slot[sidx(row, row)] * M.v[m][r];
+                }
+        } else {
+            gemm_slot_reg(slot, bM, Xn, w, h, c);             // X M
+        }
         {
             const float* xs = slot + 4 * h * kSP + pcol(col);
 #pragma unroll
