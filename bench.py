@@ -70,16 +70,19 @@ def factor_dims(opt, root_p):
 
 def newton_flops(n, p, iters):
     """Coupled-Newton GEMM flops of one n x n root: X T, then T^p M by
-    repeated squaring (log2 p - 1 squarings after T^2) and the M update."""
+    repeated squaring (log2 p - 1 squarings after T^2) and the M update, per
+    iteration; X_0 is diagonal, so the first X T is a row scaling and not a
+    product (every root path forms it that way)."""
     gemms = 2 + int(round(math.log2(p))) if p > 1 else 2
-    return gemms * 2.0 * n ** 3 * iters
+    return gemms * 2.0 * n ** 3 * iters - 2.0 * n ** 3
 
 
 def work_model(wl, opt, n_fp64_factors_per_pass):
     """Algorithmic flops / bytes per launch of each kernel family.
 
     Statistics and apply count every product of the formulas as a dense GEMM
-    (2 M N K); the root counts 4 n^3 GEMMs x 2 flops x iterations per factor
+    (2 M N K); the root counts 4 n^3 GEMMs x 2 flops x iterations per factor,
+    less the first X T (a row scaling)
     (p = 4: X T, T^2, T^4, T^4 M).  Elementwise kernels count the bytes the
     formulas must move once (fp32)."""
     nb = opt.n_blocks
@@ -323,9 +326,7 @@ def main():
     fdims = factor_dims(opt, wl.root_p)
     fl = [newton_flops(n, p, wl.newton_iters) for n, p in fdims]
     f32 = wl.root_mode != "f64"
-    # the fused kernel forms X_1 = X_0 T_0 as a row scaling (X_0 is diagonal):
-    # one product of n^3 fewer per factor
-    flops_fused_root = sum(x - 2.0 * n ** 3 for x, (n, _) in zip(fl, fdims) if f32 and n <= 128)
+    flops_fused_root = sum(x for x, (n, _) in zip(fl, fdims) if f32 and n <= 128)
     flops_f32_root = sum(x for x, (n, _) in zip(fl, fdims) if f32 and n > 128)
     flops_f64_root = sum(x for x, d in zip(fl, diag) if d.status & S.FACTOR_FP64)
     alg = {

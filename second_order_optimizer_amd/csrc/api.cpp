@@ -102,6 +102,7 @@ struct NewtonChunk {
     bool compact = false;                    // gated fp64 chain on packed slots: the jobs
     int64_t slot_jobs_off = 0;               // are written on the device (arena bytes)
     std::vector<NewtonStage> stages[2];      // per parity
+    std::vector<NewtonStage> first;          // iteration 0 (the start forms X_1)
 };
 
 // The launches of one root pass over a set of factors.
@@ -391,37 +392,8 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
         t.norm_slot = -1;
         return t;
     };
-    for (int q = 0; q < 2; ++q) {
-        std::vector<std::vector<GemmTask>> st(newton_stage_count(p));
-        for (size_t s = 0; s < fids.size(); ++s) {
-            const int64_t b = (int64_t)s * 6 * mat;
-            const int64_t Xq = b + q * mat, Xn = b + (1 - q) * mat;
-            const int64_t Mq = b + (2 + q) * mat, Mn = b + (3 - q) * mat;
-            const int64_t T2 = b + 4 * mat, T4 = b + 5 * mat;
-            const int fid = gids ? (*gids)[s] : fids[s];
-            // stage 0: X <- X T(M) and T(M)^2 (p = 1: M <- T(M) M).  X, M and
-            // T(M) are polynomials in the same matrix A, so every product
-            // here is symmetric: upper tiles only (16), mirrored (32)
-            st[0].push_back(mk(Xq, Mq, Xn, 8 | 16 | 32, fid));
-            if (p == 1) {
-                st[0].push_back(mk(Mq, Mq, Mn, 4 | 16 | 32, fid));
-                continue;
-            }
-            // the squarings and the M update likewise
-            st[0].push_back(mk(Mq, Mq, T2, 4 | 8 | 16 | 32, fid));
-            int k = 1;
-            int64_t cur = T2;
-            for (int e = 2; e < p; e *= 2) {
-                const int64_t nxt = (cur == T2) ? T4 : T2;
-                st[k++].push_back(mk(cur, cur, nxt, 16 | 32, fid));
-                cur = nxt;
-            }
-            st[k].push_back(mk(cur, Mq, Mn, 16 | 32, fid));
-        }
-        // a stage with few tiles is split over k: part c of a product sums
-        // k in [c ld/parts, (c+1) ld/parts) into its own partial (upper
-        // tiles), and the sum writes both triangles of the destination
-        const int ut = tiles1 * (tiles1 + 1) / 2;
+    // the launches of one iteration's stages (products per stage, per slot)
+    auto emit = [&](const std::vector<std::vector<GemmTask>>& st, std::vector<NewtonStage>& out) {
         // a packed fp64 chain of factors up to 128 (one tile per product):
         // one launch per iteration in the persistent form, each workgroup
         // taking a slot's products in order (X T, T^2, ..., T^p M); with
@@ -441,9 +413,13 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
             ns.sorted = true;
             ns.chain = per;
             ns.gemm = add_launch_sorted(h->blob, seq);
-            ch.stages[q].push_back(ns);
-            continue;
+            out.push_back(ns);
+            return;
         }
+        // a stage with few tiles is split over k: part c of a product sums
+        // k in [c ld/parts, (c+1) ld/parts) into its own partial (upper
+        // tiles), and the sum writes both triangles of the destination
+        const int ut = tiles1 * (tiles1 + 1) / 2;
         for (auto& tasks : st) {
             NewtonStage ns;
             const int parts = newton_split((int)tasks.size() * ut, ld);
@@ -476,7 +452,45 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
                 ns.sum_tiles_off = h->blob.add(tl);
                 ns.sum_ntiles = (int)tl.size();
             }
-            ch.stages[q].push_back(ns);
+            out.push_back(ns);
+        }
+    };
+    for (int q = 0; q < 2; ++q) {
+        std::vector<std::vector<GemmTask>> st(newton_stage_count(p));
+        for (size_t s = 0; s < fids.size(); ++s) {
+            const int64_t b = (int64_t)s * 6 * mat;
+            const int64_t Xq = b + q * mat, Xn = b + (1 - q) * mat;
+            const int64_t Mq = b + (2 + q) * mat, Mn = b + (3 - q) * mat;
+            const int64_t T2 = b + 4 * mat, T4 = b + 5 * mat;
+            const int fid = gids ? (*gids)[s] : fids[s];
+            // stage 0: X <- X T(M) and T(M)^2 (p = 1: M <- T(M) M).  X, M and
+            // T(M) are polynomials in the same matrix A, so every product
+            // here is symmetric: upper tiles only (16), mirrored (32)
+            st[0].push_back(mk(Xq, Mq, Xn, 8 | 16 | 32, fid));
+            if (p == 1) {
+                st[0].push_back(mk(Mq, Mq, Mn, 4 | 16 | 32, fid));
+                continue;
+            }
+            // the squarings and the M update likewise
+            st[0].push_back(mk(Mq, Mq, T2, 4 | 8 | 16 | 32, fid));
+            int k = 1;
+            int64_t cur = T2;
+            for (int e = 2; e < p; e *= 2) {
+                const int64_t nxt = (cur == T2) ? T4 : T2;
+                st[k++].push_back(mk(cur, cur, nxt, 16 | 32, fid));
+                cur = nxt;
+            }
+            st[k].push_back(mk(cur, Mq, Mn, 16 | 32, fid));
+        }
+        emit(st, ch.stages[q]);
+        if (q == 0) {
+            // iteration 0 without X T: X_0 is diagonal, and the start writes
+            // X_1 = X_0 T(M_0) itself (stage 0 holds X T and one more product
+            // per slot)
+            std::vector<std::vector<GemmTask>> st0 = st;
+            st0[0].clear();
+            for (size_t i = 1; i < st[0].size(); i += 2) st0[0].push_back(st[0][i]);
+            emit(st0, ch.first);
         }
     }
 }
@@ -1640,7 +1654,7 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
         }
         if (rc) return rc;
         for (int it = 0; it < ch.iters; ++it) {
-            for (const NewtonStage& S : ch.stages[it & 1]) {
+            for (const NewtonStage& S : it == 0 ? ch.first : ch.stages[it & 1]) {
                 const GemmTask* tk = tab<GemmTask>(h, S.gemm.tasks_off);
                 const TileRef* tl = tab<TileRef>(h, S.gemm.tiles_off);
                 ProfScope ps(h, fp64 ? PC_NEWTON_GEMM64 : PC_NEWTON_GEMM32, s);

@@ -1210,7 +1210,9 @@ __global__ __launch_bounds__(1024) void k_route_compact(const CompactClass* __re
 // gridDim.x workgroups (tile = blockIdx.x + k gridDim.x); each thread takes 4
 // consecutive columns of one row of a tile.  The statistic is read from its
 // upper triangle: a tile below the diagonal reads its mirror tile
-// (coalesced) and transposes it in LDS.
+// (coalesced) and transposes it in LDS.  X_0 is diagonal, so the first
+// product X_1 = X_0 T(M_0) is a row scaling: the start writes X_1 (into the
+// second X buffer) and the chain's first iteration skips that product.
 template <typename T>
 __global__ __launch_bounds__(256) void k_newton_init(const FactorJob* __restrict__ jobs,
                                                     const double* __restrict__ stats,
@@ -1232,8 +1234,9 @@ __global__ __launch_bounds__(256) void k_newton_init(const FactorJob* __restrict
     const T zr = ok ? T(pow((args.p + 1) / (2.0 * lam), 1.0 / args.p)) : T(1);
     const T e = T(dg.eps);
     const double* S = stats + jb.s_off;
-    T* X = scratch + jb.x_off;
+    T* X = scratch + jb.x_off + (int64_t)ld * ld;   // X_1, the buffer of iteration 1
     T* M = scratch + jb.m_off;
+    const T c1 = T((double)(args.p + 1) / args.p), c2 = T(-1.0 / args.p);   // as the product's loader
     const int r = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 4;
     for (int tile = blockIdx.x; tile < nt * nt; tile += gridDim.x) {
         const int ti = tile / nt, tj = tile % nt;
@@ -1253,7 +1256,10 @@ __global__ __launch_bounds__(256) void k_newton_init(const FactorJob* __restrict
                 const int a = ti < tj ? r : (ti > tj ? c : min(r, c));
                 const int b = ti < tj ? c : (ti > tj ? r : max(r, c));
                 m = z * (T(ts[a][b]) + (i == j ? e : T(0)));
-                x = (i == j) ? zr : T(0);
+                // T(M_0) as the product's operand loader forms it, times z^(1/p)
+                T tv = m * c2;
+                if (i == j) tv += c1;
+                x = zr * tv;
             } else {
                 m = (i == j) ? T(1) : T(0);
                 x = (i == j) ? T(1) : T(0);

@@ -252,5 +252,5 @@ def test_newton_scratch_budget_from_environment(monkeypatch):
     saved = (8 - 2) * per32 + (8 - 1) * per64
     saved += _newton_split_bytes(8, 256, 4) - _newton_split_bytes(2, 256, 4)
     saved += _newton_split_bytes(8, 256, 8) - _newton_split_bytes(1, 256, 8)
-    # the launch tables of the extra chunks (a few KB) take some of it back
-    assert 0 <= saved - (full - small) < 64 << 10
+    # the launch tables of the extra chunks (tens of KB) take some of it back
+    assert 0 <= saved - (full - small) < 256 << 10
