@@ -399,7 +399,7 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
         // taking a slot's products in order (X T, T^2, ..., T^p M); with
         // nothing routed that is one launch of a few hundred workgroups that
         // stop at once, instead of one launch per stage and a workgroup per tile
-        if (gids != nullptr && ld <= kTile) {
+        if (fp64 && gids != nullptr && ld <= kTile) {   // the persistent form is fp64 only
             const size_t n = fids.size();
             std::vector<GemmTask> seq;
             int per = 0;
