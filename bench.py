@@ -224,7 +224,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(the multi-GPU sharding is a design in DESIGN.md, not built)", file=sys.stderr)
+              f"(sharding the blocks over GPUs is designed, not built)", file=sys.stderr)
         sys.exit(2)
 
     import torch
