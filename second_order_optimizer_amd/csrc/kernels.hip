@@ -1574,19 +1574,21 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
         if constexpr (PP == 1) {
             gemm_slot_reg(slot, bM, M, w, h, c);              // M' = T M
         } else {
-            CStrip Tp;
-            gemm_slot_slot(slot, Tp, w, h, c);             // T^2
+            // slot: Q = T^(p/2) by repeated squaring (p = 2: T itself), then
+            // M' = Q (Q M): two products against register strips, so T^p
+            // itself is never stored
 #pragma unroll
-            for (int e2 = 2; e2 < PP; e2 *= 2) {           // T^4, T^8
+            for (int e2 = 2; e2 < PP; e2 *= 2) {               // T^2, T^4
+                CStrip Tp;
+                gemm_slot_slot(slot, Tp, w, h, c);
                 __syncthreads();
                 cstrip_store(slot, Tp, w, h, c);
                 __syncthreads();
-                gemm_slot_slot(slot, Tp, w, h, c);
             }
-            __syncthreads();
-            cstrip_store(slot, Tp, w, h, c);
-            __syncthreads();
-            gemm_slot_reg(slot, bM, M, w, h, c);              // M' = T^p M
+            CStrip Pm;
+            gemm_slot_reg(slot, bM, Pm, w, h, c);             // Q M
+            auto bP = [&](int mb, int r) { return Pm.v[mb][r]; };
+            gemm_slot_reg(slot, bP, M, w, h, c);              // M' = Q (Q M)
         }
         __syncthreads();
         cstrip_store(slot, Xn, w, h, c);
