@@ -403,6 +403,16 @@ def test_small_blocks_p2_and_beta1_zero():
     run_parity(wl)
 
 
+@pytest.mark.parametrize("root_p", [1, 8])
+def test_root_exponents_1_and_8(root_p):
+    """Inverse p-th roots for p = 1 (the inverse) and p = 8: the fused kernel
+    (factors up to 128) and the batched chain (a 200 x 150 block: factors of
+    ld 224 and 160), AUTO routing; p = 1 runs the scaled iteration count."""
+    T = synth.TensorSpec
+    wl = _custom([T("a", 200, 150), T("b", 100, 70)], 256, cadence=1, steps=3, root_p=root_p)
+    run_parity(wl)
+
+
 def test_fallback_and_sparse_rows():
     T = synth.TensorSpec
     wl = _custom([T("dense", 96, 80), T("wide", 48, 300), T("emb", 1000, 128, kind="sparse",
