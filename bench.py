@@ -12,9 +12,15 @@ timed region (the one at t = 0 is warm-up).
 
 Prints one JSON line: steps/s per 100M parameters (the headline), the
 inverse-root blocks/s and %MFMA of each MFMA stage, a per-kernel breakdown
-from HIP events recorded around every launch inside the timed region, the
+from HIP events recorded around the launches inside the timed region, the
 roofline of the dominant kernel, and the fp64 CPU oracle timed on a bounded
 sample of the same workload on this host.
+
+Inside the timed region the per-launch events are recorded in the steps that
+recompute roots and in the step after each (events around every launch of
+every step cost about 0.025 ms per step on Transformer-base, 2 %); every
+root-pass launch is timed, and each family's launches per step, counted on
+the warm-up steps, scale its sampled average to the whole region.
 """
 from __future__ import annotations
 
@@ -274,21 +280,35 @@ def main():
         dense, sparse = pool[t % len(pool)]
         opt.step(params, dense, t, wl.cadence, sparse if sparse else None)
 
+    def kind(t):   # which roots a step recomputes (S.ROOTS_NONE: none)
+        return S.root_selector(t, wl.cadence, cfg.root_parts)
+
+    def sampled(t):   # timed steps that carry per-launch events
+        return kind(t) != S.ROOTS_NONE or (t > 0 and kind(t - 1) != S.ROOTS_NONE)
+
+    # warm-up; each family's launches per step, by the roots the step recomputes
+    per_kind = {}
     for t in range(args.warmup):
+        if not args.no_profile:
+            opt.profile(True)
         step(t)
+        if not args.no_profile:
+            per_kind[kind(t)] = {k: v[0] for k, v in opt.profile_read().items() if v[0] > 0}
+            opt.profile(False)
     torch.cuda.synchronize()
     print(f"# warm-up {args.warmup} steps done", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if not args.no_profile:
-        opt.profile(True)
         opt.profile_read()        # reset
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev0.record(stream)
     marks = []                  # one event after every step: per-step GPU time
     for t in range(args.warmup, args.warmup + args.steps):
+        if not args.no_profile:
+            opt.profile(sampled(t))
         step(t)
         e = torch.cuda.Event(enable_timing=True)
         e.record(stream)
@@ -355,11 +375,16 @@ def main():
     t_mfma_step = (wm["gram_small"] / (PEAK_TFLOPS["f64"] * 1e12) +
                    wm["apply_small"] / (PEAK_TFLOPS["f32"] * 1e12))
     t_hbm_step = wm["step_small_bytes"] / (PEAK_HBM_GBS * 1e9)
+    timed = range(args.warmup, args.warmup + args.steps)
     for name, (launches, tot) in prof.items():
         if launches == 0:
             continue
-        rec = {"launches": int(launches), "avg_ms": tot / launches,
-               "ms_per_step": tot / args.steps}
+        # launches of the family over the whole timed region (from the warm-up
+        # counts per step kind); the sampled launches give its average
+        total = sum(per_kind.get(kind(t), {}).get(name, 0) for t in timed)
+        total = max(total, int(launches))
+        rec = {"launches": int(total), "launches_timed": int(launches), "avg_ms": tot / launches,
+               "ms_per_step": tot / launches * total / args.steps}
         if name == "step_fused":
             sec = rec["avg_ms"] / 1e3
             rec.update({"mfma_floor_frac": t_mfma_step / sec, "hbm_floor_frac": t_hbm_step / sec,
@@ -378,13 +403,13 @@ def main():
         if name in alg:
             work, unit, bound, peak = alg[name]
         elif name == "newton_fused_f32" and flops_fused_root > 0:
-            work = flops_fused_root * n_root_passes / launches
+            work = flops_fused_root * n_root_passes / total
             unit, bound, peak = "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]
         elif name == "newton_gemm_f32" and flops_f32_root > 0:
-            work = flops_f32_root * n_root_passes / launches
+            work = flops_f32_root * n_root_passes / total
             unit, bound, peak = "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]
         elif name == "newton_gemm_f64" and flops_f64_root > 0:
-            work = flops_f64_root * n_root_passes / launches
+            work = flops_f64_root * n_root_passes / total
             unit, bound, peak = "TFLOP/s", "mfma", PEAK_TFLOPS["f64"]
         if work is not None:
             sec = rec["avg_ms"] / 1e3
@@ -410,9 +435,10 @@ def main():
                     "peak": dom[1]["peak"], "unit": dom[1]["unit"], "frac": dom[1]["frac"],
                     "traffic": traffic}
 
-    root_ms = sum(prof.get(n, (0, 0.0))[1] for n in
+    root_ms = sum(stages[n]["ms_per_step"] * args.steps for n in
                   ("lanczos_stats", "lanczos_roots", "newton_init", "newton_gemm_f32",
-                   "newton_gemm_f64", "newton_commit", "newton_fused_f32", "route_compact"))
+                   "newton_gemm_f64", "newton_commit", "newton_fused_f32", "route_compact")
+                  if n in stages)
     inv_root_blocks_per_s = (opt.n_blocks * n_root_passes / (root_ms / 1e3)) if root_ms > 0 else None
     mfma_pct = {k: round(100 * v["frac"], 2) for k, v in stages.items() if v.get("bound") == "mfma"}
 

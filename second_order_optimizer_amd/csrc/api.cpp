@@ -1653,20 +1653,25 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
                                             na, s));
         }
         if (rc) return rc;
-        for (int it = 0; it < ch.iters; ++it) {
-            for (const NewtonStage& S : it == 0 ? ch.first : ch.stages[it & 1]) {
-                const GemmTask* tk = tab<GemmTask>(h, S.gemm.tasks_off);
-                const TileRef* tl = tab<TileRef>(h, S.gemm.tiles_off);
-                ProfScope ps(h, fp64 ? PC_NEWTON_GEMM64 : PC_NEWTON_GEMM32, s);
-                g.persist = (fp64 && S.sorted) ? kPersistGrid : 0;
-                g.chain = S.chain;
-                rc = hip_err(fp64 ? launch_gemm_f64(tk, tl, S.gemm.ntiles, bases, g, s)
-                                  : launch_gemm_f32(tk, tl, S.gemm.ntiles, bases, g, s));
-                if (!rc && S.parts > 1)
-                    rc = hip_err(launch_split_sum(fp64, tab<SplitSumJob>(h, S.sum_jobs_off),
-                                                  tab<TileRef>(h, S.sum_tiles_off), S.sum_ntiles,
-                                                  h->arena, g.gate, g.gate_val, s));
-                if (rc) return rc;
+        {
+            // one timing scope over the chunk's whole iteration (per-launch
+            // events around its many short launches would cost more than
+            // they measure)
+            ProfScope ps(h, fp64 ? PC_NEWTON_GEMM64 : PC_NEWTON_GEMM32, s);
+            for (int it = 0; it < ch.iters; ++it) {
+                for (const NewtonStage& S : it == 0 ? ch.first : ch.stages[it & 1]) {
+                    const GemmTask* tk = tab<GemmTask>(h, S.gemm.tasks_off);
+                    const TileRef* tl = tab<TileRef>(h, S.gemm.tiles_off);
+                    g.persist = (fp64 && S.sorted) ? kPersistGrid : 0;
+                    g.chain = S.chain;
+                    rc = hip_err(fp64 ? launch_gemm_f64(tk, tl, S.gemm.ntiles, bases, g, s)
+                                      : launch_gemm_f32(tk, tl, S.gemm.ntiles, bases, g, s));
+                    if (!rc && S.parts > 1)
+                        rc = hip_err(launch_split_sum(fp64, tab<SplitSumJob>(h, S.sum_jobs_off),
+                                                      tab<TileRef>(h, S.sum_tiles_off), S.sum_ntiles,
+                                                      h->arena, g.gate, g.gate_val, s));
+                    if (rc) return rc;
+                }
             }
         }
         // the final X, M sit in buffer (iters % 2) of each slot
