@@ -109,7 +109,7 @@ def work_model(wl, opt, n_fp64_factors_per_pass):
     sparse_os = [b for b in onesided if wl.tensors[b.tensor].kind == "sparse"]
     dense_os = [b for b in onesided if wl.tensors[b.tensor].kind == "dense"]
     dims = [(dim, p) for dim, p in factor_dims(opt, wl.root_p)]
-    root_flops_all = sum(newton_flops(n, p, wl.newton_iters) for n, p in dims)
+    root_flops_all = sum(newton_flops(n, p, wl.newton_iters) for n, p in dims)   # full count
     shampoo_params = sum(b.rows * b.cols for b in blocks) + sum(b.rows * b.cols for b in dense_os)
     small = [b for b in blocks if b.rows <= 128 and b.cols <= 128]
     big = [b for b in blocks if not (b.rows <= 128 and b.cols <= 128)] + dense_os
@@ -210,6 +210,8 @@ def main():
                     help="0: 256x512 b128, 1: Transformer-base b128 (default), 2: BERT-large "
                          "b512, 3: ResNet-50 b256, 4: CTR MLP b1024 + sparse tables")
     ap.add_argument("--root-mode", default=None, choices=["f32", "f64", "auto"])
+    ap.add_argument("--newton-tol", type=float, default=None,
+                    help="fused-root convergence tolerance (0: the full iteration count)")
     ap.add_argument("--pool", type=int, default=4, help="distinct gradient sets kept in HBM")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -237,6 +239,8 @@ def main():
     from second_order_optimizer_amd import shampoo as S
 
     wl = synth.workload(args.workload)
+    if args.newton_tol is not None:
+        wl.newton_tol = args.newton_tol
     if args.root_mode:
         wl.root_mode = args.root_mode
     dev = torch.device("cuda", 0)
@@ -245,6 +249,7 @@ def main():
                         newton_iters=wl.newton_iters, root_mode=wl.root_mode, beta1=wl.beta1,
                         beta2=wl.beta2, lr=wl.lr, eps_rel=wl.eps_rel, graft_eps=wl.graft_eps,
                         fp64_cond_threshold=wl.fp64_cond_threshold, root_parts=args.root_parts,
+                        newton_tol=wl.newton_tol,
                         large_layer=1 if args.large_layer else 0)
     shapes = [(t.rows, t.cols, 0 if t.kind == "dense" else 1) for t in wl.tensors]
     t0 = time.time()
@@ -344,7 +349,10 @@ def main():
     stages = {}
     fp64_share = n64 / max(len(diag), 1)
     fdims = factor_dims(opt, wl.root_p)
-    fl = [newton_flops(n, p, wl.newton_iters) for n, p in fdims]
+    # the steps each root ran in the last pass (a fused root with a tolerance
+    # stops at convergence; the batched paths run the full count)
+    fl = [newton_flops(n, p, d.iters) if d.iters > 0 else 0.0 for (n, p), d in zip(fdims, diag)]
+    iters_run = [d.iters for (n, _), d in zip(fdims, diag) if n <= 128 and d.iters > 0]
     f32 = wl.root_mode != "f64"
     flops_fused_root = sum(x for x, (n, _) in zip(fl, fdims) if f32 and n <= 128)
     flops_f32_root = sum(x for x, (n, _) in zip(fl, fdims) if f32 and n > 128)
@@ -457,7 +465,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "params": wl.n_params, "blocks": opt.n_blocks,
                    "block_size": wl.block_size, "root_cadence": wl.cadence,
-                   "newton_iters": wl.newton_iters, "root_mode": wl.root_mode,
+                   "newton_iters": wl.newton_iters, "newton_tol": wl.newton_tol,
+                   "root_mode": wl.root_mode,
                    "root_parts": args.root_parts, "async_roots": bool(args.async_roots),
                    "large_layer": bool(args.large_layer),
                    "max_precond_dim": wl.max_precond_dim, "parallelism": "single-gpu"},
@@ -465,6 +474,9 @@ def main():
         "inv_root_blocks_per_s": inv_root_blocks_per_s,
         "root_passes_timed": n_root_passes,
         "fp64_factor_share_last_pass": fp64_share,
+        "fused_root_iters_last_pass": ({"mean": sum(iters_run) / len(iters_run),
+                                        "min": min(iters_run), "max": max(iters_run)}
+                                       if iters_run else None),
         "mfma_pct": mfma_pct,
         "stages": stages,
         "roofline": roofline,

@@ -112,6 +112,13 @@ typedef struct {
     double eps_rel;           /* eps = eps_rel * lambda_max(S) per factor                */
     double graft_eps;         /* delta in A = G / (sqrt(a) + delta)                      */
     double fp64_cond_threshold; /* AUTO mode: kappa(S + eps I) above this -> fp64 root  */
+    double newton_tol;        /* 0 = every root runs its full iteration count.  In [0, 1):
+                                 a root of a factor up to 128 computed in fp32 stops one
+                                 step after max |M_k - I| first falls below newton_tol
+                                 (the coupled iteration's convergence test; near I the
+                                 error squares each step), at most the full count.  The
+                                 batched paths (factors above 128, fp64) always run the
+                                 full count.  E.g. 1e-3                                  */
 } shampoo_config;
 
 /* Row-sparse gradient of one SHAMPOO_SPARSE_ROWS table: n_rows distinct row
@@ -133,6 +140,8 @@ typedef struct {
     int32_t side;        /* 0: L (rows), 1: R (columns)                               */
     int32_t dim;         /* factor dimension                                          */
     int32_t status;      /* bit mask of SHAMPOO_FACTOR_* below                         */
+    int32_t iters;       /* coupled-Newton steps run (0: none, e.g. a zero factor)    */
+    int32_t reserved;
 } shampoo_factor_diag;
 
 enum {

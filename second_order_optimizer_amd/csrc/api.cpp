@@ -1316,7 +1316,8 @@ int shampoo_create(const shampoo_config* cfg, int32_t n_tensors, const shampoo_t
     if (c.block_size < 1 || c.newton_iters < 1 || c.max_precond_dim < 0 || c.lanczos_steps < 0)
         return SHAMPOO_E_ARG;
     if (!(c.beta2 > 0.0 && c.beta2 <= 1.0) || !(c.eps_rel >= 0.0) || !(c.graft_eps >= 0.0) ||
-        !std::isfinite(c.beta1) || !std::isfinite(c.lr) || c.root_parts < 0)
+        !std::isfinite(c.beta1) || !std::isfinite(c.lr) || c.root_parts < 0 ||
+        !(c.newton_tol >= 0.0 && c.newton_tol < 1.0))
         return SHAMPOO_E_ARG;
     if (c.root_mode < SHAMPOO_ROOT_F32 || c.root_mode > SHAMPOO_ROOT_AUTO) return SHAMPOO_E_ARG;
     if (c.root_p != 1 && c.root_p != 2 && c.root_p != 4 && c.root_p != 8)
@@ -1620,6 +1621,7 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
     for (auto& ch : chunks) {
         const int p = ch.p;
         na.p = p;
+        na.iters = ch.iters;
         g.xc1 = (double)(p + 1) / p;
         g.xc2 = -1.0 / p;
         // a packed chain reads the slot jobs written by k_route_compact and
@@ -1641,6 +1643,7 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
             fa.auto_route = h->cfg.root_mode == SHAMPOO_ROOT_AUTO ? 1 : 0;
             fa.eps_rel = h->cfg.eps_rel;
             fa.threshold = h->cfg.fp64_cond_threshold;
+            fa.tol = (float)h->cfg.newton_tol;
             ProfScope ps(h, PC_NEWTON_FUSED, s);
             rc = hip_err(launch_newton128(jobs, ch.njobs, at<double>(h, 0), at<float>(h, 0), diag,
                                           prec, fa, s));

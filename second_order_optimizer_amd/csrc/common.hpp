@@ -199,6 +199,7 @@ struct SosJob {
 struct FactorDiag {
     double lambda_max, eps, kappa_est, residual;
     int32_t block, side, dim, status;
+    int32_t iters, reserved_;
 };
 
 }  // namespace shampoo

@@ -67,6 +67,10 @@ __device__ __forceinline__ double wave_max(double v) {
     for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
     return v;
 }
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
 
 // Fixed-order block reduction over 256 threads (deterministic).
 __device__ __forceinline__ double block_sum_256(double v, double* red) {
@@ -859,6 +863,7 @@ __device__ __forceinline__ void lanczos_finish(const LanczosArgs& args, const La
         dg.status = st;
         dg.kappa_est = 0.0;
         dg.residual = 0.0;
+        dg.iters = 0;
         if (args.prec) args.prec[jb.factor] = args.route_all_fp64 ? 1 : 0;
     } else {
         // root: lambda_max(P) = (lambda_min(S) + eps)^(-1/p) -> kappa estimate.
@@ -1338,6 +1343,7 @@ __global__ __launch_bounds__(256) void k_newton_commit(const FactorJob* __restri
         else st &= ~SHAMPOO_FACTOR_FP64_;
         dg.status = st;
         dg.residual = res;
+        dg.iters = st0 == 0 ? args.iters : 0;
     }
     if (keep) return;
     const bool ident = (st & SHAMPOO_FACTOR_ZERO_) != 0;
@@ -1481,6 +1487,7 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
     __shared__ LanczosSlot lz;
     __shared__ double red[4];
     __shared__ double sh_lmax;   // re-read after the iteration: no set-up value lives across it
+    __shared__ float sh_dev[4];  // per-wave max |M - I| of the iterate just formed
     const FactorJob jb = jobs[blockIdx.x];
     const int n = jb.n, ld = jb.ld;
     constexpr int p = PP;
@@ -1544,6 +1551,12 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
 
     // slot: X, registers: M.  X T = c1 X + c2 X M, so the first product takes
     // M itself as its right operand.
+    // With a tolerance, the iteration ends one step after max |M - I| first
+    // falls below it: near I the error squares each step (times (p+1)/(2p)),
+    // so that step leaves about tol^2, below fp32 resolution for tol <= 1e-3.
+    const float tol = args.tol;
+    int ran = iters;
+    bool last = false;
     for (int it = 0; it < iters; ++it) {
         auto bM = [&](int mb, int r) { return M.v[mb][r]; };
         CStrip Xn;
@@ -1592,7 +1605,33 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
         }
         __syncthreads();
         cstrip_store(slot, Xn, w, h, c);
+        if (tol > 0.f) {
+            // the diagonal tests are the same every step; an opaque column
+            // keeps them from being hoisted out of the loop as 64 live masks
+            int dcol = col;
+            asm volatile("" : "+v"(dcol));
+            float dv = 0.f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * m + 8 * (r >> 2) + 4 * h + (r & 3);
+                    dv = fmaxf(dv, fabsf(M.v[m][r] - (row == dcol ? 1.f : 0.f)));
+                }
+            dv = wave_max(dv);
+            if (lane == 0) sh_dev[w] = dv;
+        }
         __syncthreads();
+        if (tol > 0.f) {
+            // every thread reads the four values after the barrier above and
+            // before the next step's first barrier, after which they are
+            // written again: the exit is uniform over the workgroup
+            if (last) {
+                ran = it + 1;
+                break;
+            }
+            last = fmaxf(fmaxf(sh_dev[0], sh_dev[1]), fmaxf(sh_dev[2], sh_dev[3])) < tol;
+        }
     }
 
     // ---- commit.  Outside n x n both iterates hold the identity, so the
@@ -1653,6 +1692,7 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
         dg.kappa_est = kap;
         dg.status = st;
         dg.residual = ok ? res : 0.0;
+        dg.iters = ok ? ran : 0;
         if (prec) {
             const bool weak = (st & (SHAMPOO_FACTOR_NONFINITE_ROOT_ | SHAMPOO_FACTOR_RESIDUAL_HIGH_)) != 0;
             prec[jb.factor] = (args.auto_route && ok && (kap > args.threshold || weak)) ? 1 : 0;

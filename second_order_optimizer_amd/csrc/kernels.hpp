@@ -57,6 +57,7 @@ struct NewtonArgs {
     int is_fp64;
     const int32_t* gate;
     int32_t gate_val;
+    int iters;                 // iterations run (recorded in the diagnostics)
     unsigned long long* chk;   // per factor: [2f] max |M - I| (bits), [2f + 1] non-finite flag
 };
 
@@ -65,6 +66,7 @@ struct FusedArgs {          // fused fp32 root of factors up to 128
     int steps_s, steps_p;   // Lanczos steps on S (lambda_max) and on the root (kappa)
     int auto_route;         // set prec flags from the kappa estimate
     double eps_rel, threshold;
+    float tol;              // > 0: stop one step after max |M - I| < tol (at most iters)
 };
 
 struct UpdateArgs {

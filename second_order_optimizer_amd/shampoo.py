@@ -36,7 +36,7 @@ class Config(ctypes.Structure):
                 ("root_parts", ctypes.c_int32), ("large_layer", ctypes.c_int32),
                 ("beta1", ctypes.c_double), ("beta2", ctypes.c_double), ("lr", ctypes.c_double),
                 ("eps_rel", ctypes.c_double), ("graft_eps", ctypes.c_double),
-                ("fp64_cond_threshold", ctypes.c_double)]
+                ("fp64_cond_threshold", ctypes.c_double), ("newton_tol", ctypes.c_double)]
 
 
 class SparseRows(ctypes.Structure):
@@ -48,7 +48,8 @@ class FactorDiag(ctypes.Structure):
     _fields_ = [("lambda_max", ctypes.c_double), ("eps", ctypes.c_double),
                 ("kappa_est", ctypes.c_double), ("residual", ctypes.c_double),
                 ("block", ctypes.c_int32), ("side", ctypes.c_int32), ("dim", ctypes.c_int32),
-                ("status", ctypes.c_int32)]
+                ("status", ctypes.c_int32), ("iters", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class BlockLayout(ctypes.Structure):
@@ -130,10 +131,10 @@ def make_config(block_size: int, *, max_precond_dim: int = 0, root_p: int = 4,
                 beta1: float = 0.9, beta2: float = 0.999, lr: float = 1e-3,
                 eps_rel: float = 1e-6, graft_eps: float = 1e-10,
                 fp64_cond_threshold: float = 1e5, root_parts: int = 0,
-                large_layer: int = 0) -> Config:
+                large_layer: int = 0, newton_tol: float = 1e-3) -> Config:
     return Config(block_size, max_precond_dim, root_p, newton_iters, ROOT_MODES[root_mode],
                   lanczos_steps, root_parts, large_layer, beta1, beta2, lr, eps_rel, graft_eps,
-                  fp64_cond_threshold)
+                  fp64_cond_threshold, newton_tol)
 
 
 ROOTS_NONE, ROOTS_ALL = -1, -2
