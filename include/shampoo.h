@@ -230,7 +230,8 @@ int shampoo_update_stats(shampoo_t* h, const float* const* grads,
 /* Inverse roots (cue 10, 12, 14): for every factor S, lambda_max by Lanczos,
  * eps = eps_rel * lambda_max, then P = (S + eps I)^(-1/p) (p = root_p, or
  * root_p / 2 for the factor of a one-sided block) by coupled Newton
- * iteration (newton_iters steps; fp32, fp64 or routed per root_mode).  A
+ * iteration (newton_iters steps, or fewer for a fused fp32 root that meets
+ * newton_tol; fp32, fp64 or routed per root_mode).  A
  * factor with non-finite S or a non-finite result keeps its previous root; a
  * factor with lambda_max <= 0 gets P = I.  The caller decides the cadence
  * (call it when step % k == 0); in between, the last roots are used.
