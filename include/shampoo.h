@@ -114,7 +114,7 @@ typedef struct {
     double fp64_cond_threshold; /* AUTO mode: kappa(S + eps I) above this -> fp64 root  */
     double newton_tol;        /* 0 = every root runs its full iteration count.  In [0, 1):
                                  a root of a factor up to 128 computed in fp32 stops one
-                                 step after max |M_k - I| first falls below newton_tol
+                                 step after ||M_k - I||_F first falls below newton_tol
                                  (the coupled iteration's convergence test; near I the
                                  error squares each step), at most the full count.  The
                                  batched paths (factors above 128, fp64) always run the

@@ -67,10 +67,6 @@ __device__ __forceinline__ double wave_max(double v) {
     for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
     return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
-}
 
 // Fixed-order block reduction over 256 threads (deterministic).
 __device__ __forceinline__ double block_sum_256(double v, double* red) {
@@ -1487,7 +1483,7 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
     __shared__ LanczosSlot lz;
     __shared__ double red[4];
     __shared__ double sh_lmax;   // re-read after the iteration: no set-up value lives across it
-    __shared__ float sh_dev[4];  // per-wave max |M - I| of the iterate just formed
+    __shared__ float sh_dev[4];  // per-wave sum of (M - I)^2 of the iterate just formed
     const FactorJob jb = jobs[blockIdx.x];
     const int n = jb.n, ld = jb.ld;
     constexpr int p = PP;
@@ -1551,9 +1547,10 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
 
     // slot: X, registers: M.  X T = c1 X + c2 X M, so the first product takes
     // M itself as its right operand.
-    // With a tolerance, the iteration ends one step after max |M - I| first
-    // falls below it: near I the error squares each step (times (p+1)/(2p)),
-    // so that step leaves about tol^2, below fp32 resolution for tol <= 1e-3.
+    // With a tolerance, the iteration ends one step after ||M - I||_F first
+    // falls below it.  The Frobenius norm bounds the spectral one, and near I
+    // the spectral error e maps to about (p+1)/(2p) e^2, so that step leaves
+    // at most about tol^2: below fp32 resolution for tol <= 1e-3.
     const float tol = args.tol;
     int ran = iters;
     bool last = false;
@@ -1616,9 +1613,10 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = 32 * m + 8 * (r >> 2) + 4 * h + (r & 3);
-                    dv = fmaxf(dv, fabsf(M.v[m][r] - (row == dcol ? 1.f : 0.f)));
+                    const float e = M.v[m][r] - (row == dcol ? 1.f : 0.f);
+                    dv = fmaf(e, e, dv);
                 }
-            dv = wave_max(dv);
+            dv = wave_sum(dv);
             if (lane == 0) sh_dev[w] = dv;
         }
         __syncthreads();
@@ -1630,7 +1628,7 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
                 ran = it + 1;
                 break;
             }
-            last = fmaxf(fmaxf(sh_dev[0], sh_dev[1]), fmaxf(sh_dev[2], sh_dev[3])) < tol;
+            last = (sh_dev[0] + sh_dev[1]) + (sh_dev[2] + sh_dev[3]) < tol * tol;
         }
     }
 

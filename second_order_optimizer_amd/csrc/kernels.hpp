@@ -66,7 +66,7 @@ struct FusedArgs {          // fused fp32 root of factors up to 128
     int steps_s, steps_p;   // Lanczos steps on S (lambda_max) and on the root (kappa)
     int auto_route;         // set prec flags from the kappa estimate
     double eps_rel, threshold;
-    float tol;              // > 0: stop one step after max |M - I| < tol (at most iters)
+    float tol;              // > 0: stop one step after ||M - I||_F < tol (at most iters)
 };
 
 struct UpdateArgs {

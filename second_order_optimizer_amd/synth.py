@@ -52,7 +52,7 @@ class Workload:
     fp64_cond_threshold: float = 1e5
     cadence: int = 1                # inverse roots recomputed when step % cadence == 0
     newton_iters: int = 20
-    newton_tol: float = 1e-3        # fused roots stop one step after max|M - I| < this
+    newton_tol: float = 1e-3        # fused roots stop one step after ||M - I||_F < this
     root_p: int = 4
     beta1: float = 0.9
     beta2: float = 0.999

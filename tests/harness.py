@@ -98,3 +98,18 @@ def make_oracle(wl, ids, **over):
     shapes = [(s.rows, s.cols, s.kind) for s in specs]
     W0 = [synth.initial_weight(wl, i) for i in ids]
     return O.ShampooOracle(oracle_config(wl, **over), shapes, W0)
+
+
+def newton_steps(eigs, lam_max, eps, p, tol, cap):
+    """Steps the coupled Newton iteration runs in exact arithmetic when it
+    stops one step after ||M_k - I||_F < tol (at most cap).  M_k is a
+    function of A = S + eps I, so each eigenvalue of S follows the scalar
+    map m <- m ((p + 1 - m) / p)^p from m_0 = z (lambda + eps), with
+    z = (p + 1) / (2 (lam_max + eps))."""
+    import numpy as np
+    m = (p + 1) / (2.0 * (lam_max + eps)) * (np.asarray(eigs, dtype=np.float64) + eps)
+    for k in range(1, cap + 1):
+        m = m * ((p + 1 - m) / p) ** p
+        if np.sqrt(np.sum((m - 1.0) ** 2)) < tol:     # ||M_k - I||_F
+            return min(k + 1, cap)
+    return cap

@@ -11,7 +11,7 @@ import sys
 import numpy as np
 import pytest
 
-from harness import GpuRun, make_oracle, rel_fro
+from harness import GpuRun, make_oracle, newton_steps, rel_fro
 from oracle import shampoo_oracle as O
 from second_order_optimizer_amd import synth
 
@@ -413,23 +413,9 @@ def test_root_exponents_1_and_8(root_p):
     run_parity(wl)
 
 
-def _newton_steps(S, d, p, tol, cap):
-    """Steps the coupled iteration needs in exact arithmetic: M_k is a
-    function of S + eps I, so each eigenvalue follows the scalar map
-    m <- m ((p + 1 - m) / p)^p from m_0 = z (lambda + eps), z = (p+1)/(2
-    (lambda_max + eps)) with the GPU's own lambda_max and eps; the
-    iteration stops one step after max |m_k - 1| < tol, at most cap."""
-    m = (p + 1) / (2.0 * (d.lambda_max + d.eps)) * (np.linalg.eigvalsh(S) + d.eps)
-    for k in range(1, cap + 1):
-        m = m * ((p + 1 - m) / p) ** p
-        if np.max(np.abs(m - 1.0)) < tol:
-            return min(k + 1, cap)
-    return cap
-
-
 @pytest.mark.parametrize("tol", [0.0, 1e-3])
 def test_fused_root_convergence_exit(tol):
-    """Factors up to 128 in fp32 stop one step after max |M - I| < tol: each
+    """Factors up to 128 in fp32 stop one step after ||M - I||_F < tol: each
     factor's step count matches the scalar eigenvalue map of its own
     spectrum (within one step: the fp32 residual near the threshold), the
     roots and updates still meet their bars, and tol = 0 runs the full count.
@@ -448,7 +434,8 @@ def test_fused_root_convergence_exit(tol):
             if tol == 0.0 or d.status & FP64:
                 assert d.iters == wl.newton_iters, (b, f, d.iters, d.status)
                 continue
-            pred = _newton_steps(_np(S), d, wl.root_p, tol, wl.newton_iters)
+            pred = newton_steps(np.linalg.eigvalsh(_np(S)), d.lambda_max, d.eps, wl.root_p, tol,
+                                wl.newton_iters)
             assert abs(d.iters - pred) <= 1, (b, f, d.iters, pred)
             counts.append(d.iters)
     if tol > 0.0:

@@ -255,3 +255,46 @@ def test_newton_scratch_budget_from_environment(monkeypatch):
     saved += _newton_split_bytes(8, 256, 8) - _newton_split_bytes(1, 256, 8)
     # the launch tables of the extra chunks (tens of KB) take some of it back
     assert 0 <= saved - (full - small) < 256 << 10
+
+
+@pytest.mark.parametrize("p", [1, 2, 4, 8])
+def test_newton_step_count_model(p):
+    """The step-count model the GPU test holds the fused root's convergence
+    exit to: a dense fp64 coupled Newton iteration (Guo & Higham: X_0 =
+    z^(1/p) I, M_0 = z A, T = ((p+1) I - M) / p, X <- X T, M <- T^p M) on an
+    SPD matrix with a log-spaced spectrum has, step by step, the Frobenius
+    norm ||M_k - I||_F the scalar eigenvalue map gives (the norm is unitarily
+    invariant), so it stops at the model's step; the root it leaves is
+    within the bound the exit rule implies."""
+    from harness import newton_steps
+    rng = np.random.default_rng(7)
+    for kappa in (10.0, 1e3, 1e5):
+        n = 24
+        lam = np.logspace(-np.log10(kappa), 0.0, n)
+        q, _ = np.linalg.qr(rng.standard_normal((n, n)))
+        A = (q * lam) @ q.T
+        z = (p + 1) / 2.0
+        X, M = z ** (1.0 / p) * np.eye(n), z * A
+        m = z * lam
+        stop, dense_steps = False, None
+        for k in range(1, 41):
+            T = ((p + 1) * np.eye(n) - M) / p
+            X = X @ T
+            M = np.linalg.matrix_power(T, p) @ M
+            m = m * ((p + 1 - m) / p) ** p
+            d_dense = np.linalg.norm(M - np.eye(n))
+            d_map = np.sqrt(np.sum((m - 1.0) ** 2))
+            assert abs(d_dense - d_map) <= 1e-9 * max(1.0, d_map), (p, kappa, k, d_dense, d_map)
+            if stop:
+                dense_steps = k
+                break
+            stop = d_dense < 1e-3
+        assert dense_steps == newton_steps(lam, 1.0, 0.0, p, 1e-3, 40), (p, kappa)
+        # one step after ||M - I||_F < 1e-3 the spectral error is at most about
+        # (p+1)/(2p) 1e-6, and the root's relative error about that over p
+        # the stopped iterate is the root to about the map's last residual
+        ref = (q * lam ** (-1.0 / p)) @ q.T
+        assert np.linalg.norm(X - ref) / np.linalg.norm(ref) < 2e-6, (p, kappa)
+    if p == 4:
+        assert [newton_steps(np.logspace(-e, 0, 50), 1.0, 0.0, 4, 1e-3, 40)
+                for e in (1, 3, 5)] == [6, 11, 16]
