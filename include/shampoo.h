@@ -113,12 +113,13 @@ typedef struct {
     double graft_eps;         /* delta in A = G / (sqrt(a) + delta)                      */
     double fp64_cond_threshold; /* AUTO mode: kappa(S + eps I) above this -> fp64 root  */
     double newton_tol;        /* 0 = every root runs its full iteration count.  In [0, 1):
-                                 a root of a factor up to 128 computed in fp32 stops one
-                                 step after ||M_k - I||_F first falls below newton_tol
-                                 (the coupled iteration's convergence test; near I the
-                                 error squares each step), at most the full count.  The
-                                 batched paths (factors above 128, fp64) always run the
-                                 full count.  E.g. 1e-3                                  */
+                                 an fp32 root stops once ||M_k - I||_F has fallen below
+                                 newton_tol (the coupled iteration's convergence test;
+                                 near I the error squares each step), at most the full
+                                 count: a factor up to 128 one step after, a larger one
+                                 (batched chain, checked at step counts of the full
+                                 count's parity from 4 on) two steps after.  fp64 roots
+                                 always run the full count.  E.g. 1e-3                   */
 } shampoo_config;
 
 /* Row-sparse gradient of one SHAMPOO_SPARSE_ROWS table: n_rows distinct row

@@ -159,6 +159,7 @@ struct shampoo_s {
     // arena layout (bytes)
     size_t total = 0;
     int64_t off_bases = 0, off_sparse = 0, off_tables = 0, off_diag = 0, off_prec = 0, off_chk = 0;
+    int64_t off_stop = 0;
     int64_t off_lzwork = 0;
     int64_t off_slot_jobs = 0, off_slot_live = 0;  // packed fp64 chain: slot jobs and flags
     int64_t slot_tmpl_off = 0;                     // and the template job of every slot entry
@@ -589,6 +590,7 @@ int build_plan(shampoo_s* h) {
     h->off_diag = take((int64_t)std::max(nf, 1) * sizeof(FactorDiag));
     h->off_prec = take((int64_t)std::max(nf, 1) * 4);
     h->off_chk = take((int64_t)std::max(nf, 1) * 16);   // Newton finish: per-factor check slots
+    h->off_stop = take((int64_t)std::max(nf, 1) * 8);   // fp32 chain exit: stop, conv flags
     h->off_lzwork = take((int64_t)kLanczosSplitMax * kLzWork * 8);  // split Lanczos records
     for (auto& f : h->factors) f.off_s = take((int64_t)f.ld * f.ld * 8);  // fp64 statistics
     for (auto& f : h->factors) f.off_p = take((int64_t)f.ld * f.ld * 4);
@@ -1609,6 +1611,12 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
     na.gate = gate;
     na.gate_val = gate_val;
     na.chk = at<unsigned long long>(h, h->off_chk);
+    // the fp32 chain's convergence exit: stop flags gate its products
+    const bool exit32 = !fp64 && h->cfg.newton_tol > 0.0;
+    if (exit32) {
+        na.stop = at<int32_t>(h, h->off_stop);
+        na.conv = na.stop + std::max((int)h->factors.size(), 1);
+    }
     void* scratch = h->arena + (fp64 ? h->off_scr64 : h->off_scr32);
     FactorDiag* diag = at<FactorDiag>(h, h->off_diag);
     GemmArgs g{};
@@ -1629,8 +1637,8 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
         const FactorJob* jobs = ch.compact ? at<FactorJob>(h, ch.slot_jobs_off)
                                            : tab<FactorJob>(h, ch.jobs_off);
         na.gate = ch.compact ? nullptr : gate;
-        g.gate = ch.compact ? at<int32_t>(h, h->off_slot_live) : gate;
-        g.gate_val = ch.compact ? 1 : gate_val;
+        g.gate = ch.compact ? at<int32_t>(h, h->off_slot_live) : exit32 ? na.stop : gate;
+        g.gate_val = ch.compact ? 1 : exit32 ? 0 : gate_val;
         int rc;
         if (ch.fused) {
             // lambda_max, eps, the root and the kappa estimate of every factor
@@ -1673,6 +1681,19 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
                         rc = hip_err(launch_split_sum(fp64, tab<SplitSumJob>(h, S.sum_jobs_off),
                                                       tab<TileRef>(h, S.sum_tiles_off), S.sum_ntiles,
                                                       h->arena, g.gate, g.gate_val, s));
+                    if (rc) return rc;
+                }
+                // convergence checks at step counts of the full count's
+                // parity: a factor stops two steps after it meets the
+                // tolerance, with its final iterate in the buffer the finish
+                // reads
+                const int k = it + 1;
+                if (exit32 && k >= 4 && k < ch.iters && ((ch.iters - k) & 1) == 0) {
+                    rc = hip_err(launch_newton_conv(
+                        jobs, ch.njobs,
+                        reinterpret_cast<const float*>(static_cast<unsigned char*>(scratch) +
+                                                       (size_t)(k & 1) * ch.ld * ch.ld * 4),
+                        diag, na, k, h->cfg.newton_tol * h->cfg.newton_tol, s));
                     if (rc) return rc;
                 }
             }

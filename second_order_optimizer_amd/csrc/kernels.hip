@@ -1227,6 +1227,10 @@ __global__ __launch_bounds__(256) void k_newton_init(const FactorJob* __restrict
     if (blockIdx.x == 0 && threadIdx.x == 0) {   // the finish's check slots of this pass
         args.chk[2 * jb.factor] = 0ull;
         args.chk[2 * jb.factor + 1] = 0ull;
+        if (args.stop) {
+            args.stop[jb.factor] = 0;
+            args.conv[jb.factor] = 0;
+        }
     }
     const FactorDiag dg = diag[jb.factor];
     const bool ok = dg.status == 0;
@@ -1311,6 +1315,41 @@ __global__ __launch_bounds__(256) void k_newton_check(const FactorJob* __restric
     }
 }
 
+__global__ __launch_bounds__(256) void k_newton_conv(const FactorJob* __restrict__ jobs,
+                                                    const float* __restrict__ scratch,
+                                                    FactorDiag* __restrict__ diag, NewtonArgs args,
+                                                    int k, double tol2) {
+    __shared__ double red[4];
+    const FactorJob jb = jobs[blockIdx.x];
+    if (jb.factor < 0 || args.stop[jb.factor]) return;
+    if (diag[jb.factor].status & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_ZERO_)) return;
+    if (args.conv[jb.factor]) {          // met the tolerance two steps ago
+        if (threadIdx.x == 0) {
+            args.stop[jb.factor] = 1;
+            diag[jb.factor].iters = k;
+        }
+        return;
+    }
+    const int n = jb.n, ld = jb.ld;
+    const float* M = scratch + jb.m_off;
+    // rows of n in 16-byte pieces (ld is a multiple of 32; the piece that
+    // crosses column n is masked)
+    const int pr = (n + 3) >> 2;
+    double acc = 0.0;
+    for (int e = threadIdx.x; e < n * pr; e += 256) {
+        const int i = e / pr, j0 = 4 * (e - i * pr);
+        const float4 v = *reinterpret_cast<const float4*>(M + (int64_t)i * ld + j0);
+        const float q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const double d = (j0 + u < n) ? double(q[u]) - (i == j0 + u ? 1.0 : 0.0) : 0.0;
+            acc = fma(d, d, acc);
+        }
+    }
+    acc = block_sum_256(acc, red);
+    if (threadIdx.x == 0 && acc < tol2) args.conv[jb.factor] = 1;   // NaN: keeps running
+}
+
 // Finish, part 2 (same sharing of tiles): unless the factor's input or iterate went
 // non-finite (then its previous root stays), the root is the symmetric part
 // of X (the tile and its mirror, transposed in LDS), the identity for a
@@ -1339,7 +1378,7 @@ __global__ __launch_bounds__(256) void k_newton_commit(const FactorJob* __restri
         else st &= ~SHAMPOO_FACTOR_FP64_;
         dg.status = st;
         dg.residual = res;
-        dg.iters = st0 == 0 ? args.iters : 0;
+        if (!(args.stop && args.stop[jb.factor])) dg.iters = st0 == 0 ? args.iters : 0;
     }
     if (keep) return;
     const bool ident = (st & SHAMPOO_FACTOR_ZERO_) != 0;
@@ -2750,6 +2789,15 @@ hipError_t launch_route_compact(const CompactClass* cls, int ncls, const FactorJ
                        live);
     return hipGetLastError();
 }
+hipError_t launch_newton_conv(const FactorJob* jobs, int njobs, const float* scratch,
+                              FactorDiag* diag, const NewtonArgs& a, int k, double tol2,
+                              hipStream_t s) {
+    if (njobs <= 0) return hipSuccess;
+    if (!a.stop || !a.conv) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_newton_conv, dim3(njobs), dim3(256), 0, s, jobs, scratch, diag, a, k, tol2);
+    return hipGetLastError();
+}
+
 hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, int ld,
                               const double* stats, void* scratch, const FactorDiag* diag,
                               const NewtonArgs& a, hipStream_t s) {

@@ -113,3 +113,17 @@ def newton_steps(eigs, lam_max, eps, p, tol, cap):
         if np.sqrt(np.sum((m - 1.0) ** 2)) < tol:     # ||M_k - I||_F
             return min(k + 1, cap)
     return cap
+
+
+def newton_steps_checked(eigs, lam_max, eps, p, tol, cap, first=4):
+    """The batched chain's rule in exact arithmetic: ||M_k - I||_F is checked
+    only at step counts k >= first of the parity of cap, and the factor
+    stops two steps after the first check that meets tol (at most cap)."""
+    import numpy as np
+    m = (p + 1) / (2.0 * (lam_max + eps)) * (np.asarray(eigs, dtype=np.float64) + eps)
+    for k in range(1, cap + 1):
+        m = m * ((p + 1 - m) / p) ** p
+        if k >= first and k < cap and (cap - k) % 2 == 0 and \
+                np.sqrt(np.sum((m - 1.0) ** 2)) < tol:
+            return min(k + 2, cap)
+    return cap
