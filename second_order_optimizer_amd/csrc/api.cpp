@@ -159,7 +159,7 @@ struct shampoo_s {
     // arena layout (bytes)
     size_t total = 0;
     int64_t off_bases = 0, off_sparse = 0, off_tables = 0, off_diag = 0, off_prec = 0, off_chk = 0;
-    int64_t off_stop = 0;
+    int64_t off_stop = 0, off_convp = 0;
     int64_t off_lzwork = 0;
     int64_t off_slot_jobs = 0, off_slot_live = 0;  // packed fp64 chain: slot jobs and flags
     int64_t slot_tmpl_off = 0;                     // and the template job of every slot entry
@@ -590,7 +590,8 @@ int build_plan(shampoo_s* h) {
     h->off_diag = take((int64_t)std::max(nf, 1) * sizeof(FactorDiag));
     h->off_prec = take((int64_t)std::max(nf, 1) * 4);
     h->off_chk = take((int64_t)std::max(nf, 1) * 16);   // Newton finish: per-factor check slots
-    h->off_stop = take((int64_t)std::max(nf, 1) * 8);   // fp32 chain exit: stop, conv flags
+    h->off_stop = take((int64_t)std::max(nf, 1) * 12);  // fp32 chain exit: stop, conv, cnt
+    h->off_convp = take((int64_t)std::max(nf, 1) * 32 * 8);   // and the checks' partial sums
     h->off_lzwork = take((int64_t)kLanczosSplitMax * kLzWork * 8);  // split Lanczos records
     for (auto& f : h->factors) f.off_s = take((int64_t)f.ld * f.ld * 8);  // fp64 statistics
     for (auto& f : h->factors) f.off_p = take((int64_t)f.ld * f.ld * 4);
@@ -1616,6 +1617,8 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
     if (exit32) {
         na.stop = at<int32_t>(h, h->off_stop);
         na.conv = na.stop + std::max((int)h->factors.size(), 1);
+        na.cnt = na.conv + std::max((int)h->factors.size(), 1);
+        na.part = at<double>(h, h->off_convp);
     }
     void* scratch = h->arena + (fp64 ? h->off_scr64 : h->off_scr32);
     FactorDiag* diag = at<FactorDiag>(h, h->off_diag);
@@ -1690,7 +1693,7 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
                 const int k = it + 1;
                 if (exit32 && k >= 4 && k < ch.iters && ((ch.iters - k) & 1) == 0) {
                     rc = hip_err(launch_newton_conv(
-                        jobs, ch.njobs,
+                        jobs, ch.njobs, ch.ld,
                         reinterpret_cast<const float*>(static_cast<unsigned char*>(scratch) +
                                                        (size_t)(k & 1) * ch.ld * ch.ld * 4),
                         diag, na, k, h->cfg.newton_tol * h->cfg.newton_tol, s));

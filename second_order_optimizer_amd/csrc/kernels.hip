@@ -1230,6 +1230,7 @@ __global__ __launch_bounds__(256) void k_newton_init(const FactorJob* __restrict
         if (args.stop) {
             args.stop[jb.factor] = 0;
             args.conv[jb.factor] = 0;
+            args.cnt[jb.factor] = 0;
         }
     }
     const FactorDiag dg = diag[jb.factor];
@@ -1320,23 +1321,27 @@ __global__ __launch_bounds__(256) void k_newton_conv(const FactorJob* __restrict
                                                     FactorDiag* __restrict__ diag, NewtonArgs args,
                                                     int k, double tol2) {
     __shared__ double red[4];
-    const FactorJob jb = jobs[blockIdx.x];
-    if (jb.factor < 0 || args.stop[jb.factor]) return;
-    if (diag[jb.factor].status & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_ZERO_)) return;
-    if (args.conv[jb.factor]) {          // met the tolerance two steps ago
-        if (threadIdx.x == 0) {
-            args.stop[jb.factor] = 1;
-            diag[jb.factor].iters = k;
+    __shared__ int last;
+    const FactorJob jb = jobs[blockIdx.y];
+    const int f = jb.factor;
+    if (f < 0 || args.stop[f]) return;
+    if (diag[f].status & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_ZERO_)) return;
+    if (args.conv[f] != 0 && args.conv[f] < k) {   // met the tolerance two steps ago
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            args.stop[f] = 1;
+            diag[f].iters = k;
         }
         return;
     }
     const int n = jb.n, ld = jb.ld;
     const float* M = scratch + jb.m_off;
     // rows of n in 16-byte pieces (ld is a multiple of 32; the piece that
-    // crosses column n is masked)
-    const int pr = (n + 3) >> 2;
+    // crosses column n is masked), split into gridDim.x contiguous ranges
+    const int pr = (n + 3) >> 2, total = n * pr;
+    const int per = (total + gridDim.x - 1) / gridDim.x;
+    const int e0 = blockIdx.x * per, e1 = min(total, e0 + per);
     double acc = 0.0;
-    for (int e = threadIdx.x; e < n * pr; e += 256) {
+    for (int e = e0 + threadIdx.x; e < e1; e += 256) {
         const int i = e / pr, j0 = 4 * (e - i * pr);
         const float4 v = *reinterpret_cast<const float4*>(M + (int64_t)i * ld + j0);
         const float q[4] = {v.x, v.y, v.z, v.w};
@@ -1347,7 +1352,19 @@ __global__ __launch_bounds__(256) void k_newton_conv(const FactorJob* __restrict
         }
     }
     acc = block_sum_256(acc, red);
-    if (threadIdx.x == 0 && acc < tol2) args.conv[jb.factor] = 1;   // NaN: keeps running
+    if (threadIdx.x == 0) {
+        args.part[32 * f + blockIdx.x] = acc;
+        __threadfence();
+        last = atomicAdd(&args.cnt[f], 1) == (int)gridDim.x - 1;
+    }
+    __syncthreads();
+    if (!last || threadIdx.x != 0) return;
+    __threadfence();
+    double sum = 0.0;
+    for (int q = 0; q < (int)gridDim.x; ++q)   // fixed order: a deterministic decision
+        sum += __hip_atomic_load(&args.part[32 * f + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    args.cnt[f] = 0;
+    if (sum < tol2) args.conv[f] = k;          // NaN: keeps running
 }
 
 // Finish, part 2 (same sharing of tiles): unless the factor's input or iterate went
@@ -2789,12 +2806,17 @@ hipError_t launch_route_compact(const CompactClass* cls, int ncls, const FactorJ
                        live);
     return hipGetLastError();
 }
-hipError_t launch_newton_conv(const FactorJob* jobs, int njobs, const float* scratch,
+hipError_t launch_newton_conv(const FactorJob* jobs, int njobs, int ld, const float* scratch,
                               FactorDiag* diag, const NewtonArgs& a, int k, double tol2,
                               hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
-    if (!a.stop || !a.conv) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_newton_conv, dim3(njobs), dim3(256), 0, s, jobs, scratch, diag, a, k, tol2);
+    if (!a.stop || !a.conv || !a.cnt || !a.part || ld < 1) return hipErrorInvalidValue;
+    // at least 64 KB of M per workgroup, at most 32 per factor, and about
+    // 2048 workgroups in all (a chunk of many factors needs no split)
+    const int parts = std::max(1, std::min({32, (int)(((int64_t)ld * ld + 16383) / 16384),
+                                            (2048 + njobs - 1) / njobs}));
+    hipLaunchKernelGGL(k_newton_conv, dim3(parts, njobs), dim3(256), 0, s, jobs, scratch, diag, a, k,
+                       tol2);
     return hipGetLastError();
 }
 

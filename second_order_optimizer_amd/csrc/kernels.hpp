@@ -59,10 +59,14 @@ struct NewtonArgs {
     int32_t gate_val;
     int iters;                 // iterations run (recorded in the diagnostics)
     // fp32 chain with a tolerance: stop[f] != 0 once factor f has stopped
-    // (its products are gated off), conv[f] once it met the tolerance at a
-    // check; both cleared by the start.  Null otherwise.
+    // (its products are gated off); conv[f] = the step count of the check
+    // where it met the tolerance; cnt[f] counts the workgroups of a check
+    // done, part[32 f ..] their partial sums.  Cleared by the start.  Null
+    // otherwise.
     int32_t* stop;
     int32_t* conv;
+    int32_t* cnt;
+    double* part;
     unsigned long long* chk;   // per factor: [2f] max |M - I| (bits), [2f + 1] non-finite flag
 };
 
@@ -107,10 +111,11 @@ hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, int l
                               const NewtonArgs& a, hipStream_t s);
 // Convergence check of the fp32 chain after k steps (k of the parity of the
 // full count, so a stopped factor's final iterate is in the buffer the finish
-// reads): one workgroup per factor forms ||M_k - I||_F^2 over n x n in a fixed
-// order; a factor that met tol at the previous check stops (diagnostics
-// record k steps), one that meets it now is marked.
-hipError_t launch_newton_conv(const FactorJob* jobs, int njobs, const float* scratch,
+// reads): up to 32 workgroups per factor form partial sums of ||M_k - I||_F^2
+// over n x n, and the last one to finish adds them in a fixed order; a factor
+// that met tol at an earlier check stops (diagnostics record k steps), one
+// that meets it now is marked with k.
+hipError_t launch_newton_conv(const FactorJob* jobs, int njobs, int ld, const float* scratch,
                               FactorDiag* diag, const NewtonArgs& a, int k, double tol2,
                               hipStream_t s);
 hipError_t launch_newton_commit(bool fp64, const FactorJob* jobs, int njobs, int ld, float* arena,
