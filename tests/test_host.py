@@ -266,7 +266,7 @@ def test_newton_step_count_model(p):
     norm ||M_k - I||_F the scalar eigenvalue map gives (the norm is unitarily
     invariant), so it stops at the model's step; the root it leaves is
     within the bound the exit rule implies."""
-    from harness import newton_steps
+    from harness import newton_steps, newton_steps_checked
     rng = np.random.default_rng(7)
     for kappa in (10.0, 1e3, 1e5):
         n = 24
@@ -290,6 +290,20 @@ def test_newton_step_count_model(p):
                 break
             stop = d_dense < 1e-3
         assert dense_steps == newton_steps(lam, 1.0, 0.0, p, 1e-3, 40), (p, kappa)
+        # the batched chain's rule: checks only at step counts k >= 4 of the
+        # parity of the full count (cap), a stop two steps after the first
+        # check that meets the tolerance; from the same dense iteration
+        for cap in (20, 23):
+            Xc, Mc = z ** (1.0 / p) * np.eye(n), z * A
+            checked = cap
+            for k in range(1, cap + 1):
+                Tc = ((p + 1) * np.eye(n) - Mc) / p
+                Xc, Mc = Xc @ Tc, np.linalg.matrix_power(Tc, p) @ Mc
+                if 4 <= k < cap and (cap - k) % 2 == 0 and np.linalg.norm(Mc - np.eye(n)) < 1e-3:
+                    checked = min(k + 2, cap)
+                    break
+            assert checked == newton_steps_checked(lam, 1.0, 0.0, p, 1e-3, cap), (p, kappa, cap)
+            assert (checked - cap) % 2 == 0   # the finish's buffer parity
         # one step after ||M - I||_F < 1e-3 the spectral error is at most about
         # (p+1)/(2p) 1e-6, and the root's relative error about that over p
         # the stopped iterate is the root to about the map's last residual
