@@ -343,6 +343,28 @@ typedef struct {
 int shampoo_profile_enable(shampoo_t* h, int32_t on);
 int shampoo_profile_read(shampoo_t* h, shampoo_kernel_time* out, int32_t cap, int32_t* n_out);
 
+/* Machine peaks measured on the current device, for measurement tools that
+ * report kernel rates as fractions of a peak.  None of the method's
+ * arithmetic: the matrix-core issue rate of the two MFMA instructions the
+ * products use (fp32 v_mfma_f32_32x32x2f32, fp64 v_mfma_f64_16x16x4f64),
+ * every wave of a full grid issuing independent products from registers
+ * with no memory traffic, and a plain device-to-device copy (bytes read plus
+ * bytes written, per second).  Each is the median of three timed launches
+ * (HIP events on `stream`) after one warm-up; the call waits for them. */
+typedef struct {
+    double mfma_f32_tflops;  /* TFLOP/s, 2 flops per multiply-add                  */
+    double mfma_f64_tflops;
+    double copy_gbs;         /* GB/s (1e9 bytes), read + write                       */
+    int64_t copy_bytes;      /* bytes read by one copy (half the scratch, rounded)  */
+} shampoo_peaks;
+
+/* scratch: device memory, 256-byte aligned, at least 2 MiB; the copy reads
+ * its first half and writes its second half, the MFMA probes write a few KiB
+ * at its start (contents are overwritten, never interpreted).  Needs no
+ * handle.  Errors: SHAMPOO_E_ARG (null, unaligned or too small scratch),
+ * SHAMPOO_E_HIP. */
+int shampoo_measure_peaks(shampoo_peaks* out, void* scratch, size_t scratch_bytes, void* stream);
+
 /* Free the handle (host memory only; the caller frees the state buffer). */
 void shampoo_destroy(shampoo_t* h);
 

@@ -132,14 +132,15 @@ enum ProfCat : int {
     PC_STATS = 0, PC_LANCZOS_S, PC_LANCZOS_P, PC_NEWTON_INIT, PC_NEWTON_GEMM32, PC_NEWTON_GEMM64,
     PC_NEWTON_COMMIT, PC_ADAGRAD, PC_APPLY_T, PC_APPLY_D, PC_SCALE, PC_UPDATE, PC_SPARSE,
     PC_NEWTON_FUSED, PC_APPLY_FUSED, PC_STEP_FUSED, PC_STATS_SPLITK, PC_SOS_STATS, PC_SOS_NORM,
-    PC_SOS_APPLY, PC_SOS_UPDATE, PC_ROUTE, PC_COUNT
+    PC_SOS_APPLY, PC_SOS_UPDATE, PC_ROUTE, PC_NEWTON_CONV, PC_NEWTON_SPLIT, PC_STATS_SMALL,
+    PC_COUNT
 };
 const char* const kProfNames[PC_COUNT] = {
     "stats_gram_f64", "lanczos_stats", "lanczos_roots", "newton_init", "newton_gemm_f32",
     "newton_gemm_f64", "newton_commit", "adagrad_norm", "apply_gemm_t", "apply_gemm_d",
     "block_scale", "update", "sparse_rows", "newton_fused_f32", "apply_fused", "step_fused",
     "stats_onesided", "stats_onesided_rows", "onesided_rows_norm", "apply_onesided_rows",
-    "onesided_rows_update", "route_compact"};
+    "onesided_rows_update", "route_compact", "newton_conv", "newton_split_sum", "stats_gram128"};
 
 struct ProfRec {
     int cat;
@@ -1337,8 +1338,9 @@ int shampoo_create(const shampoo_config* cfg, int32_t n_tensors, const shampoo_t
     if (!h) return SHAMPOO_E_NOMEM;
     try {
         h->cfg = c;
-        // lanczos_steps == 0: 20 steps for factors up to 128, 24 above (lambda_max
-        // to ~1e-9 relative on the workloads' statistics); 8 for the kappa estimate
+        // lanczos_steps == 0: lambda_max by Lanczos until the top Ritz pair's
+        // residual is within kLanczosTol of theta (checked after 8 steps and
+        // every 4th step), at most 64 steps; 8 steps for the kappa estimate
         h->n = n_tensors;
         h->tensors.resize(n_tensors);
         for (int t = 0; t < n_tensors; ++t) {
@@ -1503,15 +1505,15 @@ int enqueue_stats(shampoo_s* h, hipStream_t s, bool skip_small, const shampoo_sp
     // fp32 gradients, fp64 products and statistics (exact products; the
     // statistics keep the near-null spectrum that fp32 storage would round
     // into the eps damping)
+    if (!skip_small) {
+        ProfScope ps(h, PC_STATS_SMALL, s, h->n_gram128 > 0);
+        const int rc2 = hip_err(launch_gram128(tab<GramJob>(h, h->gram128_off), h->n_gram128,
+                                               at<uint64_t>(h, h->off_bases), at<double>(h, 0),
+                                               a.alpha, a.beta, s));
+        if (rc2) return rc2;
+    }
     {
-        ProfScope ps(h, PC_STATS, s,
-                     h->gram.ntiles > 0 || h->gsplit.ntiles > 0 || (!skip_small && h->n_gram128 > 0));
-        if (!skip_small) {
-            const int rc2 = hip_err(launch_gram128(tab<GramJob>(h, h->gram128_off), h->n_gram128,
-                                                   at<uint64_t>(h, h->off_bases), at<double>(h, 0),
-                                                   a.alpha, a.beta, s));
-            if (rc2) return rc2;
-        }
+        ProfScope ps(h, PC_STATS, s, h->gram.ntiles > 0 || h->gsplit.ntiles > 0);
         int rc = hip_err(launch_gemm_f64_from_f32(tab<GemmTask>(h, h->gram.tasks_off),
                                                   tab<TileRef>(h, h->gram.tiles_off),
                                                   h->gram.ntiles, at<uint64_t>(h, h->off_bases),
@@ -1649,7 +1651,10 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
             FusedArgs fa{};
             fa.p = p;
             fa.iters = ch.iters;
-            fa.steps_s = h->cfg.lanczos_steps > 0 ? h->cfg.lanczos_steps : 20;
+            // lambda_max: lanczos_steps steps, or (0) until the top Ritz
+            // residual is within kLanczosTol, at most 64 steps
+            fa.steps_s = h->cfg.lanczos_steps > 0 ? h->cfg.lanczos_steps : 64;
+            fa.lz_tol = h->cfg.lanczos_steps > 0 ? 0.0 : kLanczosTol;
             fa.steps_p = h->cfg.lanczos_steps > 0 ? std::min(h->cfg.lanczos_steps, 8) : 8;
             fa.auto_route = h->cfg.root_mode == SHAMPOO_ROOT_AUTO ? 1 : 0;
             fa.eps_rel = h->cfg.eps_rel;
@@ -1668,22 +1673,25 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
         }
         if (rc) return rc;
         {
-            // one timing scope over the chunk's whole iteration (per-launch
-            // events around its many short launches would cost more than
-            // they measure)
-            ProfScope ps(h, fp64 ? PC_NEWTON_GEMM64 : PC_NEWTON_GEMM32, s);
+            // timing scopes per launch: products, split-K sums and
+            // convergence checks are separate kernel families
             for (int it = 0; it < ch.iters; ++it) {
                 for (const NewtonStage& S : it == 0 ? ch.first : ch.stages[it & 1]) {
                     const GemmTask* tk = tab<GemmTask>(h, S.gemm.tasks_off);
                     const TileRef* tl = tab<TileRef>(h, S.gemm.tiles_off);
                     g.persist = (fp64 && S.sorted) ? kPersistGrid : 0;
                     g.chain = S.chain;
-                    rc = hip_err(fp64 ? launch_gemm_f64(tk, tl, S.gemm.ntiles, bases, g, s)
-                                      : launch_gemm_f32(tk, tl, S.gemm.ntiles, bases, g, s));
-                    if (!rc && S.parts > 1)
+                    {
+                        ProfScope ps(h, fp64 ? PC_NEWTON_GEMM64 : PC_NEWTON_GEMM32, s);
+                        rc = hip_err(fp64 ? launch_gemm_f64(tk, tl, S.gemm.ntiles, bases, g, s)
+                                          : launch_gemm_f32(tk, tl, S.gemm.ntiles, bases, g, s));
+                    }
+                    if (!rc && S.parts > 1) {
+                        ProfScope ps(h, PC_NEWTON_SPLIT, s);
                         rc = hip_err(launch_split_sum(fp64, tab<SplitSumJob>(h, S.sum_jobs_off),
                                                       tab<TileRef>(h, S.sum_tiles_off), S.sum_ntiles,
                                                       h->arena, g.gate, g.gate_val, s));
+                    }
                     if (rc) return rc;
                 }
                 // convergence checks at step counts of the full count's
@@ -1692,6 +1700,7 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
                 // reads
                 const int k = it + 1;
                 if (exit32 && k >= 4 && k < ch.iters && ((ch.iters - k) & 1) == 0) {
+                    ProfScope ps(h, PC_NEWTON_CONV, s);
                     rc = hip_err(launch_newton_conv(
                         jobs, ch.njobs, ch.ld,
                         reinterpret_cast<const float*>(static_cast<unsigned char*>(scratch) +
@@ -1726,7 +1735,8 @@ int enqueue_roots(shampoo_s* h, RootTables& rt, hipStream_t s) {
     FactorDiag* diag = at<FactorDiag>(h, h->off_diag);
     int32_t* prec = at<int32_t>(h, h->off_prec);
     LanczosArgs la{};
-    la.steps = c.lanczos_steps > 0 ? c.lanczos_steps : 24;
+    la.steps = c.lanczos_steps > 0 ? c.lanczos_steps : 64;
+    la.tol = c.lanczos_steps > 0 ? 0.0 : kLanczosTol;
     la.mode = 0;
     la.eps_rel = c.eps_rel;
     la.threshold = c.fp64_cond_threshold;
@@ -1737,6 +1747,7 @@ int enqueue_roots(shampoo_s* h, RootTables& rt, hipStream_t s) {
     LanczosArgs lp = la;
     lp.mode = 1;
     lp.steps = std::min(la.steps, 8);  // kappa estimate: a factor-2 decision
+    lp.tol = 0.0;
     int rc = SHAMPOO_OK;
     auto lanczos = [&](int64_t small_off, int64_t big_off, bool on_stats, bool with_small,
                        const LanczosArgs& a) -> int {
@@ -1777,7 +1788,7 @@ int enqueue_roots(shampoo_s* h, RootTables& rt, hipStream_t s) {
     }
     // all fp64
     LanczosArgs la_small = la;
-    la_small.steps = c.lanczos_steps > 0 ? c.lanczos_steps : 20;
+    la_small.steps = c.lanczos_steps > 0 ? c.lanczos_steps : 64;
     {
         ProfScope ps(h, PC_LANCZOS_S, s);
         rc = hip_err(launch_lanczos(tab<LanczosJob>(h, rt.lanczos_s_small_off), rt.n_lanczos_small,
@@ -2030,7 +2041,7 @@ int enqueue_sos_apply(shampoo_s* h, float* const* params, const shampoo_sparse_r
         ProfScope ps(h, PC_SOS_APPLY, s, L.ntiles > 0);
         rc = hip_err(launch_gemm_f32(at<GemmTask>(h, h->off_sos_apply + L.tasks_off),
                                      at<TileRef>(h, h->off_sos_apply + L.tiles_off), L.ntiles,
-                                     at<uint64_t>(h, h->off_bases), g, s));
+                                     at<uint64_t>(h, h->off_bases), g, s, 2));
     }
     if (rc) return rc;
     {
@@ -2081,13 +2092,15 @@ int enqueue_apply(shampoo_s* h, float* const* params, const shampoo_sparse_rows*
     {
         ProfScope ps(h, PC_APPLY_T, s, h->apply1.ntiles > 0);
         rc = hip_err(launch_gemm_f32(tab<GemmTask>(h, h->apply1.tasks_off),
-                                     tab<TileRef>(h, h->apply1.tiles_off), h->apply1.ntiles, bases, g, s));
+                                     tab<TileRef>(h, h->apply1.tiles_off), h->apply1.ntiles, bases, g, s,
+                                     1));
     }
     if (rc) return rc;
     {
         ProfScope ps(h, PC_APPLY_D, s, h->apply2.ntiles > 0);
         rc = hip_err(launch_gemm_f32(tab<GemmTask>(h, h->apply2.tasks_off),
-                                     tab<TileRef>(h, h->apply2.tiles_off), h->apply2.ntiles, bases, g, s));
+                                     tab<TileRef>(h, h->apply2.tiles_off), h->apply2.ntiles, bases, g, s,
+                                     2));
     }
     if (rc) return rc;
     {

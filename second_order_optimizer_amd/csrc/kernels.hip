@@ -455,7 +455,10 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
     return true;
 }
 
-template <typename T, typename TA, typename TB, int MINW, bool AXPBY, bool PERSIST>
+// ROLE only names the instantiation (0: Newton products and statistics, 1 and
+// 2: the first and second product of the two-sided apply), so that kernel
+// traces and counters tell the launch families apart.
+template <typename T, typename TA, typename TB, int MINW, bool AXPBY, bool PERSIST, int ROLE = 0>
 __global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__ tasks,
                                              const TileRef* __restrict__ tiles,
                                              const uint64_t* __restrict__ bases, GemmArgs args) {
@@ -708,6 +711,33 @@ __device__ __forceinline__ double tridiag_max_wave(const double* al, const doubl
     return hi;
 }
 
+// Residual norm beta_m |y_m| of the top Ritz pair (theta, y) of the m x m
+// Lanczos tridiagonal (al, be; be[m-1] couples it to the next Lanczos
+// vector): some eigenvalue of the matrix lies within it of theta.  y_m comes
+// from one step of inverse iteration with the shift sigma just above theta,
+// started from e_m: with T - sigma I = L D L^T (negative definite, so the
+// pivots d_j are the Sturm recurrence and never vanish), x = (T - sigma I)^-1
+// e_m has x_m = 1/d_m and x_j = -l_j x_{j+1} (l_j = be_j / d_j), so
+// y_m^2 = x_m^2 / |x|^2 = 1 / S with S = sum_j prod_{i >= j} l_i^2, formed
+// forward as S <- S l_j^2 + 1.  No arrays; an overflow of S means a
+// converged pair (residual 0).
+__device__ __forceinline__ double ritz_residual(const double* al, const double* be, int m,
+                                                double theta) {
+    const double sigma = theta + 1e-10 * fabs(theta);
+    double d = al[0] - sigma, S = 1.0;
+    for (int j = 0; j + 1 < m; ++j) {
+        const double b2 = be[j] * be[j];
+        S = fma(S, b2 / (d * d), 1.0);
+        d = (al[j + 1] - sigma) - b2 / d;
+    }
+    return fabs(be[m - 1]) / sqrt(S);
+}
+
+// Check points of the adaptive Lanczos stop: after 8 steps and every 4th
+// step from there (a top Ritz pair's residual falls steadily until it is
+// converged; checking every 4 steps keeps the multisection's cost small).
+__device__ __forceinline__ bool lanczos_check_step(int m) { return m >= 8 && (m & 3) == 0; }
+
 // 128 x 128 fp32 matrices in LDS ("slots"): row pitch 129 floats, the column
 // index stored with its bits 2 and 5 exchanged.  With this layout the MFMA
 // operand reads of the fused kernels (lane (h, c) at row c, column k + 4h, or
@@ -748,6 +778,7 @@ struct LanczosSlot {
     double al[kLanczosMaxSteps], be[kLanczosMaxSteps];
     double ra[4], rb[4];
     double res;
+    int stop;
 };
 
 // Largest Ritz value of the symmetric n x n matrix held in a slot (entries
@@ -761,9 +792,13 @@ struct LanczosSlot {
 // values by about 1e-6 of lambda_max; the recurrence itself runs in fp64.
 // ROWREG: the thread's 64 matrix entries are read into registers once.
 // Sums run in a fixed order: every thread sees the same alpha and beta, so
-// the early stop is uniform.
+// the early stop is uniform.  tol > 0: stop at the first check point where
+// the top Ritz pair's residual is at most tol theta (theta is then within
+// tol theta of an eigenvalue, the largest one for a start vector that meets
+// its eigenvector), at most `steps` steps.
 template <bool ROWREG>
-__device__ __forceinline__ double lanczos_slot(const float* slot, int n, int steps, LanczosSlot& L) {
+__device__ __forceinline__ double lanczos_slot(const float* slot, int n, int steps, LanczosSlot& L,
+                                               double tol = 0.0) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int r = 32 * w + (lane & 31), hf = lane >> 5;
     steps = min(steps, min(n, kLanczosMaxSteps));
@@ -780,6 +815,7 @@ __device__ __forceinline__ double lanczos_slot(const float* slot, int n, int ste
         v /= sqrt((L.ra[0] + L.ra[1]) + (L.ra[2] + L.ra[3]));
     }
     if (hf == 0) L.vf[r] = (float)v;
+    if (t == 0) L.stop = 0;
     // physical columns 32hf + 64u + q hold logical columns pcol(64u + q) + 4hf;
     // pcol keeps bits 0-1, so four consecutive q are four consecutive columns
     const float* Ar = slot + r * kSP + 32 * hf;
@@ -828,6 +864,19 @@ __device__ __forceinline__ double lanczos_slot(const float* slot, int n, int ste
         if (!(beta > 1e-13 * fabs(alpha)) || !isfinite(alpha) || !isfinite(beta)) {
             m_used = k + 1;
             break;
+        }
+        if (tol > 0.0 && k + 1 < steps && lanczos_check_step(k + 1)) {
+            __syncthreads();   // al, be of this step written
+            if (w == 0) {
+                const double th = tridiag_max_wave(L.al, L.be, k + 1);
+                const double rs = ritz_residual(L.al, L.be, k + 1, th);
+                if (lane == 0) L.stop = !(rs > tol * th);
+            }
+            __syncthreads();
+            if (L.stop) {      // uniform: every thread reads the same word
+                m_used = k + 1;
+                break;
+            }
         }
         v0 = v;
         v = x / beta;
@@ -887,7 +936,7 @@ __global__ __launch_bounds__(256, 2) void k_lanczos(const LanczosJob* __restrict
     const LanczosJob jb = jobs[blockIdx.x];
     stage_sym(slot, arena + jb.off, jb.n, jb.ld);
     __syncthreads();
-    const double lmax = lanczos_slot<true>(slot, jb.n, args.steps, lz);
+    const double lmax = lanczos_slot<true>(slot, jb.n, args.steps, lz, args.tol);
     if (threadIdx.x == 0) lanczos_finish(args, jb, isfinite(lmax), lmax);
 }
 
@@ -905,6 +954,7 @@ struct LanczosBig {
     double red[16];
     double res;
     int m_used, stop;
+    int rstop;   // the adaptive stop's decision at the last check point
 };
 
 __device__ __forceinline__ double block_sum_512(double v, double* red) {
@@ -950,7 +1000,10 @@ __global__ __launch_bounds__(1024) void k_lanczos_big(const LanczosJob* __restri
     }
     const double inv = 1.0 / sqrt(block_sum_1024(s2, L.red));
     for (int i = t; i < n; i += 1024) L.v1[i] *= inv;
-    if (t == 0) L.m_used = steps;
+    if (t == 0) {
+        L.m_used = steps;
+        L.rstop = 0;
+    }
     __syncthreads();
 
     double beta_prev = 0.0;
@@ -1020,6 +1073,19 @@ __global__ __launch_bounds__(1024) void k_lanczos_big(const LanczosJob* __restri
             if (t == 0) L.m_used = k + 1;
             __syncthreads();
             break;
+        }
+        if (args.tol > 0.0 && k + 1 < steps && lanczos_check_step(k + 1)) {
+            __syncthreads();   // al, be of this step written
+            if (w == 0) {
+                const double th = tridiag_max_wave(L.al, L.be, k + 1);
+                const double rs = ritz_residual(L.al, L.be, k + 1, th);
+                if (l == 0) {
+                    L.rstop = !(rs > args.tol * th);
+                    if (L.rstop) L.m_used = k + 1;
+                }
+            }
+            __syncthreads();
+            if (L.rstop) break;   // uniform
         }
         for (int j = t; j < n; j += 1024) {
             L.v0[j] = L.v1[j];
@@ -1109,8 +1175,9 @@ __global__ __launch_bounds__(256) void k_lz_matvec(const LanczosJob* __restrict_
 }
 
 __global__ __launch_bounds__(1024) void k_lz_update(const LanczosJob* __restrict__ jobs,
-                                                   double* __restrict__ work, int k) {
+                                                   double* __restrict__ work, int k, double tol) {
     __shared__ double red[16];
+    __shared__ int rstop;
     const LanczosJob jb = jobs[blockIdx.x];
     double* wk = work + (int64_t)blockIdx.x * kLzWork;
     const int n = jb.n, t = threadIdx.x;
@@ -1137,6 +1204,22 @@ __global__ __launch_bounds__(1024) void k_lz_update(const LanczosJob* __restrict
         wk[kLzMisc] = beta;
     }
     if (stop) return;
+    if (tol > 0.0 && k + 1 < (int)wk[kLzMisc + 1] && lanczos_check_step(k + 1)) {
+        __syncthreads();   // this step's al, be written (same workgroup)
+        if (t < 64) {
+            const double th = tridiag_max_wave(wk + kLzAl, wk + kLzBe, k + 1);
+            const double rs = ritz_residual(wk + kLzAl, wk + kLzBe, k + 1, th);
+            if (t == 0) {
+                rstop = !(rs > tol * th);
+                if (rstop) {
+                    wk[kLzMisc + 1] = (double)(k + 1);
+                    wk[kLzMisc + 2] = 1.0;
+                }
+            }
+        }
+        __syncthreads();
+        if (rstop) return;   // uniform
+    }
     for (int j = t; j < n; j += 1024) {
         wk[kLzV0 + j] = wk[kLzV1 + j];
         wk[kLzV1 + j] = wk[kLzW + j] / beta;
@@ -1564,7 +1647,7 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
     int iters;
     bool okp;
     {
-        const double lm = lanczos_slot<true>(slot, n, args.steps_s, lz);
+        const double lm = lanczos_slot<true>(slot, n, args.steps_s, lz, args.lz_tol);
         if (t == 0) sh_lmax = lm;
         int st;
         double ep, la;
@@ -2704,11 +2787,17 @@ __global__ __launch_bounds__(256) void k_sparse_rows(const SparseJob* __restrict
 
 // ================================================================ launches
 hipError_t launch_gemm_f32(const GemmTask* tasks, const TileRef* tiles, int ntiles,
-                           const uint64_t* bases, const GemmArgs& a, hipStream_t s) {
+                           const uint64_t* bases, const GemmArgs& a, hipStream_t s, int role) {
     if (ntiles <= 0) return hipSuccess;
     if (a.epi == EPI_AXPBY)
         hipLaunchKernelGGL((k_gemm<float, float, float, 1, true, false>), dim3(ntiles), dim3(256), 0, s,
                            tasks, tiles, bases, a);
+    else if (role == 1)
+        hipLaunchKernelGGL((k_gemm<float, float, float, 1, false, false, 1>), dim3(ntiles), dim3(256), 0,
+                           s, tasks, tiles, bases, a);
+    else if (role == 2)
+        hipLaunchKernelGGL((k_gemm<float, float, float, 1, false, false, 2>), dim3(ntiles), dim3(256), 0,
+                           s, tasks, tiles, bases, a);
     else
         hipLaunchKernelGGL((k_gemm<float, float, float, 1, false, false>), dim3(ntiles), dim3(256), 0, s,
                            tasks, tiles, bases, a);
@@ -2767,7 +2856,7 @@ hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, 
             else
                 hipLaunchKernelGGL(k_lz_matvec<float>, mv, dim3(256), 0, s, jobs,
                                    static_cast<const float*>(arena), a.work, k);
-            hipLaunchKernelGGL(k_lz_update, dim3(njobs), dim3(1024), 0, s, jobs, a.work, k);
+            hipLaunchKernelGGL(k_lz_update, dim3(njobs), dim3(1024), 0, s, jobs, a.work, k, a.tol);
         }
         hipLaunchKernelGGL(k_lz_finish, dim3(njobs), dim3(64), 0, s, jobs, a.work, a);
     } else if (big) {

@@ -40,8 +40,13 @@ struct GemmArgs {
 constexpr int kLanczosSplitMax = 32;
 constexpr int kLzWork = 3 * 1024 + 2 * 64 + 4;
 
+// Relative Ritz residual at which the adaptive Lanczos stops: the estimate of
+// lambda_max is then within this fraction of an eigenvalue.
+constexpr double kLanczosTol = 5e-5;
+
 struct LanczosArgs {
-    int steps;
+    int steps;            // at most this many steps
+    double tol;           // > 0: stop once the top Ritz residual <= tol theta
     int mode;             // 0: statistics (lambda_max, eps), 1: roots (kappa estimate)
     int auto_route;       // mode 1: set prec flags from the kappa estimate
     int route_all_fp64;   // mode 0: initial prec flag value
@@ -73,6 +78,7 @@ struct NewtonArgs {
 struct FusedArgs {          // fused fp32 root of factors up to 128
     int p, iters;
     int steps_s, steps_p;   // Lanczos steps on S (lambda_max) and on the root (kappa)
+    double lz_tol;          // > 0: Lanczos on S stops once its Ritz residual <= lz_tol theta
     int auto_route;         // set prec flags from the kappa estimate
     double eps_rel, threshold;
     float tol;              // > 0: stop one step after ||M - I||_F < tol (at most iters)
@@ -82,8 +88,10 @@ struct UpdateArgs {
     float beta1, lr, delta;
 };
 
+// role: 0 Newton products, 1 / 2 the first / second product of the apply
+// (the same kernel; the role only names the instantiation for profilers)
 hipError_t launch_gemm_f32(const GemmTask* tasks, const TileRef* tiles, int ntiles,
-                           const uint64_t* bases, const GemmArgs& a, hipStream_t s);
+                           const uint64_t* bases, const GemmArgs& a, hipStream_t s, int role = 0);
 hipError_t launch_gemm_f64(const GemmTask* tasks, const TileRef* tiles, int ntiles,
                            const uint64_t* bases, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f64_from_f32(const GemmTask* tasks, const TileRef* tiles, int ntiles,

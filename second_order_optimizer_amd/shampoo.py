@@ -62,6 +62,11 @@ class BlockLayout(ctypes.Structure):
                 ("off_pl64", ctypes.c_int64), ("off_pr64", ctypes.c_int64)]
 
 
+class Peaks(ctypes.Structure):
+    _fields_ = [("mfma_f32_tflops", ctypes.c_double), ("mfma_f64_tflops", ctypes.c_double),
+                ("copy_gbs", ctypes.c_double), ("copy_bytes", ctypes.c_int64)]
+
+
 class KernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64),
                 ("total_ms", ctypes.c_double)]
@@ -94,6 +99,7 @@ SIGNATURES = {
     "shampoo_profile_enable": (ctypes.c_int, [_P, ctypes.c_int32]),
     "shampoo_profile_read": (ctypes.c_int, [_P, ctypes.POINTER(KernelTime), ctypes.c_int32,
                                             ctypes.POINTER(ctypes.c_int32)]),
+    "shampoo_measure_peaks": (ctypes.c_int, [ctypes.POINTER(Peaks), _P, ctypes.c_size_t, _P]),
     "shampoo_destroy": (None, [_P]),
     "shampoo_strerror": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -138,6 +144,22 @@ def make_config(block_size: int, *, max_precond_dim: int = 0, root_p: int = 4,
 
 
 ROOTS_NONE, ROOTS_ALL = -1, -2
+
+
+def measure_peaks(device="cuda", scratch_mib: int = 2048) -> dict:
+    """Matrix-core and copy peaks of the device (shampoo_measure_peaks): fp32
+    and fp64 MFMA TFLOP/s with no memory traffic, and the GB/s of a plain
+    device copy of scratch_mib / 2 MiB."""
+    import torch
+    dev = torch.device(device)
+    buf = torch.empty(scratch_mib << 20, dtype=torch.uint8, device=dev)
+    out = Peaks()
+    s = _P(torch.cuda.current_stream(dev).cuda_stream)
+    _check(lib().shampoo_measure_peaks(ctypes.byref(out), buf.data_ptr(), buf.numel(), s),
+           "shampoo_measure_peaks")
+    del buf
+    return {"mfma_f32_tflops": out.mfma_f32_tflops, "mfma_f64_tflops": out.mfma_f64_tflops,
+            "copy_gbs": out.copy_gbs, "copy_bytes": out.copy_bytes}
 
 
 def root_selector(step: int, cadence: int, parts: int) -> int:

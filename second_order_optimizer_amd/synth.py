@@ -135,8 +135,9 @@ def workload(wid: int) -> Workload:
     """The five synthetic workloads, by id 0..4."""
     if wid == 0:
         return Workload(0, "single-256x512-b128", [TensorSpec("w", 256, 512)], 128,
-                        cadence=1, steps=10,
-                        notes="one fp32 weight, 8 blocks of 128x128, roots every step")
+                        cadence=1, steps=10, newton_tol=0.0,
+                        notes="one fp32 weight, 8 blocks of 128x128, roots every step "
+                              "with the full 20 coupled-Newton iterations")
     if wid == 1:
         return Workload(1, "transformer-base-b128", _transformer_base(), 128,
                         max_precond_dim=4096, cadence=20, steps=80,

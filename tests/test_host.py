@@ -39,6 +39,7 @@ def test_struct_sizes_match_header():
     assert ctypes.sizeof(S.FactorDiag) == 56
     assert ctypes.sizeof(S.BlockLayout) == 88
     assert ctypes.sizeof(S.KernelTime) == 48
+    assert ctypes.sizeof(S.Peaks) == 32
 
 
 def test_strerror_and_argument_errors():
@@ -85,6 +86,12 @@ def test_strerror_and_argument_errors():
     assert L.shampoo_create(ctypes.byref(c), 1, descs, ctypes.byref(h)) == -1
     assert L.shampoo_update_stats(p.h, None, None, None) == -1
     p.close()
+    # the peak probe checks its scratch before touching the device
+    pk = S.Peaks()
+    assert L.shampoo_measure_peaks(None, S._P(256), 1 << 22, None) == -1
+    assert L.shampoo_measure_peaks(ctypes.byref(pk), None, 1 << 22, None) == -1
+    assert L.shampoo_measure_peaks(ctypes.byref(pk), S._P(257), 1 << 22, None) == -1
+    assert L.shampoo_measure_peaks(ctypes.byref(pk), S._P(256), 1 << 20, None) == -1
 
 
 EXPECTED_BLOCKS = {0: 8, 1: 2688, 2: 1152, 3: 422, 4: 3}
