@@ -249,6 +249,25 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream);
  * SHAMPOO_E_STATE, SHAMPOO_E_HIP. */
 int shampoo_compute_inverse_roots_part(shampoo_t* h, int32_t part, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * root pass as shampoo_compute_inverse_roots, every factor, whose batched
+ * coupled-Newton iterates (factors above 128 in fp32, every fp64 root) live
+ * in a static device array of the library, 64 MiB per GPU (held from the
+ * first shampoo_bind_state on that GPU until the process ends), instead of
+ * the scratch part of the state buffer; no split-K stages.  It calls no
+ * hipMalloc, hipFree or other allocating routine, and records no profiling
+ * events.  Results: statistics-derived diagnostics and routing as the whole
+ * pass; roots to rounding of it (products summed without the split).  Every
+ * call on one GPU shares that GPU's array and leaves its last contents there
+ * (nothing in it needs clearing: each chunk writes every iterate it reads),
+ * so calls that overlap on one GPU (several handles or streams at once) race.
+ * Must be called with the device current at shampoo_bind_state.
+ * Errors: SHAMPOO_E_STATE (not bound, a part in flight, another device
+ * current), SHAMPOO_E_UNSUPPORTED (a chain slot larger than the array: not
+ * for factors up to 1024), SHAMPOO_E_HIP. */
+int shampoo_compute_inverse_roots_noalloc(shampoo_t* h, void* stream);
+
 /* The same part computed in the background (cues 14-16: the roots are
  * produced off the critical path while training continues on the last ones,
  * and swapped in when ready).  shampoo_roots_async_begin enqueues on `stream`

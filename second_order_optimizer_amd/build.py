@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libshampoo_mi355x.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.cpp", "kernels.hip", "peaks.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.cpp", "kernels.hip", "peaks.hip", "noalloc.hip")]
 HEADERS = [os.path.join(HERE, "csrc", f) for f in ("common.hpp", "kernels.hpp")] + [
     os.path.join(ROOT, "include", "shampoo.h")]
 

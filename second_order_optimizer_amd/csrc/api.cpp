@@ -16,6 +16,8 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -187,6 +189,12 @@ struct shampoo_s {
     // root-pass tables: [0] every factor; [1 + q] part q of a staggered pass
     // (factors of the blocks b with b % root_parts == q)
     std::vector<RootTables> roots;
+    // the allocation-free pass: every factor, batched-chain iterates in the
+    // static device scratch (pointer-table entry 1 + 2n) in chunks that fit it
+    RootTables roots_na;
+    bool noalloc_ok = false;          // every chain slot fits the static scratch
+    void* na_ptr = nullptr;           // this device's static scratch (set at bind)
+    int device = -1;                  // the device current at bind
     // the asynchronous pass: per part, root tables on the snapshot/staging
     // areas and the copy jobs around them; a side stream and its events
     std::vector<RootTables> async_roots;
@@ -353,9 +361,13 @@ int newton_iters_for(const shampoo_config& c, int p) {
 // Builds the per-parity GEMM launches of one Newton chunk.
 // gids: the gating id of each factor's products (default: the factor id).
 // split_off_bytes: the partial-product scratch of split stages.
+// base_idx: pointer-table entry the products' offsets are relative to (0:
+// the state buffer; the allocation-free pass: its static scratch).
+// allow_split: stages with few tiles may be split over k.
 void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& fids, int ld,
                         bool fp64, bool fused, int64_t scratch_off_bytes, int p,
-                        int64_t split_off_bytes, const std::vector<int>* gids = nullptr) {
+                        int64_t split_off_bytes, const std::vector<int>* gids = nullptr,
+                        int base_idx = 0, bool allow_split = true) {
     ch.p = p;
     ch.iters = newton_iters_for(h->cfg, p);
     const int64_t esz = fp64 ? 8 : 4;
@@ -385,7 +397,7 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
     auto mk = [&](int64_t a, int64_t b, int64_t c, int trans, int fid) {
         GemmTask t{};
         t.a_off = sbase + a; t.b_off = sbase + b; t.c_off = sbase + c;
-        t.a_base = t.b_base = t.c_base = 0;
+        t.a_base = t.b_base = t.c_base = base_idx;
         t.M = t.N = t.K = ld;
         t.lda = t.ldb = t.ldc = ld;
         t.trans = trans;
@@ -424,7 +436,7 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
         const int ut = tiles1 * (tiles1 + 1) / 2;
         for (auto& tasks : st) {
             NewtonStage ns;
-            const int parts = newton_split((int)tasks.size() * ut, ld);
+            const int parts = allow_split ? newton_split((int)tasks.size() * ut, ld) : 1;
             if (parts == 1) {
                 ns.gemm = add_launch(h->blob, tasks);
             } else {
@@ -586,7 +598,9 @@ int build_plan(shampoo_s* h) {
     const int nb = (int)h->blocks.size();
 
     // arena: per-call tables, diagnostics, factor matrices
-    h->off_bases = take((1 + 2 * (int64_t)h->n) * 8);
+    // pointer table: the state buffer, n gradients, n weights, the static
+    // scratch of the allocation-free root pass
+    h->off_bases = take((2 + 2 * (int64_t)h->n) * 8);
     h->off_sparse = take((int64_t)std::max(h->n_sparse, 1) * sizeof(SparseJob));
     h->off_diag = take((int64_t)std::max(nf, 1) * sizeof(FactorDiag));
     h->off_prec = take((int64_t)std::max(nf, 1) * 4);
@@ -684,6 +698,7 @@ int build_plan(shampoo_s* h) {
         bool compact = false; int cap = 0; int slot_first = 0;
     };
     int n_slots = 0;
+    std::map<std::pair<int, int>, int> na_slot_first;   // (ld, p) -> first slot, every factor
     int64_t split32 = 0, split64 = 0;
     int64_t scratch_budget = (int64_t)kNewtonScratchBudget;
     if (const char* e = std::getenv("SHAMPOO_NEWTON_SCRATCH_BYTES")) {
@@ -723,6 +738,7 @@ int build_plan(shampoo_s* h) {
                 pd.compact = true;
                 pd.cap = cap;
                 pd.slot_first = n_slots;
+                if (set == 0) na_slot_first[{ld, pe}] = n_slots;
                 n_slots += (int)fids.size();
                 const int n = (int)fids.size();
                 scr64 = std::max(scr64, per * (int64_t)std::min(n, cap));
@@ -1137,6 +1153,71 @@ int build_plan(shampoo_s* h) {
     h->slot_tmpl_off = blob.add(slot_tmpl);
     for (auto& rt : h->roots) rt.compact_off = blob.add(rt.compact);
     for (auto& rt : h->async_roots) rt.compact_off = blob.add(rt.compact);
+    // The allocation-free pass over every factor: the same Lanczos tables,
+    // fused roots and packed-slot arrangement as the whole pass, its
+    // batched-chain iterates in the static device scratch in chunks that fit
+    // it, and no split stages (their partials would need more scratch).  The
+    // fp32 chain, then the fp64 one, run in stream order, so both start at
+    // the scratch's beginning; nothing in it needs clearing first (the start
+    // writes every iterate a product reads, and products skip unrouted slots).
+    {
+        RootTables& na = h->roots_na;
+        const RootTables& r0 = h->roots[0];
+        na.lanczos_s_small_off = r0.lanczos_s_small_off;
+        na.lanczos_p_small_off = r0.lanczos_p_small_off;
+        na.lanczos_s_big_off = r0.lanczos_s_big_off;
+        na.lanczos_p_big_off = r0.lanczos_p_big_off;
+        na.n_lanczos_small = r0.n_lanczos_small;
+        na.n_lanczos_big = r0.n_lanczos_big;
+        h->noalloc_ok = true;
+        const int na_base = 1 + 2 * h->n;
+        for (auto [ld, pe] : lds) {
+            std::vector<int> fids;
+            for (int i = 0; i < nf; ++i)
+                if (h->factors[i].ld == ld && h->factors[i].p == pe) fids.push_back(i);
+            if (fids.empty()) continue;
+            for (int prec = 0; prec < 2; ++prec) {
+                const bool fp64 = prec == 1;
+                if ((fp64 && !use_fp64(c)) || (!fp64 && !use_fp32(c))) continue;
+                if (!fp64 && ld <= 128) {
+                    NewtonChunk ch;
+                    build_newton_chunk(h, ch, fids, ld, false, true, 0, pe, 0);
+                    na.chunks32.push_back(std::move(ch));
+                    continue;
+                }
+                const int64_t per = 6 * (int64_t)ld * ld * (fp64 ? 8 : 4);
+                if (per > (int64_t)kNoallocScratchBytes) {
+                    h->noalloc_ok = false;
+                    continue;
+                }
+                const int cap = (int)((int64_t)kNoallocScratchBytes / per);
+                const int n = (int)fids.size();
+                if (fp64 && c.root_mode == SHAMPOO_ROOT_AUTO) {
+                    const int first = na_slot_first.at({ld, pe});
+                    na.compact.push_back(CompactClass{first, n, cap, 0, (int64_t)ld * ld});
+                    for (int q0 = 0; q0 < n; q0 += cap) {
+                        const int m = std::min(cap, n - q0);
+                        std::vector<int> sub(fids.begin() + q0, fids.begin() + q0 + m), gids(m);
+                        for (int k = 0; k < m; ++k) gids[k] = first + q0 + k;
+                        NewtonChunk ch;
+                        build_newton_chunk(h, ch, sub, ld, true, false, 0, pe, 0, &gids, na_base,
+                                           false);
+                        ch.compact = true;
+                        ch.slot_jobs_off = h->off_slot_jobs + (int64_t)(first + q0) * sizeof(FactorJob);
+                        na.chunks64.push_back(std::move(ch));
+                    }
+                    continue;
+                }
+                for (int q0 = 0; q0 < n; q0 += cap) {
+                    std::vector<int> sub(fids.begin() + q0, fids.begin() + std::min(n, q0 + cap));
+                    NewtonChunk ch;
+                    build_newton_chunk(h, ch, sub, ld, fp64, false, 0, pe, 0, nullptr, na_base, false);
+                    (fp64 ? na.chunks64 : na.chunks32).push_back(std::move(ch));
+                }
+            }
+        }
+        na.compact_off = blob.add(na.compact);
+    }
     // copy jobs of the asynchronous pass: snapshot S and P of a part, and the
     // swap of its staged roots
     h->async_begin_off.assign(nparts, 0);
@@ -1290,8 +1371,9 @@ int stage_upload(shampoo_s* h, const void* src, size_t bytes, int64_t dst_off, h
 int refresh_bases(shampoo_s* h, const float* const* grads, float* const* params,
                   const shampoo_sparse_rows* sparse, hipStream_t s) {
     std::vector<uint64_t> nb = h->bases_host;
-    if (nb.empty()) nb.assign(1 + 2 * (size_t)h->n, 0);
+    if (nb.empty()) nb.assign(2 + 2 * (size_t)h->n, 0);
     nb[0] = reinterpret_cast<uint64_t>(h->arena);
+    nb[1 + 2 * h->n] = reinterpret_cast<uint64_t>(h->na_ptr);   // the static scratch
     for (int t = 0; t < h->n; ++t) {
         if (grads) nb[1 + t] = reinterpret_cast<uint64_t>(grads[t]);
         if (params) nb[1 + h->n + t] = reinterpret_cast<uint64_t>(params[t]);
@@ -1434,7 +1516,7 @@ int shampoo_bind_state(shampoo_t* h, void* dev_state, size_t bytes, void* stream
     h->bases_host.clear();
     if (!h->ring) {
         h->slot_bytes = (size_t)align_up(
-            std::max<int64_t>({(1 + 2 * (int64_t)h->n) * 8,
+            std::max<int64_t>({(2 + 2 * (int64_t)h->n) * 8,
                                (int64_t)std::max(h->n_sparse, 1) * (int64_t)sizeof(SparseJob),
                                h->sos.empty() ? 0 : (int64_t)64 << 10}),
             256);
@@ -1459,6 +1541,9 @@ int shampoo_bind_state(shampoo_t* h, void* dev_state, size_t bytes, void* stream
             return SHAMPOO_E_HIP;
     }
     h->async_part = -1;
+    // set-up of the allocation-free root pass: this device's static scratch
+    if (hipGetDevice(&h->device) != hipSuccess) return SHAMPOO_E_HIP;
+    if (noalloc_scratch_ptr(&h->na_ptr) != hipSuccess) return SHAMPOO_E_HIP;
     int rc = hip_err(hipMemsetAsync(h->arena, 0, h->off_tables, s));
     if (rc) return rc;
     rc = hip_err(hipMemcpyAsync(h->arena + h->off_tables, h->blob.bytes.data(), h->blob.bytes.size(),
@@ -1607,8 +1692,9 @@ int shampoo_update_stats(shampoo_t* h, const float* const* grads,
 }
 
 namespace {
+// scr: the chain's iterate scratch, or null for the state buffer's own.
 int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const int32_t* gate,
-               int gate_val, int32_t* prec, hipStream_t s) {
+               int gate_val, int32_t* prec, hipStream_t s, unsigned char* scr = nullptr) {
     NewtonArgs na{};
     na.is_fp64 = fp64 ? 1 : 0;
     na.gate = gate;
@@ -1622,7 +1708,7 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
         na.cnt = na.conv + std::max((int)h->factors.size(), 1);
         na.part = at<double>(h, h->off_convp);
     }
-    void* scratch = h->arena + (fp64 ? h->off_scr64 : h->off_scr32);
+    void* scratch = scr ? scr : h->arena + (fp64 ? h->off_scr64 : h->off_scr32);
     FactorDiag* diag = at<FactorDiag>(h, h->off_diag);
     GemmArgs g{};
     g.epi = EPI_STORE;
@@ -1728,7 +1814,7 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
 namespace {
 // One root pass over the factors of rt (every factor, or one part of a
 // staggered pass).
-int enqueue_roots(shampoo_s* h, RootTables& rt, hipStream_t s) {
+int enqueue_roots(shampoo_s* h, RootTables& rt, hipStream_t s, unsigned char* scr = nullptr) {
     const int nf = (int)h->factors.size();
     if (nf == 0) return SHAMPOO_OK;
     const shampoo_config& c = h->cfg;
@@ -1767,7 +1853,7 @@ int enqueue_roots(shampoo_s* h, RootTables& rt, hipStream_t s) {
         // Lanczos on S, batched fp32 Newton, Lanczos on the root
         rc = lanczos(rt.lanczos_s_small_off, rt.lanczos_s_big_off, true, false, la);
         if (rc) return rc;
-        rc = run_newton(h, rt.chunks32, false, nullptr, 0, prec, s);
+        rc = run_newton(h, rt.chunks32, false, nullptr, 0, prec, s, scr);
         if (rc) return rc;
         lp.auto_route = c.root_mode == SHAMPOO_ROOT_AUTO ? 1 : 0;
         rc = lanczos(rt.lanczos_p_small_off, rt.lanczos_p_big_off, false, false, lp);
@@ -1782,7 +1868,7 @@ int enqueue_roots(shampoo_s* h, RootTables& rt, hipStream_t s) {
                                                   at<int32_t>(h, h->off_slot_live), s));
             }
             if (rc) return rc;
-            rc = run_newton(h, rt.chunks64, true, prec, 1, prec, s);
+            rc = run_newton(h, rt.chunks64, true, prec, 1, prec, s, scr);
         }
         return rc;
     }
@@ -1798,7 +1884,7 @@ int enqueue_roots(shampoo_s* h, RootTables& rt, hipStream_t s) {
                                         h->arena, true, true, la, s));
     }
     if (rc) return rc;
-    rc = run_newton(h, rt.chunks64, true, nullptr, 1, prec, s);
+    rc = run_newton(h, rt.chunks64, true, nullptr, 1, prec, s, scr);
     if (rc) return rc;
     lp.auto_route = 0;
     return lanczos(rt.lanczos_p_small_off, rt.lanczos_p_big_off, false, true, lp);
@@ -1811,6 +1897,22 @@ int shampoo_compute_inverse_roots(shampoo_t* h, void* stream) {
     if (!h) return SHAMPOO_E_ARG;
     if (!h->bound || h->async_part >= 0) return SHAMPOO_E_STATE;
     return enqueue_roots(h, h->roots[0], static_cast<hipStream_t>(stream));
+}
+
+int shampoo_compute_inverse_roots_noalloc(shampoo_t* h, void* stream) {
+    if (!h) return SHAMPOO_E_ARG;
+    if (!h->bound || h->async_part >= 0 || !h->na_ptr) return SHAMPOO_E_STATE;
+    if (!h->noalloc_ok) return SHAMPOO_E_UNSUPPORTED;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return SHAMPOO_E_HIP;
+    if (dev != h->device) return SHAMPOO_E_STATE;
+    // no timing events here (creating one may allocate)
+    const bool prof = h->prof_on;
+    h->prof_on = false;
+    const int rc = enqueue_roots(h, h->roots_na, static_cast<hipStream_t>(stream),
+                                 static_cast<unsigned char*>(h->na_ptr));
+    h->prof_on = prof;
+    return rc;
 }
 
 int shampoo_compute_inverse_roots_part(shampoo_t* h, int32_t part, void* stream) {

@@ -88,6 +88,14 @@ struct UpdateArgs {
     float beta1, lr, delta;
 };
 
+// Static device scratch of the allocation-free root pass
+// (shampoo_compute_inverse_roots_noalloc): the batched coupled-Newton iterates,
+// six ld x ld matrices per factor slot; one fp64 slot of the largest factor
+// (ld 1024) takes 48 MiB.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+// Its address on the current device (asked of the runtime once per device).
+hipError_t noalloc_scratch_ptr(void** out);
+
 // role: 0 Newton products, 1 / 2 the first / second product of the apply
 // (the same kernel; the role only names the instantiation for profilers)
 hipError_t launch_gemm_f32(const GemmTask* tasks, const TileRef* tiles, int ntiles,

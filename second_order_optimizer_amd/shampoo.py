@@ -82,6 +82,7 @@ SIGNATURES = {
     "shampoo_update_stats": (ctypes.c_int, [_P, ctypes.POINTER(_P), ctypes.POINTER(SparseRows), _P]),
     "shampoo_compute_inverse_roots": (ctypes.c_int, [_P, _P]),
     "shampoo_compute_inverse_roots_part": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
+    "shampoo_compute_inverse_roots_noalloc": (ctypes.c_int, [_P, _P]),
     "shampoo_roots_async_begin": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
     "shampoo_roots_async_end": (ctypes.c_int, [_P, _P]),
     "shampoo_precondition_and_apply": (ctypes.c_int, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P),
@@ -266,6 +267,12 @@ class Shampoo(Plan):
     def compute_inverse_roots(self):
         _check(lib().shampoo_compute_inverse_roots(self.h, self._stream()),
                "shampoo_compute_inverse_roots")
+
+    def compute_inverse_roots_noalloc(self):
+        """The same root pass with the Newton iterates in the library's static
+        device scratch (shampoo_compute_inverse_roots_noalloc)."""
+        _check(lib().shampoo_compute_inverse_roots_noalloc(self.h, self._stream()),
+               "shampoo_compute_inverse_roots_noalloc")
 
     def compute_inverse_roots_part(self, part: int):
         _check(lib().shampoo_compute_inverse_roots_part(self.h, part, self._stream()),

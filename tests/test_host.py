@@ -70,6 +70,8 @@ def test_strerror_and_argument_errors():
     arr = (S._P * 1)()
     assert L.shampoo_update_stats(p.h, arr, None, None) == -2
     assert L.shampoo_compute_inverse_roots(p.h, None) == -2
+    assert L.shampoo_compute_inverse_roots_noalloc(p.h, None) == -2
+    assert L.shampoo_compute_inverse_roots_noalloc(None, None) == -1
     assert L.shampoo_step(p.h, arr, arr, None, S.ROOTS_NONE, None) == -2
     assert L.shampoo_step(p.h, None, arr, None, S.ROOTS_ALL, None) == -1
     # a part index needs a plan with root_parts >= 2
