@@ -67,7 +67,7 @@ UNIT = "optimizer steps/s x (params / 1e8)"
 
 # MI355X published peaks (dense)
 PEAK_HBM_GBS = 8000.0
-PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6}
+PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6, "bf16": 2500.0}
 
 KERNEL_SOURCES = [os.path.join(HERE, "second_order_optimizer_amd", "csrc", f)
                   for f in ("kernels.hip", "api.cpp", "common.hpp", "kernels.hpp")]
@@ -171,6 +171,13 @@ def work_model(wl, opt):
         "apply_small_bytes": apply_small_bytes, "unfused_params": unfused_params,
         "apply_t_big": sum(2.0 * b.rows * b.cols ** 2 for b in big),
         "apply_d_big": sum(2.0 * b.rows ** 2 * b.cols for b in big) + os_apply(dense_os),
+        # split-precision apply: the first product reads P_R and G and takes
+        # G through the Adagrad accumulator (a read and written) and writes
+        # T^T; the second reads P_L and T^T and writes D
+        "apply_t_bytes": sum(16.0 * b.rows * b.cols + 4.0 * b.ld_r ** 2 for b in big),
+        "apply_d_bytes": sum(8.0 * b.rows * b.cols + 4.0 * b.ld_l ** 2 for b in big) +
+        sum(8.0 * b.rows * b.cols + 4.0 * (b.ld_r if b.factor_r >= 0 else b.ld_l) ** 2
+            for b in dense_os),
         "stats_onesided": os_stats(dense_os),
         "stats_onesided_rows": os_stats(sparse_os), "apply_onesided_rows": os_apply(sparse_os),
         "onesided_rows_elems": sum(listed_rows(b) * b.cols for b in sparse_os),
@@ -321,7 +328,8 @@ def run_pass(wl, args, tol, pool, dev, peaks):
                         newton_iters=wl.newton_iters, root_mode=wl.root_mode, beta1=wl.beta1,
                         beta2=wl.beta2, lr=wl.lr, eps_rel=wl.eps_rel, graft_eps=wl.graft_eps,
                         fp64_cond_threshold=wl.fp64_cond_threshold, root_parts=args.root_parts,
-                        newton_tol=tol, large_layer=1 if args.large_layer else 0)
+                        newton_tol=tol, large_layer=1 if args.large_layer else 0,
+                        apply_precision=wl.apply_precision)
     shapes = [(t.rows, t.cols, 0 if t.kind == "dense" else 1) for t in wl.tensors]
     opt = S.Shampoo(shapes, cfg, device=dev, async_roots=args.async_roots)
     params = [torch.from_numpy(synth.initial_weight(wl, i)).to(dev) for i in range(len(shapes))]
@@ -424,6 +432,16 @@ def run_pass(wl, args, tol, pool, dev, peaks):
         # g read, a and W read and written, row ids
         "sparse_rows": (wm["sparse_elems"] * 20.0, "GB/s", "hbm", PEAK_HBM_GBS),
     }
+    if wl.apply_precision == "bf16x3":
+        # three bf16 products per fp32 product on the bf16 matrix cores; each
+        # launch is bounded by whichever of that floor and its HBM floor
+        # (bytes above) is higher
+        for name, fk, bk in (("apply_gemm_t", "apply_t_big", "apply_t_bytes"),
+                             ("apply_gemm_d", "apply_d_big", "apply_d_bytes")):
+            t_m = 3.0 * wm[fk] / (PEAK_TFLOPS["bf16"] * 1e12)
+            t_h = wm[bk] / (PEAK_HBM_GBS * 1e9)
+            alg[name] = ((3.0 * wm[fk], "TFLOP/s", "mfma", PEAK_TFLOPS["bf16"]) if t_m >= t_h
+                         else (wm[bk], "GB/s", "hbm", PEAK_HBM_GBS))
     # the fused apply is bounded by whichever of its MFMA and HBM floors is higher
     if wm["apply_small"] / (PEAK_TFLOPS["f32"] * 1e12) >= wm["apply_small_bytes"] / (PEAK_HBM_GBS * 1e9):
         alg["apply_fused"] = (wm["apply_small"], "TFLOP/s", "mfma", PEAK_TFLOPS["f32"])
@@ -478,6 +496,7 @@ def run_pass(wl, args, tol, pool, dev, peaks):
             if peaks:
                 mp = (peaks["copy_gbs"] if unit == "GB/s" else
                       peaks["mfma_f64_tflops"] if peak == PEAK_TFLOPS["f64"] else
+                      peaks["mfma_bf16_tflops"] if peak == PEAK_TFLOPS["bf16"] else
                       peaks["mfma_f32_tflops"])
                 rec["frac_of_measured_peak"] = ach / mp
         stages[name] = rec
@@ -544,6 +563,8 @@ def main():
                     help="0: 256x512 b128, 1: Transformer-base b128, 2: BERT-large b512 "
                          "(default), 3: ResNet-50 b256, 4: CTR MLP b1024 + sparse tables")
     ap.add_argument("--root-mode", default=None, choices=["f32", "f64", "auto"])
+    ap.add_argument("--apply-precision", default=None, choices=["fp32", "bf16x3"],
+                    help="products of the apply for blocks above 128 (default: the workload's)")
     ap.add_argument("--newton-tol", type=float, default=None,
                     help="fp32-root convergence tolerance (0: the full iteration count)")
     ap.add_argument("--no-full-count", action="store_true",
@@ -595,6 +616,8 @@ def main():
         wl.newton_tol = args.newton_tol
     if args.root_mode:
         wl.root_mode = args.root_mode
+    if args.apply_precision:
+        wl.apply_precision = args.apply_precision
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     t0 = time.time()
@@ -641,7 +664,7 @@ def main():
         "config": {"workload": wl.name, "params": wl.n_params, "blocks": main_pass["n_blocks"],
                    "block_size": wl.block_size, "root_cadence": wl.cadence,
                    "newton_iters": wl.newton_iters, "newton_tol": wl.newton_tol,
-                   "root_mode": wl.root_mode,
+                   "root_mode": wl.root_mode, "apply_precision": wl.apply_precision,
                    "root_parts": args.root_parts, "async_roots": bool(args.async_roots),
                    "large_layer": bool(args.large_layer),
                    "max_precond_dim": wl.max_precond_dim, "parallelism": "single-gpu"},
@@ -657,7 +680,8 @@ def main():
         "step_ms": main_pass["step_ms"],
         "peaks_measured": peaks,
         "peaks_published": {"mfma_f32_tflops": PEAK_TFLOPS["f32"],
-                            "mfma_f64_tflops": PEAK_TFLOPS["f64"], "hbm_gbs": PEAK_HBM_GBS},
+                            "mfma_f64_tflops": PEAK_TFLOPS["f64"],
+                            "mfma_bf16_tflops": PEAK_TFLOPS["bf16"], "hbm_gbs": PEAK_HBM_GBS},
     }
     if full is not None:
         out["full_iteration_count"] = {
@@ -687,7 +711,7 @@ def _csv_rows(pattern):
 
 def _short(name):
     """Kernel name without its argument list and return type."""
-    name = name.replace("(anonymous namespace)::", "")
+    name = name.replace("(anonymous namespace)::", "").replace("shampoo::", "")
     if name.startswith("void "):
         name = name[5:]
     depth = 0
@@ -725,6 +749,8 @@ FAMILY_OF = [
     ("k_gemm<double, float, float, 2, true, false", "stats_gram_f64", "f64"),
     ("k_gemm<float, float, float, 1, false, false, 1>", "apply_gemm_t", "f32"),
     ("k_gemm<float, float, float, 1, false, false, 2>", "apply_gemm_d", "f32"),
+    ("k_gemm_nt3<true>", "apply_gemm_t", "bf16"),
+    ("k_gemm_nt3<false>", "apply_gemm_d", "bf16"),
     ("k_gemm<float, float, float, 1, false, false, 0>", "newton_gemm_f32", "f32"),
     ("k_gemm<float, float, float, 1, false, false>", "newton_gemm_f32", "f32"),
     ("k_gemm<double, double, double, 2", "newton_gemm_f64", "f64"),
@@ -806,7 +832,8 @@ def counters_summary(d, wl, trace_dir, title, command):
         fb = fetch[k].get("FETCH_SIZE", 0.0) * 1024.0 * fs
         wb = write.get(k, {}).get("WRITE_SIZE", 0.0) * 1024.0 * ws
         c = sq.get(k, {})
-        mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_F64", 0.0)
+        mops = (c.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_F64", 0.0) +
+                c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0))
         exe = mops * 512.0
         busy = None
         if c.get("GRBM_GUI_ACTIVE"):

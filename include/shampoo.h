@@ -87,8 +87,11 @@ typedef struct {
                                  (p = 2: 23, p = 1: 26 for 20), the steps that close the
                                  same eigenvalue gap                                     */
     int32_t root_mode;        /* shampoo_root_mode                                       */
-    int32_t lanczos_steps;    /* Krylov steps for lambda_max; 0 = 20 for factors up to
-                                 128 and 24 above; the kappa estimate uses min(8, this)  */
+    int32_t lanczos_steps;    /* Krylov steps for lambda_max; 0 = adaptive: stop at the
+                                 first check (after 8 steps, then every 4th) where the
+                                 top Ritz pair's residual is within 5e-5 of theta, at
+                                 most 64 steps; the kappa estimate uses min(8, this), 8
+                                 when 0                                                  */
     int32_t root_parts;       /* staggered root pass (cue 14-16: roots are computed off
                                  the critical path and swapped in): 0 or 1 = one pass
                                  over every factor; P >= 2 also plans P parts, part q
@@ -104,6 +107,17 @@ typedef struct {
                                  With 1, sparse-row tables whose columns fit (any, when
                                  max_precond_dim is 0) get the column side instead of
                                  sparse-row Adagrad                                      */
+    int32_t apply_precision;  /* the two products of D = P_L G P_R for blocks above 128
+                                 (and D = G P_R of a one-sided column side): 0 = fp32
+                                 matrix cores; 1 = split precision (bf16x3): each fp32
+                                 operand x split into hi = bf16(x), lo = bf16(x - hi),
+                                 the product formed as hi*hi + hi*lo + lo*hi on the bf16
+                                 matrix cores with fp32 accumulation (about 2^-16
+                                 relative per term instead of 2^-24), the Adagrad pass
+                                 of those blocks fused into the first product; needs
+                                 root_p >= 4 (the roots' condition kappa^(1/p) amplifies
+                                 the rounding, p = 1 at kappa 1e6: ~1e-2 of the update)  */
+    int32_t reserved;         /* must be 0                                                */
     double beta1;             /* momentum: mom <- beta1 mom + U                          */
     double beta2;             /* statistics: S <- beta2 S + (1-beta2) outer(G) (beta2<1),
                                  S <- S + outer(G) when beta2 == 1; 1 - beta2 is formed in
@@ -184,8 +198,9 @@ typedef struct {
  * block (tensors in order), with one factor for the side that fits (R for a
  * table).  Errors: SHAMPOO_E_ARG (null pointer, n_tensors < 1, a dimension
  * < 1, block_size < 1, newton_iters < 1, beta2 outside (0,1], eps_rel < 0,
- * unknown kind or root_mode, large_layer not 0 or 1), SHAMPOO_E_UNSUPPORTED
- * (root_p not in {1,2,4,8}; root_p odd with large_layer = 1; a factor
+ * unknown kind or root_mode, large_layer or apply_precision not 0 or 1,
+ * reserved not 0), SHAMPOO_E_UNSUPPORTED (root_p not in {1,2,4,8}; root_p odd
+ * with large_layer = 1; apply_precision 1 with root_p < 4; a factor
  * dimension above 1024; rows above 2^31 - 1 or cols above 2^20),
  * SHAMPOO_E_NOMEM.
  * Scratch: the batched coupled-Newton iteration (fp32 factors above 128 and
@@ -364,8 +379,9 @@ int shampoo_profile_read(shampoo_t* h, shampoo_kernel_time* out, int32_t cap, in
 
 /* Machine peaks measured on the current device, for measurement tools that
  * report kernel rates as fractions of a peak.  None of the method's
- * arithmetic: the matrix-core issue rate of the two MFMA instructions the
- * products use (fp32 v_mfma_f32_32x32x2f32, fp64 v_mfma_f64_16x16x4f64),
+ * arithmetic: the matrix-core issue rate of the MFMA instructions the
+ * products use (fp32 v_mfma_f32_32x32x2f32, fp64 v_mfma_f64_16x16x4f64, bf16
+ * v_mfma_f32_32x32x16_bf16),
  * every wave of a full grid issuing independent products from registers
  * with no memory traffic, and a plain device-to-device copy (bytes read plus
  * bytes written, per second).  Each is the median of three timed launches
@@ -373,6 +389,7 @@ int shampoo_profile_read(shampoo_t* h, shampoo_kernel_time* out, int32_t cap, in
 typedef struct {
     double mfma_f32_tflops;  /* TFLOP/s, 2 flops per multiply-add                  */
     double mfma_f64_tflops;
+    double mfma_bf16_tflops; /* v_mfma_f32_32x32x16_bf16 (fp32 accumulation)         */
     double copy_gbs;         /* GB/s (1e9 bytes), read + write                       */
     int64_t copy_bytes;      /* bytes read by one copy (half the scratch, rounded)  */
 } shampoo_peaks;

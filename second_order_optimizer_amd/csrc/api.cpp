@@ -172,6 +172,9 @@ struct shampoo_s {
     Blob blob;  // static tables (offsets relative to off_tables)
 
     LaunchRef gram, apply1, apply2;   // blocks with a side > 128
+    // the same products in split precision (apply_precision 1): T^T = P_R G^T
+    // with the Adagrad pass of G fused in, then D = P_L T
+    LaunchRef nt1, nt2;
     LaunchRef splitk;                 // one-sided statistics: partial products
     LaunchRef gsplit;                 // blocks > 128 when few: statistics split over k
     int64_t gred_jobs_off = 0, gred_tiles_off = 0;
@@ -317,6 +320,24 @@ LaunchRef add_launch_sorted(Blob& blob, const std::vector<GemmTask>& tasks) {
 
 LaunchRef add_launch(Blob& blob, const std::vector<GemmTask>& tasks) {
     const std::vector<TileRef> tiles = xcd_tile_order(tasks);
+    LaunchRef L;
+    L.tasks_off = blob.add(tasks);
+    L.tiles_off = blob.add(tiles);
+    L.ntiles = (int)tiles.size();
+    return L;
+}
+
+// A launch of the split-precision C = A B^T kernel: its tiles in the same
+// XCD-aware order as a batched-GEMM launch of the same shapes.
+LaunchRef add_launch_nt(Blob& blob, const std::vector<NtTask>& tasks) {
+    std::vector<GemmTask> shape(tasks.size());
+    for (size_t i = 0; i < tasks.size(); ++i) {
+        shape[i].M = tasks[i].M;
+        shape[i].N = tasks[i].N;
+        shape[i].K = tasks[i].K;
+        shape[i].tiles_n = tasks[i].tiles_n;
+    }
+    const std::vector<TileRef> tiles = xcd_tile_order(shape);
     LaunchRef L;
     L.tasks_off = blob.add(tasks);
     L.tiles_off = blob.add(tiles);
@@ -672,10 +693,15 @@ int build_plan(shampoo_s* h) {
 
     // norm partial slots
     int na = 0, nd = 0;
+    const bool split_apply = c.apply_precision == 1;
     for (auto& bp : h->blocks) {
         const int rows_per = (int)std::max<int64_t>(1, kElemChunk / bp.nb);
         bp.a_slot = na;
-        bp.a_chunks = bp.small ? 1 : ceil_div(bp.mb, rows_per);
+        // split-precision apply: the first product's tiles of row 0 take the
+        // Adagrad pass of the block, one partial per 128 rows of G
+        bp.a_chunks = bp.small ? 1
+                      : (split_apply && !bp.one_sided) ? ceil_div(bp.mb, kTile)
+                                                        : ceil_div(bp.mb, rows_per);
         na += bp.a_chunks;
         bp.d_slot = nd;
         bp.d_tiles = bp.small ? 1 : ceil_div(bp.mb, kTile) * ceil_div(bp.nb, kTile);
@@ -965,6 +991,7 @@ int build_plan(shampoo_s* h) {
     // apply: T = G_b P_R, then D = P_L T with ||D||^2 partials (cue 10)
     {
         std::vector<GemmTask> t1, t2;
+        std::vector<NtTask> n1, n2;
         std::vector<ApplyJob> small;
         std::vector<StepJob> steps;
         for (auto& bp : h->blocks) {
@@ -972,6 +999,19 @@ int build_plan(shampoo_s* h) {
             const FactorPlan& fl = h->factors[bp.fl];
             const FactorPlan& fr = h->factors[bp.fr];
             if (bp.one_sided && tp.mode == 2) continue;   // sparse rows: per call
+            if (bp.one_sided && split_apply && fl.side == 1) {
+                // D = G P in split precision: C = A B^T with B = P (symmetric)
+                NtTask u{};
+                u.a_base = 1 + bp.tensor; u.a_off = 0; u.lda = (int)tp.cols;
+                u.b_base = 0; u.b_off = fl.off_p / 4; u.ldb = fl.ld;
+                u.c_base = 0; u.c_off = tp.off_d / 4; u.ldc = (int)tp.cols;
+                u.M = bp.mb; u.N = bp.nb; u.K = bp.nb;
+                u.tiles_n = ceil_div(u.N, kTile);
+                u.norm_slot = bp.d_slot;
+                u.acc_off = -1;
+                n2.push_back(u);
+                continue;
+            }
             if (bp.one_sided) {
                 // D = G P (R) or P G (L), with ||D||^2 partials per tile
                 GemmTask u{};
@@ -1020,6 +1060,34 @@ int build_plan(shampoo_s* h) {
                 steps.push_back(sj);
                 continue;
             }
+            if (split_apply) {
+                // T^T = P_R G_b^T (nb x mb, at off_t): C = A B^T with A = P_R
+                // and B = G_b, both k-contiguous; the tiles of row 0 also
+                // run the block's Adagrad pass.  Then D = P_L T: A = P_L and
+                // B = T^T, whose rows are T's columns.
+                NtTask t{};
+                t.a_base = 0; t.a_off = fr.off_p / 4; t.lda = fr.ld;
+                t.b_base = 1 + bp.tensor; t.b_off = (int64_t)bp.r0 * tp.cols + bp.c0;
+                t.ldb = (int)tp.cols;
+                t.c_base = 0; t.c_off = bp.off_t / 4; t.ldc = bp.mb;
+                t.M = bp.nb; t.N = bp.mb; t.K = bp.nb;
+                t.tiles_n = ceil_div(t.N, kTile);
+                t.norm_slot = -1;
+                t.acc_off = tp.off_a / 4 + (int64_t)bp.r0 * tp.cols + bp.c0;
+                t.acc_slot = bp.a_slot;
+                n1.push_back(t);
+                NtTask u{};
+                u.a_base = 0; u.a_off = fl.off_p / 4; u.lda = fl.ld;
+                u.b_base = 0; u.b_off = bp.off_t / 4; u.ldb = bp.mb;
+                u.c_base = 0; u.c_off = tp.off_d / 4 + (int64_t)bp.r0 * tp.cols + bp.c0;
+                u.ldc = (int)tp.cols;
+                u.M = bp.mb; u.N = bp.nb; u.K = bp.mb;
+                u.tiles_n = ceil_div(u.N, kTile);
+                u.norm_slot = bp.d_slot;
+                u.acc_off = -1;
+                n2.push_back(u);
+                continue;
+            }
             GemmTask t{};
             t.a_base = 1 + bp.tensor;
             t.a_off = (int64_t)bp.r0 * tp.cols + bp.c0;
@@ -1050,6 +1118,8 @@ int build_plan(shampoo_s* h) {
         }
         h->apply1 = add_launch(blob, t1);
         h->apply2 = add_launch(blob, t2);
+        h->nt1 = add_launch_nt(blob, n1);
+        h->nt2 = add_launch_nt(blob, n2);
         h->n_apply128 = (int)small.size();
         h->apply128_off = blob.add(small);
         h->step128_off = blob.add(steps);
@@ -1248,7 +1318,8 @@ int build_plan(shampoo_s* h) {
             const TensorPlan& tp = h->tensors[bp.tensor];
             const int rows_per = (int)std::max<int64_t>(1, kElemChunk / bp.nb);
             if (tp.mode == 2) continue;   // sparse one-sided table: norms per call
-            for (int k = 0; !bp.small && k < bp.a_chunks; ++k) {
+            const bool fused_adagrad = c.apply_precision == 1 && !bp.small && !bp.one_sided;
+            for (int k = 0; !bp.small && !fused_adagrad && k < bp.a_chunks; ++k) {
                 BlockChunk q{};
                 q.tensor = bp.tensor;
                 q.block = (int)i;
@@ -1409,6 +1480,12 @@ int shampoo_create(const shampoo_config* cfg, int32_t n_tensors, const shampoo_t
     if (c.root_p != 1 && c.root_p != 2 && c.root_p != 4 && c.root_p != 8)
         return SHAMPOO_E_UNSUPPORTED;
     if (c.large_layer != 0 && c.large_layer != 1) return SHAMPOO_E_ARG;
+    if (c.apply_precision != 0 && c.apply_precision != 1) return SHAMPOO_E_ARG;
+    // the split-precision apply multiplies by the roots, whose condition is
+    // kappa(S + eps I)^(1/p): for p < 4 its rounding is amplified past the
+    // fp32 apply's (p = 1 at kappa 1e6: about 1e-2 of the update)
+    if (c.apply_precision == 1 && c.root_p < 4) return SHAMPOO_E_UNSUPPORTED;
+    if (c.reserved != 0) return SHAMPOO_E_ARG;
     if (c.large_layer == 1 && c.root_p % 2) return SHAMPOO_E_UNSUPPORTED;  // exponent -2/root_p
     for (int t = 0; t < n_tensors; ++t) {
         const shampoo_tensor_desc& d = tensors[t];
@@ -2187,6 +2264,24 @@ int enqueue_apply(shampoo_s* h, float* const* params, const shampoo_sparse_rows*
                                      (float)c.graft_eps, partA, partD, ua, s));
     }
     if (rc) return rc;
+    if (h->nt1.ntiles > 0 || h->nt2.ntiles > 0) {
+        // split precision: T^T = P_R G^T (with the Adagrad pass), D = P_L T
+        NtArgs na{partD, partA, arena, (float)c.graft_eps};
+        {
+            ProfScope ps(h, PC_APPLY_T, s, h->nt1.ntiles > 0);
+            rc = hip_err(launch_gemm_nt3(tab<NtTask>(h, h->nt1.tasks_off),
+                                         tab<TileRef>(h, h->nt1.tiles_off), h->nt1.ntiles, bases,
+                                         na, true, s));
+        }
+        if (rc) return rc;
+        {
+            ProfScope ps(h, PC_APPLY_D, s, h->nt2.ntiles > 0);
+            rc = hip_err(launch_gemm_nt3(tab<NtTask>(h, h->nt2.tasks_off),
+                                         tab<TileRef>(h, h->nt2.tiles_off), h->nt2.ntiles, bases,
+                                         na, false, s));
+        }
+        if (rc) return rc;
+    }
     GemmArgs g{};
     g.epi = EPI_STORE;
     g.alpha = 1.0;

@@ -90,6 +90,24 @@ struct SplitSumJob {
     int32_t gate;       // gating id (-1: always run)
 };
 
+// One C = A B^T problem of the split-precision (bf16x3) GEMM kernel: A is
+// M x K and B is N x K, both row-major with k contiguous (fp32), C is M x N
+// fp32.  Used for the two products of the apply, D = P_L (P_R G^T)^T: the
+// first product's B is the gradient block, whose elements the kernel can
+// also take through the Adagrad accumulator on the way.
+struct NtTask {
+    int64_t a_off, b_off, c_off;  // element offsets from their bases
+    int32_t a_base, b_base, c_base;
+    int32_t M, N, K;
+    int32_t lda, ldb, ldc;
+    int32_t tiles_n;              // ceil(N / 128)
+    int32_t norm_slot;            // first slot of per-tile ||C||^2 partials, -1: none
+    int64_t acc_off;              // >= 0: Adagrad accumulator of B's elements (arena floats,
+                                  // leading dim ldb), updated by the tiles of row 0
+    int32_t acc_slot;             // first ||A||^2 partial slot (one per tile column)
+    int32_t pad_;
+};
+
 // A tile of the batched GEMM launch: which task and which 128x128 tile.
 struct TileRef {
     int32_t task;

@@ -491,6 +491,214 @@ __global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__
     }
 }
 
+// ================================== split-precision (bf16x3) products
+// C = A B^T with fp32 A (M x K) and B (N x K), both rows k-contiguous, on the
+// bf16 matrix cores (v_mfma_f32_32x32x16_bf16): every operand x is split
+// into hi = bf16(x) and lo = bf16(x - hi) as it is staged into LDS, and C
+// accumulates lo*hi + hi*lo + hi*hi in fp32.  The dropped lo*lo term and the
+// rounding of lo leave about 2^-16 of |a||b| per term (fp32 products: 2^-24),
+// well inside the apply's update bar; the products run at the bf16 rate.
+// 128 x 128 tiles, four waves of 64 x 64 (2 x 2 tiles of 32 x 32), BK = 32
+// per LDS stage with the next stage prefetched into registers.  The operand
+// of lane l in one instruction is row l % 32 and k in [8 (l / 32), +8) of
+// the 16-deep step, the same for A and B (any k order shared by both gives
+// the same sums; checked on the device), read as one 16-byte LDS load; the
+// row pitch of 40 bf16 (80 bytes) puts the rows of eight lanes on distinct
+// banks.  ADAG: the tiles of row 0 also take B's elements (a gradient block)
+// through the Adagrad accumulator a <- a + g^2 and sum (g / (sqrt(a) + delta))^2
+// for the graft, reading each element of B once per launch.
+constexpr int kNtBK = 32;
+constexpr int kNtP = kNtBK + 8;
+
+typedef __bf16 nt_bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 nt_bf16x4 __attribute__((ext_vector_type(4)));
+typedef float nt_acc_t __attribute__((ext_vector_type(16)));
+
+// Rows [r0, r0 + 128) x k [k0, k0 + 32) of a k-contiguous fp32 matrix into
+// registers: thread t takes rows r0 + t/8 + 32p (p < 4), k = k0 + 4 (t % 8) + e.
+// Out-of-range elements are zero.
+__device__ __forceinline__ void nt_load(const float* __restrict__ X, int ld, int r0, int R, int k0,
+                                        int K, bool aligned, float4 (&v)[4]) {
+    const int t = threadIdx.x, kq = t & 7, rr = t >> 3;
+    const int k = k0 + 4 * kq;
+    const bool kin = aligned && k0 + kNtBK <= K;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int r = r0 + rr + 32 * p;
+        if (kin && r < R) {
+            v[p] = *reinterpret_cast<const float4*>(X + (int64_t)r * ld + k);
+        } else {
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (r < R && k + e < K) ? X[(int64_t)r * ld + k + e] : 0.f;
+            v[p] = make_float4(x[0], x[1], x[2], x[3]);
+        }
+    }
+}
+
+// Splits the thread's 16 values into hi / lo bf16 and stores them at rows
+// t/8 + 32p, k 4 (t % 8) .. +3 of the stage.
+__device__ __forceinline__ void nt_store(const float4 (&v)[4], __bf16* H, __bf16* L) {
+    const int t = threadIdx.x, kq = t & 7, rr = t >> 3;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float x[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+        nt_bf16x4 h, l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[e] = (__bf16)x[e];
+            l[e] = (__bf16)(x[e] - (float)h[e]);
+        }
+        const int o = (rr + 32 * p) * kNtP + 4 * kq;
+        *reinterpret_cast<nt_bf16x4*>(H + o) = h;
+        *reinterpret_cast<nt_bf16x4*>(L + o) = l;
+    }
+}
+
+template <bool ADAG>
+__global__ __launch_bounds__(256, 2) void k_gemm_nt3(const NtTask* __restrict__ tasks,
+                                                    const TileRef* __restrict__ tiles,
+                                                    const uint64_t* __restrict__ bases, NtArgs args) {
+    __shared__ __align__(16) __bf16 Ah[BM * kNtP];
+    __shared__ __align__(16) __bf16 Al[BM * kNtP];
+    __shared__ __align__(16) __bf16 Bh[BN * kNtP];
+    __shared__ __align__(16) __bf16 Bl[BN * kNtP];
+    __shared__ double red[4];
+    const TileRef tr = tiles[blockIdx.x];
+    const NtTask tk = tasks[tr.task];
+    const int ti = tr.tile / tk.tiles_n, tj = tr.tile % tk.tiles_n;
+    const int i0 = ti * BM, j0 = tj * BN;
+    const float* A = base_ptr<const float>(bases, tk.a_base, tk.a_off);
+    const float* B = base_ptr<const float>(bases, tk.b_base, tk.b_off);
+    float* C = base_ptr<float>(bases, tk.c_base, tk.c_off);
+    const bool a_al = ((reinterpret_cast<uintptr_t>(A) & 15) == 0) && (tk.lda % 4 == 0);
+    const bool b_al = ((reinterpret_cast<uintptr_t>(B) & 15) == 0) && (tk.ldb % 4 == 0);
+    // the Adagrad pass over B's elements, by the tiles of row 0 (uniform)
+    const bool adag = ADAG && tk.acc_off >= 0 && ti == 0;
+    float* acc = args.arena + (adag ? tk.acc_off : 0);
+    const bool c_al = b_al && ((reinterpret_cast<uintptr_t>(acc) & 15) == 0);
+    const float delta = args.delta;
+    double asum = 0.0;
+
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int wm = w >> 1, wn = w & 1, h = lane >> 5, c = lane & 31;
+    nt_acc_t cc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) cc[i][j][v] = 0.f;
+
+    float4 av[4], bv[4], gv[4];
+    auto acc_load = [&](int k0) {
+        const int kq = t & 7, rr = t >> 3, k = k0 + 4 * kq;
+        const bool kin = c_al && k0 + kNtBK <= tk.K;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int r = j0 + rr + 32 * p;
+            if (kin && r < tk.N) {
+                gv[p] = *reinterpret_cast<const float4*>(acc + (int64_t)r * tk.ldb + k);
+            } else {
+                float x[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x[e] = (r < tk.N && k + e < tk.K) ? acc[(int64_t)r * tk.ldb + k + e] : 0.f;
+                gv[p] = make_float4(x[0], x[1], x[2], x[3]);
+            }
+        }
+    };
+    // a <- a + g^2 on the stage's elements of B, and their share of ||A||^2
+    auto acc_update = [&](int k0) {
+        const int kq = t & 7, rr = t >> 3, k = k0 + 4 * kq;
+        const bool kin = c_al && k0 + kNtBK <= tk.K;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int r = j0 + rr + 32 * p;
+            const float g[4] = {bv[p].x, bv[p].y, bv[p].z, bv[p].w};
+            float a[4] = {gv[p].x, gv[p].y, gv[p].z, gv[p].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[e] += g[e] * g[e];
+                const float Ae = g[e] / (sqrtf(a[e]) + delta);
+                if (r < tk.N && k + e < tk.K) asum += (double)(Ae * Ae);
+            }
+            if (kin && r < tk.N) {
+                *reinterpret_cast<float4*>(acc + (int64_t)r * tk.ldb + k) = make_float4(a[0], a[1], a[2], a[3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (r < tk.N && k + e < tk.K) acc[(int64_t)r * tk.ldb + k + e] = a[e];
+            }
+        }
+    };
+
+    nt_load(A, tk.lda, i0, tk.M, 0, tk.K, a_al, av);
+    nt_load(B, tk.ldb, j0, tk.N, 0, tk.K, b_al, bv);
+    if (adag) acc_load(0);
+    for (int k0 = 0; k0 < tk.K; k0 += kNtBK) {
+        if (adag) acc_update(k0);
+        __syncthreads();   // the previous stage's LDS reads are done
+        nt_store(av, Ah, Al);
+        nt_store(bv, Bh, Bl);
+        __syncthreads();
+        if (k0 + kNtBK < tk.K) {
+            nt_load(A, tk.lda, i0, tk.M, k0 + kNtBK, tk.K, a_al, av);
+            nt_load(B, tk.ldb, j0, tk.N, k0 + kNtBK, tk.K, b_al, bv);
+            if (adag) acc_load(k0 + kNtBK);
+        }
+#pragma unroll
+        for (int kk = 0; kk < kNtBK; kk += 16) {
+            nt_bf16x8 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int o = (wm * 64 + i * 32 + c) * kNtP + kk + 8 * h;
+                ah[i] = *reinterpret_cast<const nt_bf16x8*>(Ah + o);
+                al[i] = *reinterpret_cast<const nt_bf16x8*>(Al + o);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int o = (wn * 64 + j * 32 + c) * kNtP + kk + 8 * h;
+                bh[j] = *reinterpret_cast<const nt_bf16x8*>(Bh + o);
+                bl[j] = *reinterpret_cast<const nt_bf16x8*>(Bl + o);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    cc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[j], cc[i][j], 0, 0, 0);
+                    cc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[j], cc[i][j], 0, 0, 0);
+                    cc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[j], cc[i][j], 0, 0, 0);
+                }
+        }
+    }
+
+    // C and the tile's ||C||^2 (lane (h, c), register v: row 8 (v/4) + 4h + v%4, column c)
+    double nrm = 0.0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = i0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                const int col = j0 + wn * 64 + j * 32 + c;
+                if (r < tk.M && col < tk.N) {
+                    const float o = cc[i][j][v];
+                    C[(int64_t)r * tk.ldc + col] = o;
+                    nrm += double(o) * double(o);
+                }
+            }
+    if (tk.norm_slot >= 0 && args.norms) {
+        const double sn = block_sum_256(nrm, red);
+        if (t == 0) args.norms[tk.norm_slot + tr.tile] = sn;
+    }
+    if (adag) {
+        const double sa = block_sum_256(asum, red);
+        if (t == 0) args.partA[tk.acc_slot + tj] = sa;
+    }
+}
+
 // ====================================================== statistics <= 128
 // L <- beta L + alpha G G^T and R <- beta R + alpha G^T G for one block of at
 // most 128 x 128 per workgroup: G is read from HBM once into LDS (fp32,
@@ -2801,6 +3009,15 @@ hipError_t launch_gemm_f32(const GemmTask* tasks, const TileRef* tiles, int ntil
     else
         hipLaunchKernelGGL((k_gemm<float, float, float, 1, false, false>), dim3(ntiles), dim3(256), 0, s,
                            tasks, tiles, bases, a);
+    return hipGetLastError();
+}
+hipError_t launch_gemm_nt3(const NtTask* tasks, const TileRef* tiles, int ntiles,
+                           const uint64_t* bases, const NtArgs& a, bool adagrad, hipStream_t s) {
+    if (ntiles <= 0) return hipSuccess;
+    if (adagrad)
+        hipLaunchKernelGGL(k_gemm_nt3<true>, dim3(ntiles), dim3(256), 0, s, tasks, tiles, bases, a);
+    else
+        hipLaunchKernelGGL(k_gemm_nt3<false>, dim3(ntiles), dim3(256), 0, s, tasks, tiles, bases, a);
     return hipGetLastError();
 }
 hipError_t launch_gemm_f64(const GemmTask* tasks, const TileRef* tiles, int ntiles,

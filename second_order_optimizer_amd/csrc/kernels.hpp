@@ -84,6 +84,13 @@ struct FusedArgs {          // fused fp32 root of factors up to 128
     float tol;              // > 0: stop one step after ||M - I||_F < tol (at most iters)
 };
 
+struct NtArgs {
+    double* norms;        // per-tile ||C||^2 partials (tasks with norm_slot >= 0)
+    double* partA;        // ||A||^2 partials of the Adagrad-fused tasks
+    float* arena;         // base of the accumulator offsets
+    float delta;          // graft epsilon of A = G / (sqrt(a) + delta)
+};
+
 struct UpdateArgs {
     float beta1, lr, delta;
 };
@@ -100,6 +107,10 @@ hipError_t noalloc_scratch_ptr(void** out);
 // (the same kernel; the role only names the instantiation for profilers)
 hipError_t launch_gemm_f32(const GemmTask* tasks, const TileRef* tiles, int ntiles,
                            const uint64_t* bases, const GemmArgs& a, hipStream_t s, int role = 0);
+// The split-precision (bf16x3) C = A B^T products of the apply; adagrad:
+// tasks with acc_off >= 0 also run the Adagrad pass over B's elements.
+hipError_t launch_gemm_nt3(const NtTask* tasks, const TileRef* tiles, int ntiles,
+                           const uint64_t* bases, const NtArgs& a, bool adagrad, hipStream_t s);
 hipError_t launch_gemm_f64(const GemmTask* tasks, const TileRef* tiles, int ntiles,
                            const uint64_t* bases, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f64_from_f32(const GemmTask* tasks, const TileRef* tiles, int ntiles,

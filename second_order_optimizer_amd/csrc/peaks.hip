@@ -1,6 +1,7 @@
 // Machine-peak probes for measurement tools: the matrix-core issue rate with
-// no memory traffic (fp32 v_mfma_f32_32x32x2f32 and fp64 v_mfma_f64_16x16x4f64,
-// the instructions the optimizer's products run on) and a plain device copy.
+// no memory traffic (fp32 v_mfma_f32_32x32x2f32, fp64 v_mfma_f64_16x16x4f64
+// and bf16 v_mfma_f32_32x32x16_bf16, the instructions the optimizer's
+// products run on) and a plain device copy.
 // They hold none of the method's arithmetic; measured peaks sit beside the
 // published ones when kernel rates are reported as fractions of a peak.
 #include "../../include/shampoo.h"
@@ -59,6 +60,33 @@ __global__ __launch_bounds__(256) void k_peak_mfma_f64(double* out, double seed)
     for (int i = 0; i < kPeakAcc; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) s += acc[i][v];
+    if ((threadIdx.x & 63) == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
+}
+
+typedef __bf16 pb8 __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(256) void k_peak_mfma_bf16(float* out, float seed) {
+    pf16 acc[kPeakAcc];
+#pragma unroll
+    for (int i = 0; i < kPeakAcc; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+    pb8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(seed * (1.0f + 0.01f * ((threadIdx.x + e) & 7)));
+        b[e] = (__bf16)seed;
+    }
+    for (int it = 0; it < kPeakIters; ++it) {
+#pragma unroll
+        for (int i = 0; i < kPeakAcc; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPeakAcc; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s += acc[i][v];
     if ((threadIdx.x & 63) == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
 }
 
@@ -148,6 +176,13 @@ extern "C" int shampoo_measure_peaks(shampoo_peaks* out, void* scratch, size_t s
         s, &ms);
     if (rc) return rc;
     out->mfma_f64_tflops = waves * kPeakIters * kPeakAcc * (2.0 * 16 * 16 * 4) / (ms * 1e-3) / 1e12;
+    rc = time_launches(
+        [&] {
+            k_peak_mfma_bf16<<<kPeakGrid, 256, 0, s>>>(static_cast<float*>(scratch), 0.5f);
+        },
+        s, &ms);
+    if (rc) return rc;
+    out->mfma_bf16_tflops = waves * kPeakIters * kPeakAcc * (2.0 * 32 * 32 * 16) / (ms * 1e-3) / 1e12;
     const int64_t n4 = (int64_t)(half / sizeof(pv4));
     const pv4* src = static_cast<const pv4*>(scratch);
     pv4* dst = reinterpret_cast<pv4*>(static_cast<unsigned char*>(scratch) + half);

@@ -15,6 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libshampoo_mi355x.so")
 
 ROOT_MODES = {"f32": 0, "f64": 1, "auto": 2}
+APPLY_PRECISIONS = {"fp32": 0, "bf16x3": 1}
 DENSE, SPARSE_ROWS = 0, 1
 
 FACTOR_NONFINITE_INPUT = 1
@@ -34,6 +35,7 @@ class Config(ctypes.Structure):
                 ("root_p", ctypes.c_int32), ("newton_iters", ctypes.c_int32),
                 ("root_mode", ctypes.c_int32), ("lanczos_steps", ctypes.c_int32),
                 ("root_parts", ctypes.c_int32), ("large_layer", ctypes.c_int32),
+                ("apply_precision", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("beta1", ctypes.c_double), ("beta2", ctypes.c_double), ("lr", ctypes.c_double),
                 ("eps_rel", ctypes.c_double), ("graft_eps", ctypes.c_double),
                 ("fp64_cond_threshold", ctypes.c_double), ("newton_tol", ctypes.c_double)]
@@ -64,6 +66,7 @@ class BlockLayout(ctypes.Structure):
 
 class Peaks(ctypes.Structure):
     _fields_ = [("mfma_f32_tflops", ctypes.c_double), ("mfma_f64_tflops", ctypes.c_double),
+                ("mfma_bf16_tflops", ctypes.c_double),
                 ("copy_gbs", ctypes.c_double), ("copy_bytes", ctypes.c_int64)]
 
 
@@ -138,10 +141,11 @@ def make_config(block_size: int, *, max_precond_dim: int = 0, root_p: int = 4,
                 beta1: float = 0.9, beta2: float = 0.999, lr: float = 1e-3,
                 eps_rel: float = 1e-6, graft_eps: float = 1e-10,
                 fp64_cond_threshold: float = 1e5, root_parts: int = 0,
-                large_layer: int = 0, newton_tol: float = 1e-3) -> Config:
+                large_layer: int = 0, newton_tol: float = 1e-3,
+                apply_precision: str = "fp32") -> Config:
     return Config(block_size, max_precond_dim, root_p, newton_iters, ROOT_MODES[root_mode],
-                  lanczos_steps, root_parts, large_layer, beta1, beta2, lr, eps_rel, graft_eps,
-                  fp64_cond_threshold, newton_tol)
+                  lanczos_steps, root_parts, large_layer, APPLY_PRECISIONS[apply_precision], 0,
+                  beta1, beta2, lr, eps_rel, graft_eps, fp64_cond_threshold, newton_tol)
 
 
 ROOTS_NONE, ROOTS_ALL = -1, -2
@@ -160,7 +164,8 @@ def measure_peaks(device="cuda", scratch_mib: int = 2048) -> dict:
            "shampoo_measure_peaks")
     del buf
     return {"mfma_f32_tflops": out.mfma_f32_tflops, "mfma_f64_tflops": out.mfma_f64_tflops,
-            "copy_gbs": out.copy_gbs, "copy_bytes": out.copy_bytes}
+            "mfma_bf16_tflops": out.mfma_bf16_tflops, "copy_gbs": out.copy_gbs,
+            "copy_bytes": out.copy_bytes}
 
 
 def root_selector(step: int, cadence: int, parts: int) -> int:

@@ -53,6 +53,7 @@ class Workload:
     cadence: int = 1                # inverse roots recomputed when step % cadence == 0
     newton_iters: int = 20
     newton_tol: float = 1e-3        # fused roots stop one step after ||M - I||_F < this
+    apply_precision: str = "bf16x3" # products of the apply above 128: "fp32" or "bf16x3"
     root_p: int = 4
     beta1: float = 0.9
     beta2: float = 0.999

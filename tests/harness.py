@@ -25,7 +25,8 @@ def gpu_config(wl: synth.Workload, **over):
     kw = dict(max_precond_dim=wl.max_precond_dim, root_p=wl.root_p,
               newton_iters=wl.newton_iters, root_mode=wl.root_mode, beta1=wl.beta1,
               beta2=wl.beta2, lr=wl.lr, eps_rel=wl.eps_rel, graft_eps=wl.graft_eps,
-              fp64_cond_threshold=wl.fp64_cond_threshold, newton_tol=wl.newton_tol)
+              fp64_cond_threshold=wl.fp64_cond_threshold, newton_tol=wl.newton_tol,
+              apply_precision=wl.apply_precision)
     kw.update(over)
     return S.make_config(wl.block_size, **kw)
 

@@ -283,8 +283,8 @@ def _custom(tensors, b, **kw):
     return synth.Workload(wid=50 + b, name=f"custom-b{b}", tensors=tensors, block_size=b, **kw)
 
 
-@pytest.mark.parametrize("root_p", [4, 2])
-def test_one_sided_large_layers(root_p):
+@pytest.mark.parametrize("root_p,apply_precision", [(4, "fp32"), (2, "fp32"), (4, "bf16x3")])
+def test_one_sided_large_layers(root_p, apply_precision):
     """Lemma 1 (large_layer = 1): tensors with one dimension above
     max_precond_dim = 320 are preconditioned on the side that fits, with
     exponent -2/root_p, grafted over the whole tensor.  A tall tensor whose
@@ -305,7 +305,7 @@ def test_one_sided_large_layers(root_p):
     if root_p == 4:
         tensors.append(T("emb", 700, 64, kind="sparse", grad="sparse_rows"))
     wl = _custom(tensors, 128, max_precond_dim=320, cadence=2, steps=4, root_p=root_p)
-    run, orc = run_parity(wl, large_layer=1)
+    run, orc = run_parity(wl, large_layer=1, apply_precision=apply_precision)
     assert sorted(orc.one_sided) == ([0, 2, 3, 5] if root_p == 4 else [0, 2, 3])
 
 
@@ -390,13 +390,16 @@ def test_one_sided_sparse_table_empty_call_and_step_entry():
         check_one_sided(run, orc, 0, t, due)
 
 
-def test_ragged_multitile_and_stale_roots():
+@pytest.mark.parametrize("apply_precision", ["fp32", "bf16x3"])
+def test_ragged_multitile_and_stale_roots(apply_precision):
     """Ragged edges (1-row block, 147- and 130-wide), multi-tile blocks (256),
-    non-multiple-of-4 leading dimensions, roots every 2 steps."""
+    non-multiple-of-4 leading dimensions, roots every 2 steps; the apply of
+    the blocks above 128 on fp32 matrix cores and in split precision (bf16x3,
+    with the Adagrad pass fused into its first product)."""
     T = synth.TensorSpec
     wl = _custom([T("a", 300, 200), T("b", 64, 147), T("c", 513, 130, grad="student_t")], 256,
                  cadence=2, steps=4)
-    run_parity(wl)
+    run_parity(wl, apply_precision=apply_precision)
 
 
 def test_small_blocks_p2_and_beta1_zero():
@@ -404,6 +407,7 @@ def test_small_blocks_p2_and_beta1_zero():
     # p = 2 grows the smallest eigenvalues more slowly per step than p = 4,
     # so the fp64 bar needs a few more iterations at kappa ~ 1e6
     wl = _custom([T("a", 100, 70), T("b", 33, 65)], 32, cadence=1, steps=3, root_p=2, beta1=0.0,
+                 apply_precision="fp32",
                  newton_iters=28)
     run_parity(wl)
 
@@ -414,7 +418,8 @@ def test_root_exponents_1_and_8(root_p):
     (factors up to 128) and the batched chain (a 200 x 150 block: factors of
     ld 224 and 160), AUTO routing; p = 1 runs the scaled iteration count."""
     T = synth.TensorSpec
-    wl = _custom([T("a", 200, 150), T("b", 100, 70)], 256, cadence=1, steps=3, root_p=root_p)
+    wl = _custom([T("a", 200, 150), T("b", 100, 70)], 256, cadence=1, steps=3, root_p=root_p,
+                 apply_precision="fp32" if root_p < 4 else "bf16x3")
     run_parity(wl)
 
 
@@ -457,8 +462,8 @@ def test_newton_convergence_exit(tol):
         say(f"steps at tol {tol}: {counts}")
 
 
-@pytest.mark.parametrize("tol", [0.0, 1e-3])
-def test_fp32_chain_ld1024_and_512(tol):
+@pytest.mark.parametrize("tol,apply_precision", [(0.0, "fp32"), (1e-3, "bf16x3")])
+def test_fp32_chain_ld1024_and_512(tol, apply_precision):
     """The batched fp32 chain at ld 1024 (a 1024 x 1024 block: the CTR
     tower's size class) and 512 (a 1024 x 512 block), AUTO routing: at t = 0
     the one-gradient statistics are ill-conditioned and go fp64, at t = 2
@@ -467,7 +472,7 @@ def test_fp32_chain_ld1024_and_512(tol):
     stage-isolated against the oracle, and the updates per block."""
     T = synth.TensorSpec
     wl = _custom([T("a", 1024, 1024), T("b", 1024, 512)], 1024, cadence=2, steps=3)
-    run, _ = run_parity(wl, newton_tol=tol)
+    run, _ = run_parity(wl, newton_tol=tol, apply_precision=apply_precision)
     d = run.opt.diagnostics()        # the t = 2 pass
     dims32 = sorted({x.dim for x in d if not x.status & FP64})
     assert 1024 in dims32 and 512 in dims32, [(x.dim, x.status, x.kappa_est) for x in d]
@@ -559,8 +564,8 @@ def test_committed_roots_are_symmetric():
                 assert torch.equal(P, P.T), (mode, b)
 
 
-@pytest.mark.parametrize("parts", [0, 3])
-def test_step_entry_point_matches_separate_calls(parts):
+@pytest.mark.parametrize("parts,apply_precision", [(0, "fp32"), (3, "fp32"), (0, "bf16x3")])
+def test_step_entry_point_matches_separate_calls(parts, apply_precision):
     """shampoo_step (on steps without roots: statistics and apply of each
     block <= 128 in the fused step kernel) against the three separate calls:
     statistics and Adagrad accumulators bit for bit (same per-element
@@ -572,7 +577,8 @@ def test_step_entry_point_matches_separate_calls(parts):
     wl = _custom([T("small", 100, 70), T("big", 300, 200), T("wide", 40, 400),
                   T("emb", 500, 32, kind="sparse", grad="sparse_rows"), T("sq", 128, 128)], 256,
                  max_precond_dim=256, cadence=6 if parts else 3, steps=7)
-    runs = [GpuRun(wl, root_parts=parts), GpuRun(wl, root_parts=parts)]
+    runs = [GpuRun(wl, root_parts=parts, apply_precision=apply_precision),
+            GpuRun(wl, root_parts=parts, apply_precision=apply_precision)]
     worst = 0.0
     for t in range(7):
         W0 = [p.clone() for p in runs[1].params]

@@ -34,12 +34,12 @@ def test_library_exports_every_declared_symbol():
 def test_struct_sizes_match_header():
     # sizes the C compiler gives (natural alignment, x86-64 / amdgcn agree)
     assert ctypes.sizeof(S.TensorDesc) == 24
-    assert ctypes.sizeof(S.Config) == 88
+    assert ctypes.sizeof(S.Config) == 96
     assert ctypes.sizeof(S.SparseRows) == 24
     assert ctypes.sizeof(S.FactorDiag) == 56
     assert ctypes.sizeof(S.BlockLayout) == 88
     assert ctypes.sizeof(S.KernelTime) == 48
-    assert ctypes.sizeof(S.Peaks) == 32
+    assert ctypes.sizeof(S.Peaks) == 40
 
 
 def test_strerror_and_argument_errors():
@@ -55,9 +55,13 @@ def test_strerror_and_argument_errors():
     assert L.shampoo_create(ctypes.byref(cfg), 1, bad, ctypes.byref(h)) == -1
     badk = (S.TensorDesc * 1)(S.TensorDesc(4, 4, 7, 0))
     assert L.shampoo_create(ctypes.byref(cfg), 1, badk, ctypes.byref(h)) == -1
+    c = S.make_config(128, root_p=2, apply_precision="bf16x3")
+    assert L.shampoo_create(ctypes.byref(c), 1, descs, ctypes.byref(h)) == -5
     for field, val, rc in (("root_p", 3, -5), ("root_p", 16, -5), ("beta2", 0.0, -1),
                            ("beta2", 1.5, -1), ("block_size", 0, -1), ("newton_iters", 0, -1),
                            ("root_mode", 5, -1), ("eps_rel", -1.0, -1), ("newton_tol", -1e-3, -1),
+                           ("apply_precision", 2, -1), ("apply_precision", -1, -1),
+                           ("reserved", 1, -1),
                            ("newton_tol", 1.0, -1), ("newton_tol", float("nan"), -1)):
         c = S.make_config(128)
         setattr(c, field, val)
