@@ -556,7 +556,7 @@ __device__ __forceinline__ void nt_store(const float4 (&v)[4], __bf16* H, __bf16
 }
 
 template <bool ADAG>
-__global__ __launch_bounds__(256, 2) void k_gemm_nt3(const NtTask* __restrict__ tasks,
+__global__ __launch_bounds__(256, ADAG ? 2 : 3) void k_gemm_nt3(const NtTask* __restrict__ tasks,
                                                     const TileRef* __restrict__ tiles,
                                                     const uint64_t* __restrict__ bases, NtArgs args) {
     __shared__ __align__(16) __bf16 Ah[BM * kNtP];
@@ -3007,7 +3007,7 @@ hipError_t launch_gemm_f32(const GemmTask* tasks, const TileRef* tiles, int ntil
         hipLaunchKernelGGL((k_gemm<float, float, float, 1, false, false, 2>), dim3(ntiles), dim3(256), 0,
                            s, tasks, tiles, bases, a);
     else
-        hipLaunchKernelGGL((k_gemm<float, float, float, 1, false, false>), dim3(ntiles), dim3(256), 0, s,
+        hipLaunchKernelGGL((k_gemm<float, float, float, 3, false, false>), dim3(ntiles), dim3(256), 0, s,
                            tasks, tiles, bases, a);
     return hipGetLastError();
 }
