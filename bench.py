@@ -29,10 +29,12 @@ iteration, whose iterates are all polynomials in one matrix) counts the
 multiply-adds of its upper triangle, n (n + 1) k flops for an n x n result
 over k; other products count 2 m n k.
 
-Inside the timed region the per-launch events are recorded in the steps that
-recompute roots and in the step after each; every root-pass launch is timed,
-and each family's launches per step, counted on the warm-up steps, scale its
-sampled average to the whole region.
+The timed steps carry no per-launch events (one event after each step).  The
+per-kernel breakdown comes from as many steps again, run right after them:
+there the per-launch events are recorded in the steps that recompute roots
+and in the step after each; every root-pass launch is timed, and each
+family's launches per step, counted on the warm-up steps, scale its sampled
+average to the whole region.
 
 Two offline modes turn rocprofv3 output into the summaries under profiles/:
     python bench.py --trace-summary DIR --title T --command C > profiles/X.md
@@ -361,15 +363,12 @@ def run_pass(wl, args, tol, pool, dev, peaks):
 
     stream = torch.cuda.current_stream(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if not args.no_profile:
-        opt.profile_read()        # reset
+    # the timed steps: no per-launch events (only one event after each step)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev0.record(stream)
     marks = []                  # one event after every step: per-step GPU time
     for t in range(args.warmup, args.warmup + args.steps):
-        if not args.no_profile:
-            opt.profile(sampled(t))
         step(t)
         e = torch.cuda.Event(enable_timing=True)
         e.record(stream)
@@ -387,11 +386,26 @@ def run_pass(wl, args, tol, pool, dev, peaks):
     step_ms = {"p50": per_step[len(per_step) // 2],
                "p99": per_step[min(len(per_step) - 1, int(0.99 * len(per_step)))],
                "max": per_step[-1]}
-    prof = opt.profile_read() if not args.no_profile else {}
-    opt.profile(False)
     ms_step = ms_total / args.steps
-    timed = range(args.warmup, args.warmup + args.steps)
-    n_root_passes = sum(1 for t in timed if t % wl.cadence == 0)
+    # the per-kernel breakdown: as many steps again, right after, with events
+    # around the launches of the steps that recompute roots and the step
+    # after each (kept out of the timed steps: events around many short
+    # launches would slow them)
+    prof = {}
+    timed = range(args.warmup + args.steps, args.warmup + 2 * args.steps)
+    if not args.no_profile:
+        opt.profile_read()        # reset
+        for t in timed:
+            opt.profile(sampled(t))
+            step(t)
+        if args.async_roots:
+            opt.roots_async_end()
+        torch.cuda.synchronize()
+        prof = opt.profile_read()
+        opt.profile(False)
+    n_root_passes = sum(1 for t in range(args.warmup, args.warmup + args.steps)
+                        if t % wl.cadence == 0)
+    n_root_passes_prof = sum(1 for t in timed if t % wl.cadence == 0)
     diag = opt.diagnostics()
     n64 = sum(1 for d in diag if d.status & S.FACTOR_FP64)
     wm = work_model(wl, opt)
@@ -480,13 +494,13 @@ def run_pass(wl, args, tol, pool, dev, peaks):
         if name in alg:
             work, unit, bound, peak = alg[name]
         elif name == "newton_fused_f32" and flops_fused_root > 0:
-            work = flops_fused_root * n_root_passes / total
+            work = flops_fused_root * n_root_passes_prof / total
             unit, bound, peak = "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]
         elif name == "newton_gemm_f32" and flops_f32_root > 0:
-            work = flops_f32_root * n_root_passes / total
+            work = flops_f32_root * n_root_passes_prof / total
             unit, bound, peak = "TFLOP/s", "mfma", PEAK_TFLOPS["f32"]
         elif name == "newton_gemm_f64" and flops_f64_root > 0:
-            work = flops_f64_root * n_root_passes / total
+            work = flops_f64_root * n_root_passes_prof / total
             unit, bound, peak = "TFLOP/s", "mfma", PEAK_TFLOPS["f64"]
         if work is not None and work > 0:
             sec = rec["avg_ms"] / 1e3
@@ -536,7 +550,7 @@ def run_pass(wl, args, tol, pool, dev, peaks):
                    "newton_gemm_f64", "newton_commit", "newton_fused_f32", "route_compact",
                    "newton_conv", "newton_split_sum")
                   if n in stages)
-    inv_root_blocks_per_s = (opt.n_blocks * n_root_passes / (root_ms / 1e3)) if root_ms > 0 else None
+    inv_root_blocks_per_s = (opt.n_blocks * n_root_passes_prof / (root_ms / 1e3)) if root_ms > 0 else None
     mfma_pct = {k: round(100 * v["frac"], 2) for k, v in stages.items() if v.get("bound") == "mfma"}
     res = {
         "value": value, "ms_per_step": ms_step, "steps_per_s": steps_per_s,
@@ -569,7 +583,7 @@ def main():
                     help="fp32-root convergence tolerance (0: the full iteration count)")
     ap.add_argument("--no-full-count", action="store_true",
                     help="skip the second timed pass at newton_tol 0")
-    ap.add_argument("--pool", type=int, default=2, help="distinct gradient sets kept in HBM")
+    ap.add_argument("--pool", type=int, default=4, help="distinct gradient sets kept in HBM")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the machine-peak probes")
     ap.add_argument("--root-parts", type=int, default=0,

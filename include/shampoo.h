@@ -88,10 +88,10 @@ typedef struct {
                                  same eigenvalue gap                                     */
     int32_t root_mode;        /* shampoo_root_mode                                       */
     int32_t lanczos_steps;    /* Krylov steps for lambda_max; 0 = adaptive: stop at the
-                                 first check (after 8 steps, then every 4th) where the
-                                 top Ritz pair's residual is within 5e-5 of theta, at
-                                 most 64 steps; the kappa estimate uses min(8, this), 8
-                                 when 0                                                  */
+                                 first check (after 12 steps, every 4th to 32, every 8th
+                                 after) where the top Ritz pair's residual is within
+                                 5e-5 of theta, at most 64 steps; the kappa estimate
+                                 uses min(8, this), 8 when 0                            */
     int32_t root_parts;       /* staggered root pass (cue 14-16: roots are computed off
                                  the critical path and swapped in): 0 or 1 = one pass
                                  over every factor; P >= 2 also plans P parts, part q
@@ -381,11 +381,11 @@ int shampoo_profile_read(shampoo_t* h, shampoo_kernel_time* out, int32_t cap, in
  * report kernel rates as fractions of a peak.  None of the method's
  * arithmetic: the matrix-core issue rate of the MFMA instructions the
  * products use (fp32 v_mfma_f32_32x32x2f32, fp64 v_mfma_f64_16x16x4f64, bf16
- * v_mfma_f32_32x32x16_bf16),
- * every wave of a full grid issuing independent products from registers
- * with no memory traffic, and a plain device-to-device copy (bytes read plus
- * bytes written, per second).  Each is the median of three timed launches
- * (HIP events on `stream`) after one warm-up; the call waits for them. */
+ * v_mfma_f32_32x32x16_bf16), every wave of a full grid issuing independent
+ * products from registers with no memory traffic; and the best of a few
+ * shapes of a plain device-to-device copy (bytes read plus bytes written, per
+ * second).  Each figure is the median of three timed launches (HIP events on
+ * `stream`) after one warm-up; the call waits for them. */
 typedef struct {
     double mfma_f32_tflops;  /* TFLOP/s, 2 flops per multiply-add                  */
     double mfma_f64_tflops;

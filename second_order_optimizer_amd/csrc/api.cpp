@@ -1498,8 +1498,9 @@ int shampoo_create(const shampoo_config* cfg, int32_t n_tensors, const shampoo_t
     try {
         h->cfg = c;
         // lanczos_steps == 0: lambda_max by Lanczos until the top Ritz pair's
-        // residual is within kLanczosTol of theta (checked after 8 steps and
-        // every 4th step), at most 64 steps; 8 steps for the kappa estimate
+        // residual is within kLanczosTol of theta (checked after 12 steps,
+        // every 4th to 32, every 8th after), at most 64 steps; 8 steps for
+        // the kappa estimate
         h->n = n_tensors;
         h->tensors.resize(n_tensors);
         for (int t = 0; t < n_tensors; ++t) {

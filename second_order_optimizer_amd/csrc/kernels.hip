@@ -876,8 +876,10 @@ __device__ __forceinline__ double sturm_step(double d, double a_minus_x, double 
 // Largest eigenvalue of the m x m tridiagonal (al, be) by Sturm-count
 // multisection on one wave: every lane counts the eigenvalues below two
 // points of the bracket (two independent recurrences in flight), so each
-// round shrinks it 129-fold.  NaN for non-finite input.
-__device__ __forceinline__ double tridiag_max_wave(const double* al, const double* be, int m) {
+// round shrinks it 129-fold, until the bracket is within rtol of its upper
+// end (which is returned).  NaN for non-finite input.
+__device__ __forceinline__ double tridiag_max_wave(const double* al, const double* be, int m,
+                                                   double rtol = 1e-15) {
     const int lane = threadIdx.x & 63;
     double lo = 0.0, hi = 0.0;
     bool finite = true;
@@ -889,7 +891,7 @@ __device__ __forceinline__ double tridiag_max_wave(const double* al, const doubl
     }
     if (!finite) return NAN;
     for (int round = 0; round < 12; ++round) {
-        if (!(hi - lo > 1e-15 * fmax(fabs(lo), fabs(hi)))) break;
+        if (!(hi - lo > rtol * fmax(fabs(lo), fabs(hi)))) break;
         const double h = (hi - lo) / 129.0;
         const double x0 = lo + h * (double)(2 * lane + 1), x1 = lo + h * (double)(2 * lane + 2);
         double d0 = al[0] - x0, d1 = al[0] - x1;
@@ -941,10 +943,23 @@ __device__ __forceinline__ double ritz_residual(const double* al, const double* 
     return fabs(be[m - 1]) / sqrt(S);
 }
 
-// Check points of the adaptive Lanczos stop: after 8 steps and every 4th
-// step from there (a top Ritz pair's residual falls steadily until it is
-// converged; checking every 4 steps keeps the multisection's cost small).
-__device__ __forceinline__ bool lanczos_check_step(int m) { return m >= 8 && (m & 3) == 0; }
+// The adaptive stop's test on one wave: is the top Ritz pair of the m x m
+// tridiagonal within tol of converged?  Out of line, so that the registers
+// of the multisection are not added to those of the kernels that inline the
+// Lanczos loop (the fused root).
+__device__ __attribute__((noinline)) bool ritz_converged(const double* al, const double* be, int m,
+                                                        double tol) {
+    const double th = tridiag_max_wave(al, be, m);
+    return !(ritz_residual(al, be, m, th) > tol * th);
+}
+
+// Check points of the adaptive Lanczos stop: after 12 steps, every 4th step
+// up to 32 and every 8th after (a top Ritz pair's residual falls steadily
+// until it is converged; sparse checks keep the multisection's cost small).
+__device__ __forceinline__ bool lanczos_check_step(int m) {
+    return m >= 12 && ((m <= 32 && (m & 3) == 0) || (m & 7) == 0);
+}
+
 
 // 128 x 128 fp32 matrices in LDS ("slots"): row pitch 129 floats, the column
 // index stored with its bits 2 and 5 exchanged.  With this layout the MFMA
@@ -1076,9 +1091,8 @@ __device__ __forceinline__ double lanczos_slot(const float* slot, int n, int ste
         if (tol > 0.0 && k + 1 < steps && lanczos_check_step(k + 1)) {
             __syncthreads();   // al, be of this step written
             if (w == 0) {
-                const double th = tridiag_max_wave(L.al, L.be, k + 1);
-                const double rs = ritz_residual(L.al, L.be, k + 1, th);
-                if (lane == 0) L.stop = !(rs > tol * th);
+                const bool conv = ritz_converged(L.al, L.be, k + 1, tol);
+                if (lane == 0) L.stop = conv;
             }
             __syncthreads();
             if (L.stop) {      // uniform: every thread reads the same word
@@ -2802,33 +2816,81 @@ __global__ __launch_bounds__(256) void k_update(const RowChunk* __restrict__ chu
     const float b1 = args.beta1, lr = args.lr, dl = args.delta;
     const bool vec = (ch.cols % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0) &&
                      ((reinterpret_cast<uintptr_t>(G) & 15) == 0);
-    if (vec) {
+    if (vec && ch.mode == 0) {
+        // Shampoo tensor: every load of kU 16-byte groups (D, momentum,
+        // weight) issued before their stores, so each thread keeps 3 kU loads
+        // in flight (the arrays do not alias, but the compiler cannot know)
+        constexpr int kU = 4;
         const int64_t t4 = total / 4;
         const int c4 = ch.cols / 4;
-        for (int64_t e = threadIdx.x; e < t4; e += 256) {
-            const int64_t idx = base + 4 * e;
-            float4 u;
-            if (ch.mode == 0) {
-                const int r = ch.row0 + (int)(e / c4);
-                const int c = 4 * (int)(e % c4);
-                const int blk = ch.first_block + (r / ch.block_size) * ch.nbc + c / ch.block_size;
-                const float s = scale[blk];
-                const float4 d = *reinterpret_cast<const float4*>(D + idx);
-                u = make_float4(s * d.x, s * d.y, s * d.z, s * d.w);
-            } else {
-                const float4 g = *reinterpret_cast<const float4*>(G + idx);
-                float4 av = *reinterpret_cast<const float4*>(a + idx);
-                av.x += g.x * g.x; av.y += g.y * g.y; av.z += g.z * g.z; av.w += g.w * g.w;
-                *reinterpret_cast<float4*>(a + idx) = av;
-                u = make_float4(g.x / (sqrtf(av.x) + dl), g.y / (sqrtf(av.y) + dl),
-                                g.z / (sqrtf(av.z) + dl), g.w / (sqrtf(av.w) + dl));
+        for (int64_t e0 = threadIdx.x; e0 < t4; e0 += 256 * kU) {
+            float4 d[kU], m[kU], w[kU];
+            float sc[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t e = e0 + 256 * u;
+                if (e < t4) {
+                    const int64_t idx = base + 4 * e;
+                    d[u] = *reinterpret_cast<const float4*>(D + idx);
+                    m[u] = *reinterpret_cast<const float4*>(mom + idx);
+                    w[u] = *reinterpret_cast<const float4*>(W + idx);
+                    const int r = ch.row0 + (int)(e / c4);
+                    const int c = 4 * (int)(e % c4);
+                    sc[u] = scale[ch.first_block + (r / ch.block_size) * ch.nbc + c / ch.block_size];
+                }
             }
-            float4 m = *reinterpret_cast<const float4*>(mom + idx);
-            float4 w = *reinterpret_cast<const float4*>(W + idx);
-            m.x = b1 * m.x + u.x; m.y = b1 * m.y + u.y; m.z = b1 * m.z + u.z; m.w = b1 * m.w + u.w;
-            w.x -= lr * m.x; w.y -= lr * m.y; w.z -= lr * m.z; w.w -= lr * m.w;
-            *reinterpret_cast<float4*>(mom + idx) = m;
-            *reinterpret_cast<float4*>(W + idx) = w;
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t e = e0 + 256 * u;
+                if (e < t4) {
+                    const int64_t idx = base + 4 * e;
+                    const float s = sc[u];
+                    const float4 uu = make_float4(s * d[u].x, s * d[u].y, s * d[u].z, s * d[u].w);
+                    float4 mm = m[u], ww = w[u];
+                    mm.x = b1 * mm.x + uu.x; mm.y = b1 * mm.y + uu.y;
+                    mm.z = b1 * mm.z + uu.z; mm.w = b1 * mm.w + uu.w;
+                    ww.x -= lr * mm.x; ww.y -= lr * mm.y; ww.z -= lr * mm.z; ww.w -= lr * mm.w;
+                    *reinterpret_cast<float4*>(mom + idx) = mm;
+                    *reinterpret_cast<float4*>(W + idx) = ww;
+                }
+            }
+        }
+    } else if (vec) {
+        // dense Adagrad: the loads of kU groups (G, a, momentum, weight)
+        // before their stores, as above
+        constexpr int kU = 4;
+        const int64_t t4 = total / 4;
+        for (int64_t e0 = threadIdx.x; e0 < t4; e0 += 256 * kU) {
+            float4 g[kU], av[kU], m[kU], w[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t e = e0 + 256 * u;
+                if (e < t4) {
+                    const int64_t idx = base + 4 * e;
+                    g[u] = *reinterpret_cast<const float4*>(G + idx);
+                    av[u] = *reinterpret_cast<const float4*>(a + idx);
+                    m[u] = *reinterpret_cast<const float4*>(mom + idx);
+                    w[u] = *reinterpret_cast<const float4*>(W + idx);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t e = e0 + 256 * u;
+                if (e < t4) {
+                    const int64_t idx = base + 4 * e;
+                    float4 aa = av[u], mm = m[u], ww = w[u];
+                    const float4 gg = g[u];
+                    aa.x += gg.x * gg.x; aa.y += gg.y * gg.y; aa.z += gg.z * gg.z; aa.w += gg.w * gg.w;
+                    const float4 uu = make_float4(gg.x / (sqrtf(aa.x) + dl), gg.y / (sqrtf(aa.y) + dl),
+                                                  gg.z / (sqrtf(aa.z) + dl), gg.w / (sqrtf(aa.w) + dl));
+                    mm.x = b1 * mm.x + uu.x; mm.y = b1 * mm.y + uu.y;
+                    mm.z = b1 * mm.z + uu.z; mm.w = b1 * mm.w + uu.w;
+                    ww.x -= lr * mm.x; ww.y -= lr * mm.y; ww.z -= lr * mm.z; ww.w -= lr * mm.w;
+                    *reinterpret_cast<float4*>(a + idx) = aa;
+                    *reinterpret_cast<float4*>(mom + idx) = mm;
+                    *reinterpret_cast<float4*>(W + idx) = ww;
+                }
+            }
         }
     } else {
         for (int64_t e = threadIdx.x; e < total; e += 256) {
