@@ -850,6 +850,20 @@ int build_plan(shampoo_s* h) {
     // Blocks of at most 128 x 128 go to the fused kernel, larger ones to the
     // batched GEMM (two tasks per block).
     {
+        // The statistics keep their upper triangle; the split Lanczos of a
+        // pass with at most kLanczosSplitMax factors above 128 reads whole
+        // rows, so only then are the off-diagonal tiles also stored mirrored.
+        bool mirror_stats = false;
+        {
+            const int np = c.root_parts > 1 ? c.root_parts : 0;
+            for (int set = 0; set <= np; ++set) {
+                int nbig = 0;
+                for (const FactorPlan& f : h->factors)
+                    if (f.ld > 128 && (set == 0 || f.block % np == set - 1)) ++nbig;
+                if (nbig > 0 && nbig <= kLanczosSplitMax) mirror_stats = true;
+            }
+        }
+        const int mbit = mirror_stats ? 32 : 0;
         std::vector<GemmTask> tasks;
         std::vector<GramJob> small;
         std::vector<GemmTask> sk, gs;
@@ -964,7 +978,7 @@ int build_plan(shampoo_s* h) {
             t.ldc = fl.ld;
             t.M = t.N = bp.mb;
             t.K = bp.nb;
-            t.trans = 2 | 16 | 32;   // symmetric: upper tiles, mirrored
+            t.trans = 2 | 16 | mbit;   // symmetric: upper tiles (mirrored for a split Lanczos)
             t.tiles_n = ceil_div(t.N, kTile);
             tasks.push_back(t);
             // R: op(A) = G_b^T (nb x mb), op(B) = G_b
@@ -972,7 +986,7 @@ int build_plan(shampoo_s* h) {
             t.ldc = fr.ld;
             t.M = t.N = bp.nb;
             t.K = bp.mb;
-            t.trans = 1 | 16 | 32;
+            t.trans = 1 | 16 | mbit;
             t.tiles_n = ceil_div(t.N, kTile);
             tasks.push_back(t);
         }
