@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -335,6 +336,26 @@ template <> struct WaveTile<double> {
                     acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     }
+    // the same from fp32 stages of BK = 32 (fp32 operands: each value is
+    // converted to fp64 as it is read, exactly)
+    __device__ __forceinline__ void compute_f32(const float* As, const float* Bs, int wm, int wn) {
+        constexpr int P = BM + GemmTraits<float>::PADE;
+        const int lane = threadIdx.x & 63;
+        const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+        for (int kk = 0; kk < GemmTraits<float>::BK; kk += 4) {
+            double a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = (double)As[(kk + g) * P + wm * 64 + i * 16 + c];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = (double)Bs[(kk + g) * P + wn * 64 + j * 16 + c];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    }
     // accumulator value idx = (4 i + j) 4 + v and its place (r, c) in the tile
     static constexpr int NV = 64;
     __device__ __forceinline__ double get(int idx, int wm, int wn, int& r, int& c) const {
@@ -351,12 +372,22 @@ template <> struct WaveTile<double> {
 // exact: fp32 x fp32 fits the fp64 mantissa).
 // One tile of a batched-GEMM launch (entry e of the tile table); false if
 // its task is gated off.
+// fp64 products of fp32 operands (the statistics) stage their operands in
+// LDS as fp32, 32 deep, and convert them as they are read: half the LDS bytes
+// and barriers per k of fp64 stages.
+template <typename T, typename TA, typename TB>
+constexpr bool kStageF32 = sizeof(T) == 8 && sizeof(TA) == 4 && sizeof(TB) == 4;
+
 template <typename T, typename TA, typename TB, bool AXPBY>
 __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ tasks,
                                           const TileRef* __restrict__ tiles,
                                           const uint64_t* __restrict__ bases, const GemmArgs& args,
-                                          T* As, T* Bs, double* red) {
-    constexpr int BK = GemmTraits<T>::BK;
+                                          void* As_, void* Bs_, double* red) {
+    constexpr bool F32S = kStageF32<T, TA, TB>;
+    using S = typename std::conditional<F32S, float, T>::type;   // staged type
+    S* As = static_cast<S*>(As_);
+    S* Bs = static_cast<S*>(Bs_);
+    constexpr int BK = GemmTraits<S>::BK;
     const TileRef tr = tiles[e];
     const GemmTask tk = tasks[tr.task];
     if (args.gate && tk.factor >= 0 && args.gate[tk.factor] != args.gate_val) return false;
@@ -372,18 +403,18 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
     const bool a_kc = !ta;
     // op(B)[k][j]: B^T stored B[j][k] -> k contiguous; B stored B[k][j] -> j contiguous.
     const bool b_kc = tb;
-    constexpr int VEC = GemmTraits<T>::VEC;
+    constexpr int VEC = GemmTraits<S>::VEC;
     const bool a_al = ((reinterpret_cast<uintptr_t>(A) % (VEC * sizeof(TA))) == 0) && (tk.lda % VEC == 0);
     const bool b_al = ((reinterpret_cast<uintptr_t>(B) % (VEC * sizeof(TB))) == 0) && (tk.ldb % VEC == 0);
-    const T c1 = T(args.xc1), c2 = T(args.xc2);
+    const S c1 = S(args.xc1), c2 = S(args.xc2);
 
     const int w = threadIdx.x >> 6;
     const int wm = w >> 1, wn = w & 1;
     WaveTile<T> wt;
     wt.zero();
 
-    StageLoader<T, TA> la;
-    StageLoader<T, TB> lb;
+    StageLoader<S, TA> la;
+    StageLoader<S, TB> lb;
     // A split-K part sums k in [kb, K).  fp32: the operands are offset to
     // k = kb and the loop runs from 0 (a Newton operand's diagonal is found
     // with offset kb); fp64: the loop runs from kb.  The two forms compute the
@@ -407,7 +438,8 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
             la.load(A, tk.lda, a_kc, i0, k0 + BK, tk.M, Kp, a_al, xa, c1, c2, dk);
             lb.load(B, tk.ldb, b_kc, j0, k0 + BK, tk.N, Kp, b_al, xb, c1, c2, dk);
         }
-        wt.compute(As, Bs, wm, wn);
+        if constexpr (F32S) wt.compute_f32(As, Bs, wm, wn);
+        else wt.compute(As, Bs, wm, wn);
     }
 
     const T alpha = T(args.alpha), beta = T(args.beta);
@@ -462,10 +494,11 @@ template <typename T, typename TA, typename TB, int MINW, bool AXPBY, bool PERSI
 __global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__ tasks,
                                              const TileRef* __restrict__ tiles,
                                              const uint64_t* __restrict__ bases, GemmArgs args) {
-    constexpr int BK = GemmTraits<T>::BK;
-    constexpr int P = BM + GemmTraits<T>::PADE;
-    __shared__ __align__(16) T As[BK * P];
-    __shared__ __align__(16) T Bs[BK * P];
+    using S = typename std::conditional<kStageF32<T, TA, TB>, float, T>::type;
+    constexpr int BK = GemmTraits<S>::BK;
+    constexpr int P = BM + GemmTraits<S>::PADE;
+    __shared__ __align__(16) S As[BK * P];
+    __shared__ __align__(16) S Bs[BK * P];
     __shared__ double red[4];
     if constexpr (PERSIST) {
         // the table is sorted by gating id and the live ids are a prefix, so
