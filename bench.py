@@ -548,7 +548,7 @@ def run_pass(wl, args, tol, pool, dev, peaks):
     root_ms = sum(stages[n]["ms_per_step"] * args.steps for n in
                   ("lanczos_stats", "lanczos_roots", "newton_init", "newton_gemm_f32",
                    "newton_gemm_f64", "newton_commit", "newton_fused_f32", "route_compact",
-                   "newton_conv", "newton_split_sum")
+                   "newton_split_sum")
                   if n in stages)
     inv_root_blocks_per_s = (opt.n_blocks * n_root_passes_prof / (root_ms / 1e3)) if root_ms > 0 else None
     mfma_pct = {k: round(100 * v["frac"], 2) for k, v in stages.items() if v.get("bound") == "mfma"}
@@ -771,7 +771,6 @@ FAMILY_OF = [
     ("k_adagrad_norm", "adagrad_norm", None),
     ("k_update", "update", None),
     ("k_sparse_rows", "sparse_rows", None),
-    ("k_newton_conv", "newton_conv", None),
     ("k_lanczos_big<double>", "lanczos_stats", None),
     ("k_lanczos_big<float>", "lanczos_roots", None),
 ]

@@ -134,7 +134,7 @@ enum ProfCat : int {
     PC_STATS = 0, PC_LANCZOS_S, PC_LANCZOS_P, PC_NEWTON_INIT, PC_NEWTON_GEMM32, PC_NEWTON_GEMM64,
     PC_NEWTON_COMMIT, PC_ADAGRAD, PC_APPLY_T, PC_APPLY_D, PC_SCALE, PC_UPDATE, PC_SPARSE,
     PC_NEWTON_FUSED, PC_APPLY_FUSED, PC_STEP_FUSED, PC_STATS_SPLITK, PC_SOS_STATS, PC_SOS_NORM,
-    PC_SOS_APPLY, PC_SOS_UPDATE, PC_ROUTE, PC_NEWTON_CONV, PC_NEWTON_SPLIT, PC_STATS_SMALL,
+    PC_SOS_APPLY, PC_SOS_UPDATE, PC_ROUTE, PC_NEWTON_SPLIT, PC_STATS_SMALL,
     PC_COUNT
 };
 const char* const kProfNames[PC_COUNT] = {
@@ -142,7 +142,7 @@ const char* const kProfNames[PC_COUNT] = {
     "newton_gemm_f64", "newton_commit", "adagrad_norm", "apply_gemm_t", "apply_gemm_d",
     "block_scale", "update", "sparse_rows", "newton_fused_f32", "apply_fused", "step_fused",
     "stats_onesided", "stats_onesided_rows", "onesided_rows_norm", "apply_onesided_rows",
-    "onesided_rows_update", "route_compact", "newton_conv", "newton_split_sum", "stats_gram128"};
+    "onesided_rows_update", "route_compact", "newton_split_sum", "stats_gram128"};
 
 struct ProfRec {
     int cat;
@@ -162,7 +162,6 @@ struct shampoo_s {
     // arena layout (bytes)
     size_t total = 0;
     int64_t off_bases = 0, off_sparse = 0, off_tables = 0, off_diag = 0, off_prec = 0, off_chk = 0;
-    int64_t off_stop = 0, off_convp = 0;
     int64_t off_lzwork = 0;
     int64_t off_slot_jobs = 0, off_slot_live = 0;  // packed fp64 chain: slot jobs and flags
     int64_t slot_tmpl_off = 0;                     // and the template job of every slot entry
@@ -377,6 +376,57 @@ int newton_iters_for(const shampoo_config& c, int p) {
     if (p >= 4) return c.newton_iters;
     const double g4 = 4.0 * std::log(5.0 / 4.0), gp = p * std::log((p + 1.0) / p);
     return (int)std::ceil(c.newton_iters * g4 / gp);
+}
+
+// Per-step scaling of the batched coupled-Newton iteration (with a
+// convergence exit, newton_tol > 0).  Step k scales M_k by mu_k and X_k by
+// mu_k^(1/p) before T = ((p+1) I - M) / p is formed, which keeps
+// M_k = X_k^p A; so the products take T' = mu^(1/p) ((p+1) I - mu M) / p in
+// place of T, and X <- X T', M <- T'^p M.  Every eigenvalue m of M follows the
+// scalar map f(m) = m ((p+1-m)/p)^p after the scaling.  The spectrum of M_0 =
+// z A lies in [lo, hi] with lo = (p+1)/2 eps_rel / (1 + eps_rel) (A's
+// eigenvalues are at least eps) and hi = (p+1)/2 (1 + 1e-2) (a margin for the
+// estimate of lambda_max), so the interval is carried through the map and mu_k
+// chosen from it alone: the largest mu with mu hi <= 0.7 (p+1) (T' keeps the
+// top of the spectrum away from 0, where fp32 rounding would be amplified)
+// and f(mu lo) <= f(mu hi) (the bottom's image is the new lower end), until lo
+// reaches 1/2, and 1 after that.  mu is the same for every factor (it
+// depends on p and eps_rel only), and so is the step count: conv_steps is the
+// first k at which the interval of M_k lies within tau of 1, plus two steps
+// (at most iters).
+void newton_schedule(int p, double eps_rel, int iters, double tau, std::vector<double>& mu,
+                     int& conv_steps) {
+    auto f = [p](double m) { return m * std::pow((p + 1 - m) / p, p); };
+    double lo = 0.5 * (p + 1) * eps_rel / (1.0 + eps_rel), hi = 0.5 * (p + 1) * 1.01;
+    const double cap = 0.7 * (p + 1);
+    mu.assign(iters, 1.0);
+    conv_steps = iters;
+    bool found = false;
+    for (int k = 0; k < iters; ++k) {
+        if (!found && std::max(1.0 - lo, hi - 1.0) <= tau) {
+            conv_steps = std::min(iters, k + 2);
+            found = true;
+        }
+        double m = 1.0;
+        if (lo < 0.5) {
+            double a = 1.0 / hi, b = cap / hi;
+            if (f(b * lo) <= f(b * hi)) {
+                m = b;
+            } else {
+                for (int it = 0; it < 100; ++it) {   // f(c lo) - f(c hi) grows with c
+                    const double c = 0.5 * (a + b);
+                    if (f(c * lo) < f(c * hi)) a = c;
+                    else b = c;
+                }
+                m = std::max(a, 1.0);
+            }
+        }
+        mu[k] = m;
+        const double x = f(m * lo), y = f(m * hi);
+        const double top = (m * lo <= 1.0 && 1.0 <= m * hi) ? 1.0 : std::max(x, y);
+        lo = std::min(x, y);
+        hi = top;
+    }
 }
 
 // Builds the per-parity GEMM launches of one Newton chunk.
@@ -626,8 +676,6 @@ int build_plan(shampoo_s* h) {
     h->off_diag = take((int64_t)std::max(nf, 1) * sizeof(FactorDiag));
     h->off_prec = take((int64_t)std::max(nf, 1) * 4);
     h->off_chk = take((int64_t)std::max(nf, 1) * 16);   // Newton finish: per-factor check slots
-    h->off_stop = take((int64_t)std::max(nf, 1) * 12);  // fp32 chain exit: stop, conv, cnt
-    h->off_convp = take((int64_t)std::max(nf, 1) * 32 * 8);   // and the checks' partial sums
     h->off_lzwork = take((int64_t)kLanczosSplitMax * kLzWork * 8);  // split Lanczos records
     for (auto& f : h->factors) f.off_s = take((int64_t)f.ld * f.ld * 8);  // fp64 statistics
     for (auto& f : h->factors) f.off_p = take((int64_t)f.ld * f.ld * 4);
@@ -1792,14 +1840,6 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
     na.gate = gate;
     na.gate_val = gate_val;
     na.chk = at<unsigned long long>(h, h->off_chk);
-    // the fp32 chain's convergence exit: stop flags gate its products
-    const bool exit32 = !fp64 && h->cfg.newton_tol > 0.0;
-    if (exit32) {
-        na.stop = at<int32_t>(h, h->off_stop);
-        na.conv = na.stop + std::max((int)h->factors.size(), 1);
-        na.cnt = na.conv + std::max((int)h->factors.size(), 1);
-        na.part = at<double>(h, h->off_convp);
-    }
     void* scratch = scr ? scr : h->arena + (fp64 ? h->off_scr64 : h->off_scr32);
     FactorDiag* diag = at<FactorDiag>(h, h->off_diag);
     GemmArgs g{};
@@ -1812,16 +1852,31 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
     for (auto& ch : chunks) {
         const int p = ch.p;
         na.p = p;
-        na.iters = ch.iters;
-        g.xc1 = (double)(p + 1) / p;
-        g.xc2 = -1.0 / p;
+        // with a convergence exit (newton_tol > 0) the chain takes the scaled
+        // steps and stops two steps after the one where every eigenvalue of
+        // M is within newton_tol of 1 by the schedule's bound (about
+        // 0.6 tol^2, then 0.25 tol^4 from I: the last T moves X by about that
+        // squared); without an eps floor there is no bound: the full count
+        const bool scaled = h->cfg.newton_tol > 0.0 && h->cfg.eps_rel > 0.0 && !ch.fused;
+        std::vector<double> mu(ch.iters, 1.0);
+        int conv_steps = ch.iters;
+        if (scaled) newton_schedule(p, h->cfg.eps_rel, ch.iters, h->cfg.newton_tol, mu, conv_steps);
+        const int iters = std::min(ch.iters, conv_steps);
+        na.iters = iters;
+        auto set_step = [&](int it) {
+            g.xc1 = std::pow(mu[it], 1.0 / p) * (p + 1) / p;
+            g.xc2 = -std::pow(mu[it], 1.0 + 1.0 / p) / p;
+        };
+        set_step(0);
+        na.xc1 = g.xc1;
+        na.xc2 = g.xc2;
         // a packed chain reads the slot jobs written by k_route_compact and
         // gates its products by the slot flags
         const FactorJob* jobs = ch.compact ? at<FactorJob>(h, ch.slot_jobs_off)
                                            : tab<FactorJob>(h, ch.jobs_off);
         na.gate = ch.compact ? nullptr : gate;
-        g.gate = ch.compact ? at<int32_t>(h, h->off_slot_live) : exit32 ? na.stop : gate;
-        g.gate_val = ch.compact ? 1 : exit32 ? 0 : gate_val;
+        g.gate = ch.compact ? at<int32_t>(h, h->off_slot_live) : gate;
+        g.gate_val = ch.compact ? 1 : gate_val;
         int rc;
         if (ch.fused) {
             // lambda_max, eps, the root and the kappa estimate of every factor
@@ -1853,7 +1908,8 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
         {
             // timing scopes per launch: products, split-K sums and
             // convergence checks are separate kernel families
-            for (int it = 0; it < ch.iters; ++it) {
+            for (int it = 0; it < iters; ++it) {
+                set_step(it);
                 for (const NewtonStage& S : it == 0 ? ch.first : ch.stages[it & 1]) {
                     const GemmTask* tk = tab<GemmTask>(h, S.gemm.tasks_off);
                     const TileRef* tl = tab<TileRef>(h, S.gemm.tiles_off);
@@ -1872,27 +1928,13 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
                     }
                     if (rc) return rc;
                 }
-                // convergence checks at step counts of the full count's
-                // parity: a factor stops two steps after it meets the
-                // tolerance, with its final iterate in the buffer the finish
-                // reads
-                const int k = it + 1;
-                if (exit32 && k >= 4 && k < ch.iters && ((ch.iters - k) & 1) == 0) {
-                    ProfScope ps(h, PC_NEWTON_CONV, s);
-                    rc = hip_err(launch_newton_conv(
-                        jobs, ch.njobs, ch.ld,
-                        reinterpret_cast<const float*>(static_cast<unsigned char*>(scratch) +
-                                                       (size_t)(k & 1) * ch.ld * ch.ld * 4),
-                        diag, na, k, h->cfg.newton_tol * h->cfg.newton_tol, s));
-                    if (rc) return rc;
-                }
             }
         }
         // the final X, M sit in buffer (iters % 2) of each slot
         ProfScope ps(h, PC_NEWTON_COMMIT, s);
         rc = hip_err(launch_newton_commit(fp64, jobs, ch.njobs, ch.ld, at<float>(h, 0),
                                           static_cast<unsigned char*>(scratch) +
-                                              (size_t)(ch.iters & 1) * ch.ld * ch.ld *
+                                              (size_t)(iters & 1) * ch.ld * ch.ld *
                                                   (fp64 ? 8 : 4),
                                           diag, na, s));
         if (rc) return rc;

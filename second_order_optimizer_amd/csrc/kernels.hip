@@ -275,22 +275,39 @@ template <> struct WaveTile<float> {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
     }
+    // The operands of step kk + 2 are read from LDS before the products of
+    // step kk are issued (the scheduling groups keep that order), so a read's
+    // latency overlaps four MFMAs instead of stalling the wave.
     __device__ __forceinline__ void compute(const float* As, const float* Bs, int wm, int wn) {
         constexpr int P = BM + GemmTraits<float>::PADE;
+        constexpr int BK = GemmTraits<float>::BK;
         const int lane = threadIdx.x & 63;
         const int h = lane >> 5, c = lane & 31;
+        float a[2], b[2];
 #pragma unroll
-        for (int kk = 0; kk < GemmTraits<float>::BK; kk += 2) {
-            float a[2], b[2];
+        for (int i = 0; i < 2; ++i) a[i] = As[h * P + wm * 64 + i * 32 + c];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = As[(kk + h) * P + wm * 64 + i * 32 + c];
+        for (int j = 0; j < 2; ++j) b[j] = Bs[h * P + wn * 64 + j * 32 + c];
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
 #pragma unroll
-            for (int j = 0; j < 2; ++j) b[j] = Bs[(kk + h) * P + wn * 64 + j * 32 + c];
+        for (int kk = 0; kk < BK; kk += 2) {
+            float an[2], bn[2];
+            if (kk + 2 < BK) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) an[i] = As[(kk + 2 + h) * P + wm * 64 + i * 32 + c];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) bn[j] = Bs[(kk + 2 + h) * P + wn * 64 + j * 32 + c];
+            }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+            if (kk + 2 < BK) {
+                a[0] = an[0]; a[1] = an[1]; b[0] = bn[0]; b[1] = bn[1];
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // next step's reads
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);       // then 4 MFMAs
         }
     }
     // accumulator value idx = (2 i + j) 16 + v and its place (r, c) in the tile
@@ -338,22 +355,43 @@ template <> struct WaveTile<double> {
     }
     // the same from fp32 stages of BK = 32 (fp32 operands: each value is
     // converted to fp64 as it is read, exactly)
+    // (with the next step's operands read from LDS before this step's 16
+    // products, as in the fp32 tile)
     __device__ __forceinline__ void compute_f32(const float* As, const float* Bs, int wm, int wn) {
         constexpr int P = BM + GemmTraits<float>::PADE;
+        constexpr int BK = GemmTraits<float>::BK;
         const int lane = threadIdx.x & 63;
         const int g = lane >> 4, c = lane & 15;
+        float a[4], b[4];
 #pragma unroll
-        for (int kk = 0; kk < GemmTraits<float>::BK; kk += 4) {
-            double a[4], b[4];
+        for (int i = 0; i < 4; ++i) a[i] = As[g * P + wm * 64 + i * 16 + c];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = (double)As[(kk + g) * P + wm * 64 + i * 16 + c];
+        for (int j = 0; j < 4; ++j) b[j] = Bs[g * P + wn * 64 + j * 16 + c];
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = (double)Bs[(kk + g) * P + wn * 64 + j * 16 + c];
+        for (int kk = 0; kk < BK; kk += 4) {
+            float an[4], bn[4];
+            if (kk + 4 < BK) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) an[i] = As[(kk + 4 + g) * P + wm * 64 + i * 16 + c];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bn[j] = Bs[(kk + 4 + g) * P + wn * 64 + j * 16 + c];
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[i], (double)b[j], acc[i][j],
+                                                                     0, 0, 0);
+            if (kk + 4 < BK) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a[i] = an[i];
+                    b[i] = bn[i];
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
         }
     }
     // accumulator value idx = (4 i + j) 4 + v and its place (r, c) in the tile
@@ -378,7 +416,7 @@ template <> struct WaveTile<double> {
 template <typename T, typename TA, typename TB>
 constexpr bool kStageF32 = sizeof(T) == 8 && sizeof(TA) == 4 && sizeof(TB) == 4;
 
-template <typename T, typename TA, typename TB, bool AXPBY>
+template <typename T, typename TA, typename TB, bool AXPBY, bool XF>
 __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ tasks,
                                           const TileRef* __restrict__ tiles,
                                           const uint64_t* __restrict__ bases, const GemmArgs& args,
@@ -398,7 +436,8 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
     const TB* B = base_ptr<TB>(bases, tk.b_base, tk.b_off);
     T* C = base_ptr<T>(bases, tk.c_base, tk.c_off);
     const bool ta = tk.trans & 1, tb = (tk.trans >> 1) & 1;
-    const bool xa = (tk.trans >> 2) & 1, xb = (tk.trans >> 3) & 1;
+    // the Newton operand transform, compiled only where XF
+    const bool xa = XF && ((tk.trans >> 2) & 1), xb = XF && ((tk.trans >> 3) & 1);
     // op(A) = A: A[i][k] has k contiguous.  op(A) = A^T: A[k][i], i contiguous.
     const bool a_kc = !ta;
     // op(B)[k][j]: B^T stored B[j][k] -> k contiguous; B stored B[k][j] -> j contiguous.
@@ -495,6 +534,8 @@ __global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__
                                              const TileRef* __restrict__ tiles,
                                              const uint64_t* __restrict__ bases, GemmArgs args) {
     using S = typename std::conditional<kStageF32<T, TA, TB>, float, T>::type;
+    // only the Newton products take the operand transform
+    constexpr bool XF = ROLE == 0 && !kStageF32<T, TA, TB>;
     constexpr int BK = GemmTraits<S>::BK;
     constexpr int P = BM + GemmTraits<S>::PADE;
     __shared__ __align__(16) S As[BK * P];
@@ -512,7 +553,7 @@ __global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__
             for (int j = 0; j < C && e0 + j < args.ntiles; ++j) {
                 if (!first) __syncthreads();   // the previous tile's LDS reads and stores are done
                 first = false;
-                if (!gemm_tile<T, TA, TB, AXPBY>(e0 + j, tasks, tiles, bases, args, As, Bs, red)) {
+                if (!gemm_tile<T, TA, TB, AXPBY, XF>(e0 + j, tasks, tiles, bases, args, As, Bs, red)) {
                     live = false;
                     break;
                 }
@@ -520,7 +561,7 @@ __global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__
             if (!live) break;
         }
     } else {
-        (void)gemm_tile<T, TA, TB, AXPBY>(blockIdx.x, tasks, tiles, bases, args, As, Bs, red);
+        (void)gemm_tile<T, TA, TB, AXPBY, XF>(blockIdx.x, tasks, tiles, bases, args, As, Bs, red);
     }
 }
 
@@ -828,12 +869,12 @@ __device__ __forceinline__ void gram_quadrant(const float* Gs, int qi, int qj, i
         }
 }
 
-__global__ __launch_bounds__(512, 4) void k_gram128(const GramJob* __restrict__ jobs,
-                                                   const uint64_t* __restrict__ bases,
-                                                   double* __restrict__ stats, double alpha,
-                                                   double beta) {
-    __shared__ __align__(16) float Gs[128 * kGP];
-    const GramJob jb = jobs[blockIdx.x];
+// The statistics of one block of at most 128 x 128 on a 512-thread
+// workgroup; Gs: 128 x kGP floats of LDS.
+__device__ __forceinline__ void gram128_block(const GramJob& job, const uint64_t* __restrict__ bases,
+                                              double* __restrict__ stats, double alpha, double beta,
+                                              float* Gs) {
+    const GramJob jb = job;
     const float* G = base_ptr<const float>(bases, jb.g_base, jb.g_off);
     const int t = threadIdx.x;
     const int mb = jb.mb, nb = jb.nb, ld = jb.ldg;
@@ -882,6 +923,14 @@ __global__ __launch_bounds__(512, 4) void k_gram128(const GramJob* __restrict__ 
         case 6: gram_quadrant<false, true, 0, 2>(Gs, 0, 1, KR, R, jb.ld_r, nb, alpha, beta, c, g); break;
         default: gram_quadrant<false, true, 2, 4>(Gs, 0, 1, KR, R, jb.ld_r, nb, alpha, beta, c, g); break;
     }
+}
+
+__global__ __launch_bounds__(512, 4) void k_gram128(const GramJob* __restrict__ jobs,
+                                                   const uint64_t* __restrict__ bases,
+                                                   double* __restrict__ stats, double alpha,
+                                                   double beta) {
+    __shared__ __align__(16) float Gs[128 * kGP];
+    gram128_block(jobs[blockIdx.x], bases, stats, alpha, beta, Gs);
 }
 
 // ================================================================ Lanczos
@@ -1565,11 +1614,6 @@ __global__ __launch_bounds__(256) void k_newton_init(const FactorJob* __restrict
     if (blockIdx.x == 0 && threadIdx.x == 0) {   // the finish's check slots of this pass
         args.chk[2 * jb.factor] = 0ull;
         args.chk[2 * jb.factor + 1] = 0ull;
-        if (args.stop) {
-            args.stop[jb.factor] = 0;
-            args.conv[jb.factor] = 0;
-            args.cnt[jb.factor] = 0;
-        }
     }
     const FactorDiag dg = diag[jb.factor];
     const bool ok = dg.status == 0;
@@ -1580,7 +1624,7 @@ __global__ __launch_bounds__(256) void k_newton_init(const FactorJob* __restrict
     const double* S = stats + jb.s_off;
     T* X = scratch + jb.x_off + (int64_t)ld * ld;   // X_1, the buffer of iteration 1
     T* M = scratch + jb.m_off;
-    const T c1 = T((double)(args.p + 1) / args.p), c2 = T(-1.0 / args.p);   // as the product's loader
+    const T c1 = T(args.xc1), c2 = T(args.xc2);   // the first step's T, as the product's loader
     const int r = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 4;
     for (int tile = blockIdx.x; tile < nt * nt; tile += gridDim.x) {
         const int ti = tile / nt, tj = tile % nt;
@@ -1654,57 +1698,6 @@ __global__ __launch_bounds__(256) void k_newton_check(const FactorJob* __restric
     }
 }
 
-__global__ __launch_bounds__(256) void k_newton_conv(const FactorJob* __restrict__ jobs,
-                                                    const float* __restrict__ scratch,
-                                                    FactorDiag* __restrict__ diag, NewtonArgs args,
-                                                    int k, double tol2) {
-    __shared__ double red[4];
-    __shared__ int last;
-    const FactorJob jb = jobs[blockIdx.y];
-    const int f = jb.factor;
-    if (f < 0 || args.stop[f]) return;
-    if (diag[f].status & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_ZERO_)) return;
-    if (args.conv[f] != 0 && args.conv[f] < k) {   // met the tolerance two steps ago
-        if (blockIdx.x == 0 && threadIdx.x == 0) {
-            args.stop[f] = 1;
-            diag[f].iters = k;
-        }
-        return;
-    }
-    const int n = jb.n, ld = jb.ld;
-    const float* M = scratch + jb.m_off;
-    // rows of n in 16-byte pieces (ld is a multiple of 32; the piece that
-    // crosses column n is masked), split into gridDim.x contiguous ranges
-    const int pr = (n + 3) >> 2, total = n * pr;
-    const int per = (total + gridDim.x - 1) / gridDim.x;
-    const int e0 = blockIdx.x * per, e1 = min(total, e0 + per);
-    double acc = 0.0;
-    for (int e = e0 + threadIdx.x; e < e1; e += 256) {
-        const int i = e / pr, j0 = 4 * (e - i * pr);
-        const float4 v = *reinterpret_cast<const float4*>(M + (int64_t)i * ld + j0);
-        const float q[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const double d = (j0 + u < n) ? double(q[u]) - (i == j0 + u ? 1.0 : 0.0) : 0.0;
-            acc = fma(d, d, acc);
-        }
-    }
-    acc = block_sum_256(acc, red);
-    if (threadIdx.x == 0) {
-        args.part[32 * f + blockIdx.x] = acc;
-        __threadfence();
-        last = atomicAdd(&args.cnt[f], 1) == (int)gridDim.x - 1;
-    }
-    __syncthreads();
-    if (!last || threadIdx.x != 0) return;
-    __threadfence();
-    double sum = 0.0;
-    for (int q = 0; q < (int)gridDim.x; ++q)   // fixed order: a deterministic decision
-        sum += __hip_atomic_load(&args.part[32 * f + q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    args.cnt[f] = 0;
-    if (sum < tol2) args.conv[f] = k;          // NaN: keeps running
-}
-
 // Finish, part 2 (same sharing of tiles): unless the factor's input or iterate went
 // non-finite (then its previous root stays), the root is the symmetric part
 // of X (the tile and its mirror, transposed in LDS), the identity for a
@@ -1733,7 +1726,7 @@ __global__ __launch_bounds__(256) void k_newton_commit(const FactorJob* __restri
         else st &= ~SHAMPOO_FACTOR_FP64_;
         dg.status = st;
         dg.residual = res;
-        if (!(args.stop && args.stop[jb.factor])) dg.iters = st0 == 0 ? args.iters : 0;
+        dg.iters = st0 == 0 ? args.iters : 0;
     }
     if (keep) return;
     const bool ident = (st & SHAMPOO_FACTOR_ZERO_) != 0;
@@ -2104,14 +2097,13 @@ __global__ __launch_bounds__(256, 2) void k_newton128(const FactorJob* __restric
 //     symmetric, so this is P_L itself -- again streamed with prefetch;
 //  4. ||D||^2, then D written in the tensor's layout, or (fuse) the graft,
 //     momentum and weight update applied in place from D staged in LDS.
-__global__ __launch_bounds__(512, 4) void k_apply128(const ApplyJob* __restrict__ jobs,
-                                                    const uint64_t* __restrict__ bases,
-                                                    float* __restrict__ arena, float delta,
-                                                    double* __restrict__ partA,
-                                                    double* __restrict__ partD, UpdateArgs ua) {
-    __shared__ __align__(16) float Sl[128 * kNP];
-    __shared__ double red[8];
-    const ApplyJob jb = jobs[blockIdx.x];
+// Apply, graft and update of one block of at most 128 x 128 on a 512-thread
+// workgroup; Sl: 128 x kNP floats of LDS, red: 8 doubles.
+__device__ __forceinline__ void apply128_block(const ApplyJob& job, const uint64_t* __restrict__ bases,
+                                               float* __restrict__ arena, float delta,
+                                               double* __restrict__ partA, double* __restrict__ partD,
+                                               const UpdateArgs& ua, float* Sl, double* red) {
+    const ApplyJob jb = job;
     const float* G = base_ptr<const float>(bases, jb.g_base, jb.g_off);
     float* a = arena + jb.a_off;
     const int mb = jb.mb, nb = jb.nb, ld = jb.ldg;
@@ -2339,6 +2331,16 @@ __global__ __launch_bounds__(512, 4) void k_apply128(const ApplyJob* __restrict_
                 if (i < mb && j < nb) Dg[(int64_t)i * ld + j] = dacc[q][v];
             }
     }
+}
+
+__global__ __launch_bounds__(512, 4) void k_apply128(const ApplyJob* __restrict__ jobs,
+                                                    const uint64_t* __restrict__ bases,
+                                                    float* __restrict__ arena, float delta,
+                                                    double* __restrict__ partA,
+                                                    double* __restrict__ partD, UpdateArgs ua) {
+    __shared__ __align__(16) float Sl[128 * kNP];
+    __shared__ double red[8];
+    apply128_block(jobs[blockIdx.x], bases, arena, delta, partA, partD, ua, Sl, red);
 }
 
 // ------------------------------------------------ fused step, blocks <= 128
@@ -3205,19 +3207,6 @@ hipError_t launch_route_compact(const CompactClass* cls, int ncls, const FactorJ
     if (ncls <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_route_compact, dim3(ncls), dim3(1024), 0, s, cls, tmpl, prec, gate_val, slots,
                        live);
-    return hipGetLastError();
-}
-hipError_t launch_newton_conv(const FactorJob* jobs, int njobs, int ld, const float* scratch,
-                              FactorDiag* diag, const NewtonArgs& a, int k, double tol2,
-                              hipStream_t s) {
-    if (njobs <= 0) return hipSuccess;
-    if (!a.stop || !a.conv || !a.cnt || !a.part || ld < 1) return hipErrorInvalidValue;
-    // at least 64 KB of M per workgroup, at most 32 per factor, and about
-    // 2048 workgroups in all (a chunk of many factors needs no split)
-    const int parts = std::max(1, std::min({32, (int)(((int64_t)ld * ld + 16383) / 16384),
-                                            (2048 + njobs - 1) / njobs}));
-    hipLaunchKernelGGL(k_newton_conv, dim3(parts, njobs), dim3(256), 0, s, jobs, scratch, diag, a, k,
-                       tol2);
     return hipGetLastError();
 }
 

@@ -101,6 +101,34 @@ def make_oracle(wl, ids, **over):
     return O.ShampooOracle(oracle_config(wl, **over), shapes, W0)
 
 
+def newton_scaling(p, eps_rel, n, tau=1e-3):
+    """The scaled coupled-Newton schedule by its definition: the interval
+    [lo, hi] that holds the spectrum of M_0 = z A (lo = (p+1)/2 eps_rel /
+    (1 + eps_rel), hi = (p+1)/2 * 1.01) is carried through the scalar map
+    f(m) = m ((p+1-m)/p)^p; while lo < 1/2 the step scales M by the largest mu
+    with mu hi <= 0.7 (p+1) and f(mu lo) <= f(mu hi), else by 1.  Returns the
+    n scalings and the step count of the batched chains: the first k at which
+    the interval of M_k lies within tau (newton_tol) of 1, plus two steps (at
+    most n)."""
+    from scipy.optimize import brentq
+    f = lambda m: m * ((p + 1 - m) / p) ** p
+    lo, hi = 0.5 * (p + 1) * eps_rel / (1 + eps_rel), 0.5 * (p + 1) * 1.01
+    mus, conv = [], n
+    for k in range(n):
+        if conv == n and max(1 - lo, hi - 1) <= tau:
+            conv = min(n, k + 2)
+        if lo >= 0.5:
+            mu = 1.0
+        else:
+            top = 0.7 * (p + 1) / hi
+            g = lambda c: f(c * lo) - f(c * hi)
+            mu = top if g(top) <= 0 else max(brentq(g, 1.0 / hi, top, xtol=1e-15), 1.0)
+        mus.append(mu)
+        a, b = f(mu * lo), f(mu * hi)
+        lo, hi = min(a, b), (1.0 if mu * lo <= 1.0 <= mu * hi else max(a, b))
+    return mus, conv
+
+
 def newton_steps(eigs, lam_max, eps, p, tol, cap):
     """Steps the coupled Newton iteration runs in exact arithmetic when it
     stops one step after ||M_k - I||_F < tol (at most cap).  M_k is a
@@ -113,18 +141,4 @@ def newton_steps(eigs, lam_max, eps, p, tol, cap):
         m = m * ((p + 1 - m) / p) ** p
         if np.sqrt(np.sum((m - 1.0) ** 2)) < tol:     # ||M_k - I||_F
             return min(k + 1, cap)
-    return cap
-
-
-def newton_steps_checked(eigs, lam_max, eps, p, tol, cap, first=4):
-    """The batched chain's rule in exact arithmetic: ||M_k - I||_F is checked
-    only at step counts k >= first of the parity of cap, and the factor
-    stops two steps after the first check that meets tol (at most cap)."""
-    import numpy as np
-    m = (p + 1) / (2.0 * (lam_max + eps)) * (np.asarray(eigs, dtype=np.float64) + eps)
-    for k in range(1, cap + 1):
-        m = m * ((p + 1 - m) / p) ** p
-        if k >= first and k < cap and (cap - k) % 2 == 0 and \
-                np.sqrt(np.sum((m - 1.0) ** 2)) < tol:
-            return min(k + 2, cap)
     return cap

@@ -279,7 +279,7 @@ def test_newton_step_count_model(p):
     norm ||M_k - I||_F the scalar eigenvalue map gives (the norm is unitarily
     invariant), so it stops at the model's step; the root it leaves is
     within the bound the exit rule implies."""
-    from harness import newton_steps, newton_steps_checked
+    from harness import newton_steps
     rng = np.random.default_rng(7)
     for kappa in (10.0, 1e3, 1e5):
         n = 24
@@ -303,20 +303,6 @@ def test_newton_step_count_model(p):
                 break
             stop = d_dense < 1e-3
         assert dense_steps == newton_steps(lam, 1.0, 0.0, p, 1e-3, 40), (p, kappa)
-        # the batched chain's rule: checks only at step counts k >= 4 of the
-        # parity of the full count (cap), a stop two steps after the first
-        # check that meets the tolerance; from the same dense iteration
-        for cap in (20, 23):
-            Xc, Mc = z ** (1.0 / p) * np.eye(n), z * A
-            checked = cap
-            for k in range(1, cap + 1):
-                Tc = ((p + 1) * np.eye(n) - Mc) / p
-                Xc, Mc = Xc @ Tc, np.linalg.matrix_power(Tc, p) @ Mc
-                if 4 <= k < cap and (cap - k) % 2 == 0 and np.linalg.norm(Mc - np.eye(n)) < 1e-3:
-                    checked = min(k + 2, cap)
-                    break
-            assert checked == newton_steps_checked(lam, 1.0, 0.0, p, 1e-3, cap), (p, kappa, cap)
-            assert (checked - cap) % 2 == 0   # the finish's buffer parity
         # one step after ||M - I||_F < 1e-3 the spectral error is at most about
         # (p+1)/(2p) 1e-6, and the root's relative error about that over p
         # the stopped iterate is the root to about the map's last residual
@@ -325,3 +311,51 @@ def test_newton_step_count_model(p):
     if p == 4:
         assert [newton_steps(np.logspace(-e, 0, 50), 1.0, 0.0, 4, 1e-3, 40)
                 for e in (1, 3, 5)] == [6, 11, 16]
+
+
+@pytest.mark.parametrize("p", [1, 2, 4, 8])
+def test_scaled_newton_model(p):
+    """The scaled steps the batched chains take with a convergence exit: a
+    dense fp64 coupled Newton iteration that scales M by mu_k and X by
+    mu_k^(1/p) before each step keeps M_k = X_k^p A, its ||M_k - I||_F follows
+    the scalar map with the same scalings step by step, and after the
+    schedule's count (its interval bound within 1e-3 of 1, plus two steps) the
+    root is exact to rounding, also at the worst conditioning the eps floor
+    allows (an eigenvalue of S at 0: kappa = 1 + 1/eps_rel).  The count is
+    well below the unscaled iteration's, and the bound holds: every scaled
+    eigenvalue stays inside the interval."""
+    from harness import newton_scaling
+    eps_rel = 1e-6
+    n_full = {1: 26, 2: 23, 4: 20, 8: 20}[p]
+    mus, conv = newton_scaling(p, eps_rel, n_full)
+    assert conv < n_full and all(m >= 1.0 for m in mus)
+    assert conv == {1: 19, 2: 14, 4: 11, 8: 10}[p], conv
+    rng = np.random.default_rng(11)
+    n = 32
+    for spec in ("floor", "log3", "flat"):
+        if spec == "floor":
+            lam_s = np.concatenate([[0.0], np.logspace(-6, 0, n - 1)])
+        elif spec == "log3":
+            lam_s = np.logspace(-3, 0, n)
+        else:
+            lam_s = np.full(n, 0.5)
+        q, _ = np.linalg.qr(rng.standard_normal((n, n)))
+        lmax = lam_s.max()
+        eps = eps_rel * lmax
+        lam = lam_s + eps
+        A = (q * lam) @ q.T
+        z = (p + 1) / (2.0 * lmax * (1 + eps_rel))
+        X, M = z ** (1.0 / p) * np.eye(n), z * A
+        m = z * lam
+        for k in range(conv):
+            mu = mus[k]
+            T = ((p + 1) * np.eye(n) - mu * M) / p
+            X = mu ** (1.0 / p) * X @ T
+            M = np.linalg.matrix_power(T, p) @ (mu * M)
+            m = mu * m * ((p + 1 - mu * m) / p) ** p
+            assert abs(np.linalg.norm(M - np.eye(n)) - np.sqrt(np.sum((m - 1) ** 2))) <= \
+                1e-9 * max(1.0, np.sqrt(np.sum((m - 1) ** 2))), (p, spec, k)
+            assert np.all(m > 0) and np.all(m < p + 1), (p, spec, k)
+        ref = (q * lam ** (-1.0 / p)) @ q.T
+        err = np.linalg.norm(X - ref) / np.linalg.norm(ref)
+        assert err < 1e-9, (p, spec, err)   # fp64 rounding: up to about kappa^(1/p) u
