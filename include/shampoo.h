@@ -150,7 +150,8 @@ typedef struct {
     double lambda_max;   /* Krylov estimate of the largest eigenvalue of S           */
     double eps;          /* eps_rel * lambda_max: the damping added to S              */
     double kappa_est;    /* estimate of kappa(S + eps I) from the fp32 root (0: none) */
-    double residual;     /* max |M_N - I| of the coupled iteration that was committed */
+    double residual;     /* max |M - I| of the committed coupled iteration's last M
+                            (the batched chains form no M in their last step: M_{N-1}) */
     int32_t block;       /* block index (see shampoo_block_info)                      */
     int32_t side;        /* 0: L (rows), 1: R (columns)                               */
     int32_t dim;         /* factor dimension                                          */

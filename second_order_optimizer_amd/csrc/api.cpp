@@ -105,6 +105,7 @@ struct NewtonChunk {
     int64_t slot_jobs_off = 0;               // are written on the device (arena bytes)
     std::vector<NewtonStage> stages[2];      // per parity
     std::vector<NewtonStage> first;          // iteration 0 (the start forms X_1)
+    std::vector<NewtonStage> last[2];        // the last iteration: X T only (per parity)
 };
 
 // The launches of one root pass over a set of factors.
@@ -568,6 +569,12 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
             st[k].push_back(mk(cur, Mq, Mn, 16 | 32, fid));
         }
         emit(st, ch.stages[q]);
+        {
+            // the last iteration's M is not needed: its X T products alone
+            std::vector<std::vector<GemmTask>> stl(1);
+            for (size_t i = 0; i < st[0].size(); i += 2) stl[0].push_back(st[0][i]);
+            emit(stl, ch.last[q]);
+        }
         if (q == 0) {
             // iteration 0 without X T: X_0 is diagonal, and the start writes
             // X_1 = X_0 T(M_0) itself (stage 0 holds X T and one more product
@@ -1908,9 +1915,15 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
         {
             // timing scopes per launch: products, split-K sums and
             // convergence checks are separate kernel families
+            static const std::vector<NewtonStage> kNone;
             for (int it = 0; it < iters; ++it) {
                 set_step(it);
-                for (const NewtonStage& S : it == 0 ? ch.first : ch.stages[it & 1]) {
+                // the last step forms X only (M_iters is never read); a single
+                // step is the start's X_1 alone
+                const bool last = it == iters - 1;
+                const std::vector<NewtonStage>& stg =
+                    it == 0 ? (last ? kNone : ch.first) : (last ? ch.last[it & 1] : ch.stages[it & 1]);
+                for (const NewtonStage& S : stg) {
                     const GemmTask* tk = tab<GemmTask>(h, S.gemm.tasks_off);
                     const TileRef* tl = tab<TileRef>(h, S.gemm.tiles_off);
                     g.persist = (fp64 && S.sorted) ? kPersistGrid : 0;
@@ -1930,12 +1943,14 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
                 }
             }
         }
-        // the final X, M sit in buffer (iters % 2) of each slot
+        // the final X sits in buffer (iters % 2) of each slot, the last M
+        // formed (M_{iters-1}, from which the last T came) in the other
         ProfScope ps(h, PC_NEWTON_COMMIT, s);
+        const size_t mat_bytes = (size_t)ch.ld * ch.ld * (fp64 ? 8 : 4);
         rc = hip_err(launch_newton_commit(fp64, jobs, ch.njobs, ch.ld, at<float>(h, 0),
+                                          static_cast<unsigned char*>(scratch) + (size_t)(iters & 1) * mat_bytes,
                                           static_cast<unsigned char*>(scratch) +
-                                              (size_t)(iters & 1) * ch.ld * ch.ld *
-                                                  (fp64 ? 8 : 4),
+                                              (size_t)((iters - 1) & 1) * mat_bytes,
                                           diag, na, s));
         if (rc) return rc;
     }

@@ -447,7 +447,8 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
     const bool b_al = ((reinterpret_cast<uintptr_t>(B) % (VEC * sizeof(TB))) == 0) && (tk.ldb % VEC == 0);
     const S c1 = S(args.xc1), c2 = S(args.xc2);
 
-    const int w = threadIdx.x >> 6;
+    // the wave index as a scalar: branches on it are uniform to the compiler
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = w >> 1, wn = w & 1;
     WaveTile<T> wt;
     wt.zero();
@@ -1658,13 +1659,15 @@ __global__ __launch_bounds__(256) void k_newton_init(const FactorJob* __restrict
     }
 }
 
-// Finish, part 1 (same sharing of tiles): max |M - I| and whether X or M went
+// Finish, part 1 (same sharing of tiles): max |M - I| of the last M formed
+// (the one the last T came from) and whether X or M went
 // non-finite, over the real n x n part, into the factor's check slots
 // (atomic max of the bit patterns of non-negative doubles, which order like
 // the values, so the result does not depend on the order).
 template <typename T>
 __global__ __launch_bounds__(256) void k_newton_check(const FactorJob* __restrict__ jobs,
                                                      const T* __restrict__ scratch,
+                                                     const T* __restrict__ scratch_m,
                                                      const FactorDiag* __restrict__ diag,
                                                      NewtonArgs args) {
     __shared__ double red[4];
@@ -1673,7 +1676,7 @@ __global__ __launch_bounds__(256) void k_newton_check(const FactorJob* __restric
     if (diag[jb.factor].status & (SHAMPOO_FACTOR_NONFINITE_INPUT_ | SHAMPOO_FACTOR_ZERO_)) return;
     const int n = jb.n, ld = jb.ld, nt = ld >> 5;
     const T* X = scratch + jb.x_off;
-    const T* M = scratch + jb.m_off;
+    const T* M = scratch_m + jb.m_off;
     const int r = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 4;
     double res = 0.0, bad = 0.0;
     for (int tile = blockIdx.x; tile < nt * nt; tile += gridDim.x) {
@@ -3226,20 +3229,22 @@ hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, int l
     return hipGetLastError();
 }
 hipError_t launch_newton_commit(bool fp64, const FactorJob* jobs, int njobs, int ld, float* arena,
-                                const void* scratch, FactorDiag* diag, const NewtonArgs& a,
-                                hipStream_t s) {
+                                const void* scratch, const void* scratch_m, FactorDiag* diag,
+                                const NewtonArgs& a, hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
     // one workgroup per tile; factors up to 128 (chunks of the gated fp64
     // chain, where most factors exit at once) one workgroup per factor
     const dim3 grid(ld <= 128 ? 1 : (ld / 32) * (ld / 32), njobs);
     if (fp64) {
         hipLaunchKernelGGL(k_newton_check<double>, grid, dim3(256), 0, s, jobs,
-                           static_cast<const double*>(scratch), diag, a);
+                           static_cast<const double*>(scratch), static_cast<const double*>(scratch_m),
+                           diag, a);
         hipLaunchKernelGGL(k_newton_commit<double>, grid, dim3(256), 0, s, jobs, arena,
                            static_cast<const double*>(scratch), diag, a);
     } else {
         hipLaunchKernelGGL(k_newton_check<float>, grid, dim3(256), 0, s, jobs,
-                           static_cast<const float*>(scratch), diag, a);
+                           static_cast<const float*>(scratch), static_cast<const float*>(scratch_m),
+                           diag, a);
         hipLaunchKernelGGL(k_newton_commit<float>, grid, dim3(256), 0, s, jobs, arena,
                            static_cast<const float*>(scratch), diag, a);
     }

@@ -124,13 +124,14 @@ hipError_t launch_route_compact(const CompactClass* cls, int ncls, const FactorJ
                                 const int32_t* prec, int gate_val, FactorJob* slots, int32_t* live,
                                 hipStream_t s);
 // Newton start and finish, one workgroup per 32 x 32 tile of every factor of
-// a chunk (factors of leading dimension ld).
+// a chunk (factors of leading dimension ld).  The finish takes X from the
+// buffer set at `scratch` and the last M formed from the one at `scratch_m`.
 hipError_t launch_newton_init(bool fp64, const FactorJob* jobs, int njobs, int ld,
                               const double* stats, void* scratch, const FactorDiag* diag,
                               const NewtonArgs& a, hipStream_t s);
 hipError_t launch_newton_commit(bool fp64, const FactorJob* jobs, int njobs, int ld, float* arena,
-                                const void* scratch, FactorDiag* diag, const NewtonArgs& a,
-                                hipStream_t s);
+                                const void* scratch, const void* scratch_m, FactorDiag* diag,
+                                const NewtonArgs& a, hipStream_t s);
 hipError_t launch_newton128(const FactorJob* jobs, int njobs, const double* stats, float* arena,
                             FactorDiag* diag, int32_t* prec, const FusedArgs& a, hipStream_t s);
 hipError_t launch_apply128(const ApplyJob* jobs, int njobs, const uint64_t* bases, float* arena,
