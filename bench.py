@@ -97,10 +97,14 @@ def newton_products(p):
     return 2 if p == 1 else 2 + int(round(math.log2(p)))
 
 
-def newton_flops(n, p, iters):
+def newton_flops(n, p, iters, batched):
     """One n x n root of `iters` steps.  X, M and T are polynomials in the
     same matrix, so every product is symmetric (counted on its triangle);
-    X_0 is diagonal, so the first X T is a row scaling and not a product."""
+    X_0 is diagonal, so the first X T is a row scaling and not a product.  The
+    batched chains form only X in their last step (that step's M is never
+    read)."""
+    if batched:
+        return newton_products(p) * sym(n, n) * max(iters - 1, 0)
     return newton_products(p) * sym(n, n) * iters - sym(n, n)
 
 
@@ -414,17 +418,20 @@ def run_pass(wl, args, tol, pool, dev, peaks):
 
     stages = {}
     fdims = factor_dims(opt, wl.root_p)
-    # the steps each root ran in the last pass (fp32 roots with a tolerance
-    # stop at convergence; fp64 roots run the full count)
-    fl = [newton_flops(n, p, d.iters) if d.iters > 0 else 0.0 for (n, p), d in zip(fdims, diag)]
+    # the steps each root ran in the last pass (with a tolerance the fused
+    # fp32 roots stop at convergence and the batched chains run the count of
+    # their scaled steps' bound)
+    fl = [newton_flops(n, p, d.iters, n > 128 or bool(d.status & S.FACTOR_FP64)) if d.iters > 0
+          else 0.0 for (n, p), d in zip(fdims, diag)]
     iters32 = {"fused": [d.iters for (n, _), d in zip(fdims, diag)
                          if n <= 128 and d.iters > 0 and not d.status & S.FACTOR_FP64],
                "chain": [d.iters for (n, _), d in zip(fdims, diag)
-                         if n > 128 and d.iters > 0 and not d.status & S.FACTOR_FP64]}
+                         if n > 128 and d.iters > 0 and not d.status & S.FACTOR_FP64],
+               "fp64": [d.iters for d in diag if d.iters > 0 and d.status & S.FACTOR_FP64]}
     f32 = wl.root_mode != "f64"
     # in AUTO mode the fp32 iteration runs on every factor first and the
     # routed ones are redone in fp64; a routed factor's fp32 steps are not
-    # recorded, so it counts at the steps of its fp64 root (the full count)
+    # recorded, so it counts at the steps of its fp64 root
     flops_fused_root = sum(x for x, (n, _) in zip(fl, fdims) if f32 and n <= 128)
     flops_f32_root = sum(x for x, (n, _) in zip(fl, fdims) if f32 and n > 128)
     flops_f64_root = sum(x for x, d in zip(fl, diag) if d.status & S.FACTOR_FP64)
@@ -556,7 +563,7 @@ def run_pass(wl, args, tol, pool, dev, peaks):
         "value": value, "ms_per_step": ms_step, "steps_per_s": steps_per_s,
         "newton_tol": tol, "inv_root_blocks_per_s": inv_root_blocks_per_s,
         "root_passes_timed": n_root_passes, "fp64_factor_share_last_pass": n64 / max(len(diag), 1),
-        "fp32_root_steps_last_pass": {k: ({"mean": sum(v) / len(v), "min": min(v), "max": max(v),
+        "root_steps_last_pass": {k: ({"mean": sum(v) / len(v), "min": min(v), "max": max(v),
                                            "factors": len(v)} if v else None)
                                       for k, v in iters32.items()},
         "mfma_pct": mfma_pct, "stages": stages, "roofline": roofline, "wall_s_timed": wall,
@@ -686,7 +693,7 @@ def main():
         "inv_root_blocks_per_s": main_pass["inv_root_blocks_per_s"],
         "root_passes_timed": main_pass["root_passes_timed"],
         "fp64_factor_share_last_pass": main_pass["fp64_factor_share_last_pass"],
-        "fp32_root_steps_last_pass": main_pass["fp32_root_steps_last_pass"],
+        "root_steps_last_pass": main_pass["root_steps_last_pass"],
         "mfma_pct": main_pass["mfma_pct"],
         "stages": main_pass["stages"],
         "roofline": main_pass["roofline"],
@@ -701,7 +708,7 @@ def main():
         out["full_iteration_count"] = {
             k: full[k] for k in ("value", "ms_per_step", "steps_per_s", "newton_tol",
                                  "inv_root_blocks_per_s", "fp64_factor_share_last_pass",
-                                 "fp32_root_steps_last_pass", "roofline", "mfma_pct")}
+                                 "root_steps_last_pass", "roofline", "mfma_pct")}
         out["full_iteration_count"]["stages_ms_per_step"] = {
             k: v["ms_per_step"] for k, v in full["stages"].items()}
     if not args.no_cpu_baseline:
@@ -765,8 +772,7 @@ FAMILY_OF = [
     ("k_gemm<float, float, float, 1, false, false, 2>", "apply_gemm_d", "f32"),
     ("k_gemm_nt3<true>", "apply_gemm_t", "bf16"),
     ("k_gemm_nt3<false>", "apply_gemm_d", "bf16"),
-    ("k_gemm<float, float, float, 1, false, false, 0>", "newton_gemm_f32", "f32"),
-    ("k_gemm<float, float, float, 1, false, false>", "newton_gemm_f32", "f32"),
+    ("k_gemm<float, float, float, 3, false, false", "newton_gemm_f32", "f32"),
     ("k_gemm<double, double, double, 2", "newton_gemm_f64", "f64"),
     ("k_adagrad_norm", "adagrad_norm", None),
     ("k_update", "update", None),

@@ -126,14 +126,22 @@ typedef struct {
     double eps_rel;           /* eps = eps_rel * lambda_max(S) per factor                */
     double graft_eps;         /* delta in A = G / (sqrt(a) + delta)                      */
     double fp64_cond_threshold; /* AUTO mode: kappa(S + eps I) above this -> fp64 root  */
-    double newton_tol;        /* 0 = every root runs its full iteration count.  In [0, 1):
-                                 an fp32 root stops once ||M_k - I||_F has fallen below
-                                 newton_tol (the coupled iteration's convergence test;
-                                 near I the error squares each step), at most the full
-                                 count: a factor up to 128 one step after, a larger one
-                                 (batched chain, checked at step counts of the full
-                                 count's parity from 4 on) two steps after.  fp64 roots
-                                 always run the full count.  E.g. 1e-3                   */
+    double newton_tol;        /* 0 = every root runs its full iteration count, the
+                                 plain coupled iteration.  In (0, 1): the iteration stops
+                                 once M_k is within newton_tol of I (its convergence
+                                 test; near I the error squares each step), at most the
+                                 full count.  An fp32 root of a factor up to 128 (fused
+                                 kernel) stops one step after ||M_k - I||_F < newton_tol.
+                                 The batched chains (fp32 above 128, every fp64 root)
+                                 take scaled steps (M_k scaled by mu_k, X_k by
+                                 mu_k^(1/p), mu_k chosen from a bound on the spectrum of
+                                 M_k that the eps floor gives, the same for every factor)
+                                 and run one step (fp32) or two (fp64) past the first
+                                 step count at which that bound puts every eigenvalue
+                                 of M_k within newton_tol of 1 (10 and 11 steps at
+                                 p = 4, eps_rel 1e-6, newton_tol 1e-3); the last step
+                                 forms X only.  With
+                                 eps_rel = 0 there is no bound: the full count.  E.g. 1e-3 */
 } shampoo_config;
 
 /* Row-sparse gradient of one SHAMPOO_SPARSE_ROWS table: n_rows distinct row

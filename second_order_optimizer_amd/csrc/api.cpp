@@ -393,10 +393,10 @@ int newton_iters_for(const shampoo_config& c, int p) {
 // and f(mu lo) <= f(mu hi) (the bottom's image is the new lower end), until lo
 // reaches 1/2, and 1 after that.  mu is the same for every factor (it
 // depends on p and eps_rel only), and so is the step count: conv_steps is the
-// first k at which the interval of M_k lies within tau of 1, plus two steps
-// (at most iters).
-void newton_schedule(int p, double eps_rel, int iters, double tau, std::vector<double>& mu,
-                     int& conv_steps) {
+// first k at which the interval of M_k lies within tau of 1, plus `extra`
+// steps (at most iters).
+void newton_schedule(int p, double eps_rel, int iters, double tau, int extra,
+                     std::vector<double>& mu, int& conv_steps) {
     auto f = [p](double m) { return m * std::pow((p + 1 - m) / p, p); };
     double lo = 0.5 * (p + 1) * eps_rel / (1.0 + eps_rel), hi = 0.5 * (p + 1) * 1.01;
     const double cap = 0.7 * (p + 1);
@@ -405,7 +405,7 @@ void newton_schedule(int p, double eps_rel, int iters, double tau, std::vector<d
     bool found = false;
     for (int k = 0; k < iters; ++k) {
         if (!found && std::max(1.0 - lo, hi - 1.0) <= tau) {
-            conv_steps = std::min(iters, k + 2);
+            conv_steps = std::min(iters, k + extra);
             found = true;
         }
         double m = 1.0;
@@ -1860,14 +1860,17 @@ int run_newton(shampoo_s* h, std::vector<NewtonChunk>& chunks, bool fp64, const 
         const int p = ch.p;
         na.p = p;
         // with a convergence exit (newton_tol > 0) the chain takes the scaled
-        // steps and stops two steps after the one where every eigenvalue of
-        // M is within newton_tol of 1 by the schedule's bound (about
-        // 0.6 tol^2, then 0.25 tol^4 from I: the last T moves X by about that
-        // squared); without an eps floor there is no bound: the full count
+        // steps and stops after the one where every eigenvalue of M is within
+        // newton_tol of 1 by the schedule's bound: one step after in fp32
+        // (the error is then about (p+1)/(2p) tol^2, 6e-7 for 1e-3, and the
+        // root's about that over p, at fp32 rounding), two in fp64 (about
+        // 0.24 tol^4); without an eps floor there is no bound: the full count
         const bool scaled = h->cfg.newton_tol > 0.0 && h->cfg.eps_rel > 0.0 && !ch.fused;
         std::vector<double> mu(ch.iters, 1.0);
         int conv_steps = ch.iters;
-        if (scaled) newton_schedule(p, h->cfg.eps_rel, ch.iters, h->cfg.newton_tol, mu, conv_steps);
+        if (scaled)
+            newton_schedule(p, h->cfg.eps_rel, ch.iters, h->cfg.newton_tol, fp64 ? 2 : 1, mu,
+                            conv_steps);
         const int iters = std::min(ch.iters, conv_steps);
         na.iters = iters;
         auto set_step = [&](int it) {

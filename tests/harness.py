@@ -101,22 +101,22 @@ def make_oracle(wl, ids, **over):
     return O.ShampooOracle(oracle_config(wl, **over), shapes, W0)
 
 
-def newton_scaling(p, eps_rel, n, tau=1e-3):
+def newton_scaling(p, eps_rel, n, tau=1e-3, extra=2):
     """The scaled coupled-Newton schedule by its definition: the interval
     [lo, hi] that holds the spectrum of M_0 = z A (lo = (p+1)/2 eps_rel /
     (1 + eps_rel), hi = (p+1)/2 * 1.01) is carried through the scalar map
     f(m) = m ((p+1-m)/p)^p; while lo < 1/2 the step scales M by the largest mu
     with mu hi <= 0.7 (p+1) and f(mu lo) <= f(mu hi), else by 1.  Returns the
     n scalings and the step count of the batched chains: the first k at which
-    the interval of M_k lies within tau (newton_tol) of 1, plus two steps (at
-    most n)."""
+    the interval of M_k lies within tau (newton_tol) of 1, plus `extra` steps
+    (the fp32 chain 1, the fp64 chain 2; at most n)."""
     from scipy.optimize import brentq
     f = lambda m: m * ((p + 1 - m) / p) ** p
     lo, hi = 0.5 * (p + 1) * eps_rel / (1 + eps_rel), 0.5 * (p + 1) * 1.01
     mus, conv = [], n
     for k in range(n):
         if conv == n and max(1 - lo, hi - 1) <= tau:
-            conv = min(n, k + 2)
+            conv = min(n, k + extra)
         if lo >= 0.5:
             mu = 1.0
         else:

@@ -440,14 +440,15 @@ def test_newton_convergence_exit(tol):
     counts = {"fused": [], "batched": [], "fp64": []}
     # with the exit the batched chains (fp32 above 128, every fp64 factor)
     # take the scaled steps, as many as the schedule's bound needs
-    _, conv = newton_scaling(wl.root_p, wl.eps_rel, wl.newton_iters, tol)
+    _, conv32 = newton_scaling(wl.root_p, wl.eps_rel, wl.newton_iters, tol, extra=1)
+    _, conv64 = newton_scaling(wl.root_p, wl.eps_rel, wl.newton_iters, tol, extra=2)
     for b in range(run.opt.n_blocks):
         bl = run.opt.block(b)
         for S, f in zip(run.opt.stats(b), (bl.factor_l, bl.factor_r)):
             d = diag[f]
             fused = d.dim <= 128 and not d.status & FP64
             if tol == 0.0 or not fused:
-                want = conv if tol > 0.0 else wl.newton_iters
+                want = (conv64 if d.status & FP64 else conv32) if tol > 0.0 else wl.newton_iters
                 assert d.iters == want, (b, f, d.dim, d.iters, d.status, want)
                 counts["fp64" if d.status & FP64 else "batched"].append(d.iters)
                 continue
