@@ -133,11 +133,11 @@ struct StageLoader {
     static constexpr int VEC = GemmTraits<T>::VEC;
     typedef TI vec_t __attribute__((ext_vector_type(VEC)));
     T v[4][VEC];
+    int t;   // thread index (set per tile: see gemm_tile)
 
     __device__ __forceinline__ void load(const TI* __restrict__ X, int ld, bool kcontig,
                                          int r0, int k0, int R, int K, bool aligned,
                                          bool xf, T c1, T c2, int dk) {
-        const int t = threadIdx.x;
         // uniform over the workgroup: the whole stage is in range (no checks),
         // and whether it meets the diagonal r == k
         const bool full = aligned && r0 + BM <= R && k0 + BK <= K;
@@ -236,7 +236,6 @@ struct StageLoader {
     // LDS layout: S[k][r] with row pitch 128 + PADE (r contiguous).
     __device__ __forceinline__ void store(T* S, bool kcontig) const {
         constexpr int P = BM + GemmTraits<T>::PADE;
-        const int t = threadIdx.x;
         if (kcontig) {
             const int kq = t & 7, rr = t >> 3;
 #pragma unroll
@@ -318,6 +317,26 @@ template <> struct WaveTile<float> {
         r = wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         c = wn * 64 + j * 32 + (lane & 31);
         return acc[i][j][v];
+    }
+    // alpha times the wave's sub-tile, transposed, at Ct (Ct[c * ldc + r]):
+    // registers v = 4q .. 4q + 3 of a lane are four consecutive rows r, so
+    // each lane stores 16 bytes per group (one row of the transpose)
+    __device__ __forceinline__ void store_transposed(float* Ct, int ldc, int wm, int wn,
+                                                     float alpha) const {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = wm * 64 + i * 32 + 8 * q + 4 * (lane >> 5);
+                    const int c = wn * 64 + j * 32 + (lane & 31);
+                    const float4 x = make_float4(alpha * acc[i][j][4 * q], alpha * acc[i][j][4 * q + 1],
+                                                 alpha * acc[i][j][4 * q + 2],
+                                                 alpha * acc[i][j][4 * q + 3]);
+                    *reinterpret_cast<float4*>(Ct + (int64_t)c * ldc + r) = x;
+                }
     }
 };
 
@@ -416,7 +435,7 @@ template <> struct WaveTile<double> {
 template <typename T, typename TA, typename TB>
 constexpr bool kStageF32 = sizeof(T) == 8 && sizeof(TA) == 4 && sizeof(TB) == 4;
 
-template <typename T, typename TA, typename TB, bool AXPBY, bool XF>
+template <typename T, typename TA, typename TB, bool AXPBY, bool XF, bool PERSIST>
 __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ tasks,
                                           const TileRef* __restrict__ tiles,
                                           const uint64_t* __restrict__ bases, const GemmArgs& args,
@@ -455,6 +474,13 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
 
     StageLoader<S, TA> la;
     StageLoader<S, TB> lb;
+    // in a persistent launch the thread index goes through an opaque copy:
+    // values derived from it are then formed per tile, not hoisted out of
+    // the tile loop (kept live across it they spilled)
+    int tid = threadIdx.x;
+    if constexpr (PERSIST) asm volatile("" : "+v"(tid));
+    la.t = tid;
+    lb.t = tid;
     // A split-K part sums k in [kb, K).  fp32: the operands are offset to
     // k = kb and the loop runs from 0 (a Newton operand's diagonal is found
     // with offset kb); fp64: the loop runs from kb.  The two forms compute the
@@ -487,6 +513,11 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
     // symmetric result computed on upper tiles only: an off-diagonal tile
     // also writes its transpose
     const bool mirror = ((tk.trans >> 5) & 1) && ti != tj;
+    // fp32 results of a tile wholly in range mirror with 16-byte stores
+    // after the tile's own stores (aligned: ldc and the offsets of such
+    // products are multiples of 4)
+    const bool vmirror = sizeof(T) == 4 && !AXPBY && mirror && i0 + BM <= tk.M && j0 + BN <= tk.N &&
+                         (tk.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0;
     // in groups of 16 values: the old C values of a group are all loaded
     // before its stores (a store may alias a later load as far as the
     // compiler knows, so one element at a time would serialize the round
@@ -515,10 +546,13 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
                 T o = alpha * v;
                 if constexpr (axpby) o += beta * old[e];
                 C[(int64_t)i * tk.ldc + j] = o;
-                if (mirror) C[(int64_t)j * tk.ldc + i] = o;
+                if (mirror && !vmirror) C[(int64_t)j * tk.ldc + i] = o;
                 nrm += double(o) * double(o);
             }
         }
+    }
+    if constexpr (sizeof(T) == 4 && !AXPBY) {
+        if (vmirror) wt.store_transposed(C + (int64_t)j0 * tk.ldc + i0, tk.ldc, wm, wn, alpha);
     }
     if (tk.norm_slot >= 0 && args.norms) {
         const double s = block_sum_256(nrm, red);
@@ -554,7 +588,7 @@ __global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__
             for (int j = 0; j < C && e0 + j < args.ntiles; ++j) {
                 if (!first) __syncthreads();   // the previous tile's LDS reads and stores are done
                 first = false;
-                if (!gemm_tile<T, TA, TB, AXPBY, XF>(e0 + j, tasks, tiles, bases, args, As, Bs, red)) {
+                if (!gemm_tile<T, TA, TB, AXPBY, XF, PERSIST>(e0 + j, tasks, tiles, bases, args, As, Bs, red)) {
                     live = false;
                     break;
                 }
@@ -562,7 +596,7 @@ __global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__
             if (!live) break;
         }
     } else {
-        (void)gemm_tile<T, TA, TB, AXPBY, XF>(blockIdx.x, tasks, tiles, bases, args, As, Bs, red);
+        (void)gemm_tile<T, TA, TB, AXPBY, XF, PERSIST>(blockIdx.x, tasks, tiles, bases, args, As, Bs, red);
     }
 }
 
