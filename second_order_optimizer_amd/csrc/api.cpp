@@ -113,6 +113,7 @@ struct RootTables {
     int64_t lanczos_s_small_off = 0, lanczos_p_small_off = 0;   // factors with ld <= 128
     int64_t lanczos_s_big_off = 0, lanczos_p_big_off = 0;       // factors with ld > 128
     int n_lanczos_small = 0, n_lanczos_big = 0;
+    int lanczos_big_max_n = 0;                                  // largest dimension above 128
     std::vector<NewtonChunk> chunks32, chunks64;
     std::vector<CompactClass> compact;       // classes of the packed fp64 chain
     int64_t compact_off = 0;
@@ -1216,6 +1217,7 @@ int build_plan(shampoo_s* h) {
         }
         for (int set = 0; set <= 2 * nparts; ++set) {
             std::vector<LanczosJob> jss, jps, jsb, jpb;
+            int max_n = 0;
             const bool async = set > nparts;
             for (int i = 0; i < nf; ++i) {
                 if (!in_set(set, i)) continue;
@@ -1227,8 +1229,10 @@ int build_plan(shampoo_s* h) {
                 }
                 (big ? jsb : jss).push_back(a);
                 (big ? jpb : jps).push_back(b);
+                if (big) max_n = std::max(max_n, h->factors[i].dim);
             }
             RootTables& rt = async ? h->async_roots[set - 1 - nparts] : h->roots[set];
+            rt.lanczos_big_max_n = max_n;
             rt.n_lanczos_small = (int)jss.size();
             rt.n_lanczos_big = (int)jsb.size();
             rt.lanczos_s_small_off = blob.add(jss);
@@ -1308,6 +1312,7 @@ int build_plan(shampoo_s* h) {
         na.lanczos_p_big_off = r0.lanczos_p_big_off;
         na.n_lanczos_small = r0.n_lanczos_small;
         na.n_lanczos_big = r0.n_lanczos_big;
+        na.lanczos_big_max_n = r0.lanczos_big_max_n;
         h->noalloc_ok = true;
         const int na_base = 1 + 2 * h->n;
         for (auto [ld, pe] : lds) {
@@ -1997,8 +2002,10 @@ int enqueue_roots(shampoo_s* h, RootTables& rt, hipStream_t s, unsigned char* sc
             r = hip_err(launch_lanczos(tab<LanczosJob>(h, small_off), rt.n_lanczos_small, base,
                                        on_stats, false, a, s));
         if (r) return r;
+        LanczosArgs ab = a;
+        ab.max_n = rt.lanczos_big_max_n;
         return hip_err(launch_lanczos(tab<LanczosJob>(h, big_off), rt.n_lanczos_big, base, on_stats,
-                                      true, a, s));
+                                      true, ab, s));
     };
     if (use_fp32(c)) {
         // factors up to 128: everything inside the fused kernel; larger ones:
@@ -2031,9 +2038,11 @@ int enqueue_roots(shampoo_s* h, RootTables& rt, hipStream_t s, unsigned char* sc
         ProfScope ps(h, PC_LANCZOS_S, s);
         rc = hip_err(launch_lanczos(tab<LanczosJob>(h, rt.lanczos_s_small_off), rt.n_lanczos_small,
                                     h->arena, true, false, la_small, s));
+        LanczosArgs lb = la;
+        lb.max_n = rt.lanczos_big_max_n;
         if (!rc)
             rc = hip_err(launch_lanczos(tab<LanczosJob>(h, rt.lanczos_s_big_off), rt.n_lanczos_big,
-                                        h->arena, true, true, la, s));
+                                        h->arena, true, true, lb, s));
     }
     if (rc) return rc;
     rc = run_newton(h, rt.chunks64, true, nullptr, 1, prec, s, scr);

@@ -1327,7 +1327,7 @@ __device__ __forceinline__ double block_sum_1024(double v, double* red) {
     return s0 + s1;
 }
 
-template <typename TM>
+template <typename TM, int NM>
 __global__ __launch_bounds__(1024) void k_lanczos_big(const LanczosJob* __restrict__ jobs,
                                                     const TM* __restrict__ arena, LanczosArgs args) {
     __shared__ LanczosBig L;
@@ -1336,6 +1336,10 @@ __global__ __launch_bounds__(1024) void k_lanczos_big(const LanczosJob* __restri
     const TM* S = arena + jb.off;
     const int t = threadIdx.x, w = t >> 6, l = t & 63;
     const int steps = min(args.steps, min(n, kLanczosMaxSteps));
+    if (n > 64 * NM) {   // not launched so (the host picks NM); a visible failure if it were
+        if (t == 0) lanczos_finish(args, jb, false, 0.0);
+        return;
+    }
 
     double s2 = 0.0;
     for (int i = t; i < n; i += 1024) {
@@ -1360,41 +1364,41 @@ __global__ __launch_bounds__(1024) void k_lanczos_big(const LanczosJob* __restri
         // row i's entries j >= i give its dot product with v (summed over the
         // wave), and each entry j > i also adds S_ij v_i to the lane's
         // partial of w_j.  v in registers; each wave takes rows w, w + 16,
-        // ..., four rows' loads in flight at once.
-        double vr[16], wc[16];
+        // ..., with all of a row's loads in flight at once.
+        double vr[NM], wc[NM];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
+        for (int m = 0; m < NM; ++m) {
             vr[m] = (l + 64 * m < n) ? L.v1[l + 64 * m] : 0.0;
             wc[m] = 0.0;
         }
-        for (int i0 = w; i0 < n; i0 += 64) {
-            double acc[4];
+        for (int i = w; i < n; i += 16) {
+            // the row's loads first, with the column clamped into [i, n)
+            // (lanes outside the triangle read S_ii or S_i,n-1, one cache
+            // line, and discard it): no branches, so no load waits on the
+            // one before it
+            // (in batches of up to 8 blocks, for the registers)
+            constexpr int NB = NM < 8 ? NM : 8;
+            const TM* row = S + (int64_t)i * ld;
+            const double vi = L.v1[i];
+            double acc = 0.0;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                acc[r] = 0.0;
-                const int i = i0 + 16 * r;
-                if (i < n) {
-                    const TM* row = S + (int64_t)i * ld;
-                    const double vi = L.v1[i];
+            for (int m0 = 0; m0 < NM; m0 += NB) {
+                TM sv[NB];
 #pragma unroll
-                    for (int m = 0; m < 16; ++m) {
-                        const int j = l + 64 * m;
-                        if (j >= i && j < n) {
-                            const double sij = (double)row[j];
-                            acc[r] += sij * vr[m];
-                            if (j > i) wc[m] += sij * vi;
-                        }
-                    }
+                for (int q = 0; q < NB; ++q) sv[q] = row[min(max(l + 64 * (m0 + q), i), n - 1)];
+#pragma unroll
+                for (int q = 0; q < NB; ++q) {
+                    const int m = m0 + q, j = l + 64 * m;
+                    const double sij = (j >= i && j < n) ? (double)sv[q] : 0.0;
+                    acc += sij * vr[m];
+                    wc[m] += (j > i) ? sij * vi : 0.0;
                 }
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const double x = wave_sum(acc[r]);
-                if (l == 0 && i0 + 16 * r < n) L.wv[i0 + 16 * r] = x;
-            }
+            const double x = wave_sum(acc);
+            if (l == 0) L.wv[i] = x;
         }
 #pragma unroll
-        for (int m = 0; m < 16; ++m)
+        for (int m = 0; m < NM; ++m)
             if (l + 64 * m < n) L.part[w * kLanczosMaxN + l + 64 * m] = wc[m];
         __syncthreads();
         // w_j = (row part) + the sixteen waves' column parts, in wave order
@@ -3220,12 +3224,20 @@ hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, 
         }
         hipLaunchKernelGGL(k_lz_finish, dim3(njobs), dim3(64), 0, s, jobs, a.work, a);
     } else if (big) {
-        if (fp64_matrix)
-            hipLaunchKernelGGL(k_lanczos_big<double>, dim3(njobs), dim3(1024), 0, s, jobs,
-                               static_cast<const double*>(arena), a);
-        else
-            hipLaunchKernelGGL(k_lanczos_big<float>, dim3(njobs), dim3(1024), 0, s, jobs,
-                               static_cast<const float*>(arena), a);
+        // 64-column blocks per row: the fewest that cover the largest factor
+        const int nm = a.max_n > 0 && a.max_n <= 256 ? 4 : a.max_n > 0 && a.max_n <= 512 ? 8 : 16;
+        auto go = [&](auto nmc) {
+            constexpr int NM = decltype(nmc)::value;
+            if (fp64_matrix)
+                hipLaunchKernelGGL((k_lanczos_big<double, NM>), dim3(njobs), dim3(1024), 0, s, jobs,
+                                   static_cast<const double*>(arena), a);
+            else
+                hipLaunchKernelGGL((k_lanczos_big<float, NM>), dim3(njobs), dim3(1024), 0, s, jobs,
+                                   static_cast<const float*>(arena), a);
+        };
+        if (nm == 4) go(std::integral_constant<int, 4>{});
+        else if (nm == 8) go(std::integral_constant<int, 8>{});
+        else go(std::integral_constant<int, 16>{});
     } else {
         if (fp64_matrix)
             hipLaunchKernelGGL(k_lanczos<double>, dim3(njobs), dim3(256), 0, s, jobs,

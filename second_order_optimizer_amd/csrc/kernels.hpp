@@ -55,6 +55,7 @@ struct LanczosArgs {
     FactorDiag* diag;
     int32_t* prec;
     double* work;         // factors > 128: split Lanczos work records (kLanczosSplitMax of them)
+    int max_n;            // factors > 128: the largest dimension among the jobs (0: up to 1024)
 };
 
 struct NewtonArgs {
