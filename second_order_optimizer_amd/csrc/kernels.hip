@@ -1510,11 +1510,12 @@ __global__ __launch_bounds__(256) void k_lz_matvec(const LanczosJob* __restrict_
         for (int r = 0; r < 4; ++r) {
             acc[r] = 0.0;
             const int i = i0 + 4 * r;
-            if (i < n && i < r0 + 64) {
+            if (i < n && i < r0 + 64) {   // uniform
+                // columns past n clamped to n - 1 (their v entry is 0): no
+                // branches around the loads, so they are all in flight at once
                 const TM* row = S + (int64_t)i * ld;
 #pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    if (l + 64 * m < n) acc[r] += (double)row[l + 64 * m] * vr[m];
+                for (int m = 0; m < 16; ++m) acc[r] += (double)row[min(l + 64 * m, n - 1)] * vr[m];
             }
         }
 #pragma unroll
@@ -1729,12 +1730,20 @@ __global__ __launch_bounds__(256) void k_newton_check(const FactorJob* __restric
     for (int tile = blockIdx.x; tile < nt * nt; tile += gridDim.x) {
         const int ti = tile / nt, tj = tile % nt;
         const int i = 32 * ti + r;
+        // every (i, j) < ld is inside the ld x ld buffers: the loads carry
+        // no branches (all in flight at once) and the padding is masked after
+        T xv[4], mv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            xv[q] = X[(int64_t)i * ld + 32 * tj + c0 + q];
+            mv[q] = M[(int64_t)i * ld + 32 * tj + c0 + q];
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int j = 32 * tj + c0 + q;
             if (i < n && j < n) {
-                const double x = double(X[(int64_t)i * ld + j]);
-                const double d = fabs(double(M[(int64_t)i * ld + j]) - (i == j ? 1.0 : 0.0));
+                const double x = double(xv[q]);
+                const double d = fabs(double(mv[q]) - (i == j ? 1.0 : 0.0));
                 if (!isfinite(x) || !isfinite(d)) bad = 1.0;
                 else res = fmax(res, d);
             }
@@ -1786,20 +1795,25 @@ __global__ __launch_bounds__(256) void k_newton_commit(const FactorJob* __restri
     const int r = threadIdx.x >> 3, c0 = (threadIdx.x & 7) * 4;
     for (int tile = blockIdx.x; tile < nt * nt; tile += gridDim.x) {
         const int ti = tile / nt, tj = tile % nt;
-        __syncthreads();   // the previous tile's reads of tm are done
-        if (!ident) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                tm[r][c0 + q] = double(X[(int64_t)(32 * tj + r) * ld + 32 * ti + c0 + q]);
-        }
-        __syncthreads();
         const int i = 32 * ti + r;
+        // both tiles' values, inside the ld x ld buffer: loaded without
+        // branches, all in flight at once (unused for an identity root)
+        T xv[4], xt[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            xv[q] = X[(int64_t)i * ld + 32 * tj + c0 + q];
+            xt[q] = X[(int64_t)(32 * tj + r) * ld + 32 * ti + c0 + q];
+        }
+        __syncthreads();   // the previous tile's reads of tm are done
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tm[r][c0 + q] = double(xt[q]);
+        __syncthreads();
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int c = c0 + q, j = 32 * tj + c;
             double x;
             if (ident || i >= n || j >= n) x = (i == j) ? 1.0 : 0.0;
-            else x = 0.5 * (double(X[(int64_t)i * ld + j]) + tm[c][r]);   // symmetric part
+            else x = 0.5 * (double(xv[q]) + tm[c][r]);   // symmetric part
             P[(int64_t)i * ld + j] = float(x);
             if (P64) P64[(int64_t)i * ld + j] = x;
         }
