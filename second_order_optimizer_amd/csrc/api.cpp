@@ -257,6 +257,26 @@ int newton_stage_count(int p) {  // GEMM launches per iteration
     return s + 1;                  // M <- T^p M
 }
 
+// The tile entries of one task: all tiles, or a symmetric product's upper
+// ones -- with trans bit 6 (fp64 statistics of at least four tiles per side)
+// the tiles above the diagonal and then the groups of the diagonal band, four
+// 64 x 64 units each, as tile indices -1 - q.
+constexpr int kBandBit = 64;
+void task_tiles(const GemmTask& t, int32_t i, std::vector<TileRef>& out) {
+    const int nt = ceil_div(t.M, kTile) * t.tiles_n;
+    const bool upper = (t.trans >> 4) & 1, band = t.trans & kBandBit;
+    for (int e = 0; e < nt; ++e) {
+        const int ti = e / t.tiles_n, tj = e % t.tiles_n;
+        if (!upper || ti < tj || (ti == tj && !band)) out.push_back({i, e});
+    }
+    if (band)
+        for (int q = 0; q < ceil_div(3 * t.tiles_n, 4); ++q) out.push_back({i, -1 - q});
+}
+
+// The band bit for a statistics task: the groups of four units cover the
+// diagonal band of T tiles per side in ceil(3T / 4) workgroups instead of T.
+int32_t band_bit(int tiles_n) { return tiles_n >= 4 ? kBandBit : 0; }
+
 // The tile table of one batched-GEMM launch, in dispatch order.  Workgroup b
 // runs on XCD b % 8, and each XCD has its own L2; the tiles of one task
 // share its A and B panels.  So whole tasks go to XCDs (in order, each to the
@@ -268,13 +288,9 @@ std::vector<TileRef> xcd_tile_order(const std::vector<GemmTask>& tasks) {
     std::vector<double> load(kXcds, 0.0);
     size_t n = 0;
     for (size_t i = 0; i < tasks.size(); ++i) {
-        const int nt = ceil_div(tasks[i].M, kTile) * tasks[i].tiles_n;
-        const bool upper = (tasks[i].trans >> 4) & 1;
         const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
         const size_t before = lists[x].size();
-        for (int t = 0; t < nt; ++t)
-            if (!upper || t / tasks[i].tiles_n <= t % tasks[i].tiles_n)
-                lists[x].push_back({(int32_t)i, t});
+        task_tiles(tasks[i], (int32_t)i, lists[x]);
         n += lists[x].size() - before;
         load[x] += (double)(lists[x].size() - before) * std::max(tasks[i].K, 1);
     }
@@ -306,12 +322,7 @@ std::vector<TileRef> xcd_tile_order(const std::vector<GemmTask>& tasks) {
 // the persistent form of the GEMM kernel.
 LaunchRef add_launch_sorted(Blob& blob, const std::vector<GemmTask>& tasks) {
     std::vector<TileRef> tiles;
-    for (size_t i = 0; i < tasks.size(); ++i) {
-        const int nt = ceil_div(tasks[i].M, kTile) * tasks[i].tiles_n;
-        const bool upper = (tasks[i].trans >> 4) & 1;
-        for (int t = 0; t < nt; ++t)
-            if (!upper || t / tasks[i].tiles_n <= t % tasks[i].tiles_n) tiles.push_back({(int32_t)i, t});
-    }
+    for (size_t i = 0; i < tasks.size(); ++i) task_tiles(tasks[i], (int32_t)i, tiles);
     LaunchRef L;
     L.tasks_off = blob.add(tasks);
     L.tiles_off = blob.add(tiles);
@@ -948,8 +959,8 @@ int build_plan(shampoo_s* h) {
                     t.ldc = f.ld;
                     t.M = t.N = f.dim;
                     t.K = (int)std::min<int64_t>(len, K - k0);
-                    t.trans = (f.side == 1 ? 1 : 2) | 16;
                     t.tiles_n = ceil_div(t.N, kTile);
+                    t.trans = (f.side == 1 ? 1 : 2) | 16 | band_bit(t.tiles_n);
                     t.factor = -1;
                     t.norm_slot = -1;
                     sk.push_back(t);
@@ -1001,8 +1012,8 @@ int build_plan(shampoo_s* h) {
                         t.ldc = f.ld;
                         t.M = t.N = f.dim;
                         t.K = (int)std::min<int64_t>(len, K - k0);
-                        t.trans = (side == 0 ? 2 : 1) | 16;
                         t.tiles_n = ceil_div(t.N, kTile);
+                        t.trans = (side == 0 ? 2 : 1) | 16 | band_bit(t.tiles_n);
                         t.factor = -1;
                         t.norm_slot = -1;
                         gs.push_back(t);
@@ -1034,16 +1045,17 @@ int build_plan(shampoo_s* h) {
             t.ldc = fl.ld;
             t.M = t.N = bp.mb;
             t.K = bp.nb;
-            t.trans = 2 | 16 | mbit;   // symmetric: upper tiles (mirrored for a split Lanczos)
             t.tiles_n = ceil_div(t.N, kTile);
+            // symmetric: upper tiles (mirrored for a split Lanczos)
+            t.trans = 2 | 16 | mbit | band_bit(t.tiles_n);
             tasks.push_back(t);
             // R: op(A) = G_b^T (nb x mb), op(B) = G_b
             t.c_off = fr.off_s / 8;
             t.ldc = fr.ld;
             t.M = t.N = bp.nb;
             t.K = bp.mb;
-            t.trans = 1 | 16 | mbit;
             t.tiles_n = ceil_div(t.N, kTile);
+            t.trans = 1 | 16 | mbit | band_bit(t.tiles_n);
             tasks.push_back(t);
         }
         h->gram = add_launch(blob, tasks);
@@ -2191,8 +2203,8 @@ int enqueue_sos_stats(shampoo_s* h, const shampoo_sparse_rows* sparse, hipStream
                 t.ldc = f.ld;
                 t.M = t.N = f.dim;
                 t.K = (int)std::min<int64_t>(len, n - k0);
-                t.trans = 1 | 16;
                 t.tiles_n = ceil_div(t.N, kTile);
+                t.trans = 1 | 16 | band_bit(t.tiles_n);
                 t.factor = -1;
                 t.norm_slot = -1;
                 tasks.push_back(t);

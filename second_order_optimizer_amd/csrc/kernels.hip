@@ -373,28 +373,29 @@ template <> struct WaveTile<double> {
         }
     }
     // the same from fp32 stages of BK = 32 (fp32 operands: each value is
-    // converted to fp64 as it is read, exactly)
+    // converted to fp64 as it is read, exactly), the wave's 64 rows of op(A)
+    // and 64 columns of op(B) at Ap and Bp (stage layout [k][P])
     // (with the next step's operands read from LDS before this step's 16
     // products, as in the fp32 tile)
-    __device__ __forceinline__ void compute_f32(const float* As, const float* Bs, int wm, int wn) {
+    __device__ __forceinline__ void compute_f32(const float* Ap, const float* Bp) {
         constexpr int P = BM + GemmTraits<float>::PADE;
         constexpr int BK = GemmTraits<float>::BK;
         const int lane = threadIdx.x & 63;
         const int g = lane >> 4, c = lane & 15;
         float a[4], b[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = As[g * P + wm * 64 + i * 16 + c];
+        for (int i = 0; i < 4; ++i) a[i] = Ap[g * P + i * 16 + c];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = Bs[g * P + wn * 64 + j * 16 + c];
+        for (int j = 0; j < 4; ++j) b[j] = Bp[g * P + j * 16 + c];
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 4) {
             float an[4], bn[4];
             if (kk + 4 < BK) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) an[i] = As[(kk + 4 + g) * P + wm * 64 + i * 16 + c];
+                for (int i = 0; i < 4; ++i) an[i] = Ap[(kk + 4 + g) * P + i * 16 + c];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) bn[j] = Bs[(kk + 4 + g) * P + wn * 64 + j * 16 + c];
+                for (int j = 0; j < 4; ++j) bn[j] = Bp[(kk + 4 + g) * P + j * 16 + c];
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -449,7 +450,11 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
     const GemmTask tk = tasks[tr.task];
     if (args.gate && tk.factor >= 0 && args.gate[tk.factor] != args.gate_val) return false;
 
-    const int ti = tr.tile / tk.tiles_n, tj = tr.tile % tk.tiles_n;
+    // fp64 statistics (trans bit 6): a negative tile index -1 - q stands for
+    // group q of the diagonal band (below), staged as tile (t0, t0 + 1)
+    const bool band = F32S && tr.tile < 0;
+    const int q = -1 - tr.tile, t0 = (4 * q) / 3;
+    const int ti = band ? t0 : tr.tile / tk.tiles_n, tj = band ? t0 + 1 : tr.tile % tk.tiles_n;
     const int i0 = ti * BM, j0 = tj * BN;
     const TA* A = base_ptr<TA>(bases, tk.a_base, tk.a_off);
     const TB* B = base_ptr<TB>(bases, tk.b_base, tk.b_off);
@@ -469,6 +474,30 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
     // the wave index as a scalar: branches on it are uniform to the compiler
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = w >> 1, wn = w & 1;
+    // The wave's operand slots: 64-row halves of the stages, 0 and 1 of A's,
+    // 2 and 3 of B's, and the rows / columns of C its 64 x 64 result covers.
+    // A symmetric product's A and B stages of one 64-row panel are equal, so
+    // a slot serves either operand.  The band of a symmetric product with T
+    // tiles of 128 per side is its 3T units of 64 x 64 on and next to the
+    // diagonal -- (2t, 2t), (2t, 2t + 1), (2t + 1, 2t + 1) for each t, whose
+    // upper triangles cover those of the diagonal tiles -- in groups of four
+    // consecutive units, which lie in the panels of tiles t0 and t0 + 1.  A
+    // wave past the band's end computes on slot 0 and stores nothing.
+    int ua = wm, ub = 2 + wn, rbase = i0 + 64 * wm, cbase = j0 + 64 * wn;
+    if constexpr (F32S) {
+        if (band) {
+            const int u = 4 * q + w, tu = u / 3, v = u - 3 * tu;
+            const int pa = 2 * tu + (v == 2), pb = 2 * tu + (v != 0);
+            ua = pa - 2 * t0;
+            ub = pb - 2 * t0;
+            rbase = 64 * pa;
+            cbase = 64 * pb;
+            if (u >= 3 * tk.tiles_n) {
+                ua = ub = 0;
+                rbase = tk.M;
+            }
+        }
+    }
     WaveTile<T> wt;
     wt.zero();
 
@@ -504,7 +533,8 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
             la.load(A, tk.lda, a_kc, i0, k0 + BK, tk.M, Kp, a_al, xa, c1, c2, dk);
             lb.load(B, tk.ldb, b_kc, j0, k0 + BK, tk.N, Kp, b_al, xb, c1, c2, dk);
         }
-        if constexpr (F32S) wt.compute_f32(As, Bs, wm, wn);
+        if constexpr (F32S)
+            wt.compute_f32((ua < 2 ? As : Bs) + 64 * (ua & 1), (ub < 2 ? As : Bs) + 64 * (ub & 1));
         else wt.compute(As, Bs, wm, wn);
     }
 
@@ -512,7 +542,10 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
     constexpr bool axpby = AXPBY;   // the launcher picks it from args.epi
     // symmetric result computed on upper tiles only: an off-diagonal tile
     // also writes its transpose
-    const bool mirror = ((tk.trans >> 5) & 1) && ti != tj;
+    const bool mirror = ((tk.trans >> 5) & 1) && (band ? rbase != cbase : ti != tj);
+    // where C's rows and columns of the wave's result start, less the offsets
+    // the accumulator places add (64 wm, 64 wn)
+    const int ci0 = rbase - 64 * wm, cj0 = cbase - 64 * wn;
     // fp32 results of a tile wholly in range mirror with 16-byte stores
     // after the tile's own stores (aligned: ldc and the offsets of such
     // products are multiples of 4)
@@ -533,7 +566,7 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
             for (int e = 0; e < GRP; ++e) {
                 int r, c;
                 (void)wt.get(g0 + e, wm, wn, r, c);
-                const int i = i0 + r, j = j0 + c;
+                const int i = ci0 + r, j = cj0 + c;
                 old[e] = (i < tk.M && j < tk.N) ? C[(int64_t)i * tk.ldc + j] : T(0);
             }
         }
@@ -541,7 +574,7 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
         for (int e = 0; e < GRP; ++e) {
             int r, c;
             const T v = wt.get(g0 + e, wm, wn, r, c);
-            const int i = i0 + r, j = j0 + c;
+            const int i = ci0 + r, j = cj0 + c;
             if (i < tk.M && j < tk.N) {
                 T o = alpha * v;
                 if constexpr (axpby) o += beta * old[e];

@@ -242,6 +242,22 @@ def test_staggered_root_parts_large_blocks():
     run_parity(wl, root_parts=3)
 
 
+def test_band_statistics():
+    """fp64 statistics of factors with four or more 128-tiles per side cover
+    their diagonal band in groups of four 64 x 64 units: ragged factors of
+    600 (five tiles: a group with a wave past the band's end, units past the
+    edge), 500 and 420 (four), few enough that the split Lanczos reads whole
+    rows, so the band's off-diagonal units are also stored mirrored.
+    Statistics, roots (stage-isolated) and updates against the oracle."""
+    T = synth.TensorSpec
+    wl = _custom([T("a", 600, 500), T("b", 130, 420)], 640, cadence=2, steps=4)
+    run = run_parity(wl)[0]
+    for b in range(run.opt.n_blocks):
+        for S in run.opt.stats(b, raw=True):
+            if S is not None and S.shape[0] > 128:   # both triangles kept
+                assert torch.allclose(S, S.T, rtol=1e-14, atol=0.0), b
+
+
 @pytest.mark.parametrize("fused_step", [False, True])
 def test_async_root_parts(fused_step):
     """Roots in the background: 4 parts, roots every 4 steps, each part begun
