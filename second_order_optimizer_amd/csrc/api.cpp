@@ -484,7 +484,10 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
         t.a_base = t.b_base = t.c_base = base_idx;
         t.M = t.N = t.K = ld;
         t.lda = t.ldb = t.ldc = ld;
-        t.trans = trans;
+        // a square of one symmetric operand (the same transform on both
+        // sides) stages equal A and B panels: its diagonal band in groups
+        const bool square = a == b && ((trans >> 2) & 1) == ((trans >> 3) & 1) && (trans & 16);
+        t.trans = trans | (square ? band_bit(tiles1) : 0);
         t.tiles_n = tiles1;
         t.factor = fid;
         t.norm_slot = -1;

@@ -277,25 +277,27 @@ template <> struct WaveTile<float> {
     // The operands of step kk + 2 are read from LDS before the products of
     // step kk are issued (the scheduling groups keep that order), so a read's
     // latency overlaps four MFMAs instead of stalling the wave.
-    __device__ __forceinline__ void compute(const float* As, const float* Bs, int wm, int wn) {
+    // Ap, Bp: the wave's 64 rows of op(A) and 64 columns of op(B) in the
+    // stages (layout [k][P]).
+    __device__ __forceinline__ void compute(const float* Ap, const float* Bp) {
         constexpr int P = BM + GemmTraits<float>::PADE;
         constexpr int BK = GemmTraits<float>::BK;
         const int lane = threadIdx.x & 63;
         const int h = lane >> 5, c = lane & 31;
         float a[2], b[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) a[i] = As[h * P + wm * 64 + i * 32 + c];
+        for (int i = 0; i < 2; ++i) a[i] = Ap[h * P + i * 32 + c];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) b[j] = Bs[h * P + wn * 64 + j * 32 + c];
+        for (int j = 0; j < 2; ++j) b[j] = Bp[h * P + j * 32 + c];
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 2) {
             float an[2], bn[2];
             if (kk + 2 < BK) {
 #pragma unroll
-                for (int i = 0; i < 2; ++i) an[i] = As[(kk + 2 + h) * P + wm * 64 + i * 32 + c];
+                for (int i = 0; i < 2; ++i) an[i] = Ap[(kk + 2 + h) * P + i * 32 + c];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) bn[j] = Bs[(kk + 2 + h) * P + wn * 64 + j * 32 + c];
+                for (int j = 0; j < 2; ++j) bn[j] = Bp[(kk + 2 + h) * P + j * 32 + c];
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -354,7 +356,7 @@ template <> struct WaveTile<double> {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0;
     }
-    __device__ __forceinline__ void compute(const double* As, const double* Bs, int wm, int wn) {
+    __device__ __forceinline__ void compute(const double* Ap, const double* Bp) {
         constexpr int P = BM + GemmTraits<double>::PADE;
         const int lane = threadIdx.x & 63;
         const int g = lane >> 4, c = lane & 15;
@@ -362,9 +364,9 @@ template <> struct WaveTile<double> {
         for (int kk = 0; kk < GemmTraits<double>::BK; kk += 4) {
             double a[4], b[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = As[(kk + g) * P + wm * 64 + i * 16 + c];
+            for (int i = 0; i < 4; ++i) a[i] = Ap[(kk + g) * P + i * 16 + c];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = Bs[(kk + g) * P + wn * 64 + j * 16 + c];
+            for (int j = 0; j < 4; ++j) b[j] = Bp[(kk + g) * P + j * 16 + c];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -450,9 +452,10 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
     const GemmTask tk = tasks[tr.task];
     if (args.gate && tk.factor >= 0 && args.gate[tk.factor] != args.gate_val) return false;
 
-    // fp64 statistics (trans bit 6): a negative tile index -1 - q stands for
-    // group q of the diagonal band (below), staged as tile (t0, t0 + 1)
-    const bool band = F32S && tr.tile < 0;
+    // symmetric squares (trans bit 6: the statistics, and Newton products of
+    // one operand with itself): a negative tile index -1 - q stands for group
+    // q of the diagonal band (below), staged as tile (t0, t0 + 1)
+    const bool band = (F32S || XF) && tr.tile < 0;
     const int q = -1 - tr.tile, t0 = (4 * q) / 3;
     const int ti = band ? t0 : tr.tile / tk.tiles_n, tj = band ? t0 + 1 : tr.tile % tk.tiles_n;
     const int i0 = ti * BM, j0 = tj * BN;
@@ -484,7 +487,7 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
     // consecutive units, which lie in the panels of tiles t0 and t0 + 1.  A
     // wave past the band's end computes on slot 0 and stores nothing.
     int ua = wm, ub = 2 + wn, rbase = i0 + 64 * wm, cbase = j0 + 64 * wn;
-    if constexpr (F32S) {
+    if constexpr (F32S || XF) {
         if (band) {
             const int u = 4 * q + w, tu = u / 3, v = u - 3 * tu;
             const int pa = 2 * tu + (v == 2), pb = 2 * tu + (v != 0);
@@ -533,9 +536,10 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
             la.load(A, tk.lda, a_kc, i0, k0 + BK, tk.M, Kp, a_al, xa, c1, c2, dk);
             lb.load(B, tk.ldb, b_kc, j0, k0 + BK, tk.N, Kp, b_al, xb, c1, c2, dk);
         }
-        if constexpr (F32S)
-            wt.compute_f32((ua < 2 ? As : Bs) + 64 * (ua & 1), (ub < 2 ? As : Bs) + 64 * (ub & 1));
-        else wt.compute(As, Bs, wm, wn);
+        const S* Ap = (ua < 2 ? As : Bs) + 64 * (ua & 1);
+        const S* Bp = (ub < 2 ? As : Bs) + 64 * (ub & 1);
+        if constexpr (F32S) wt.compute_f32(Ap, Bp);
+        else wt.compute(Ap, Bp);
     }
 
     const T alpha = T(args.alpha), beta = T(args.beta);
@@ -549,7 +553,9 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
     // fp32 results of a tile wholly in range mirror with 16-byte stores
     // after the tile's own stores (aligned: ldc and the offsets of such
     // products are multiples of 4)
-    const bool vmirror = sizeof(T) == 4 && !AXPBY && mirror && i0 + BM <= tk.M && j0 + BN <= tk.N &&
+    const bool vmirror = sizeof(T) == 4 && !AXPBY && mirror &&
+                         (band ? rbase + 64 <= tk.M && cbase + 64 <= tk.N
+                               : i0 + BM <= tk.M && j0 + BN <= tk.N) &&
                          (tk.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0;
     // in groups of 16 values: the old C values of a group are all loaded
     // before its stores (a store may alias a later load as far as the
@@ -585,7 +591,7 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
         }
     }
     if constexpr (sizeof(T) == 4 && !AXPBY) {
-        if (vmirror) wt.store_transposed(C + (int64_t)j0 * tk.ldc + i0, tk.ldc, wm, wn, alpha);
+        if (vmirror) wt.store_transposed(C + (int64_t)cj0 * tk.ldc + ci0, tk.ldc, wm, wn, alpha);
     }
     if (tk.norm_slot >= 0 && args.norms) {
         const double s = block_sum_256(nrm, red);
