@@ -501,6 +501,15 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
             }
         }
     }
+    // A mirrored symmetric product is stored bitwise symmetric: on a diagonal
+    // tile the lower-left wave stores nothing (rows from M on are masked) and
+    // the upper-right one also writes its transpose, as off-diagonal tiles
+    // do; a wave on the diagonal stores its upper triangle and mirrors it
+    // (below).  (Products that are symmetric only in exact arithmetic, X T'
+    // and T'^p M, would otherwise leave the two triangles a rounding apart,
+    // and a band unit may read either one as its operand.)
+    if (!band && ti == tj && ((tk.trans >> 4) & 1) && ((tk.trans >> 5) & 1) && wm == 1 && wn == 0)
+        rbase = tk.M;
     WaveTile<T> wt;
     wt.zero();
 
@@ -544,18 +553,19 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
 
     const T alpha = T(args.alpha), beta = T(args.beta);
     constexpr bool axpby = AXPBY;   // the launcher picks it from args.epi
-    // symmetric result computed on upper tiles only: an off-diagonal tile
-    // also writes its transpose
-    const bool mirror = ((tk.trans >> 5) & 1) && (band ? rbase != cbase : ti != tj);
+    // symmetric result computed on upper tiles only: a wave whose part lies
+    // off the diagonal also writes its transpose
+    const bool mirror = ((tk.trans >> 5) & 1) && rbase != cbase;
+    // ... and one on the diagonal forms j >= i only, each value also stored at
+    // its transpose (as the split-K sum does)
+    const bool sdiag = ((tk.trans >> 4) & 1) && ((tk.trans >> 5) & 1) && rbase == cbase;
     // where C's rows and columns of the wave's result start, less the offsets
     // the accumulator places add (64 wm, 64 wn)
     const int ci0 = rbase - 64 * wm, cj0 = cbase - 64 * wn;
-    // fp32 results of a tile wholly in range mirror with 16-byte stores
-    // after the tile's own stores (aligned: ldc and the offsets of such
-    // products are multiples of 4)
-    const bool vmirror = sizeof(T) == 4 && !AXPBY && mirror &&
-                         (band ? rbase + 64 <= tk.M && cbase + 64 <= tk.N
-                               : i0 + BM <= tk.M && j0 + BN <= tk.N) &&
+    // fp32 results of a wave whose 64 x 64 part is wholly in range mirror
+    // with 16-byte stores after its own stores (aligned: ldc and the offsets
+    // of such products are multiples of 4)
+    const bool vmirror = sizeof(T) == 4 && !AXPBY && mirror && rbase + 64 <= tk.M && cbase + 64 <= tk.N &&
                          (tk.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0;
     // in groups of 16 values: the old C values of a group are all loaded
     // before its stores (a store may alias a later load as far as the
@@ -581,11 +591,11 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
             int r, c;
             const T v = wt.get(g0 + e, wm, wn, r, c);
             const int i = ci0 + r, j = cj0 + c;
-            if (i < tk.M && j < tk.N) {
+            if (i < tk.M && j < tk.N && (!sdiag || j >= i)) {
                 T o = alpha * v;
                 if constexpr (axpby) o += beta * old[e];
                 C[(int64_t)i * tk.ldc + j] = o;
-                if (mirror && !vmirror) C[(int64_t)j * tk.ldc + i] = o;
+                if ((mirror && !vmirror) || (sdiag && j > i)) C[(int64_t)j * tk.ldc + i] = o;
                 nrm += double(o) * double(o);
             }
         }
