@@ -777,8 +777,8 @@ FAMILY_OF = [
     ("k_adagrad_norm", "adagrad_norm", None),
     ("k_update", "update", None),
     ("k_sparse_rows", "sparse_rows", None),
-    ("k_lanczos_big<double>", "lanczos_stats", None),
-    ("k_lanczos_big<float>", "lanczos_roots", None),
+    ("k_lanczos_big<double", "lanczos_stats", None),
+    ("k_lanczos_big<float", "lanczos_roots", None),
 ]
 
 
