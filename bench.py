@@ -168,8 +168,10 @@ def work_model(wl, opt):
     apply_small_bytes = sum((28.0 if b.tensor not in has_big else 16.0) * b.rows * b.cols +
                             4.0 * (b.ld_l ** 2 + b.ld_r ** 2) for b in small)
     # fused step kernel (steps without roots, blocks <= 128): statistics
-    # (upper triangles read and written in fp64) plus the apply
-    step_small_bytes = apply_small_bytes + sum(
+    # (upper triangles read and written in fp64) plus the apply, and the
+    # dense-Adagrad rows its launch also runs (g, a, momentum, weight: 28 B)
+    fold = dense_fallback * 28.0 if small else 0.0
+    step_small_bytes = apply_small_bytes + fold + sum(
         8.0 * (b.rows * (b.rows + 1) + b.cols * (b.cols + 1)) for b in small)
     return {
         "gram": gram(blocks), "gram_small": gram(small), "gram_big": gram(big),
@@ -189,6 +191,7 @@ def work_model(wl, opt):
         "onesided_rows_elems": sum(listed_rows(b) * b.cols for b in sparse_os),
         "shampoo_params_big": sum(b.rows * b.cols for b in big + dense_os),
         "shampoo_params": shampoo_params, "dense_fallback": dense_fallback,
+        "fold_bytes": fold,
         "sparse_elems": sum(round(wl.sparse_frac * t.rows) * t.cols
                             for i, t in enumerate(wl.tensors)
                             if t.kind == "sparse" and i not in {b.tensor for b in sparse_os}),
@@ -483,6 +486,21 @@ def run_pass(wl, args, tol, pool, dev, peaks):
         total = max(total, int(launches))
         rec = {"launches": int(total), "launches_timed": int(launches), "avg_ms": tot / launches,
                "ms_per_step": tot / launches * total / args.steps}
+        if name == "update" and wm["fold_bytes"] > 0:
+            # the update of a step through the fused step kernel leaves the
+            # dense-Adagrad rows to that kernel: bytes per launch by the kind
+            # of step each sampled launch came from
+            nr = nf = 0
+            for t in timed:
+                if sampled(t):
+                    n = per_kind.get(kind(t), {}).get(name, 0)
+                    if kind(t) == S.ROOTS_NONE:
+                        nf += n
+                    else:
+                        nr += n
+            wr = wm["unfused_params"] * 20.0 + wm["dense_fallback"] * 28.0
+            wf = wm["unfused_params"] * 20.0
+            alg[name] = ((nr * wr + nf * wf) / max(nr + nf, 1), "GB/s", "hbm", PEAK_HBM_GBS)
         if name == "step_fused":
             sec = rec["avg_ms"] / 1e3
             rec.update({"mfma_floor_frac": t_mfma_step / sec, "hbm_floor_frac": t_hbm_step / sec,

@@ -210,6 +210,10 @@ struct shampoo_s {
     int async_part = -1;             // part in flight, or -1
     int64_t blockchunks_off = 0, blocknorms_off = 0, rowchunks_off = 0;
     int n_blockchunks = 0, n_rowchunks = 0, n_blocknorms = 0;
+    // steps through the fused kernel: its dense-Adagrad row chunks (larger,
+    // for 1024 threads) and the update's remaining (Shampoo) chunks
+    int64_t fold_off = 0, shampoo_rows_off = 0;
+    int n_fold = 0, n_shampoo_rows = 0;
     std::vector<FactorDiag> diag_init;
 
     // binding
@@ -1452,6 +1456,30 @@ int build_plan(shampoo_s* h) {
         }
         h->n_rowchunks = (int)rcs.size();
         h->rowchunks_off = blob.add(rcs);
+        std::vector<RowChunk> fold, rest;
+        for (const RowChunk& q : rcs)
+            if (q.mode == 0) rest.push_back(q);
+        for (int t = 0; t < h->n; ++t) {
+            const TensorPlan& tp = h->tensors[t];
+            if (tp.mode != 1 || tp.fused) continue;
+            const int rows_per = (int)std::max<int64_t>(1, 4 * kElemChunk / tp.cols);
+            for (int64_t r0 = 0; r0 < tp.rows; r0 += rows_per) {
+                RowChunk q{};
+                q.tensor = t;
+                q.mode = 1;
+                q.row0 = (int)r0;
+                q.nrows = (int)std::min<int64_t>(rows_per, tp.rows - r0);
+                q.cols = (int)tp.cols;
+                q.block_size = b;
+                q.a_off = tp.off_a / 4;
+                q.m_off = tp.off_mom / 4;
+                fold.push_back(q);
+            }
+        }
+        h->n_fold = (int)fold.size();
+        h->fold_off = blob.add(fold);
+        h->n_shampoo_rows = (int)rest.size();
+        h->shampoo_rows_off = blob.add(rest);
     }
     h->total = (size_t)align_up(h->off_tables + (int64_t)blob.bytes.size(), 256);
     return SHAMPOO_OK;
@@ -2352,11 +2380,14 @@ int enqueue_apply(shampoo_s* h, float* const* params, const shampoo_sparse_rows*
                                      arena, (float)c.graft_eps, partA, s));
     }
     if (rc) return rc;
+    // the fused step's launch also takes the dense-Adagrad rows
+    const bool fold = fused_small && h->n_apply128 > 0 && h->n_fold > 0;
     if (fused_small) {
         const GemmArgs sa = stats_args(h);
         ProfScope ps(h, PC_STEP_FUSED, s, h->n_apply128 > 0);
-        rc = hip_err(launch_step128(tab<StepJob>(h, h->step128_off), h->n_apply128, bases, arena,
-                                    sa.alpha, sa.beta, (float)c.graft_eps, partA, partD, ua, s));
+        rc = hip_err(launch_step128(tab<StepJob>(h, h->step128_off), h->n_apply128,
+                                    tab<RowChunk>(h, h->fold_off), fold ? h->n_fold : 0, h->n, bases,
+                                    arena, sa.alpha, sa.beta, (float)c.graft_eps, partA, partD, ua, s));
     } else {
         ProfScope ps(h, PC_APPLY_FUSED, s, h->n_apply128 > 0);
         rc = hip_err(launch_apply128(tab<ApplyJob>(h, h->apply128_off), h->n_apply128, bases, arena,
@@ -2406,9 +2437,10 @@ int enqueue_apply(shampoo_s* h, float* const* params, const shampoo_sparse_rows*
     }
     if (rc) return rc;
     {
-        ProfScope ps(h, PC_UPDATE, s, h->n_rowchunks > 0);
-        rc = hip_err(launch_update(tab<RowChunk>(h, h->rowchunks_off), h->n_rowchunks, bases, h->n,
-                                   arena, scale, ua, s));
+        const int n = fold ? h->n_shampoo_rows : h->n_rowchunks;
+        ProfScope ps(h, PC_UPDATE, s, n > 0);
+        rc = hip_err(launch_update(tab<RowChunk>(h, fold ? h->shampoo_rows_off : h->rowchunks_off), n,
+                                   bases, h->n, arena, scale, ua, s));
     }
     if (rc) return rc;
     if (!h->sos.empty()) {

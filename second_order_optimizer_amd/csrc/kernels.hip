@@ -2477,10 +2477,19 @@ __global__ __launch_bounds__(512, 4) void k_apply128(const ApplyJob* __restrict_
 //     blocks > 128) by all waves, in row-major 16-byte accesses.
 // Each SIMD holds two waves of each half, so the fp64 products of one half
 // overlap the memory traffic of the other.
+// Extra workgroups of the launch take row chunks of dense-Adagrad tensors
+// (independent of the blocks: their G, a, mom and W are their own), spread
+// through the grid: their streaming uses memory bandwidth the blocks leave
+// idle, and the launch's last round of blocks is no longer half empty.
 typedef float f4v __attribute__((ext_vector_type(4)));
 
+template <int NT>
+__device__ __forceinline__ void update_chunk(const RowChunk& ch, const uint64_t* __restrict__ bases,
+                                             int n_tensors, float* __restrict__ arena,
+                                             const float* __restrict__ scale, const UpdateArgs& args);
 
-__global__ __launch_bounds__(1024) void k_step128(const StepJob* __restrict__ jobs,
+__global__ __launch_bounds__(1024) void k_step128(const StepJob* __restrict__ jobs, int njobs,
+                                                 const RowChunk* __restrict__ fold, int n_tensors,
                                                  const uint64_t* __restrict__ bases,
                                                  float* __restrict__ arena, double alpha, double beta,
                                                  float delta, double* __restrict__ partA,
@@ -2488,7 +2497,23 @@ __global__ __launch_bounds__(1024) void k_step128(const StepJob* __restrict__ jo
     __shared__ __align__(16) float Gs[128 * kGP];
     __shared__ __align__(16) float Ps[128 * kGP];
     __shared__ double red[16];
-    const StepJob sj = jobs[blockIdx.x];
+    // the row chunks sit at every sp-th place of the grid (sp = grid / chunks,
+    // so all fit), spreading their streaming over the launch; the other
+    // places are the blocks in order
+    int bid = blockIdx.x;
+    {
+        const int nfold = (int)gridDim.x - njobs;
+        if (nfold > 0) {
+            const int sp = (int)gridDim.x / nfold;
+            const int q = bid / sp;
+            if (bid % sp == sp - 1 && q < nfold) {
+                update_chunk<1024>(fold[q], bases, n_tensors, arena, nullptr, ua);
+                return;
+            }
+            bid -= min(nfold, (bid + 1) / sp);
+        }
+    }
+    const StepJob sj = jobs[bid];
     const ApplyJob& jb = sj.ap;
     const float* G = base_ptr<const float>(bases, jb.g_base, jb.g_off);
     float* a = arena + jb.a_off;
@@ -2949,11 +2974,11 @@ __global__ __launch_bounds__(256) void k_block_scale(const BlockNorms* __restric
 // ================================================== elementwise: update
 // Shampoo rows:  U = scale_b D;  dense-Adagrad rows: a += g^2, U = g/(sqrt(a)+delta).
 // Then mom <- beta1 mom + U and W <- W - lr mom.
-__global__ __launch_bounds__(256) void k_update(const RowChunk* __restrict__ chunks,
-                                               const uint64_t* __restrict__ bases, int n_tensors,
-                                               float* __restrict__ arena,
-                                               const float* __restrict__ scale, UpdateArgs args) {
-    const RowChunk ch = chunks[blockIdx.x];
+// One row chunk of the update on a workgroup of NT threads.
+template <int NT>
+__device__ __forceinline__ void update_chunk(const RowChunk& ch, const uint64_t* __restrict__ bases,
+                                             int n_tensors, float* __restrict__ arena,
+                                             const float* __restrict__ scale, const UpdateArgs& args) {
     const float* G = base_ptr<const float>(bases, 1 + ch.tensor, 0);
     float* W = base_ptr<float>(bases, 1 + n_tensors + ch.tensor, 0);
     float* a = arena + ch.a_off;
@@ -2971,12 +2996,12 @@ __global__ __launch_bounds__(256) void k_update(const RowChunk* __restrict__ chu
         constexpr int kU = 4;
         const int64_t t4 = total / 4;
         const int c4 = ch.cols / 4;
-        for (int64_t e0 = threadIdx.x; e0 < t4; e0 += 256 * kU) {
+        for (int64_t e0 = threadIdx.x; e0 < t4; e0 += NT * kU) {
             float4 d[kU], m[kU], w[kU];
             float sc[kU];
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
-                const int64_t e = e0 + 256 * u;
+                const int64_t e = e0 + NT * u;
                 if (e < t4) {
                     const int64_t idx = base + 4 * e;
                     d[u] = *reinterpret_cast<const float4*>(D + idx);
@@ -2989,7 +3014,7 @@ __global__ __launch_bounds__(256) void k_update(const RowChunk* __restrict__ chu
             }
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
-                const int64_t e = e0 + 256 * u;
+                const int64_t e = e0 + NT * u;
                 if (e < t4) {
                     const int64_t idx = base + 4 * e;
                     const float s = sc[u];
@@ -3008,11 +3033,11 @@ __global__ __launch_bounds__(256) void k_update(const RowChunk* __restrict__ chu
         // before their stores, as above
         constexpr int kU = 4;
         const int64_t t4 = total / 4;
-        for (int64_t e0 = threadIdx.x; e0 < t4; e0 += 256 * kU) {
+        for (int64_t e0 = threadIdx.x; e0 < t4; e0 += NT * kU) {
             float4 g[kU], av[kU], m[kU], w[kU];
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
-                const int64_t e = e0 + 256 * u;
+                const int64_t e = e0 + NT * u;
                 if (e < t4) {
                     const int64_t idx = base + 4 * e;
                     g[u] = *reinterpret_cast<const float4*>(G + idx);
@@ -3023,7 +3048,7 @@ __global__ __launch_bounds__(256) void k_update(const RowChunk* __restrict__ chu
             }
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
-                const int64_t e = e0 + 256 * u;
+                const int64_t e = e0 + NT * u;
                 if (e < t4) {
                     const int64_t idx = base + 4 * e;
                     float4 aa = av[u], mm = m[u], ww = w[u];
@@ -3041,7 +3066,7 @@ __global__ __launch_bounds__(256) void k_update(const RowChunk* __restrict__ chu
             }
         }
     } else {
-        for (int64_t e = threadIdx.x; e < total; e += 256) {
+        for (int64_t e = threadIdx.x; e < total; e += NT) {
             const int64_t idx = base + e;
             float u;
             if (ch.mode == 0) {
@@ -3060,6 +3085,13 @@ __global__ __launch_bounds__(256) void k_update(const RowChunk* __restrict__ chu
             W[idx] -= lr * m;
         }
     }
+}
+
+__global__ __launch_bounds__(256) void k_update(const RowChunk* __restrict__ chunks,
+                                               const uint64_t* __restrict__ bases, int n_tensors,
+                                               float* __restrict__ arena,
+                                               const float* __restrict__ scale, UpdateArgs args) {
+    update_chunk<256>(chunks[blockIdx.x], bases, n_tensors, arena, scale, args);
 }
 
 // ============================= sparse-row tables, one-sided preconditioning
@@ -3380,12 +3412,13 @@ hipError_t launch_newton128(const FactorJob* jobs, int njobs, const double* stat
     }
     return hipGetLastError();
 }
-hipError_t launch_step128(const StepJob* jobs, int njobs, const uint64_t* bases, float* arena,
-                          double alpha, double beta, float delta, double* partA, double* partD,
-                          const UpdateArgs& ua, hipStream_t s) {
+hipError_t launch_step128(const StepJob* jobs, int njobs, const RowChunk* fold, int nfold,
+                          int n_tensors, const uint64_t* bases, float* arena, double alpha, double beta,
+                          float delta, double* partA, double* partD, const UpdateArgs& ua,
+                          hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_step128, dim3(njobs), dim3(1024), 0, s, jobs, bases, arena, alpha, beta,
-                       delta, partA, partD, ua);
+    hipLaunchKernelGGL(k_step128, dim3(njobs + nfold), dim3(1024), 0, s, jobs, njobs, fold, n_tensors,
+                       bases, arena, alpha, beta, delta, partA, partD, ua);
     return hipGetLastError();
 }
 hipError_t launch_apply128(const ApplyJob* jobs, int njobs, const uint64_t* bases, float* arena,

@@ -110,9 +110,12 @@ hipError_t launch_gemm_f64_from_f32(const GemmTask* tasks, const TileRef* tiles,
                                     const uint64_t* bases, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gram128(const GramJob* jobs, int njobs, const uint64_t* bases, double* stats,
                           double alpha, double beta, hipStream_t s);
-hipError_t launch_step128(const StepJob* jobs, int njobs, const uint64_t* bases, float* arena,
-                          double alpha, double beta, float delta, double* partA, double* partD,
-                          const UpdateArgs& ua, hipStream_t s);
+// Blocks <= 128 of a step without a root pass; with nfold > 0 the launch also
+// runs the dense-Adagrad row chunks `fold` (workgroups after the blocks).
+hipError_t launch_step128(const StepJob* jobs, int njobs, const RowChunk* fold, int nfold,
+                          int n_tensors, const uint64_t* bases, float* arena, double alpha, double beta,
+                          float delta, double* partA, double* partD, const UpdateArgs& ua,
+                          hipStream_t s);
 hipError_t launch_lanczos(const LanczosJob* jobs, int njobs, const void* arena, bool fp64_matrix,
                           bool big, const LanczosArgs& a, hipStream_t s);
 // Sums the split-K parts of symmetric Newton products (one workgroup per
