@@ -512,6 +512,18 @@ def test_fallback_and_sparse_rows():
                 assert np.array_equal(W[r], run.W0[k][r])
 
 
+def test_folded_dense_adagrad_rows():
+    """Steps without a root pass run the dense-Adagrad rows of tensors past
+    max_precond_dim inside the fused step's launch, spread through its grid:
+    four blocks of 64 beside fallback tensors of 2000 x 131 (odd width: the
+    unvectorised path) and 3000 x 200, 14 row chunks, more than the blocks.
+    Updates and statistics against the oracle on every step, roots every 4."""
+    T = synth.TensorSpec
+    wl = _custom([T("dense", 96, 80), T("tall", 2000, 131), T("big", 3000, 200)], 64,
+                 max_precond_dim=128, cadence=4, steps=6)
+    run_parity(wl)
+
+
 def test_deterministic_bitwise():
     wl = synth.workload(0)
     outs = []
