@@ -343,7 +343,12 @@ enum {
  * selects, then shampoo_precondition_and_apply, with the same arguments.  On
  * a step without roots the statistics of a block (G, L, R) and its apply (G,
  * a, P, mom, W) share only read-only inputs, so every block of at most
- * 128 x 128 gets both from one kernel that reads G once.  Results:
+ * 128 x 128 gets both from one kernel that reads G once, and (unless
+ * per-kernel profiling is enabled) the statistics of the larger blocks run on
+ * a stream of the library's (default priority) beside the apply: forked from `stream` by an event after this call's
+ * pointer upload and joined back into it before the call's last work, so
+ * work issued on `stream` afterwards sees the whole step (the fork and join
+ * are events, which stream capture into a graph follows).  Results:
  * statistics and Adagrad accumulators bit for bit those of the separate
  * calls; momentum and weights to rounding (the two block norms of the graft
  * are summed in another fixed order).  Errors: as the separate calls, and
@@ -373,7 +378,8 @@ int shampoo_tensor_info(const shampoo_t* h, int32_t tensor, int64_t* adagrad_off
 /* Per-kernel GPU time, for measurement tools.  While enabled, every kernel
  * launch of the calls above is bracketed by two HIP events recorded on the
  * call's stream (a few microseconds of host time per launch, no device
- * synchronisation).  shampoo_profile_read waits for the recorded events, adds
+ * synchronisation), and shampoo_step runs every stage in order on that
+ * stream (no statistics beside the apply), so each launch is timed alone.  shampoo_profile_read waits for the recorded events, adds
  * their elapsed times per kernel family into `out` (up to `cap` records, in a
  * fixed order; *n_out receives the number written) and resets the counters.
  * Errors: SHAMPOO_E_ARG, SHAMPOO_E_HIP. */

@@ -207,6 +207,10 @@ struct shampoo_s {
     int64_t off_snap = 0, off_stage = 0;
     hipStream_t side = nullptr;
     hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    // steps without a root pass: the statistics of the blocks above 128 on
+    // this stream beside the apply (default priority)
+    hipStream_t ovl = nullptr;
+    hipEvent_t ov_fork = nullptr, ov_join = nullptr;
     int async_part = -1;             // part in flight, or -1
     int64_t blockchunks_off = 0, blocknorms_off = 0, rowchunks_off = 0;
     int n_blockchunks = 0, n_rowchunks = 0, n_blocknorms = 0;
@@ -246,6 +250,9 @@ struct shampoo_s {
         if (ev_fork) (void)hipEventDestroy(ev_fork);
         if (ev_join) (void)hipEventDestroy(ev_join);
         if (side) (void)hipStreamDestroy(side);
+        if (ov_fork) (void)hipEventDestroy(ov_fork);
+        if (ov_join) (void)hipEventDestroy(ov_join);
+        if (ovl) (void)hipStreamDestroy(ovl);
     }
 };
 
@@ -1735,6 +1742,15 @@ int shampoo_bind_state(shampoo_t* h, void* dev_state, size_t bytes, void* stream
             hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess)
             return SHAMPOO_E_HIP;
     }
+    if ((h->gram.ntiles > 0 || h->gsplit.ntiles > 0) && !h->ovl) {
+        if (hipStreamCreateWithFlags(&h->ovl, hipStreamNonBlocking) != hipSuccess) {
+            h->ovl = nullptr;
+            return SHAMPOO_E_HIP;
+        }
+        if (hipEventCreateWithFlags(&h->ov_fork, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&h->ov_join, hipEventDisableTiming) != hipSuccess)
+            return SHAMPOO_E_HIP;
+    }
     h->async_part = -1;
     // set-up of the allocation-free root pass: this device's static scratch
     if (hipGetDevice(&h->device) != hipSuccess) return SHAMPOO_E_HIP;
@@ -1780,7 +1796,33 @@ int enqueue_sos_stats(shampoo_s* h, const shampoo_sparse_rows* sparse, hipStream
 // Statistics kernels on stream s (pointer table already current).  With
 // skip_small the blocks of at most 128 x 128 are left to the fused step
 // kernel (enqueue_apply with fused_small).
-int enqueue_stats(shampoo_s* h, hipStream_t s, bool skip_small, const shampoo_sparse_rows* sparse) {
+// The statistics of the two-sided blocks above 128 (the batched GEMM, and the
+// column-split partials of a few large blocks with their sum).
+int enqueue_stats_big(shampoo_s* h, hipStream_t s) {
+    const GemmArgs a = stats_args(h);
+    ProfScope ps(h, PC_STATS, s, h->gram.ntiles > 0 || h->gsplit.ntiles > 0);
+    int rc = hip_err(launch_gemm_f64_from_f32(tab<GemmTask>(h, h->gram.tasks_off),
+                                              tab<TileRef>(h, h->gram.tiles_off), h->gram.ntiles,
+                                              at<uint64_t>(h, h->off_bases), a, s));
+    if (rc || h->gsplit.ntiles == 0) return rc;
+    // a few large blocks: partial products over k, then their fixed-order
+    // sum into S = beta2 S + w sum_c part_c
+    GemmArgs pa{};
+    pa.epi = EPI_STORE;
+    pa.alpha = 1.0;
+    rc = hip_err(launch_gemm_f64_from_f32(tab<GemmTask>(h, h->gsplit.tasks_off),
+                                          tab<TileRef>(h, h->gsplit.tiles_off), h->gsplit.ntiles,
+                                          at<uint64_t>(h, h->off_bases), pa, s));
+    if (!rc)
+        rc = hip_err(launch_sym_reduce(tab<SymReduceJob>(h, h->gred_jobs_off),
+                                       tab<TileRef>(h, h->gred_tiles_off), h->n_gred_tiles,
+                                       at<double>(h, 0), a.alpha, a.beta, s));
+    return rc;
+}
+
+// skip_big: the caller runs enqueue_stats_big itself (on another stream).
+int enqueue_stats(shampoo_s* h, hipStream_t s, bool skip_small, const shampoo_sparse_rows* sparse,
+                  bool skip_big) {
     const GemmArgs a = stats_args(h);
     // fp32 gradients, fp64 products and statistics (exact products; the
     // statistics keep the near-null spectrum that fp32 storage would round
@@ -1792,28 +1834,9 @@ int enqueue_stats(shampoo_s* h, hipStream_t s, bool skip_small, const shampoo_sp
                                                a.alpha, a.beta, s));
         if (rc2) return rc2;
     }
-    {
-        ProfScope ps(h, PC_STATS, s, h->gram.ntiles > 0 || h->gsplit.ntiles > 0);
-        int rc = hip_err(launch_gemm_f64_from_f32(tab<GemmTask>(h, h->gram.tasks_off),
-                                                  tab<TileRef>(h, h->gram.tiles_off),
-                                                  h->gram.ntiles, at<uint64_t>(h, h->off_bases),
-                                                  a, s));
-        if (rc) return rc;
-        if (h->gsplit.ntiles > 0) {
-            // a few large blocks: partial products over k, then their
-            // fixed-order sum into S = beta2 S + w sum_c part_c
-            GemmArgs pa{};
-            pa.epi = EPI_STORE;
-            pa.alpha = 1.0;
-            rc = hip_err(launch_gemm_f64_from_f32(tab<GemmTask>(h, h->gsplit.tasks_off),
-                                                  tab<TileRef>(h, h->gsplit.tiles_off), h->gsplit.ntiles,
-                                                  at<uint64_t>(h, h->off_bases), pa, s));
-            if (!rc)
-                rc = hip_err(launch_sym_reduce(tab<SymReduceJob>(h, h->gred_jobs_off),
-                                               tab<TileRef>(h, h->gred_tiles_off), h->n_gred_tiles,
-                                               at<double>(h, 0), a.alpha, a.beta, s));
-            if (rc) return rc;
-        }
+    if (!skip_big) {
+        const int rc2 = enqueue_stats_big(h, s);
+        if (rc2) return rc2;
     }
     if (!h->sos.empty()) {
         const int rc = enqueue_sos_stats(h, sparse, s);
@@ -1883,7 +1906,7 @@ int shampoo_update_stats(shampoo_t* h, const float* const* grads,
     hipStream_t s = static_cast<hipStream_t>(stream);
     rc = refresh_bases(h, grads, nullptr, sparse, s);
     if (rc) return rc;
-    return enqueue_stats(h, s, false, sparse);
+    return enqueue_stats(h, s, false, sparse, false);
 }
 
 namespace {
@@ -2190,14 +2213,36 @@ int shampoo_step(shampoo_t* h, float* const* params, const float* const* grads,
     if (rc) return rc;
     if (roots != SHAMPOO_ROOTS_NONE) {
         // the roots need this step's statistics, the apply needs the roots
-        rc = enqueue_stats(h, s, false, sparse);
+        rc = enqueue_stats(h, s, false, sparse, false);
         if (!rc) rc = enqueue_roots(h, h->roots[roots == SHAMPOO_ROOTS_ALL ? 0 : 1 + roots], s);
         if (!rc) rc = enqueue_apply(h, params, sparse, s, false);
         return rc;
     }
-    // no root pass: statistics and apply of each block <= 128 share one kernel
-    rc = enqueue_stats(h, s, true, sparse);
+    // no root pass: statistics and apply of each block <= 128 share one
+    // kernel, and the statistics of the larger blocks (fp64 MFMA) run on a
+    // second stream beside the apply (bf16 products and streaming), with
+    // which they share only read-only inputs; the step ends when both have
+    // (with per-launch profiling on, in order on one stream: each launch is
+    // then timed alone)
+    const bool ovl = h->ovl && !h->prof_on && (h->gram.ntiles > 0 || h->gsplit.ntiles > 0);
+    if (ovl) {
+        rc = hip_err(hipEventRecord(h->ov_fork, s));
+        if (!rc) rc = hip_err(hipStreamWaitEvent(h->ovl, h->ov_fork, 0));
+        if (rc) return rc;   // nothing on the second stream
+        rc = enqueue_stats_big(h, h->ovl);
+        const int rj = hip_err(hipEventRecord(h->ov_join, h->ovl));
+        if (rj) return rj;
+        if (rc) {
+            (void)hipStreamWaitEvent(s, h->ov_join, 0);
+            return rc;
+        }
+    }
+    rc = enqueue_stats(h, s, true, sparse, ovl);
     if (!rc) rc = enqueue_apply(h, params, sparse, s, true);
+    if (ovl) {
+        const int rj = hip_err(hipStreamWaitEvent(s, h->ov_join, 0));
+        if (!rc) rc = rj;
+    }
     return rc;
 }
 
