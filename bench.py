@@ -550,12 +550,13 @@ def run_pass(wl, args, tol, pool, dev, peaks):
         for fam, ent in tj.get(wl.name, {}).items():
             if isinstance(ent, dict) and ent.get("kernel_hash") == kh:
                 counters[fam] = ent
+    # MFMA busy as the counter run measured it (SQ_VALU_MFMA_BUSY_CYCLES over
+    # the family's own dispatches; that run's launch mix includes the t = 0
+    # root pass, so it is not divided by this run's launch times)
     for name, rec in stages.items():
         ent = counters.get(name)
-        if ent and ent.get("executed_flops_per_launch") and rec.get("bound") == "mfma":
-            prec = ent.get("precision", "f32")
-            rec["mfma_executed_frac"] = (ent["executed_flops_per_launch"] / (rec["avg_ms"] / 1e3)
-                                         / 1e12 / PEAK_TFLOPS[prec])
+        if ent and ent.get("mfma_busy") is not None and rec.get("bound") == "mfma":
+            rec["mfma_busy_counters"] = ent["mfma_busy"]
 
     # the dominant kernel family by time in the timed region
     roofline = None
@@ -566,7 +567,7 @@ def run_pass(wl, args, tol, pool, dev, peaks):
                     "peak": dom[1]["peak"], "unit": dom[1]["unit"], "frac": dom[1]["frac"],
                     "traffic": ent.get("bytes_per_launch") if ent else None,
                     "count": "symmetric results at their upper triangle's flops"}
-        for k in ("frac_of_measured_peak", "mfma_executed_frac"):
+        for k in ("frac_of_measured_peak", "mfma_busy_counters"):
             if k in dom[1]:
                 roofline[k] = dom[1][k]
 

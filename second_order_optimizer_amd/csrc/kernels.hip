@@ -534,62 +534,92 @@ __device__ __forceinline__ bool gemm_tile(int e, const GemmTask* __restrict__ ta
         A += a_kc ? (int64_t)kb : (int64_t)kb * tk.lda;
         B += b_kc ? (int64_t)kb : (int64_t)kb * tk.ldb;
     }
+    // where C's rows and columns of the wave's result start, less the offsets
+    // the accumulator places add (64 wm, 64 wn)
+    const int ci0 = rbase - 64 * wm, cj0 = cbase - 64 * wn;
+    const S* Ap = (ua < 2 ? As : Bs) + 64 * (ua & 1);
+    const S* Bp = (ub < 2 ? As : Bs) + 64 * (ub & 1);
+    constexpr bool axpby = AXPBY;   // the launcher picks it from args.epi
+    // C <- alpha op(A) op(B) + beta C (the statistics): the old values of C
+    // are read in halves of the wave's result, the first half while the last
+    // stage's products run (that stage is peeled off the loop, so the stage
+    // registers are dead by then and the loaded values need no registers of
+    // their own inside the loop), the second half after the first is stored:
+    // one exposed round trip per tile instead of one per group of 16
+    constexpr int NV = WaveTile<T>::NV, HALF = NV / 2;
+    T old[HALF];
+    auto load_old = [&](int h0) {
+#pragma unroll
+        for (int e = 0; e < HALF; ++e) {
+            int r, c;
+            (void)wt.get(h0 + e, wm, wn, r, c);
+            const int i = ci0 + r, j = cj0 + c;
+            old[e] = (i < tk.M && j < tk.N) ? C[(int64_t)i * tk.ldc + j] : T(0);
+        }
+    };
     la.load(A, tk.lda, a_kc, i0, kfirst, tk.M, Kp, a_al, xa, c1, c2, dk);
     lb.load(B, tk.ldb, b_kc, j0, kfirst, tk.N, Kp, b_al, xb, c1, c2, dk);
-    for (int k0 = kfirst; k0 < Kp; k0 += BK) {
-        __syncthreads();
-        la.store(As, a_kc);
-        lb.store(Bs, b_kc);
-        __syncthreads();
-        if (k0 + BK < tk.K) {
-            la.load(A, tk.lda, a_kc, i0, k0 + BK, tk.M, Kp, a_al, xa, c1, c2, dk);
-            lb.load(B, tk.ldb, b_kc, j0, k0 + BK, tk.N, Kp, b_al, xb, c1, c2, dk);
+    if constexpr (axpby) {
+        if (Kp > kfirst) {
+            int k0 = kfirst;
+            for (; k0 + BK < Kp; k0 += BK) {   // every stage but the last
+                __syncthreads();
+                la.store(As, a_kc);
+                lb.store(Bs, b_kc);
+                __syncthreads();
+                la.load(A, tk.lda, a_kc, i0, k0 + BK, tk.M, Kp, a_al, xa, c1, c2, dk);
+                lb.load(B, tk.ldb, b_kc, j0, k0 + BK, tk.N, Kp, b_al, xb, c1, c2, dk);
+                if constexpr (F32S) wt.compute_f32(Ap, Bp);
+                else wt.compute(Ap, Bp);
+            }
+            __syncthreads();
+            la.store(As, a_kc);
+            lb.store(Bs, b_kc);
+            __syncthreads();
+            load_old(0);
+            if constexpr (F32S) wt.compute_f32(Ap, Bp);
+            else wt.compute(Ap, Bp);
+        } else {
+            load_old(0);
         }
-        const S* Ap = (ua < 2 ? As : Bs) + 64 * (ua & 1);
-        const S* Bp = (ub < 2 ? As : Bs) + 64 * (ub & 1);
-        if constexpr (F32S) wt.compute_f32(Ap, Bp);
-        else wt.compute(Ap, Bp);
+    } else {
+        for (int k0 = kfirst; k0 < Kp; k0 += BK) {
+            __syncthreads();
+            la.store(As, a_kc);
+            lb.store(Bs, b_kc);
+            __syncthreads();
+            if (k0 + BK < tk.K) {
+                la.load(A, tk.lda, a_kc, i0, k0 + BK, tk.M, Kp, a_al, xa, c1, c2, dk);
+                lb.load(B, tk.ldb, b_kc, j0, k0 + BK, tk.N, Kp, b_al, xb, c1, c2, dk);
+            }
+            if constexpr (F32S) wt.compute_f32(Ap, Bp);
+            else wt.compute(Ap, Bp);
+        }
     }
 
     const T alpha = T(args.alpha), beta = T(args.beta);
-    constexpr bool axpby = AXPBY;   // the launcher picks it from args.epi
     // symmetric result computed on upper tiles only: a wave whose part lies
     // off the diagonal also writes its transpose
     const bool mirror = ((tk.trans >> 5) & 1) && rbase != cbase;
     // ... and one on the diagonal forms j >= i only, each value also stored at
     // its transpose (as the split-K sum does)
     const bool sdiag = ((tk.trans >> 4) & 1) && ((tk.trans >> 5) & 1) && rbase == cbase;
-    // where C's rows and columns of the wave's result start, less the offsets
-    // the accumulator places add (64 wm, 64 wn)
-    const int ci0 = rbase - 64 * wm, cj0 = cbase - 64 * wn;
     // fp32 results of a wave whose 64 x 64 part is wholly in range mirror
     // with 16-byte stores after its own stores (aligned: ldc and the offsets
     // of such products are multiples of 4)
     const bool vmirror = sizeof(T) == 4 && !AXPBY && mirror && rbase + 64 <= tk.M && cbase + 64 <= tk.N &&
                          (tk.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0;
-    // in groups of 16 values: the old C values of a group are all loaded
-    // before its stores (a store may alias a later load as far as the
-    // compiler knows, so one element at a time would serialize the round
-    // trips); mirrored values land in the transposed tile, which no
-    // workgroup reads
+    // mirrored values land in the transposed tile, which no workgroup reads
     double nrm = 0.0;
-    constexpr int NV = WaveTile<T>::NV, GRP = 16;
 #pragma unroll
-    for (int g0 = 0; g0 < NV; g0 += GRP) {
-        T old[GRP];
+    for (int h0 = 0; h0 < NV; h0 += HALF) {
         if constexpr (axpby) {
-#pragma unroll
-            for (int e = 0; e < GRP; ++e) {
-                int r, c;
-                (void)wt.get(g0 + e, wm, wn, r, c);
-                const int i = ci0 + r, j = cj0 + c;
-                old[e] = (i < tk.M && j < tk.N) ? C[(int64_t)i * tk.ldc + j] : T(0);
-            }
+            if (h0 > 0) load_old(h0);   // (a store may alias it as far as the compiler knows)
         }
 #pragma unroll
-        for (int e = 0; e < GRP; ++e) {
+        for (int e = 0; e < HALF; ++e) {
             int r, c;
-            const T v = wt.get(g0 + e, wm, wn, r, c);
+            const T v = wt.get(h0 + e, wm, wn, r, c);
             const int i = ci0 + r, j = cj0 + c;
             if (i < tk.M && j < tk.N && (!sdiag || j >= i)) {
                 T o = alpha * v;
