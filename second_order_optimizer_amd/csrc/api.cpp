@@ -294,16 +294,22 @@ int32_t band_bit(int tiles_n) { return tiles_n >= 4 ? kBandBit : 0; }
 // least-loaded one by tiles x K, which balances uneven tasks and spreads the
 // tasks of a gated launch), the per-XCD counts are evened out by moving tail
 // tiles, and the lists are interleaved: entry 8k + x is XCD x's k-th tile.
-std::vector<TileRef> xcd_tile_order(const std::vector<GemmTask>& tasks) {
+// `group` consecutive tasks that read the same operand (the L and R
+// statistics of one block both read G_b) go to one XCD together, their tiles
+// one after the other, so that the second task's reads can hit that L2.
+std::vector<TileRef> xcd_tile_order(const std::vector<GemmTask>& tasks, int group = 1) {
     std::vector<std::vector<TileRef>> lists(kXcds);
     std::vector<double> load(kXcds, 0.0);
     size_t n = 0;
-    for (size_t i = 0; i < tasks.size(); ++i) {
+    const size_t gs = (size_t)std::max(group, 1);
+    for (size_t i0 = 0; i0 < tasks.size(); i0 += gs) {
         const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-        const size_t before = lists[x].size();
-        task_tiles(tasks[i], (int32_t)i, lists[x]);
-        n += lists[x].size() - before;
-        load[x] += (double)(lists[x].size() - before) * std::max(tasks[i].K, 1);
+        for (size_t i = i0; i < std::min(tasks.size(), i0 + gs); ++i) {
+            const size_t before = lists[x].size();
+            task_tiles(tasks[i], (int32_t)i, lists[x]);
+            n += lists[x].size() - before;
+            load[x] += (double)(lists[x].size() - before) * std::max(tasks[i].K, 1);
+        }
     }
     const size_t q = n / kXcds, r = n % kXcds;
     std::vector<TileRef> pool;
@@ -341,8 +347,8 @@ LaunchRef add_launch_sorted(Blob& blob, const std::vector<GemmTask>& tasks) {
     return L;
 }
 
-LaunchRef add_launch(Blob& blob, const std::vector<GemmTask>& tasks) {
-    const std::vector<TileRef> tiles = xcd_tile_order(tasks);
+LaunchRef add_launch(Blob& blob, const std::vector<GemmTask>& tasks, int group = 1) {
+    const std::vector<TileRef> tiles = xcd_tile_order(tasks, group);
     LaunchRef L;
     L.tasks_off = blob.add(tasks);
     L.tiles_off = blob.add(tiles);
@@ -536,7 +542,10 @@ void build_newton_chunk(shampoo_s* h, NewtonChunk& ch, const std::vector<int>& f
             NewtonStage ns;
             const int parts = allow_split ? newton_split((int)tasks.size() * ut, ld) : 1;
             if (parts == 1) {
-                ns.gemm = add_launch(h->blob, tasks);
+                // the products of one slot in a stage (X T(M) and T(M)^2 both
+                // read M) on one XCD
+                const int per = fids.empty() ? 1 : (int)(tasks.size() / fids.size());
+                ns.gemm = add_launch(h->blob, tasks, per);
             } else {
                 const int64_t pbase = split_off_bytes / esz;
                 const int kp = ld / parts, t32 = ld / 32;
@@ -1072,7 +1081,7 @@ int build_plan(shampoo_s* h) {
             t.trans = 1 | 16 | mbit | band_bit(t.tiles_n);
             tasks.push_back(t);
         }
-        h->gram = add_launch(blob, tasks);
+        h->gram = add_launch(blob, tasks, 2);   // L and R of a block on one XCD
         h->n_gram128 = (int)small.size();
         h->gram128_off = blob.add(small);
         h->splitk = add_launch(blob, sk);
