@@ -789,8 +789,8 @@ FAMILY_OF = [
     ("k_gemm<double, float, float, 2, true, false", "stats_gram_f64", "f64"),
     ("k_gemm<float, float, float, 1, false, false, 1>", "apply_gemm_t", "f32"),
     ("k_gemm<float, float, float, 1, false, false, 2>", "apply_gemm_d", "f32"),
-    ("k_gemm_nt3<true>", "apply_gemm_t", "bf16"),
-    ("k_gemm_nt3<false>", "apply_gemm_d", "bf16"),
+    ("k_gemm_nt3<true", "apply_gemm_t", "bf16"),
+    ("k_gemm_nt3<false", "apply_gemm_d", "bf16"),
     ("k_gemm<float, float, float, 3, false, false", "newton_gemm_f32", "f32"),
     ("k_gemm<double, double, double, 2", "newton_gemm_f64", "f64"),
     ("k_adagrad_norm", "adagrad_norm", None),
