@@ -787,10 +787,10 @@ int build_plan(shampoo_s* h) {
     for (auto& bp : h->blocks) {
         const int rows_per = (int)std::max<int64_t>(1, kElemChunk / bp.nb);
         bp.a_slot = na;
-        // split-precision apply: the first product's tiles of row 0 take the
-        // Adagrad pass of the block, one partial per 128 rows of G
+        // split-precision apply: the first product's tiles take the Adagrad
+        // pass of the block between them, one partial per tile
         bp.a_chunks = bp.small ? 1
-                      : (split_apply && !bp.one_sided) ? ceil_div(bp.mb, kTile)
+                      : (split_apply && !bp.one_sided) ? ceil_div(bp.nb, kTile) * ceil_div(bp.mb, kTile)
                                                         : ceil_div(bp.mb, rows_per);
         na += bp.a_chunks;
         bp.d_slot = nd;
@@ -1167,8 +1167,8 @@ int build_plan(shampoo_s* h) {
             }
             if (split_apply) {
                 // T^T = P_R G_b^T (nb x mb, at off_t): C = A B^T with A = P_R
-                // and B = G_b, both k-contiguous; the tiles of row 0 also
-                // run the block's Adagrad pass.  Then D = P_L T: A = P_L and
+                // and B = G_b, both k-contiguous; its tiles also run the
+                // block's Adagrad pass.  Then D = P_L T: A = P_L and
                 // B = T^T, whose rows are T's columns.
                 NtTask t{};
                 t.a_base = 0; t.a_off = fr.off_p / 4; t.lda = fr.ld;

@@ -692,9 +692,10 @@ __global__ __launch_bounds__(256, MINW) void k_gemm(const GemmTask* __restrict__
 // the 16-deep step, the same for A and B (any k order shared by both gives
 // the same sums; checked on the device), read as one 16-byte LDS load; the
 // row pitch of 40 bf16 (80 bytes) puts the rows of eight lanes on distinct
-// banks.  ADAG: the tiles of row 0 also take B's elements (a gradient block)
-// through the Adagrad accumulator a <- a + g^2 and sum (g / (sqrt(a) + delta))^2
-// for the graft, reading each element of B once per launch.
+// banks.  ADAG: the tiles also take B's elements (a gradient block) through
+// the Adagrad accumulator a <- a + g^2 and sum (g / (sqrt(a) + delta))^2 for
+// the graft, each element of B once per launch: the k-stages of a row of B
+// are spread over the tiles that read it.
 constexpr int kNtBK = 32;
 constexpr int kNtP = kNtBK + 8;
 
@@ -770,8 +771,12 @@ __global__ __launch_bounds__(256, ADAG ? 2 : 3) void k_gemm_nt3(const NtTask* __
     float* C = base_ptr<float>(bases, tk.c_base, tk.c_off);
     const bool a_al = ((reinterpret_cast<uintptr_t>(A) & 15) == 0) && (tk.lda % 4 == 0);
     const bool b_al = ((reinterpret_cast<uintptr_t>(B) & 15) == 0) && (tk.ldb % 4 == 0);
-    // the Adagrad pass over B's elements, by the tiles of row 0 (uniform)
-    const bool adag = ADAG && tk.acc_off >= 0 && ti == 0;
+    // the Adagrad pass over B's elements, spread over the tile rows: tile
+    // (ti, tj) takes the k-stages s with s mod (tile rows) == ti of B's rows
+    // [128 tj, +128), so each element is taken once (uniform per workgroup)
+    const bool adag = ADAG && tk.acc_off >= 0;
+    const int tiles_m = (tk.M + BM - 1) / BM;
+    auto mine = [&](int k0) { return adag && (k0 / kNtBK) % tiles_m == ti; };
     float* acc = args.arena + (adag ? tk.acc_off : 0);
     const bool c_al = b_al && ((reinterpret_cast<uintptr_t>(acc) & 15) == 0);
     const float delta = args.delta;
@@ -832,9 +837,9 @@ __global__ __launch_bounds__(256, ADAG ? 2 : 3) void k_gemm_nt3(const NtTask* __
 
     nt_load<ADAG>(A, tk.lda, i0, tk.M, 0, tk.K, a_al, av);
     nt_load<ADAG>(B, tk.ldb, j0, tk.N, 0, tk.K, b_al, bv);
-    if (adag) acc_load(0);
+    if (mine(0)) acc_load(0);
     for (int k0 = 0; k0 < tk.K; k0 += kNtBK) {
-        if (adag) acc_update(k0);
+        if (mine(k0)) acc_update(k0);
         __syncthreads();   // the previous stage's LDS reads are done
         nt_store(av, Ah, Al);
         nt_store(bv, Bh, Bl);
@@ -842,7 +847,7 @@ __global__ __launch_bounds__(256, ADAG ? 2 : 3) void k_gemm_nt3(const NtTask* __
         if (k0 + kNtBK < tk.K) {
             nt_load<ADAG>(A, tk.lda, i0, tk.M, k0 + kNtBK, tk.K, a_al, av);
             nt_load<ADAG>(B, tk.ldb, j0, tk.N, k0 + kNtBK, tk.K, b_al, bv);
-            if (adag) acc_load(k0 + kNtBK);
+            if (mine(k0 + kNtBK)) acc_load(k0 + kNtBK);
         }
 #pragma unroll
         for (int kk = 0; kk < kNtBK; kk += 16) {
@@ -892,7 +897,7 @@ __global__ __launch_bounds__(256, ADAG ? 2 : 3) void k_gemm_nt3(const NtTask* __
     }
     if (adag) {
         const double sa = block_sum_256(asum, red);
-        if (t == 0) args.partA[tk.acc_slot + tj] = sa;
+        if (t == 0) args.partA[tk.acc_slot + ti * tk.tiles_n + tj] = sa;
     }
 }
 
